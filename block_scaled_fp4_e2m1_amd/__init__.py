@@ -1,0 +1,207 @@
+"""Python binding of the gfx950 two-level block-scaled FP4 library (libfp4_e2m1.so).
+
+Argument marshalling only: every step of quantization and of the products runs in the
+HIP kernels behind the C ABI declared in ``include/fp4_e2m1.h``. torch provides device
+memory and the current stream. There is no CPU path: if the library is missing or the
+device is not gfx950 the calls raise.
+
+Names follow the C ABI: ``quantize_fp4``, ``dequantize_fp4``, ``gemm_w4aX``,
+``grouped_gemm_w4aX``, ``fp4_workspace_bytes``, ``fp4_policy_select``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4_e2m1.so")
+
+FP4_OK = 0
+F32, BF16 = 0, 1
+A16, A8, A4 = 16, 8, 4
+ELEM_E2M1, ELEM_E4M3 = 0, 1
+LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
+POLICY_AUTO, POLICY_Q4, POLICY_Q8 = 0, 4, 8
+
+EXPORTED = ["quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
+            "fp4_workspace_bytes", "fp4_policy_select", "fp4_status_string",
+            "fp4_device_check"]
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("micro", ctypes.c_void_p),
+                ("macro", ctypes.c_void_p), ("rows", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("elem", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m block_scaled_fp4_e2m1_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    T = ctypes.POINTER(_Tensor)
+    lib.quantize_fp4.argtypes = [vp, i32, i64, i64, i64, i32, i32, vp, vp, vp, vp]
+    lib.dequantize_fp4.argtypes = [T, vp, i32, i64, vp]
+    lib.gemm_w4aX.argtypes = [i32, vp, i32, i64, i64, T, vp, i32, i64, vp, sz, vp]
+    lib.grouped_gemm_w4aX.argtypes = [i32, vp, i32, i64, i64, vp, vp, i32, i64, T, vp, i32,
+                                      i64, vp, sz, vp]
+    lib.fp4_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    lib.fp4_workspace_bytes.restype = sz
+    lib.fp4_policy_select.argtypes = [i32, i32]
+    lib.fp4_policy_select.restype = i32
+    lib.fp4_status_string.argtypes = [i32]
+    lib.fp4_status_string.restype = ctypes.c_char_p
+    lib.fp4_device_check.argtypes = []
+    for name in ("quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
+                 "fp4_device_check"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().fp4_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != FP4_OK:
+        raise Fp4Error(status, where)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+@dataclass
+class QTensor:
+    """A quantized [rows x k] tensor in device memory (see include/fp4_e2m1.h)."""
+    codes: torch.Tensor   # uint8
+    micro: torch.Tensor   # uint8, rows*k/16
+    macro: torch.Tensor   # int16 holding FP16 bit patterns, rows*k/256
+    rows: int
+    k: int
+    elem: int = ELEM_E2M1
+    layout: int = LAYOUT_CANONICAL
+
+    def c_struct(self) -> _Tensor:
+        return _Tensor(self.codes.data_ptr(), self.micro.data_ptr(), self.macro.data_ptr(),
+                       self.rows, self.k, self.elem, self.layout)
+
+
+def empty_qtensor(rows: int, k: int, elem: int = ELEM_E2M1, layout: int = LAYOUT_CANONICAL,
+                  device="cuda") -> QTensor:
+    ncodes = rows * k // 2 if elem == ELEM_E2M1 else rows * k
+    return QTensor(torch.empty(ncodes, dtype=torch.uint8, device=device),
+                   torch.empty(rows * k // 16, dtype=torch.uint8, device=device),
+                   torch.empty(rows * k // 256, dtype=torch.int16, device=device),
+                   rows, k, elem, layout)
+
+
+def quantize_fp4(x: torch.Tensor, elem: int = ELEM_E2M1, layout: int = LAYOUT_CANONICAL,
+                 out: QTensor | None = None) -> QTensor:
+    """Two-level block-scaled quantization of a 2-D float32/bf16 device tensor."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    rows, k = x.shape
+    q = out if out is not None else empty_qtensor(rows, k, elem, layout, x.device)
+    st = library().quantize_fp4(_ptr(x), _dtype_code(x.dtype), rows, k, x.stride(0), elem,
+                                layout, _ptr(q.codes), _ptr(q.micro), _ptr(q.macro), _stream())
+    _check(st, "quantize_fp4")
+    return q
+
+
+def dequantize_fp4(q: QTensor, dtype: torch.dtype = torch.float32,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    y = out if out is not None else torch.empty(q.rows, q.k, dtype=dtype, device=q.codes.device)
+    ts = q.c_struct()
+    st = library().dequantize_fp4(ctypes.byref(ts), _ptr(y), _dtype_code(y.dtype), y.stride(0),
+                                  _stream())
+    _check(st, "dequantize_fp4")
+    return y
+
+
+def fp4_workspace_bytes(act: int, m_or_rows: int, n: int, k: int) -> int:
+    return int(library().fp4_workspace_bytes(act, m_or_rows, n, k))
+
+
+def fp4_policy_select(mode: int, layer_flag: bool) -> int:
+    r = int(library().fp4_policy_select(mode, int(bool(layer_flag))))
+    if r < 0:
+        raise Fp4Error(-r, "fp4_policy_select")
+    return r
+
+
+def fp4_device_check() -> int:
+    return int(library().fp4_device_check())
+
+
+def _workspace(act: int, rows: int, n: int, k: int, device, workspace):
+    need = fp4_workspace_bytes(act, rows, n, k)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def gemm_w4aX(act: int, a: torch.Tensor, w: QTensor, out_dtype: torch.dtype = torch.bfloat16,
+              out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """C = A_hat . W_hat^T (W tiled E2M1 [n x k]); act in {A16, A8, A4}."""
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("a must be 2-D with contiguous rows")
+    m = a.shape[0]
+    c = out if out is not None else torch.empty(m, w.rows, dtype=out_dtype, device=a.device)
+    ws, wsb = _workspace(act, m, w.rows, w.k, a.device, workspace)
+    ts = w.c_struct()
+    st = library().gemm_w4aX(act, _ptr(a), _dtype_code(a.dtype), m, a.stride(0), ctypes.byref(ts),
+                             _ptr(c), _dtype_code(c.dtype), c.stride(0), _ptr(ws), wsb, _stream())
+    _check(st, "gemm_w4aX")
+    return c
+
+
+def grouped_gemm_w4aX(act: int, a: torch.Tensor, row_token: torch.Tensor | None,
+                      expert_offsets: torch.Tensor, n_experts: int, total_rows: int, w: QTensor,
+                      out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Mixture-of-experts product over routed rows (experts stacked in w along rows)."""
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("a must be 2-D with contiguous rows")
+    n = w.rows // n_experts
+    c = out if out is not None else torch.empty(total_rows, n, dtype=out_dtype, device=a.device)
+    ws, wsb = _workspace(act, a.shape[0], n, w.k, a.device, workspace)
+    ts = w.c_struct()
+    st = library().grouped_gemm_w4aX(act, _ptr(a), _dtype_code(a.dtype), a.shape[0], a.stride(0),
+                                     _ptr(row_token), _ptr(expert_offsets), n_experts, total_rows,
+                                     ctypes.byref(ts), _ptr(c), _dtype_code(c.dtype), c.stride(0),
+                                     _ptr(ws), wsb, _stream())
+    _check(st, "grouped_gemm_w4aX")
+    return c

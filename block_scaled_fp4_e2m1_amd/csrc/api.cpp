@@ -1,0 +1,244 @@
+// C ABI of the gfx950 two-level block-scaled FP4 library: argument validation, the
+// device-architecture check, and dispatch to the kernels. Every error is reported before
+// anything is enqueued; no other precision or path is ever substituted.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/fp4_e2m1.h"
+#include "fp4_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+fp4_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP4_E_NO_DEVICE;
+  if (dev < kMaxDevices && g_arch_state[dev] != 0) return g_arch_state[dev] == 1 ? FP4_OK : FP4_E_ARCH;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP4_E_NO_DEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_state[dev] = ok ? 1 : 2;
+  return ok ? FP4_OK : FP4_E_ARCH;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t dtype_size(int32_t dt) { return dt == FP4_F32 ? 4 : 2; }
+bool valid_dtype(int32_t dt) { return dt == FP4_F32 || dt == FP4_BF16; }
+bool valid_act(int32_t act) { return act == FP4_A16 || act == FP4_A8 || act == FP4_A4; }
+
+fp4_status launched(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_E_HIP; }
+
+// Checks on a quantized weight tensor shared by the matrix entry points.
+fp4_status check_weights(const fp4_tensor* w) {
+  if (!w || !w->codes || !w->micro || !w->macro) return FP4_E_NULL;
+  if (w->elem != FP4_ELEM_E2M1) return w->elem == FP4_ELEM_E4M3 ? FP4_E_DTYPE : FP4_E_MODE;
+  if (w->layout != FP4_LAYOUT_TILED)
+    return w->layout == FP4_LAYOUT_CANONICAL ? FP4_E_LAYOUT : FP4_E_MODE;
+  if (w->rows < 16 || w->rows % 16 || w->k < 256 || w->k % 256) return FP4_E_SHAPE;
+  if (!aligned16(w->codes) || !aligned16(w->micro) || !aligned(w->macro, 8)) return FP4_E_ALIGN;
+  return FP4_OK;
+}
+
+size_t act_workspace(int32_t act, int64_t rows, int64_t k) {
+  if (act == FP4_A16) return 0;
+  const size_t aq = ((size_t)rows * (size_t)k * 2 + 255) & ~(size_t)255;
+  return aq + (size_t)rows * (size_t)(k / 256) * 4;
+}
+
+// Runs the activation pass when needed and fills the activation part of GemmArgs.
+fp4_status prepare_activations(int32_t act, const void* a, int32_t a_dtype, int64_t rows,
+                               int64_t k, int64_t lda, void* ws, fp4lib::GemmArgs& g,
+                               hipStream_t st) {
+  if (act == FP4_A16) {
+    g.a = a;
+    g.a_is_bf16 = 1;
+    g.lda = lda;
+    g.a_scale = nullptr;
+    return FP4_OK;
+  }
+  _Float16* aq = static_cast<_Float16*>(ws);
+  float* scale = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                          (((size_t)rows * (size_t)k * 2 + 255) & ~(size_t)255));
+  const hipError_t e = fp4lib::launch_act_prep(a, a_dtype == FP4_BF16, rows, k, lda,
+                                               act == FP4_A8, aq, scale, st);
+  if (e != hipSuccess) return FP4_E_HIP;
+  g.a = aq;
+  g.a_is_bf16 = 0;
+  g.lda = k;
+  g.a_scale = scale;
+  return FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp4_status_string(fp4_status s) {
+  switch (s) {
+    case FP4_OK: return "ok";
+    case FP4_E_NULL: return "null pointer";
+    case FP4_E_SHAPE: return "invalid shape";
+    case FP4_E_ALIGN: return "misaligned pointer or stride";
+    case FP4_E_DTYPE: return "unsupported dtype combination";
+    case FP4_E_MODE: return "unknown mode, element type or layout";
+    case FP4_E_NO_DEVICE: return "no HIP device";
+    case FP4_E_ARCH: return "device is not gfx950";
+    case FP4_E_HIP: return "HIP launch failed";
+    case FP4_E_WORKSPACE: return "workspace missing or too small";
+    case FP4_E_LAYOUT: return "wrong packed layout for this operation";
+    default: return "unknown status";
+  }
+}
+
+fp4_status fp4_device_check(void) { return check_device(); }
+
+int32_t fp4_policy_select(int32_t mode, int32_t layer_flag) {
+  switch (mode) {
+    case FP4_POLICY_Q4: return FP4_A4;
+    case FP4_POLICY_Q8: return FP4_A8;
+    case FP4_POLICY_AUTO: return layer_flag ? FP4_A8 : FP4_A4;
+    default: return -FP4_E_MODE;
+  }
+}
+
+size_t fp4_workspace_bytes(int32_t act, int64_t m_or_rows, int64_t n, int64_t k) {
+  (void)n;
+  if (!valid_act(act) || m_or_rows < 0 || k < 0) return 0;
+  return act_workspace(act, m_or_rows, k);
+}
+
+fp4_status quantize_fp4(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                        int32_t elem, int32_t layout, void* codes, uint8_t* micro,
+                        uint16_t* macro, void* stream) {
+  if (!x || !codes || !micro || !macro) return FP4_E_NULL;
+  if (!valid_dtype(x_dtype)) return FP4_E_DTYPE;
+  if (elem != FP4_ELEM_E2M1 && elem != FP4_ELEM_E4M3) return FP4_E_MODE;
+  if (layout != FP4_LAYOUT_CANONICAL && layout != FP4_LAYOUT_TILED) return FP4_E_MODE;
+  if (elem == FP4_ELEM_E4M3 && layout == FP4_LAYOUT_TILED) return FP4_E_LAYOUT;
+  if (rows < 1 || k < 256 || k % 256 || ldx < k) return FP4_E_SHAPE;
+  if (layout == FP4_LAYOUT_TILED && rows % 16) return FP4_E_SHAPE;
+  if (!aligned16(x) || (ldx * (int64_t)dtype_size(x_dtype)) % 16 || !aligned16(codes) ||
+      !aligned16(micro) || !aligned(macro, 2))
+    return FP4_E_ALIGN;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  return launched(fp4lib::launch_quantize(x, x_dtype == FP4_BF16, rows, k, ldx,
+                                          elem == FP4_ELEM_E4M3, layout == FP4_LAYOUT_TILED,
+                                          static_cast<uint8_t*>(codes), micro, macro,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t ldy,
+                          void* stream) {
+  if (!q || !q->codes || !q->micro || !q->macro || !y) return FP4_E_NULL;
+  if (!valid_dtype(y_dtype)) return FP4_E_DTYPE;
+  if (q->elem != FP4_ELEM_E2M1 && q->elem != FP4_ELEM_E4M3) return FP4_E_MODE;
+  if (q->layout != FP4_LAYOUT_CANONICAL && q->layout != FP4_LAYOUT_TILED) return FP4_E_MODE;
+  if (q->elem == FP4_ELEM_E4M3 && q->layout == FP4_LAYOUT_TILED) return FP4_E_LAYOUT;
+  if (q->rows < 1 || q->k < 256 || q->k % 256 || ldy < q->k) return FP4_E_SHAPE;
+  if (q->layout == FP4_LAYOUT_TILED && q->rows % 16) return FP4_E_SHAPE;
+  if (!aligned16(y) || (ldy * (int64_t)dtype_size(y_dtype)) % 16 || !aligned16(q->codes) ||
+      !aligned(q->macro, 2))
+    return FP4_E_ALIGN;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  return launched(fp4lib::launch_dequantize(
+      static_cast<const uint8_t*>(q->codes), q->micro, q->macro, q->rows, q->k,
+      q->elem == FP4_ELEM_E4M3, q->layout == FP4_LAYOUT_TILED, y, y_dtype == FP4_BF16, ldy,
+      static_cast<hipStream_t>(stream)));
+}
+
+fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,
+                     const fp4_tensor* w, void* c, int32_t c_dtype, int64_t ldc,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_act(act)) return FP4_E_MODE;
+  if (!a || !c) return FP4_E_NULL;
+  const fp4_status ws_ok = check_weights(w);
+  if (ws_ok != FP4_OK) return ws_ok;
+  if (!valid_dtype(a_dtype) || !valid_dtype(c_dtype)) return FP4_E_DTYPE;
+  const int64_t n = w->rows, k = w->k;
+  if (m < 1 || lda < k || ldc < n) return FP4_E_SHAPE;
+  if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
+  if (!aligned(c, dtype_size(c_dtype))) return FP4_E_ALIGN;
+  const size_t need = act_workspace(act, m, k);
+  if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return FP4_E_WORKSPACE;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t* codes = static_cast<const uint8_t*>(w->codes);
+
+  if (act == FP4_A16 && a_dtype == FP4_F32)
+    return launched(fp4lib::launch_gemm_f32act(static_cast<const float*>(a), lda, m, k, codes,
+                                               w->micro, w->macro, n, c, c_dtype == FP4_BF16,
+                                               ldc, st));
+  if (act == FP4_A16 && fp4lib::gemv_supports(m, n, k))
+    return launched(fp4lib::launch_gemv_bf16(static_cast<const uint16_t*>(a), lda, m, k, codes,
+                                             w->micro, w->macro, n, c, c_dtype == FP4_BF16,
+                                             ldc, st));
+  fp4lib::GemmArgs g{};
+  const fp4_status prep = prepare_activations(act, a, a_dtype, m, k, lda, workspace, g, st);
+  if (prep != FP4_OK) return prep;
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  g.codes = codes;
+  g.micro = w->micro;
+  g.macro = w->macro;
+  g.c = c;
+  g.c_is_bf16 = c_dtype == FP4_BF16;
+  g.ldc = ldc;
+  return launched(fp4lib::launch_gemm(g, st));
+}
+
+fp4_status grouped_gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t a_rows,
+                             int64_t lda, const int32_t* row_token,
+                             const int32_t* expert_offsets, int32_t n_experts,
+                             int64_t total_rows, const fp4_tensor* w, void* c,
+                             int32_t c_dtype, int64_t ldc, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!valid_act(act)) return FP4_E_MODE;
+  if (!a || !c || !expert_offsets) return FP4_E_NULL;
+  const fp4_status ws_ok = check_weights(w);
+  if (ws_ok != FP4_OK) return ws_ok;
+  if (!valid_dtype(a_dtype) || !valid_dtype(c_dtype)) return FP4_E_DTYPE;
+  if (act == FP4_A16 && a_dtype != FP4_BF16) return FP4_E_DTYPE;
+  if (n_experts < 1 || w->rows % n_experts) return FP4_E_SHAPE;
+  const int64_t n = w->rows / n_experts, k = w->k;
+  if (n % 16 || a_rows < 1 || total_rows < 0 || lda < k || ldc < n) return FP4_E_SHAPE;
+  if (!row_token && total_rows > a_rows) return FP4_E_SHAPE;
+  if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
+  if (!aligned(c, dtype_size(c_dtype)) || !aligned(expert_offsets, 4) ||
+      (row_token && !aligned(row_token, 4)))
+    return FP4_E_ALIGN;
+  const size_t need = act_workspace(act, a_rows, k);
+  if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return FP4_E_WORKSPACE;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  if (total_rows == 0) return FP4_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  fp4lib::GemmArgs g{};
+  const fp4_status prep = prepare_activations(act, a, a_dtype, a_rows, k, lda, workspace, g, st);
+  if (prep != FP4_OK) return prep;
+  g.m = total_rows;
+  g.n = n;
+  g.k = k;
+  g.codes = static_cast<const uint8_t*>(w->codes);
+  g.micro = w->micro;
+  g.macro = w->macro;
+  g.c = c;
+  g.c_is_bf16 = c_dtype == FP4_BF16;
+  g.ldc = ldc;
+  g.row_token = row_token;
+  g.expert_offsets = expert_offsets;
+  g.n_experts = n_experts;
+  return launched(fp4lib::launch_gemm(g, st));
+}
+
+}  // extern "C"

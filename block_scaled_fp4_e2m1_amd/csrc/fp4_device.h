@@ -1,0 +1,133 @@
+// Device helpers shared by the gfx950 kernels: exact scale conversions, vector types,
+// the packed-layout index maps. Format: "NVIDIA Ships TensorRT-LLM 0.16: Native FP4
+// Quantization for Blackwell B200", section "The Mathematical Breakthrough of
+// Microscopic FP4 Scaling" (E2M1 elements, FP8 E4M3 per 16, FP16 per 256).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4dev {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed data that is read once).
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+constexpr int kBlock = 16;    // elements per micro-scale
+constexpr int kGroup = 256;   // elements per macro-scale
+constexpr int kTileRows = 16;
+constexpr int kTileCodeBytes = 2048;  // 16 rows x 256 E2M1 codes
+constexpr int kTileMicroBytes = 256;  // 16 rows x 16 micro-scales
+constexpr int kTileMacro = 16;        // 16 rows x 1 macro-scale
+
+// Round a finite t > 0 to OCP E4M3 (nearest, ties to even significand, saturating at
+// 448) and return the byte. Integer arithmetic on the float32 bits, so the result is the
+// correctly rounded one whatever the hardware rounding mode is.
+__device__ __forceinline__ uint32_t e4m3_rne_pos(float t) {
+  if (!(t > 0x1p-10f)) return 0u;        // at or below half the smallest subnormal
+  if (t >= 464.0f) return 0x7Eu;         // would round past 448
+  const uint32_t u = __float_as_uint(t);
+  const int e = (int)(u >> 23) - 127;    // t > 2^-10 is a normal float32
+  const uint32_t sig = (u & 0x7FFFFFu) | 0x800000u;
+  const int eq = e > -6 ? e : -6;        // binade of the result (or the subnormal range)
+  const int shift = 20 + (eq - e);       // keep 3 fraction bits: units of 2^(eq-3)
+  uint32_t q = sig >> shift;
+  const uint32_t rem = sig & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+  const uint32_t byte = (uint32_t)((eq + 6) * 8) + q;  // q in [0, 16] carries into e
+  return byte < 0x7Eu ? byte : 0x7Eu;
+}
+
+// Value of an E4M3 byte (no NaN bytes are ever produced by this library).
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))  // 2^(e-7)(1+m/8)
+                : (float)m * 0x1p-9f;
+  return (b & 0x80u) ? -mag : mag;
+}
+
+// Round a finite t > 0 to FP16 and clamp into [2^-24, 65504]; returns the bit pattern.
+__device__ __forceinline__ uint32_t fp16_rne_pos_clamped(float t) {
+  if (t >= 65504.0f) return 0x7BFFu;
+  const uint32_t u = __float_as_uint(t);
+  const int e = (int)(u >> 23) - 127;
+  if (e < -25) return 0x0001u;           // rounds to zero: clamp to the smallest subnormal
+  const uint32_t sig = (u & 0x7FFFFFu) | 0x800000u;
+  const int eq = e > -14 ? e : -14;
+  const int shift = 13 + (eq - e);       // keep 10 fraction bits
+  uint32_t q = sig >> shift;
+  const uint32_t rem = sig & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+  uint32_t bits = (uint32_t)((eq + 14) * 1024) + q;
+  if (bits == 0u) bits = 1u;
+  return bits < 0x7BFFu ? bits : 0x7BFFu;
+}
+
+// Value of an FP16 bit pattern (exact, subnormals included).
+__device__ __forceinline__ float fp16_value(uint32_t h) {
+  const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+  float mag = e ? __uint_as_float(((e + 112u) << 23) | (m << 13)) : (float)m * 0x1p-24f;
+  return (h & 0x8000u) ? -mag : mag;
+}
+
+// bfloat16 bits of a finite float32, round to nearest even.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
+
+// E2M1 magnitude (3-bit code) of |x| for effective scale s > 0, by comparing against the
+// exact tie points t*s (t = .25 .75 1.25 1.75 2.5 3.5 5); '>' vs '>=' alternates so that a
+// tie resolves to the even significand. Each t*s is exact in float32.
+struct E2M1Thresholds {
+  float s025, s075, s125, s175, s25, s35, s5;
+  __device__ __forceinline__ explicit E2M1Thresholds(float s)
+      : s025(0.25f * s), s075(0.75f * s), s125(1.25f * s), s175(1.75f * s), s25(2.5f * s),
+        s35(3.5f * s), s5(5.0f * s) {}
+  __device__ __forceinline__ uint32_t mag(float ax) const {
+    const bool b2 = ax >= s175;
+    const bool b1 = ax >= (b2 ? s35 : s075);
+    const float t0 = b2 ? (b1 ? s5 : s25) : (b1 ? s125 : s025);
+    const bool b0 = ax > t0;
+    return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+  }
+};
+
+__device__ __forceinline__ float e2m1_mag_value(uint32_t mag) {
+  // 0, .5, 1, 1.5, 2, 3, 4, 6
+  const uint32_t e = mag >> 1, m = mag & 1u;
+  return e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
+}
+
+// Byte offset of the code dword (8 codes) for row r, columns [c8*8, c8*8+8) inside the
+// tiled layout, and the micro/macro offsets (see the header for the layout).
+__device__ __forceinline__ int64_t tiled_code_offset(int64_t r, int64_t col, int64_t groups) {
+  const int64_t tile = (r >> 4) * groups + (col >> 8);
+  const int c = (int)(col & 255), n = (int)(r & 15);
+  const int t = c >> 5, j = (c >> 3) & 3;
+  return tile * kTileCodeBytes + (t >> 2) * 1024 + (16 * j + n) * 16 + (t & 3) * 4;
+}
+__device__ __forceinline__ int64_t tiled_micro_offset(int64_t r, int64_t col, int64_t groups) {
+  const int64_t tile = (r >> 4) * groups + (col >> 8);
+  const int c = (int)(col & 255), n = (int)(r & 15);
+  const int b = c >> 4;
+  return tile * kTileMicroBytes + (b & 1) * 128 + n * 8 + (b >> 1);
+}
+__device__ __forceinline__ int64_t tiled_macro_offset(int64_t r, int64_t col, int64_t groups) {
+  return ((r >> 4) * groups + (col >> 8)) * kTileMacro + (r & 15);
+}
+
+}  // namespace fp4dev

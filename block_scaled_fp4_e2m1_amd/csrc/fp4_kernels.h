@@ -1,0 +1,56 @@
+// Kernel launchers of the gfx950 library (host side). Each returns the HIP error of the
+// launch; all of them enqueue on the given stream and never synchronize.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4lib {
+
+hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, int64_t ldx,
+                           int elem_e4m3, int tiled, uint8_t* codes, uint8_t* micro,
+                           uint16_t* macro, hipStream_t st);
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const uint16_t* macro,
+                             int64_t rows, int64_t k, int elem_e4m3, int tiled, void* y,
+                             int out_bf16, int64_t ldy, hipStream_t st);
+
+// Activation pass for the matrix kernels: aq[r, c] * scale[r, c/256] == A_hat[r, c].
+hipError_t launch_act_prep(const void* a, int in_bf16, int64_t rows, int64_t k, int64_t lda,
+                           int elem_e4m3, _Float16* aq, float* scale, hipStream_t st);
+
+// Decode product for m <= 8 bf16 activation rows against tiled E2M1 weights [n x k].
+// Returns hipErrorInvalidValue when the shape is outside what the kernel covers.
+bool gemv_supports(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemv_bf16(const uint16_t* a, int64_t lda, int64_t m, int64_t k,
+                            const uint8_t* codes, const uint8_t* micro, const uint16_t* macro,
+                            int64_t n, void* c, int out_bf16, int64_t ldc, hipStream_t st);
+
+// Dense / grouped product on MFMA. The A operand is either the FP16 output of
+// launch_act_prep (with its per-group factors) or raw bf16 activations (factor 1).
+// For the grouped form, rows of expert e are expert_offsets[e] .. expert_offsets[e+1]
+// of the routed list; row_token (optional) maps a routed row to its source row of A.
+struct GemmArgs {
+  const void* a;            // _Float16 (a_is_bf16 == 0) or bf16 bits
+  int a_is_bf16;
+  int64_t lda;              // elements
+  const float* a_scale;     // [a_rows x k/256] or nullptr (== 1)
+  int64_t m;                // rows of C (dense) / total routed rows (grouped)
+  int64_t n, k;
+  const uint8_t* codes;     // tiled E2M1 weights; experts stacked along rows
+  const uint8_t* micro;
+  const uint16_t* macro;
+  void* c;
+  int c_is_bf16;
+  int64_t ldc;
+  const int32_t* row_token;       // grouped only, may be nullptr
+  const int32_t* expert_offsets;  // grouped only; nullptr for a dense product
+  int32_t n_experts;
+};
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+
+// Plain float32 product for float32 activations (small shapes): one thread per output.
+hipError_t launch_gemm_f32act(const float* a, int64_t lda, int64_t m, int64_t k,
+                              const uint8_t* codes, const uint8_t* micro, const uint16_t* macro,
+                              int64_t n, void* c, int out_bf16, int64_t ldc, hipStream_t st);
+
+}  // namespace fp4lib

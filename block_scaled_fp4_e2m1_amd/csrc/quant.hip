@@ -1,0 +1,261 @@
+// Two-level block-scaled quantization kernels for gfx950: quantize (E2M1 or E4M3
+// elements; canonical or tiled output), dequantize, and the activation pass that feeds
+// the matrix kernels.
+//
+// Work mapping: 32 lanes own one 256-element group of one row, 8 consecutive elements
+// per lane (one 16-byte load for bf16, two for float32). A 16-element micro-vector is a
+// lane pair, so its max is one cross-lane exchange; the group max is four more.
+// Source of the method: "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for
+// Blackwell B200", section "The Mathematical Breakthrough of Microscopic FP4 Scaling".
+#include "fp4_device.h"
+#include "fp4_kernels.h"
+
+using namespace fp4dev;
+
+namespace {
+
+template <int IN_BF16>
+__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, float v[8]) {
+  if (IN_BF16) {
+    const uint4 p = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// Scales of the lane's group/block. Returns s = mu * M (exact); writes the FP16 bits of M
+// and the E4M3 byte of mu.
+__device__ __forceinline__ float group_scales(const float v[8], float emax, uint32_t& m_bits,
+                                              uint32_t& mu_byte, float& m_val) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const float amax_b = fmaxf(amax, __shfl_xor(amax, 1));
+  float amax_g = amax_b;
+#pragma unroll
+  for (int o = 2; o < 32; o <<= 1) amax_g = fmaxf(amax_g, __shfl_xor(amax_g, o));
+  m_bits = 0u;
+  m_val = 0.0f;
+  mu_byte = 0u;
+  if (amax_g > 0.0f) {
+    m_bits = fp16_rne_pos_clamped(amax_g / (emax * 448.0f));
+    m_val = fp16_value(m_bits);
+    mu_byte = e4m3_rne_pos(amax_b / (emax * m_val));
+  }
+  return e4m3_value(mu_byte) * m_val;
+}
+
+__device__ __forceinline__ uint32_t sign_of(float f) { return __float_as_uint(f) >> 31; }
+
+template <int IN_BF16, int ELEM_E4M3, int TILED>
+__global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t ldx,
+                                                  int64_t rows, int64_t k,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ micro,
+                                                  uint16_t* __restrict__ macro) {
+  const int64_t groups = k >> 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t seg = gid >> 5;
+  const int li = threadIdx.x & 31;
+  if (seg >= rows * groups) return;  // whole 32-lane segments leave together
+  const int64_t r = seg / groups, g = seg - r * groups;
+  const int64_t col = g * kGroup + li * 8;
+
+  float v[8];
+  load8<IN_BF16>(x, r * ldx + col, v);
+  uint32_t m_bits, mu_byte;
+  float m_val;
+  const float s = group_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
+
+  if (!ELEM_E4M3) {
+    uint32_t word = 0u;
+    if (s > 0.0f) {
+      const E2M1Thresholds th(s);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        word |= (th.mag(fabsf(v[i])) | (sign_of(v[i]) << 3)) << (4 * i);
+    }
+    const int64_t off = TILED ? tiled_code_offset(r, col, groups) : r * (k >> 1) + (col >> 1);
+    *reinterpret_cast<uint32_t*>(codes + off) = word;
+  } else {
+    uint32_t lo = 0u, hi = 0u;
+    if (s > 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b = e4m3_rne_pos(fabsf(v[i]) / s) | (sign_of(v[i]) << 7);
+        if (i < 4) lo |= b << (8 * i); else hi |= b << (8 * (i - 4));
+      }
+    }
+    *reinterpret_cast<uint2*>(codes + r * k + col) = make_uint2(lo, hi);
+  }
+  if ((li & 1) == 0) {
+    const int64_t off = TILED ? tiled_micro_offset(r, col, groups) : r * (k >> 4) + (col >> 4);
+    micro[off] = (uint8_t)mu_byte;
+  }
+  if (li == 0) {
+    const int64_t off = TILED ? tiled_macro_offset(r, col, groups) : r * groups + g;
+    macro[off] = (uint16_t)m_bits;
+  }
+}
+
+template <int OUT_BF16, int ELEM_E4M3, int TILED>
+__global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
+                                                    const uint8_t* __restrict__ micro,
+                                                    const uint16_t* __restrict__ macro,
+                                                    int64_t rows, int64_t k, void* __restrict__ y,
+                                                    int64_t ldy) {
+  const int64_t groups = k >> 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t seg = gid >> 5;
+  const int li = threadIdx.x & 31;
+  if (seg >= rows * groups) return;
+  const int64_t r = seg / groups, g = seg - r * groups;
+  const int64_t col = g * kGroup + li * 8;
+
+  const int64_t mu_off = TILED ? tiled_micro_offset(r, col, groups) : r * (k >> 4) + (col >> 4);
+  const int64_t m_off = TILED ? tiled_macro_offset(r, col, groups) : r * groups + g;
+  const float scale = e4m3_value(micro[mu_off]) * fp16_value(macro[m_off]);  // exact
+  float v[8];
+  if (!ELEM_E4M3) {
+    const int64_t off = TILED ? tiled_code_offset(r, col, groups) : r * (k >> 1) + (col >> 1);
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = (word >> (4 * i)) & 15u;
+      const float mag = e2m1_mag_value(c & 7u) * scale;
+      v[i] = (c & 8u) ? -mag : mag;
+    }
+  } else {
+    const uint2 p = *reinterpret_cast<const uint2*>(codes + r * k + col);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = ((i < 4 ? p.x : p.y) >> (8 * (i & 3))) & 0xFFu;
+      v[i] = e4m3_value(b) * scale;
+    }
+  }
+  if (OUT_BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = bf16_rne_bits(v[2 * i]) | (bf16_rne_bits(v[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + r * ldy + col) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(y) + r * ldy + col);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// Activation pass for the matrix kernels. Quantizes each row like k_quantize and writes
+// the *decoded* element times its micro-scale as FP16 (exact: E2M1 * mu has at most 6
+// significant bits in [2^-10, 2688]; E4M3 * mu * 2^-3 at most 8 bits in [2^-21, 25088]),
+// plus one float32 factor per 256-group (M, or 8*M for E4M3 elements), so that
+//   A_hat[r, c] = aq[r, c] * scale[r, c / 256]   exactly.
+template <int IN_BF16, int ELEM_E4M3>
+__global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, int64_t lda,
+                                                  int64_t rows, int64_t k,
+                                                  _Float16* __restrict__ aq,
+                                                  float* __restrict__ scale) {
+  const int64_t groups = k >> 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t seg = gid >> 5;
+  const int li = threadIdx.x & 31;
+  if (seg >= rows * groups) return;
+  const int64_t r = seg / groups, g = seg - r * groups;
+  const int64_t col = g * kGroup + li * 8;
+
+  float v[8];
+  load8<IN_BF16>(a, r * lda + col, v);
+  uint32_t m_bits, mu_byte;
+  float m_val;
+  const float s = group_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
+  const float mu = e4m3_value(mu_byte);
+  half2_t out[4];
+  if (!ELEM_E4M3) {
+    const E2M1Thresholds th(s > 0.0f ? s : 1.0f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float mag = s > 0.0f ? e2m1_mag_value(th.mag(fabsf(v[i]))) * mu : 0.0f;
+      const _Float16 h = (_Float16)(sign_of(v[i]) ? -mag : mag);
+      if (i & 1) out[i >> 1][1] = h; else out[i >> 1][0] = h;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e = s > 0.0f ? e4m3_value(e4m3_rne_pos(fabsf(v[i]) / s)) : 0.0f;
+      const float mag = e * mu * 0.125f;
+      const _Float16 h = (_Float16)(sign_of(v[i]) ? -mag : mag);
+      if (i & 1) out[i >> 1][1] = h; else out[i >> 1][0] = h;
+    }
+  }
+  uint4 pk;
+  pk.x = __builtin_bit_cast(uint32_t, out[0]);
+  pk.y = __builtin_bit_cast(uint32_t, out[1]);
+  pk.z = __builtin_bit_cast(uint32_t, out[2]);
+  pk.w = __builtin_bit_cast(uint32_t, out[3]);
+  *reinterpret_cast<uint4*>(aq + r * k + col) = pk;
+  if (li == 0) scale[r * groups + g] = ELEM_E4M3 ? m_val * 8.0f : m_val;
+}
+
+inline unsigned blocks_for(int64_t rows, int64_t k) {
+  const int64_t threads = rows * (k >> 8) * 32;
+  return (unsigned)((threads + 255) / 256);
+}
+
+}  // namespace
+
+namespace fp4lib {
+
+hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, int64_t ldx,
+                           int elem_e4m3, int tiled, uint8_t* codes, uint8_t* micro,
+                           uint16_t* macro, hipStream_t st) {
+  const dim3 grid(blocks_for(rows, k)), block(256);
+#define FP4_Q(B, E, T) \
+  hipLaunchKernelGGL((k_quantize<B, E, T>), grid, block, 0, st, x, ldx, rows, k, codes, micro, macro)
+  if (in_bf16) {
+    if (elem_e4m3) FP4_Q(1, 1, 0); else if (tiled) FP4_Q(1, 0, 1); else FP4_Q(1, 0, 0);
+  } else {
+    if (elem_e4m3) FP4_Q(0, 1, 0); else if (tiled) FP4_Q(0, 0, 1); else FP4_Q(0, 0, 0);
+  }
+#undef FP4_Q
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const uint16_t* macro,
+                             int64_t rows, int64_t k, int elem_e4m3, int tiled, void* y,
+                             int out_bf16, int64_t ldy, hipStream_t st) {
+  const dim3 grid(blocks_for(rows, k)), block(256);
+#define FP4_D(B, E, T) \
+  hipLaunchKernelGGL((k_dequantize<B, E, T>), grid, block, 0, st, codes, micro, macro, rows, k, y, ldy)
+  if (out_bf16) {
+    if (elem_e4m3) FP4_D(1, 1, 0); else if (tiled) FP4_D(1, 0, 1); else FP4_D(1, 0, 0);
+  } else {
+    if (elem_e4m3) FP4_D(0, 1, 0); else if (tiled) FP4_D(0, 0, 1); else FP4_D(0, 0, 0);
+  }
+#undef FP4_D
+  return hipGetLastError();
+}
+
+hipError_t launch_act_prep(const void* a, int in_bf16, int64_t rows, int64_t k, int64_t lda,
+                           int elem_e4m3, _Float16* aq, float* scale, hipStream_t st) {
+  const dim3 grid(blocks_for(rows, k)), block(256);
+  if (in_bf16) {
+    if (elem_e4m3) hipLaunchKernelGGL((k_act_prep<1, 1>), grid, block, 0, st, a, lda, rows, k, aq, scale);
+    else hipLaunchKernelGGL((k_act_prep<1, 0>), grid, block, 0, st, a, lda, rows, k, aq, scale);
+  } else {
+    if (elem_e4m3) hipLaunchKernelGGL((k_act_prep<0, 1>), grid, block, 0, st, a, lda, rows, k, aq, scale);
+    else hipLaunchKernelGGL((k_act_prep<0, 0>), grid, block, 0, st, a, lda, rows, k, aq, scale);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp4lib

@@ -1,0 +1,168 @@
+/*
+ * fp4_e2m1.h -- C ABI of the MI355X (gfx950) two-level block-scaled FP4 library.
+ *
+ * The format ("NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for Blackwell
+ * B200", section "The Mathematical Breakthrough of Microscopic FP4 Scaling", items 1-3):
+ *   - elements are E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; magnitudes
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6}; no Inf/NaN;
+ *   - each micro-vector of 16 consecutive elements (along K, inside one row) carries an
+ *     FP8 E4M3 (OCP, max 448) micro-scale mu;
+ *   - each run of 16 micro-vectors (256 elements) shares an FP16 macro-scale M;
+ *   - value(x) = e2m1(code) * mu * M.
+ * Scale selection (max-abs): M = RNE_fp16(amax_256 / (emax * 448)) clamped to
+ * [2^-24, 65504] when amax_256 > 0 (else 0); mu = RNE_e4m3(amax_16 / (emax * M));
+ * code = RNE_elem(|x| / (mu * M)) with the sign of x kept (a block whose mu*M is 0 gets
+ * code 0). emax = 6 for E2M1 elements, 448 for E4M3 elements (8-bit activations of W4A8
+ * layers, "llama.cpp Put Precision Policy Inside the Model", section "One model can need
+ * more than one precision"). Every rounding is to nearest, ties to even, saturating.
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller (e.g. torch tensors);
+ *     the library never allocates, frees or synchronizes.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it and the
+ *     call returns; device faults surface at the caller's next synchronization.
+ *   - Arguments are validated before anything is enqueued. On any error nothing is
+ *     enqueued and a status code is returned. There is no fallback to another precision
+ *     or another path (fail fast, as the AdaLLM page describes its decode path).
+ *   - Inputs must be finite; non-finite inputs give unspecified codes.
+ *   - The library runs only on gfx950 (FP4_E_ARCH elsewhere).
+ *
+ * Packed layouts of a quantized [rows x k] tensor (k % 256 == 0):
+ *   CANONICAL  codes: row-major, E2M1 two per byte (element 2i in the low nibble of byte
+ *              i) or E4M3 one per byte; micro[r*k/16 + b]; macro[r*k/256 + g].
+ *   TILED      (E2M1 only, rows % 16 == 0) the same bytes permuted so that a 64-lane
+ *              wave reads a 16-row x 256-column tile with two coalesced 16-byte loads
+ *              per lane. Tile T = (r/16) * (k/256) + g. Inside a tile, with n = r % 16,
+ *              column c = k_in_tile (0..255), t = c / 32, j = (c % 32) / 8:
+ *                code byte  T*2048 + (t/4)*1024 + (16*j + n)*16 + (t%4)*4 + (c%8)/2
+ *                           (nibble order inside the byte as canonical)
+ *                micro byte T*256 + p*128 + n*8 + t   for block b = c/16 = 2t + p
+ *                macro      T*16 + n                  (uint16 index)
+ *              Total sizes equal the canonical ones.
+ */
+#ifndef FP4_E2M1_H
+#define FP4_E2M1_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fp4_status;
+enum {
+  FP4_OK = 0,
+  FP4_E_NULL = 1,       /* a required pointer is NULL                                  */
+  FP4_E_SHAPE = 2,      /* bad size: k % 256, rows % 16 (tiled), m/n/rows < 1, ld < k  */
+  FP4_E_ALIGN = 3,      /* a pointer or row stride is not 16-byte aligned              */
+  FP4_E_DTYPE = 4,      /* unsupported dtype / precision combination                    */
+  FP4_E_MODE = 5,       /* unknown act, elem, layout or policy value                    */
+  FP4_E_NO_DEVICE = 6,  /* no HIP device is visible                                    */
+  FP4_E_ARCH = 7,       /* the current device is not gfx950                             */
+  FP4_E_HIP = 8,        /* a HIP runtime call or kernel launch failed                   */
+  FP4_E_WORKSPACE = 9,  /* workspace NULL/too small for fp4_workspace_bytes()           */
+  FP4_E_LAYOUT = 10     /* the operation needs the other packed layout                  */
+};
+
+enum { FP4_F32 = 0, FP4_BF16 = 1 };                         /* element types of x/y/a/c */
+enum { FP4_A16 = 16, FP4_A8 = 8, FP4_A4 = 4 };              /* activation precision      */
+enum { FP4_ELEM_E2M1 = 0, FP4_ELEM_E4M3 = 1 };              /* quantized element type    */
+enum { FP4_LAYOUT_CANONICAL = 0, FP4_LAYOUT_TILED = 1 };
+enum { FP4_POLICY_AUTO = 0, FP4_POLICY_Q4 = 4, FP4_POLICY_Q8 = 8 };
+
+/* A quantized tensor in device memory (see the layouts above). */
+typedef struct fp4_tensor {
+  const void* codes;       /* packed codes                                   */
+  const uint8_t* micro;    /* rows * k / 16 E4M3 micro-scales                */
+  const uint16_t* macro;   /* rows * k / 256 FP16 macro-scales (bit patterns) */
+  int64_t rows;
+  int64_t k;
+  int32_t elem;            /* FP4_ELEM_*   */
+  int32_t layout;          /* FP4_LAYOUT_* */
+} fp4_tensor;
+
+/*
+ * quantize_fp4 -- two-level block-scaled quantization of x [rows x k].
+ *   x        device, FP4_F32 or FP4_BF16 values, row r at x + r*ldx elements
+ *   ldx      row stride in elements (>= k; ldx * sizeof(elem) % 16 == 0)
+ *   elem     FP4_ELEM_E2M1 (4-bit codes) or FP4_ELEM_E4M3 (8-bit codes, canonical only)
+ *   layout   FP4_LAYOUT_CANONICAL or FP4_LAYOUT_TILED (E2M1, rows % 16 == 0)
+ *   codes    device out: rows*k/2 bytes (E2M1) or rows*k bytes (E4M3), 16-byte aligned
+ *   micro    device out: rows*k/16 bytes
+ *   macro    device out: rows*k/256 uint16
+ * Source: TensorRT-LLM FP4 page, section on microscopic FP4 scaling, items 1-2.
+ */
+fp4_status quantize_fp4(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                        int32_t elem, int32_t layout, void* codes, uint8_t* micro,
+                        uint16_t* macro, void* stream);
+
+/*
+ * dequantize_fp4 -- y = value(code) * mu * M for every element of q (either layout).
+ *   y        device out [q->rows x q->k], FP4_F32 (exact) or FP4_BF16 (round to nearest
+ *            even of the exact value), row stride ldy elements (16-byte aligned rows)
+ * Source: TensorRT-LLM FP4 page, section on microscopic FP4 scaling, item 3 (scales are
+ * applied before the dot products).
+ */
+fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t ldy,
+                          void* stream);
+
+/*
+ * gemm_w4aX -- C[m x n] = A_hat . W_hat^T with float32 accumulation.
+ *   act      FP4_A16: A_hat = A;  FP4_A4: A_hat = dequant(quant_e2m1(A));
+ *            FP4_A8: A_hat = dequant(quant_e4m3(A)); A is quantized on the device per
+ *            call (dynamic activation quantization, no calibration).
+ *   a        device [m x k] (FP4_BF16, or FP4_F32), row stride lda elements
+ *   w        quantized weights [n x k], E2M1, TILED layout (FP4_E_LAYOUT otherwise)
+ *   c        device out [m x n], FP4_BF16 (round to nearest even) or FP4_F32, stride ldc
+ *   workspace device scratch of at least fp4_workspace_bytes(act, m, n, k) bytes
+ *            (may be NULL when that is 0); contents are overwritten
+ * Source: "llama.cpp Put Precision Policy Inside the Model", intro and section "One model
+ * can need more than one precision" (W4A4, W4A8 and W4A16 layers).
+ */
+fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,
+                     const fp4_tensor* w, void* c, int32_t c_dtype, int64_t ldc,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * grouped_gemm_w4aX -- mixture-of-experts product: for expert e and every routed row r
+ * in [expert_offsets[e], expert_offsets[e+1]):
+ *     C[r, :] = A_hat[src(r), :] . W_hat_e^T,  src(r) = row_token ? row_token[r] : r
+ *   a              device [a_rows x k], row stride lda (bf16 or f32)
+ *   row_token      device int32 [total_rows] source row of each routed row, or NULL
+ *   expert_offsets device int32 [n_experts + 1], non-decreasing, [0] = 0,
+ *                  [n_experts] = total_rows (checked only in debug builds)
+ *   w              quantized weights, experts stacked: rows = n_experts * n, TILED
+ *   c              device out [total_rows x n] (bf16/f32), stride ldc
+ *   workspace      >= fp4_workspace_bytes(act, a_rows, n, k)
+ * Source: llama.cpp precision-policy page, section "One model can need more than one
+ * precision" (the same routing for mixture-of-experts operations).
+ */
+fp4_status grouped_gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t a_rows,
+                             int64_t lda, const int32_t* row_token,
+                             const int32_t* expert_offsets, int32_t n_experts,
+                             int64_t total_rows, const fp4_tensor* w, void* c,
+                             int32_t c_dtype, int64_t ldc, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace gemm_w4aX / grouped_gemm_w4aX need (0 for FP4_A16). */
+size_t fp4_workspace_bytes(int32_t act, int64_t m_or_rows, int64_t n, int64_t k);
+
+/*
+ * fp4_policy_select -- per-layer precision policy: FP4_POLICY_Q4 -> FP4_A4,
+ * FP4_POLICY_Q8 -> FP4_A8, FP4_POLICY_AUTO -> (layer_flag ? FP4_A8 : FP4_A4).
+ * Returns -FP4_E_MODE for an unknown mode. Source: llama.cpp precision-policy page,
+ * section "Local inference is becoming a policy engine" (q4 / q8 / auto).
+ */
+int32_t fp4_policy_select(int32_t mode, int32_t layer_flag);
+
+/* Static, human-readable name of a status code. */
+const char* fp4_status_string(fp4_status status);
+
+/* Device check without launching anything: FP4_OK on gfx950, else the error code. */
+fp4_status fp4_device_check(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4_E2M1_H */

@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports every function include/fp4_e2m1.h declares, and its
+host-side logic (validation before any launch, policy table, workspace sizes, status
+strings) behaves as documented. No compute is run here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4_e2m1.h")
+
+lib_mod = pytest.importorskip("block_scaled_fp4_e2m1_amd")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lib_mod.LIB_PATH):
+        pytest.fail("libfp4_e2m1.so is not built (python -m block_scaled_fp4_e2m1_amd.build)")
+    return lib_mod.library()
+
+
+def test_header_declares_the_four_operations():
+    names = _declared_functions()
+    for n in ("quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(lib_mod.EXPORTED) == names
+
+
+def test_status_strings(lib):
+    assert lib_mod.status_string(0) == "ok"
+    for s in range(1, 11):
+        assert lib_mod.status_string(s) not in ("ok", "unknown status")
+    assert lib_mod.status_string(99) == "unknown status"
+
+
+def test_policy_select(lib):
+    P = lib_mod
+    assert P.fp4_policy_select(P.POLICY_Q4, True) == P.A4
+    assert P.fp4_policy_select(P.POLICY_Q4, False) == P.A4
+    assert P.fp4_policy_select(P.POLICY_Q8, False) == P.A8
+    assert P.fp4_policy_select(P.POLICY_AUTO, True) == P.A8
+    assert P.fp4_policy_select(P.POLICY_AUTO, False) == P.A4
+    with pytest.raises(P.Fp4Error):
+        P.fp4_policy_select(3, False)
+
+
+def test_workspace_bytes(lib):
+    P = lib_mod
+    assert P.fp4_workspace_bytes(P.A16, 2048, 4096, 4096) == 0
+    m, k = 2048, 4096
+    need = P.fp4_workspace_bytes(P.A4, m, 4096, k)
+    assert need >= m * k * 2 + m * (k // 256) * 4
+    assert P.fp4_workspace_bytes(P.A8, m, 4096, k) == need
+    assert P.fp4_workspace_bytes(7, m, 4096, k) == 0
+
+
+def test_validation_happens_before_any_device_use(lib):
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)  # never dereferenced: every call below fails validation first
+    null = vp(0)
+    # null input
+    assert lib.quantize_fp4(null, 1, 16, 256, 256, 0, 0, fake, fake, fake, null) == 1
+    # bad dtype / elem / layout / shapes / alignment
+    assert lib.quantize_fp4(fake, 7, 16, 256, 256, 0, 0, fake, fake, fake, null) == 4
+    assert lib.quantize_fp4(fake, 1, 16, 256, 256, 5, 0, fake, fake, fake, null) == 5
+    assert lib.quantize_fp4(fake, 1, 16, 256, 256, 1, 1, fake, fake, fake, null) == 10
+    assert lib.quantize_fp4(fake, 1, 16, 300, 300, 0, 0, fake, fake, fake, null) == 2
+    assert lib.quantize_fp4(fake, 1, 15, 256, 256, 0, 1, fake, fake, fake, null) == 2
+    assert lib.quantize_fp4(fake, 1, 16, 256, 100, 0, 0, fake, fake, fake, null) == 2
+    assert lib.quantize_fp4(vp((1 << 20) + 2), 1, 16, 256, 256, 0, 0, fake, fake, fake, null) == 3
+    assert lib.quantize_fp4(fake, 1, 16, 256, 260, 0, 0, fake, fake, fake, null) == 3
+    T = lib_mod._Tensor
+    w = T(1 << 20, 1 << 21, 1 << 22, 256, 512, 0, 1)
+    assert lib.gemm_w4aX(5, fake, 1, 8, 512, ctypes.byref(w), fake, 1, 256, null, 0, null) == 5
+    wc = T(1 << 20, 1 << 21, 1 << 22, 256, 512, 0, 0)  # canonical weights
+    assert lib.gemm_w4aX(16, fake, 1, 8, 512, ctypes.byref(wc), fake, 1, 256, null, 0, null) == 10
+    w8 = T(1 << 20, 1 << 21, 1 << 22, 256, 512, 1, 1)  # E4M3 weights
+    assert lib.gemm_w4aX(16, fake, 1, 8, 512, ctypes.byref(w8), fake, 1, 256, null, 0, null) == 4
+    wr = T(1 << 20, 1 << 21, 1 << 22, 250, 512, 0, 1)  # rows not a multiple of 16
+    assert lib.gemm_w4aX(16, fake, 1, 8, 512, ctypes.byref(wr), fake, 1, 256, null, 0, null) == 2
+    # A4 needs a workspace
+    assert lib.gemm_w4aX(4, fake, 1, 8, 512, ctypes.byref(w), fake, 1, 256, null, 0, null) == 9
+    # grouped: expert count must divide the stacked rows; offsets are required
+    assert lib.grouped_gemm_w4aX(4, fake, 1, 64, 512, null, fake, 3, 64, ctypes.byref(w), fake, 1,
+                                 256, fake, 1 << 30, null) == 2
+    assert lib.grouped_gemm_w4aX(4, fake, 1, 64, 512, null, null, 2, 64, ctypes.byref(w), fake, 1,
+                                 256, fake, 1 << 30, null) == 1
+
+
+def test_device_check_reports_missing_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.fp4_device_check() == 6

@@ -1,0 +1,217 @@
+"""GPU parity of gemm_w4aX (W4A16 decode / W4A16 / W4A8 / W4A4) and grouped_gemm_w4aX
+against the float64 oracle, through the C ABI.
+
+Gates (float32 accumulation on exact operands):
+  float32 output: ||C - C64||_F / ||C64||_F <= 1e-5
+  bf16 output:    ||C - RNE_bf16(C64)||_F / ||RNE_bf16(C64)||_F <= 1e-3 and >= 99.9% of
+                  elements equal to RNE_bf16(C64) or one bf16 step away.
+Full-size workloads are checked on sampled rows/columns that the oracle computes one by
+one; small shapes (several tiles plus ragged tails) are checked in full."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._util import host, to_device_bf16, bf16_values, bf16_gate, f32_gate
+
+pytestmark = pytest.mark.gpu
+
+fp4 = pytest.importorskip("block_scaled_fp4_e2m1_amd")
+
+ACTS = {16: "A16", 8: "A8", 4: "A4"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert fp4.fp4_device_check() == 0, "device is not gfx950"
+
+
+def _wq(w: np.ndarray) -> "fp4.QTensor":
+    return fp4.quantize_fp4(torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda(),
+                            layout=fp4.LAYOUT_TILED)
+
+
+def _oracle_c(a_vals: np.ndarray, w: np.ndarray, act: int) -> np.ndarray:
+    return oracle.gemm(a_vals, oracle.quantize(w.astype(np.float64)), act)
+
+
+def test_tiny_w4a16_fp32():
+    a, w = workloads.tiny()
+    print("[case] tiny W4A16 fp32 16x512x256", flush=True)
+    c = fp4.gemm_w4aX(fp4.A16, torch.from_numpy(a).cuda(), _wq(w), out_dtype=torch.float32)
+    f32_gate(host(c), _oracle_c(a.astype(np.float64), w, oracle.A16))
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("k,n", [(256, 16), (1024, 48), (4096, 1024), (8192, 64)])
+def test_decode_gemv_shapes(m, k, n):
+    rng = np.random.default_rng(200 + m + k + n)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    w[:, rng.choice(k, 2, replace=False)] *= 100
+    a = workloads.to_bf16_values(rng.standard_normal((m, k)).astype(np.float32))
+    print(f"[case] gemv m={m} k={k} n={n}", flush=True)
+    wq = _wq(w)
+    ad = to_device_bf16(a)
+    ref = _oracle_c(a.astype(np.float64), w, oracle.A16)
+    f32_gate(host(fp4.gemm_w4aX(fp4.A16, ad, wq, out_dtype=torch.float32)), ref)
+    bf16_gate(bf16_values(fp4.gemm_w4aX(fp4.A16, ad, wq)), oracle.formats.bf16_round(ref))
+
+
+def test_decode_workload_full_size_sampled():
+    a, w, _ = workloads.decode()
+    print("[case] decode W4A16 8x4096x14336 (sampled columns)", flush=True)
+    wq = _wq(w)
+    c = fp4.gemm_w4aX(fp4.A16, to_device_bf16(a), wq)
+    cols = np.sort(np.random.default_rng(201).choice(w.shape[0], 512, replace=False))
+    ref = _oracle_c(a.astype(np.float64), w[cols], oracle.A16)
+    bf16_gate(bf16_values(c)[:, cols], oracle.formats.bf16_round(ref))
+
+
+@pytest.mark.parametrize("act", [16, 8, 4])
+@pytest.mark.parametrize("m,n,k", [(200, 400, 768), (17, 128, 256), (130, 272, 1280)])
+def test_gemm_small_shapes(act, m, n, k):
+    rng = np.random.default_rng(300 + act + m + n + k)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    a[:, rng.choice(k, 3, replace=False)] *= 50
+    a = workloads.to_bf16_values(a)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    print(f"[case] gemm {ACTS[act]} m={m} n={n} k={k}", flush=True)
+    wq = _wq(w)
+    ad = to_device_bf16(a)
+    ref = _oracle_c(a.astype(np.float64), w, act)
+    f32_gate(host(fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32)), ref)
+    bf16_gate(bf16_values(fp4.gemm_w4aX(act, ad, wq)), oracle.formats.bf16_round(ref))
+
+
+def test_gemm_float32_activations_a4():
+    rng = np.random.default_rng(302)
+    a = rng.standard_normal((40, 512)).astype(np.float32)
+    w = (0.02 * rng.standard_normal((64, 512))).astype(np.float32)
+    print("[case] gemm A4 float32 activations", flush=True)
+    c = fp4.gemm_w4aX(fp4.A4, torch.from_numpy(a).cuda(), _wq(w), out_dtype=torch.float32)
+    f32_gate(host(c), _oracle_c(a.astype(np.float64), w, oracle.A4))
+
+
+def test_prefill_w4a4_full_size_sampled():
+    a, w, _ = workloads.prefill()
+    print("[case] prefill W4A4 2048x4096x4096 (sampled)", flush=True)
+    c = fp4.gemm_w4aX(fp4.A4, to_device_bf16(a), _wq(w))
+    rng = np.random.default_rng(203)
+    rows = np.sort(rng.choice(a.shape[0], 96, replace=False))
+    cols = np.sort(rng.choice(w.shape[0], 384, replace=False))
+    ref = _oracle_c(a[rows].astype(np.float64), w[cols], oracle.A4)
+    bf16_gate(bf16_values(c)[np.ix_(rows, cols)], oracle.formats.bf16_round(ref))
+
+
+@pytest.mark.parametrize("mode", [fp4.POLICY_AUTO, fp4.POLICY_Q4, fp4.POLICY_Q8])
+def test_policy_stack_full_size_sampled(mode):
+    flags = workloads.policy_flags()
+    rng = np.random.default_rng(204 + mode)
+    for layer in range(8):
+        w, x = workloads.policy_layer(layer)
+        act = fp4.fp4_policy_select(mode, bool(flags[layer]))
+        assert act == oracle.policy_select(mode, bool(flags[layer]))
+        print(f"[case] policy mode={mode} layer={layer} act={ACTS[act]}", flush=True)
+        c = fp4.gemm_w4aX(act, to_device_bf16(x), _wq(w))
+        rows = np.sort(rng.choice(x.shape[0], 32, replace=False))
+        cols = np.sort(rng.choice(w.shape[0], 128, replace=False))
+        ref = _oracle_c(x[rows].astype(np.float64), w[cols], act)
+        bf16_gate(bf16_values(c)[np.ix_(rows, cols)], oracle.formats.bf16_round(ref))
+        if mode != fp4.POLICY_AUTO:
+            break  # forced modes: one layer is enough
+
+
+def _grouped_case(act, tokens, experts, top_k, k, n, seed, with_token_map=True):
+    _, row_token, offsets, _ = workloads.moe_routing(tokens=tokens, experts=experts, top_k=top_k, seed=seed)
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((tokens, k)).astype(np.float32)
+    a[:, rng.choice(k, 2, replace=False)] *= 50
+    a = workloads.to_bf16_values(a)
+    w = (0.02 * rng.standard_normal((experts * n, k))).astype(np.float32)
+    R = int(offsets[-1])
+    if not with_token_map:
+        a = a[row_token]
+    wq = _wq(w)
+    c = fp4.grouped_gemm_w4aX(act, to_device_bf16(a),
+                              torch.from_numpy(row_token).cuda() if with_token_map else None,
+                              torch.from_numpy(offsets).cuda(), experts, R, wq,
+                              out_dtype=torch.float32)
+    got = host(c)
+    ref = oracle.grouped_gemm(a.astype(np.float64), row_token if with_token_map else None,
+                              offsets, oracle.quantize(w.astype(np.float64)), experts, act)
+    full = np.concatenate([ref[e] for e in range(experts)], axis=0)
+    f32_gate(got, full)
+    return offsets
+
+
+@pytest.mark.parametrize("act", [4, 8, 16])
+@pytest.mark.parametrize("with_token_map", [True, False])
+def test_grouped_small(act, with_token_map):
+    print(f"[case] grouped {ACTS[act]} token_map={with_token_map}", flush=True)
+    offsets = _grouped_case(act, tokens=420, experts=5, top_k=2, k=512, n=144, seed=7,
+                            with_token_map=with_token_map)
+    assert np.any(np.diff(offsets) > 128)  # some expert spans several row tiles
+
+
+def test_grouped_empty_expert_and_many_experts():
+    print("[case] grouped with empty experts, 100 experts", flush=True)
+    offsets = _grouped_case(4, tokens=40, experts=100, top_k=2, k=256, n=32, seed=11)
+    assert np.any(np.diff(offsets) == 0)
+
+
+def test_moe_workload_full_size_subset_of_experts():
+    cfg = workloads.WORKLOADS["moe_w4a4"]
+    E, H, I, T = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["tokens"]
+    _, row_token, offsets, _ = workloads.moe_routing()
+    R = int(offsets[-1])
+    x = workloads.moe_tokens()
+    counts = np.diff(offsets)
+    picks = sorted({int(np.argmin(counts)), int(np.argmax(counts)), 5, 77})
+    print(f"[case] MoE W4A4 full size, experts checked {picks}", flush=True)
+    w1q = fp4.empty_qtensor(E * 2 * I, H, layout=fp4.LAYOUT_TILED)
+    w2q = fp4.empty_qtensor(E * H, I, layout=fp4.LAYOUT_TILED)
+    w1_keep, w2_keep = {}, {}
+    for e in range(E):
+        w1, w2 = workloads.moe_expert_weights(e)
+        for wt, q, keep in ((w1, w1q, w1_keep), (w2, w2q, w2_keep)):
+            rows, k = wt.shape
+            sub = fp4.QTensor(q.codes[e * rows * k // 2:(e + 1) * rows * k // 2],
+                              q.micro[e * rows * k // 16:(e + 1) * rows * k // 16],
+                              q.macro[e * rows * k // 256:(e + 1) * rows * k // 256],
+                              rows, k, 0, fp4.LAYOUT_TILED)
+            fp4.quantize_fp4(torch.from_numpy(wt).cuda(), layout=fp4.LAYOUT_TILED, out=sub)
+            if e in picks:
+                keep[e] = wt
+    xd = to_device_bf16(x)
+    rt = torch.from_numpy(row_token).cuda()
+    off = torch.from_numpy(offsets).cuda()
+    y1 = fp4.grouped_gemm_w4aX(fp4.A4, xd, rt, off, E, R, w1q)
+    x2 = workloads.moe_down_inputs(R)
+    y2 = fp4.grouped_gemm_w4aX(fp4.A4, to_device_bf16(x2), None, off, E, R, w2q)
+    y1h, y2h = bf16_values(y1), bf16_values(y2)
+    for e in picks:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        r1 = oracle.gemm(x[row_token[lo:hi]].astype(np.float64),
+                         oracle.quantize(w1_keep[e].astype(np.float64)), oracle.A4)
+        r2 = oracle.gemm(x2[lo:hi].astype(np.float64),
+                         oracle.quantize(w2_keep[e].astype(np.float64)), oracle.A4)
+        if hi > lo:
+            bf16_gate(y1h[lo:hi], oracle.formats.bf16_round(r1))
+            bf16_gate(y2h[lo:hi], oracle.formats.bf16_round(r2))
+
+
+def test_gemm_deterministic():
+    rng = np.random.default_rng(400)
+    a = workloads.to_bf16_values(rng.standard_normal((300, 1024)).astype(np.float32))
+    w = (0.02 * rng.standard_normal((512, 1024))).astype(np.float32)
+    wq, ad = _wq(w), to_device_bf16(a)
+    for act in (16, 8, 4):
+        c1 = fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32)
+        c2 = fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32)
+        assert torch.equal(c1, c2)
+    g1 = fp4.gemm_w4aX(16, ad[:8], wq, out_dtype=torch.float32)
+    g2 = fp4.gemm_w4aX(16, ad[:8], wq, out_dtype=torch.float32)
+    assert torch.equal(g1, g2)
