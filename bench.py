@@ -1,0 +1,352 @@
+"""Benchmark of the block-FP4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-secondary] [--no-cpu-baseline]
+
+Flagship step: one W4A16 decode product (8 bf16 activation rows x a 14336 x 4096 weight
+matrix in two-level block FP4, bf16 output). Its throughput in GB/s of algorithmic
+traffic is ``value``. Weights are pre-quantized on the device and kept resident in HBM;
+the timed region rotates through 16 copies (over 512 MB) so the 256 MB Infinity Cache
+cannot hold the stream, and launches are replayed from a HIP graph.
+
+Also reported (same JSON line, "secondary"): the W4A4 prefill product (2048 x 4096 x
+4096, activations quantized on the device every step) in TFLOP/s, the 8-layer W4A4/W4A8
+policy stack, and the 128-expert top-8 mixture-of-experts grouped products, each with its
+roofline fraction; the oracle's CPU time on a bounded sample ("cpu_baseline").
+
+Rank 0 prints one JSON line. Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-FP4 W4A4 GEMM TFLOPS + decode GEMV GB/s, as fraction of roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0   # dense MFMA bf16/fp16
+FP4_PEAK_TFLOPS = 10100.0   # dense MFMA fp4 (not reachable with 16-element E4M3 scales)
+ROTATE = 16
+
+
+def algorithmic_bytes_gemv(m, n, k):
+    """Bytes the decode product must move: codes + micro + macro + A + C (bf16)."""
+    return n * k // 2 + n * k // 16 + n * (k // 256) * 2 + m * k * 2 + m * n * 2
+
+
+def algorithmic_bytes_gemm(m, n, k):
+    """Prefill product with dynamic activation quantization: read A (bf16) once, read
+    packed W once, write C (bf16)."""
+    return m * k * 2 + n * k // 2 + n * k // 16 + n * (k // 256) * 2 + m * n * 2
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "gemv": ["block_scaled_fp4_e2m1_amd/csrc/gemv.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
+    "gemm": ["block_scaled_fp4_e2m1_amd/csrc/gemm.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
+}
+
+
+def load_traffic(name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != source_hash(KERNEL_SOURCES[rec["kernel_group"]]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP-event timing on the stream the work is enqueued on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def region(self, fn, reps):
+        t = self.torch
+        s = t.cuda.current_stream()
+        t.cuda.synchronize()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3  # seconds
+
+
+def capture(torch, fns):
+    """A HIP graph replaying the given launches in order."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    return g
+
+
+def run_steps(torch, timer, graph, fns, steps):
+    """Exactly ``steps`` launches: whole graph replays plus an eager remainder."""
+    full, rest = divmod(steps, len(fns))
+
+    def body():
+        for _ in range(full):
+            graph.replay()
+        for f in fns[:rest]:
+            f()
+    return timer.region(body, 1)
+
+
+def bench_decode(torch, fp4, workloads, steps, warmup):
+    m, k, n = 8, 4096, 14336
+    a, w, _ = workloads.decode()
+    wq0 = fp4.quantize_fp4(torch.from_numpy(w).cuda(), layout=fp4.LAYOUT_TILED)
+    del w
+    copies = [wq0] + [fp4.QTensor(wq0.codes.clone(), wq0.micro.clone(), wq0.macro.clone(), n, k,
+                                  0, fp4.LAYOUT_TILED) for _ in range(ROTATE - 1)]
+    ad = torch.from_numpy(a).cuda().to(torch.bfloat16)
+    outs = [torch.empty(m, n, dtype=torch.bfloat16, device="cuda") for _ in range(ROTATE)]
+    fns = [(lambda q=q, o=o: fp4.gemm_w4aX(fp4.A16, ad, q, out=o)) for q, o in zip(copies, outs)]
+    for i in range(warmup):
+        fns[i % ROTATE]()
+    torch.cuda.synchronize()
+    g = capture(torch, fns)
+    g.replay()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    secs = run_steps(torch, timer, g, fns, steps)
+    per = secs / steps
+    nbytes = algorithmic_bytes_gemv(m, n, k)
+    torch.cuda.synchronize()
+    same = all(torch.equal(outs[0], o) for o in outs[1:])
+    return dict(m=m, n=n, k=k, seconds=secs, per_launch_s=per, bytes=nbytes,
+                gbs=nbytes / per / 1e9, flops=2 * m * n * k, outputs_identical=bool(same))
+
+
+def bench_prefill(torch, fp4, workloads, steps):
+    m, k, n = 2048, 4096, 4096
+    a, w, _ = workloads.prefill()
+    wq = fp4.quantize_fp4(torch.from_numpy(w).cuda(), layout=fp4.LAYOUT_TILED)
+    ad = torch.from_numpy(a).cuda().to(torch.bfloat16)
+    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(fp4.fp4_workspace_bytes(fp4.A4, m, n, k), dtype=torch.uint8, device="cuda")
+    fn = lambda: fp4.gemm_w4aX(fp4.A4, ad, wq, out=out, workspace=ws)
+    for _ in range(3):
+        fn()
+    g = capture(torch, [fn] * 4)
+    g.replay()
+    timer = Timer(torch)
+    secs = run_steps(torch, timer, g, [fn] * 4, steps)
+    per = secs / steps
+    flops = 2 * m * n * k
+    tfl = flops / per / 1e12
+    return dict(m=m, n=n, k=k, per_step_s=per, tflops=tfl,
+                frac_bf16_peak=tfl / BF16_PEAK_TFLOPS, frac_fp4_peak=tfl / FP4_PEAK_TFLOPS,
+                bytes=algorithmic_bytes_gemm(m, n, k))
+
+
+def bench_policy(torch, fp4, workloads, steps):
+    cfg = workloads.WORKLOADS["policy_stack"]
+    m, k, n = cfg["m"], cfg["k"], cfg["n"]
+    flags = workloads.policy_flags()
+    layers = []
+    for l in range(cfg["layers"]):
+        w, x = workloads.policy_layer(l)
+        act = fp4.fp4_policy_select(fp4.POLICY_AUTO, bool(flags[l]))
+        layers.append((act, fp4.quantize_fp4(torch.from_numpy(w).cuda(), layout=fp4.LAYOUT_TILED),
+                       torch.from_numpy(x).cuda().to(torch.bfloat16)))
+    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(fp4.fp4_workspace_bytes(fp4.A4, m, n, k), dtype=torch.uint8, device="cuda")
+    fns = [(lambda a=act, q=wq, x=x: fp4.gemm_w4aX(a, x, q, out=out, workspace=ws))
+           for act, wq, x in layers]
+    for f in fns:
+        f()
+    g = capture(torch, fns)
+    g.replay()
+    timer = Timer(torch)
+    secs = timer.region(g.replay, steps)
+    per = secs / steps
+    flops = 2 * m * n * k * len(fns)
+    # per precision: time one A4 and one A8 layer alone
+    a4 = next(f for f, (act, _, _) in zip(fns, layers) if act == fp4.A4)
+    a8 = next(f for f, (act, _, _) in zip(fns, layers) if act == fp4.A8)
+    t4 = timer.region(a4, 8) / 8
+    t8 = timer.region(a8, 8) / 8
+    tfl = flops / per / 1e12
+    return dict(layers=len(fns), flagged=[int(i) for i in np.nonzero(flags)[0]], per_step_s=per,
+                tflops=tfl, frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
+                layer_a4_s=t4, layer_a8_s=t8)
+
+
+def bench_moe(torch, fp4, workloads, steps):
+    cfg = workloads.WORKLOADS["moe_w4a4"]
+    E, H, I, T = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["tokens"]
+    _, row_token, offsets, _ = workloads.moe_routing()
+    R = int(offsets[-1])
+    w1q = fp4.empty_qtensor(E * 2 * I, H, layout=fp4.LAYOUT_TILED)
+    w2q = fp4.empty_qtensor(E * H, I, layout=fp4.LAYOUT_TILED)
+    for e in range(E):
+        w1, w2 = workloads.moe_expert_weights(e)
+        for wt, q in ((w1, w1q), (w2, w2q)):
+            rows, k = wt.shape
+            sub = fp4.QTensor(q.codes[e * rows * k // 2:(e + 1) * rows * k // 2],
+                              q.micro[e * rows * k // 16:(e + 1) * rows * k // 16],
+                              q.macro[e * rows * k // 256:(e + 1) * rows * k // 256],
+                              rows, k, 0, fp4.LAYOUT_TILED)
+            fp4.quantize_fp4(torch.from_numpy(wt).cuda(), layout=fp4.LAYOUT_TILED, out=sub)
+    xd = torch.from_numpy(workloads.moe_tokens()).cuda().to(torch.bfloat16)
+    x2 = torch.from_numpy(workloads.moe_down_inputs(R)).cuda().to(torch.bfloat16)
+    rt = torch.from_numpy(row_token).cuda()
+    off = torch.from_numpy(offsets).cuda()
+    y1 = torch.empty(R, 2 * I, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty(R, H, dtype=torch.bfloat16, device="cuda")
+    ws1 = torch.empty(fp4.fp4_workspace_bytes(fp4.A4, T, 2 * I, H), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(fp4.fp4_workspace_bytes(fp4.A4, R, H, I), dtype=torch.uint8, device="cuda")
+
+    def step():
+        fp4.grouped_gemm_w4aX(fp4.A4, xd, rt, off, E, R, w1q, out=y1, workspace=ws1)
+        fp4.grouped_gemm_w4aX(fp4.A4, x2, None, off, E, R, w2q, out=y2, workspace=ws2)
+    step()
+    g = capture(torch, [step])
+    g.replay()
+    timer = Timer(torch)
+    secs = timer.region(g.replay, steps)
+    per = secs / steps
+    flops = 2 * R * (2 * I) * H + 2 * R * H * I
+    tfl = flops / per / 1e12
+    counts = np.diff(offsets)
+    return dict(experts=E, top_k=cfg["top_k"], tokens=T, routed_rows=R, per_step_s=per, tflops=tfl,
+                frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
+                rows_per_expert=dict(min=int(counts.min()), max=int(counts.max()),
+                                     mean=float(counts.mean())))
+
+
+def cpu_baseline(workloads, budget_s=12.0):
+    """The oracle, as written, on a bounded sample of the decode workload: quantize rows of
+    W, dequantize, float64 product with the 8 activation rows; GB/s of the same
+    algorithmic traffic per processed weight row."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count() or 1
+    a, w, _ = workloads.decode()
+    m, k, n = 8, 4096, 14336
+    a64 = a.astype(np.float64)
+    rows_done, t0 = 0, time.perf_counter()
+    chunk = 512
+    t_quant = 0.0
+    while time.perf_counter() - t0 < budget_s and rows_done < n:
+        sl = w[rows_done:rows_done + chunk].astype(np.float64)
+        tq = time.perf_counter()
+        q = oracle.quantize(sl)
+        t_quant += time.perf_counter() - tq
+        _ = oracle.gemm(a64, q, oracle.A16)
+        rows_done += sl.shape[0]
+    secs = time.perf_counter() - t0
+    t_prod = secs - t_quant
+    frac = rows_done / n
+    nbytes = algorithmic_bytes_gemv(m, n, k) * frac
+    return {"value": nbytes / t_prod / 1e9, "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"decode W4A16 product on {rows_done} of {n} weight rows "
+                      f"(dequantize + float64 matmul {t_prod:.2f} s; the oracle's quantization "
+                      f"of those rows took {t_quant:.2f} s more); numpy elementwise work is "
+                      f"single-threaded, the float64 matmul uses {blas_threads} BLAS threads; "
+                      f"host has {os.cpu_count()} CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=320)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--skip-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe"], default=None,
+                    help="run one workload only (for profiling); prints its record")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_fp4_e2m1_amd as fp4
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if fp4.fp4_device_check() != 0:
+        print("device is not gfx950", file=sys.stderr)
+        sys.exit(1)
+
+    if args.only:
+        fn = {"decode": lambda: bench_decode(torch, fp4, workloads, args.steps, args.warmup),
+              "prefill": lambda: bench_prefill(torch, fp4, workloads, args.steps),
+              "policy": lambda: bench_policy(torch, fp4, workloads, args.steps),
+              "moe": lambda: bench_moe(torch, fp4, workloads, args.steps)}[args.only]
+        print(json.dumps({args.only: fn()}), flush=True)
+        return
+
+    dec = bench_decode(torch, fp4, workloads, args.steps, args.warmup)
+    print(f"# decode done: {dec['per_launch_s'] * 1e6:.2f} us/launch", file=sys.stderr, flush=True)
+    secondary = {}
+    if not args.skip_secondary:
+        secondary["prefill_w4a4"] = bench_prefill(torch, fp4, workloads, max(8, args.steps // 8))
+        print("# prefill done", file=sys.stderr, flush=True)
+        secondary["policy_stack"] = bench_policy(torch, fp4, workloads, max(4, args.steps // 32))
+        print("# policy done", file=sys.stderr, flush=True)
+        secondary["moe_w4a4"] = bench_moe(torch, fp4, workloads, max(4, args.steps // 32))
+        print("# moe done", file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(workloads)
+
+    traffic = load_traffic("gemv_decode_w4a16")
+    achieved = dec["gbs"]
+    rec = {
+        "metric": METRIC,
+        "value": round(dec["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["per_launch_s"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_w4a16: A bf16 [8 x 4096] . W^T, W two-level block FP4 "
+                               "[14336 x 4096] (E2M1, E4M3 per 16, FP16 per 256), C bf16",
+                   "m": 8, "k": 4096, "n": 14336, "weight_copies_rotated": ROTATE,
+                   "launch": "HIP graph replay"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dec["bytes"]},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,6 +22,20 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// s_waitcnt immediate that waits until at most N vector-memory operations are pending
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at "no wait").
+template <int N>
+struct kVmcntWait {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  static constexpr int value = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+};
+
+// Same, also waiting for every pending LDS / scalar-memory operation (lgkmcnt 0).
+template <int N>
+struct kVmcntLgkmWait {
+  static constexpr int value = kVmcntWait<N>::value & ~(15 << 8);
+};
+
 constexpr int kBlock = 16;    // elements per micro-scale
 constexpr int kGroup = 256;   // elements per macro-scale
 constexpr int kTileRows = 16;
@@ -79,6 +93,12 @@ __device__ __forceinline__ float fp16_value(uint32_t h) {
   const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
   float mag = e ? __uint_as_float(((e + 112u) << 23) | (m << 13)) : (float)m * 0x1p-24f;
   return (h & 0x8000u) ? -mag : mag;
+}
+
+// Same value through the hardware conversion (exact; FP16 denormals are kept in the
+// default floating-point mode). Branch-free, for the inner loops.
+__device__ __forceinline__ float fp16_value_hw(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
 // bfloat16 bits of a finite float32, round to nearest even.

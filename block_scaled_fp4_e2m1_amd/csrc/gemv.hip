@@ -13,8 +13,15 @@
 // just the E2M1 value (one hardware conversion per two codes, exact in bf16), so the
 // per-element work stays far below the bandwidth budget.
 //
-// Work split: a workgroup of KS waves owns RB 16-row blocks; wave w owns a contiguous run
-// of at most GPW 256-column groups; partial results meet in LDS.
+// Work split: a workgroup of RBW x KS waves owns RBW 16-row blocks over the whole of k;
+// wave (rb, ks) streams row block rb over its run of at most GPW 256-column groups,
+// issuing every weight load of that run before computing. The activations (m <= 8
+// rows) are copied once per workgroup into LDS by LDS-DMA loads (no registers), in
+// MFMA-fragment order, so a wave's operand read is 512 contiguous bytes. Operand lanes
+// outside their micro-block read from a small zero region instead (no branches). The
+// KS partial results of a row block meet in LDS. With k = 4096 one workgroup holds 8
+// waves and 76 KB of LDS, two fit on a CU, and the whole weight stream is requested in
+// a single round.
 #include "fp4_device.h"
 #include "fp4_kernels.h"
 
@@ -22,134 +29,155 @@ using namespace fp4dev;
 
 namespace {
 
-template <int RB, int GPW>
+constexpr int kMaxWaves = 16;  // waves per workgroup (row blocks x waves along k)
+constexpr int kMaxKS = 8;      // waves along k per row block
+constexpr int kZeroBytes = 4096;  // zero region: covers the per-group operand offsets
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+template <int GPW>
 struct GemvRegs {
-  uint4 code[GPW][RB][2];   // 64 codes per lane per tile
-  uint4 mu[GPW][RB][2];     // 32 micro-scales: rows 4q..4q+3, blocks of parity p
-  uint2 mac[GPW][RB];       // 4 macro-scales: rows 4q..4q+3
-  uint4 act[GPW][8];        // activation fragment per 32-column step
+  uint4 code[GPW][2];   // 64 codes per lane per tile
+  uint32_t mac[GPW];    // macro-scale of the lane's weight row (low 16 bits)
 };
 
-template <int RB, int GPW, int OUT_BF16>
-__global__ __launch_bounds__(1024) void k_gemv_bf16(const uint16_t* __restrict__ a, int64_t lda,
-                                                    int m, int64_t k,
-                                                    const uint8_t* __restrict__ codes,
-                                                    const uint8_t* __restrict__ micro,
-                                                    const uint16_t* __restrict__ macro,
-                                                    int64_t n, void* __restrict__ c, int64_t ldc) {
-  extern __shared__ float red[];  // [KS][RB*16][8]
-  const int ks = blockDim.x >> 6;
+// LDS: [A chunks: (k/8) x 8 rows x 16 B][zero region][micro-scale tiles: one 256-byte
+// slot per (wave, group); reused for float red[KS][RBW*16][8] at the end]
+template <int kRBW, int GPW, int OUT_BF16>
+__global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_bf16(  // <= 128 VGPRs
+    const uint16_t* __restrict__ a, int64_t lda, int m, int64_t k,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ micro,
+    const uint16_t* __restrict__ macro, int64_t n, void* __restrict__ c, int64_t ldc) {
+  extern __shared__ uint4 smem[];
+  const int nwaves = blockDim.x >> 6;
+  const int ks_count = nwaves / kRBW;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  const int rb = wave % kRBW, ks = wave / kRBW;
   const int q = lane >> 4;        // k-slot group of the operands, row quad of the output
-  const int col = lane & 15;      // output column = (activation row, micro-block parity)
-  const int mrow = col & 7, p = col >> 3;
+  const int l16 = lane & 15;      // weight row of the lane (operand and output column)
+  const int mrow = l16 & 7;       // activation row this lane feeds (operand row = p*8+m)
+  const int p_op = l16 >> 3;      // micro-block parity of the operand row this lane feeds
+  const int p = q >> 1;           // micro-block parity of this lane's output rows 4q..4q+3
   const int64_t groups = k >> 8;
   const int64_t nblocks = n >> 4;
-  const int64_t nb0 = (int64_t)blockIdx.x * RB;
-  const int64_t g0 = (int64_t)wave * GPW;
-  const bool act_lane = ((q >> 1) == p) && (mrow < m);
+  const int64_t nb = (int64_t)blockIdx.x * kRBW + rb;
+  const int64_t g0 = (int64_t)ks * GPW;
+  const bool act_lane = ((q >> 1) == p_op) && (mrow < m);
+  const int a_chunks = (int)(k >> 3) * 8;
+  uint4* zero = smem + a_chunks;
+  uint4* mu_lds = zero + kZeroBytes / 16;                 // [nwaves][GPW][256 B]
+  float* red = reinterpret_cast<float*>(mu_lds);
 
-  GemvRegs<RB, GPW> R;
-  // ---- issue every load of this wave first (weights stream, activations hit L2) ----
+  for (int i = threadIdx.x; i < kZeroBytes / 16; i += blockDim.x) zero[i] = make_uint4(0, 0, 0, 0);
+
+  // ---- activations: LDS-DMA copies, chunk (c8, row) -> smem[c8 * 8 + row] ----
+  // Each wave instruction fills 64 consecutive chunks; rows >= m copy row m-1 (those
+  // chunks are never read).
+  for (int s = wave; s < a_chunks / 64; s += nwaves) {
+    const int i = s * 64 + lane;
+    const int c8 = i >> 3, row = min(i & 7, m - 1);
+    __builtin_amdgcn_global_load_lds((global_void_ptr)(a + row * lda + (int64_t)c8 * 8),
+                                     (lds_void_ptr)(smem + s * 64), 16, 0, 0);
+  }
+
+  // ---- this wave's GPW tiles (consecutive in memory). A row block past the end (odd
+  // block count) re-reads the last one and is not stored, so every load is
+  // unconditional and every wait can be counted. Micro-scales go to LDS by DMA (one
+  // 256-byte tile per instruction) ahead of the code stream; codes and macro-scales go
+  // to registers. ----
+  const int64_t tile0 = min(nb, nblocks - 1) * groups + g0;
+  uint4* mu_wave = mu_lds + wave * GPW * (kTileMicroBytes / 16);
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi)
+    __builtin_amdgcn_global_load_lds(
+        (global_void_ptr)(micro + (tile0 + gi) * kTileMicroBytes + lane * 4),
+        (lds_void_ptr)(mu_wave + gi * (kTileMicroBytes / 16)), 4, 0, 0);
+  GemvRegs<GPW> R;
+  const uint4* cp = reinterpret_cast<const uint4*>(codes + tile0 * kTileCodeBytes) + lane;
+  const uint16_t* hp = macro + tile0 * kTileMacro + l16;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
-    const int64_t g = g0 + gi;
-    const bool gv = g < groups;
+    R.code[gi][0] = load_nt16(cp + gi * (kTileCodeBytes / 16));
+    R.code[gi][1] = load_nt16(cp + gi * (kTileCodeBytes / 16) + 64);
+    R.mac[gi] = hp[gi * kTileMacro];
+  }
+  // wait for this wave's LDS-DMA copies and zero-region writes only (issued first; the
+  // 3 * GPW code / macro loads may still be in flight), then a bare barrier: LDS is coherent
+  // inside the workgroup, and no global data needs ordering here.
+  // (sched_barrier keeps the weight loads above the wait: the count depends on it)
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<3 * GPW>::value);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // operand chunk of step t of local group gi: a_lane + gi * a_step + t * 32 chunks
+  const uint4* a_lane = act_lane ? smem + (g0 * 32 + q) * 8 + mrow : zero;
+  const int a_step = act_lane ? 32 * 8 : 0;
+
+  // ---- compute. Each MFMA step is pinned in order (decode, MFMA, micro-scale FMA) so
+  // the scheduler cannot front-load MFMAs and park their results; the activation
+  // fragment of the next step is read one step ahead. ----
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 a_next = a_lane[0];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const bool v = gv && (nb0 + r) < nblocks;
-      const int64_t tile = (nb0 + r) * groups + g;
-      if (v) {
-        const uint4* cp = reinterpret_cast<const uint4*>(codes + tile * kTileCodeBytes) + lane;
-        R.code[gi][r][0] = load_nt16(cp);
-        R.code[gi][r][1] = load_nt16(cp + 64);
-        const uint4* mp = reinterpret_cast<const uint4*>(micro + tile * kTileMicroBytes + p * 128 + q * 32);
-        R.mu[gi][r][0] = mp[0];
-        R.mu[gi][r][1] = mp[1];
-        R.mac[gi][r] = *reinterpret_cast<const uint2*>(macro + tile * kTileMacro + 4 * q);
-      } else {
-        R.code[gi][r][0] = R.code[gi][r][1] = make_uint4(0, 0, 0, 0);
-        R.mu[gi][r][0] = R.mu[gi][r][1] = make_uint4(0, 0, 0, 0);
-        R.mac[gi][r] = make_uint2(0, 0);
-      }
-    }
+  for (int gi = 0; gi < GPW; ++gi) {
+    const uint4* ag = a_lane + gi * a_step;
+    // micro-scales of the lane's weight row, blocks 2t+p (t = 0..7): 8 bytes
+    const uint2 mu8 = *reinterpret_cast<const uint2*>(
+        reinterpret_cast<const uint8_t*>(mu_wave + gi * (kTileMicroBytes / 16)) + p * 128 + l16 * 8);
+    float accg[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      if (gv && act_lane)
-        R.act[gi][t] = *reinterpret_cast<const uint4*>(a + mrow * lda + g * kGroup + 32 * t + 8 * q);
-      else
-        R.act[gi][t] = make_uint4(0, 0, 0, 0);
+      const uint4 a_cur = a_next;
+      if (t < 7) a_next = ag[(t + 1) * 32];
+      else if (gi + 1 < GPW) a_next = (ag + a_step)[0];
+      const uint4 cw4 = R.code[gi][t >> 2];
+      const uint32_t cw = (t & 3) == 0 ? cw4.x : (t & 3) == 1 ? cw4.y : (t & 3) == 2 ? cw4.z : cw4.w;
+      const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 0);
+      const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 1);
+      const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 2);
+      const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 3);
+      const bf16x8_t wf = {w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+      const float4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a_cur), wf,
+                                                                 zero4, 0, 0, 0);
+      const uint32_t mw = (t < 4) ? mu8.x : mu8.y;
+      float mu_f;
+      switch (t & 3) {
+        case 0: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 0); break;
+        case 1: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 1); break;
+        case 2: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 2); break;
+        default: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 3); break;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) accg[i] = fmaf(mu_f, d[i], accg[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    const float M = fp16_value_hw(R.mac[gi] & 0xFFFFu);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(M, accg[i], acc[i]);
   }
 
-  // ---- compute ----
-  float acc[RB][4];
+  // ---- fold the two micro-block columns, then the k-split waves, then store ----
+  // output rows 4q+i = (p, m = 4(q&1)+i); the two parities meet across lane ^ 32
 #pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[r][i] = 0.0f;
-
-  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      // micro-scales of rows 4q+i, block 2t+p, as float: mus[i][t]
-      float mus[4][8];
-      const uint32_t mw[8] = {R.mu[gi][r][0].x, R.mu[gi][r][0].y, R.mu[gi][r][0].z, R.mu[gi][r][0].w,
-                              R.mu[gi][r][1].x, R.mu[gi][r][1].y, R.mu[gi][r][1].z, R.mu[gi][r][1].w};
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)mw[d], false);
-        const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)mw[d], true);
-        mus[d >> 1][(d & 1) * 4 + 0] = lo[0];
-        mus[d >> 1][(d & 1) * 4 + 1] = lo[1];
-        mus[d >> 1][(d & 1) * 4 + 2] = hi[0];
-        mus[d >> 1][(d & 1) * 4 + 3] = hi[1];
-      }
-      float accg[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint4 cw4 = R.code[gi][r][t >> 2];
-        const uint32_t cw = (t & 3) == 0 ? cw4.x : (t & 3) == 1 ? cw4.y : (t & 3) == 2 ? cw4.z : cw4.w;
-        const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 0);
-        const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 1);
-        const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 2);
-        const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 3);
-        const bf16x8_t wf = {w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, R.act[gi][t]);
-        const float4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, af, zero, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) accg[i] = fmaf(mus[i][t], d[i], accg[i]);
-      }
-      const uint2 mc = R.mac[gi][r];
-      const float M[4] = {fp16_value(mc.x & 0xFFFFu), fp16_value(mc.x >> 16),
-                          fp16_value(mc.y & 0xFFFFu), fp16_value(mc.y >> 16)};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[r][i] = fmaf(M[i], accg[i], acc[r][i]);
-    }
-  }
-
-  // ---- fold the two micro-block columns, then the waves, then store ----
-#pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[r][i] += __shfl_xor(acc[r][i], 8);
+  for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], 32);
+  __syncthreads();  // every wave is done with its micro-scale slots (red reuses them)
   if (p == 0) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[(wave * RB * 16 + r * 16 + 4 * q + i) * 8 + mrow] = acc[r][i];
+    for (int i = 0; i < 4; ++i) red[((ks * kRBW + rb) * 16 + l16) * 8 + 4 * q + i] = acc[i];
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < RB * 16 * 8; o += blockDim.x) {
-    const int nl = o % (RB * 16), mm = o / (RB * 16);
+  for (int o = threadIdx.x; o < kRBW * 16 * 8; o += blockDim.x) {
+    const int nl = o % (kRBW * 16), mm = o / (kRBW * 16);
     if (mm >= m) continue;
-    const int64_t nn = nb0 * 16 + nl;
+    const int64_t nn = (int64_t)blockIdx.x * kRBW * 16 + nl;
     if (nn >= n) continue;
+    const int r = nl >> 4, row = nl & 15;
     float s = 0.0f;
-    for (int w = 0; w < ks; ++w) s += red[(w * RB * 16 + nl) * 8 + mm];
+    for (int w = 0; w < ks_count; ++w) s += red[((w * kRBW + r) * 16 + row) * 8 + mm];
     if (OUT_BF16)
       static_cast<uint16_t*>(c)[mm * ldc + nn] = (uint16_t)bf16_rne_bits(s);
     else
@@ -157,12 +185,11 @@ __global__ __launch_bounds__(1024) void k_gemv_bf16(const uint16_t* __restrict__
   }
 }
 
-constexpr int kRB = 1;
-
+// groups per wave: a divisor of the group count, at most 4 (register budget), with at
+// most kMaxKS waves along k; 0 when no such split exists
 int gemv_gpw(int64_t groups) {
-  // groups per wave so that at most 16 waves cover k
-  if (groups <= 16) return 1;
-  if (groups <= 32) return 2;
+  for (int gpw : {4, 2, 1})
+    if (groups % gpw == 0 && groups / gpw <= kMaxKS && (gpw == 1 || groups / gpw >= 2)) return gpw;
   return 0;
 }
 
@@ -171,7 +198,10 @@ int gemv_gpw(int64_t groups) {
 namespace fp4lib {
 
 bool gemv_supports(int64_t m, int64_t n, int64_t k) {
-  return m >= 1 && m <= 8 && (n % 16) == 0 && (k % 256) == 0 && gemv_gpw(k >> 8) > 0;
+  if (!(m >= 1 && m <= 8 && (n % 16) == 0 && (k % 256) == 0)) return false;
+  const int gpw = gemv_gpw(k >> 8);
+  if (gpw == 0) return false;
+  return true;
 }
 
 hipError_t launch_gemv_bf16(const uint16_t* a, int64_t lda, int64_t m, int64_t k,
@@ -182,15 +212,24 @@ hipError_t launch_gemv_bf16(const uint16_t* a, int64_t lda, int64_t m, int64_t k
   const int gpw = gemv_gpw(groups);
   const int ks = (int)((groups + gpw - 1) / gpw);
   const int64_t nblocks = n >> 4;
-  const dim3 grid((unsigned)((nblocks + kRB - 1) / kRB)), block(64 * ks);
-  const size_t lds = (size_t)ks * kRB * 16 * 8 * sizeof(float);
-#define FP4_GEMV(G, B) \
-  hipLaunchKernelGGL((k_gemv_bf16<kRB, G, B>), grid, block, lds, st, a, lda, (int)m, k, codes, micro, macro, n, c, ldc)
-  if (out_bf16) {
-    if (gpw == 1) FP4_GEMV(1, 1); else FP4_GEMV(2, 1);
-  } else {
-    if (gpw == 1) FP4_GEMV(1, 0); else FP4_GEMV(2, 0);
-  }
+  // row blocks per workgroup: as many as fit while keeping roughly a workgroup per CU
+  // (each workgroup copies all of A once, so fewer, wider workgroups move less)
+  int rbw = 1;
+  for (int r : {4, 2})
+    if (r * ks <= kMaxWaves && nblocks / r >= 200) { rbw = r; break; }
+  const dim3 grid((unsigned)((nblocks + rbw - 1) / rbw)), block(64 * rbw * ks);
+  const size_t mu_bytes = (size_t)ks * rbw * gpw * kTileMicroBytes;
+  const size_t red_bytes = (size_t)ks * rbw * 16 * 8 * sizeof(float);
+  const size_t lds = (size_t)k * 16 + kZeroBytes + (mu_bytes > red_bytes ? mu_bytes : red_bytes);
+#define FP4_GEMV(R, G, B) \
+  hipLaunchKernelGGL((k_gemv_bf16<R, G, B>), grid, block, lds, st, a, lda, (int)m, k, codes, micro, macro, n, c, ldc)
+#define FP4_GEMV_G(R, B) \
+  do { if (gpw == 1) FP4_GEMV(R, 1, B); else if (gpw == 2) FP4_GEMV(R, 2, B); else FP4_GEMV(R, 4, B); } while (0)
+#define FP4_GEMV_R(B) \
+  do { if (rbw == 4) FP4_GEMV_G(4, B); else if (rbw == 2) FP4_GEMV_G(2, B); else FP4_GEMV_G(1, B); } while (0)
+  if (out_bf16) FP4_GEMV_R(1); else FP4_GEMV_R(0);
+#undef FP4_GEMV_R
+#undef FP4_GEMV_G
 #undef FP4_GEMV
   return hipGetLastError();
 }
