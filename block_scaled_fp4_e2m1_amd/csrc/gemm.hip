@@ -28,7 +28,8 @@ using fp4lib::GemmArgs;
 
 namespace {
 
-constexpr int BM = 128, BN = 128;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
 
 template <int A_BF16>
 struct OpTraits;
@@ -80,7 +81,7 @@ struct OpTraits<1> {  // bf16 operands
 // counts (each lane sums a contiguous range of experts, then a 64-lane scan); the lane
 // whose range holds t finds the expert. Returns false past the last tile.
 __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_experts, int64_t t,
-                                 int& expert, int64_t& row_begin, int64_t& row_end) {
+                                 int& expert, int64_t& row_begin, int64_t& row_end, int BM) {
   __shared__ int s_expert;
   __shared__ int s_first;
   if (threadIdx.x == 0) s_expert = -1;
@@ -115,133 +116,222 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
   return true;
 }
 
+// ---------------------------------------------------------------------------------
+// Main product kernel. Workgroup: 4 waves side by side along n; tile 64 rows x 256
+// weight rows; each wave owns a 64 x 64 block as 4 x 4 MFMA tiles, so every weight
+// fragment is decoded by exactly one wave. The k loop runs in half-groups of 128:
+//   - activation tiles (64 x 128, 16 KB) are copied into LDS by LDS-DMA in MFMA-fragment
+//     order, double-buffered in two separate LDS objects (so the copy into one buffer
+//     never has to wait for reads of the other);
+//   - weight codes of the next half-group are prefetched into registers, micro-scales
+//     one group ahead;
+//   - the per-row activation factors and per-column macro-scales of every group are
+//     copied into LDS once, at the start.
+// Each 256-column group accumulates into fresh MFMA sums that are folded into the
+// running sums with one float32 multiply-add (factor sA * M_W) per output element.
+// ---------------------------------------------------------------------------------
+constexpr int kBM = 64;              // rows per workgroup
+constexpr int kBN = 256;             // weight rows (output columns) per workgroup
+constexpr int kHalf = 128;           // k per pipeline stage
+constexpr int kMaxGroupsLds = 64;    // k <= 16384 for the LDS factor tables
+constexpr int kAStage = kBM * kHalf * 2 / 16;  // 16-byte chunks per activation stage
+
+__shared__ uint4 g_abuf0[kAStage];
+__shared__ uint4 g_abuf1[kAStage];
+__shared__ float g_sa[kBM * kMaxGroupsLds];         // [row][group] activation factors
+__shared__ uint16_t g_mw[(kBN / 16) * kMaxGroupsLds * 16];  // tiled macro-scales of the tile
+
 template <int A_BF16, int C_BF16, int GROUPED>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs args) {
+__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs args) {
   typedef OpTraits<A_BF16> Op;
   typedef typename Op::frag frag;
-  const int64_t groups = args.k >> 8;
+  const int groups = (int)(args.k >> 8);
   const int64_t n = args.n;
-  const int64_t tiles_n = (n + BN - 1) / BN;
-  const int64_t tn = blockIdx.x % tiles_n;
-  const int64_t tm = blockIdx.x / tiles_n;
+  const int64_t nblocks = n >> 4;
+  const int tiles_n = (int)((n + kBN - 1) / kBN);
 
-  int64_t row_begin, row_end;
-  int64_t w_row_base = 0;  // first weight row of this product (expert offset)
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; give each XCD a
+  // contiguous run of tiles (n fastest) so its L2 keeps the same activation rows.
+  int bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  const int tn = bid % tiles_n;
+  const int tm = bid / tiles_n;
+
+  int64_t row_begin, row_end, w_row_base = 0;
   if (GROUPED) {
     int expert;
-    if (!find_expert_tile(args.expert_offsets, args.n_experts, tm, expert, row_begin, row_end))
+    if (!find_expert_tile(args.expert_offsets, args.n_experts, tm, expert, row_begin, row_end, kBM))
       return;
     w_row_base = (int64_t)expert * n;
   } else {
-    row_begin = tm * BM;
+    row_begin = (int64_t)tm * kBM;
     row_end = args.m;
+    if (row_begin >= row_end) return;
   }
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, l16 = lane & 15;
-  const int64_t m0 = row_begin + wm * 64;      // first routed row of this wave
-  const int64_t n0 = tn * BN + wn * 64;         // first output column of this wave
-  const int64_t nblocks = n >> 4;
+  const int64_t n0 = (int64_t)tn * kBN + wave * 64;  // first output column of this wave
+  const int64_t nb_tile0 = w_row_base / 16 + (int64_t)tn * (kBN / 16);  // first row block of the tile
 
-  // source rows of the A operand for this lane (operand row = l16 of each 16-row tile)
-  int64_t a_row[4];
-  bool a_ok[4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int64_t r = m0 + 16 * mi + l16;
-    a_ok[mi] = r < row_end;
-    int64_t src = r;
-    if (GROUPED && args.row_token && a_ok[mi]) src = args.row_token[r];
-    a_row[mi] = a_ok[mi] ? src : 0;
-  }
-  // source rows of the lane's output elements (for the activation factors)
-  int64_t o_src[4][4];
-  bool o_ok[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = m0 + 16 * mi + 4 * q + i;
-      o_ok[mi][i] = r < row_end;
-      int64_t src = r;
-      if (GROUPED && args.row_token && o_ok[mi][i]) src = args.row_token[r];
-      o_src[mi][i] = o_ok[mi][i] ? src : 0;
+  // ---- one-time tables: activation factors [row][g] and macro-scales of the tile ----
+  {
+    // activation factors: lane-wise DMA of 4-byte elements (row r, group g) -> g_sa[r*G+g]
+    const int elems = kBM * groups;
+    for (int e0 = wave * 64; e0 < elems; e0 += 256) {
+      const int e = min(e0 + lane, elems - 1);
+      const int r = e / groups, g = e - r * groups;
+      int64_t src_row = min(row_begin + r, row_end - 1);
+      if (GROUPED && args.row_token) src_row = args.row_token[src_row];
+      const float* src = args.a_scale ? args.a_scale + src_row * groups + g : nullptr;
+      if (src)
+        __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(g_sa + e0), 4, 0, 0);
     }
+    // macro-scales: the tile's 16 row blocks x G groups x 16 rows are contiguous
+    const int mw_elems = (kBN / 16) * groups * 16;       // uint16 count
+    const int64_t mw_first = nb_tile0 * groups * 16;
+    const int64_t mw_last = (w_row_base / 16 + nblocks) * groups * 16;  // exclusive bound
+    for (int c0 = wave * 64 * 2; c0 < mw_elems; c0 += 256 * 2) {  // 4-byte lanes = 2 entries
+      const int64_t src = min(mw_first + c0 + 2 * lane, mw_last - 2);
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(args.macro + src), (lds_void_ptr)(g_mw + c0), 4, 0, 0);
+    }
+  }
+
+  // ---- activation DMA: wave w copies row tile mi = w (16 rows) for the 4 steps of a stage ----
+  const uint16_t* a16 = static_cast<const uint16_t*>(args.a);
+  int64_t a_src_row = min(row_begin + wave * 16 + l16, row_end - 1);
+  if (GROUPED && args.row_token) a_src_row = args.row_token[a_src_row];
+  const uint16_t* a_lane_src = a16 + a_src_row * args.lda + 8 * q;
+  auto dma_stage = [&](uint4* buf, int stage) {  // stage = 2 g + h
+    const int64_t k0 = (int64_t)stage * kHalf;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(a_lane_src + k0 + 32 * t),
+                                       (lds_void_ptr)(buf + (wave * 4 + t) * 64), 16, 0, 0);
+  };
+
+  // ---- weights: 4 row blocks (16 columns each) per wave ----
+  int64_t wtile0[4];
   bool w_ok[4];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) w_ok[ni] = (n0 / 16 + ni) < nblocks;
+  for (int ni = 0; ni < 4; ++ni) {
+    const int64_t nb = n0 / 16 + ni;
+    w_ok[ni] = nb < nblocks;
+    wtile0[ni] = (w_row_base / 16 + min(nb, nblocks - 1)) * groups;
+  }
+  auto load_codes = [&](uint4 (&wc)[4], int stage) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      wc[ni] = *(reinterpret_cast<const uint4*>(args.codes + (wtile0[ni] + (stage >> 1)) * kTileCodeBytes +
+                                                (stage & 1) * 1024) + lane);
+  };
+  auto load_micro = [&](uint2 (&mu)[4], int g) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      mu[ni] = *reinterpret_cast<const uint2*>(args.micro + (wtile0[ni] + g) * kTileMicroBytes +
+                                               (q >> 1) * 128 + l16 * 8);
+  };
 
   float4_t acc[4][4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float4_t part[4][4];
 
-  const uint16_t* a16 = static_cast<const uint16_t*>(args.a);
+  uint4 wc0[4], wc1[4];   // codes of the current / next half-group
+  uint2 mu_cur[4], mu_nxt[4];
 
-  for (int64_t g = 0; g < groups; ++g) {
-    // weight fragments of this group: codes, micro-scales, macro-scale per column
-    uint4 wc[4][2];
-    uint2 wmu[4];
-    float wM[4];
+  // prologue: stage 0 in flight
+  dma_stage(g_abuf0, 0);
+  load_codes(wc0, 0);
+  load_micro(mu_cur, 0);
+
+  // one pipeline stage: 4 MFMA steps over the LDS buffer, weight codes wc, steps 4h..4h+3
+  auto compute_stage = [&](const uint4* buf, const uint4 (&wc)[4], const uint2 (&mu)[4], int h) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int64_t tile = (w_row_base / 16 + n0 / 16 + ni) * groups + g;
-      if (w_ok[ni]) {
-        const uint4* cp = reinterpret_cast<const uint4*>(args.codes + tile * kTileCodeBytes) + lane;
-        wc[ni][0] = cp[0];
-        wc[ni][1] = cp[64];
-        wmu[ni] = *reinterpret_cast<const uint2*>(args.micro + tile * kTileMicroBytes + (q >> 1) * 128 + l16 * 8);
-        wM[ni] = fp16_value(args.macro[tile * kTileMacro + l16]);
-      } else {
-        wc[ni][0] = wc[ni][1] = make_uint4(0, 0, 0, 0);
-        wmu[ni] = make_uint2(0, 0);
-        wM[ni] = 0.0f;
-      }
-    }
-    float4_t part[4][4];
+    for (int t = 0; t < 4; ++t) {
+      frag af[4], wf[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      frag af[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (a_ok[mi]) v = *reinterpret_cast<const uint4*>(a16 + a_row[mi] * args.lda + g * kGroup + 32 * t + 8 * q);
-        af[mi] = __builtin_bit_cast(frag, v);
-      }
-      frag wf[4];
+      for (int mi = 0; mi < 4; ++mi) af[mi] = __builtin_bit_cast(frag, buf[(mi * 4 + t) * 64 + lane]);
+      const int tt = h * 4 + t;  // step within the group: micro-block 2tt + (q >> 1)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
-        const uint4 c4 = wc[ni][t >> 2];
-        const uint32_t cw = (t & 3) == 0 ? c4.x : (t & 3) == 1 ? c4.y : (t & 3) == 2 ? c4.z : c4.w;
-        const uint32_t mw = (t < 4) ? wmu[ni].x : wmu[ni].y;
-        const float2_t mu2 = (t & 2) ? __builtin_amdgcn_cvt_pk_f32_fp8((int)mw, true)
-                                     : __builtin_amdgcn_cvt_pk_f32_fp8((int)mw, false);
-        wf[ni] = Op::weight(cw, (t & 1) ? mu2[1] : mu2[0]);
+        const uint32_t cw = t == 0 ? wc[ni].x : t == 1 ? wc[ni].y : t == 2 ? wc[ni].z : wc[ni].w;
+        const uint32_t mw = h == 0 ? mu[ni].x : mu[ni].y;
+        float mu_f;
+        switch (t) {
+          case 0: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 0); break;
+          case 1: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 1); break;
+          case 2: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 2); break;
+          default: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 3); break;
+        }
+        wf[ni] = Op::weight(cw, mu_f);
       }
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-          part[mi][ni] = Op::mfma(af[mi], wf[ni], t == 0 ? float4_t{0.0f, 0.0f, 0.0f, 0.0f} : part[mi][ni]);
+          part[mi][ni] = Op::mfma(af[mi], wf[ni], tt == 0 ? float4_t{0.0f, 0.0f, 0.0f, 0.0f} : part[mi][ni]);
+      __builtin_amdgcn_sched_barrier(0);  // one step's operands live at a time
     }
-    // fold this group's partial sums with its factors
+  };
+
+  // vm operations issued per stage by each wave (all counted by the waits below)
+  constexpr int kDmaPerStage = 4, kCodesPerStage = 4, kMicroPerGroup = 4;
+
+  for (int g = 0; g < groups; ++g) {
+    // ---------- first half of group g (buffer 0) ----------
+    dma_stage(g_abuf1, 2 * g + 1);
+    load_codes(wc1, 2 * g + 1);
+    // wait for stage 2g (issued one stage ago): the 8 operations just issued may pend
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kVmcntWait<kDmaPerStage + kCodesPerStage>::value);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage(g_abuf0, wc0, mu_cur, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();  // every wave is done reading buffer 0
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---------- second half of group g (buffer 1) ----------
+    const bool more = g + 1 < groups;
+    if (more) {
+      dma_stage(g_abuf0, 2 * g + 2);
+      load_codes(wc0, 2 * g + 2);
+      load_micro(mu_nxt, g + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kVmcntWait<kDmaPerStage + kCodesPerStage + kMicroPerGroup>::value);
+    } else {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
+    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage(g_abuf1, wc1, mu_cur, 1);
+
+    // ---------- fold group g ----------
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       float sa[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        sa[i] = (args.a_scale && o_ok[mi][i]) ? args.a_scale[o_src[mi][i] * groups + g] : 1.0f;
+        sa[i] = args.a_scale ? g_sa[(mi * 16 + 4 * q + i) * groups + g] : 1.0f;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < 4; ++ni) {
+        const float mw = fp16_value_hw(g_mw[((wave * 4 + ni) * groups + g) * 16 + l16]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[mi][ni][i] = fmaf(sa[i] * wM[ni], part[mi][ni][i], acc[mi][ni][i]);
+        for (int i = 0; i < 4; ++i) acc[mi][ni][i] = fmaf(sa[i] * mw, part[mi][ni][i], acc[mi][ni][i]);
+      }
     }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) mu_cur[ni] = mu_nxt[ni];
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();  // every wave is done reading buffer 1
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // store
+  // ---- store ----
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -250,8 +340,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs args) {
       const int64_t col = n0 + 16 * ni + l16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (!o_ok[mi][i]) continue;
-        const int64_t r = m0 + 16 * mi + 4 * q + i;
+        const int64_t r = row_begin + 16 * mi + 4 * q + i;
+        if (r >= row_end) continue;
         if (C_BF16)
           static_cast<uint16_t*>(args.c)[r * args.ldc + col] = (uint16_t)bf16_rne_bits(acc[mi][ni][i]);
         else
@@ -300,11 +390,14 @@ __global__ __launch_bounds__(256) void k_gemm_f32act(const float* __restrict__ a
 
 namespace fp4lib {
 
+bool gemm_supports(int64_t k) { return (k >> 8) <= kMaxGroupsLds; }
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
-  const int64_t tiles_n = (g.n + BN - 1) / BN;
+  if (!gemm_supports(g.k)) return hipErrorInvalidValue;
+  const int64_t tiles_n = (g.n + kBN - 1) / kBN;
   int64_t tiles_m;
-  if (g.expert_offsets) tiles_m = (g.m + BM - 1) / BM + g.n_experts;  // upper bound
-  else tiles_m = (g.m + BM - 1) / BM;
+  if (g.expert_offsets) tiles_m = (g.m + kBM - 1) / kBM + g.n_experts;  // upper bound
+  else tiles_m = (g.m + kBM - 1) / kBM;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(256);
