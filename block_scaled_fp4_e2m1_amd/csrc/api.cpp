@@ -44,9 +44,13 @@ fp4_status check_weights(const fp4_tensor* w) {
   return FP4_OK;
 }
 
+// Row stride (elements) of the FP16 activation workspace. Dense rows: padding the rows
+// (k + 64) measured slower with the product kernel's LDS-DMA operand copies.
+int64_t act_ws_stride(int64_t k) { return k; }
+
 size_t act_workspace(int32_t act, int64_t rows, int64_t k) {
   if (act == FP4_A16) return 0;
-  const size_t aq = ((size_t)rows * (size_t)k * 2 + 255) & ~(size_t)255;
+  const size_t aq = ((size_t)rows * (size_t)act_ws_stride(k) * 2 + 255) & ~(size_t)255;
   return aq + (size_t)rows * (size_t)(k / 256) * 4;
 }
 
@@ -61,15 +65,16 @@ fp4_status prepare_activations(int32_t act, const void* a, int32_t a_dtype, int6
     g.a_scale = nullptr;
     return FP4_OK;
   }
+  const int64_t ldq = act_ws_stride(k);
   _Float16* aq = static_cast<_Float16*>(ws);
   float* scale = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
-                                          (((size_t)rows * (size_t)k * 2 + 255) & ~(size_t)255));
+                                          (((size_t)rows * (size_t)ldq * 2 + 255) & ~(size_t)255));
   const hipError_t e = fp4lib::launch_act_prep(a, a_dtype == FP4_BF16, rows, k, lda,
-                                               act == FP4_A8, aq, scale, st);
+                                               act == FP4_A8, aq, ldq, scale, st);
   if (e != hipSuccess) return FP4_E_HIP;
   g.a = aq;
   g.a_is_bf16 = 0;
-  g.lda = k;
+  g.lda = ldq;
   g.a_scale = scale;
   return FP4_OK;
 }

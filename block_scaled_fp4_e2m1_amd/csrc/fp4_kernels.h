@@ -16,7 +16,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const u
 
 // Activation pass for the matrix kernels: aq[r, c] * scale[r, c/256] == A_hat[r, c].
 hipError_t launch_act_prep(const void* a, int in_bf16, int64_t rows, int64_t k, int64_t lda,
-                           int elem_e4m3, _Float16* aq, float* scale, hipStream_t st);
+                           int elem_e4m3, _Float16* aq, int64_t ldq, float* scale, hipStream_t st);
 
 // Decode product for m <= 8 bf16 activation rows against tiled E2M1 weights [n x k].
 // Returns hipErrorInvalidValue when the shape is outside what the kernel covers.

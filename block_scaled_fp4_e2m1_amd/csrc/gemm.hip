@@ -7,15 +7,15 @@
 // bf16 activations (sA = 1). The weight operand e2m1 * mu is exact in FP16 (at most 6
 // significant bits, range [2^-10, 2688]) and in bf16, so every MFMA product is exact and
 // only the float32 accumulation rounds. The per-256 factors cannot be folded into the
-// 16-bit operands exactly, so each 256-column group is accumulated separately and folded
-// into the running sums with one float32 multiply-add per output element per group.
+// 16-bit operands exactly; the running sums are instead kept in units of the current
+// group's factors and rescaled at each group boundary (see the kernel comment).
 //
-// Tiling: 256 threads = 2 x 2 waves, 64 x 64 outputs per wave as 4 x 4 tiles of
-// v_mfma_f32_16x16x32_{f16,bf16}; the workgroup covers 128 rows x 128 weight rows.
-// Weight fragments come straight from the tiled layout (each lane's 16-byte load is one
-// MFMA operand row); activation fragments are 16-byte row loads.
+// Tiling: 256 threads = 4 waves side by side along n, 64 x 64 outputs per wave as 4 x 4
+// tiles of v_mfma_f32_16x16x32_{f16,bf16}; the workgroup covers 64 rows x 256 weight rows.
+// Weight fragments come straight from the tiled layout (each lane's 16 bytes are one
+// MFMA operand row for four k-steps); activation fragments are 16-byte row pieces.
 //
-// Grouped form: the workgroup grid enumerates (expert, 128-row tile) pairs; each
+// Grouped form: the workgroup grid enumerates (expert, 64-row tile) pairs; each
 // workgroup finds its expert by a prefix sum over the per-expert tile counts, so one
 // launch covers every expert whatever the routing produced (including empty experts).
 // "llama.cpp Put Precision Policy Inside the Model", section "One model can need more
@@ -37,9 +37,13 @@ struct OpTraits;
 template <>
 struct OpTraits<0> {  // FP16 operands
   typedef half8_t frag;
-  __device__ static __forceinline__ frag weight(uint32_t cw, float mu) {
-    const _Float16 h = (_Float16)mu;  // E4M3 values are exact in FP16
-    const half2_t m2 = {h, h};
+  // micro-scale operand: the E4M3 byte shifted into the FP16 bit positions of both halves
+  // is mu * 2^-8 exactly (E4M3 subnormals land on FP16 subnormals); the 2^8 is folded
+  // into the column factor
+  static constexpr float kMicroUnit = 256.0f;
+  __device__ static __forceinline__ uint32_t micro_operand(uint32_t byte) { return (byte << 7) | (byte << 23); }
+  __device__ static __forceinline__ frag weight(uint32_t cw, uint32_t mu_op) {
+    const half2_t m2 = __builtin_bit_cast(half2_t, mu_op);
     const half2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * m2;
     const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * m2;
     const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * m2;
@@ -54,11 +58,17 @@ struct OpTraits<0> {  // FP16 operands
 template <>
 struct OpTraits<1> {  // bf16 operands
   typedef bf16x8_t frag;
+  // micro-scale operand: the E4M3 value as float32 bits
+  static constexpr float kMicroUnit = 1.0f;
+  __device__ static __forceinline__ uint32_t micro_operand(uint32_t byte) {
+    return __float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)byte, 0));
+  }
   __device__ static __forceinline__ uint32_t pack(float lo, float hi) {
     // both values are exact in bf16: take the high halves
     return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
   }
-  __device__ static __forceinline__ frag weight(uint32_t cw, float mu) {
+  __device__ static __forceinline__ frag weight(uint32_t cw, uint32_t mu_op) {
+    const float mu = __uint_as_float(mu_op);
     uint32_t w[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -119,36 +129,119 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 // ---------------------------------------------------------------------------------
 // Main product kernel. Workgroup: 4 waves side by side along n; tile 64 rows x 256
 // weight rows; each wave owns a 64 x 64 block as 4 x 4 MFMA tiles, so every weight
-// fragment is decoded by exactly one wave. The k loop runs in half-groups of 128:
-//   - activation tiles (64 x 128, 16 KB) are copied into LDS by LDS-DMA in MFMA-fragment
-//     order, double-buffered in two separate LDS objects (so the copy into one buffer
-//     never has to wait for reads of the other);
-//   - weight codes of the next half-group are prefetched into registers, micro-scales
-//     one group ahead;
-//   - the per-row activation factors and per-column macro-scales of every group are
-//     copied into LDS once, at the start.
-// Each 256-column group accumulates into fresh MFMA sums that are folded into the
-// running sums with one float32 multiply-add (factor sA * M_W) per output element.
+// fragment is decoded by exactly one wave. Sized for two workgroups per CU (two waves
+// per SIMD: at most 256 registers and ~80 KB of LDS each), which is what keeps the
+// matrix pipes busy.
+// The k loop runs in stages of half a 256-column group:
+//   - the activation tile (64 x 128, 16 KB, MFMA-fragment order) and the weight codes
+//     (4 waves x 4 row blocks x 1 KB, contiguous in the tiled layout) are copied into LDS
+//     by LDS-DMA, double-buffered in separate LDS objects, one stage ahead;
+//   - micro-scales of the next group are prefetched into registers;
+//   - per-row activation factors and the tile's macro-scales for every group are
+//     copied into LDS once, at the start (dynamic LDS, sized by the group count).
+// One barrier per stage: it both publishes stage s and frees the buffers of stage s-1
+// for the copies of stage s+1. Inside a stage, the weight decode and LDS reads of MFMA
+// step t+1 are interleaved 3 VALU : 1 MFMA with the 16 MFMAs of step t.
+// Per-group factors without separate partial sums: the running sum X is kept in units
+// of the current group's factor s_g = sA[row, g] * M_W[col, g]. At the start of group g
+// X is multiplied by s_{g-1} / s_g (a per-row ratio times a per-column ratio; a zero
+// factor counts as 1, its group contributes nothing), the group's MFMAs accumulate
+// straight into X, and the result is s_last * X. The extra float32 roundings are a few
+// units of 2^-24 per group. (On the FP16 path the weight operand carries mu * 2^-8, so
+// the column factor is 256 * M_W.)
 // ---------------------------------------------------------------------------------
 constexpr int kBM = 64;              // rows per workgroup
 constexpr int kBN = 256;             // weight rows (output columns) per workgroup
-constexpr int kHalf = 128;           // k per pipeline stage
-constexpr int kMaxGroupsLds = 64;    // k <= 16384 for the LDS factor tables
-constexpr int kAStage = kBM * kHalf * 2 / 16;  // 16-byte chunks per activation stage
+constexpr int kStageK = 128;         // k per pipeline stage
+constexpr int kAStage = kBM * kStageK * 2 / 16;  // 16-byte chunks: [mi 4][t 4][64]
+constexpr int kWStage = kBN * kStageK / 2 / 16;  // 16-byte chunks: [wave 4][ni 4][64]
 
-__shared__ uint4 g_abuf0[kAStage];
-__shared__ uint4 g_abuf1[kAStage];
-__shared__ float g_sa[kBM * kMaxGroupsLds];         // [row][group] activation factors
-__shared__ uint16_t g_mw[(kBN / 16) * kMaxGroupsLds * 16];  // tiled macro-scales of the tile
+__shared__ uint4 g_a0[kAStage];
+__shared__ uint4 g_a1[kAStage];
+__shared__ uint4 g_w0[kWStage];
+__shared__ uint4 g_w1[kWStage];
 
-template <int A_BF16, int C_BF16, int GROUPED>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs args) {
+// dynamic LDS: float sa[G][64] then uint16 mw[16][G][16]
+size_t gemm_dynamic_lds(int groups) { return (size_t)groups * kBM * 4 + (size_t)(kBN / 16) * groups * 16 * 2; }
+
+template <int A_BF16>
+struct StepOperands {
+  typedef typename OpTraits<A_BF16>::frag frag;
+  frag af[4], wf[4];
+};
+
+// operands of step T (0..3) of a stage: activation fragments from LDS, weight fragments
+// decoded from the stage's code words (dword T of the lane's 16 bytes per row block)
+// with micro-scale byte (4h+T)
+template <int A_BF16, int T>
+__device__ __forceinline__ void stage_operands(const uint4* abuf, const uint4 (&cw)[4],
+                                               int lane, const uint2 (&mu)[4], int h,
+                                               StepOperands<A_BF16>& o) {
   typedef OpTraits<A_BF16> Op;
   typedef typename Op::frag frag;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) o.af[mi] = __builtin_bit_cast(frag, abuf[(mi * 4 + T) * 64 + lane]);
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const uint32_t c = T == 0 ? cw[ni].x : T == 1 ? cw[ni].y : T == 2 ? cw[ni].z : cw[ni].w;
+    const uint32_t mw = h == 0 ? mu[ni].x : mu[ni].y;
+    o.wf[ni] = Op::weight(c, Op::micro_operand((mw >> (8 * T)) & 0xFFu));
+  }
+}
+
+template <int A_BF16, int T>
+__device__ __forceinline__ void stage_mfma(const StepOperands<A_BF16>& o, float4_t (&x)[4][4]) {
+  typedef OpTraits<A_BF16> Op;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
+}
+
+// 1 MFMA : 3 VALU interleave for the 16 MFMAs of a step
+__device__ __forceinline__ void interleave_step() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+  }
+}
+
+template <int A_BF16>
+__device__ __forceinline__ void compute_stage(const uint4* abuf, const uint4* wbuf, int wave, int lane,
+                                              const uint2 (&mu)[4], int h, float4_t (&x)[4][4]) {
+  // the lane's 16 bytes of code words per row block (one conflict-free 128-bit read each)
+  uint4 cw[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) cw[ni] = wbuf[(wave * 4 + ni) * 64 + lane];
+  StepOperands<A_BF16> o0, o1;
+  stage_operands<A_BF16, 0>(abuf, cw, lane, mu, h, o0);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_mfma<A_BF16, 0>(o0, x);
+  stage_operands<A_BF16, 1>(abuf, cw, lane, mu, h, o1);
+  interleave_step();
+  __builtin_amdgcn_sched_barrier(0);
+  stage_mfma<A_BF16, 1>(o1, x);
+  stage_operands<A_BF16, 2>(abuf, cw, lane, mu, h, o0);
+  interleave_step();
+  __builtin_amdgcn_sched_barrier(0);
+  stage_mfma<A_BF16, 2>(o0, x);
+  stage_operands<A_BF16, 3>(abuf, cw, lane, mu, h, o1);
+  interleave_step();
+  __builtin_amdgcn_sched_barrier(0);
+  stage_mfma<A_BF16, 3>(o1, x);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int A_BF16, int C_BF16, int GROUPED>
+__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
+  extern __shared__ uint8_t g_dyn[];
   const int groups = (int)(args.k >> 8);
   const int64_t n = args.n;
   const int64_t nblocks = n >> 4;
   const int tiles_n = (int)((n + kBN - 1) / kBN);
+  float* g_sa = reinterpret_cast<float*>(g_dyn);                               // [g][64]
+  uint16_t* g_mw = reinterpret_cast<uint16_t*>(g_dyn + (size_t)groups * kBM * 4);  // [16][g][16]
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; give each XCD a
   // contiguous run of tiles (n fastest) so its L2 keeps the same activation rows.
@@ -174,21 +267,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs args) {
   const int64_t n0 = (int64_t)tn * kBN + wave * 64;  // first output column of this wave
   const int64_t nb_tile0 = w_row_base / 16 + (int64_t)tn * (kBN / 16);  // first row block of the tile
 
-  // ---- one-time tables: activation factors [row][g] and macro-scales of the tile ----
+  // ---- one-time tables: activation factors [g][row] and the tile's macro-scales ----
+  if (!A_BF16) {  // the FP16 operand path always carries activation factors
+    int64_t src_row = min(row_begin + lane, row_end - 1);  // lane = row of the tile
+    if (GROUPED && args.row_token) src_row = args.row_token[src_row];
+    for (int g = wave; g < groups; g += 4)  // one 64-row column of factors per DMA
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(args.a_scale + src_row * groups + g),
+                                       (lds_void_ptr)(g_sa + g * kBM), 4, 0, 0);
+  }
   {
-    // activation factors: lane-wise DMA of 4-byte elements (row r, group g) -> g_sa[r*G+g]
-    const int elems = kBM * groups;
-    for (int e0 = wave * 64; e0 < elems; e0 += 256) {
-      const int e = min(e0 + lane, elems - 1);
-      const int r = e / groups, g = e - r * groups;
-      int64_t src_row = min(row_begin + r, row_end - 1);
-      if (GROUPED && args.row_token) src_row = args.row_token[src_row];
-      const float* src = args.a_scale ? args.a_scale + src_row * groups + g : nullptr;
-      if (src)
-        __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(g_sa + e0), 4, 0, 0);
-    }
-    // macro-scales: the tile's 16 row blocks x G groups x 16 rows are contiguous
-    const int mw_elems = (kBN / 16) * groups * 16;       // uint16 count
+    // the tile's 16 row blocks x G groups x 16 rows of macro-scales are contiguous
+    const int mw_elems = (kBN / 16) * groups * 16;  // uint16 count
     const int64_t mw_first = nb_tile0 * groups * 16;
     const int64_t mw_last = (w_row_base / 16 + nblocks) * groups * 16;  // exclusive bound
     for (int c0 = wave * 64 * 2; c0 < mw_elems; c0 += 256 * 2) {  // 4-byte lanes = 2 entries
@@ -197,18 +286,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs args) {
     }
   }
 
-  // ---- activation DMA: wave w copies row tile mi = w (16 rows) for the 4 steps of a stage ----
+  // ---- activation copies: wave w moves row tile mi = w (16 rows), 4 steps per stage ----
   const uint16_t* a16 = static_cast<const uint16_t*>(args.a);
   int64_t a_src_row = min(row_begin + wave * 16 + l16, row_end - 1);
   if (GROUPED && args.row_token) a_src_row = args.row_token[a_src_row];
   const uint16_t* a_lane_src = a16 + a_src_row * args.lda + 8 * q;
-  auto dma_stage = [&](uint4* buf, int stage) {  // stage = 2 g + h
-    const int64_t k0 = (int64_t)stage * kHalf;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      __builtin_amdgcn_global_load_lds((global_void_ptr)(a_lane_src + k0 + 32 * t),
-                                       (lds_void_ptr)(buf + (wave * 4 + t) * 64), 16, 0, 0);
-  };
 
   // ---- weights: 4 row blocks (16 columns each) per wave ----
   int64_t wtile0[4];
@@ -219,11 +301,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs args) {
     w_ok[ni] = nb < nblocks;
     wtile0[ni] = (w_row_base / 16 + min(nb, nblocks - 1)) * groups;
   }
-  auto load_codes = [&](uint4 (&wc)[4], int stage) {
+  auto copy_stage = [&](uint4* abuf, uint4* wbuf, int s) {  // stage s = 2 g + h
+    const int g = s >> 1, h = s & 1;
+    const int64_t k0 = (int64_t)s * kStageK;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(a_lane_src + k0 + 32 * t),
+                                       (lds_void_ptr)(abuf + (wave * 4 + t) * 64), 16, 0, 0);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
-      wc[ni] = *(reinterpret_cast<const uint4*>(args.codes + (wtile0[ni] + (stage >> 1)) * kTileCodeBytes +
-                                                (stage & 1) * 1024) + lane);
+      __builtin_amdgcn_global_load_lds(
+          (global_void_ptr)(args.codes + (wtile0[ni] + g) * kTileCodeBytes + h * 1024 + lane * 16),
+          (lds_void_ptr)(wbuf + (wave * 4 + ni) * 64), 16, 0, 0);
   };
   auto load_micro = [&](uint2 (&mu)[4], int g) {
 #pragma unroll
@@ -232,108 +321,80 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs args) {
                                                (q >> 1) * 128 + l16 * 8);
   };
 
-  float4_t acc[4][4];
+  float4_t x[4][4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float4_t part[4][4];
+    for (int ni = 0; ni < 4; ++ni) x[mi][ni] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  uint4 wc0[4], wc1[4];   // codes of the current / next half-group
-  uint2 mu_cur[4], mu_nxt[4];
-
-  // prologue: stage 0 in flight
-  dma_stage(g_abuf0, 0);
-  load_codes(wc0, 0);
-  load_micro(mu_cur, 0);
-
-  // one pipeline stage: 4 MFMA steps over the LDS buffer, weight codes wc, steps 4h..4h+3
-  auto compute_stage = [&](const uint4* buf, const uint4 (&wc)[4], const uint2 (&mu)[4], int h) {
+  const float* sa_lane = g_sa + 4 * q;                               // + g*64 + mi*16: rows 4q..4q+3
+  const uint16_t* mw_lane = g_mw + (wave * 4) * groups * 16 + l16;    // + (ni*G + g)*16
+  // factors of group g (a zero factor counts as 1)
+  auto col_factor = [&](int ni, int g) {
+    const float v = fp16_value_hw(mw_lane[(ni * groups + g) * 16]);
+    return v != 0.0f ? v * OpTraits<A_BF16>::kMicroUnit : 1.0f;
+  };
+  auto row_factors = [&](int mi, int g) {
+    float4 v = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+    if (!A_BF16) {
+      v = *reinterpret_cast<const float4*>(sa_lane + g * kBM + mi * 16);
+      v.x = v.x != 0.0f ? v.x : 1.0f;
+      v.y = v.y != 0.0f ? v.y : 1.0f;
+      v.z = v.z != 0.0f ? v.z : 1.0f;
+      v.w = v.w != 0.0f ? v.w : 1.0f;
+    }
+    return v;
+  };
+  // X *= s_{g-1} / s_g before group g's MFMAs
+  auto rescale = [&](int g) {
+    float rw[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      frag af[4], wf[4];
+    for (int ni = 0; ni < 4; ++ni) rw[ni] = col_factor(ni, g - 1) * __builtin_amdgcn_rcpf(col_factor(ni, g));
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) af[mi] = __builtin_bit_cast(frag, buf[(mi * 4 + t) * 64 + lane]);
-      const int tt = h * 4 + t;  // step within the group: micro-block 2tt + (q >> 1)
+    for (int mi = 0; mi < 4; ++mi) {
+      const float4 p = row_factors(mi, g - 1), c = row_factors(mi, g);
+      const float ra[4] = {p.x * __builtin_amdgcn_rcpf(c.x), p.y * __builtin_amdgcn_rcpf(c.y),
+                           p.z * __builtin_amdgcn_rcpf(c.z), p.w * __builtin_amdgcn_rcpf(c.w)};
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const uint32_t cw = t == 0 ? wc[ni].x : t == 1 ? wc[ni].y : t == 2 ? wc[ni].z : wc[ni].w;
-        const uint32_t mw = h == 0 ? mu[ni].x : mu[ni].y;
-        float mu_f;
-        switch (t) {
-          case 0: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 0); break;
-          case 1: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 1); break;
-          case 2: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 2); break;
-          default: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 3); break;
-        }
-        wf[ni] = Op::weight(cw, mu_f);
-      }
+      for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          part[mi][ni] = Op::mfma(af[mi], wf[ni], tt == 0 ? float4_t{0.0f, 0.0f, 0.0f, 0.0f} : part[mi][ni]);
-      __builtin_amdgcn_sched_barrier(0);  // one step's operands live at a time
+        for (int i = 0; i < 4; ++i) x[mi][ni][i] = x[mi][ni][i] * ra[i] * rw[ni];
     }
   };
 
-  // vm operations issued per stage by each wave (all counted by the waits below)
-  constexpr int kDmaPerStage = 4, kCodesPerStage = 4, kMicroPerGroup = 4;
+  uint2 mu_cur[4], mu_nxt[4];
+  const int stages = 2 * groups;
+  copy_stage(g_a0, g_w0, 0);
+  load_micro(mu_cur, 0);
 
-  for (int g = 0; g < groups; ++g) {
-    // ---------- first half of group g (buffer 0) ----------
-    dma_stage(g_abuf1, 2 * g + 1);
-    load_codes(wc1, 2 * g + 1);
-    // wait for stage 2g (issued one stage ago): the 8 operations just issued may pend
+  // stage s in buffers (s & 1): the barrier publishes it and frees the other buffers,
+  // which then receive stage s + 1 while stage s computes
+  auto run_stage = [&](const uint4* abuf, const uint4* wbuf, uint4* nabuf, uint4* nwbuf, int s) {
+    __syncthreads();
+    if (s + 1 < stages) copy_stage(nabuf, nwbuf, s + 1);
+    const int h = s & 1;
+    if (h == 0 && s + 2 < stages) load_micro(mu_nxt, (s >> 1) + 1);
+    if (h == 0 && s > 0) rescale(s >> 1);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kVmcntWait<kDmaPerStage + kCodesPerStage>::value);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    compute_stage(g_abuf0, wc0, mu_cur, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();  // every wave is done reading buffer 0
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---------- second half of group g (buffer 1) ----------
-    const bool more = g + 1 < groups;
-    if (more) {
-      dma_stage(g_abuf0, 2 * g + 2);
-      load_codes(wc0, 2 * g + 2);
-      load_micro(mu_nxt, g + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(kVmcntWait<kDmaPerStage + kCodesPerStage + kMicroPerGroup>::value);
-    } else {
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
+    compute_stage<A_BF16>(abuf, wbuf, wave, lane, mu_cur, h, x);
+    if (h == 1) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) mu_cur[ni] = mu_nxt[ni];
     }
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    compute_stage(g_abuf1, wc1, mu_cur, 1);
-
-    // ---------- fold group g ----------
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      float sa[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sa[i] = args.a_scale ? g_sa[(mi * 16 + 4 * q + i) * groups + g] : 1.0f;
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const float mw = fp16_value_hw(g_mw[((wave * 4 + ni) * groups + g) * 16 + l16]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mi][ni][i] = fmaf(sa[i] * mw, part[mi][ni][i], acc[mi][ni][i]);
-      }
-    }
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) mu_cur[ni] = mu_nxt[ni];
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();  // every wave is done reading buffer 1
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int s = 0; s < stages; s += 2) {
+    run_stage(g_a0, g_w0, g_a1, g_w1, s);
+    run_stage(g_a1, g_w1, g_a0, g_w0, s + 1);
   }
 
-  // ---- store ----
+  // ---- result = s_last * X, store ----
+  float cf[4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int ni = 0; ni < 4; ++ni) cf[ni] = col_factor(ni, groups - 1);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const float4 rf4 = row_factors(mi, groups - 1);
+    const float rf[4] = {rf4.x, rf4.y, rf4.z, rf4.w};
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       if (!w_ok[ni]) continue;
@@ -342,12 +403,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs args) {
       for (int i = 0; i < 4; ++i) {
         const int64_t r = row_begin + 16 * mi + 4 * q + i;
         if (r >= row_end) continue;
+        const float v = x[mi][ni][i] * rf[i] * cf[ni];
         if (C_BF16)
-          static_cast<uint16_t*>(args.c)[r * args.ldc + col] = (uint16_t)bf16_rne_bits(acc[mi][ni][i]);
+          static_cast<uint16_t*>(args.c)[r * args.ldc + col] = (uint16_t)bf16_rne_bits(v);
         else
-          static_cast<float*>(args.c)[r * args.ldc + col] = acc[mi][ni][i];
+          static_cast<float*>(args.c)[r * args.ldc + col] = v;
       }
     }
+  }
 }
 
 // float32 activations: one thread per output, exact weight values, float32 FMA.
@@ -390,7 +453,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32act(const float* __restrict__ a
 
 namespace fp4lib {
 
-bool gemm_supports(int64_t k) { return (k >> 8) <= kMaxGroupsLds; }
+bool gemm_supports(int64_t k) { return gemm_dynamic_lds((int)(k >> 8)) <= 64 * 1024; }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (!gemm_supports(g.k)) return hipErrorInvalidValue;
@@ -401,7 +464,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(256);
-#define FP4_GEMM(A, C, G) hipLaunchKernelGGL((k_gemm<A, C, G>), grid, block, 0, st, g)
+  const size_t lds = gemm_dynamic_lds((int)(g.k >> 8));
+#define FP4_GEMM(A, C, G) hipLaunchKernelGGL((k_gemm<A, C, G>), grid, block, lds, st, g)
   const int grouped = g.expert_offsets != nullptr;
   if (g.a_is_bf16) {
     if (g.c_is_bf16) { if (grouped) FP4_GEMM(1, 1, 1); else FP4_GEMM(1, 1, 0); }

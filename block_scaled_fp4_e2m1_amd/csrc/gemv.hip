@@ -212,11 +212,10 @@ hipError_t launch_gemv_bf16(const uint16_t* a, int64_t lda, int64_t m, int64_t k
   const int gpw = gemv_gpw(groups);
   const int ks = (int)((groups + gpw - 1) / gpw);
   const int64_t nblocks = n >> 4;
-  // row blocks per workgroup: as many as fit while keeping roughly a workgroup per CU
-  // (each workgroup copies all of A once, so fewer, wider workgroups move less)
-  int rbw = 1;
-  for (int r : {4, 2})
-    if (r * ks <= kMaxWaves && nblocks / r >= 200) { rbw = r; break; }
+  // row blocks per workgroup: two when that still leaves at least a workgroup per CU
+  // (each workgroup copies all of A once, so wider workgroups move less; four per
+  // workgroup measured slower than two on the 14336-row decode shape)
+  const int rbw = (2 * ks <= kMaxWaves && nblocks / 2 >= 256) ? 2 : 1;
   const dim3 grid((unsigned)((nblocks + rbw - 1) / rbw)), block(64 * rbw * ks);
   const size_t mu_bytes = (size_t)ks * rbw * gpw * kTileMicroBytes;
   const size_t red_bytes = (size_t)ks * rbw * 16 * 8 * sizeof(float);
@@ -226,7 +225,7 @@ hipError_t launch_gemv_bf16(const uint16_t* a, int64_t lda, int64_t m, int64_t k
 #define FP4_GEMV_G(R, B) \
   do { if (gpw == 1) FP4_GEMV(R, 1, B); else if (gpw == 2) FP4_GEMV(R, 2, B); else FP4_GEMV(R, 4, B); } while (0)
 #define FP4_GEMV_R(B) \
-  do { if (rbw == 4) FP4_GEMV_G(4, B); else if (rbw == 2) FP4_GEMV_G(2, B); else FP4_GEMV_G(1, B); } while (0)
+  do { if (rbw == 2) FP4_GEMV_G(2, B); else FP4_GEMV_G(1, B); } while (0)
   if (out_bf16) FP4_GEMV_R(1); else FP4_GEMV_R(0);
 #undef FP4_GEMV_R
 #undef FP4_GEMV_G

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 template <int IN_BF16, int ELEM_E4M3>
 __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, int64_t lda,
                                                   int64_t rows, int64_t k,
-                                                  _Float16* __restrict__ aq,
+                                                  _Float16* __restrict__ aq, int64_t ldq,
                                                   float* __restrict__ scale) {
   const int64_t groups = k >> 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, in
   pk.y = __builtin_bit_cast(uint32_t, out[1]);
   pk.z = __builtin_bit_cast(uint32_t, out[2]);
   pk.w = __builtin_bit_cast(uint32_t, out[3]);
-  *reinterpret_cast<uint4*>(aq + r * k + col) = pk;
+  *reinterpret_cast<uint4*>(aq + r * ldq + col) = pk;
   if (li == 0) scale[r * groups + g] = ELEM_E4M3 ? m_val * 8.0f : m_val;
 }
 
@@ -246,14 +246,14 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const u
 }
 
 hipError_t launch_act_prep(const void* a, int in_bf16, int64_t rows, int64_t k, int64_t lda,
-                           int elem_e4m3, _Float16* aq, float* scale, hipStream_t st) {
+                           int elem_e4m3, _Float16* aq, int64_t ldq, float* scale, hipStream_t st) {
   const dim3 grid(blocks_for(rows, k)), block(256);
   if (in_bf16) {
-    if (elem_e4m3) hipLaunchKernelGGL((k_act_prep<1, 1>), grid, block, 0, st, a, lda, rows, k, aq, scale);
-    else hipLaunchKernelGGL((k_act_prep<1, 0>), grid, block, 0, st, a, lda, rows, k, aq, scale);
+    if (elem_e4m3) hipLaunchKernelGGL((k_act_prep<1, 1>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
+    else hipLaunchKernelGGL((k_act_prep<1, 0>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
   } else {
-    if (elem_e4m3) hipLaunchKernelGGL((k_act_prep<0, 1>), grid, block, 0, st, a, lda, rows, k, aq, scale);
-    else hipLaunchKernelGGL((k_act_prep<0, 0>), grid, block, 0, st, a, lda, rows, k, aq, scale);
+    if (elem_e4m3) hipLaunchKernelGGL((k_act_prep<0, 1>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
+    else hipLaunchKernelGGL((k_act_prep<0, 0>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
   }
   return hipGetLastError();
 }
