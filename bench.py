@@ -134,10 +134,21 @@ def bench_decode(torch, fp4, workloads, steps, warmup):
     secs = run_steps(torch, timer, g, fns, steps)
     per = secs / steps
     nbytes = algorithmic_bytes_gemv(m, n, k)
+    # spread: per-launch average of each graph replay (16 launches), separate pass
+    reps = []
+    s_ = torch.cuda.current_stream()
+    for _ in range(max(8, steps // ROTATE)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s_)
+        g.replay()
+        e1.record(s_)
+        reps.append((e0, e1))
     torch.cuda.synchronize()
+    per_rep = np.array([a.elapsed_time(b) * 1e3 / ROTATE for a, b in reps])
     same = all(torch.equal(outs[0], o) for o in outs[1:])
     return dict(m=m, n=n, k=k, seconds=secs, per_launch_s=per, bytes=nbytes,
-                gbs=nbytes / per / 1e9, flops=2 * m * n * k, outputs_identical=bool(same))
+                gbs=nbytes / per / 1e9, flops=2 * m * n * k, outputs_identical=bool(same),
+                launch_us_p10_p50_p90=[round(float(np.percentile(per_rep, q)), 3) for q in (10, 50, 90)])
 
 
 def bench_prefill(torch, fp4, workloads, steps):
@@ -160,6 +171,109 @@ def bench_prefill(torch, fp4, workloads, steps):
     return dict(m=m, n=n, k=k, per_step_s=per, tflops=tfl,
                 frac_bf16_peak=tfl / BF16_PEAK_TFLOPS, frac_fp4_peak=tfl / FP4_PEAK_TFLOPS,
                 bytes=algorithmic_bytes_gemm(m, n, k))
+
+
+def bench_quantize(torch, fp4, workloads, steps):
+    """quantize_fp4 on its two hot uses: the decode weights (float32 [14336 x 4096] to the
+    tiled E2M1 layout, done once per model load) and the prefill activations (bf16
+    [2048 x 4096] to canonical E2M1). HBM-bound; GB/s of input + codes + scales."""
+    out = {}
+    _, w, _ = workloads.decode()
+    wd = [torch.from_numpy(w).cuda()]
+    wd.append(wd[0].clone())  # two copies (470 MB) so the Infinity Cache cannot hold the input
+    del w
+    n, k = wd[0].shape
+    qs = [fp4.empty_qtensor(n, k, layout=fp4.LAYOUT_TILED) for _ in wd]
+    fns = [(lambda x=x, q=q: fp4.quantize_fp4(x, layout=fp4.LAYOUT_TILED, out=q)) for x, q in zip(wd, qs)]
+    for f in fns:
+        f()
+    timer = Timer(torch)
+    reps = max(4, steps // 16)
+    secs = timer.region(lambda: [f() for f in fns], reps) / (reps * len(fns))
+    nbytes = n * k * 4 + n * k // 2 + n * k // 16 + n * (k // 256) * 2
+    out["weights_f32_tiled"] = dict(rows=n, k=k, per_call_s=secs, bytes=nbytes,
+                                    gbs=nbytes / secs / 1e9, frac_hbm_peak=nbytes / secs / 1e9 / HBM_PEAK_GBS)
+    del wd, qs, fns
+    a, _, _ = workloads.prefill()
+    a0 = torch.from_numpy(a).cuda().to(torch.bfloat16)
+    m, k = a0.shape
+    xs = [a0] + [a0.clone() for _ in range(ROTATE - 1)]
+    qs = [fp4.empty_qtensor(m, k, layout=fp4.LAYOUT_CANONICAL) for _ in xs]
+    fns = [(lambda x=x, q=q: fp4.quantize_fp4(x, layout=fp4.LAYOUT_CANONICAL, out=q)) for x, q in zip(xs, qs)]
+    for f in fns:
+        f()
+    g = capture(torch, fns)
+    g.replay()
+    secs = run_steps(torch, timer, g, fns, max(ROTATE, steps)) / max(ROTATE, steps)
+    nbytes = m * k * 2 + m * k // 2 + m * k // 16 + m * (k // 256) * 2
+    out["activations_bf16_canonical"] = dict(rows=m, k=k, per_call_s=secs, bytes=nbytes,
+                                             gbs=nbytes / secs / 1e9,
+                                             frac_hbm_peak=nbytes / secs / 1e9 / HBM_PEAK_GBS)
+    return out
+
+
+def copy_probe(torch, mib=256, reps=4):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+    of a counter run to bytes (the copy moves exactly mib MiB each way)."""
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return dict(bytes_each_way=mib << 20, launches=reps)
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_stats(stats_csv, title, command):
+    """Markdown summary of a rocprofv3 --stats kernel table (durations in ns)."""
+    rows = _read_csv(stats_csv)
+    lines = [f"# {title}", "", "Command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):", "",
+             "```", command, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    return "\n".join(lines) + "\n"
+
+
+def summarize_traffic(fetch_csv, write_csv, kernel_substr, group, name, commands):
+    """Per-launch HBM bytes of one kernel from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE; values per dispatch), each scaled by what the same counter reads for the
+    plain copy of known size in the same run."""
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _read_csv(path) if r["Counter_Name"] == counter]
+        # the probe's copies are the run's last copy dispatches
+        copies = sorted((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows
+                        if "copyBuffer" in r["Kernel_Name"])
+        kern = [float(r["Counter_Value"]) for r in rows if kernel_substr in r["Kernel_Name"]]
+        if len(copies) < 4 or not kern:
+            raise SystemExit(f"{path}: no probe copies or no {kernel_substr} dispatches")
+        copy_v = float(np.median([v for _, v in copies[-4:]]))
+        factor = (256 << 20) / copy_v
+        out[counter] = dict(kernel_counter_median=float(np.median(kern)), dispatches=len(kern),
+                            copy_counter_median=copy_v, bytes_per_unit=factor,
+                            bytes_per_launch=float(np.median(kern)) * factor)
+    total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    rec = {"kernel_group": group, "source_hash": source_hash(KERNEL_SOURCES[group]),
+           "kernel": kernel_substr, "bytes_per_launch": round(total),
+           "fetch_bytes_per_launch": round(out["FETCH_SIZE"]["bytes_per_launch"]),
+           "write_bytes_per_launch": round(out["WRITE_SIZE"]["bytes_per_launch"]),
+           "counters": out, "commands": commands}
+    with open(os.path.join(ROOT, "profiles", f"{name}_traffic.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    return rec
 
 
 def bench_policy(torch, fp4, workloads, steps):
@@ -281,9 +395,25 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--skip-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize"], default=None,
                     help="run one workload only (for profiling); prints its record")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="with --only: end with 256 MiB device copies (counter calibration)")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "TITLE", "COMMAND"),
+                    help="print a markdown summary of a rocprofv3 kernel-stats CSV and exit")
+    ap.add_argument("--summarize-traffic", nargs=5,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "GROUP", "NAME"),
+                    help="write profiles/NAME_traffic.json from two counter runs and exit")
+    ap.add_argument("--commands", nargs="*", default=[], help="commands recorded with --summarize-traffic")
     args = ap.parse_args()
+    if args.summarize_stats:
+        sys.stdout.write(summarize_stats(*args.summarize_stats))
+        return
+    if args.summarize_traffic:
+        rec = summarize_traffic(*args.summarize_traffic, commands=args.commands)
+        print(json.dumps({k: rec[k] for k in ("kernel", "bytes_per_launch", "fetch_bytes_per_launch",
+                                              "write_bytes_per_launch")}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path).", file=sys.stderr)
@@ -303,8 +433,12 @@ def main():
         fn = {"decode": lambda: bench_decode(torch, fp4, workloads, args.steps, args.warmup),
               "prefill": lambda: bench_prefill(torch, fp4, workloads, args.steps),
               "policy": lambda: bench_policy(torch, fp4, workloads, args.steps),
-              "moe": lambda: bench_moe(torch, fp4, workloads, args.steps)}[args.only]
-        print(json.dumps({args.only: fn()}), flush=True)
+              "moe": lambda: bench_moe(torch, fp4, workloads, args.steps),
+              "quantize": lambda: bench_quantize(torch, fp4, workloads, args.steps)}[args.only]
+        rec = {args.only: fn()}
+        if args.copy_probe:
+            rec["copy_probe"] = copy_probe(torch)
+        print(json.dumps(rec), flush=True)
         return
 
     dec = bench_decode(torch, fp4, workloads, args.steps, args.warmup)
@@ -317,6 +451,8 @@ def main():
         print("# policy done", file=sys.stderr, flush=True)
         secondary["moe_w4a4"] = bench_moe(torch, fp4, workloads, max(4, args.steps // 32))
         print("# moe done", file=sys.stderr, flush=True)
+        secondary["quantize"] = bench_quantize(torch, fp4, workloads, args.steps)
+        print("# quantize done", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads)
 
     traffic = load_traffic("gemv_decode_w4a16")
@@ -337,7 +473,8 @@ def main():
         "config": {"workload": "decode_w4a16: A bf16 [8 x 4096] . W^T, W two-level block FP4 "
                                "[14336 x 4096] (E2M1, E4M3 per 16, FP16 per 256), C bf16",
                    "m": 8, "k": 4096, "n": 14336, "weight_copies_rotated": ROTATE,
-                   "launch": "HIP graph replay"},
+                   "launch": "HIP graph replay",
+                   "launch_us_p10_p50_p90": dec["launch_us_p10_p50_p90"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
