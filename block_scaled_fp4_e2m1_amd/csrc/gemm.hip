@@ -20,6 +20,8 @@
 // launch covers every expert whatever the routing produced (including empty experts).
 // "llama.cpp Put Precision Policy Inside the Model", section "One model can need more
 // than one precision": the same W4A4/W4A8 routing serves dense and mixture-of-experts.
+#include <type_traits>
+
 #include "fp4_device.h"
 #include "fp4_kernels.h"
 
@@ -143,11 +145,12 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 // for the copies of stage s+1. Inside a stage, the weight decode and LDS reads of MFMA
 // step t+1 are interleaved 3 VALU : 1 MFMA with the 16 MFMAs of step t.
 // Per-group factors without separate partial sums: the running sum X is kept in units
-// of the current group's factor s_g = sA[row, g] * M_W[col, g]. At the start of group g
-// X is multiplied by s_{g-1} / s_g (a per-row ratio times a per-column ratio; a zero
-// factor counts as 1, its group contributes nothing), the group's MFMAs accumulate
-// straight into X, and the result is s_last * X. The extra float32 roundings are a few
-// units of 2^-24 per group. (On the FP16 path the weight operand carries mu * 2^-8, so
+// of the current group's factor s_g = sA[row, g] * M_W[col, g]. At the end of group g
+// X is multiplied by s_g / s_{g+1} (a per-row ratio times a per-column ratio; a zero
+// factor counts as 1, its group contributes nothing), the next group's MFMAs accumulate
+// straight into X; after the last group X is multiplied by s_last itself. The
+// multiplies ride in the last MFMA step of the group, where the VALU is otherwise idle.
+// The extra float32 roundings are a few units of 2^-24 per group. (On the FP16 path the weight operand carries mu * 2^-8, so
 // the column factor is 256 * M_W.)
 // ---------------------------------------------------------------------------------
 constexpr int kBM = 64;              // rows per workgroup
@@ -207,9 +210,42 @@ __device__ __forceinline__ void interleave_step() {
   }
 }
 
-template <int A_BF16>
+// per-row (ra) and per-column (rw) ratios s_g / s_{g+1} for the boundary after group g
+struct Rescale {
+  float ra[4][4];
+  float rw[4];
+};
+
+// Step 3 of the last stage of a group: its 16 MFMAs interleaved with the group-boundary
+// rescale of the running sums (ratios computed here: the operands of step 2 are dead
+// and no next-step decode competes for the VALU).
+template <int A_BF16, typename RatioFn>
+__device__ __forceinline__ void last_step_rescale(const StepOperands<A_BF16>& o, float4_t (&x)[4][4],
+                                                  RatioFn&& ratios) {
+  typedef OpTraits<A_BF16> Op;
+  Rescale r;
+  ratios(r);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[mi][ni][i] *= r.ra[mi][i] * r.rw[ni];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+  }
+}
+
+template <int A_BF16, bool RESCALE, typename RatioFn>
 __device__ __forceinline__ void compute_stage(const uint4* abuf, const uint4* wbuf, int wave, int lane,
-                                              const uint2 (&mu)[4], int h, float4_t (&x)[4][4]) {
+                                              const uint2 (&mu)[4], int h, float4_t (&x)[4][4],
+                                              RatioFn&& ratios) {
   // the lane's 16 bytes of code words per row block (one conflict-free 128-bit read each)
   uint4 cw[4];
 #pragma unroll
@@ -229,7 +265,11 @@ __device__ __forceinline__ void compute_stage(const uint4* abuf, const uint4* wb
   stage_operands<A_BF16, 3>(abuf, cw, lane, mu, h, o1);
   interleave_step();
   __builtin_amdgcn_sched_barrier(0);
-  stage_mfma<A_BF16, 3>(o1, x);
+  if (RESCALE) {
+    last_step_rescale<A_BF16>(o1, x, ratios);
+  } else {
+    stage_mfma<A_BF16, 3>(o1, x);
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -345,20 +385,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     }
     return v;
   };
-  // X *= s_{g-1} / s_g before group g's MFMAs
-  auto rescale = [&](int g) {
-    float rw[4];
+  // ratios s_g / s_{g+1} for the boundary after group g, with s_G = 1: after the last
+  // group the "ratio" is the final factor itself
+  auto ratios_after = [&](int g, Rescale& r) {
+    const bool last = g + 1 >= groups;
+    const int gn = last ? g : g + 1;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) rw[ni] = col_factor(ni, g - 1) * __builtin_amdgcn_rcpf(col_factor(ni, g));
+    for (int ni = 0; ni < 4; ++ni) {
+      const float cn = last ? 1.0f : __builtin_amdgcn_rcpf(col_factor(ni, gn));
+      r.rw[ni] = col_factor(ni, g) * cn;
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-      const float4 p = row_factors(mi, g - 1), c = row_factors(mi, g);
-      const float ra[4] = {p.x * __builtin_amdgcn_rcpf(c.x), p.y * __builtin_amdgcn_rcpf(c.y),
-                           p.z * __builtin_amdgcn_rcpf(c.z), p.w * __builtin_amdgcn_rcpf(c.w)};
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[mi][ni][i] = x[mi][ni][i] * ra[i] * rw[ni];
+      const float4 p = row_factors(mi, g), c = row_factors(mi, gn);
+      r.ra[mi][0] = p.x * (last ? 1.0f : __builtin_amdgcn_rcpf(c.x));
+      r.ra[mi][1] = p.y * (last ? 1.0f : __builtin_amdgcn_rcpf(c.y));
+      r.ra[mi][2] = p.z * (last ? 1.0f : __builtin_amdgcn_rcpf(c.z));
+      r.ra[mi][3] = p.w * (last ? 1.0f : __builtin_amdgcn_rcpf(c.w));
     }
   };
 
@@ -368,33 +411,30 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   load_micro(mu_cur, 0);
 
   // stage s in buffers (s & 1): the barrier publishes it and frees the other buffers,
-  // which then receive stage s + 1 while stage s computes
-  auto run_stage = [&](const uint4* abuf, const uint4* wbuf, uint4* nabuf, uint4* nwbuf, int s) {
+  // which then receive stage s + 1 while stage s computes. H = s & 1 is a compile-time
+  // constant: the second stage of every group ends with the group-boundary rescale.
+  auto run_stage = [&](auto h_const, const uint4* abuf, const uint4* wbuf, uint4* nabuf, uint4* nwbuf,
+                       int s) {
+    constexpr int H = decltype(h_const)::value;
     __syncthreads();
     if (s + 1 < stages) copy_stage(nabuf, nwbuf, s + 1);
-    const int h = s & 1;
-    if (h == 0 && s + 2 < stages) load_micro(mu_nxt, (s >> 1) + 1);
-    if (h == 0 && s > 0) rescale(s >> 1);
+    if (H == 0 && s + 2 < stages) load_micro(mu_nxt, (s >> 1) + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute_stage<A_BF16>(abuf, wbuf, wave, lane, mu_cur, h, x);
-    if (h == 1) {
+    compute_stage<A_BF16, H == 1>(abuf, wbuf, wave, lane, mu_cur, H, x,
+                                  [&](Rescale& r) { ratios_after(s >> 1, r); });
+    if (H == 1) {
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) mu_cur[ni] = mu_nxt[ni];
     }
   };
   for (int s = 0; s < stages; s += 2) {
-    run_stage(g_a0, g_w0, g_a1, g_w1, s);
-    run_stage(g_a1, g_w1, g_a0, g_w0, s + 1);
+    run_stage(std::integral_constant<int, 0>{}, g_a0, g_w0, g_a1, g_w1, s);
+    run_stage(std::integral_constant<int, 1>{}, g_a1, g_w1, g_a0, g_w0, s + 1);
   }
 
-  // ---- result = s_last * X, store ----
-  float cf[4];
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) cf[ni] = col_factor(ni, groups - 1);
+  // ---- store (the final factors were applied with the last group) ----
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    const float4 rf4 = row_factors(mi, groups - 1);
-    const float rf[4] = {rf4.x, rf4.y, rf4.z, rf4.w};
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       if (!w_ok[ni]) continue;
@@ -403,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
       for (int i = 0; i < 4; ++i) {
         const int64_t r = row_begin + 16 * mi + 4 * q + i;
         if (r >= row_end) continue;
-        const float v = x[mi][ni][i] * rf[i] * cf[ni];
+        const float v = x[mi][ni][i];
         if (C_BF16)
           static_cast<uint16_t*>(args.c)[r * args.ldc + col] = (uint16_t)bf16_rne_bits(v);
         else
@@ -412,7 +452,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     }
   }
 }
-
 // float32 activations: one thread per output, exact weight values, float32 FMA.
 template <int C_BF16>
 __global__ __launch_bounds__(256) void k_gemm_f32act(const float* __restrict__ a, int64_t lda,
