@@ -150,8 +150,11 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 // factor counts as 1, its group contributes nothing), the next group's MFMAs accumulate
 // straight into X; after the last group X is multiplied by s_last itself. The
 // multiplies ride in the last MFMA step of the group, where the VALU is otherwise idle.
-// The extra float32 roundings are a few units of 2^-24 per group. (On the FP16 path the weight operand carries mu * 2^-8, so
-// the column factor is 256 * M_W.)
+// The extra float32 roundings are a few units of 2^-24 per group. (On the FP16 path the
+// weight operand carries mu * 2^-8, so the column factor is 256 * M_W.)
+// Each wave copies and reads only its own weight codes, so the code words and step-0
+// weight fragments of stage s+1 are read and decoded during the last MFMA step of stage
+// s, after a wait on the wave's own copies; only the activation tile needs the barrier.
 // ---------------------------------------------------------------------------------
 constexpr int kBM = 64;              // rows per workgroup
 constexpr int kBN = 256;             // weight rows (output columns) per workgroup
@@ -216,42 +219,59 @@ struct Rescale {
   float rw[4];
 };
 
-// Step 3 of the last stage of a group: its 16 MFMAs interleaved with the group-boundary
-// rescale of the running sums (ratios computed here: the operands of step 2 are dead
-// and no next-step decode competes for the VALU).
-template <int A_BF16, typename RatioFn>
-__device__ __forceinline__ void last_step_rescale(const StepOperands<A_BF16>& o, float4_t (&x)[4][4],
-                                                  RatioFn&& ratios) {
+// Last MFMA step of a stage (step 3): its 16 MFMAs interleaved with
+//   - the code words and step-0 weight fragments of the next stage (read from the
+//     wave's own LDS buffer after waiting for its own copies: at most VMCNT younger
+//     loads may stay in flight), and
+//   - for the last stage of a group, the group-boundary rescale of the running sums
+//     (ratios computed here: the operands of step 2 are dead).
+template <int A_BF16, bool RESCALE, int VMCNT, typename RatioFn>
+__device__ __forceinline__ void last_step(const StepOperands<A_BF16>& o, float4_t (&x)[4][4],
+                                          RatioFn&& ratios, const uint4* nwbuf, int wave, int lane,
+                                          const uint32_t (&mw_next)[4], uint4 (&cw)[4],
+                                          typename OpTraits<A_BF16>::frag (&wf0)[4]) {
   typedef OpTraits<A_BF16> Op;
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<VMCNT>::value);
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) cw[ni] = nwbuf[(wave * 4 + ni) * 64 + lane];
   Rescale r;
-  ratios(r);
+  if (RESCALE) ratios(r);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int ni = 0; ni < 4; ++ni)
+    wf0[ni] = Op::weight(cw[ni].x, Op::micro_operand(mw_next[ni] & 0xFFu));
+  if (RESCALE) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[mi][ni][i] *= r.ra[mi][i] * r.rw[ni];
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[mi][ni][i] *= A_BF16 ? r.rw[ni] : r.ra[mi][i] * r.rw[ni];
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x002, RESCALE ? 10 : 3, 0);  // VALU
   }
 }
 
-template <int A_BF16, bool RESCALE, typename RatioFn>
-__device__ __forceinline__ void compute_stage(const uint4* abuf, const uint4* wbuf, int wave, int lane,
-                                              const uint2 (&mu)[4], int h, float4_t (&x)[4][4],
-                                              RatioFn&& ratios) {
-  // the lane's 16 bytes of code words per row block (one conflict-free 128-bit read each)
-  uint4 cw[4];
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) cw[ni] = wbuf[(wave * 4 + ni) * 64 + lane];
+// One stage: 4 MFMA steps. On entry cw holds the stage's code words and wf0 its step-0
+// weight fragments; on exit they hold the next stage's.
+template <int A_BF16, bool RESCALE, int VMCNT, typename RatioFn>
+__device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
+                                              typename OpTraits<A_BF16>::frag (&wf0)[4], int wave,
+                                              int lane, const uint2 (&mu)[4], int h, float4_t (&x)[4][4],
+                                              RatioFn&& ratios, const uint4* nwbuf, const uint2 (&mu_next)[4],
+                                              int h_next) {
+  typedef typename OpTraits<A_BF16>::frag frag;
   StepOperands<A_BF16> o0, o1;
-  stage_operands<A_BF16, 0>(abuf, cw, lane, mu, h, o0);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) o0.af[mi] = __builtin_bit_cast(frag, abuf[(mi * 4 + 0) * 64 + lane]);
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) o0.wf[ni] = wf0[ni];
   __builtin_amdgcn_sched_barrier(0);
   stage_mfma<A_BF16, 0>(o0, x);
   stage_operands<A_BF16, 1>(abuf, cw, lane, mu, h, o1);
@@ -265,11 +285,10 @@ __device__ __forceinline__ void compute_stage(const uint4* abuf, const uint4* wb
   stage_operands<A_BF16, 3>(abuf, cw, lane, mu, h, o1);
   interleave_step();
   __builtin_amdgcn_sched_barrier(0);
-  if (RESCALE) {
-    last_step_rescale<A_BF16>(o1, x, ratios);
-  } else {
-    stage_mfma<A_BF16, 3>(o1, x);
-  }
+  uint32_t mw_next[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) mw_next[ni] = h_next == 0 ? mu_next[ni].x : mu_next[ni].y;
+  last_step<A_BF16, RESCALE, VMCNT>(o1, x, ratios, nwbuf, wave, lane, mw_next, cw, wf0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -302,7 +321,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     if (row_begin >= row_end) return;
   }
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index as a wave-uniform (scalar) value: LDS-DMA destinations derive from it
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q = lane >> 4, l16 = lane & 15;
   const int64_t n0 = (int64_t)tn * kBN + wave * 64;  // first output column of this wave
   const int64_t nb_tile0 = w_row_base / 16 + (int64_t)tn * (kBN / 16);  // first row block of the tile
@@ -369,67 +389,83 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
 
   const float* sa_lane = g_sa + 4 * q;                               // + g*64 + mi*16: rows 4q..4q+3
   const uint16_t* mw_lane = g_mw + (wave * 4) * groups * 16 + l16;    // + (ni*G + g)*16
-  // factors of group g (a zero factor counts as 1)
+  // column factor M_W of group g (a zero factor counts as 1: its columns' codes are 0)
   auto col_factor = [&](int ni, int g) {
     const float v = fp16_value_hw(mw_lane[(ni * groups + g) * 16]);
-    return v != 0.0f ? v * OpTraits<A_BF16>::kMicroUnit : 1.0f;
-  };
-  auto row_factors = [&](int mi, int g) {
-    float4 v = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-    if (!A_BF16) {
-      v = *reinterpret_cast<const float4*>(sa_lane + g * kBM + mi * 16);
-      v.x = v.x != 0.0f ? v.x : 1.0f;
-      v.y = v.y != 0.0f ? v.y : 1.0f;
-      v.z = v.z != 0.0f ? v.z : 1.0f;
-      v.w = v.w != 0.0f ? v.w : 1.0f;
-    }
-    return v;
+    return v != 0.0f ? v : 1.0f;
   };
   // ratios s_g / s_{g+1} for the boundary after group g, with s_G = 1: after the last
-  // group the "ratio" is the final factor itself
+  // group the "ratio" is the final factor itself. Row ratios come from the table built
+  // in the prologue; the FP16 path's 2^8 micro unit cancels except in the final factor.
   auto ratios_after = [&](int g, Rescale& r) {
     const bool last = g + 1 >= groups;
-    const int gn = last ? g : g + 1;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const float cn = last ? 1.0f : __builtin_amdgcn_rcpf(col_factor(ni, gn));
-      r.rw[ni] = col_factor(ni, g) * cn;
-    }
+    for (int ni = 0; ni < 4; ++ni)
+      r.rw[ni] = last ? col_factor(ni, g) * OpTraits<A_BF16>::kMicroUnit
+                      : col_factor(ni, g) * __builtin_amdgcn_rcpf(col_factor(ni, g + 1));
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-      const float4 p = row_factors(mi, g), c = row_factors(mi, gn);
-      r.ra[mi][0] = p.x * (last ? 1.0f : __builtin_amdgcn_rcpf(c.x));
-      r.ra[mi][1] = p.y * (last ? 1.0f : __builtin_amdgcn_rcpf(c.y));
-      r.ra[mi][2] = p.z * (last ? 1.0f : __builtin_amdgcn_rcpf(c.z));
-      r.ra[mi][3] = p.w * (last ? 1.0f : __builtin_amdgcn_rcpf(c.w));
+      float4 v = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+      if (!A_BF16) v = *reinterpret_cast<const float4*>(sa_lane + g * kBM + mi * 16);
+      r.ra[mi][0] = v.x; r.ra[mi][1] = v.y; r.ra[mi][2] = v.z; r.ra[mi][3] = v.w;
     }
   };
 
   uint2 mu_cur[4], mu_nxt[4];
   const int stages = 2 * groups;
   copy_stage(g_a0, g_w0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   load_micro(mu_cur, 0);
+  // stage 0's code words and step-0 weight fragments (the wave's own copies)
+  uint4 cw[4];
+  typename OpTraits<A_BF16>::frag wf0[4];
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
+  if (!A_BF16) {
+    // row factors [g][row] -> ratios f_g / f_{g+1} (last group: f_{G-1}), in place; each
+    // lane of wave 0 walks one row upwards in g, reading f_{g+1} before it is replaced
+    __syncthreads();  // every wave's factor copies have landed
+    if (wave == 0) {
+      float f = g_sa[lane];
+      for (int g = 0; g + 1 < groups; ++g) {
+        const float fn = g_sa[(g + 1) * kBM + lane];
+        g_sa[g * kBM + lane] = f / fn;
+        f = fn;
+      }
+    }
+  }
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    cw[ni] = g_w0[(wave * 4 + ni) * 64 + lane];
+    wf0[ni] = OpTraits<A_BF16>::weight(cw[ni].x, OpTraits<A_BF16>::micro_operand(mu_cur[ni].x & 0xFFu));
+  }
 
-  // stage s in buffers (s & 1): the barrier publishes it and frees the other buffers,
-  // which then receive stage s + 1 while stage s computes. H = s & 1 is a compile-time
-  // constant: the second stage of every group ends with the group-boundary rescale.
-  auto run_stage = [&](auto h_const, const uint4* abuf, const uint4* wbuf, uint4* nabuf, uint4* nwbuf,
-                       int s) {
+  // stage s in buffers (s & 1): the barrier publishes its activation tile (every wave's
+  // copies are complete) and frees the other buffers, which then receive stage s + 1
+  // while stage s computes. H = s & 1 is a compile-time constant: the second stage of
+  // every group ends with the group-boundary rescale.
+  auto run_stage = [&](auto h_const, const uint4* abuf, uint4* nabuf, uint4* nwbuf, int s) {
     constexpr int H = decltype(h_const)::value;
     __syncthreads();
     if (s + 1 < stages) copy_stage(nabuf, nwbuf, s + 1);
-    if (H == 0 && s + 2 < stages) load_micro(mu_nxt, (s >> 1) + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute_stage<A_BF16, H == 1>(abuf, wbuf, wave, lane, mu_cur, H, x,
-                                  [&](Rescale& r) { ratios_after(s >> 1, r); });
+    // (unconditional in H == 0 stages, the last group re-reading its own, so that exactly
+    // four loads follow the copies when last_step waits for them)
+    if (H == 0) load_micro(mu_nxt, min((s >> 1) + 1, groups - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    // next stage: same group (H == 0: micro-scale word 1 of mu_cur) or the next group
+    // (H == 1: word 0 of mu_nxt); the H == 0 stage's four micro-scale loads may stay in
+    // flight
+    compute_stage<A_BF16, H == 1, H == 0 ? 4 : 0>(
+        abuf, cw, wf0, wave, lane, mu_cur, H, x, [&](Rescale& r) { ratios_after(s >> 1, r); }, nwbuf,
+        H == 0 ? mu_cur : mu_nxt, 1 - H);
     if (H == 1) {
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) mu_cur[ni] = mu_nxt[ni];
     }
   };
   for (int s = 0; s < stages; s += 2) {
-    run_stage(std::integral_constant<int, 0>{}, g_a0, g_w0, g_a1, g_w1, s);
-    run_stage(std::integral_constant<int, 1>{}, g_a1, g_w1, g_a0, g_w0, s + 1);
+    run_stage(std::integral_constant<int, 0>{}, g_a0, g_a1, g_w1, s);
+    run_stage(std::integral_constant<int, 1>{}, g_a1, g_a0, g_w0, s + 1);
   }
 
   // ---- store (the final factors were applied with the last group) ----

@@ -158,7 +158,8 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 // Activation pass for the matrix kernels. Quantizes each row like k_quantize and writes
 // the *decoded* element times its micro-scale as FP16 (exact: E2M1 * mu has at most 6
 // significant bits in [2^-10, 2688]; E4M3 * mu * 2^-3 at most 8 bits in [2^-21, 25088]),
-// plus one float32 factor per 256-group (M, or 8*M for E4M3 elements), so that
+// plus one float32 factor per 256-group (M, or 8*M for E4M3 elements; 1 for an all-zero
+// group), so that
 //   A_hat[r, c] = aq[r, c] * scale[r, c / 256]   exactly.
 template <int IN_BF16, int ELEM_E4M3>
 __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, int64_t lda,
@@ -203,7 +204,9 @@ __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, in
   pk.z = __builtin_bit_cast(uint32_t, out[2]);
   pk.w = __builtin_bit_cast(uint32_t, out[3]);
   *reinterpret_cast<uint4*>(aq + r * ldq + col) = pk;
-  if (li == 0) scale[r * groups + g] = ELEM_E4M3 ? m_val * 8.0f : m_val;
+  // a group whose macro-scale is 0 has only zero operands: its factor is written as 1, so
+  // the product kernel's factor ratios never divide by zero
+  if (li == 0) scale[r * groups + g] = m_val > 0.0f ? (ELEM_E4M3 ? m_val * 8.0f : m_val) : 1.0f;
 }
 
 inline unsigned blocks_for(int64_t rows, int64_t k) {
