@@ -217,6 +217,9 @@ fp4_status grouped_gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_
   const int64_t n = w->rows / n_experts, k = w->k;
   if (n % 16 || a_rows < 1 || total_rows < 0 || lda < k || ldc < n) return FP4_E_SHAPE;
   if (!row_token && total_rows > a_rows) return FP4_E_SHAPE;
+  // gathered rows are addressed with 32-bit byte offsets from the start of the operand
+  // (bf16 A for W4A16, the FP16 activation workspace otherwise: both 2 bytes/element)
+  if (row_token && a_rows * (act == FP4_A16 ? lda : k) * 2 > (int64_t)0xFFFFFFFF) return FP4_E_SHAPE;
   if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
   if (!aligned(c, dtype_size(c_dtype)) || !aligned(expert_offsets, 4) ||
       (row_token && !aligned(row_token, 4)))

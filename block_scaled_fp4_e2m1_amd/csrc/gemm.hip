@@ -156,6 +156,7 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 // weight fragments of stage s+1 are read and decoded during the last MFMA step of stage
 // s, after a wait on the wave's own copies; only the activation tile needs the barrier.
 // ---------------------------------------------------------------------------------
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 constexpr int kBM = 64;              // rows per workgroup
 constexpr int kBN = 256;             // weight rows (output columns) per workgroup
 constexpr int kStageK = 128;         // k per pipeline stage
@@ -346,39 +347,54 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     }
   }
 
+  // Operand copies go through raw buffer resources: the per-lane byte offset is fixed for
+  // the whole k loop and the per-stage part is a scalar offset, so the loop spends no
+  // vector instructions on addresses. Reads past a resource's size return zero.
   // ---- activation copies: wave w moves row tile mi = w (16 rows), 4 steps per stage ----
   const uint16_t* a16 = static_cast<const uint16_t*>(args.a);
   int64_t a_src_row = min(row_begin + wave * 16 + l16, row_end - 1);
   if (GROUPED && args.row_token) a_src_row = args.row_token[a_src_row];
-  const uint16_t* a_lane_src = a16 + a_src_row * args.lda + 8 * q;
+  // gathered rows are addressed from the start of A (the launcher keeps A under 4 GiB);
+  // otherwise from the workgroup's first row
+  const int64_t a_base_row = (GROUPED && args.row_token) ? 0 : row_begin;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a16 + a_base_row * args.lda), (short)0, (int)0xFFFFFFFF, kRsrcWord3);
+  const uint32_t a_voff = (uint32_t)(((a_src_row - a_base_row) * args.lda + 8 * q) * 2);
 
-  // ---- weights: 4 row blocks (16 columns each) per wave ----
-  int64_t wtile0[4];
+  // ---- weights: 4 row blocks (16 columns each) per wave, consecutive in the tiled layout ----
   bool w_ok[4];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int64_t nb = n0 / 16 + ni;
-    w_ok[ni] = nb < nblocks;
-    wtile0[ni] = (w_row_base / 16 + min(nb, nblocks - 1)) * groups;
-  }
+  for (int ni = 0; ni < 4; ++ni) w_ok[ni] = n0 / 16 + ni < nblocks;
+  const int64_t wb0 = w_row_base / 16 + n0 / 16;               // the wave's first row block
+  const int64_t w_blocks_left = w_row_base / 16 + nblocks - wb0;  // row blocks up to the end
+  const int64_t w_tiles_left = w_blocks_left > 0 ? w_blocks_left * groups : 0;
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(args.codes + wb0 * groups * kTileCodeBytes), (short)0,
+      (int)min(w_tiles_left * kTileCodeBytes, (int64_t)0xFFFFFFFF), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t mu_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(args.micro + wb0 * groups * kTileMicroBytes), (short)0,
+      (int)min(w_tiles_left * kTileMicroBytes, (int64_t)0xFFFFFFFF), kRsrcWord3);
+  const uint32_t mu_voff = (uint32_t)((q >> 1) * 128 + l16 * 8);
   auto copy_stage = [&](uint4* abuf, uint4* wbuf, int s) {  // stage s = 2 g + h
     const int g = s >> 1, h = s & 1;
-    const int64_t k0 = (int64_t)s * kStageK;
+    const uint32_t a_soff = (uint32_t)s * (kStageK * 2);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      __builtin_amdgcn_global_load_lds((global_void_ptr)(a_lane_src + k0 + 32 * t),
-                                       (lds_void_ptr)(abuf + (wave * 4 + t) * 64), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(abuf + (wave * 4 + t) * 64), 16,
+                                               a_voff, a_soff + 64 * t, 0, 0);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
-      __builtin_amdgcn_global_load_lds(
-          (global_void_ptr)(args.codes + (wtile0[ni] + g) * kTileCodeBytes + h * 1024 + lane * 16),
-          (lds_void_ptr)(wbuf + (wave * 4 + ni) * 64), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_rsrc, (lds_void_ptr)(wbuf + (wave * 4 + ni) * 64), 16, (uint32_t)lane * 16,
+          (uint32_t)((ni * groups + g) * kTileCodeBytes + h * 1024), 0, 0);
   };
   auto load_micro = [&](uint2 (&mu)[4], int g) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      mu[ni] = *reinterpret_cast<const uint2*>(args.micro + (wtile0[ni] + g) * kTileMicroBytes +
-                                               (q >> 1) * 128 + l16 * 8);
+    for (int ni = 0; ni < 4; ++ni) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(mu_rsrc, mu_voff,
+                                                         (uint32_t)((ni * groups + g) * kTileMicroBytes), 0);
+      mu[ni] = make_uint2(v[0], v[1]);
+    }
   };
 
   float4_t x[4][4];

@@ -129,7 +129,9 @@ fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int
  * in [expert_offsets[e], expert_offsets[e+1]):
  *     C[r, :] = A_hat[src(r), :] . W_hat_e^T,  src(r) = row_token ? row_token[r] : r
  *   a              device [a_rows x k], row stride lda (bf16 or f32)
- *   row_token      device int32 [total_rows] source row of each routed row, or NULL
+ *   row_token      device int32 [total_rows] source row of each routed row, or NULL;
+ *                  with a gather the product's operand (bf16 A for FP4_A16, else the
+ *                  FP16 workspace copy, a_rows x k) must stay under 4 GiB (FP4_E_SHAPE)
  *   expert_offsets device int32 [n_experts + 1], non-decreasing, [0] = 0,
  *                  [n_experts] = total_rows (checked only in debug builds)
  *   w              quantized weights, experts stacked: rows = n_experts * n, TILED
