@@ -3,7 +3,7 @@
 // the matrix kernels.
 //
 // Work mapping: 32 lanes own one 256-element group of one row, 8 consecutive elements
-// per lane (one 16-byte load for bf16, two for float32). A 16-element micro-vector is a
+// per lane (one 16-byte load for bf16, two for float32); a block covers 8 groups of a row. A 16-element micro-vector is a
 // lane pair, so its max is one cross-lane exchange; the group max is four more.
 // Source of the method: "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for
 // Blackwell B200", section "The Mathematical Breakthrough of Microscopic FP4 Scaling".
@@ -56,6 +56,18 @@ __device__ __forceinline__ float group_scales(const float v[8], float emax, uint
 
 __device__ __forceinline__ uint32_t sign_of(float f) { return __float_as_uint(f) >> 31; }
 
+// Grid mapping shared by the kernels: a block of 256 threads covers 8 groups (32 lanes
+// each) of one row; block b is row b / gchunks, groups (b % gchunks) * 8 + 0..7, with
+// gchunks = ceil(groups / 8). One wave-uniform 32-bit division per thread.
+__device__ __forceinline__ bool seg_index(int64_t groups, int64_t& r, int64_t& g) {
+  const uint32_t gchunks = (uint32_t)((groups + 7) >> 3);
+  const uint32_t b = blockIdx.x;
+  const uint32_t row = b / gchunks;
+  r = row;
+  g = (int64_t)(b - row * gchunks) * 8 + (threadIdx.x >> 5);
+  return g < groups;
+}
+
 template <int IN_BF16, int ELEM_E4M3, int TILED>
 __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t ldx,
                                                   int64_t rows, int64_t k,
@@ -63,11 +75,9 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
                                                   uint8_t* __restrict__ micro,
                                                   uint16_t* __restrict__ macro) {
   const int64_t groups = k >> 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t seg = gid >> 5;
   const int li = threadIdx.x & 31;
-  if (seg >= rows * groups) return;  // whole 32-lane segments leave together
-  const int64_t r = seg / groups, g = seg - r * groups;
+  int64_t r, g;
+  if (!seg_index(groups, r, g)) return;  // whole 32-lane segments leave together
   const int64_t col = g * kGroup + li * 8;
 
   float v[8];
@@ -114,11 +124,9 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
                                                     int64_t rows, int64_t k, void* __restrict__ y,
                                                     int64_t ldy) {
   const int64_t groups = k >> 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t seg = gid >> 5;
   const int li = threadIdx.x & 31;
-  if (seg >= rows * groups) return;
-  const int64_t r = seg / groups, g = seg - r * groups;
+  int64_t r, g;
+  if (!seg_index(groups, r, g)) return;  // whole 32-lane segments leave together
   const int64_t col = g * kGroup + li * 8;
 
   const int64_t mu_off = TILED ? tiled_micro_offset(r, col, groups) : r * (k >> 4) + (col >> 4);
@@ -167,11 +175,9 @@ __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, in
                                                   _Float16* __restrict__ aq, int64_t ldq,
                                                   float* __restrict__ scale) {
   const int64_t groups = k >> 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t seg = gid >> 5;
   const int li = threadIdx.x & 31;
-  if (seg >= rows * groups) return;
-  const int64_t r = seg / groups, g = seg - r * groups;
+  int64_t r, g;
+  if (!seg_index(groups, r, g)) return;  // whole 32-lane segments leave together
   const int64_t col = g * kGroup + li * 8;
 
   float v[8];
@@ -182,13 +188,20 @@ __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, in
   const float mu = e4m3_value(mu_byte);
   half2_t out[4];
   if (!ELEM_E4M3) {
-    const E2M1Thresholds th(s > 0.0f ? s : 1.0f);
+    // codes as in k_quantize, then decoded two at a time by the hardware conversion
+    // (scale 1: exact) and multiplied by mu in FP16 (E2M1 * mu is exact in FP16)
+    uint32_t word = 0u;
+    if (s > 0.0f) {
+      const E2M1Thresholds th(s);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float mag = s > 0.0f ? e2m1_mag_value(th.mag(fabsf(v[i]))) * mu : 0.0f;
-      const _Float16 h = (_Float16)(sign_of(v[i]) ? -mag : mag);
-      if (i & 1) out[i >> 1][1] = h; else out[i >> 1][0] = h;
+      for (int i = 0; i < 8; ++i) word |= (th.mag(fabsf(v[i])) | (sign_of(v[i]) << 3)) << (4 * i);
     }
+    const _Float16 muh = (_Float16)mu;
+    const half2_t m2 = {muh, muh};
+    out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * m2;
+    out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * m2;
+    out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * m2;
+    out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * m2;
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -209,9 +222,11 @@ __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, in
   if (li == 0) scale[r * groups + g] = m_val > 0.0f ? (ELEM_E4M3 ? m_val * 8.0f : m_val) : 1.0f;
 }
 
+// one block per (row, run of 8 groups); see seg_index. 0 when the grid would exceed
+// 2^32 work-items (the launchers then refuse the shape).
 inline unsigned blocks_for(int64_t rows, int64_t k) {
-  const int64_t threads = rows * (k >> 8) * 32;
-  return (unsigned)((threads + 255) / 256);
+  const int64_t blocks = rows * (((k >> 8) + 7) >> 3);
+  return blocks <= (int64_t)0xFFFFFFFF / 256 ? (unsigned)blocks : 0u;
 }
 
 }  // namespace
@@ -222,6 +237,7 @@ hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, 
                            int elem_e4m3, int tiled, uint8_t* codes, uint8_t* micro,
                            uint16_t* macro, hipStream_t st) {
   const dim3 grid(blocks_for(rows, k)), block(256);
+  if (grid.x == 0) return hipErrorInvalidValue;
 #define FP4_Q(B, E, T) \
   hipLaunchKernelGGL((k_quantize<B, E, T>), grid, block, 0, st, x, ldx, rows, k, codes, micro, macro)
   if (in_bf16) {
@@ -237,6 +253,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const u
                              int64_t rows, int64_t k, int elem_e4m3, int tiled, void* y,
                              int out_bf16, int64_t ldy, hipStream_t st) {
   const dim3 grid(blocks_for(rows, k)), block(256);
+  if (grid.x == 0) return hipErrorInvalidValue;
 #define FP4_D(B, E, T) \
   hipLaunchKernelGGL((k_dequantize<B, E, T>), grid, block, 0, st, codes, micro, macro, rows, k, y, ldy)
   if (out_bf16) {
@@ -251,6 +268,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const u
 hipError_t launch_act_prep(const void* a, int in_bf16, int64_t rows, int64_t k, int64_t lda,
                            int elem_e4m3, _Float16* aq, int64_t ldq, float* scale, hipStream_t st) {
   const dim3 grid(blocks_for(rows, k)), block(256);
+  if (grid.x == 0) return hipErrorInvalidValue;
   if (in_bf16) {
     if (elem_e4m3) hipLaunchKernelGGL((k_act_prep<1, 1>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
     else hipLaunchKernelGGL((k_act_prep<1, 0>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
