@@ -145,11 +145,12 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 // for the copies of stage s+1. Inside a stage, the weight decode and LDS reads of MFMA
 // step t+1 are interleaved 3 VALU : 1 MFMA with the 16 MFMAs of step t.
 // Per-group factors without separate partial sums: the running sum X is kept in units
-// of the current group's factor s_g = sA[row, g] * M_W[col, g]. At the end of group g
-// X is multiplied by s_g / s_{g+1} (a per-row ratio times a per-column ratio; a zero
-// factor counts as 1, its group contributes nothing), the next group's MFMAs accumulate
-// straight into X; after the last group X is multiplied by s_last itself. The
-// multiplies ride in the last MFMA step of the group, where the VALU is otherwise idle.
+// of the current group's factor s_g = sA[row, g] * M_W[col, g]. Between groups g and
+// g+1, X is multiplied by s_g / s_{g+1} (a per-row ratio times a per-column ratio; a
+// zero factor counts as 1, its group contributes nothing) and the next group's MFMAs
+// accumulate straight into X; at the store X is multiplied by s_last itself. The ratios
+// are computed in the last MFMA step of group g (VALU otherwise idle) and each tile's
+// multiply is issued just before its first MFMA of group g+1, where it waits on nothing.
 // The extra float32 roundings are a few units of 2^-24 per group. (On the FP16 path the
 // weight operand carries mu * 2^-8, so the column factor is 256 * M_W.)
 // Each wave copies and reads only its own weight codes, so the code words and step-0
@@ -205,10 +206,18 @@ __device__ __forceinline__ void stage_mfma(const StepOperands<A_BF16>& o, float4
     for (int ni = 0; ni < 4; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
 }
 
-// 1 MFMA : 3 VALU interleave for the 16 MFMAs of a step
+// Interleave for the 16 MFMAs of a step with the next step's operand preparation: the
+// four activation-fragment LDS reads go right after the first MFMAs (their latency then
+// hides behind the rest of the step), the weight decode 3 VALU per MFMA.
 __device__ __forceinline__ void interleave_step() {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+  }
+#pragma unroll
+  for (int i = 4; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
   }
@@ -224,19 +233,18 @@ struct Rescale {
 //   - the code words and step-0 weight fragments of the next stage (read from the
 //     wave's own LDS buffer after waiting for its own copies: at most VMCNT younger
 //     loads may stay in flight), and
-//   - for the last stage of a group, the group-boundary rescale of the running sums
-//     (ratios computed here: the operands of step 2 are dead).
-template <int A_BF16, bool RESCALE, int VMCNT, typename RatioFn>
+//   - for the last stage of a group (RATIOS), the group-boundary ratios, applied in the
+//     next group's first step (the operands of step 2 are dead here).
+template <int A_BF16, bool RATIOS, int VMCNT, typename RatioFn>
 __device__ __forceinline__ void last_step(const StepOperands<A_BF16>& o, float4_t (&x)[4][4],
-                                          RatioFn&& ratios, const uint4* nwbuf, int wave, int lane,
-                                          const uint32_t (&mw_next)[4], uint4 (&cw)[4],
+                                          RatioFn&& ratios, Rescale& r, const uint4* nwbuf, int wave,
+                                          int lane, const uint32_t (&mw_next)[4], uint4 (&cw)[4],
                                           typename OpTraits<A_BF16>::frag (&wf0)[4]) {
   typedef OpTraits<A_BF16> Op;
   __builtin_amdgcn_s_waitcnt(kVmcntWait<VMCNT>::value);
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) cw[ni] = nwbuf[(wave * 4 + ni) * 64 + lane];
-  Rescale r;
-  if (RESCALE) ratios(r);
+  if (RATIOS) ratios(r);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -244,39 +252,54 @@ __device__ __forceinline__ void last_step(const StepOperands<A_BF16>& o, float4_
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni)
     wf0[ni] = Op::weight(cw[ni].x, Op::micro_operand(mw_next[ni] & 0xFFu));
-  if (RESCALE) {
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[mi][ni][i] *= A_BF16 ? r.rw[ni] : r.ra[mi][i] * r.rw[ni];
-  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, RESCALE ? 10 : 3, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x002, RATIOS ? 5 : 3, 0);  // VALU
   }
 }
 
 // One stage: 4 MFMA steps. On entry cw holds the stage's code words and wf0 its step-0
-// weight fragments; on exit they hold the next stage's.
-template <int A_BF16, bool RESCALE, int VMCNT, typename RatioFn>
+// weight fragments; on exit they hold the next stage's. RESCALE: the first stage of a
+// group multiplies each running sum by the boundary ratios r just before that tile's
+// first MFMA of the group (no wait on MFMA results: those sums were finished a step
+// earlier). RATIOS: the last stage of a group computes the next ratios into r.
+template <int A_BF16, bool RESCALE, bool RATIOS, int VMCNT, typename RatioFn>
 __device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
                                               typename OpTraits<A_BF16>::frag (&wf0)[4], int wave,
                                               int lane, const uint2 (&mu)[4], int h, float4_t (&x)[4][4],
-                                              RatioFn&& ratios, const uint4* nwbuf, const uint2 (&mu_next)[4],
-                                              int h_next) {
-  typedef typename OpTraits<A_BF16>::frag frag;
+                                              RatioFn&& ratios, Rescale& r, const uint4* nwbuf,
+                                              const uint2 (&mu_next)[4], int h_next) {
+  typedef OpTraits<A_BF16> Op;
+  typedef typename Op::frag frag;
   StepOperands<A_BF16> o0, o1;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) o0.af[mi] = __builtin_bit_cast(frag, abuf[(mi * 4 + 0) * 64 + lane]);
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) o0.wf[ni] = wf0[ni];
   __builtin_amdgcn_sched_barrier(0);
-  stage_mfma<A_BF16, 0>(o0, x);
-  stage_operands<A_BF16, 1>(abuf, cw, lane, mu, h, o1);
-  interleave_step();
+  if (RESCALE) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[mi][ni][i] *= A_BF16 ? r.rw[ni] : r.ra[mi][i] * r.rw[ni];
+        x[mi][ni] = Op::mfma(o0.af[mi], o0.wf[ni], x[mi][ni]);
+      }
+    stage_operands<A_BF16, 1>(abuf, cw, lane, mu, h, o1);
+    __builtin_amdgcn_sched_group_barrier(0x002, A_BF16 ? 4 : 8, 0);  // VALU: tile 0's rescale
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, A_BF16 ? 6 : 10, 0);  // VALU
+    }
+  } else {
+    stage_mfma<A_BF16, 0>(o0, x);
+    stage_operands<A_BF16, 1>(abuf, cw, lane, mu, h, o1);
+    interleave_step();
+  }
   __builtin_amdgcn_sched_barrier(0);
   stage_mfma<A_BF16, 1>(o1, x);
   stage_operands<A_BF16, 2>(abuf, cw, lane, mu, h, o0);
@@ -289,7 +312,7 @@ __device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
   uint32_t mw_next[4];
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) mw_next[ni] = h_next == 0 ? mu_next[ni].x : mu_next[ni].y;
-  last_step<A_BF16, RESCALE, VMCNT>(o1, x, ratios, nwbuf, wave, lane, mw_next, cw, wf0);
+  last_step<A_BF16, RATIOS, VMCNT>(o1, x, ratios, r, nwbuf, wave, lane, mw_next, cw, wf0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -459,6 +482,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   // copies are complete) and frees the other buffers, which then receive stage s + 1
   // while stage s computes. H = s & 1 is a compile-time constant: the second stage of
   // every group ends with the group-boundary rescale.
+  // boundary ratios carried from the last stage of a group into the first of the next
+  // (1 before the first group; after the last group they are the final factors)
+  Rescale resc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    resc.rw[i] = 1.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) resc.ra[i][j] = 1.0f;
+  }
   auto run_stage = [&](auto h_const, const uint4* abuf, uint4* nabuf, uint4* nwbuf, int s) {
     constexpr int H = decltype(h_const)::value;
     __syncthreads();
@@ -471,9 +503,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     // next stage: same group (H == 0: micro-scale word 1 of mu_cur) or the next group
     // (H == 1: word 0 of mu_nxt); the H == 0 stage's four micro-scale loads may stay in
     // flight
-    compute_stage<A_BF16, H == 1, H == 0 ? 4 : 0>(
-        abuf, cw, wf0, wave, lane, mu_cur, H, x, [&](Rescale& r) { ratios_after(s >> 1, r); }, nwbuf,
-        H == 0 ? mu_cur : mu_nxt, 1 - H);
+    compute_stage<A_BF16, H == 0, H == 1, H == 0 ? 4 : 0>(
+        abuf, cw, wf0, wave, lane, mu_cur, H, x, [&](Rescale& rr) { ratios_after(s >> 1, rr); }, resc,
+        nwbuf, H == 0 ? mu_cur : mu_nxt, 1 - H);
     if (H == 1) {
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) mu_cur[ni] = mu_nxt[ni];
@@ -484,7 +516,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     run_stage(std::integral_constant<int, 1>{}, g_a1, g_a0, g_w0, s + 1);
   }
 
-  // ---- store (the final factors were applied with the last group) ----
+  // ---- apply the final factors, store ----
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -495,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
       for (int i = 0; i < 4; ++i) {
         const int64_t r = row_begin + 16 * mi + 4 * q + i;
         if (r >= row_end) continue;
-        const float v = x[mi][ni][i];
+        const float v = x[mi][ni][i] * (A_BF16 ? resc.rw[ni] : resc.ra[mi][i] * resc.rw[ni]);
         if (C_BF16)
           static_cast<uint16_t*>(args.c)[r * args.ldc + col] = (uint16_t)bf16_rne_bits(v);
         else
