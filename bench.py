@@ -276,6 +276,37 @@ def summarize_traffic(fetch_csv, write_csv, kernel_substr, group, name, commands
     return rec
 
 
+def summarize_counters(csv_path, kernel_substr, title, command, simds=1024, xcds=8):
+    """Markdown summary of one rocprofv3 --pmc pass (per-dispatch medians for one kernel)
+    with the MFMA-busy fraction when the pass holds SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE: busy cycles summed over all SIMDs / (kernel cycles x SIMDs), where
+    GRBM_GUI_ACTIVE is summed over the XCDs."""
+    rows = [r for r in _read_csv(csv_path) if kernel_substr in r["Kernel_Name"]]
+    if not rows:
+        raise SystemExit(f"{csv_path}: no {kernel_substr} dispatches")
+    vals = {}
+    for r in rows:
+        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: float(np.median(v)) for k, v in vals.items()}
+    lines = [f"# {title}", "", "Command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):", "",
+             "```", command, "```", "", f"Kernel: `{rows[0]['Kernel_Name'][:100]}`, "
+             f"{len(vals[next(iter(vals))])} dispatches; per-dispatch medians:", "",
+             "| counter | median |", "|---|---|"]
+    lines += [f"| {k} | {v:.6g} |" for k, v in sorted(med.items())]
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
+        kcycles = med["GRBM_GUI_ACTIVE"] / xcds
+        busy = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (kcycles * simds)
+        lines += ["", f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} x {simds} SIMDs)"
+                      f" = {busy:.3f}"]
+        if "SQ_INSTS_MFMA" in med:
+            lines += [f"cycles per MFMA instruction per SIMD = "
+                      f"{med['SQ_VALU_MFMA_BUSY_CYCLES'] / med['SQ_INSTS_MFMA']:.2f}"]
+        if "SQ_INSTS_VALU" in med and "SQ_INSTS_MFMA" in med:
+            lines += [f"VALU instructions (MFMA included) per MFMA = "
+                      f"{med['SQ_INSTS_VALU'] / med['SQ_INSTS_MFMA']:.2f}"]
+    return "\n".join(lines) + "\n"
+
+
 def bench_policy(torch, fp4, workloads, steps):
     cfg = workloads.WORKLOADS["policy_stack"]
     m, k, n = cfg["m"], cfg["k"], cfg["n"]
@@ -405,9 +436,14 @@ def main():
                     metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "GROUP", "NAME"),
                     help="write profiles/NAME_traffic.json from two counter runs and exit")
     ap.add_argument("--commands", nargs="*", default=[], help="commands recorded with --summarize-traffic")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("PMC_CSV", "KERNEL", "TITLE", "COMMAND"),
+                    help="print a markdown summary of one rocprofv3 --pmc pass for one kernel and exit")
     args = ap.parse_args()
     if args.summarize_stats:
         sys.stdout.write(summarize_stats(*args.summarize_stats))
+        return
+    if args.summarize_counters:
+        sys.stdout.write(summarize_counters(*args.summarize_counters))
         return
     if args.summarize_traffic:
         rec = summarize_traffic(*args.summarize_traffic, commands=args.commands)
