@@ -2,9 +2,13 @@
 // elements; canonical or tiled output), dequantize, and the activation pass that feeds
 // the matrix kernels.
 //
-// Work mapping: 32 lanes own one 256-element group of one row, 8 consecutive elements
-// per lane (one 16-byte load for bf16, two for float32); a block covers 8 groups of a row. A 16-element micro-vector is a
-// lane pair, so its max is one cross-lane exchange; the group max is four more.
+// Work mapping (quantize and the activation pass): 16 lanes own one 256-element group of
+// one row, one 16-element micro-vector per lane (two 16-byte loads for bf16, four for
+// float32), so the block max is lane-local and the group max is four cross-lane
+// exchanges; the per-lane scale arithmetic (two correctly rounded divisions and two
+// round-to-nearest-even conversions) is amortized over 16 elements. A block of 256
+// threads covers 16 groups of a row. Dequantize keeps 32 lanes per group (8 elements
+// per lane, 8 groups per block).
 // Source of the method: "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for
 // Blackwell B200", section "The Mathematical Breakthrough of Microscopic FP4 Scaling".
 #include "fp4_device.h"
@@ -54,11 +58,45 @@ __device__ __forceinline__ float group_scales(const float v[8], float emax, uint
   return e4m3_value(mu_byte) * m_val;
 }
 
+template <int IN_BF16>
+__device__ __forceinline__ void load16(const void* __restrict__ x, int64_t off, float v[16]) {
+  load8<IN_BF16>(x, off, v);
+  load8<IN_BF16>(x, off + 8, v + 8);
+}
+
+// Scales of a lane that owns one whole micro-vector (16 lanes per group).
+__device__ __forceinline__ float block_scales(const float v[16], float emax, uint32_t& m_bits,
+                                              uint32_t& mu_byte, float& m_val) {
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
+  float amax_g = amax_b;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) amax_g = fmaxf(amax_g, __shfl_xor(amax_g, o));
+  m_bits = 0u;
+  m_val = 0.0f;
+  mu_byte = 0u;
+  if (amax_g > 0.0f) {
+    m_bits = fp16_rne_pos_clamped(amax_g / (emax * 448.0f));
+    m_val = fp16_value(m_bits);
+    mu_byte = e4m3_rne_pos(amax_b / (emax * m_val));
+  }
+  return e4m3_value(mu_byte) * m_val;
+}
+
 __device__ __forceinline__ uint32_t sign_of(float f) { return __float_as_uint(f) >> 31; }
 
 // Grid mapping shared by the kernels: a block of 256 threads covers 8 groups (32 lanes
 // each) of one row; block b is row b / gchunks, groups (b % gchunks) * 8 + 0..7, with
 // gchunks = ceil(groups / 8). One wave-uniform 32-bit division per thread.
+__device__ __forceinline__ bool seg_index16(int64_t groups, int64_t& r, int64_t& g) {
+  const uint32_t gchunks = (uint32_t)((groups + 15) >> 4);
+  const uint32_t b = blockIdx.x;
+  const uint32_t row = b / gchunks;
+  r = row;
+  g = (int64_t)(b - row * gchunks) * 16 + (threadIdx.x >> 4);
+  return g < groups;
+}
 __device__ __forceinline__ bool seg_index(int64_t groups, int64_t& r, int64_t& g) {
   const uint32_t gchunks = (uint32_t)((groups + 7) >> 3);
   const uint32_t b = blockIdx.x;
@@ -75,39 +113,43 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
                                                   uint8_t* __restrict__ micro,
                                                   uint16_t* __restrict__ macro) {
   const int64_t groups = k >> 8;
-  const int li = threadIdx.x & 31;
+  const int li = threadIdx.x & 15;  // micro-vector of the group
   int64_t r, g;
-  if (!seg_index(groups, r, g)) return;  // whole 32-lane segments leave together
-  const int64_t col = g * kGroup + li * 8;
+  if (!seg_index16(groups, r, g)) return;  // whole 16-lane segments leave together
+  const int64_t col = g * kGroup + li * 16;
 
-  float v[8];
-  load8<IN_BF16>(x, r * ldx + col, v);
+  float v[16];
+  load16<IN_BF16>(x, r * ldx + col, v);
   uint32_t m_bits, mu_byte;
   float m_val;
-  const float s = group_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
+  const float s = block_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
 
   if (!ELEM_E4M3) {
-    uint32_t word = 0u;
+    uint32_t w0 = 0u, w1 = 0u;
     if (s > 0.0f) {
       const E2M1Thresholds th(s);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        word |= (th.mag(fabsf(v[i])) | (sign_of(v[i]) << 3)) << (4 * i);
-    }
-    const int64_t off = TILED ? tiled_code_offset(r, col, groups) : r * (k >> 1) + (col >> 1);
-    *reinterpret_cast<uint32_t*>(codes + off) = word;
-  } else {
-    uint32_t lo = 0u, hi = 0u;
-    if (s > 0.0f) {
-#pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t b = e4m3_rne_pos(fabsf(v[i]) / s) | (sign_of(v[i]) << 7);
-        if (i < 4) lo |= b << (8 * i); else hi |= b << (8 * (i - 4));
+        w0 |= (th.mag(fabsf(v[i])) | (sign_of(v[i]) << 3)) << (4 * i);
+        w1 |= (th.mag(fabsf(v[8 + i])) | (sign_of(v[8 + i]) << 3)) << (4 * i);
       }
     }
-    *reinterpret_cast<uint2*>(codes + r * k + col) = make_uint2(lo, hi);
+    if (TILED) {
+      *reinterpret_cast<uint32_t*>(codes + tiled_code_offset(r, col, groups)) = w0;
+      *reinterpret_cast<uint32_t*>(codes + tiled_code_offset(r, col + 8, groups)) = w1;
+    } else {
+      *reinterpret_cast<uint2*>(codes + r * (k >> 1) + (col >> 1)) = make_uint2(w0, w1);
+    }
+  } else {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (s > 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        w[i >> 2] |= (e4m3_rne_pos(fabsf(v[i]) / s) | (sign_of(v[i]) << 7)) << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint4*>(codes + r * k + col) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  if ((li & 1) == 0) {
+  {
     const int64_t off = TILED ? tiled_micro_offset(r, col, groups) : r * (k >> 4) + (col >> 4);
     micro[off] = (uint8_t)mu_byte;
   }
@@ -175,51 +217,64 @@ __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, in
                                                   _Float16* __restrict__ aq, int64_t ldq,
                                                   float* __restrict__ scale) {
   const int64_t groups = k >> 8;
-  const int li = threadIdx.x & 31;
+  const int li = threadIdx.x & 15;
   int64_t r, g;
-  if (!seg_index(groups, r, g)) return;  // whole 32-lane segments leave together
-  const int64_t col = g * kGroup + li * 8;
+  if (!seg_index16(groups, r, g)) return;
+  const int64_t col = g * kGroup + li * 16;
 
-  float v[8];
-  load8<IN_BF16>(a, r * lda + col, v);
+  float v[16];
+  load16<IN_BF16>(a, r * lda + col, v);
   uint32_t m_bits, mu_byte;
   float m_val;
-  const float s = group_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
+  const float s = block_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
   const float mu = e4m3_value(mu_byte);
-  half2_t out[4];
+  half2_t out[8];
   if (!ELEM_E4M3) {
     // codes as in k_quantize, then decoded two at a time by the hardware conversion
     // (scale 1: exact) and multiplied by mu in FP16 (E2M1 * mu is exact in FP16)
-    uint32_t word = 0u;
+    uint32_t w0 = 0u, w1 = 0u;
     if (s > 0.0f) {
       const E2M1Thresholds th(s);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) word |= (th.mag(fabsf(v[i])) | (sign_of(v[i]) << 3)) << (4 * i);
+      for (int i = 0; i < 8; ++i) {
+        w0 |= (th.mag(fabsf(v[i])) | (sign_of(v[i]) << 3)) << (4 * i);
+        w1 |= (th.mag(fabsf(v[8 + i])) | (sign_of(v[8 + i]) << 3)) << (4 * i);
+      }
     }
     const _Float16 muh = (_Float16)mu;
     const half2_t m2 = {muh, muh};
-    out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * m2;
-    out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * m2;
-    out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * m2;
-    out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * m2;
+    out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0) * m2;
+    out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1) * m2;
+    out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2) * m2;
+    out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3) * m2;
+    out[4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 0) * m2;
+    out[5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 1) * m2;
+    out[6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 2) * m2;
+    out[7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3) * m2;
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
       const float e = s > 0.0f ? e4m3_value(e4m3_rne_pos(fabsf(v[i]) / s)) : 0.0f;
       const float mag = e * mu * 0.125f;
       const _Float16 h = (_Float16)(sign_of(v[i]) ? -mag : mag);
       if (i & 1) out[i >> 1][1] = h; else out[i >> 1][0] = h;
     }
   }
-  uint4 pk;
-  pk.x = __builtin_bit_cast(uint32_t, out[0]);
-  pk.y = __builtin_bit_cast(uint32_t, out[1]);
-  pk.z = __builtin_bit_cast(uint32_t, out[2]);
-  pk.w = __builtin_bit_cast(uint32_t, out[3]);
-  *reinterpret_cast<uint4*>(aq + r * ldq + col) = pk;
+  uint4* dst = reinterpret_cast<uint4*>(aq + r * ldq + col);
+  dst[0] = make_uint4(__builtin_bit_cast(uint32_t, out[0]), __builtin_bit_cast(uint32_t, out[1]),
+                      __builtin_bit_cast(uint32_t, out[2]), __builtin_bit_cast(uint32_t, out[3]));
+  dst[1] = make_uint4(__builtin_bit_cast(uint32_t, out[4]), __builtin_bit_cast(uint32_t, out[5]),
+                      __builtin_bit_cast(uint32_t, out[6]), __builtin_bit_cast(uint32_t, out[7]));
   // a group whose macro-scale is 0 has only zero operands: its factor is written as 1, so
   // the product kernel's factor ratios never divide by zero
   if (li == 0) scale[r * groups + g] = m_val > 0.0f ? (ELEM_E4M3 ? m_val * 8.0f : m_val) : 1.0f;
+}
+
+// one block per (row, run of 16 groups); see seg_index16. 0 when the grid would exceed
+// 2^32 work-items (the launchers then refuse the shape).
+inline unsigned blocks_for16(int64_t rows, int64_t k) {
+  const int64_t blocks = rows * (((k >> 8) + 15) >> 4);
+  return blocks <= (int64_t)0xFFFFFFFF / 256 ? (unsigned)blocks : 0u;
 }
 
 // one block per (row, run of 8 groups); see seg_index. 0 when the grid would exceed
@@ -236,7 +291,7 @@ namespace fp4lib {
 hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, int64_t ldx,
                            int elem_e4m3, int tiled, uint8_t* codes, uint8_t* micro,
                            uint16_t* macro, hipStream_t st) {
-  const dim3 grid(blocks_for(rows, k)), block(256);
+  const dim3 grid(blocks_for16(rows, k)), block(256);
   if (grid.x == 0) return hipErrorInvalidValue;
 #define FP4_Q(B, E, T) \
   hipLaunchKernelGGL((k_quantize<B, E, T>), grid, block, 0, st, x, ldx, rows, k, codes, micro, macro)
@@ -267,7 +322,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const u
 
 hipError_t launch_act_prep(const void* a, int in_bf16, int64_t rows, int64_t k, int64_t lda,
                            int elem_e4m3, _Float16* aq, int64_t ldq, float* scale, hipStream_t st) {
-  const dim3 grid(blocks_for(rows, k)), block(256);
+  const dim3 grid(blocks_for16(rows, k)), block(256);
   if (grid.x == 0) return hipErrorInvalidValue;
   if (in_bf16) {
     if (elem_e4m3) hipLaunchKernelGGL((k_act_prep<1, 1>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
