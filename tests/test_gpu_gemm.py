@@ -203,6 +203,26 @@ def test_moe_workload_full_size_subset_of_experts():
             bf16_gate(y2h[lo:hi], oracle.formats.bf16_round(r2))
 
 
+@pytest.mark.parametrize("act", [8, 4])
+def test_gemm_small_m_odd_groups(act):
+    """A small-m dense product with an odd group count (7) and ragged m and n: full
+    parity and bit-identical repeats."""
+    m, n, k = 150, 784, 1792
+    rng = np.random.default_rng(500 + act)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    a[:, rng.choice(k, 5, replace=False)] *= 50
+    a = workloads.to_bf16_values(a)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    print(f"[case] gemm small-m {ACTS[act]} m={m} n={n} k={k}", flush=True)
+    wq, ad = _wq(w), to_device_bf16(a)
+    ref = _oracle_c(a.astype(np.float64), w, act)
+    c1 = fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32)
+    f32_gate(host(c1), ref)
+    for _ in range(3):
+        assert torch.equal(c1, fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32))
+    bf16_gate(bf16_values(fp4.gemm_w4aX(act, ad, wq)), oracle.formats.bf16_round(ref))
+
+
 def test_gemm_deterministic():
     rng = np.random.default_rng(400)
     a = workloads.to_bf16_values(rng.standard_normal((300, 1024)).astype(np.float32))
