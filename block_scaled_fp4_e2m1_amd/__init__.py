@@ -6,7 +6,8 @@ memory and the current stream. There is no CPU path: if the library is missing o
 device is not gfx950 the calls raise.
 
 Names follow the C ABI: ``quantize_fp4``, ``dequantize_fp4``, ``gemm_w4aX``,
-``grouped_gemm_w4aX``, ``fp4_workspace_bytes``, ``fp4_policy_select``.
+``grouped_gemm_w4aX``, ``grouped_gemm_w4aX_gated``, ``moe_route``, ``moe_combine``,
+``fp4_workspace_bytes``, ``fp4_policy_select``.
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
 POLICY_AUTO, POLICY_Q4, POLICY_Q8 = 0, 4, 8
 
 EXPORTED = ["quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
+            "grouped_gemm_w4aX_gated", "moe_route", "moe_route_workspace_bytes", "moe_combine",
             "fp4_workspace_bytes", "fp4_policy_select", "fp4_status_string",
             "fp4_device_check"]
 
@@ -62,6 +64,11 @@ def library() -> ctypes.CDLL:
     lib.gemm_w4aX.argtypes = [i32, vp, i32, i64, i64, T, vp, i32, i64, vp, sz, vp]
     lib.grouped_gemm_w4aX.argtypes = [i32, vp, i32, i64, i64, vp, vp, i32, i64, T, vp, i32,
                                       i64, vp, sz, vp]
+    lib.grouped_gemm_w4aX_gated.argtypes = [i32, vp, i64, i64, vp, i32, T, vp, i32, i64, vp, sz, vp]
+    lib.moe_route_workspace_bytes.argtypes = [i32]
+    lib.moe_route_workspace_bytes.restype = sz
+    lib.moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_combine.argtypes = [vp, i32, i64, vp, vp, i64, i32, i64, vp, i32, i64, vp]
     lib.fp4_workspace_bytes.argtypes = [i32, i64, i64, i64]
     lib.fp4_workspace_bytes.restype = sz
     lib.fp4_policy_select.argtypes = [i32, i32]
@@ -70,7 +77,7 @@ def library() -> ctypes.CDLL:
     lib.fp4_status_string.restype = ctypes.c_char_p
     lib.fp4_device_check.argtypes = []
     for name in ("quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
-                 "fp4_device_check"):
+                 "grouped_gemm_w4aX_gated", "moe_route", "moe_combine", "fp4_device_check"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -205,3 +212,61 @@ def grouped_gemm_w4aX(act: int, a: torch.Tensor, row_token: torch.Tensor | None,
                                      _ptr(ws), wsb, _stream())
     _check(st, "grouped_gemm_w4aX")
     return c
+
+
+def grouped_gemm_w4aX_gated(act: int, gate_up: torch.Tensor, expert_offsets: torch.Tensor,
+                            n_experts: int, w: QTensor, out_dtype: torch.dtype = torch.bfloat16,
+                            out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Down product of a mixture-of-experts layer: rows of gate_up (bf16 [R x 2k], gate then
+    up) become h = bf16(silu(gate) * up), quantized (act A4 / A8) and multiplied by expert
+    e's weights (w stacked [n_experts * n x k]) for the rows of expert e."""
+    if gate_up.dim() != 2 or gate_up.stride(1) != 1:
+        raise ValueError("gate_up must be 2-D with contiguous rows")
+    rows, n = gate_up.shape[0], w.rows // n_experts
+    c = out if out is not None else torch.empty(rows, n, dtype=out_dtype, device=gate_up.device)
+    ws, wsb = _workspace(act, rows, n, w.k, gate_up.device, workspace)
+    ts = w.c_struct()
+    st = library().grouped_gemm_w4aX_gated(act, _ptr(gate_up), rows, gate_up.stride(0),
+                                           _ptr(expert_offsets), n_experts, ctypes.byref(ts),
+                                           _ptr(c), _dtype_code(c.dtype), c.stride(0), _ptr(ws),
+                                           wsb, _stream())
+    _check(st, "grouped_gemm_w4aX_gated")
+    return c
+
+
+def moe_route(logits: torch.Tensor, top_k: int, workspace: torch.Tensor | None = None):
+    """Float32 top-k routing. Returns (topk_ids int32 [T x k], topk_weights float32 [T x k],
+    expert_offsets int32 [E + 1], row_token int32 [T * k], token_rows int32 [T x k])."""
+    if logits.dim() != 2 or logits.dtype != torch.float32 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous float32 [tokens x experts] tensor")
+    t_count, e_count = logits.shape
+    dev = logits.device
+    ids = torch.empty(t_count, top_k, dtype=torch.int32, device=dev)
+    wts = torch.empty(t_count, top_k, dtype=torch.float32, device=dev)
+    offsets = torch.empty(e_count + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(t_count * top_k, dtype=torch.int32, device=dev)
+    token_rows = torch.empty(t_count, top_k, dtype=torch.int32, device=dev)
+    lib = library()
+    need = int(lib.moe_route_workspace_bytes(e_count))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib.moe_route(_ptr(logits), t_count, e_count, top_k, _ptr(ids), _ptr(wts), _ptr(offsets),
+                       _ptr(row_token), _ptr(token_rows), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "moe_route")
+    return ids, wts, offsets, row_token, token_rows
+
+
+def moe_combine(y: torch.Tensor, token_rows: torch.Tensor, topk_weights: torch.Tensor,
+                out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """out[t] = sum_j topk_weights[t, j] * y[token_rows[t, j]] (float32 sums, j in order)."""
+    if y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be 2-D with contiguous rows")
+    t_count, top_k = token_rows.shape
+    hidden = y.shape[1]
+    o = out if out is not None else torch.empty(t_count, hidden, dtype=out_dtype, device=y.device)
+    st = library().moe_combine(_ptr(y), _dtype_code(y.dtype), y.stride(0), _ptr(token_rows),
+                               _ptr(topk_weights), t_count, top_k, hidden, _ptr(o),
+                               _dtype_code(o.dtype), o.stride(0), _stream())
+    _check(st, "moe_combine")
+    return o

@@ -249,4 +249,96 @@ fp4_status grouped_gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_
   return launched(fp4lib::launch_gemm(g, st));
 }
 
+fp4_status grouped_gemm_w4aX_gated(int32_t act, const void* gate_up, int64_t rows, int64_t ld,
+                                   const int32_t* expert_offsets, int32_t n_experts,
+                                   const fp4_tensor* w, void* c, int32_t c_dtype, int64_t ldc,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_act(act)) return FP4_E_MODE;
+  if (act == FP4_A16) return FP4_E_DTYPE;  // the gated operand only exists quantized
+  if (!gate_up || !c || !expert_offsets) return FP4_E_NULL;
+  const fp4_status ws_ok = check_weights(w);
+  if (ws_ok != FP4_OK) return ws_ok;
+  if (!valid_dtype(c_dtype)) return FP4_E_DTYPE;
+  if (n_experts < 1 || w->rows % n_experts) return FP4_E_SHAPE;
+  const int64_t n = w->rows / n_experts, k = w->k;
+  if (n % 16 || rows < 0 || ld < 2 * k || ldc < n) return FP4_E_SHAPE;
+  if (!aligned16(gate_up) || (ld * 2) % 16) return FP4_E_ALIGN;
+  if (!aligned(c, dtype_size(c_dtype)) || !aligned(expert_offsets, 4)) return FP4_E_ALIGN;
+  const size_t need = act_workspace(act, rows, k);
+  if (rows > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return FP4_E_WORKSPACE;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  if (rows == 0) return FP4_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t ldq = act_ws_stride(k);
+  _Float16* aq = static_cast<_Float16*>(workspace);
+  float* scale = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                          (((size_t)rows * (size_t)ldq * 2 + 255) & ~(size_t)255));
+  if (fp4lib::launch_act_prep_gated(static_cast<const uint16_t*>(gate_up), rows, k, ld, act == FP4_A8,
+                                    aq, ldq, scale, st) != hipSuccess)
+    return FP4_E_HIP;
+  fp4lib::GemmArgs g{};
+  g.a = aq;
+  g.a_is_bf16 = 0;
+  g.lda = ldq;
+  g.a_scale = scale;
+  g.m = rows;
+  g.n = n;
+  g.k = k;
+  g.codes = static_cast<const uint8_t*>(w->codes);
+  g.micro = w->micro;
+  g.macro = w->macro;
+  g.c = c;
+  g.c_is_bf16 = c_dtype == FP4_BF16;
+  g.ldc = ldc;
+  g.row_token = nullptr;
+  g.expert_offsets = expert_offsets;
+  g.n_experts = n_experts;
+  return launched(fp4lib::launch_gemm(g, st));
+}
+
+size_t moe_route_workspace_bytes(int32_t n_experts) {
+  return n_experts < 1 ? 0 : (((size_t)n_experts * 4 + 255) & ~(size_t)255);
+}
+
+fp4_status moe_route(const float* logits, int64_t tokens, int32_t n_experts, int32_t top_k,
+                     int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                     int32_t* row_token, int32_t* token_rows, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!logits || !topk_ids || !topk_weights || !expert_offsets || !row_token || !token_rows)
+    return FP4_E_NULL;
+  if (tokens < 1 || tokens * (int64_t)top_k > 0x7FFFFFFF || !fp4lib::route_supports(n_experts, top_k))
+    return FP4_E_SHAPE;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
+      !aligned(expert_offsets, 4) || !aligned(row_token, 4) || !aligned(token_rows, 4))
+    return FP4_E_ALIGN;
+  if (!workspace || workspace_bytes < moe_route_workspace_bytes(n_experts) || !aligned(workspace, 256))
+    return FP4_E_WORKSPACE;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  return launched(fp4lib::launch_moe_route(logits, tokens, n_experts, top_k, topk_ids, topk_weights,
+                                           expert_offsets, row_token, token_rows,
+                                           static_cast<int32_t*>(workspace),
+                                           static_cast<hipStream_t>(stream)));
+}
+
+fp4_status moe_combine(const void* y, int32_t y_dtype, int64_t ldy, const int32_t* token_rows,
+                       const float* topk_weights, int64_t tokens, int32_t top_k, int64_t hidden,
+                       void* out, int32_t out_dtype, int64_t ldo, void* stream) {
+  if (!y || !token_rows || !topk_weights || !out) return FP4_E_NULL;
+  if (!valid_dtype(y_dtype) || !valid_dtype(out_dtype)) return FP4_E_DTYPE;
+  if (tokens < 1 || tokens > 0x7FFFFFFF || top_k < 1 || hidden < 8 || hidden % 8 || ldy < hidden ||
+      ldo < hidden)
+    return FP4_E_SHAPE;
+  if (!aligned16(y) || (ldy * (int64_t)dtype_size(y_dtype)) % 16 || !aligned16(out) ||
+      (ldo * (int64_t)dtype_size(out_dtype)) % 16 || !aligned(token_rows, 4) || !aligned(topk_weights, 4))
+    return FP4_E_ALIGN;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  return launched(fp4lib::launch_moe_combine(y, y_dtype == FP4_BF16, ldy, token_rows, topk_weights,
+                                             tokens, top_k, hidden, out, out_dtype == FP4_BF16, ldo,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -18,6 +18,11 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const u
 hipError_t launch_act_prep(const void* a, int in_bf16, int64_t rows, int64_t k, int64_t lda,
                            int elem_e4m3, _Float16* aq, int64_t ldq, float* scale, hipStream_t st);
 
+// Gated form: a row holds gate in [0, k) and up in [k, 2k) (bf16, row stride lda >= 2k);
+// the operand is h = bf16(silu(gate) * up).
+hipError_t launch_act_prep_gated(const uint16_t* a, int64_t rows, int64_t k, int64_t lda, int elem_e4m3,
+                                 _Float16* aq, int64_t ldq, float* scale, hipStream_t st);
+
 // Decode product for m <= 8 bf16 activation rows against tiled E2M1 weights [n x k].
 // Returns hipErrorInvalidValue when the shape is outside what the kernel covers.
 bool gemv_supports(int64_t m, int64_t n, int64_t k);
@@ -52,5 +57,18 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 hipError_t launch_gemm_f32act(const float* a, int64_t lda, int64_t m, int64_t k,
                               const uint8_t* codes, const uint8_t* micro, const uint16_t* macro,
                               int64_t n, void* c, int out_bf16, int64_t ldc, hipStream_t st);
+
+// Mixture-of-experts routing: top_k experts per token (float32 logits [tokens x E]),
+// softmax weights over the selected logits, routed rows ordered by (expert, token).
+// counts is int32 scratch [E]. hipErrorInvalidValue outside route_supports().
+bool route_supports(int n_experts, int top_k);
+hipError_t launch_moe_route(const float* logits, int64_t tokens, int n_experts, int top_k,
+                            int32_t* topk_ids, float* topk_w, int32_t* offsets, int32_t* row_token,
+                            int32_t* token_rows, int32_t* counts, hipStream_t st);
+
+// out[t, :] = sum_j w[t, j] * y[token_rows[t, j], :] (float32, j in order); hidden % 8 == 0.
+hipError_t launch_moe_combine(const void* y, int in_bf16, int64_t ldy, const int32_t* token_rows,
+                              const float* topk_w, int64_t tokens, int top_k, int64_t hidden,
+                              void* out, int out_bf16, int64_t ldo, hipStream_t st);
 
 }  // namespace fp4lib

@@ -1,0 +1,246 @@
+// Mixture-of-experts steps around the grouped product on gfx950: top-k routing with the
+// permutation of routed rows, and the weighted combine of the expert outputs.
+//
+// "llama.cpp Put Precision Policy Inside the Model", section "One model can need more
+// than one precision": the W4A4 / W4A8 routing covers mixture-of-experts products. The
+// router stays float32 (ClusterBid FP4 cost guide, section "Where Does FP4 Hurt
+// Accuracy?": routers are among the parts quantization hurts most).
+//
+// Routing (every step deterministic, no float atomics):
+//   1. k_route_topk: one wave per token. Each lane holds up to kMaxPerLane logits; k
+//      rounds of a wave-wide argmax (larger logit first, lower expert id on ties) pick the
+//      experts; weights are the softmax over the k selected logits, in float32.
+//   2. k_route_count: one workgroup per expert counts its tokens.
+//   3. k_route_scatter: one workgroup per expert: its first row is the sum of the
+//      counts of the experts before it; a block-wide scan over token order places each of
+//      its tokens (increasing token order) and writes row_token, token_rows and offsets.
+// Combine: out[t, :] = sum_j weight[t, j] * y[token_rows[t, j], :], float32 in rank order
+// j = 0 .. k-1, one thread per 8 consecutive columns of a token.
+#include "fp4_device.h"
+#include "fp4_kernels.h"
+
+using namespace fp4dev;
+
+namespace {
+
+constexpr int kMaxPerLane = 16;   // E <= 1024 experts
+constexpr int kRouteThreads = 256;
+
+__device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int64_t tokens,
+                                                    int n_experts, int top_k,
+                                                    int32_t* __restrict__ topk_ids,
+                                                    float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= tokens) return;  // whole waves leave together
+  // NaN ranks with -inf (below every number); a per-lane mask of taken experts makes each
+  // round pick a distinct valid expert whatever the logits hold, so the permutation below
+  // always covers every routed row.
+  float v[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    const float x = e < n_experts ? logits[t * n_experts + e] : -INFINITY;
+    v[i] = x == x ? x : -INFINITY;
+  }
+  uint32_t taken = 0;
+  // lane j keeps the j-th pick
+  float my_v = -INFINITY, v_max = 0.0f;
+  int my_e = 0;
+  for (int j = 0; j < top_k; ++j) {
+    // lane-local best (experts of this lane are lane, lane + 64, ...: increasing ids);
+    // the sentinel id loses to every untaken expert, -inf ones included
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      const int e = lane + 64 * i;
+      if (e < n_experts && !((taken >> i) & 1u) && better(v[i], e, bv, be)) { bv = v[i]; be = e; }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oe = __shfl_xor(be, o);
+      if (better(ov, oe, bv, be)) { bv = ov; be = oe; }
+    }
+    if (lane == j) { my_v = bv; my_e = be; }
+    if (j == 0) v_max = bv;
+    // the owning lane retires the chosen expert (top_k <= n_experts: one is always left)
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+  }
+  const float ex = lane < top_k ? expf(my_v - v_max) : 0.0f;
+  float sum = ex;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o);
+  if (lane < top_k) {
+    topk_ids[t * top_k + lane] = my_e;
+    topk_w[t * top_k + lane] = ex / sum;
+  }
+}
+
+// does token t route to expert e (and at which rank)
+__device__ __forceinline__ int rank_of(const int32_t* __restrict__ topk_ids, int64_t t, int top_k, int e) {
+  for (int j = 0; j < top_k; ++j)
+    if (topk_ids[t * top_k + j] == e) return j;
+  return -1;
+}
+
+// block-wide sum of one int per thread (256 threads)
+__device__ __forceinline__ int block_sum(int v, int* scratch) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const int total = scratch[0] + scratch[1] + scratch[2] + scratch[3];
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route_count(const int32_t* __restrict__ topk_ids,
+                                                               int64_t tokens, int top_k,
+                                                               int32_t* __restrict__ counts) {
+  __shared__ int scratch[4];
+  const int e = blockIdx.x;
+  int c = 0;
+  for (int64_t t = threadIdx.x; t < tokens; t += kRouteThreads) c += rank_of(topk_ids, t, top_k, e) >= 0;
+  c = block_sum(c, scratch);
+  if (threadIdx.x == 0) counts[e] = c;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* __restrict__ topk_ids,
+                                                                 int64_t tokens, int top_k,
+                                                                 int n_experts,
+                                                                 const int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ row_token,
+                                                                 int32_t* __restrict__ token_rows) {
+  __shared__ int scratch[4];
+  __shared__ int prefix[kRouteThreads];
+  const int e = blockIdx.x;
+  // first routed row of expert e
+  int before = 0;
+  for (int i = threadIdx.x; i < e; i += kRouteThreads) before += counts[i];
+  const int base = block_sum(before, scratch);
+  if (threadIdx.x == 0) {
+    offsets[e] = base;
+    if (e == n_experts - 1) offsets[n_experts] = base + counts[e];
+  }
+  // tokens in contiguous chunks per thread, chunks in thread order: a scan over the
+  // per-thread counts gives each token's rank among expert e's tokens
+  const int64_t chunk = (tokens + kRouteThreads - 1) / kRouteThreads;
+  const int64_t t0 = min((int64_t)threadIdx.x * chunk, tokens), t1 = min(t0 + chunk, tokens);
+  int mine = 0;
+  for (int64_t t = t0; t < t1; ++t) mine += rank_of(topk_ids, t, top_k, e) >= 0;
+  prefix[threadIdx.x] = mine;
+  __syncthreads();
+  // exclusive scan of 256 values by one wave (4 per lane)
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    const int a0 = prefix[4 * l], a1 = prefix[4 * l + 1], a2 = prefix[4 * l + 2], a3 = prefix[4 * l + 3];
+    const int s = a0 + a1 + a2 + a3;
+    int incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (l >= o) incl += y;
+    }
+    const int excl = incl - s;
+    prefix[4 * l] = excl;
+    prefix[4 * l + 1] = excl + a0;
+    prefix[4 * l + 2] = excl + a0 + a1;
+    prefix[4 * l + 3] = excl + a0 + a1 + a2;
+  }
+  __syncthreads();
+  int r = base + prefix[threadIdx.x];
+  for (int64_t t = t0; t < t1; ++t) {
+    const int j = rank_of(topk_ids, t, top_k, e);
+    if (j >= 0) {
+      row_token[r] = (int32_t)t;
+      token_rows[t * top_k + j] = r;
+      ++r;
+    }
+  }
+}
+
+template <int IN_BF16, int OUT_BF16>
+__global__ __launch_bounds__(256) void k_moe_combine(const void* __restrict__ y, int64_t ldy,
+                                                     const int32_t* __restrict__ token_rows,
+                                                     const float* __restrict__ topk_w,
+                                                     int64_t tokens, int top_k, int64_t hidden,
+                                                     void* __restrict__ out, int64_t ldo) {
+  const int64_t t = blockIdx.x;
+  const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8;
+  if (t >= tokens || c >= hidden) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < top_k; ++j) {
+    const int64_t r = token_rows[t * top_k + j];
+    const float w = topk_w[t * top_k + j];
+    float v[8];
+    if (IN_BF16) {
+      const uint4 p = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + r * ldy + c);
+      const uint32_t q[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(q[i] << 16);
+        v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(y) + r * ldy + c);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+  }
+  if (OUT_BF16) {
+    uint32_t q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = bf16_rne_bits(acc[2 * i]) | (bf16_rne_bits(acc[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + t * ldo + c) = make_uint4(q[0], q[1], q[2], q[3]);
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + t * ldo + c);
+    p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+}  // namespace
+
+namespace fp4lib {
+
+bool route_supports(int n_experts, int top_k) {
+  return n_experts >= 1 && n_experts <= 64 * kMaxPerLane && top_k >= 1 && top_k <= 16 &&
+         top_k <= n_experts;
+}
+
+hipError_t launch_moe_route(const float* logits, int64_t tokens, int n_experts, int top_k,
+                            int32_t* topk_ids, float* topk_w, int32_t* offsets, int32_t* row_token,
+                            int32_t* token_rows, int32_t* counts, hipStream_t st) {
+  if (!route_supports(n_experts, top_k) || tokens < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_route_topk, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, st, logits, tokens,
+                     n_experts, top_k, topk_ids, topk_w);
+  hipLaunchKernelGGL(k_route_count, dim3((unsigned)n_experts), dim3(kRouteThreads), 0, st, topk_ids,
+                     tokens, top_k, counts);
+  hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)n_experts), dim3(kRouteThreads), 0, st, topk_ids,
+                     tokens, top_k, n_experts, counts, offsets, row_token, token_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_combine(const void* y, int in_bf16, int64_t ldy, const int32_t* token_rows,
+                              const float* topk_w, int64_t tokens, int top_k, int64_t hidden,
+                              void* out, int out_bf16, int64_t ldo, hipStream_t st) {
+  if (hidden % 8 || tokens < 1 || tokens > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tokens, (unsigned)((hidden / 8 + 255) / 256)), block(256);
+#define FP4_COMB(I, O) \
+  hipLaunchKernelGGL((k_moe_combine<I, O>), grid, block, 0, st, y, ldy, token_rows, topk_w, tokens, top_k, hidden, out, ldo)
+  if (in_bf16) { if (out_bf16) FP4_COMB(1, 1); else FP4_COMB(1, 0); }
+  else { if (out_bf16) FP4_COMB(0, 1); else FP4_COMB(0, 0); }
+#undef FP4_COMB
+  return hipGetLastError();
+}
+
+}  // namespace fp4lib

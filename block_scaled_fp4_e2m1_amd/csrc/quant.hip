@@ -211,7 +211,11 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 // plus one float32 factor per 256-group (M, or 8*M for E4M3 elements; 1 for an all-zero
 // group), so that
 //   A_hat[r, c] = aq[r, c] * scale[r, c / 256]   exactly.
-template <int IN_BF16, int ELEM_E4M3>
+// GATED: the row of a holds gate in columns [0, k) and up in [k, 2k) (bf16); the operand
+// is h = bf16(silu(gate) * up), silu(x) = x / (1 + exp(-x)) in float32, quantized as
+// above (the SiLU-gated activation between a mixture-of-experts layer's gate/up and down
+// products, fused with the down product's dynamic quantization).
+template <int IN_BF16, int ELEM_E4M3, int GATED>
 __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, int64_t lda,
                                                   int64_t rows, int64_t k,
                                                   _Float16* __restrict__ aq, int64_t ldq,
@@ -224,6 +228,15 @@ __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, in
 
   float v[16];
   load16<IN_BF16>(a, r * lda + col, v);
+  if (GATED) {
+    float up[16];
+    load16<IN_BF16>(a, r * lda + k + col, up);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float h = v[i] / (1.0f + expf(-v[i])) * up[i];
+      v[i] = __uint_as_float(bf16_rne_bits(h) << 16);
+    }
+  }
   uint32_t m_bits, mu_byte;
   float m_val;
   const float s = block_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
@@ -324,13 +337,18 @@ hipError_t launch_act_prep(const void* a, int in_bf16, int64_t rows, int64_t k, 
                            int elem_e4m3, _Float16* aq, int64_t ldq, float* scale, hipStream_t st) {
   const dim3 grid(blocks_for16(rows, k)), block(256);
   if (grid.x == 0) return hipErrorInvalidValue;
-  if (in_bf16) {
-    if (elem_e4m3) hipLaunchKernelGGL((k_act_prep<1, 1>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
-    else hipLaunchKernelGGL((k_act_prep<1, 0>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
-  } else {
-    if (elem_e4m3) hipLaunchKernelGGL((k_act_prep<0, 1>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
-    else hipLaunchKernelGGL((k_act_prep<0, 0>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale);
-  }
+#define FP4_ACT(B, E, G) hipLaunchKernelGGL((k_act_prep<B, E, G>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale)
+  if (in_bf16) { if (elem_e4m3) FP4_ACT(1, 1, 0); else FP4_ACT(1, 0, 0); }
+  else { if (elem_e4m3) FP4_ACT(0, 1, 0); else FP4_ACT(0, 0, 0); }
+  return hipGetLastError();
+}
+
+hipError_t launch_act_prep_gated(const uint16_t* a, int64_t rows, int64_t k, int64_t lda, int elem_e4m3,
+                                 _Float16* aq, int64_t ldq, float* scale, hipStream_t st) {
+  const dim3 grid(blocks_for16(rows, k)), block(256);
+  if (grid.x == 0) return hipErrorInvalidValue;
+  if (elem_e4m3) FP4_ACT(1, 1, 1); else FP4_ACT(1, 0, 1);
+#undef FP4_ACT
   return hipGetLastError();
 }
 

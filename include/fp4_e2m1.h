@@ -147,6 +147,59 @@ fp4_status grouped_gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_
                              int32_t c_dtype, int64_t ldc, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * grouped_gemm_w4aX_gated -- the down product of a mixture-of-experts layer with the
+ * SiLU-gated activation fused into its dynamic activation quantization: for expert e and
+ * routed row r in [expert_offsets[e], expert_offsets[e+1]),
+ *     C[r, :] = Q(h[r, :]) . W_hat_e^T,   h = bf16(silu(gate) * up),  silu(x) = x/(1+e^-x)
+ * where gate = gate_up[r, 0:k] and up = gate_up[r, k:2k] (k = w->k), silu in float32, and Q
+ * is the FP4_A4 / FP4_A8 activation quantization of gemm_w4aX (FP4_A16: FP4_E_DTYPE).
+ *   gate_up        device bf16 [rows x 2k], row stride ld >= 2k (the gate/up product's
+ *                  output in routed-row order)
+ *   expert_offsets device int32 [n_experts + 1] as for grouped_gemm_w4aX, [n_experts] = rows
+ *   w              quantized down weights, experts stacked: rows = n_experts * n, TILED
+ *   c              device out [rows x n] (bf16/f32), stride ldc
+ *   workspace      >= fp4_workspace_bytes(act, rows, n, k)
+ * Source: llama.cpp precision-policy page, section "One model can need more than one
+ * precision" (W4A4 / W4A8 routing for mixture-of-experts operations). The pages fix no
+ * activation function; SiLU gating is the usual reading for gate/up experts.
+ */
+fp4_status grouped_gemm_w4aX_gated(int32_t act, const void* gate_up, int64_t rows, int64_t ld,
+                                   const int32_t* expert_offsets, int32_t n_experts,
+                                   const fp4_tensor* w, void* c, int32_t c_dtype, int64_t ldc,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route -- float32 top-k routing of a mixture-of-experts layer (the router is never
+ * quantized: ClusterBid FP4 cost guide, section "Where Does FP4 Hurt Accuracy?").
+ *   logits         device float32 [tokens x n_experts] (finite)
+ *   topk_ids       device out int32 [tokens x top_k]: experts by decreasing logit, equal
+ *                  logits in increasing expert id
+ *   topk_weights   device out float32 [tokens x top_k]: softmax over the selected logits
+ *   expert_offsets device out int32 [n_experts + 1]: routed rows of expert e are
+ *                  [offsets[e], offsets[e+1]), tokens in increasing order
+ *   row_token      device out int32 [tokens * top_k]: token of each routed row
+ *   token_rows     device out int32 [tokens x top_k]: routed row of each choice
+ *   workspace      >= moe_route_workspace_bytes(n_experts), 256-byte aligned
+ * 1 <= top_k <= min(16, n_experts), n_experts <= 1024 (FP4_E_SHAPE otherwise).
+ * Deterministic (no float atomics).
+ */
+size_t moe_route_workspace_bytes(int32_t n_experts);
+fp4_status moe_route(const float* logits, int64_t tokens, int32_t n_experts, int32_t top_k,
+                     int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                     int32_t* row_token, int32_t* token_rows, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * moe_combine -- out[t, :] = sum_j topk_weights[t, j] * y[token_rows[t, j], :], float32
+ * sums in rank order j = 0 .. top_k-1 (deterministic; a gather, no atomics).
+ *   y    device [routed rows x hidden] (bf16/f32), stride ldy; out device [tokens x hidden]
+ *   (bf16 round to nearest even / f32), stride ldo; hidden % 8 == 0, 16-byte aligned rows.
+ */
+fp4_status moe_combine(const void* y, int32_t y_dtype, int64_t ldy, const int32_t* token_rows,
+                       const float* topk_weights, int64_t tokens, int32_t top_k, int64_t hidden,
+                       void* out, int32_t out_dtype, int64_t ldo, void* stream);
+
 /* Bytes of device workspace gemm_w4aX / grouped_gemm_w4aX need (0 for FP4_A16). */
 size_t fp4_workspace_bytes(int32_t act, int64_t m_or_rows, int64_t n, int64_t k);
 

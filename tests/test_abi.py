@@ -103,6 +103,42 @@ def test_validation_happens_before_any_device_use(lib):
                                  256, fake, 1 << 30, null) == 1
 
 
+def test_moe_entry_points_validate_before_device_use(lib):
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)
+    null = vp(0)
+    T = lib_mod._Tensor
+    w = T(1 << 20, 1 << 21, 1 << 22, 512, 256, 0, 1)  # 2 experts x 256 rows, k = 256
+    # gated product: A16 has no gated form; gate_up row stride must hold gate and up
+    assert lib.grouped_gemm_w4aX_gated(16, fake, 64, 512, fake, 2, ctypes.byref(w), fake, 1, 256,
+                                       fake, 1 << 30, null) == 4
+    assert lib.grouped_gemm_w4aX_gated(4, fake, 64, 511, fake, 2, ctypes.byref(w), fake, 1, 256,
+                                       fake, 1 << 30, null) == 2
+    assert lib.grouped_gemm_w4aX_gated(4, fake, 64, 512, null, 2, ctypes.byref(w), fake, 1, 256,
+                                       fake, 1 << 30, null) == 1
+    assert lib.grouped_gemm_w4aX_gated(4, fake, 64, 512, fake, 3, ctypes.byref(w), fake, 1, 256,
+                                       fake, 1 << 30, null) == 2
+    assert lib.grouped_gemm_w4aX_gated(8, fake, 64, 512, fake, 2, ctypes.byref(w), fake, 1, 256,
+                                       null, 0, null) == 9
+    # routing: top_k within [1, min(16, E)], E <= 1024, workspace of E counters
+    assert lib.moe_route_workspace_bytes(128) == 512
+    assert lib.moe_route_workspace_bytes(0) == 0
+    ws = vp(1 << 24)
+    assert lib.moe_route(null, 8, 4, 2, fake, fake, fake, fake, fake, ws, 256, null) == 1
+    assert lib.moe_route(fake, 8, 4, 5, fake, fake, fake, fake, fake, ws, 256, null) == 2
+    assert lib.moe_route(fake, 8, 64, 17, fake, fake, fake, fake, fake, ws, 256, null) == 2
+    assert lib.moe_route(fake, 8, 1025, 2, fake, fake, fake, fake, fake, ws, 4096 + 256, null) == 2
+    assert lib.moe_route(fake, 0, 4, 2, fake, fake, fake, fake, fake, ws, 256, null) == 2
+    assert lib.moe_route(fake, 8, 128, 8, fake, fake, fake, fake, fake, ws, 256, null) == 9
+    assert lib.moe_route(vp((1 << 20) + 2), 8, 4, 2, fake, fake, fake, fake, fake, ws, 256, null) == 3
+    # combine: hidden a multiple of 8, 16-byte rows, known dtypes
+    assert lib.moe_combine(fake, 1, 512, fake, fake, 8, 2, 500, fake, 0, 512, null) == 2
+    assert lib.moe_combine(fake, 1, 516, fake, fake, 8, 2, 512, fake, 0, 512, null) == 3  # 1032-byte rows
+    assert lib.moe_combine(fake, 7, 512, fake, fake, 8, 2, 512, fake, 0, 512, null) == 4
+    assert lib.moe_combine(fake, 1, 512, null, fake, 8, 2, 512, fake, 0, 512, null) == 1
+    assert lib.moe_combine(fake, 1, 512, fake, fake, 8, 0, 512, fake, 0, 512, null) == 2
+
+
 def test_device_check_reports_missing_device(lib):
     import torch
     if torch.cuda.is_available():
