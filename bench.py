@@ -341,10 +341,13 @@ def bench_policy(torch, fp4, workloads, steps):
 
 
 def bench_moe(torch, fp4, workloads, steps):
+    """The whole mixture-of-experts layer on the device, one HIP graph per step: routing of
+    the float32 router logits, the gate/up grouped product (A4, rows gathered by token),
+    the SiLU-gated down product (A4) and the weighted combine. Each stage is also timed in
+    a graph of its own for the breakdown."""
     cfg = workloads.WORKLOADS["moe_w4a4"]
-    E, H, I, T = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["tokens"]
-    _, row_token, offsets, _ = workloads.moe_routing()
-    R = int(offsets[-1])
+    E, H, I, T, K = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["tokens"], cfg["top_k"]
+    R = T * K
     w1q = fp4.empty_qtensor(E * 2 * I, H, layout=fp4.LAYOUT_TILED)
     w2q = fp4.empty_qtensor(E * H, I, layout=fp4.LAYOUT_TILED)
     for e in range(E):
@@ -356,29 +359,51 @@ def bench_moe(torch, fp4, workloads, steps):
                               q.macro[e * rows * k // 256:(e + 1) * rows * k // 256],
                               rows, k, 0, fp4.LAYOUT_TILED)
             fp4.quantize_fp4(torch.from_numpy(wt).cuda(), layout=fp4.LAYOUT_TILED, out=sub)
+    logits = torch.from_numpy(workloads.moe_router_logits()).cuda()
     xd = torch.from_numpy(workloads.moe_tokens()).cuda().to(torch.bfloat16)
-    x2 = torch.from_numpy(workloads.moe_down_inputs(R)).cuda().to(torch.bfloat16)
-    rt = torch.from_numpy(row_token).cuda()
-    off = torch.from_numpy(offsets).cuda()
-    y1 = torch.empty(R, 2 * I, dtype=torch.bfloat16, device="cuda")
-    y2 = torch.empty(R, H, dtype=torch.bfloat16, device="cuda")
-    ws1 = torch.empty(fp4.fp4_workspace_bytes(fp4.A4, T, 2 * I, H), dtype=torch.uint8, device="cuda")
-    ws2 = torch.empty(fp4.fp4_workspace_bytes(fp4.A4, R, H, I), dtype=torch.uint8, device="cuda")
+    dev = xd.device
+    routed = (torch.empty(T, K, dtype=torch.int32, device=dev),
+              torch.empty(T, K, dtype=torch.float32, device=dev),
+              torch.empty(E + 1, dtype=torch.int32, device=dev),
+              torch.empty(R, dtype=torch.int32, device=dev),
+              torch.empty(T, K, dtype=torch.int32, device=dev))
+    _, wts, off, rt, tr = routed
+    wsr = torch.empty(max(256, fp4.library().moe_route_workspace_bytes(T, E)), dtype=torch.uint8, device=dev)
+    y1 = torch.empty(R, 2 * I, dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty(R, H, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    ws1 = torch.empty(fp4.fp4_workspace_bytes(fp4.A4, T, 2 * I, H), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(fp4.fp4_workspace_bytes(fp4.A4, R, H, I), dtype=torch.uint8, device=dev)
 
-    def step():
-        fp4.grouped_gemm_w4aX(fp4.A4, xd, rt, off, E, R, w1q, out=y1, workspace=ws1)
-        fp4.grouped_gemm_w4aX(fp4.A4, x2, None, off, E, R, w2q, out=y2, workspace=ws2)
-    step()
-    g = capture(torch, [step])
-    g.replay()
+    stages = {
+        "route": lambda: fp4.moe_route(logits, K, workspace=wsr, out=routed),
+        "gate_up": lambda: fp4.grouped_gemm_w4aX(fp4.A4, xd, rt, off, E, R, w1q, out=y1, workspace=ws1),
+        "gated_down": lambda: fp4.grouped_gemm_w4aX_gated(fp4.A4, y1, off, E, w2q, out=y2, workspace=ws2),
+        "combine": lambda: fp4.moe_combine(y2, tr, wts, out=out),
+    }
+
+    def layer():
+        for f in stages.values():
+            f()
+    layer()
     timer = Timer(torch)
-    secs = timer.region(g.replay, steps)
-    per = secs / steps
+    g = capture(torch, [layer])
+    g.replay()
+    per = timer.region(g.replay, steps) / steps
+    parts = {}
+    for name, f in stages.items():
+        gs = capture(torch, [f])
+        gs.replay()
+        parts[name + "_s"] = timer.region(gs.replay, steps) / steps
+    torch.cuda.synchronize()
+    counts = np.diff(off.cpu().numpy())
     flops = 2 * R * (2 * I) * H + 2 * R * H * I
-    tfl = flops / per / 1e12
-    counts = np.diff(offsets)
-    return dict(experts=E, top_k=cfg["top_k"], tokens=T, routed_rows=R, per_step_s=per, tflops=tfl,
-                frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
+    gemm_s = parts["gate_up_s"] + parts["gated_down_s"]
+    return dict(experts=E, top_k=K, tokens=T, hidden=H, inter=I, routed_rows=R,
+                layer_per_step_s=per, layer_tflops=flops / per / 1e12,
+                gemm_tflops=flops / gemm_s / 1e12,
+                frac_bf16_peak=flops / gemm_s / 1e12 / BF16_PEAK_TFLOPS,
+                stages=parts,
                 rows_per_expert=dict(min=int(counts.min()), max=int(counts.max()),
                                      mean=float(counts.mean())))
 

@@ -65,7 +65,7 @@ def library() -> ctypes.CDLL:
     lib.grouped_gemm_w4aX.argtypes = [i32, vp, i32, i64, i64, vp, vp, i32, i64, T, vp, i32,
                                       i64, vp, sz, vp]
     lib.grouped_gemm_w4aX_gated.argtypes = [i32, vp, i64, i64, vp, i32, T, vp, i32, i64, vp, sz, vp]
-    lib.moe_route_workspace_bytes.argtypes = [i32]
+    lib.moe_route_workspace_bytes.argtypes = [i64, i32]
     lib.moe_route_workspace_bytes.restype = sz
     lib.moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_combine.argtypes = [vp, i32, i64, vp, vp, i64, i32, i64, vp, i32, i64, vp]
@@ -235,20 +235,26 @@ def grouped_gemm_w4aX_gated(act: int, gate_up: torch.Tensor, expert_offsets: tor
     return c
 
 
-def moe_route(logits: torch.Tensor, top_k: int, workspace: torch.Tensor | None = None):
+def moe_route(logits: torch.Tensor, top_k: int, workspace: torch.Tensor | None = None,
+              out: tuple | None = None):
     """Float32 top-k routing. Returns (topk_ids int32 [T x k], topk_weights float32 [T x k],
-    expert_offsets int32 [E + 1], row_token int32 [T * k], token_rows int32 [T x k])."""
+    expert_offsets int32 [E + 1], row_token int32 [T * k], token_rows int32 [T x k]); with
+    ``out`` (a tuple of those five tensors) the results are written there."""
     if logits.dim() != 2 or logits.dtype != torch.float32 or not logits.is_contiguous():
         raise ValueError("logits must be a contiguous float32 [tokens x experts] tensor")
     t_count, e_count = logits.shape
     dev = logits.device
-    ids = torch.empty(t_count, top_k, dtype=torch.int32, device=dev)
-    wts = torch.empty(t_count, top_k, dtype=torch.float32, device=dev)
-    offsets = torch.empty(e_count + 1, dtype=torch.int32, device=dev)
-    row_token = torch.empty(t_count * top_k, dtype=torch.int32, device=dev)
-    token_rows = torch.empty(t_count, top_k, dtype=torch.int32, device=dev)
+    shapes = [((t_count, top_k), torch.int32), ((t_count, top_k), torch.float32),
+              ((e_count + 1,), torch.int32), ((t_count * top_k,), torch.int32),
+              ((t_count, top_k), torch.int32)]
+    if out is None:
+        out = tuple(torch.empty(shp, dtype=dt, device=dev) for shp, dt in shapes)
+    elif len(out) != 5 or any(tuple(o.shape) != shp or o.dtype != dt or not o.is_contiguous()
+                              for o, (shp, dt) in zip(out, shapes)):
+        raise ValueError("out must hold five contiguous tensors of the documented shapes and dtypes")
+    ids, wts, offsets, row_token, token_rows = out
     lib = library()
-    need = int(lib.moe_route_workspace_bytes(e_count))
+    need = int(lib.moe_route_workspace_bytes(t_count, e_count))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     st = lib.moe_route(_ptr(logits), t_count, e_count, top_k, _ptr(ids), _ptr(wts), _ptr(offsets),
@@ -262,6 +268,10 @@ def moe_combine(y: torch.Tensor, token_rows: torch.Tensor, topk_weights: torch.T
     """out[t] = sum_j topk_weights[t, j] * y[token_rows[t, j]] (float32 sums, j in order)."""
     if y.dim() != 2 or y.stride(1) != 1:
         raise ValueError("y must be 2-D with contiguous rows")
+    if (token_rows.dim() != 2 or token_rows.dtype != torch.int32 or not token_rows.is_contiguous()
+            or topk_weights.shape != token_rows.shape or topk_weights.dtype != torch.float32
+            or not topk_weights.is_contiguous()):
+        raise ValueError("token_rows (int32) and topk_weights (float32) must be contiguous [T x k]")
     t_count, top_k = token_rows.shape
     hidden = y.shape[1]
     o = out if out is not None else torch.empty(t_count, hidden, dtype=out_dtype, device=y.device)

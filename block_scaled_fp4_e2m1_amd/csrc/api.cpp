@@ -298,8 +298,8 @@ fp4_status grouped_gemm_w4aX_gated(int32_t act, const void* gate_up, int64_t row
   return launched(fp4lib::launch_gemm(g, st));
 }
 
-size_t moe_route_workspace_bytes(int32_t n_experts) {
-  return n_experts < 1 ? 0 : (((size_t)n_experts * 4 + 255) & ~(size_t)255);
+size_t moe_route_workspace_bytes(int64_t tokens, int32_t n_experts) {
+  return n_experts < 1 || tokens < 0 ? 0 : fp4lib::route_workspace_bytes(tokens, n_experts);
 }
 
 fp4_status moe_route(const float* logits, int64_t tokens, int32_t n_experts, int32_t top_k,
@@ -313,13 +313,13 @@ fp4_status moe_route(const float* logits, int64_t tokens, int32_t n_experts, int
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
       !aligned(expert_offsets, 4) || !aligned(row_token, 4) || !aligned(token_rows, 4))
     return FP4_E_ALIGN;
-  if (!workspace || workspace_bytes < moe_route_workspace_bytes(n_experts) || !aligned(workspace, 256))
+  if (!workspace || workspace_bytes < moe_route_workspace_bytes(tokens, n_experts) ||
+      !aligned(workspace, 256))
     return FP4_E_WORKSPACE;
   const fp4_status dev = check_device();
   if (dev != FP4_OK) return dev;
   return launched(fp4lib::launch_moe_route(logits, tokens, n_experts, top_k, topk_ids, topk_weights,
-                                           expert_offsets, row_token, token_rows,
-                                           static_cast<int32_t*>(workspace),
+                                           expert_offsets, row_token, token_rows, workspace,
                                            static_cast<hipStream_t>(stream)));
 }
 

@@ -60,11 +60,13 @@ hipError_t launch_gemm_f32act(const float* a, int64_t lda, int64_t m, int64_t k,
 
 // Mixture-of-experts routing: top_k experts per token (float32 logits [tokens x E]),
 // softmax weights over the selected logits, routed rows ordered by (expert, token).
-// counts is int32 scratch [E]. hipErrorInvalidValue outside route_supports().
+// workspace (256-byte aligned, route_workspace_bytes) holds the int32 expert counts and
+// a 64-bit-word expert mask per token. hipErrorInvalidValue outside route_supports().
 bool route_supports(int n_experts, int top_k);
+size_t route_workspace_bytes(int64_t tokens, int n_experts);
 hipError_t launch_moe_route(const float* logits, int64_t tokens, int n_experts, int top_k,
                             int32_t* topk_ids, float* topk_w, int32_t* offsets, int32_t* row_token,
-                            int32_t* token_rows, int32_t* counts, hipStream_t st);
+                            int32_t* token_rows, void* workspace, hipStream_t st);
 
 // out[t, :] = sum_j w[t, j] * y[token_rows[t, j], :] (float32, j in order); hidden % 8 == 0.
 hipError_t launch_moe_combine(const void* y, int in_bf16, int64_t ldy, const int32_t* token_rows,

@@ -6,14 +6,17 @@
 // router stays float32 (ClusterBid FP4 cost guide, section "Where Does FP4 Hurt
 // Accuracy?": routers are among the parts quantization hurts most).
 //
-// Routing (every step deterministic, no float atomics):
+// Routing (every step deterministic, no atomics):
 //   1. k_route_topk: one wave per token. Each lane holds up to kMaxPerLane logits; k
 //      rounds of a wave-wide argmax (larger logit first, lower expert id on ties) pick the
-//      experts; weights are the softmax over the k selected logits, in float32.
-//   2. k_route_count: one workgroup per expert counts its tokens.
-//   3. k_route_scatter: one workgroup per expert: its first row is the sum of the
-//      counts of the experts before it; a block-wide scan over token order places each of
-//      its tokens (increasing token order) and writes row_token, token_rows and offsets.
+//      experts; weights are the softmax over the k selected logits, in float32. The wave
+//      also writes the token's expert set as a bitmask (one 64-bit ballot per 64 experts).
+//   2. k_route_count: one workgroup per expert counts the tokens whose mask has its bit.
+//   3. k_route_scatter: one workgroup per expert: its first row is the sum of the counts
+//      of the experts before it; tokens are visited in rounds of 256 (thread i takes token
+//      256 * round + i), a block scan of the mask bits ranks each hit in token order, and
+//      the hit writes row_token, token_rows (its rank j among the token's choices) and the
+//      expert's offsets.
 // Combine: out[t, :] = sum_j weight[t, j] * y[token_rows[t, j], :], float32 in rank order
 // j = 0 .. k-1, one thread per 8 consecutive columns of a token.
 #include "fp4_device.h"
@@ -33,13 +36,15 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int64_t tokens,
                                                     int n_experts, int top_k,
                                                     int32_t* __restrict__ topk_ids,
-                                                    float* __restrict__ topk_w) {
+                                                    float* __restrict__ topk_w,
+                                                    uint64_t* __restrict__ mask) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= tokens) return;  // whole waves leave together
   // NaN ranks with -inf (below every number); a per-lane mask of taken experts makes each
   // round pick a distinct valid expert whatever the logits hold, so the permutation below
   // always covers every routed row.
+  const int words = (n_experts + 63) >> 6;
   float v[kMaxPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
@@ -58,6 +63,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
     int be = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
+      if (i >= words) break;  // uniform: slots past the last expert word hold nothing
       const int e = lane + 64 * i;
       if (e < n_experts && !((taken >> i) & 1u) && better(v[i], e, bv, be)) { bv = v[i]; be = e; }
     }
@@ -80,13 +86,13 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
     topk_ids[t * top_k + lane] = my_e;
     topk_w[t * top_k + lane] = ex / sum;
   }
-}
-
-// does token t route to expert e (and at which rank)
-__device__ __forceinline__ int rank_of(const int32_t* __restrict__ topk_ids, int64_t t, int top_k, int e) {
-  for (int j = 0; j < top_k; ++j)
-    if (topk_ids[t * top_k + j] == e) return j;
-  return -1;
+  // bit (e & 63) of word e >> 6: expert e = lane + 64 * i is taken by lane (e & 63)
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    if (i >= words) break;
+    const uint64_t b = __ballot((taken >> i) & 1u);
+    if (lane == i) mask[t * words + i] = b;
+  }
 }
 
 // block-wide sum of one int per thread (256 threads)
@@ -100,18 +106,27 @@ __device__ __forceinline__ int block_sum(int v, int* scratch) {
   return total;
 }
 
-__global__ __launch_bounds__(kRouteThreads) void k_route_count(const int32_t* __restrict__ topk_ids,
-                                                               int64_t tokens, int top_k,
+__device__ __forceinline__ int has_expert(const uint64_t* __restrict__ mask, int64_t t, int words, int e) {
+  return (int)((mask[t * words + (e >> 6)] >> (e & 63)) & 1u);
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route_count(const uint64_t* __restrict__ mask,
+                                                               int64_t tokens, int n_experts,
                                                                int32_t* __restrict__ counts) {
   __shared__ int scratch[4];
   const int e = blockIdx.x;
+  const int words = (n_experts + 63) >> 6;
   int c = 0;
-  for (int64_t t = threadIdx.x; t < tokens; t += kRouteThreads) c += rank_of(topk_ids, t, top_k, e) >= 0;
+#pragma unroll 8
+  for (int64_t t = threadIdx.x; t < tokens; t += kRouteThreads) c += has_expert(mask, t, words, e);
   c = block_sum(c, scratch);
   if (threadIdx.x == 0) counts[e] = c;
 }
 
+constexpr int kScanRounds = 32;  // rounds of 256 tokens per batch of the scatter
+
 __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* __restrict__ topk_ids,
+                                                                 const uint64_t* __restrict__ mask,
                                                                  int64_t tokens, int top_k,
                                                                  int n_experts,
                                                                  const int32_t* __restrict__ counts,
@@ -119,50 +134,65 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* 
                                                                  int32_t* __restrict__ row_token,
                                                                  int32_t* __restrict__ token_rows) {
   __shared__ int scratch[4];
-  __shared__ int prefix[kRouteThreads];
+  __shared__ int cnt[kScanRounds][4];        // hits per (round, wave)
+  __shared__ int round_base[kScanRounds + 1];  // first row of each round
   const int e = blockIdx.x;
+  const int words = (n_experts + 63) >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // first routed row of expert e
   int before = 0;
   for (int i = threadIdx.x; i < e; i += kRouteThreads) before += counts[i];
-  const int base = block_sum(before, scratch);
+  int base = block_sum(before, scratch);
   if (threadIdx.x == 0) {
     offsets[e] = base;
     if (e == n_experts - 1) offsets[n_experts] = base + counts[e];
   }
-  // tokens in contiguous chunks per thread, chunks in thread order: a scan over the
-  // per-thread counts gives each token's rank among expert e's tokens
-  const int64_t chunk = (tokens + kRouteThreads - 1) / kRouteThreads;
-  const int64_t t0 = min((int64_t)threadIdx.x * chunk, tokens), t1 = min(t0 + chunk, tokens);
-  int mine = 0;
-  for (int64_t t = t0; t < t1; ++t) mine += rank_of(topk_ids, t, top_k, e) >= 0;
-  prefix[threadIdx.x] = mine;
-  __syncthreads();
-  // exclusive scan of 256 values by one wave (4 per lane)
-  if (threadIdx.x < 64) {
-    const int l = threadIdx.x;
-    const int a0 = prefix[4 * l], a1 = prefix[4 * l + 1], a2 = prefix[4 * l + 2], a3 = prefix[4 * l + 3];
-    const int s = a0 + a1 + a2 + a3;
-    int incl = s;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t b0 = 0; b0 < tokens; b0 += (int64_t)kRouteThreads * kScanRounds) {
+    // all mask loads of the batch first (independent), one bit per round
+    uint32_t bits = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (l >= o) incl += y;
+    for (int i = 0; i < kScanRounds; ++i) {
+      const int64_t t = b0 + (int64_t)i * kRouteThreads + threadIdx.x;
+      if (t < tokens) bits |= (uint32_t)has_expert(mask, t, words, e) << i;
     }
-    const int excl = incl - s;
-    prefix[4 * l] = excl;
-    prefix[4 * l + 1] = excl + a0;
-    prefix[4 * l + 2] = excl + a0 + a1;
-    prefix[4 * l + 3] = excl + a0 + a1 + a2;
-  }
-  __syncthreads();
-  int r = base + prefix[threadIdx.x];
-  for (int64_t t = t0; t < t1; ++t) {
-    const int j = rank_of(topk_ids, t, top_k, e);
-    if (j >= 0) {
-      row_token[r] = (int32_t)t;
-      token_rows[t * top_k + j] = r;
-      ++r;
+#pragma unroll
+    for (int i = 0; i < kScanRounds; ++i) {
+      const uint64_t bal = __ballot((bits >> i) & 1u);
+      if (lane == 0) cnt[i][wave] = (int)__popcll(bal);
     }
+    __syncthreads();
+    if (wave == 0) {  // exclusive scan of the round totals
+      const int tot = lane < kScanRounds ? cnt[lane][0] + cnt[lane][1] + cnt[lane][2] + cnt[lane][3] : 0;
+      int incl = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      if (lane < kScanRounds) round_base[lane] = base + incl - tot;
+      if (lane == kScanRounds - 1) round_base[kScanRounds] = base + incl;
+    }
+    __syncthreads();
+    // token order = (round, wave, lane): rank = round start + earlier waves + earlier lanes
+#pragma unroll
+    for (int i = 0; i < kScanRounds; ++i) {
+      const uint32_t hit = (bits >> i) & 1u;
+      const uint64_t bal = __ballot(hit);
+      if (hit) {
+        int r = round_base[i] + (int)__popcll(bal & below);
+        for (int w = 0; w < wave; ++w) r += cnt[i][w];
+        const int64_t t = b0 + (int64_t)i * kRouteThreads + threadIdx.x;
+        int j = 0;  // the token's choice that is e (independent loads, no early exit)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (q < top_k && topk_ids[t * top_k + q] == e) j = q;
+        row_token[r] = (int32_t)t;
+        token_rows[t * top_k + j] = r;
+      }
+    }
+    base = round_base[kScanRounds];
+    __syncthreads();  // cnt and round_base are rewritten by the next batch
   }
 }
 
@@ -217,16 +247,24 @@ bool route_supports(int n_experts, int top_k) {
          top_k <= n_experts;
 }
 
+size_t route_workspace_bytes(int64_t tokens, int n_experts) {
+  const size_t counts = ((size_t)n_experts * 4 + 255) & ~(size_t)255;
+  return counts + (size_t)tokens * (size_t)((n_experts + 63) >> 6) * 8;
+}
+
 hipError_t launch_moe_route(const float* logits, int64_t tokens, int n_experts, int top_k,
                             int32_t* topk_ids, float* topk_w, int32_t* offsets, int32_t* row_token,
-                            int32_t* token_rows, int32_t* counts, hipStream_t st) {
+                            int32_t* token_rows, void* workspace, hipStream_t st) {
   if (!route_supports(n_experts, top_k) || tokens < 1) return hipErrorInvalidValue;
+  int32_t* counts = static_cast<int32_t*>(workspace);
+  uint64_t* mask = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) +
+                                               (((size_t)n_experts * 4 + 255) & ~(size_t)255));
   hipLaunchKernelGGL(k_route_topk, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, st, logits, tokens,
-                     n_experts, top_k, topk_ids, topk_w);
-  hipLaunchKernelGGL(k_route_count, dim3((unsigned)n_experts), dim3(kRouteThreads), 0, st, topk_ids,
-                     tokens, top_k, counts);
+                     n_experts, top_k, topk_ids, topk_w, mask);
+  hipLaunchKernelGGL(k_route_count, dim3((unsigned)n_experts), dim3(kRouteThreads), 0, st, mask,
+                     tokens, n_experts, counts);
   hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)n_experts), dim3(kRouteThreads), 0, st, topk_ids,
-                     tokens, top_k, n_experts, counts, offsets, row_token, token_rows);
+                     mask, tokens, top_k, n_experts, counts, offsets, row_token, token_rows);
   return hipGetLastError();
 }
 

@@ -6,9 +6,9 @@
 // one row, one 16-element micro-vector per lane (two 16-byte loads for bf16, four for
 // float32), so the block max is lane-local and the group max is four cross-lane
 // exchanges; the per-lane scale arithmetic (two correctly rounded divisions and two
-// round-to-nearest-even conversions) is amortized over 16 elements. A block of 256
-// threads covers 16 groups of a row. Dequantize keeps 32 lanes per group (8 elements
-// per lane, 8 groups per block).
+// round-to-nearest-even conversions) is amortized over 16 elements. The segments cover
+// the (row, group) pairs of the input in row-major order.
+// Dequantize keeps 32 lanes per group (8 elements per lane, 8 groups per block).
 // Source of the method: "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for
 // Blackwell B200", section "The Mathematical Breakthrough of Microscopic FP4 Scaling".
 #include "fp4_device.h"
@@ -18,50 +18,36 @@ using namespace fp4dev;
 
 namespace {
 
+// 16 consecutive input elements as raw 16-byte words, so that the next item's input can
+// be in flight while the current one is encoded.
 template <int IN_BF16>
-__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, float v[8]) {
-  if (IN_BF16) {
-    const uint4 p = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
-    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+struct Raw16 {
+  uint4 q[IN_BF16 ? 2 : 4];
+};
+
+template <int IN_BF16>
+__device__ __forceinline__ void load_raw16(const void* __restrict__ x, int64_t off, Raw16<IN_BF16>& d) {
+  const uint4* p = IN_BF16 ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off)
+                           : reinterpret_cast<const uint4*>(static_cast<const float*>(x) + off);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i) d.q[i] = p[i];
+}
+
+template <int IN_BF16>
+__device__ __forceinline__ void unpack16(const Raw16<IN_BF16>& d, float v[16]) {
+#pragma unroll
+  for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i) {
+    const uint32_t w[4] = {d.q[i].x, d.q[i].y, d.q[i].z, d.q[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (IN_BF16) {
+        v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      } else {
+        v[4 * i + j] = __uint_as_float(w[j]);
+      }
     }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
-}
-
-// Scales of the lane's group/block. Returns s = mu * M (exact); writes the FP16 bits of M
-// and the E4M3 byte of mu.
-__device__ __forceinline__ float group_scales(const float v[8], float emax, uint32_t& m_bits,
-                                              uint32_t& mu_byte, float& m_val) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const float amax_b = fmaxf(amax, __shfl_xor(amax, 1));
-  float amax_g = amax_b;
-#pragma unroll
-  for (int o = 2; o < 32; o <<= 1) amax_g = fmaxf(amax_g, __shfl_xor(amax_g, o));
-  m_bits = 0u;
-  m_val = 0.0f;
-  mu_byte = 0u;
-  if (amax_g > 0.0f) {
-    m_bits = fp16_rne_pos_clamped(amax_g / (emax * 448.0f));
-    m_val = fp16_value(m_bits);
-    mu_byte = e4m3_rne_pos(amax_b / (emax * m_val));
-  }
-  return e4m3_value(mu_byte) * m_val;
-}
-
-template <int IN_BF16>
-__device__ __forceinline__ void load16(const void* __restrict__ x, int64_t off, float v[16]) {
-  load8<IN_BF16>(x, off, v);
-  load8<IN_BF16>(x, off + 8, v + 8);
 }
 
 // Scales of a lane that owns one whole micro-vector (16 lanes per group).
@@ -86,16 +72,20 @@ __device__ __forceinline__ float block_scales(const float v[16], float emax, uin
 
 __device__ __forceinline__ uint32_t sign_of(float f) { return __float_as_uint(f) >> 31; }
 
-// Grid mapping shared by the kernels: a block of 256 threads covers 8 groups (32 lanes
-// each) of one row; block b is row b / gchunks, groups (b % gchunks) * 8 + 0..7, with
-// gchunks = ceil(groups / 8). One wave-uniform 32-bit division per thread.
-__device__ __forceinline__ bool seg_index16(int64_t groups, int64_t& r, int64_t& g) {
-  const uint32_t gchunks = (uint32_t)((groups + 15) >> 4);
-  const uint32_t b = blockIdx.x;
-  const uint32_t row = b / gchunks;
+// Grid mappings. Quantize and the activation pass: 16 lanes per 256-group; a block of 256
+// threads covers 16 consecutive (row, group) pairs of the row-major order
+// f = row * groups + group, so blocks stay full whatever the number of groups per row (a
+// block per row would leave most lanes idle for k = 768). (A capped grid walking the
+// pairs with the next pair's input in flight measured slower at every cap tried.)
+// Dequantize: 32 lanes per group, block b is row b / gchunks, groups
+// (b % gchunks) * 8 + 0..7, with gchunks = ceil(groups / 8).
+__device__ __forceinline__ bool seg_index16(int64_t rows, int64_t groups, int64_t& r, int64_t& g) {
+  const uint32_t f = blockIdx.x * 16u + (threadIdx.x >> 4);  // < 2^28: see blocks_for16
+  if ((int64_t)f >= rows * groups) return false;
+  const uint32_t row = f / (uint32_t)groups;
   r = row;
-  g = (int64_t)(b - row * gchunks) * 16 + (threadIdx.x >> 4);
-  return g < groups;
+  g = (int64_t)(f - row * (uint32_t)groups);
+  return true;
 }
 __device__ __forceinline__ bool seg_index(int64_t groups, int64_t& r, int64_t& g) {
   const uint32_t gchunks = (uint32_t)((groups + 7) >> 3);
@@ -106,20 +96,13 @@ __device__ __forceinline__ bool seg_index(int64_t groups, int64_t& r, int64_t& g
   return g < groups;
 }
 
-template <int IN_BF16, int ELEM_E4M3, int TILED>
-__global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t ldx,
-                                                  int64_t rows, int64_t k,
-                                                  uint8_t* __restrict__ codes,
-                                                  uint8_t* __restrict__ micro,
-                                                  uint16_t* __restrict__ macro) {
-  const int64_t groups = k >> 8;
-  const int li = threadIdx.x & 15;  // micro-vector of the group
-  int64_t r, g;
-  if (!seg_index16(groups, r, g)) return;  // whole 16-lane segments leave together
+// Encodes one micro-vector (v, 16 elements of row r at column col) and stores its codes,
+// micro-scale and (lane 0 of the group) macro-scale.
+template <int ELEM_E4M3, int TILED>
+__device__ __forceinline__ void quantize_item(const float v[16], int64_t r, int64_t g, int li,
+                                              int64_t k, int64_t groups, uint8_t* __restrict__ codes,
+                                              uint8_t* __restrict__ micro, uint16_t* __restrict__ macro) {
   const int64_t col = g * kGroup + li * 16;
-
-  float v[16];
-  load16<IN_BF16>(x, r * ldx + col, v);
   uint32_t m_bits, mu_byte;
   float m_val;
   const float s = block_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
@@ -157,6 +140,23 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
     const int64_t off = TILED ? tiled_macro_offset(r, col, groups) : r * groups + g;
     macro[off] = (uint16_t)m_bits;
   }
+}
+
+template <int IN_BF16, int ELEM_E4M3, int TILED>
+__global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t ldx,
+                                                  int64_t rows, int64_t k,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ micro,
+                                                  uint16_t* __restrict__ macro) {
+  const int64_t groups = k >> 8;
+  const int li = threadIdx.x & 15;  // micro-vector of the group
+  int64_t r, g;
+  if (!seg_index16(rows, groups, r, g)) return;  // whole 16-lane segments leave together
+  Raw16<IN_BF16> raw;
+  load_raw16<IN_BF16>(x, r * ldx + g * kGroup + li * 16, raw);
+  float v[16];
+  unpack16<IN_BF16>(raw, v);
+  quantize_item<ELEM_E4M3, TILED>(v, r, g, li, k, groups, codes, micro, macro);
 }
 
 template <int OUT_BF16, int ELEM_E4M3, int TILED>
@@ -212,31 +212,17 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 // group), so that
 //   A_hat[r, c] = aq[r, c] * scale[r, c / 256]   exactly.
 // GATED: the row of a holds gate in columns [0, k) and up in [k, 2k) (bf16); the operand
-// is h = bf16(silu(gate) * up), silu(x) = x / (1 + exp(-x)) in float32, quantized as
+// is h = bf16(silu(gate) * up), silu(x) = x / (1 + exp(-x)) in float32 (hardware exp and
+// reciprocal approximations), quantized as
 // above (the SiLU-gated activation between a mixture-of-experts layer's gate/up and down
 // products, fused with the down product's dynamic quantization).
-template <int IN_BF16, int ELEM_E4M3, int GATED>
-__global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, int64_t lda,
-                                                  int64_t rows, int64_t k,
-                                                  _Float16* __restrict__ aq, int64_t ldq,
-                                                  float* __restrict__ scale) {
-  const int64_t groups = k >> 8;
-  const int li = threadIdx.x & 15;
-  int64_t r, g;
-  if (!seg_index16(groups, r, g)) return;
+// Encodes one micro-vector of the activation pass (v, 16 elements of row r at column col)
+// into the FP16 operand and, from lane 0 of the group, the group factor.
+template <int ELEM_E4M3>
+__device__ __forceinline__ void act_item(float v[16], int64_t r, int64_t g, int li, int64_t groups,
+                                         _Float16* __restrict__ aq, int64_t ldq,
+                                         float* __restrict__ scale) {
   const int64_t col = g * kGroup + li * 16;
-
-  float v[16];
-  load16<IN_BF16>(a, r * lda + col, v);
-  if (GATED) {
-    float up[16];
-    load16<IN_BF16>(a, r * lda + k + col, up);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float h = v[i] / (1.0f + expf(-v[i])) * up[i];
-      v[i] = __uint_as_float(bf16_rne_bits(h) << 16);
-    }
-  }
   uint32_t m_bits, mu_byte;
   float m_val;
   const float s = block_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
@@ -283,10 +269,39 @@ __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, in
   if (li == 0) scale[r * groups + g] = m_val > 0.0f ? (ELEM_E4M3 ? m_val * 8.0f : m_val) : 1.0f;
 }
 
-// one block per (row, run of 16 groups); see seg_index16. 0 when the grid would exceed
-// 2^32 work-items (the launchers then refuse the shape).
+template <int IN_BF16, int ELEM_E4M3, int GATED>
+__global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, int64_t lda,
+                                                  int64_t rows, int64_t k,
+                                                  _Float16* __restrict__ aq, int64_t ldq,
+                                                  float* __restrict__ scale) {
+  const int64_t groups = k >> 8;
+  const int li = threadIdx.x & 15;
+  int64_t r, g;
+  if (!seg_index16(rows, groups, r, g)) return;
+  Raw16<IN_BF16> raw;
+  load_raw16<IN_BF16>(a, r * lda + g * kGroup + li * 16, raw);
+  float v[16];
+  unpack16<IN_BF16>(raw, v);
+  if (GATED) {
+    // h = bf16(silu(gate) * up); exp and reciprocal by the hardware approximations (a few
+    // float32 ulp, far below the bf16 step h is rounded to)
+    Raw16<IN_BF16> raw_up;
+    load_raw16<IN_BF16>(a, r * lda + k + g * kGroup + li * 16, raw_up);
+    float up[16];
+    unpack16<IN_BF16>(raw_up, up);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float h = v[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-v[i])) * up[i];
+      v[i] = __uint_as_float(bf16_rne_bits(h) << 16);
+    }
+  }
+  act_item<ELEM_E4M3>(v, r, g, li, groups, aq, ldq, scale);
+}
+
+// one block per 16 (row, group) pairs; 0 when the grid would exceed 2^32 work-items (the
+// launchers then refuse the shape).
 inline unsigned blocks_for16(int64_t rows, int64_t k) {
-  const int64_t blocks = rows * (((k >> 8) + 15) >> 4);
+  const int64_t blocks = (rows * (k >> 8) + 15) >> 4;
   return blocks <= (int64_t)0xFFFFFFFF / 256 ? (unsigned)blocks : 0u;
 }
 

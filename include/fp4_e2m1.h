@@ -152,7 +152,8 @@ fp4_status grouped_gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_
  * SiLU-gated activation fused into its dynamic activation quantization: for expert e and
  * routed row r in [expert_offsets[e], expert_offsets[e+1]),
  *     C[r, :] = Q(h[r, :]) . W_hat_e^T,   h = bf16(silu(gate) * up),  silu(x) = x/(1+e^-x)
- * where gate = gate_up[r, 0:k] and up = gate_up[r, k:2k] (k = w->k), silu in float32, and Q
+ * where gate = gate_up[r, 0:k] and up = gate_up[r, k:2k] (k = w->k), silu in float32 (the
+ * exponential and reciprocal by the hardware approximations, a few ulp), and Q
  * is the FP4_A4 / FP4_A8 activation quantization of gemm_w4aX (FP4_A16: FP4_E_DTYPE).
  *   gate_up        device bf16 [rows x 2k], row stride ld >= 2k (the gate/up product's
  *                  output in routed-row order)
@@ -172,7 +173,9 @@ fp4_status grouped_gemm_w4aX_gated(int32_t act, const void* gate_up, int64_t row
 /*
  * moe_route -- float32 top-k routing of a mixture-of-experts layer (the router is never
  * quantized: ClusterBid FP4 cost guide, section "Where Does FP4 Hurt Accuracy?").
- *   logits         device float32 [tokens x n_experts] (finite)
+ *   logits         device float32 [tokens x n_experts]; -inf masks an expert out (it
+ *                  ranks last, weight 0); NaN ranks with -inf, so the outputs always
+ *                  stay a valid routing (the weights are then unspecified)
  *   topk_ids       device out int32 [tokens x top_k]: experts by decreasing logit, equal
  *                  logits in increasing expert id
  *   topk_weights   device out float32 [tokens x top_k]: softmax over the selected logits
@@ -180,11 +183,12 @@ fp4_status grouped_gemm_w4aX_gated(int32_t act, const void* gate_up, int64_t row
  *                  [offsets[e], offsets[e+1]), tokens in increasing order
  *   row_token      device out int32 [tokens * top_k]: token of each routed row
  *   token_rows     device out int32 [tokens x top_k]: routed row of each choice
- *   workspace      >= moe_route_workspace_bytes(n_experts), 256-byte aligned
- * 1 <= top_k <= min(16, n_experts), n_experts <= 1024 (FP4_E_SHAPE otherwise).
- * Deterministic (no float atomics).
+ *   workspace      >= moe_route_workspace_bytes(tokens, n_experts), 256-byte aligned
+ *                  (expert counts and one bit per (token, expert))
+ * 1 <= top_k <= min(16, n_experts), n_experts <= 1024, tokens * top_k < 2^31
+ * (FP4_E_SHAPE otherwise). Deterministic (no atomics). Buffers are caller-owned.
  */
-size_t moe_route_workspace_bytes(int32_t n_experts);
+size_t moe_route_workspace_bytes(int64_t tokens, int32_t n_experts);
 fp4_status moe_route(const float* logits, int64_t tokens, int32_t n_experts, int32_t top_k,
                      int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
                      int32_t* row_token, int32_t* token_rows, void* workspace,

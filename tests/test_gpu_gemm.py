@@ -125,7 +125,8 @@ def test_policy_stack_full_size_sampled(mode):
 
 
 def _grouped_case(act, tokens, experts, top_k, k, n, seed, with_token_map=True):
-    _, row_token, offsets, _ = workloads.moe_routing(tokens=tokens, experts=experts, top_k=top_k, seed=seed)
+    logits = workloads.moe_router_logits(tokens=tokens, experts=experts, seed=seed)
+    _, _, offsets, row_token, _ = oracle.route(logits, top_k)
     rng = np.random.default_rng(seed)
     a = rng.standard_normal((tokens, k)).astype(np.float32)
     a[:, rng.choice(k, 2, replace=False)] *= 50
@@ -165,7 +166,7 @@ def test_grouped_empty_expert_and_many_experts():
 def test_moe_workload_full_size_subset_of_experts():
     cfg = workloads.WORKLOADS["moe_w4a4"]
     E, H, I, T = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["tokens"]
-    _, row_token, offsets, _ = workloads.moe_routing()
+    _, _, offsets, row_token, _ = oracle.route(workloads.moe_router_logits(), cfg["top_k"])
     R = int(offsets[-1])
     x = workloads.moe_tokens()
     counts = np.diff(offsets)

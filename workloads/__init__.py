@@ -20,7 +20,7 @@ import math
 import numpy as np
 
 __all__ = ["normal", "to_bf16_values", "outlier_channels", "tiny", "decode", "prefill",
-           "policy_flags", "policy_outliers", "policy_layer", "moe_routing", "moe_tokens",
+           "policy_flags", "policy_outliers", "policy_layer", "moe_router_logits", "moe_tokens",
            "moe_expert_weights", "moe_down_inputs", "WORKLOADS"]
 
 WORKLOADS = {
@@ -105,21 +105,11 @@ def policy_layer(layer: int, m=512, k=5120, n=5120, seed=3, outlier_frac=0.005,
     return w, to_bf16_values(x)
 
 
-def moe_routing(tokens=4096, experts=128, top_k=8, seed=4):
-    """Router logits N(0, 1) fp32 [tokens, experts]; each token goes to its top_k experts
-    (softmax is monotone, so this is top_k of the logits; ties -> lower expert id).
-    Routed rows are ordered by (expert, token).
-    Returns (logits, row_token int32 [R], offsets int32 [E + 1], topk_ids [T, top_k])."""
-    logits = normal(_child(seed, 0), 1.0, (tokens, experts))
-    order = np.lexsort((np.arange(experts)[None, :].repeat(tokens, 0), -logits), axis=1)
-    topk = order[:, :top_k]
-    tok = np.repeat(np.arange(tokens), top_k)
-    exp = topk.reshape(-1)
-    perm = np.lexsort((tok, exp))
-    row_token = tok[perm].astype(np.int32)
-    counts = np.bincount(exp, minlength=experts)
-    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    return logits, row_token, offsets, topk.astype(np.int32)
+def moe_router_logits(tokens=4096, experts=128, seed=4):
+    """Router logits fp32 [tokens, experts] ~ N(0, 1). (The routing itself, top-k with its
+    softmax weights and the permutation of routed rows, is a step of the layer: the oracle
+    and the library each compute it from these logits.)"""
+    return normal(_child(seed, 0), 1.0, (tokens, experts))
 
 
 def moe_tokens(tokens=4096, hidden=2048, seed=4, outlier_frac=0.005, outlier_gain=50.0):
@@ -140,6 +130,6 @@ def moe_expert_weights(expert: int, hidden=2048, inter=768, seed=4):
 
 
 def moe_down_inputs(rows: int, inter=768, seed=4):
-    """Inputs of the down projection, bf16 [rows, inter] ~ N(0, 1) (the gate/up ->
-    down activation function is outside the grouped product)."""
+    """Stand-in inputs of the down projection alone, bf16 [rows, inter] ~ N(0, 1) (for
+    tests of the plain grouped product; the layer itself feeds it silu(gate) * up)."""
     return to_bf16_values(normal(_child(seed, 3), 1.0, (rows, inter)))
