@@ -61,7 +61,7 @@ hipError_t launch_gemm_f32act(const float* a, int64_t lda, int64_t m, int64_t k,
 // Mixture-of-experts routing: top_k experts per token (float32 logits [tokens x E]),
 // softmax weights over the selected logits, routed rows ordered by (expert, token).
 // workspace (256-byte aligned, route_workspace_bytes) holds the int32 expert counts and
-// a 64-bit-word expert mask per token. hipErrorInvalidValue outside route_supports().
+// five 64-bit-word bit-planes per token and 64 experts (chosen, 4 rank bits). hipErrorInvalidValue outside route_supports().
 bool route_supports(int n_experts, int top_k);
 size_t route_workspace_bytes(int64_t tokens, int n_experts);
 hipError_t launch_moe_route(const float* logits, int64_t tokens, int n_experts, int top_k,

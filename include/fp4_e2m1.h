@@ -184,7 +184,7 @@ fp4_status grouped_gemm_w4aX_gated(int32_t act, const void* gate_up, int64_t row
  *   row_token      device out int32 [tokens * top_k]: token of each routed row
  *   token_rows     device out int32 [tokens x top_k]: routed row of each choice
  *   workspace      >= moe_route_workspace_bytes(tokens, n_experts), 256-byte aligned
- *                  (expert counts and one bit per (token, expert))
+ *                  (expert counts, and five bits per (token, expert): chosen, rank)
  * 1 <= top_k <= min(16, n_experts), n_experts <= 1024, tokens * top_k < 2^31
  * (FP4_E_SHAPE otherwise). Deterministic (no atomics). Buffers are caller-owned.
  */

@@ -121,9 +121,9 @@ def test_moe_entry_points_validate_before_device_use(lib):
     assert lib.grouped_gemm_w4aX_gated(8, fake, 64, 512, fake, 2, ctypes.byref(w), fake, 1, 256,
                                        null, 0, null) == 9
     # routing: top_k within [1, min(16, E)], E <= 1024; workspace = E counters (256-byte
-    # aligned) + one 64-bit mask word per token and 64 experts
-    assert lib.moe_route_workspace_bytes(4096, 128) == 512 + 4096 * 2 * 8
-    assert lib.moe_route_workspace_bytes(10, 65) == 512 + 10 * 2 * 8
+    # aligned) + five 64-bit plane words per token and 64 experts
+    assert lib.moe_route_workspace_bytes(4096, 128) == 512 + 4096 * 2 * 8 * 5
+    assert lib.moe_route_workspace_bytes(10, 65) == 512 + 10 * 2 * 8 * 5
     assert lib.moe_route_workspace_bytes(10, 0) == 0
     ws, big = vp(1 << 24), 1 << 20
     assert lib.moe_route(null, 8, 4, 2, fake, fake, fake, fake, fake, ws, big, null) == 1
@@ -132,7 +132,7 @@ def test_moe_entry_points_validate_before_device_use(lib):
     assert lib.moe_route(fake, 8, 1025, 2, fake, fake, fake, fake, fake, ws, big, null) == 2
     assert lib.moe_route(fake, 0, 4, 2, fake, fake, fake, fake, fake, ws, big, null) == 2
     assert lib.moe_route(fake, 1 << 28, 128, 8, fake, fake, fake, fake, fake, ws, big, null) == 2
-    assert lib.moe_route(fake, 8, 128, 8, fake, fake, fake, fake, fake, ws, 512 + 8 * 16 - 1, null) == 9
+    assert lib.moe_route(fake, 8, 128, 8, fake, fake, fake, fake, fake, ws, 512 + 8 * 80 - 1, null) == 9
     assert lib.moe_route(fake, 8, 128, 8, fake, fake, fake, fake, fake, vp((1 << 24) + 16), big, null) == 9
     assert lib.moe_route(vp((1 << 20) + 2), 8, 4, 2, fake, fake, fake, fake, fake, ws, big, null) == 3
     # combine: hidden a multiple of 8, 16-byte rows, known dtypes
