@@ -1,7 +1,7 @@
 """CPU oracle for two-level block-scaled FP4 (E2M1 elements, E4M3 micro-scales per 16,
-FP16 macro-scales per 256), the W4A16 / W4A8 / W4A4 products built on it, and the
+FP16 macro-scales per 256), the W4A16 / W4A8 / W4A4 products built on it, the
 mixture-of-experts layer steps around the grouped product (routing, gated activation,
-combine).
+combine), and decode attention over a KV cache kept in the same format.
 
 TEST INFRASTRUCTURE ONLY. A plain, slow, float64 numpy restatement of the method that
 the HIP library is checked against. It shares no code with the library. Only tests,
@@ -17,3 +17,4 @@ from .quant import (quantize, dequantize, pack_e2m1, unpack_e2m1, element_values
 from .gemm import (activation_values, gemm, gemm_bf16, grouped_gemm, policy_select,
                    A16, A8, A4, POLICY_AUTO, POLICY_Q4, POLICY_Q8)
 from .moe import route, silu_gate, combine
+from .attention import kv_quantize_rows, kv_dequantize_rows, attention_decode
