@@ -7,7 +7,8 @@ device is not gfx950 the calls raise.
 
 Names follow the C ABI: ``quantize_fp4``, ``dequantize_fp4``, ``gemm_w4aX``,
 ``grouped_gemm_w4aX``, ``grouped_gemm_w4aX_gated``, ``moe_route``, ``moe_combine``,
-``fp4_workspace_bytes``, ``fp4_policy_select``.
+``kv_cache_append``, ``attention_decode_fp4kv``, ``fp4_workspace_bytes``,
+``fp4_policy_select``.
 """
 from __future__ import annotations
 
@@ -30,7 +31,9 @@ POLICY_AUTO, POLICY_Q4, POLICY_Q8 = 0, 4, 8
 EXPORTED = ["quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
             "grouped_gemm_w4aX_gated", "moe_route", "moe_route_workspace_bytes", "moe_combine",
             "fp4_workspace_bytes", "fp4_policy_select", "fp4_status_string",
-            "fp4_device_check"]
+            "fp4_device_check", "fp4_kv_cache_bytes", "kv_cache_append",
+            "attention_workspace_bytes", "attention_decode_fp4kv"]
+KV_CODES, KV_MICRO, KV_MACRO = 0, 1, 2
 
 
 class Fp4Error(RuntimeError):
@@ -43,6 +46,14 @@ class _Tensor(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("micro", ctypes.c_void_p),
                 ("macro", ctypes.c_void_p), ("rows", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("elem", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+class _KvCache(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("k_micro", ctypes.c_void_p),
+                ("k_macro", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("v_micro", ctypes.c_void_p), ("v_macro", ctypes.c_void_p),
+                ("n_seq", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
 
 
 _lib = None
@@ -76,8 +87,16 @@ def library() -> ctypes.CDLL:
     lib.fp4_status_string.argtypes = [i32]
     lib.fp4_status_string.restype = ctypes.c_char_p
     lib.fp4_device_check.argtypes = []
+    KV = ctypes.POINTER(_KvCache)
+    lib.fp4_kv_cache_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.fp4_kv_cache_bytes.restype = sz
+    lib.kv_cache_append.argtypes = [KV, vp, vp, i32, i64, vp, i32, vp]
+    lib.attention_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.attention_workspace_bytes.restype = sz
+    lib.attention_decode_fp4kv.argtypes = [vp, i32, KV, vp, ctypes.c_float, vp, i32, vp, sz, vp]
     for name in ("quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
-                 "grouped_gemm_w4aX_gated", "moe_route", "moe_combine", "fp4_device_check"):
+                 "grouped_gemm_w4aX_gated", "moe_route", "moe_combine", "fp4_device_check",
+                 "kv_cache_append", "attention_decode_fp4kv"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -279,4 +298,72 @@ def moe_combine(y: torch.Tensor, token_rows: torch.Tensor, topk_weights: torch.T
                                _ptr(topk_weights), t_count, top_k, hidden, _ptr(o),
                                _dtype_code(o.dtype), o.stride(0), _stream())
     _check(st, "moe_combine")
+    return o
+
+
+class KvCache:
+    """Device arrays of a KV cache in the two-level FP4 format (layout: include/fp4_e2m1.h).
+    Only allocation happens here (torch); the arrays are filled by ``kv_cache_append``."""
+
+    def __init__(self, n_seq: int, max_tokens: int, kv_heads: int, head_dim: int = 128,
+                 device="cuda"):
+        lib = library()
+        sizes = [int(lib.fp4_kv_cache_bytes(n_seq, max_tokens, kv_heads, head_dim, part))
+                 for part in (KV_CODES, KV_MICRO, KV_MACRO)]
+        if sizes[0] == 0:
+            raise Fp4Error(2, "KvCache")
+        self.n_seq, self.max_tokens, self.kv_heads, self.head_dim = n_seq, max_tokens, kv_heads, head_dim
+        self.k_codes = torch.zeros(sizes[0], dtype=torch.uint8, device=device)
+        self.k_micro = torch.zeros(sizes[1], dtype=torch.uint8, device=device)
+        self.k_macro = torch.zeros(sizes[2] // 2, dtype=torch.int16, device=device)
+        self.v_codes = torch.zeros(sizes[0], dtype=torch.uint8, device=device)
+        self.v_micro = torch.zeros(sizes[1], dtype=torch.uint8, device=device)
+        self.v_macro = torch.zeros(sizes[2] // 2, dtype=torch.int16, device=device)
+
+    def c_struct(self) -> _KvCache:
+        return _KvCache(self.k_codes.data_ptr(), self.k_micro.data_ptr(), self.k_macro.data_ptr(),
+                        self.v_codes.data_ptr(), self.v_micro.data_ptr(), self.v_macro.data_ptr(),
+                        self.n_seq, self.max_tokens, self.kv_heads, self.head_dim)
+
+
+def kv_cache_append(cache: KvCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                    positions: torch.Tensor) -> None:
+    """k_new, v_new [n_seq * n_new, kv_heads * head_dim] (bf16 or float32): row
+    b * n_new + i becomes token positions[b] + i of sequence b."""
+    if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype or k_new.dim() != 2 or \
+            k_new.stride(0) != v_new.stride(0) or k_new.stride(1) != 1 or v_new.stride(1) != 1:
+        raise ValueError("k_new and v_new must be 2-D with equal shapes, dtypes and row strides")
+    if positions.dtype != torch.int32 or positions.numel() != cache.n_seq:
+        raise ValueError("positions must be int32 [n_seq]")
+    n_new = k_new.shape[0] // cache.n_seq
+    if n_new * cache.n_seq != k_new.shape[0]:
+        raise ValueError("k_new rows must be n_seq * n_new")
+    cs = cache.c_struct()
+    st = library().kv_cache_append(ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _dtype_code(k_new.dtype),
+                                   k_new.stride(0), _ptr(positions), n_new, _stream())
+    _check(st, "kv_cache_append")
+
+
+def attention_decode_fp4kv(q: torch.Tensor, cache: KvCache, lengths: torch.Tensor,
+                           scale: float | None = None, out_dtype: torch.dtype = torch.bfloat16,
+                           out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """q bf16 [n_seq, q_heads, head_dim] -> out [n_seq, q_heads, head_dim]."""
+    if q.dim() != 3 or q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [n_seq, q_heads, head_dim] tensor")
+    if lengths.dtype != torch.int32 or lengths.numel() != cache.n_seq:
+        raise ValueError("lengths must be int32 [n_seq]")
+    q_heads = q.shape[1]
+    o = out if out is not None else torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if not o.is_contiguous() or o.shape != q.shape:
+        raise ValueError("out must be contiguous with the shape of q")
+    lib = library()
+    need = int(lib.attention_workspace_bytes(cache.n_seq, q_heads, cache.max_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    cs = cache.c_struct()
+    sc = (1.0 / cache.head_dim ** 0.5) if scale is None else float(scale)
+    st = lib.attention_decode_fp4kv(_ptr(q), q_heads, ctypes.byref(cs), _ptr(lengths), sc, _ptr(o),
+                                    _dtype_code(o.dtype), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "attention_decode_fp4kv")
     return o

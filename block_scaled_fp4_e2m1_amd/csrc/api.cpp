@@ -341,4 +341,86 @@ fp4_status moe_combine(const void* y, int32_t y_dtype, int64_t ldy, const int32_
                                              static_cast<hipStream_t>(stream)));
 }
 
+// ---- KV cache and decode attention ----
+
+namespace {
+fp4_status check_kv_cache(const fp4_kv_cache* c) {
+  if (!c || !c->k_codes || !c->k_micro || !c->k_macro || !c->v_codes || !c->v_micro || !c->v_macro)
+    return FP4_E_NULL;
+  if (c->n_seq < 1 || c->n_seq > 65535 ||
+      !fp4lib::kv_cache_supports(c->max_tokens, c->kv_heads, c->head_dim))
+    return FP4_E_SHAPE;
+  if (!aligned16(c->k_codes) || !aligned16(c->v_codes) || !aligned(c->k_micro, 8) ||
+      !aligned(c->v_micro, 8) || !aligned(c->k_macro, 8) || !aligned(c->v_macro, 8))
+    return FP4_E_ALIGN;
+  return FP4_OK;
+}
+fp4lib::KvCacheArgs kv_args(const fp4_kv_cache* c) {
+  fp4lib::KvCacheArgs a;
+  a.k_codes = static_cast<uint8_t*>(c->k_codes);
+  a.k_micro = c->k_micro;
+  a.k_macro = c->k_macro;
+  a.v_codes = static_cast<uint8_t*>(c->v_codes);
+  a.v_micro = c->v_micro;
+  a.v_macro = c->v_macro;
+  a.n_seq = c->n_seq;
+  a.max_tokens = c->max_tokens;
+  a.kv_heads = c->kv_heads;
+  return a;
+}
+}  // namespace
+
+size_t fp4_kv_cache_bytes(int32_t n_seq, int32_t max_tokens, int32_t kv_heads, int32_t head_dim,
+                          int32_t part) {
+  if (n_seq < 1 || !fp4lib::kv_cache_supports(max_tokens, kv_heads, head_dim)) return 0;
+  const size_t tokens = (size_t)n_seq * (size_t)kv_heads * (size_t)max_tokens;
+  switch (part) {
+    case FP4_KV_CODES: return tokens * (size_t)head_dim / 2;
+    case FP4_KV_MICRO: return tokens * (size_t)head_dim / 16;
+    case FP4_KV_MACRO: return tokens / 2 * sizeof(uint16_t);
+    default: return 0;
+  }
+}
+
+fp4_status kv_cache_append(const fp4_kv_cache* cache, const void* k_new, const void* v_new,
+                           int32_t dtype, int64_t ld, const int32_t* positions, int32_t n_new,
+                           void* stream) {
+  const fp4_status cs = check_kv_cache(cache);
+  if (cs != FP4_OK) return cs;
+  if (!k_new || !v_new || !positions) return FP4_E_NULL;
+  if (!valid_dtype(dtype)) return FP4_E_DTYPE;
+  if (n_new < 1 || n_new > (1 << 20) || ld < (int64_t)cache->kv_heads * cache->head_dim) return FP4_E_SHAPE;
+  if (!aligned16(k_new) || !aligned16(v_new) || (ld * (int64_t)dtype_size(dtype)) % 16 ||
+      !aligned(positions, 4))
+    return FP4_E_ALIGN;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  return launched(fp4lib::launch_kv_append(kv_args(cache), k_new, v_new, dtype == FP4_BF16, ld, positions,
+                                           n_new, static_cast<hipStream_t>(stream)));
+}
+
+size_t attention_workspace_bytes(int32_t n_seq, int32_t q_heads, int32_t max_tokens) {
+  if (n_seq < 1 || q_heads < 1 || max_tokens < 1) return 0;
+  return fp4lib::attention_partial_bytes(n_seq, q_heads, max_tokens);
+}
+
+fp4_status attention_decode_fp4kv(const void* q, int32_t q_heads, const fp4_kv_cache* cache,
+                                  const int32_t* lengths, float scale, void* out, int32_t out_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const fp4_status cs = check_kv_cache(cache);
+  if (cs != FP4_OK) return cs;
+  if (!q || !lengths || !out) return FP4_E_NULL;
+  if (!valid_dtype(out_dtype)) return FP4_E_DTYPE;
+  if (q_heads < 1 || q_heads % cache->kv_heads || q_heads / cache->kv_heads > 16) return FP4_E_SHAPE;
+  if (!aligned16(q) || !aligned(lengths, 4) || !aligned(out, dtype_size(out_dtype))) return FP4_E_ALIGN;
+  if (!workspace || !aligned(workspace, 256) ||
+      workspace_bytes < attention_workspace_bytes(cache->n_seq, q_heads, cache->max_tokens))
+    return FP4_E_WORKSPACE;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  return launched(fp4lib::launch_attention_decode(kv_args(cache), static_cast<const uint16_t*>(q), q_heads,
+                                                  lengths, scale, static_cast<float*>(workspace), out,
+                                                  out_dtype == FP4_BF16, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

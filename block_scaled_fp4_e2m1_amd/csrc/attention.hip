@@ -1,0 +1,487 @@
+// Decode attention over a KV cache kept in the two-level block-scaled FP4 format on gfx950,
+// and the append that quantizes new tokens into the cache.
+//
+// "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for Blackwell B200": the codec
+// (section "The Mathematical Breakthrough of Microscopic FP4 Scaling") and FP4 KV caches
+// (its section on what open-source frameworks must rebuild: smaller footprint, less
+// bandwidth, new attention kernels). "AdaLLM Breakthrough: First NVFP4-Only Inference
+// Engine for RTX 4090 Unveiled": a quantized KV cache read by its own decode kernel.
+//
+// Codec reading: each token's key (value) vector over all KV heads, kv_heads * 128
+// elements, is one codec row: E4M3 micro-scale per 16 elements, FP16 macro-scale per 256
+// (a pair of heads). head_dim is 128.
+//
+// Cache layout (per sequence b, KV head h, T = max_tokens, a multiple of 32):
+//   k_codes [b][h][T][64 B]: a token-head's 128 codes, dword 4g + s holding d = 32s + 8g ..
+//           +7 (low nibble first), so that lane group g of an MFMA reads 16 contiguous bytes;
+//   k_micro [b][h][T][8]      the token-head's 8 micro-scales (block d / 16);
+//   k_macro [b][h/2][T]       FP16 macro-scale of the token's 256-group (head pair);
+//   v_codes [b][h][T/32][128 d][16 B]: a 32-token tile transposed, byte 16d + m holding
+//           slots 2m (low nibble) and 2m+1 of column d;
+//   v_micro [b][h][T/32][8 blk][32 slots];
+//   v_macro [b][h/2][T].
+// Slot 8g + i of a tile is token 4g + i (i < 4) or 16 + 4g + i - 4 (i >= 4): the k order in
+// which the P.V step meets the tile's tokens, so one dword gives a lane its 8 tokens.
+//
+// Attention (k_attn_decode): one workgroup per (sequence, KV head, chunk of 1024 tokens),
+// 4 waves of 256 tokens, 32-token tiles. Per tile and wave:
+//   S^T = K' . Q'^T by 8 MFMA 16x16x32 f16 (rows: 16 tokens; columns: the KV head's query
+//   heads, up to 16); K' = e2m1 * mu * 2^-8 is exact in FP16; Q' = q * 2^e with one power
+//   of two per head (exact), so the scores are exact products accumulated in float32;
+//   online softmax per head in base 2;
+//   O^T += V'^T . P''^T by 16 MFMAs (rows: 16 head-dim columns; k: 32 slots); V' = e2m1 *
+//   mu * 2^-8 (per-slot micro-scales, exact in FP16), P'' = p * 2^12 * M_V[t] / M_ref
+//   (M_ref the largest value macro-scale of the wave's tokens) as an FP16 pair hi + lo,
+//   one MFMA each, so the weights keep ~22 bits.
+// Waves are combined through LDS; chunks by k_attn_combine.
+#include "fp4_device.h"
+#include "fp4_kernels.h"
+
+using namespace fp4dev;
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kTile = 32;          // tokens per tile
+constexpr int kWaveTokens = 256;   // tokens per wave and chunk
+constexpr int kChunk = 1024;       // tokens per attention workgroup
+constexpr int kPartial = kHeadDim + 2;  // O[128], m, l per (sequence, head, chunk)
+
+// slot of token t (0..31) inside its tile, and back
+__device__ __forceinline__ int token_slot(int t) {
+  return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + ((t - 16) & 3);
+}
+
+// --------------------------------------------------------------------------------------
+// Append: one workgroup (one wave) per (sequence, tile touched by the new tokens).
+
+template <int IN_BF16>
+__global__ __launch_bounds__(64) void k_kv_append(fp4lib::KvCacheArgs c, const void* __restrict__ k_new,
+                                                  const void* __restrict__ v_new, int64_t ld,
+                                                  const int32_t* __restrict__ positions, int n_new) {
+  extern __shared__ uint32_t vtile[];  // kv_heads x 512 dwords: the tile's V codes
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t T = c.max_tokens;
+  const int64_t pos0 = positions[b];
+  if (pos0 < 0) return;
+  const int64_t tile = pos0 / kTile + blockIdx.y;
+  const int64_t t_lo = max(pos0, tile * kTile);
+  const int64_t t_hi = min(min(pos0 + n_new, tile * kTile + kTile), T);
+  if (t_lo >= t_hi) return;
+  const int H = c.kv_heads;
+  const int mv_count = H * (kHeadDim / 16);  // micro-vectors per token row
+  const int64_t tiles = T / kTile;
+  uint8_t* const vt8 = reinterpret_cast<uint8_t*>(vtile);
+
+  // the tile's current V codes (tokens of the tile that are not rewritten keep theirs)
+  const bool whole = t_lo == tile * kTile && t_hi == tile * kTile + kTile;
+  for (int i = lane; i < H * 512; i += 64) {
+    const int h = i >> 9;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(
+        c.v_codes + (((int64_t)b * H + h) * tiles + tile) * 2048);
+    vtile[i] = whole ? 0u : src[i & 511];
+  }
+  __syncthreads();
+
+  for (int64_t t = t_lo; t < t_hi; ++t) {
+    const int64_t row = (int64_t)b * n_new + (t - pos0);
+    const int slot = token_slot((int)(t - tile * kTile));
+    for (int base = 0; base < mv_count; base += 64) {  // uniform trip count: shuffles stay whole
+      const int mv = base + lane;
+      const bool live = mv < mv_count;
+      const int h = mv >> 3, j = mv & 7;  // head, micro-vector inside the head
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        const void* src = which ? v_new : k_new;
+        float v[16];
+        if (live) {
+          Raw16<IN_BF16> raw;
+          load_raw16<IN_BF16>(src, row * ld + (int64_t)mv * 16, raw);
+          unpack16<IN_BF16>(raw, v);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+        }
+        uint32_t m_bits, mu_byte;
+        float m_val;
+        const float s = block_scales(v, 6.0f, m_bits, mu_byte, m_val);
+        uint32_t w0, w1;
+        e2m1_encode16(v, s, w0, w1);
+        if (!live) continue;
+        const int64_t th = (int64_t)b * H + h;          // (sequence, head)
+        const int64_t pair = (int64_t)b * (H / 2) + (h >> 1);
+        if (which == 0) {
+          uint32_t* kc = reinterpret_cast<uint32_t*>(c.k_codes + (th * T + t) * 64);
+          kc[(2 * (j & 1)) * 4 + (j >> 1)] = w0;      // d = 16j .. 16j+7
+          kc[(2 * (j & 1) + 1) * 4 + (j >> 1)] = w1;  // d = 16j+8 .. 16j+15
+          c.k_micro[(th * T + t) * 8 + j] = (uint8_t)mu_byte;
+          if ((mv & 15) == 0) c.k_macro[pair * T + t] = (uint16_t)m_bits;
+        } else {
+          c.v_micro[(th * tiles + tile) * 256 + j * 32 + slot] = (uint8_t)mu_byte;
+          if ((mv & 15) == 0) c.v_macro[pair * T + t] = (uint16_t)m_bits;
+          // 16 nibbles into 16 rows d of the transposed tile (rows are lane-private)
+          uint8_t* hb = vt8 + h * 2048 + (slot >> 1);
+          const int sh = (slot & 1) * 4;
+          const uint8_t keep = (uint8_t)(0xF0u >> sh);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t code = ((e < 8 ? w0 : w1) >> (4 * (e & 7))) & 15u;
+            uint8_t* p = hb + (16 * j + e) * 16;
+            *p = (uint8_t)((*p & keep) | (code << sh));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = lane; i < H * 512; i += 64) {
+    const int h = i >> 9;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(c.v_codes + (((int64_t)b * H + h) * tiles + tile) * 2048);
+    dst[i & 511] = vtile[i];
+  }
+}
+
+// --------------------------------------------------------------------------------------
+// Attention.
+
+__device__ __forceinline__ half8_t decode_uniform(uint32_t cw, uint32_t mu_op) {
+  const half2_t m2 = __builtin_bit_cast(half2_t, mu_op);
+  const half2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * m2;
+  const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * m2;
+  const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * m2;
+  const half2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * m2;
+  return half8_t{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+}
+
+// 8 codes with one micro-scale each: bytes of (lo, hi) are the 8 E4M3 micro-scales
+__device__ __forceinline__ half8_t decode_per_slot(uint32_t cw, uint32_t mu_lo, uint32_t mu_hi) {
+  // E4M3 byte << 7 in an FP16 half is mu * 2^-8
+  const half2_t m01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, mu_lo, 0x0C010C00u) << 7);
+  const half2_t m23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, mu_lo, 0x0C030C02u) << 7);
+  const half2_t m45 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, mu_hi, 0x0C010C00u) << 7);
+  const half2_t m67 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, mu_hi, 0x0C030C02u) << 7);
+  const half2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * m01;
+  const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * m23;
+  const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * m45;
+  const half2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * m67;
+  return half8_t{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+}
+
+// Everything one lane loads for one 32-token tile.
+struct TileLoads {
+  uint4 kc[2];      // K codes: token 16 mt + n, 16 bytes at 16 g
+  uint2 km[2];      // K micro-scales of that token
+  uint2 kM[2];      // K macro-scales of tokens 16 mt + 4g .. +3
+  uint32_t vc[8];   // V codes: column 16 dt + n, slots 8g .. 8g+7
+  uint2 vm[8];      // V micro-scales: block dt, slots 8g .. 8g+7
+  uint2 vM[2];      // V macro-scales of tokens 16 mt + 4g .. +3
+};
+
+struct AttnPtrs {
+  const uint8_t* kc;   // this (sequence, head)'s K codes
+  const uint8_t* km;
+  const uint16_t* kM;  // this (sequence, head pair)'s macro row
+  const uint8_t* vc;   // this (sequence, head)'s V tiles
+  const uint8_t* vm;
+  const uint16_t* vM;
+};
+
+__device__ __forceinline__ void load_tile(const AttnPtrs& p, int64_t t0, int n, int g, TileLoads& L) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int64_t tok = t0 + 16 * mt + n;
+    L.kc[mt] = *reinterpret_cast<const uint4*>(p.kc + tok * 64 + 16 * g);
+    L.km[mt] = *reinterpret_cast<const uint2*>(p.km + tok * 8);
+    L.kM[mt] = *reinterpret_cast<const uint2*>(p.kM + t0 + 16 * mt + 4 * g);
+    L.vM[mt] = *reinterpret_cast<const uint2*>(p.vM + t0 + 16 * mt + 4 * g);
+  }
+  const int64_t tile = t0 / kTile;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    L.vc[dt] = *reinterpret_cast<const uint32_t*>(p.vc + tile * 2048 + (16 * dt + n) * 16 + 4 * g);
+    L.vm[dt] = *reinterpret_cast<const uint2*>(p.vm + tile * 256 + dt * 32 + 8 * g);
+  }
+}
+
+__device__ __forceinline__ float fp16_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, const uint16_t* __restrict__ q,
+                                                     int q_heads, const int32_t* __restrict__ lengths,
+                                                     float scale_log2, float* __restrict__ partial,
+                                                     int chunks) {
+  __shared__ float sm_o[4][16][kHeadDim];
+  __shared__ float sm_m[4][16];
+  __shared__ float sm_l[4][16];
+  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int H = c.kv_heads;
+  const int64_t T = c.max_tokens;
+  const int64_t L = min((int64_t)max(lengths[b], 0), T);
+  const int64_t chunk_lo = (int64_t)chunk * kChunk;
+  if (chunk_lo >= L) return;  // whole workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int group = q_heads / H;
+
+  AttnPtrs p;
+  {
+    const int64_t th = (int64_t)b * H + kvh, pair = (int64_t)b * (H / 2) + (kvh >> 1);
+    p.kc = c.k_codes + th * T * 64;
+    p.km = c.k_micro + th * T * 8;
+    p.kM = c.k_macro + pair * T;
+    p.vc = c.v_codes + th * (T / kTile) * 2048;
+    p.vm = c.v_micro + th * (T / kTile) * 256;
+    p.vM = c.v_macro + pair * T;
+  }
+
+  // Q'^T operand: column n is query head kvh * group + n (zero for n >= group); k-step s,
+  // lane group g holds d = 32s + 8g .. +7. One power of two per head brings max|q| into
+  // [2^14, 2^15), so the bf16 -> FP16 conversion is exact.
+  half8_t bq[4];
+  float smul;  // score multiplier per column: scale * log2(e) * 2^8 (K' unit) / 2^e
+  {
+    float qv[4][8];
+    float qmax = 0.0f;
+    const bool real = n < group;
+    const uint16_t* qh = q + ((int64_t)b * q_heads + (int64_t)kvh * group + n) * kHeadDim;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+      if (real) raw = *reinterpret_cast<const uint4*>(qh + 32 * s + 8 * g);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qv[s][2 * i] = __uint_as_float(w[i] << 16);
+        qv[s][2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        qmax = fmaxf(qmax, fmaxf(fabsf(qv[s][2 * i]), fabsf(qv[s][2 * i + 1])));
+      }
+    }
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
+    float sq = 1.0f;
+    if (qmax > 0.0f && qmax == qmax) {
+      const int ex = (int)((__float_as_uint(qmax) >> 23) & 0xFFu);  // biased exponent
+      const int e = min(max(127 + 14 + 127 - max(ex, 1), 1), 254);   // 2^(14 - (ex - 127))
+      sq = __uint_as_float((uint32_t)e << 23);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bq[s][i] = (_Float16)(qv[s][i] * sq);
+    smul = scale_log2 * 256.0f / sq;
+  }
+
+  const int64_t w_lo = chunk_lo + (int64_t)wave * kWaveTokens;
+  const int64_t w_hi = min(L, w_lo + kWaveTokens);
+  const int n_tiles = w_hi > w_lo ? (int)((w_hi - w_lo + kTile - 1) / kTile) : 0;
+
+  // reference for the value macro-scales of this wave's tokens
+  float mref = 0.0f;
+  if (n_tiles > 0 && w_lo + 4 * lane < w_hi) {  // t < L <= T, T % 32 == 0: t + 3 < T
+    const int64_t t = w_lo + 4 * lane;
+    const uint2 mm = *reinterpret_cast<const uint2*>(p.vM + t);
+    const uint32_t hs[4] = {mm.x & 0xFFFFu, mm.x >> 16, mm.y & 0xFFFFu, mm.y >> 16};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (t + i < w_hi) mref = fmaxf(mref, fp16_bits_to_float(hs[i]));
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mref = fmaxf(mref, __shfl_xor(mref, o));
+  if (!(mref > 0.0f) || mref != mref) mref = 1.0f;
+  const float pv_mul = 4096.0f / mref;  // P'' = p * 2^12 * M_V / M_ref
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4_t acc_o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc_o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  TileLoads cur, nxt;
+  if (n_tiles > 0) load_tile(p, w_lo, n, g, cur);
+  for (int it = 0; it < n_tiles; ++it) {
+    const int64_t t0 = w_lo + (int64_t)it * kTile;
+    if (it + 1 < n_tiles) load_tile(p, t0 + kTile, n, g, nxt);
+
+    // S^T for the two 16-token halves
+    float4_t acc_s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      acc_s[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+      const uint32_t cw[4] = {cur.kc[mt].x, cur.kc[mt].y, cur.kc[mt].z, cur.kc[mt].w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int blk = 2 * s + (g >> 1);  // micro-block of d = 32s + 8g
+        const uint32_t mb = ((blk < 4 ? cur.km[mt].x : cur.km[mt].y) >> (8 * (blk & 3))) & 0xFFu;
+        const half8_t a = decode_uniform(cw[s], (mb << 7) | (mb << 23));
+        acc_s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[s], acc_s[mt], 0, 0, 0);
+      }
+    }
+    // scores (base 2) of tokens t0 + 16 mt + 4g + i for query column n
+    float sc[8], vr[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const uint32_t kh[4] = {cur.kM[mt].x & 0xFFFFu, cur.kM[mt].x >> 16, cur.kM[mt].y & 0xFFFFu, cur.kM[mt].y >> 16};
+      const uint32_t vh[4] = {cur.vM[mt].x & 0xFFFFu, cur.vM[mt].x >> 16, cur.vM[mt].y & 0xFFFFu, cur.vM[mt].y >> 16};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool live = t0 + 16 * mt + 4 * g + i < L;
+        sc[4 * mt + i] = live ? acc_s[mt][i] * (fp16_bits_to_float(kh[i]) * smul) : -INFINITY;
+        vr[4 * mt + i] = live ? fp16_bits_to_float(vh[i]) * pv_mul : 0.0f;
+      }
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.0f;
+    half8_t bp, bp_lo;  // P'' as an FP16 pair: hi + lo carries ~22 bits of the float32 value
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float pr = exp2f(sc[i] - m_new);
+      psum += pr;
+      const float x = pr * vr[i];
+      const _Float16 hi = (_Float16)x;
+      bp[i] = hi;
+      bp_lo[i] = (_Float16)(x - (float)hi);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc_o[dt] *= alpha;
+
+    // O^T += V'^T . P''^T; slots of tokens past the length get micro-scale 0 (their cache
+    // bytes may hold anything)
+    const bool tail = t0 + kTile > L;
+    uint32_t keep_lo = 0xFFFFFFFFu, keep_hi = 0xFFFFFFFFu;
+    if (tail) {
+      keep_lo = 0u;
+      keep_hi = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tok = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);
+        if (t0 + tok < L) {
+          if (i < 4) keep_lo |= 0xFFu << (8 * i); else keep_hi |= 0xFFu << (8 * (i - 4));
+        }
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const half8_t a = decode_per_slot(cur.vc[dt], cur.vm[dt].x & keep_lo, cur.vm[dt].y & keep_hi);
+      acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp, acc_o[dt], 0, 0, 0);
+      acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp_lo, acc_o[dt], 0, 0, 0);
+    }
+    if (it + 1 < n_tiles) cur = nxt;
+  }
+
+  // per-head sum over the four lane groups, then the wave's results into LDS
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  const float o_mul = mref * (1.0f / 16.0f);  // V' unit 2^-8 times P'' unit 2^12 / M_ref
+  if (n < group) {
+    if (g == 0) {
+      sm_m[wave][n] = m_run;
+      sm_l[wave][n] = l_run;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_o[wave][n][16 * dt + 4 * g + i] = acc_o[dt][i] * o_mul;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < group * kHeadDim; idx += 256) {
+    const int h = idx / kHeadDim, d = idx % kHeadDim;
+    float m = sm_m[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) m = fmaxf(m, sm_m[w][h]);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = sm_m[w][h] == -INFINITY ? 0.0f : exp2f(sm_m[w][h] - m);
+      o += f * sm_o[w][h][d];
+      l += f * sm_l[w][h];
+    }
+    float* dst = partial + (((int64_t)b * q_heads + (int64_t)kvh * group + h) * chunks + chunk) * kPartial;
+    dst[d] = o;
+    if (d == 0) {
+      dst[kHeadDim] = m;
+      dst[kHeadDim + 1] = l;
+    }
+  }
+}
+
+template <int OUT_BF16>
+__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ partial,
+                                                      const int32_t* __restrict__ lengths, int q_heads,
+                                                      int64_t max_tokens, int chunks, void* __restrict__ out) {
+  const int bh = blockIdx.x;
+  const int b = bh / q_heads;
+  const int d = threadIdx.x;
+  const int64_t L = min((int64_t)max(lengths[b], 0), max_tokens);
+  const int used = (int)((L + kChunk - 1) / kChunk);
+  const float* src = partial + (int64_t)bh * chunks * kPartial;
+  float m = -INFINITY;
+  for (int ch = 0; ch < used; ++ch) m = fmaxf(m, src[ch * kPartial + kHeadDim]);
+  float o = 0.0f, l = 0.0f;
+  for (int ch = 0; ch < used; ++ch) {
+    const float f = exp2f(src[ch * kPartial + kHeadDim] - m);
+    o += f * src[ch * kPartial + d];
+    l += f * src[ch * kPartial + kHeadDim + 1];
+  }
+  const float r = used > 0 ? o / l : 0.0f;
+  if (OUT_BF16)
+    static_cast<uint16_t*>(out)[(int64_t)bh * kHeadDim + d] = (uint16_t)bf16_rne_bits(r);
+  else
+    static_cast<float*>(out)[(int64_t)bh * kHeadDim + d] = r;
+}
+
+}  // namespace
+
+namespace fp4lib {
+
+bool kv_cache_supports(int max_tokens, int kv_heads, int head_dim) {
+  return head_dim == kHeadDim && kv_heads >= 2 && kv_heads <= 32 && kv_heads % 2 == 0 &&
+         max_tokens >= kTile && max_tokens % kTile == 0;
+}
+
+size_t attention_partial_bytes(int64_t n_seq, int q_heads, int64_t max_tokens) {
+  const int64_t chunks = (max_tokens + kChunk - 1) / kChunk;
+  return (size_t)n_seq * (size_t)q_heads * (size_t)chunks * kPartial * sizeof(float);
+}
+
+hipError_t launch_kv_append(const KvCacheArgs& c, const void* k_new, const void* v_new, int in_bf16,
+                            int64_t ld, const int32_t* positions, int n_new, hipStream_t st) {
+  if (!kv_cache_supports((int)c.max_tokens, c.kv_heads, kHeadDim) || n_new < 1 || c.n_seq < 1)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)c.n_seq, (unsigned)(n_new / kTile + 2)), block(64);
+  const size_t lds = (size_t)c.kv_heads * 2048;
+  if (in_bf16)
+    hipLaunchKernelGGL(k_kv_append<1>, grid, block, lds, st, c, k_new, v_new, ld, positions, n_new);
+  else
+    hipLaunchKernelGGL(k_kv_append<0>, grid, block, lds, st, c, k_new, v_new, ld, positions, n_new);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_decode(const KvCacheArgs& c, const uint16_t* q, int q_heads,
+                                   const int32_t* lengths, float scale, float* partial, void* out,
+                                   int out_bf16, hipStream_t st) {
+  if (!kv_cache_supports((int)c.max_tokens, c.kv_heads, kHeadDim) || q_heads % c.kv_heads ||
+      q_heads / c.kv_heads > 16 || c.n_seq < 1)
+    return hipErrorInvalidValue;
+  const int chunks = (int)((c.max_tokens + kChunk - 1) / kChunk);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(k_attn_decode, dim3((unsigned)chunks, (unsigned)c.kv_heads, (unsigned)c.n_seq),
+                     dim3(256), 0, st, c, q, q_heads, lengths, scale_log2, partial, chunks);
+  const dim3 grid2((unsigned)(c.n_seq * q_heads)), block2(kHeadDim);
+  if (out_bf16)
+    hipLaunchKernelGGL(k_attn_combine<1>, grid2, block2, 0, st, partial, lengths, q_heads, c.max_tokens, chunks, out);
+  else
+    hipLaunchKernelGGL(k_attn_combine<0>, grid2, block2, 0, st, partial, lengths, q_heads, c.max_tokens, chunks, out);
+  return hipGetLastError();
+}
+
+}  // namespace fp4lib

@@ -132,6 +132,75 @@ __device__ __forceinline__ float e2m1_mag_value(uint32_t mag) {
   return e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
 }
 
+// 16 consecutive input elements as raw 16-byte words, so that the next item's input can
+// be in flight while the current one is encoded.
+template <int IN_BF16>
+struct Raw16 {
+  uint4 q[IN_BF16 ? 2 : 4];
+};
+
+template <int IN_BF16>
+__device__ __forceinline__ void load_raw16(const void* __restrict__ x, int64_t off, Raw16<IN_BF16>& d) {
+  const uint4* p = IN_BF16 ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off)
+                           : reinterpret_cast<const uint4*>(static_cast<const float*>(x) + off);
+#pragma unroll
+  for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i) d.q[i] = p[i];
+}
+
+template <int IN_BF16>
+__device__ __forceinline__ void unpack16(const Raw16<IN_BF16>& d, float v[16]) {
+#pragma unroll
+  for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i) {
+    const uint32_t w[4] = {d.q[i].x, d.q[i].y, d.q[i].z, d.q[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (IN_BF16) {
+        v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      } else {
+        v[4 * i + j] = __uint_as_float(w[j]);
+      }
+    }
+  }
+}
+
+// Scales of a lane that owns one whole micro-vector (16 lanes per group).
+__device__ __forceinline__ float block_scales(const float v[16], float emax, uint32_t& m_bits,
+                                              uint32_t& mu_byte, float& m_val) {
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
+  float amax_g = amax_b;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) amax_g = fmaxf(amax_g, __shfl_xor(amax_g, o));
+  m_bits = 0u;
+  m_val = 0.0f;
+  mu_byte = 0u;
+  if (amax_g > 0.0f) {
+    m_bits = fp16_rne_pos_clamped(amax_g / (emax * 448.0f));
+    m_val = fp16_value(m_bits);
+    mu_byte = e4m3_rne_pos(amax_b / (emax * m_val));
+  }
+  return e4m3_value(mu_byte) * m_val;
+}
+
+__device__ __forceinline__ uint32_t sign_of(float f) { return __float_as_uint(f) >> 31; }
+
+// E2M1 codes of 16 elements for effective scale s (codes 0 when s = 0): element i of
+// v[0..7] in nibble i of w0, of v[8..15] in nibble i of w1 (low nibble first).
+__device__ __forceinline__ void e2m1_encode16(const float v[16], float s, uint32_t& w0, uint32_t& w1) {
+  w0 = 0u;
+  w1 = 0u;
+  if (s > 0.0f) {
+    const E2M1Thresholds th(s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      w0 |= (th.mag(fabsf(v[i])) | (sign_of(v[i]) << 3)) << (4 * i);
+      w1 |= (th.mag(fabsf(v[8 + i])) | (sign_of(v[8 + i]) << 3)) << (4 * i);
+    }
+  }
+}
+
 // Byte offset of the code dword (8 codes) for row r, columns [c8*8, c8*8+8) inside the
 // tiled layout, and the micro/macro offsets (see the header for the layout).
 __device__ __forceinline__ int64_t tiled_code_offset(int64_t r, int64_t col, int64_t groups) {

@@ -68,6 +68,30 @@ hipError_t launch_moe_route(const float* logits, int64_t tokens, int n_experts, 
                             int32_t* topk_ids, float* topk_w, int32_t* offsets, int32_t* row_token,
                             int32_t* token_rows, void* workspace, hipStream_t st);
 
+// KV cache in the two-level FP4 format (layout: see attention.hip). max_tokens % 32 == 0,
+// kv_heads even and <= 32, head_dim 128.
+struct KvCacheArgs {
+  uint8_t* k_codes;
+  uint8_t* k_micro;
+  uint16_t* k_macro;
+  uint8_t* v_codes;
+  uint8_t* v_micro;
+  uint16_t* v_macro;
+  int n_seq;
+  int64_t max_tokens;
+  int kv_heads;
+};
+bool kv_cache_supports(int max_tokens, int kv_heads, int head_dim);
+size_t attention_partial_bytes(int64_t n_seq, int q_heads, int64_t max_tokens);
+// n_new tokens per sequence b at positions[b] .. +n_new-1 (rows b * n_new + i of k_new /
+// v_new, row stride ld elements); writes past max_tokens are skipped.
+hipError_t launch_kv_append(const KvCacheArgs& c, const void* k_new, const void* v_new, int in_bf16,
+                            int64_t ld, const int32_t* positions, int n_new, hipStream_t st);
+// q bf16 [n_seq][q_heads][128]; out [n_seq][q_heads][128]; partial: attention_partial_bytes.
+hipError_t launch_attention_decode(const KvCacheArgs& c, const uint16_t* q, int q_heads,
+                                   const int32_t* lengths, float scale, float* partial, void* out,
+                                   int out_bf16, hipStream_t st);
+
 // out[t, :] = sum_j w[t, j] * y[token_rows[t, j], :] (float32, j in order); hidden % 8 == 0.
 hipError_t launch_moe_combine(const void* y, int in_bf16, int64_t ldy, const int32_t* token_rows,
                               const float* topk_w, int64_t tokens, int top_k, int64_t hidden,

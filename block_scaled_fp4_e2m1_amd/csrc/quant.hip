@@ -18,59 +18,6 @@ using namespace fp4dev;
 
 namespace {
 
-// 16 consecutive input elements as raw 16-byte words, so that the next item's input can
-// be in flight while the current one is encoded.
-template <int IN_BF16>
-struct Raw16 {
-  uint4 q[IN_BF16 ? 2 : 4];
-};
-
-template <int IN_BF16>
-__device__ __forceinline__ void load_raw16(const void* __restrict__ x, int64_t off, Raw16<IN_BF16>& d) {
-  const uint4* p = IN_BF16 ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off)
-                           : reinterpret_cast<const uint4*>(static_cast<const float*>(x) + off);
-#pragma unroll
-  for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i) d.q[i] = p[i];
-}
-
-template <int IN_BF16>
-__device__ __forceinline__ void unpack16(const Raw16<IN_BF16>& d, float v[16]) {
-#pragma unroll
-  for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i) {
-    const uint32_t w[4] = {d.q[i].x, d.q[i].y, d.q[i].z, d.q[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (IN_BF16) {
-        v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-      } else {
-        v[4 * i + j] = __uint_as_float(w[j]);
-      }
-    }
-  }
-}
-
-// Scales of a lane that owns one whole micro-vector (16 lanes per group).
-__device__ __forceinline__ float block_scales(const float v[16], float emax, uint32_t& m_bits,
-                                              uint32_t& mu_byte, float& m_val) {
-  float amax_b = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
-  float amax_g = amax_b;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) amax_g = fmaxf(amax_g, __shfl_xor(amax_g, o));
-  m_bits = 0u;
-  m_val = 0.0f;
-  mu_byte = 0u;
-  if (amax_g > 0.0f) {
-    m_bits = fp16_rne_pos_clamped(amax_g / (emax * 448.0f));
-    m_val = fp16_value(m_bits);
-    mu_byte = e4m3_rne_pos(amax_b / (emax * m_val));
-  }
-  return e4m3_value(mu_byte) * m_val;
-}
-
-__device__ __forceinline__ uint32_t sign_of(float f) { return __float_as_uint(f) >> 31; }
 
 // Grid mappings. Quantize and the activation pass: 16 lanes per 256-group; a block of 256
 // threads covers 16 consecutive (row, group) pairs of the row-major order
@@ -108,15 +55,8 @@ __device__ __forceinline__ void quantize_item(const float v[16], int64_t r, int6
   const float s = block_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
 
   if (!ELEM_E4M3) {
-    uint32_t w0 = 0u, w1 = 0u;
-    if (s > 0.0f) {
-      const E2M1Thresholds th(s);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        w0 |= (th.mag(fabsf(v[i])) | (sign_of(v[i]) << 3)) << (4 * i);
-        w1 |= (th.mag(fabsf(v[8 + i])) | (sign_of(v[8 + i]) << 3)) << (4 * i);
-      }
-    }
+    uint32_t w0, w1;
+    e2m1_encode16(v, s, w0, w1);
     if (TILED) {
       *reinterpret_cast<uint32_t*>(codes + tiled_code_offset(r, col, groups)) = w0;
       *reinterpret_cast<uint32_t*>(codes + tiled_code_offset(r, col + 8, groups)) = w1;
@@ -231,15 +171,8 @@ __device__ __forceinline__ void act_item(float v[16], int64_t r, int64_t g, int 
   if (!ELEM_E4M3) {
     // codes as in k_quantize, then decoded two at a time by the hardware conversion
     // (scale 1: exact) and multiplied by mu in FP16 (E2M1 * mu is exact in FP16)
-    uint32_t w0 = 0u, w1 = 0u;
-    if (s > 0.0f) {
-      const E2M1Thresholds th(s);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        w0 |= (th.mag(fabsf(v[i])) | (sign_of(v[i]) << 3)) << (4 * i);
-        w1 |= (th.mag(fabsf(v[8 + i])) | (sign_of(v[8 + i]) << 3)) << (4 * i);
-      }
-    }
+    uint32_t w0, w1;
+    e2m1_encode16(v, s, w0, w1);
     const _Float16 muh = (_Float16)mu;
     const half2_t m2 = {muh, muh};
     out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0) * m2;

@@ -204,6 +204,83 @@ fp4_status moe_combine(const void* y, int32_t y_dtype, int64_t ldy, const int32_
                        const float* topk_weights, int64_t tokens, int32_t top_k, int64_t hidden,
                        void* out, int32_t out_dtype, int64_t ldo, void* stream);
 
+/*
+ * KV cache in the two-level FP4 format, and decode attention over it.
+ * Sources: "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for Blackwell B200"
+ * (the codec, section "The Mathematical Breakthrough of Microscopic FP4 Scaling"; keeping
+ * the KV cache in FP4 to cut its footprint and bandwidth, in its section on what
+ * open-source frameworks must rebuild) and "AdaLLM Breakthrough: First NVFP4-Only
+ * Inference Engine for RTX 4090 Unveiled" (a quantized KV cache with its own decode
+ * kernel, grouped-query models).
+ *
+ * Codec reading: each token's key (value) vector over all KV heads (kv_heads x head_dim
+ * elements) is one codec row: E2M1 codes, an E4M3 micro-scale per 16 elements, an FP16
+ * macro-scale per 256 (a pair of heads). head_dim must be 128, kv_heads even and <= 32,
+ * max_tokens a multiple of 32 (FP4_E_SHAPE otherwise).
+ *
+ * Device layout (all arrays caller-owned device memory, T = max_tokens):
+ *   k_codes [n_seq][kv_heads][T][64 B]: per token-head, dword 4g + s holds the codes of
+ *           d = 32s + 8g .. 32s + 8g + 7 (low nibble first), g, s in 0..3;
+ *   k_micro [n_seq][kv_heads][T][8]: micro-scale of block d / 16;
+ *   k_macro [n_seq][kv_heads / 2][T]: FP16 bits of the head pair's macro-scale;
+ *   v_codes [n_seq][kv_heads][T / 32][128][16 B]: tiles of 32 tokens, transposed: byte
+ *           16 d + m of a tile holds slots 2m (low nibble) and 2m + 1 of column d;
+ *   v_micro [n_seq][kv_heads][T / 32][8][32]: micro-scale of block b for each slot;
+ *   v_macro [n_seq][kv_heads / 2][T].
+ * Slot 8g + i (g in 0..3, i in 0..7) of a tile is its token 4g + i for i < 4 and
+ * 16 + 4g + i - 4 for i >= 4. Alignment: codes 16 bytes, micro and macro 8 bytes.
+ * fp4_kv_cache_bytes(.., part) gives each array's size (the K and V arrays of one part
+ * have equal sizes); 0 for an unsupported shape.
+ */
+typedef struct {
+  void* k_codes;
+  uint8_t* k_micro;
+  uint16_t* k_macro;
+  void* v_codes;
+  uint8_t* v_micro;
+  uint16_t* v_macro;
+  int32_t n_seq;
+  int32_t max_tokens;
+  int32_t kv_heads;
+  int32_t head_dim;
+} fp4_kv_cache;
+
+enum { FP4_KV_CODES = 0, FP4_KV_MICRO = 1, FP4_KV_MACRO = 2 };
+
+size_t fp4_kv_cache_bytes(int32_t n_seq, int32_t max_tokens, int32_t kv_heads, int32_t head_dim,
+                          int32_t part);
+
+/*
+ * kv_cache_append -- quantize n_new new tokens per sequence into the cache: rows
+ * b * n_new + i of k_new and v_new (device, FP4_BF16 or FP4_F32, row stride ld >=
+ * kv_heads * head_dim elements, 16-byte aligned rows) become token positions[b] + i of
+ * sequence b (positions: device int32 [n_seq]). Other tokens keep their contents. Tokens
+ * at or past max_tokens, and sequences with a negative position, are skipped on the
+ * device. 1 <= n_new <= 2^20.
+ */
+fp4_status kv_cache_append(const fp4_kv_cache* cache, const void* k_new, const void* v_new,
+                           int32_t dtype, int64_t ld, const int32_t* positions, int32_t n_new,
+                           void* stream);
+
+/*
+ * attention_decode_fp4kv -- one decode step of attention for every sequence:
+ *   out[b, h, :] = sum_{t < L_b} softmax_t(scale * q[b, h, :] . K_hat[b, t, kv(h), :])
+ *                  * V_hat[b, t, kv(h), :],   kv(h) = h / (q_heads / kv_heads),
+ * K_hat, V_hat the dequantized cache and L_b = lengths[b] (device int32, clamped to
+ * [0, max_tokens]; L_b = 0 gives zeros).
+ *   q         device bf16 [n_seq][q_heads][128], 16-byte aligned; q_heads a multiple of
+ *             kv_heads with at most 16 query heads per KV head
+ *   out       device [n_seq][q_heads][128], FP4_BF16 (round to nearest even) or FP4_F32
+ *   workspace >= attention_workspace_bytes(n_seq, q_heads, max_tokens), 256-byte aligned
+ * Scores are exact products of the cache values and q (q is rescaled by a power of two
+ * per head into FP16) accumulated in float32; softmax weights enter the value product as
+ * a pair of FP16 values (about 2^-22 relative); the result is accumulated in float32.
+ */
+size_t attention_workspace_bytes(int32_t n_seq, int32_t q_heads, int32_t max_tokens);
+fp4_status attention_decode_fp4kv(const void* q, int32_t q_heads, const fp4_kv_cache* cache,
+                                  const int32_t* lengths, float scale, void* out, int32_t out_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace gemm_w4aX / grouped_gemm_w4aX need (0 for FP4_A16). */
 size_t fp4_workspace_bytes(int32_t act, int64_t m_or_rows, int64_t n, int64_t k);
 

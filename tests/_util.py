@@ -80,3 +80,53 @@ def f32_gate(got: np.ndarray, want: np.ndarray, rel_frob: float = 1e-5):
     rel = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)
     assert rel <= rel_frob, f"relative Frobenius error {rel:.3e} > {rel_frob}"
     return rel
+
+
+def kv_slot_of_token():
+    """Slot of each token (0..31) inside a 32-token V tile (include/fp4_e2m1.h: slot 8g + i
+    is token 4g + i for i < 4 and 16 + 4g + i - 4 for i >= 4)."""
+    slot = np.zeros(32, dtype=np.int64)
+    for g in range(4):
+        for i in range(8):
+            tok = 4 * g + i if i < 4 else 16 + 4 * g + i - 4
+            slot[tok] = 8 * g + i
+    return slot
+
+
+def kv_cache_to_canonical(cache, which: str, b: int, tokens):
+    """Canonical codec rows (codes4 uint8 [n, H*128], micro [n, H*8], macro uint16 [n, H/2])
+    of the given tokens of sequence b, read back from the documented device layout."""
+    H, T = cache.kv_heads, cache.max_tokens
+    tokens = np.asarray(tokens, dtype=np.int64)
+    codes_dev = host(getattr(cache, which + "_codes")).astype(np.uint8)
+    micro_dev = host(getattr(cache, which + "_micro")).astype(np.uint8)
+    macro_dev = host(getattr(cache, which + "_macro")).view(np.uint16)
+    n = len(tokens)
+    codes4 = np.zeros((n, H * 128), dtype=np.uint8)
+    micro = np.zeros((n, H * 8), dtype=np.uint8)
+    macro = np.zeros((n, H // 2), dtype=np.uint16)
+    slot = kv_slot_of_token()
+    d = np.arange(128)
+    for h in range(H):
+        th = b * H + h
+        for r, t in enumerate(tokens):
+            if which == "k":
+                rec = codes_dev[(th * T + t) * 64:(th * T + t + 1) * 64]
+                words = rec.view(np.uint32)
+                # dword 4g + s holds d = 32s + 8g + i
+                for gg in range(4):
+                    for s in range(4):
+                        w = int(words[4 * gg + s])
+                        for i in range(8):
+                            codes4[r, h * 128 + 32 * s + 8 * gg + i] = (w >> (4 * i)) & 15
+                micro[r, h * 8:(h + 1) * 8] = micro_dev[(th * T + t) * 8:(th * T + t + 1) * 8]
+            else:
+                tile, sl = t // 32, slot[t % 32]
+                base = (th * (T // 32) + tile) * 2048
+                byte = codes_dev[base + d * 16 + sl // 2]
+                codes4[r, h * 128:(h + 1) * 128] = (byte >> (4 * (sl % 2))) & 15
+                mbase = (th * (T // 32) + tile) * 256
+                micro[r, h * 8:(h + 1) * 8] = micro_dev[mbase + np.arange(8) * 32 + sl]
+    for pr in range(H // 2):
+        macro[:, pr] = macro_dev[(b * (H // 2) + pr) * T + tokens]
+    return codes4, micro, macro

@@ -143,6 +143,39 @@ def test_moe_entry_points_validate_before_device_use(lib):
     assert lib.moe_combine(fake, 1, 512, fake, fake, 8, 0, 512, fake, 0, 512, null) == 2
 
 
+def test_kv_entry_points_validate_before_device_use(lib):
+    vp = ctypes.c_void_p
+    fake, null = vp(1 << 20), vp(0)
+    KV = lib_mod._KvCache
+    # sizes: codes n_seq * kv_heads * T * 64, micro * 8, macro n_seq * kv_heads/2 * T * 2
+    assert lib.fp4_kv_cache_bytes(32, 16384, 8, 128, 0) == 32 * 8 * 16384 * 64
+    assert lib.fp4_kv_cache_bytes(32, 16384, 8, 128, 1) == 32 * 8 * 16384 * 8
+    assert lib.fp4_kv_cache_bytes(32, 16384, 8, 128, 2) == 32 * 4 * 16384 * 2
+    assert lib.fp4_kv_cache_bytes(1, 96, 2, 128, 0) == 96 * 2 * 64
+    for bad in ((1, 40, 2, 128), (1, 64, 3, 128), (1, 64, 2, 64), (1, 64, 34, 128), (0, 64, 2, 128),
+                (1, 16, 2, 128)):
+        assert lib.fp4_kv_cache_bytes(*bad, 0) == 0
+    assert lib.attention_workspace_bytes(32, 32, 16384) == 32 * 32 * 16 * 130 * 4
+    good = KV(1 << 20, 1 << 21, 1 << 22, 1 << 23, 1 << 24, 1 << 25, 4, 64, 2, 128)
+    assert lib.kv_cache_append(None, fake, fake, 1, 256, fake, 1, null) == 1
+    assert lib.kv_cache_append(ctypes.byref(good), fake, fake, 1, 255, fake, 1, null) == 2
+    assert lib.kv_cache_append(ctypes.byref(good), fake, fake, 1, 256, fake, 0, null) == 2
+    assert lib.kv_cache_append(ctypes.byref(good), fake, fake, 7, 256, fake, 1, null) == 4
+    assert lib.kv_cache_append(ctypes.byref(good), vp((1 << 20) + 8), fake, 1, 256, fake, 1, null) == 3
+    assert lib.kv_cache_append(ctypes.byref(good), fake, null, 1, 256, fake, 1, null) == 1
+    odd = KV(1 << 20, 1 << 21, 1 << 22, 1 << 23, 1 << 24, 1 << 25, 4, 64, 3, 128)
+    assert lib.kv_cache_append(ctypes.byref(odd), fake, fake, 1, 384, fake, 1, null) == 2
+    mis = KV((1 << 20) + 4, 1 << 21, 1 << 22, 1 << 23, 1 << 24, 1 << 25, 4, 64, 2, 128)
+    assert lib.kv_cache_append(ctypes.byref(mis), fake, fake, 1, 256, fake, 1, null) == 3
+    ws = vp(1 << 26)
+    assert lib.attention_decode_fp4kv(fake, 3, ctypes.byref(good), fake, 1.0, fake, 0, ws, 1 << 30, null) == 2
+    assert lib.attention_decode_fp4kv(fake, 34, ctypes.byref(good), fake, 1.0, fake, 0, ws, 1 << 30, null) == 2
+    assert lib.attention_decode_fp4kv(fake, 8, ctypes.byref(good), fake, 1.0, fake, 0, null, 0, null) == 9
+    assert lib.attention_decode_fp4kv(fake, 8, ctypes.byref(good), fake, 1.0, fake, 0, ws, 100, null) == 9
+    assert lib.attention_decode_fp4kv(null, 8, ctypes.byref(good), fake, 1.0, fake, 0, ws, 1 << 30, null) == 1
+    assert lib.attention_decode_fp4kv(fake, 8, ctypes.byref(good), fake, 1.0, fake, 5, ws, 1 << 30, null) == 4
+
+
 def test_device_check_reports_missing_device(lib):
     import torch
     if torch.cuda.is_available():

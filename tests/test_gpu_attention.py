@@ -1,0 +1,174 @@
+"""GPU parity of the FP4 KV cache (kv_cache_append) and of decode attention over it
+(attention_decode_fp4kv) against the CPU oracle, through the C ABI.
+
+Gates:
+  cache contents: codes, micro- and macro-scales bit-exact against the oracle's codec on
+      the same token rows (read back through the documented device layout);
+  attention, float32 output: relative Frobenius error <= 1e-5 against the float64 oracle
+      on the oracle's own quantization of the same inputs. The kernel's scores are exact
+      products of the cache values and q accumulated in float32 (relative ~2^-24 per sum
+      of 128); the softmax weights enter the value product as an FP16 pair hi + lo
+      (~2^-22 relative); exp2 and the sums are float32. (A single FP16 weight, 2^-12
+      relative each, measured ~1e-4 and flipped the bf16 rounding of too many outputs.);
+  attention, bf16 output: the bf16 gate (relative Frobenius <= 1e-3 against the rounded
+      float64 result, >= 99.9% of elements within one bf16 step).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._util import host, bf16_values, bf16_gate, f32_gate, kv_cache_to_canonical
+
+pytestmark = pytest.mark.gpu
+
+fp4 = pytest.importorskip("block_scaled_fp4_e2m1_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert fp4.fp4_device_check() == 0, "device is not gfx950"
+
+
+def _rows(rng, n, width, outliers=True):
+    x = rng.standard_normal((n, width)).astype(np.float32)
+    if outliers:
+        x[:, rng.choice(width, max(1, width // 200), replace=False)] *= 20
+    return x
+
+
+def _check_cache(cache, which, b, tokens, rows):
+    codes4, micro, macro = kv_cache_to_canonical(cache, which, b, tokens)
+    ref = oracle.kv_quantize_rows(rows.astype(np.float64))
+    assert np.array_equal(codes4, oracle.unpack_e2m1(ref.codes)), f"{which} codes, sequence {b}"
+    assert np.array_equal(micro, ref.micro), f"{which} micro, sequence {b}"
+    assert np.array_equal(macro, ref.macro.astype(np.uint16)), f"{which} macro, sequence {b}"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_append_prefill_then_decode_bit_exact(dtype):
+    n_seq, kv_heads, T = 3, 4, 160
+    width = kv_heads * 128
+    rng = np.random.default_rng(71)
+    cache = fp4.KvCache(n_seq, T, kv_heads)
+    pos0 = np.array([0, 5, 33], dtype=np.int32)
+    n_new = 70
+    print(f"[case] kv append prefill n_new={n_new} positions={pos0.tolist()} {dtype}", flush=True)
+    k = _rows(rng, n_seq * n_new, width)
+    v = _rows(rng, n_seq * n_new, width, outliers=False)
+    if dtype == torch.bfloat16:
+        k, v = workloads.to_bf16_values(k), workloads.to_bf16_values(v)
+    fp4.kv_cache_append(cache, torch.from_numpy(k).cuda().to(dtype), torch.from_numpy(v).cuda().to(dtype),
+                        torch.from_numpy(pos0).cuda())
+    # one decode token per sequence right after the prompt (shares a tile with it)
+    k1 = _rows(rng, n_seq, width)
+    v1 = _rows(rng, n_seq, width, outliers=False)
+    if dtype == torch.bfloat16:
+        k1, v1 = workloads.to_bf16_values(k1), workloads.to_bf16_values(v1)
+    pos1 = pos0 + n_new
+    fp4.kv_cache_append(cache, torch.from_numpy(k1).cuda().to(dtype), torch.from_numpy(v1).cuda().to(dtype),
+                        torch.from_numpy(pos1).cuda())
+    torch.cuda.synchronize()
+    for b in range(n_seq):
+        toks = np.arange(pos0[b], pos1[b] + 1)
+        krows = np.concatenate([k[b * n_new:(b + 1) * n_new], k1[b:b + 1]])
+        vrows = np.concatenate([v[b * n_new:(b + 1) * n_new], v1[b:b + 1]])
+        _check_cache(cache, "k", b, toks, krows)
+        _check_cache(cache, "v", b, toks, vrows)
+        # tokens never written keep the zeroed cache (shared V tiles included)
+        untouched = np.setdiff1d(np.arange(T), toks)
+        codes4, micro, macro = kv_cache_to_canonical(cache, "v", b, untouched)
+        assert not codes4.any() and not micro.any() and not macro.any()
+
+
+def test_append_skips_positions_past_the_cache_and_negative():
+    n_seq, kv_heads, T = 2, 2, 64
+    rng = np.random.default_rng(72)
+    cache = fp4.KvCache(n_seq, T, kv_heads)
+    k = workloads.to_bf16_values(_rows(rng, n_seq * 8, 256))
+    v = workloads.to_bf16_values(_rows(rng, n_seq * 8, 256))
+    pos = torch.tensor([T - 3, -1], dtype=torch.int32, device="cuda")
+    print("[case] kv append past the end / negative position", flush=True)
+    fp4.kv_cache_append(cache, torch.from_numpy(k).cuda().to(torch.bfloat16),
+                        torch.from_numpy(v).cuda().to(torch.bfloat16), pos)
+    torch.cuda.synchronize()
+    _check_cache(cache, "k", 0, np.arange(T - 3, T), k[:3])
+    _check_cache(cache, "v", 0, np.arange(T - 3, T), v[:3])
+    codes4, micro, macro = kv_cache_to_canonical(cache, "k", 1, np.arange(T))
+    assert not codes4.any() and not micro.any() and not macro.any()
+
+
+def _attention_case(n_seq, kv_heads, q_heads, T, lengths, seed, out_dtype):
+    rng = np.random.default_rng(seed)
+    width = kv_heads * 128
+    cache = fp4.KvCache(n_seq, T, kv_heads)
+    k = workloads.to_bf16_values(_rows(rng, n_seq * T, width))
+    v = workloads.to_bf16_values(_rows(rng, n_seq * T, width, outliers=False))
+    q = workloads.to_bf16_values(rng.standard_normal((n_seq, q_heads, 128)).astype(np.float32))
+    fp4.kv_cache_append(cache, torch.from_numpy(k).cuda().to(torch.bfloat16),
+                        torch.from_numpy(v).cuda().to(torch.bfloat16),
+                        torch.zeros(n_seq, dtype=torch.int32, device="cuda"))
+    lens = np.asarray(lengths, dtype=np.int32)
+    got = fp4.attention_decode_fp4kv(torch.from_numpy(q).cuda().to(torch.bfloat16), cache,
+                                     torch.from_numpy(lens).cuda(), out_dtype=out_dtype)
+    k_hat = oracle.kv_dequantize_rows(k).reshape(n_seq, T, kv_heads, 128)
+    v_hat = oracle.kv_dequantize_rows(v).reshape(n_seq, T, kv_heads, 128)
+    eff = np.clip(lens, 0, T)
+    ref = np.zeros((n_seq, q_heads, 128))
+    live = eff > 0
+    if live.any():
+        ref[live] = oracle.attention_decode(q[live], k_hat[live], v_hat[live], eff[live], 1.0 / np.sqrt(128))
+    return got, ref
+
+
+@pytest.mark.parametrize("kv_heads,q_heads", [(2, 8), (2, 2), (2, 32), (8, 64)])
+def test_attention_small_f32(kv_heads, q_heads):
+    T = 2112  # not a multiple of the 256-token wave span
+    lengths = [1, 31, 1057, 2112]
+    print(f"[case] attention kv_heads={kv_heads} q_heads={q_heads} T={T} lengths={lengths}", flush=True)
+    got, ref = _attention_case(4, kv_heads, q_heads, T, lengths, 73 + q_heads, torch.float32)
+    rel = f32_gate(host(got).astype(np.float64), ref, rel_frob=1e-5)
+    print(f"  relative Frobenius error {rel:.2e}", flush=True)
+
+
+def test_attention_bf16_out_and_edge_lengths():
+    T = 1088
+    lengths = [0, 32, 33, 1024, 1025, 5000]  # 0: zeros; past the cache: clamped to T
+    print(f"[case] attention bf16 out lengths={lengths}", flush=True)
+    got, ref = _attention_case(6, 2, 8, T, lengths, 79, torch.bfloat16)
+    g = bf16_values(got)
+    assert not g[0].any()
+    bf16_gate(g[1:], oracle.formats.bf16_round(ref[1:]))
+
+
+def test_attention_deterministic():
+    print("[case] attention repeat", flush=True)
+    n_seq, kv_heads, q_heads, T = 2, 2, 8, 1024
+    rng = np.random.default_rng(80)
+    cache = fp4.KvCache(n_seq, T, kv_heads)
+    k = torch.from_numpy(workloads.to_bf16_values(_rows(rng, n_seq * T, 256))).cuda().to(torch.bfloat16)
+    v = torch.from_numpy(workloads.to_bf16_values(_rows(rng, n_seq * T, 256))).cuda().to(torch.bfloat16)
+    fp4.kv_cache_append(cache, k, v, torch.zeros(n_seq, dtype=torch.int32, device="cuda"))
+    q = torch.randn(n_seq, q_heads, 128, device="cuda").to(torch.bfloat16)
+    lens = torch.tensor([1000, 777], dtype=torch.int32, device="cuda")
+    a = fp4.attention_decode_fp4kv(q, cache, lens, out_dtype=torch.float32)
+    for _ in range(3):
+        assert torch.equal(a, fp4.attention_decode_fp4kv(q, cache, lens, out_dtype=torch.float32))
+
+
+def test_attention_rejects_bad_shapes():
+    cache = fp4.KvCache(1, 64, 2)
+    q = torch.zeros(1, 6, 128, dtype=torch.bfloat16, device="cuda")  # 6 % 2 == 0 but group 3 fine
+    lens = torch.ones(1, dtype=torch.int32, device="cuda")
+    fp4.attention_decode_fp4kv(q, cache, lens)
+    with pytest.raises(fp4.Fp4Error):
+        fp4.attention_decode_fp4kv(torch.zeros(1, 3, 128, dtype=torch.bfloat16, device="cuda"), cache, lens)
+    with pytest.raises(fp4.Fp4Error):  # 17 query heads per KV head
+        fp4.attention_decode_fp4kv(torch.zeros(1, 34, 128, dtype=torch.bfloat16, device="cuda"), cache, lens)
+    with pytest.raises(fp4.Fp4Error):
+        fp4.KvCache(1, 48 + 8, 2)  # max_tokens % 32 != 0
+    with pytest.raises(fp4.Fp4Error):
+        fp4.KvCache(1, 64, 3)  # odd kv_heads
