@@ -408,6 +408,66 @@ def bench_moe(torch, fp4, workloads, steps):
                                      mean=float(counts.mean())))
 
 
+def build_kv_cache(torch, fp4, workloads, cfg, layer, chunk=4096):
+    """One layer's cache filled with max_tokens seeded tokens per sequence (device draws)."""
+    B, Hkv, D, T = cfg["n_seq"], cfg["kv_heads"], cfg["head_dim"], cfg["max_tokens"]
+    ch = workloads.kv_key_outliers(Hkv * D, 0.005, cfg["seed"])
+    cache = fp4.KvCache(B, T, Hkv)
+    for i, c0 in enumerate(range(0, T, chunk)):
+        k = workloads.kv_rows_device(torch, B * chunk, Hkv * D, cfg["seed"], 100 * layer + 2 * i, outliers=ch)
+        v = workloads.kv_rows_device(torch, B * chunk, Hkv * D, cfg["seed"], 100 * layer + 2 * i + 1)
+        fp4.kv_cache_append(cache, k, v, torch.full((B,), c0, dtype=torch.int32, device="cuda"))
+        del k, v
+    return cache
+
+
+def bench_attention(torch, fp4, workloads, steps):
+    """One decode step of attention over the FP4 KV cache: append the step's token to every
+    sequence, then attention over L + 1 tokens. Two layers' caches alternate so the 256 MB
+    Infinity Cache cannot hold the working set."""
+    cfg = workloads.WORKLOADS["decode_attention_fp4kv"]
+    B, Hq, Hkv, D, T = cfg["n_seq"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"], cfg["max_tokens"]
+    lens = workloads.kv_lengths(B, cfg["min_len"], cfg["max_len"], cfg["seed"])
+    caches = [build_kv_cache(torch, fp4, workloads, cfg, layer) for layer in range(2)]
+    q = torch.from_numpy(workloads.kv_queries(B, Hq, D, cfg["seed"])).cuda().to(torch.bfloat16)
+    rng = np.random.default_rng((cfg["seed"], 3))
+    k1 = torch.from_numpy(rng.standard_normal((B, Hkv * D), dtype=np.float32)).cuda().to(torch.bfloat16)
+    v1 = torch.from_numpy(rng.standard_normal((B, Hkv * D), dtype=np.float32)).cuda().to(torch.bfloat16)
+    pos = torch.from_numpy(lens).cuda()
+    lengths = torch.from_numpy(lens + 1).cuda()
+    outs = [torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda") for _ in caches]
+    ws = torch.empty(fp4.library().attention_workspace_bytes(B, Hq, T), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        fp4.kv_cache_append(caches[i], k1, v1, pos)
+        fp4.attention_decode_fp4kv(q, caches[i], lengths, out=outs[i], workspace=ws)
+
+    def attn(i):
+        fp4.attention_decode_fp4kv(q, caches[i], lengths, out=outs[i], workspace=ws)
+    timer = Timer(torch)
+    res = {}
+    for name, fn in (("step", step), ("attention", attn)):
+        fns = [lambda i=i: fn(i) for i in range(len(caches))]
+        for f in fns:
+            f()
+        g = capture(torch, fns)
+        g.replay()
+        res[name] = run_steps(torch, timer, g, fns, steps) / steps
+    torch.cuda.synchronize()
+    tokens = int((lens.astype(np.int64) + 1).sum())
+    per_token_head = 2 * (D // 2 + D // 16 + 1)  # K and V: codes, micro, macro (a pair's 2 B / 2)
+    cache_bytes = tokens * Hkv * per_token_head
+    io_bytes = 2 * B * Hq * D * 2  # q in, out
+    total = cache_bytes + io_bytes
+    return dict(n_seq=B, q_heads=Hq, kv_heads=Hkv, head_dim=D, max_tokens=T,
+                context_min_mean_max=[int(lens.min() + 1), float(lens.mean() + 1), int(lens.max() + 1)],
+                algorithmic_bytes=total, bf16_cache_bytes_equivalent=tokens * Hkv * 2 * D * 2,
+                step_s=res["step"], attention_s=res["attention"],
+                gbs_attention=total / res["attention"] / 1e9, gbs_step=total / res["step"] / 1e9,
+                frac_hbm_attention=total / res["attention"] / 1e9 / HBM_PEAK_GBS,
+                layers_rotated=len(caches))
+
+
 def cpu_baseline(workloads, budget_s=12.0):
     """The oracle, as written, on a bounded sample of the decode workload: quantize rows of
     W, dequantize, float64 product with the 8 activation rows; GB/s of the same
@@ -451,7 +511,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--skip-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize", "attention"],
+                    default=None,
                     help="run one workload only (for profiling); prints its record")
     ap.add_argument("--copy-probe", action="store_true",
                     help="with --only: end with 256 MiB device copies (counter calibration)")
@@ -495,7 +556,8 @@ def main():
               "prefill": lambda: bench_prefill(torch, fp4, workloads, args.steps),
               "policy": lambda: bench_policy(torch, fp4, workloads, args.steps),
               "moe": lambda: bench_moe(torch, fp4, workloads, args.steps),
-              "quantize": lambda: bench_quantize(torch, fp4, workloads, args.steps)}[args.only]
+              "quantize": lambda: bench_quantize(torch, fp4, workloads, args.steps),
+              "attention": lambda: bench_attention(torch, fp4, workloads, args.steps)}[args.only]
         rec = {args.only: fn()}
         if args.copy_probe:
             rec["copy_probe"] = copy_probe(torch)
@@ -514,6 +576,8 @@ def main():
         print("# moe done", file=sys.stderr, flush=True)
         secondary["quantize"] = bench_quantize(torch, fp4, workloads, args.steps)
         print("# quantize done", file=sys.stderr, flush=True)
+        secondary["decode_attention_fp4kv"] = bench_attention(torch, fp4, workloads, max(8, args.steps // 8))
+        print("# attention done", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads)
 
     traffic = load_traffic("gemv_decode_w4a16")

@@ -37,6 +37,8 @@
 #include "fp4_device.h"
 #include "fp4_kernels.h"
 
+#include <type_traits>
+
 using namespace fp4dev;
 
 namespace {
@@ -53,15 +55,19 @@ __device__ __forceinline__ int token_slot(int t) {
 }
 
 // --------------------------------------------------------------------------------------
-// Append: one workgroup (one wave) per (sequence, tile touched by the new tokens).
+// Append: one workgroup per (sequence, tile touched by the new tokens). All 256 threads
+// copy the tile's V codes into LDS and back (16 dwords each in flight for 8 heads); wave 0
+// quantizes the tile's new tokens one after another (V nibbles of two tokens share bytes).
+
+constexpr int kAppendThreads = 256;
 
 template <int IN_BF16>
-__global__ __launch_bounds__(64) void k_kv_append(fp4lib::KvCacheArgs c, const void* __restrict__ k_new,
+__global__ __launch_bounds__(kAppendThreads) void k_kv_append(fp4lib::KvCacheArgs c, const void* __restrict__ k_new,
                                                   const void* __restrict__ v_new, int64_t ld,
                                                   const int32_t* __restrict__ positions, int n_new) {
   extern __shared__ uint32_t vtile[];  // kv_heads x 512 dwords: the tile's V codes
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = threadIdx.x & 63;
   const int64_t T = c.max_tokens;
   const int64_t pos0 = positions[b];
   if (pos0 < 0) return;
@@ -76,15 +82,27 @@ __global__ __launch_bounds__(64) void k_kv_append(fp4lib::KvCacheArgs c, const v
 
   // the tile's current V codes (tokens of the tile that are not rewritten keep theirs)
   const bool whole = t_lo == tile * kTile && t_hi == tile * kTile + kTile;
-  for (int i = lane; i < H * 512; i += 64) {
-    const int h = i >> 9;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(
-        c.v_codes + (((int64_t)b * H + h) * tiles + tile) * 2048);
-    vtile[i] = whole ? 0u : src[i & 511];
+  for (int i0 = 0; i0 < H * 512; i0 += kAppendThreads * 16) {
+    uint32_t tmp[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {  // independent loads first
+      const int i = i0 + u * kAppendThreads + tid;
+      tmp[u] = 0u;
+      if (!whole && i < H * 512) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(
+            c.v_codes + (((int64_t)b * H + (i >> 9)) * tiles + tile) * 2048);
+        tmp[u] = src[i & 511];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * kAppendThreads + tid;
+      if (i < H * 512) vtile[i] = tmp[u];
+    }
   }
   __syncthreads();
 
-  for (int64_t t = t_lo; t < t_hi; ++t) {
+  if (tid < 64) for (int64_t t = t_lo; t < t_hi; ++t) {
     const int64_t row = (int64_t)b * n_new + (t - pos0);
     const int slot = token_slot((int)(t - tile * kTile));
     for (int base = 0; base < mv_count; base += 64) {  // uniform trip count: shuffles stay whole
@@ -135,9 +153,8 @@ __global__ __launch_bounds__(64) void k_kv_append(fp4lib::KvCacheArgs c, const v
     }
   }
   __syncthreads();
-  for (int i = lane; i < H * 512; i += 64) {
-    const int h = i >> 9;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(c.v_codes + (((int64_t)b * H + h) * tiles + tile) * 2048);
+  for (int i = tid; i < H * 512; i += kAppendThreads) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(c.v_codes + (((int64_t)b * H + (i >> 9)) * tiles + tile) * 2048);
     dst[i & 511] = vtile[i];
   }
 }
@@ -168,41 +185,51 @@ __device__ __forceinline__ half8_t decode_per_slot(uint32_t cw, uint32_t mu_lo, 
   return half8_t{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
 }
 
-// Everything one lane loads for one 32-token tile.
-struct TileLoads {
-  uint4 kc[2];      // K codes: token 16 mt + n, 16 bytes at 16 g
-  uint2 km[2];      // K micro-scales of that token
-  uint2 kM[2];      // K macro-scales of tokens 16 mt + 4g .. +3
-  uint32_t vc[8];   // V codes: column 16 dt + n, slots 8g .. 8g+7
-  uint2 vm[8];      // V micro-scales: block dt, slots 8g .. 8g+7
-  uint2 vM[2];      // V macro-scales of tokens 16 mt + 4g .. +3
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
+
+// One 32-token tile of one wave in LDS, each part laid out in the order its reader lanes
+// want it (the DMA lane that fetches a piece is the lane that later reads it):
+//   kc[mt][l]: token 16 mt + (l & 15), K code bytes 16 (l >> 4) .. +15;
+//   vc[h][l]:  V code row (column) d = 64 h + l, its 16 bytes (32 slots);
+//   km:        the tile's K micro-scales, token-major (8 bytes per token);
+//   vm:        the tile's V micro-scales, [block][slot].
+struct TileStage {
+  uint4 kc[2][64];
+  uint4 vc[2][64];
+  uint32_t km[64];
+  uint32_t vm[64];
 };
 
-struct AttnPtrs {
-  const uint8_t* kc;   // this (sequence, head)'s K codes
-  const uint8_t* km;
-  const uint16_t* kM;  // this (sequence, head pair)'s macro row
-  const uint8_t* vc;   // this (sequence, head)'s V tiles
-  const uint8_t* vm;
-  const uint16_t* vM;
-};
+constexpr int kStages = 3;  // tiles in flight per wave
+constexpr int kDmaPerTile = 6;
+static_assert(kDmaPerTile * (kStages - 1) < 64, "vmcnt range");
 
-__device__ __forceinline__ void load_tile(const AttnPtrs& p, int64_t t0, int n, int g, TileLoads& L) {
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int64_t tok = t0 + 16 * mt + n;
-    L.kc[mt] = *reinterpret_cast<const uint4*>(p.kc + tok * 64 + 16 * g);
-    L.km[mt] = *reinterpret_cast<const uint2*>(p.km + tok * 8);
-    L.kM[mt] = *reinterpret_cast<const uint2*>(p.kM + t0 + 16 * mt + 4 * g);
-    L.vM[mt] = *reinterpret_cast<const uint2*>(p.vM + t0 + 16 * mt + 4 * g);
-  }
-  const int64_t tile = t0 / kTile;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    L.vc[dt] = *reinterpret_cast<const uint32_t*>(p.vc + tile * 2048 + (16 * dt + n) * 16 + 4 * g);
-    L.vm[dt] = *reinterpret_cast<const uint2*>(p.vm + tile * 256 + dt * 32 + 8 * g);
-  }
+// One LDS object per ring stage (indexed by wave) and per macro row: reads of one stage
+// and copies into another are then provably disjoint, so the compiler adds no wait of its
+// own for the copies in flight.
+__shared__ TileStage g_st0[4];
+__shared__ TileStage g_st1[4];
+__shared__ TileStage g_st2[4];
+__shared__ uint16_t g_kM[4][kWaveTokens];  // macro-scales of each wave's 256 tokens
+__shared__ uint16_t g_vM[4][kWaveTokens];
+__shared__ float g_m[4][16];
+__shared__ float g_l[4][16];
+
+template <int S>
+__device__ __forceinline__ TileStage& stage_ref(int wave) {
+  if constexpr (S == 0) return g_st0[wave];
+  else if constexpr (S == 1) return g_st1[wave];
+  else return g_st2[wave];
 }
+
+// After the token loop a wave's results O[head][128] go to its own stage 0 (heads 0..8,
+// 9 x 512 bytes = one TileStage) and stage 1 (heads 9..15).
+__device__ __forceinline__ float* o_row(int wave, int h) {
+  return h < 9 ? reinterpret_cast<float*>(&g_st0[wave]) + h * kHeadDim
+               : reinterpret_cast<float*>(&g_st1[wave]) + (h - 9) * kHeadDim;
+}
+static_assert(sizeof(TileStage) == 9 * kHeadDim * 4, "nine head rows per stage");
 
 __device__ __forceinline__ float fp16_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
@@ -212,9 +239,6 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
                                                      int q_heads, const int32_t* __restrict__ lengths,
                                                      float scale_log2, float* __restrict__ partial,
                                                      int chunks) {
-  __shared__ float sm_o[4][16][kHeadDim];
-  __shared__ float sm_m[4][16];
-  __shared__ float sm_l[4][16];
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int H = c.kv_heads;
   const int64_t T = c.max_tokens;
@@ -222,20 +246,68 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
   const int64_t chunk_lo = (int64_t)chunk * kChunk;
   if (chunk_lo >= L) return;  // whole workgroup
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
   const int n = lane & 15, g = lane >> 4;
   const int group = q_heads / H;
 
-  AttnPtrs p;
+  // Raw buffer resources over this (sequence, head)'s arrays: every copy below is bounded
+  // by the array (reads past it return zero), so tiles past the cache can be requested.
+  const int64_t th = (int64_t)b * H + kvh, pair = (int64_t)b * (H / 2) + (kvh >> 1);
+  const __amdgpu_buffer_rsrc_t kc_r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.k_codes + th * T * 64), (short)0, (int)(T * 64), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t km_r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.k_micro + th * T * 8), (short)0, (int)(T * 8), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vc_r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.v_codes + th * (T / kTile) * 2048), (short)0, (int)(T * 64), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vm_r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.v_micro + th * (T / kTile) * 256), (short)0, (int)(T * 8), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t kM_r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.k_macro + pair * T), (short)0, (int)(T * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vM_r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.v_macro + pair * T), (short)0, (int)(T * 2), kRsrcWord3);
+
+  const int64_t w_lo = chunk_lo + (int64_t)wave * kWaveTokens;
+  const int64_t w_hi = min(L, w_lo + kWaveTokens);
+  const int n_tiles = w_hi > w_lo ? (int)((w_hi - w_lo + kTile - 1) / kTile) : 0;
+
+  // the query rows first (plain loads, older than every copy below)
+  const bool q_real = n < group;
+  uint4 qraw[4];
   {
-    const int64_t th = (int64_t)b * H + kvh, pair = (int64_t)b * (H / 2) + (kvh >> 1);
-    p.kc = c.k_codes + th * T * 64;
-    p.km = c.k_micro + th * T * 8;
-    p.kM = c.k_macro + pair * T;
-    p.vc = c.v_codes + th * (T / kTile) * 2048;
-    p.vm = c.v_micro + th * (T / kTile) * 256;
-    p.vM = c.v_macro + pair * T;
+    // padding columns load the KV head's first query row (no branch around the loads) and
+    // are zeroed below
+    const int qn = q_real ? n : 0;
+    const uint16_t* qh = q + ((int64_t)b * q_heads + (int64_t)kvh * group + qn) * kHeadDim;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qh + 32 * s + 8 * g);
   }
+
+  // the wave's macro-scales (4 copies of 256 bytes), then the first kStages - 1 tiles
+  const uint32_t w_lo32 = (uint32_t)w_lo;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kM_r, (lds_void_ptr)(g_kM[wave] + 128 * i), 4,
+                                             (uint32_t)lane * 4, w_lo32 * 2 + 256 * i, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vM_r, (lds_void_ptr)(g_vM[wave] + 128 * i), 4,
+                                             (uint32_t)lane * 4, w_lo32 * 2 + 256 * i, 0, 0);
+  }
+  const uint32_t kc_voff = (uint32_t)(n * 64 + 16 * g);
+  auto issue_tile = [&](TileStage& s, int it) {
+    const uint32_t t0 = w_lo32 + (uint32_t)it * kTile;  // may lie past the cache: reads give 0
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kc_r, (lds_void_ptr)s.kc[mt], 16, kc_voff,
+                                               t0 * 64 + 1024 * mt, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vc_r, (lds_void_ptr)s.vc[h], 16, (uint32_t)lane * 16,
+                                               (t0 / kTile) * 2048 + 1024 * h, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(km_r, (lds_void_ptr)s.km, 4, (uint32_t)lane * 4, t0 * 8, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vm_r, (lds_void_ptr)s.vm, 4, (uint32_t)lane * 4,
+                                             (t0 / kTile) * 256, 0, 0);
+  };
+  issue_tile(stage_ref<0>(wave), 0);
+  issue_tile(stage_ref<1>(wave), 1);
 
   // Q'^T operand: column n is query head kvh * group + n (zero for n >= group); k-step s,
   // lane group g holds d = 32s + 8g .. +7. One power of two per head brings max|q| into
@@ -245,13 +317,10 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
   {
     float qv[4][8];
     float qmax = 0.0f;
-    const bool real = n < group;
-    const uint16_t* qh = q + ((int64_t)b * q_heads + (int64_t)kvh * group + n) * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-      if (real) raw = *reinterpret_cast<const uint4*>(qh + 32 * s + 8 * g);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t w[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
+      if (!q_real) w[0] = w[1] = w[2] = w[3] = 0u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         qv[s][2 * i] = __uint_as_float(w[i] << 16);
@@ -274,19 +343,16 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
     smul = scale_log2 * 256.0f / sq;
   }
 
-  const int64_t w_lo = chunk_lo + (int64_t)wave * kWaveTokens;
-  const int64_t w_hi = min(L, w_lo + kWaveTokens);
-  const int n_tiles = w_hi > w_lo ? (int)((w_hi - w_lo + kTile - 1) / kTile) : 0;
-
-  // reference for the value macro-scales of this wave's tokens
-  float mref = 0.0f;
-  if (n_tiles > 0 && w_lo + 4 * lane < w_hi) {  // t < L <= T, T % 32 == 0: t + 3 < T
-    const int64_t t = w_lo + 4 * lane;
-    const uint2 mm = *reinterpret_cast<const uint2*>(p.vM + t);
+  // the macro copies were issued first: at most the kStages - 1 tiles behind them pending
+  // (the q load above is a plain load the compiler already waited for)
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<kDmaPerTile * (kStages - 1)>::value);
+  float mref = 0.0f;  // reference for the value macro-scales of this wave's tokens
+  {
+    const uint2 mm = *reinterpret_cast<const uint2*>(g_vM[wave] + 4 * lane);
     const uint32_t hs[4] = {mm.x & 0xFFFFu, mm.x >> 16, mm.y & 0xFFFFu, mm.y >> 16};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (t + i < w_hi) mref = fmaxf(mref, fp16_bits_to_float(hs[i]));
+      if (w_lo + 4 * lane + i < w_hi) mref = fmaxf(mref, fp16_bits_to_float(hs[i]));
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) mref = fmaxf(mref, __shfl_xor(mref, o));
@@ -298,22 +364,26 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) acc_o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  TileLoads cur, nxt;
-  if (n_tiles > 0) load_tile(p, w_lo, n, g, cur);
-  for (int it = 0; it < n_tiles; ++it) {
+  // one tile; S = it % kStages as a constant
+  auto step = [&](auto s_const, int it) {
+    constexpr int S = decltype(s_const)::value;
+    issue_tile(stage_ref<(S + kStages - 1) % kStages>(wave), it + kStages - 1);  // stage of tile it - 1
+    __builtin_amdgcn_s_waitcnt(kVmcntWait<kDmaPerTile * (kStages - 1)>::value);  // tile it has landed
+    const TileStage& st = stage_ref<S>(wave);
     const int64_t t0 = w_lo + (int64_t)it * kTile;
-    if (it + 1 < n_tiles) load_tile(p, t0 + kTile, n, g, nxt);
 
     // S^T for the two 16-token halves
     float4_t acc_s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       acc_s[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-      const uint32_t cw[4] = {cur.kc[mt].x, cur.kc[mt].y, cur.kc[mt].z, cur.kc[mt].w};
+      const uint4 kc = st.kc[mt][lane];
+      const uint2 km = *reinterpret_cast<const uint2*>(&st.km[2 * (16 * mt + n)]);
+      const uint32_t cw[4] = {kc.x, kc.y, kc.z, kc.w};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int blk = 2 * s + (g >> 1);  // micro-block of d = 32s + 8g
-        const uint32_t mb = ((blk < 4 ? cur.km[mt].x : cur.km[mt].y) >> (8 * (blk & 3))) & 0xFFu;
+        const uint32_t mb = ((blk < 4 ? km.x : km.y) >> (8 * (blk & 3))) & 0xFFu;
         const half8_t a = decode_uniform(cw[s], (mb << 7) | (mb << 23));
         acc_s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[s], acc_s[mt], 0, 0, 0);
       }
@@ -322,8 +392,11 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
     float sc[8], vr[8];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const uint32_t kh[4] = {cur.kM[mt].x & 0xFFFFu, cur.kM[mt].x >> 16, cur.kM[mt].y & 0xFFFFu, cur.kM[mt].y >> 16};
-      const uint32_t vh[4] = {cur.vM[mt].x & 0xFFFFu, cur.vM[mt].x >> 16, cur.vM[mt].y & 0xFFFFu, cur.vM[mt].y >> 16};
+      const int tk = it * kTile + 16 * mt + 4 * g;  // token index inside the wave
+      const uint2 kM = *reinterpret_cast<const uint2*>(g_kM[wave] + tk);
+      const uint2 vM = *reinterpret_cast<const uint2*>(g_vM[wave] + tk);
+      const uint32_t kh[4] = {kM.x & 0xFFFFu, kM.x >> 16, kM.y & 0xFFFFu, kM.y >> 16};
+      const uint32_t vh[4] = {vM.x & 0xFFFFu, vM.x >> 16, vM.y & 0xFFFFu, vM.y >> 16};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool live = t0 + 16 * mt + 4 * g + i < L;
@@ -371,39 +444,50 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const half8_t a = decode_per_slot(cur.vc[dt], cur.vm[dt].x & keep_lo, cur.vm[dt].y & keep_hi);
+      // column d = 16 dt + n is V code row 64 (dt / 4) + 16 (dt % 4) + n; its dword g holds
+      // slots 8g .. 8g + 7
+      const uint32_t vc = reinterpret_cast<const uint32_t*>(&st.vc[dt >> 2][16 * (dt & 3) + n])[g];
+      const uint2 vm = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(st.vm) + dt * 32 + 8 * g);
+      const half8_t a = decode_per_slot(vc, vm.x & keep_lo, vm.y & keep_hi);
       acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp, acc_o[dt], 0, 0, 0);
       acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp_lo, acc_o[dt], 0, 0, 0);
     }
-    if (it + 1 < n_tiles) cur = nxt;
+  };
+  for (int it0 = 0; it0 < n_tiles; it0 += kStages) {
+    step(std::integral_constant<int, 0>(), it0);
+    if (it0 + 1 < n_tiles) step(std::integral_constant<int, 1>(), it0 + 1);
+    if (it0 + 2 < n_tiles) step(std::integral_constant<int, 2>(), it0 + 2);
   }
+  // copies issued past the last tile must land before the ring is reused below
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
 
   // per-head sum over the four lane groups, then the wave's results into LDS
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   const float o_mul = mref * (1.0f / 16.0f);  // V' unit 2^-8 times P'' unit 2^12 / M_ref
-  if (n < group) {
+  if (n < group) {  // into this wave's own stages (no other wave reads them before the barrier)
     if (g == 0) {
-      sm_m[wave][n] = m_run;
-      sm_l[wave][n] = l_run;
+      g_m[wave][n] = m_run;
+      g_l[wave][n] = l_run;
     }
+    float* orow = o_row(wave, n);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[wave][n][16 * dt + 4 * g + i] = acc_o[dt][i] * o_mul;
+      for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = acc_o[dt][i] * o_mul;
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < group * kHeadDim; idx += 256) {
     const int h = idx / kHeadDim, d = idx % kHeadDim;
-    float m = sm_m[0][h];
+    float m = g_m[0][h];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) m = fmaxf(m, sm_m[w][h]);
+    for (int w = 1; w < 4; ++w) m = fmaxf(m, g_m[w][h]);
     float o = 0.0f, l = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = sm_m[w][h] == -INFINITY ? 0.0f : exp2f(sm_m[w][h] - m);
-      o += f * sm_o[w][h][d];
-      l += f * sm_l[w][h];
+      const float f = g_m[w][h] == -INFINITY ? 0.0f : exp2f(g_m[w][h] - m);
+      o += f * o_row(w, h)[d];
+      l += f * g_l[w][h];
     }
     float* dst = partial + (((int64_t)b * q_heads + (int64_t)kvh * group + h) * chunks + chunk) * kPartial;
     dst[d] = o;
@@ -457,7 +541,7 @@ hipError_t launch_kv_append(const KvCacheArgs& c, const void* k_new, const void*
                             int64_t ld, const int32_t* positions, int n_new, hipStream_t st) {
   if (!kv_cache_supports((int)c.max_tokens, c.kv_heads, kHeadDim) || n_new < 1 || c.n_seq < 1)
     return hipErrorInvalidValue;
-  const dim3 grid((unsigned)c.n_seq, (unsigned)(n_new / kTile + 2)), block(64);
+  const dim3 grid((unsigned)c.n_seq, (unsigned)(n_new / kTile + 2)), block(kAppendThreads);
   const size_t lds = (size_t)c.kv_heads * 2048;
   if (in_bf16)
     hipLaunchKernelGGL(k_kv_append<1>, grid, block, lds, st, c, k_new, v_new, ld, positions, n_new);

@@ -21,7 +21,8 @@ import numpy as np
 
 __all__ = ["normal", "to_bf16_values", "outlier_channels", "tiny", "decode", "prefill",
            "policy_flags", "policy_outliers", "policy_layer", "moe_router_logits", "moe_tokens",
-           "moe_expert_weights", "moe_down_inputs", "WORKLOADS"]
+           "moe_expert_weights", "moe_down_inputs", "kv_lengths", "kv_key_outliers", "kv_queries",
+           "kv_rows_device", "WORKLOADS"]
 
 WORKLOADS = {
     "tiny_w4a16": dict(seed=0, m=16, k=512, n=256),
@@ -29,6 +30,8 @@ WORKLOADS = {
     "prefill_w4a4": dict(seed=2, m=2048, k=4096, n=4096, outlier_frac=0.005, outlier_gain=50.0),
     "policy_stack": dict(seed=3, layers=8, flagged=2, m=512, k=5120, n=5120,
                          outlier_frac=0.005, outlier_gain=50.0),
+    "decode_attention_fp4kv": dict(seed=5, n_seq=32, q_heads=32, kv_heads=8, head_dim=128,
+                                   max_tokens=16384, min_len=8192, max_len=16383),
     "moe_w4a4": dict(seed=4, experts=128, top_k=8, tokens=4096, hidden=2048,
                      inter=768, outlier_frac=0.005, outlier_gain=50.0),
 }
@@ -133,3 +136,31 @@ def moe_down_inputs(rows: int, inter=768, seed=4):
     """Stand-in inputs of the down projection alone, bf16 [rows, inter] ~ N(0, 1) (for
     tests of the plain grouped product; the layer itself feeds it silu(gate) * up)."""
     return to_bf16_values(normal(_child(seed, 3), 1.0, (rows, inter)))
+
+
+def kv_lengths(n_seq=32, min_len=8192, max_len=16383, seed=5) -> np.ndarray:
+    """Cached tokens per sequence before the decode step, int32 uniform in [min_len, max_len]."""
+    return _child(seed, 0).integers(min_len, max_len + 1, size=n_seq).astype(np.int32)
+
+
+def kv_key_outliers(width=1024, frac=0.005, seed=5) -> np.ndarray:
+    """Key channels (of the kv_heads * head_dim row) scaled up: 0.5% of them."""
+    return outlier_channels(_child(seed, 1), width, frac)
+
+
+def kv_queries(n_seq=32, q_heads=32, head_dim=128, seed=5) -> np.ndarray:
+    """Decode queries, bf16 values of N(0, 1) [n_seq, q_heads, head_dim]."""
+    return to_bf16_values(normal(_child(seed, 2), 1.0, (n_seq, q_heads, head_dim)))
+
+
+def kv_rows_device(torch, rows: int, width: int, seed: int, stream: int, outliers=None,
+                   gain: float = 20.0, device="cuda"):
+    """Cache rows bf16 [rows, width] ~ N(0, 1) from torch's seeded generator on the device
+    (about 10^9 values at full size are too many to draw on the host); ``outliers``
+    channels scaled by ``gain``. Tests copy the rows they check back to the host."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1000 + stream)
+    x = torch.randn(rows, width, generator=g, device=device, dtype=torch.float32)
+    if outliers is not None and len(outliers):
+        x[:, torch.as_tensor(np.asarray(outliers), device=device)] *= gain
+    return x.to(torch.bfloat16)
