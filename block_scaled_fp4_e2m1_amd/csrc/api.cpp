@@ -347,7 +347,8 @@ namespace {
 fp4_status check_kv_cache(const fp4_kv_cache* c) {
   if (!c || !c->k_codes || !c->k_micro || !c->k_macro || !c->v_codes || !c->v_micro || !c->v_macro)
     return FP4_E_NULL;
-  if (c->n_seq < 1 || c->n_seq > 65535 ||
+  // per (sequence, head) arrays stay under 2^31 bytes (32-bit buffer offsets)
+  if (c->n_seq < 1 || c->n_seq > 65535 || c->max_tokens > (1 << 24) ||
       !fp4lib::kv_cache_supports(c->max_tokens, c->kv_heads, c->head_dim))
     return FP4_E_SHAPE;
   if (!aligned16(c->k_codes) || !aligned16(c->v_codes) || !aligned(c->k_micro, 8) ||

@@ -30,7 +30,7 @@
 //   of two per head (exact), so the scores are exact products accumulated in float32;
 //   online softmax per head in base 2;
 //   O^T += V'^T . P''^T by 16 MFMAs (rows: 16 head-dim columns; k: 32 slots); V' = e2m1 *
-//   mu * 2^-8 (per-slot micro-scales, exact in FP16), P'' = p * 2^12 * M_V[t] / M_ref
+//   mu (per-slot micro-scales, exact in FP16), P'' = p * 2^12 * M_V[t] / M_ref
 //   (M_ref the largest value macro-scale of the wave's tokens) as an FP16 pair hi + lo,
 //   one MFMA each, so the weights keep ~22 bits.
 // Waves are combined through LDS; chunks by k_attn_combine.
@@ -45,8 +45,14 @@ namespace {
 
 constexpr int kHeadDim = 128;
 constexpr int kTile = 32;          // tokens per tile
-constexpr int kWaveTokens = 256;   // tokens per wave and chunk
-constexpr int kChunk = 1024;       // tokens per attention workgroup
+#ifndef FP4_ATTN_WAVE_TOKENS
+#define FP4_ATTN_WAVE_TOKENS 512
+#endif
+#ifndef FP4_ATTN_STAGES
+#define FP4_ATTN_STAGES 2
+#endif
+constexpr int kWaveTokens = FP4_ATTN_WAVE_TOKENS;  // tokens per wave
+constexpr int kChunk = 4 * kWaveTokens;            // tokens per attention workgroup
 constexpr int kPartial = kHeadDim + 2;  // O[128], m, l per (sequence, head, chunk)
 
 // slot of token t (0..31) inside its tile, and back
@@ -57,7 +63,8 @@ __device__ __forceinline__ int token_slot(int t) {
 // --------------------------------------------------------------------------------------
 // Append: one workgroup per (sequence, tile touched by the new tokens). All 256 threads
 // copy the tile's V codes into LDS and back (16 dwords each in flight for 8 heads); wave 0
-// quantizes the tile's new tokens one after another (V nibbles of two tokens share bytes).
+// quantizes the tile's new key rows and wave 1 its value rows, each one token after
+// another (the V nibbles of two tokens share bytes; only wave 1 touches them).
 
 constexpr int kAppendThreads = 256;
 
@@ -102,15 +109,15 @@ __global__ __launch_bounds__(kAppendThreads) void k_kv_append(fp4lib::KvCacheArg
   }
   __syncthreads();
 
-  if (tid < 64) for (int64_t t = t_lo; t < t_hi; ++t) {
+  const int which = tid >> 6;  // 0: keys, 1: values, 2-3: copy only
+  if (which < 2) for (int64_t t = t_lo; t < t_hi; ++t) {
     const int64_t row = (int64_t)b * n_new + (t - pos0);
     const int slot = token_slot((int)(t - tile * kTile));
     for (int base = 0; base < mv_count; base += 64) {  // uniform trip count: shuffles stay whole
       const int mv = base + lane;
       const bool live = mv < mv_count;
       const int h = mv >> 3, j = mv & 7;  // head, micro-vector inside the head
-#pragma unroll
-      for (int which = 0; which < 2; ++which) {
+      {
         const void* src = which ? v_new : k_new;
         float v[16];
         if (live) {
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(kAppendThreads) void k_kv_append(fp4lib::KvCacheArg
         const float s = block_scales(v, 6.0f, m_bits, mu_byte, m_val);
         uint32_t w0, w1;
         e2m1_encode16(v, s, w0, w1);
-        if (!live) continue;
+        if (live) {
         const int64_t th = (int64_t)b * H + h;          // (sequence, head)
         const int64_t pair = (int64_t)b * (H / 2) + (h >> 1);
         if (which == 0) {
@@ -148,6 +155,7 @@ __global__ __launch_bounds__(kAppendThreads) void k_kv_append(fp4lib::KvCacheArg
             uint8_t* p = hb + (16 * j + e) * 16;
             *p = (uint8_t)((*p & keep) | (code << sh));
           }
+        }
         }
       }
     }
@@ -171,13 +179,14 @@ __device__ __forceinline__ half8_t decode_uniform(uint32_t cw, uint32_t mu_op) {
   return half8_t{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
 }
 
-// 8 codes with one micro-scale each: bytes of (lo, hi) are the 8 E4M3 micro-scales
+// 8 codes with one micro-scale each: bytes of (lo, hi) are the 8 E4M3 micro-scales, turned
+// into FP16 pairs by the hardware conversion (every E4M3 value is an FP16 value); the
+// products e2m1 * mu (at most 6 significant bits, 2^-10 .. 2688) are exact in FP16
 __device__ __forceinline__ half8_t decode_per_slot(uint32_t cw, uint32_t mu_lo, uint32_t mu_hi) {
-  // E4M3 byte << 7 in an FP16 half is mu * 2^-8
-  const half2_t m01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, mu_lo, 0x0C010C00u) << 7);
-  const half2_t m23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, mu_lo, 0x0C030C02u) << 7);
-  const half2_t m45 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, mu_hi, 0x0C010C00u) << 7);
-  const half2_t m67 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, mu_hi, 0x0C030C02u) << 7);
+  const half2_t m01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(mu_lo, 1.0f, false);
+  const half2_t m23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(mu_lo, 1.0f, true);
+  const half2_t m45 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(mu_hi, 1.0f, false);
+  const half2_t m67 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(mu_hi, 1.0f, true);
   const half2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * m01;
   const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * m23;
   const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * m45;
@@ -201,7 +210,8 @@ struct TileStage {
   uint32_t vm[64];
 };
 
-constexpr int kStages = 3;  // tiles in flight per wave
+constexpr int kStages = FP4_ATTN_STAGES;  // ring depth: tiles in flight per wave
+static_assert(kStages == 2 || kStages == 3, "ring depth");
 constexpr int kDmaPerTile = 6;
 static_assert(kDmaPerTile * (kStages - 1) < 64, "vmcnt range");
 
@@ -210,8 +220,8 @@ static_assert(kDmaPerTile * (kStages - 1) < 64, "vmcnt range");
 // own for the copies in flight.
 __shared__ TileStage g_st0[4];
 __shared__ TileStage g_st1[4];
-__shared__ TileStage g_st2[4];
-__shared__ uint16_t g_kM[4][kWaveTokens];  // macro-scales of each wave's 256 tokens
+__shared__ TileStage g_st2[kStages > 2 ? 4 : 1];
+__shared__ uint16_t g_kM[4][kWaveTokens];  // macro-scales of each wave's tokens
 __shared__ uint16_t g_vM[4][kWaveTokens];
 __shared__ float g_m[4][16];
 __shared__ float g_l[4][16];
@@ -219,7 +229,7 @@ __shared__ float g_l[4][16];
 template <int S>
 __device__ __forceinline__ TileStage& stage_ref(int wave) {
   if constexpr (S == 0) return g_st0[wave];
-  else if constexpr (S == 1) return g_st1[wave];
+  else if constexpr (S == 1 || kStages == 2) return g_st1[wave];
   else return g_st2[wave];
 }
 
@@ -282,32 +292,35 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
     for (int s = 0; s < 4; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qh + 32 * s + 8 * g);
   }
 
-  // the wave's macro-scales (4 copies of 256 bytes), then the first kStages - 1 tiles
+  // the wave's macro-scales (copies of 256 bytes), then the first kStages - 1 tiles
   const uint32_t w_lo32 = (uint32_t)w_lo;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kWaveTokens / 128; ++i) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kM_r, (lds_void_ptr)(g_kM[wave] + 128 * i), 4,
                                              (uint32_t)lane * 4, w_lo32 * 2 + 256 * i, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vM_r, (lds_void_ptr)(g_vM[wave] + 128 * i), 4,
                                              (uint32_t)lane * 4, w_lo32 * 2 + 256 * i, 0, 0);
   }
   const uint32_t kc_voff = (uint32_t)(n * 64 + 16 * g);
+  // a tile past the wave's range gets an offset past every resource (2^31 > T * 64): the
+  // copy returns zeros without touching memory and the wait counts stay fixed
   auto issue_tile = [&](TileStage& s, int it) {
-    const uint32_t t0 = w_lo32 + (uint32_t)it * kTile;  // may lie past the cache: reads give 0
+    const uint32_t oob = it < n_tiles ? 0u : 0x80000000u;
+    const uint32_t t0 = w_lo32 + (uint32_t)it * kTile;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kc_r, (lds_void_ptr)s.kc[mt], 16, kc_voff,
-                                               t0 * 64 + 1024 * mt, 0, 0);
+                                               (t0 * 64 + 1024 * mt) | oob, 0, 0);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vc_r, (lds_void_ptr)s.vc[h], 16, (uint32_t)lane * 16,
-                                               (t0 / kTile) * 2048 + 1024 * h, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(km_r, (lds_void_ptr)s.km, 4, (uint32_t)lane * 4, t0 * 8, 0, 0);
+                                               ((t0 / kTile) * 2048 + 1024 * h) | oob, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(km_r, (lds_void_ptr)s.km, 4, (uint32_t)lane * 4, (t0 * 8) | oob, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vm_r, (lds_void_ptr)s.vm, 4, (uint32_t)lane * 4,
-                                             (t0 / kTile) * 256, 0, 0);
+                                             ((t0 / kTile) * 256) | oob, 0, 0);
   };
   issue_tile(stage_ref<0>(wave), 0);
-  issue_tile(stage_ref<1>(wave), 1);
+  if constexpr (kStages > 2) issue_tile(stage_ref<1>(wave), 1);
 
   // Q'^T operand: column n is query head kvh * group + n (zero for n >= group); k-step s,
   // lane group g holds d = 32s + 8g .. +7. One power of two per head brings max|q| into
@@ -347,12 +360,14 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
   // (the q load above is a plain load the compiler already waited for)
   __builtin_amdgcn_s_waitcnt(kVmcntWait<kDmaPerTile * (kStages - 1)>::value);
   float mref = 0.0f;  // reference for the value macro-scales of this wave's tokens
-  {
-    const uint2 mm = *reinterpret_cast<const uint2*>(g_vM[wave] + 4 * lane);
+#pragma unroll
+  for (int part = 0; part < kWaveTokens / 256; ++part) {
+    const int t = 256 * part + 4 * lane;  // token inside the wave
+    const uint2 mm = *reinterpret_cast<const uint2*>(g_vM[wave] + t);
     const uint32_t hs[4] = {mm.x & 0xFFFFu, mm.x >> 16, mm.y & 0xFFFFu, mm.y >> 16};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (w_lo + 4 * lane + i < w_hi) mref = fmaxf(mref, fp16_bits_to_float(hs[i]));
+      if (w_lo + t + i < w_hi) mref = fmaxf(mref, fp16_bits_to_float(hs[i]));
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) mref = fmaxf(mref, __shfl_xor(mref, o));
@@ -410,22 +425,26 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
     float psum = 0.0f;
     half8_t bp, bp_lo;  // P'' as an FP16 pair: hi + lo carries ~22 bits of the float32 value
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float pr = exp2f(sc[i] - m_new);
+      const float pr = __builtin_amdgcn_exp2f(sc[i] - m_new);  // v_exp_f32; -inf gives 0
       psum += pr;
       const float x = pr * vr[i];
       const _Float16 hi = (_Float16)x;
       bp[i] = hi;
       bp_lo[i] = (_Float16)(x - (float)hi);
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    // rescale only when some column's running max grew (rare after the first tiles)
+    if (__ballot(m_new > m_run) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc_o[dt] *= alpha;
+      for (int dt = 0; dt < 8; ++dt) acc_o[dt] *= alpha;
+    }
+    l_run += psum;
+    m_run = m_new;
 
     // O^T += V'^T . P''^T; slots of tokens past the length get micro-scale 0 (their cache
     // bytes may hold anything)
@@ -456,7 +475,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
   for (int it0 = 0; it0 < n_tiles; it0 += kStages) {
     step(std::integral_constant<int, 0>(), it0);
     if (it0 + 1 < n_tiles) step(std::integral_constant<int, 1>(), it0 + 1);
-    if (it0 + 2 < n_tiles) step(std::integral_constant<int, 2>(), it0 + 2);
+    if constexpr (kStages > 2)
+      if (it0 + 2 < n_tiles) step(std::integral_constant<int, 2>(), it0 + 2);
   }
   // copies issued past the last tile must land before the ring is reused below
   __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
@@ -464,7 +484,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
   // per-head sum over the four lane groups, then the wave's results into LDS
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  const float o_mul = mref * (1.0f / 16.0f);  // V' unit 2^-8 times P'' unit 2^12 / M_ref
+  const float o_mul = mref * (1.0f / 4096.0f);  // P'' unit 2^12 / M_ref (V' = e2m1 * mu)
   if (n < group) {  // into this wave's own stages (no other wave reads them before the barrier)
     if (g == 0) {
       g_m[wave][n] = m_run;
@@ -508,13 +528,32 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
   const int64_t L = min((int64_t)max(lengths[b], 0), max_tokens);
   const int used = (int)((L + kChunk - 1) / kChunk);
   const float* src = partial + (int64_t)bh * chunks * kPartial;
-  float m = -INFINITY;
-  for (int ch = 0; ch < used; ++ch) m = fmaxf(m, src[ch * kPartial + kHeadDim]);
-  float o = 0.0f, l = 0.0f;
-  for (int ch = 0; ch < used; ++ch) {
-    const float f = exp2f(src[ch * kPartial + kHeadDim] - m);
-    o += f * src[ch * kPartial + d];
-    l += f * src[ch * kPartial + kHeadDim + 1];
+  // batches of 8 chunks, each batch's loads issued together, merged online
+  float m = -INFINITY, o = 0.0f, l = 0.0f;
+  for (int c0 = 0; c0 < used; c0 += 8) {
+    float mc[8], oc[8], lc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool live = c0 + i < used;
+      const float* p = src + (int64_t)(live ? c0 + i : 0) * kPartial;
+      mc[i] = live ? p[kHeadDim] : -INFINITY;
+      lc[i] = p[kHeadDim + 1];
+      oc[i] = p[d];
+    }
+    float mb = mc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mb = fmaxf(mb, mc[i]);
+    const float mn = fmaxf(m, mb);
+    const float f = m == -INFINITY ? 0.0f : exp2f(m - mn);
+    o *= f;
+    l *= f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float w = mc[i] == -INFINITY ? 0.0f : exp2f(mc[i] - mn);
+      o += w * oc[i];
+      l += w * lc[i];
+    }
+    m = mn;
   }
   const float r = used > 0 ? o / l : 0.0f;
   if (OUT_BF16)

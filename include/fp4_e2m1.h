@@ -216,7 +216,7 @@ fp4_status moe_combine(const void* y, int32_t y_dtype, int64_t ldy, const int32_
  * Codec reading: each token's key (value) vector over all KV heads (kv_heads x head_dim
  * elements) is one codec row: E2M1 codes, an E4M3 micro-scale per 16 elements, an FP16
  * macro-scale per 256 (a pair of heads). head_dim must be 128, kv_heads even and <= 32,
- * max_tokens a multiple of 32 (FP4_E_SHAPE otherwise).
+ * max_tokens a multiple of 32 and at most 2^24 (FP4_E_SHAPE otherwise).
  *
  * Device layout (all arrays caller-owned device memory, T = max_tokens):
  *   k_codes [n_seq][kv_heads][T][64 B]: per token-head, dword 4g + s holds the codes of
