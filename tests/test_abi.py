@@ -155,7 +155,8 @@ def test_kv_entry_points_validate_before_device_use(lib):
     for bad in ((1, 40, 2, 128), (1, 64, 3, 128), (1, 64, 2, 64), (1, 64, 34, 128), (0, 64, 2, 128),
                 (1, 16, 2, 128)):
         assert lib.fp4_kv_cache_bytes(*bad, 0) == 0
-    assert lib.attention_workspace_bytes(32, 32, 16384) == 32 * 32 * 16 * 130 * 4
+    # 2048-token chunks: 8 per sequence at 16384 tokens; O[128], m, l per (sequence, head, chunk)
+    assert lib.attention_workspace_bytes(32, 32, 16384) == 32 * 32 * 8 * 130 * 4
     good = KV(1 << 20, 1 << 21, 1 << 22, 1 << 23, 1 << 24, 1 << 25, 4, 64, 2, 128)
     assert lib.kv_cache_append(None, fake, fake, 1, 256, fake, 1, null) == 1
     assert lib.kv_cache_append(ctypes.byref(good), fake, fake, 1, 255, fake, 1, null) == 2
