@@ -58,6 +58,7 @@ def source_hash(files):
 KERNEL_SOURCES = {
     "gemv": ["block_scaled_fp4_e2m1_amd/csrc/gemv.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
     "gemm": ["block_scaled_fp4_e2m1_amd/csrc/gemm.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
+    "attention": ["block_scaled_fp4_e2m1_amd/csrc/attention.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
 }
 
 
@@ -465,6 +466,7 @@ def bench_attention(torch, fp4, workloads, steps):
                 step_s=res["step"], attention_s=res["attention"],
                 gbs_attention=total / res["attention"] / 1e9, gbs_step=total / res["step"] / 1e9,
                 frac_hbm_attention=total / res["attention"] / 1e9 / HBM_PEAK_GBS,
+                traffic_bytes_per_launch=load_traffic("attention_decode_fp4kv"),
                 layers_rotated=len(caches))
 
 

@@ -23,8 +23,9 @@
 // Slot 8g + i of a tile is token 4g + i (i < 4) or 16 + 4g + i - 4 (i >= 4): the k order in
 // which the P.V step meets the tile's tokens, so one dword gives a lane its 8 tokens.
 //
-// Attention (k_attn_decode): one workgroup per (sequence, KV head, chunk of 1024 tokens),
-// 4 waves of 256 tokens, 32-token tiles. Per tile and wave:
+// Attention (k_attn_decode): one workgroup per (sequence, KV head, chunk of 2048 tokens),
+// 4 waves of 512 tokens, 32-token tiles copied by LDS-DMA into a two-stage ring per wave
+// (the next tile lands while the current one is computed). Per tile and wave:
 //   S^T = K' . Q'^T by 8 MFMA 16x16x32 f16 (rows: 16 tokens; columns: the KV head's query
 //   heads, up to 16); K' = e2m1 * mu * 2^-8 is exact in FP16; Q' = q * 2^e with one power
 //   of two per head (exact), so the scores are exact products accumulated in float32;
