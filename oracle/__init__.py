@@ -1,7 +1,8 @@
 """CPU oracle for two-level block-scaled FP4 (E2M1 elements, E4M3 micro-scales per 16,
 FP16 macro-scales per 256), the W4A16 / W4A8 / W4A4 products built on it, the
 mixture-of-experts layer steps around the grouped product (routing, gated activation,
-combine), and decode attention over a KV cache kept in the same format.
+combine), decode attention over a KV cache kept in the same format, and the MX-native
+FP4 variant (E8M0 power-of-two scale per 32) with its product.
 
 TEST INFRASTRUCTURE ONLY. A plain, slow, float64 numpy restatement of the method that
 the HIP library is checked against. It shares no code with the library. Only tests,
@@ -18,3 +19,4 @@ from .gemm import (activation_values, gemm, gemm_bf16, grouped_gemm, policy_sele
                    A16, A8, A4, POLICY_AUTO, POLICY_Q4, POLICY_Q8)
 from .moe import route, silu_gate, combine
 from .attention import kv_quantize_rows, kv_dequantize_rows, attention_decode
+from .mx import MX_BLOCK, e8m0_value, mx_quantize, mx_dequantize, mx_gemm
