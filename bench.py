@@ -174,6 +174,46 @@ def bench_prefill(torch, fp4, workloads, steps):
                 bytes=algorithmic_bytes_gemm(m, n, k))
 
 
+def bench_mx(torch, fp4, workloads, steps):
+    """The prefill product (2048 x 4096 x 4096) in the MX-native FP4 format on the
+    block-scaled FP4 matrix instruction: per step the activations are quantized (E2M1,
+    E8M0 per 32) and multiplied; the weights are quantized once. Also reports the accuracy
+    of both formats against the unquantized float32 product of the same inputs (relative
+    Frobenius error), the two-level W4A4 path of the pages beside the MX one."""
+    m, k, n = 2048, 4096, 4096
+    a, w, _ = workloads.prefill()
+    wd = torch.from_numpy(w).cuda()
+    ad = torch.from_numpy(a).cuda().to(torch.bfloat16)
+    wq = fp4.quantize_mxfp4(wd)
+    aq = fp4.quantize_mxfp4(ad)
+    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    step = lambda: (fp4.quantize_mxfp4(ad, out=aq), fp4.gemm_mxfp4(aq, wq, out=out))
+    gemm = lambda: fp4.gemm_mxfp4(aq, wq, out=out)
+    timer = Timer(torch)
+    res = {}
+    for name, fn in (("step", step), ("gemm", gemm)):
+        for _ in range(3):
+            fn()
+        g = capture(torch, [fn] * 4)
+        g.replay()
+        res[name] = run_steps(torch, timer, g, [fn] * 4, steps) / steps
+    flops = 2 * m * n * k
+    # accuracy against the float32 product of the unquantized (bf16) activations and weights
+    ref = ad.float() @ wd.t()
+    mx = fp4.gemm_mxfp4(aq, wq, out_dtype=torch.float32)
+    wq2 = fp4.quantize_fp4(wd, layout=fp4.LAYOUT_TILED)
+    two = fp4.gemm_w4aX(fp4.A4, ad, wq2, out_dtype=torch.float32)
+    nref = torch.linalg.norm(ref).item()
+    err_mx = torch.linalg.norm(mx - ref).item() / nref
+    err_two = torch.linalg.norm(two - ref).item() / nref
+    torch.cuda.synchronize()
+    tfl = flops / res["step"] / 1e12
+    tfl_g = flops / res["gemm"] / 1e12
+    return dict(m=m, n=n, k=k, per_step_s=res["step"], gemm_s=res["gemm"], tflops=tfl, gemm_tflops=tfl_g,
+                frac_fp4_peak=tfl / FP4_PEAK_TFLOPS, gemm_frac_fp4_peak=tfl_g / FP4_PEAK_TFLOPS,
+                rel_error_vs_fp32_product=dict(mx_fp4=err_mx, two_level_w4a4=err_two))
+
+
 def bench_quantize(torch, fp4, workloads, steps):
     """quantize_fp4 on its two hot uses: the decode weights (float32 [14336 x 4096] to the
     tiled E2M1 layout, done once per model load) and the prefill activations (bf16
@@ -513,7 +553,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--skip-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize", "attention"],
+    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize", "attention", "mx"],
                     default=None,
                     help="run one workload only (for profiling); prints its record")
     ap.add_argument("--copy-probe", action="store_true",
@@ -559,7 +599,8 @@ def main():
               "policy": lambda: bench_policy(torch, fp4, workloads, args.steps),
               "moe": lambda: bench_moe(torch, fp4, workloads, args.steps),
               "quantize": lambda: bench_quantize(torch, fp4, workloads, args.steps),
-              "attention": lambda: bench_attention(torch, fp4, workloads, args.steps)}[args.only]
+              "attention": lambda: bench_attention(torch, fp4, workloads, args.steps),
+              "mx": lambda: bench_mx(torch, fp4, workloads, args.steps)}[args.only]
         rec = {args.only: fn()}
         if args.copy_probe:
             rec["copy_probe"] = copy_probe(torch)
@@ -580,6 +621,8 @@ def main():
         print("# quantize done", file=sys.stderr, flush=True)
         secondary["decode_attention_fp4kv"] = bench_attention(torch, fp4, workloads, max(8, args.steps // 8))
         print("# attention done", file=sys.stderr, flush=True)
+        secondary["prefill_mx_fp4"] = bench_mx(torch, fp4, workloads, max(8, args.steps // 8))
+        print("# mx done", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads)
 
     traffic = load_traffic("gemv_decode_w4a16")

@@ -32,7 +32,8 @@ EXPORTED = ["quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
             "grouped_gemm_w4aX_gated", "moe_route", "moe_route_workspace_bytes", "moe_combine",
             "fp4_workspace_bytes", "fp4_policy_select", "fp4_status_string",
             "fp4_device_check", "fp4_kv_cache_bytes", "kv_cache_append",
-            "attention_workspace_bytes", "attention_decode_fp4kv"]
+            "attention_workspace_bytes", "attention_decode_fp4kv", "mxfp4_bytes",
+            "quantize_mxfp4", "gemm_mxfp4"]
 KV_CODES, KV_MICRO, KV_MACRO = 0, 1, 2
 
 
@@ -94,9 +95,13 @@ def library() -> ctypes.CDLL:
     lib.attention_workspace_bytes.argtypes = [i32, i32, i32]
     lib.attention_workspace_bytes.restype = sz
     lib.attention_decode_fp4kv.argtypes = [vp, i32, KV, vp, ctypes.c_float, vp, i32, vp, sz, vp]
+    lib.mxfp4_bytes.argtypes = [i64, i64, i32]
+    lib.mxfp4_bytes.restype = sz
+    lib.quantize_mxfp4.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
+    lib.gemm_mxfp4.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, i32, i64, vp]
     for name in ("quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
                  "grouped_gemm_w4aX_gated", "moe_route", "moe_combine", "fp4_device_check",
-                 "kv_cache_append", "attention_decode_fp4kv"):
+                 "kv_cache_append", "attention_decode_fp4kv", "quantize_mxfp4", "gemm_mxfp4"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -367,3 +372,43 @@ def attention_decode_fp4kv(q: torch.Tensor, cache: KvCache, lengths: torch.Tenso
                                     _dtype_code(o.dtype), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "attention_decode_fp4kv")
     return o
+
+
+@dataclass
+class MxTensor:
+    """MX-native FP4 tensor in the tiled layout (include/fp4_e2m1.h): codes, E8M0 scales."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    k: int
+
+
+def quantize_mxfp4(x: torch.Tensor, out: MxTensor | None = None) -> MxTensor:
+    """x [rows, k] (bf16 or float32, contiguous rows) -> MX-native FP4 (tiled)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    rows, k = x.shape
+    lib = library()
+    nc, ns = int(lib.mxfp4_bytes(rows, k, 0)), int(lib.mxfp4_bytes(rows, k, 1))
+    if nc == 0:
+        raise Fp4Error(2, "quantize_mxfp4")
+    q = out if out is not None else MxTensor(torch.empty(nc, dtype=torch.uint8, device=x.device),
+                                             torch.empty(ns, dtype=torch.uint8, device=x.device), rows, k)
+    if q.codes.numel() < nc or q.scales.numel() < ns or q.rows != rows or q.k != k:
+        raise ValueError("out does not match x")
+    st = lib.quantize_mxfp4(_ptr(x), _dtype_code(x.dtype), rows, k, x.stride(0), _ptr(q.codes), _ptr(q.scales),
+                            _stream())
+    _check(st, "quantize_mxfp4")
+    return q
+
+
+def gemm_mxfp4(a: MxTensor, w: MxTensor, out_dtype: torch.dtype = torch.bfloat16,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """C [a.rows, w.rows] = A_hat . W_hat^T on the block-scaled FP4 matrix instruction."""
+    if a.k != w.k:
+        raise ValueError("a and w must have the same k")
+    c = out if out is not None else torch.empty(a.rows, w.rows, dtype=out_dtype, device=a.codes.device)
+    st = library().gemm_mxfp4(_ptr(a.codes), _ptr(a.scales), a.rows, _ptr(w.codes), _ptr(w.scales), w.rows, a.k,
+                              _ptr(c), _dtype_code(c.dtype), c.stride(0), _stream())
+    _check(st, "gemm_mxfp4")
+    return c

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp4_e2m1.so")
-SOURCES = ["api.cpp", "quant.hip", "gemv.hip", "gemm.hip", "moe.hip", "attention.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemv.hip", "gemm.hip", "moe.hip", "attention.hip", "mx.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

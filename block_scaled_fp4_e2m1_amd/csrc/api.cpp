@@ -341,6 +341,42 @@ fp4_status moe_combine(const void* y, int32_t y_dtype, int64_t ldy, const int32_
                                              static_cast<hipStream_t>(stream)));
 }
 
+// ---- MX-native FP4 ----
+
+size_t mxfp4_bytes(int64_t rows, int64_t k, int32_t part) {
+  if (rows < 1 || k < 128 || k % 128) return 0;
+  const size_t padded = (size_t)fp4lib::mx_padded_rows(rows);
+  if (part == FP4_MX_CODES) return padded * (size_t)k / 2;
+  if (part == FP4_MX_SCALES) return padded * (size_t)k / 32;
+  return 0;
+}
+
+fp4_status quantize_mxfp4(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx, void* codes,
+                          uint8_t* scales, void* stream) {
+  if (!x || !codes || !scales) return FP4_E_NULL;
+  if (!valid_dtype(x_dtype)) return FP4_E_DTYPE;
+  if (rows < 1 || k < 128 || k % 128 || ldx < k) return FP4_E_SHAPE;
+  if (!aligned16(x) || (ldx * (int64_t)dtype_size(x_dtype)) % 16 || !aligned16(codes)) return FP4_E_ALIGN;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  return launched(fp4lib::launch_mx_quantize(x, x_dtype == FP4_BF16, rows, k, ldx, static_cast<uint8_t*>(codes),
+                                             scales, static_cast<hipStream_t>(stream)));
+}
+
+fp4_status gemm_mxfp4(const void* a_codes, const uint8_t* a_scales, int64_t m, const void* w_codes,
+                      const uint8_t* w_scales, int64_t n, int64_t k, void* c, int32_t c_dtype, int64_t ldc,
+                      void* stream) {
+  if (!a_codes || !a_scales || !w_codes || !w_scales || !c) return FP4_E_NULL;
+  if (!valid_dtype(c_dtype)) return FP4_E_DTYPE;
+  if (m < 1 || n < 1 || k < 128 || k % 128 || ldc < n || (m + 127) / 128 > 65535) return FP4_E_SHAPE;
+  if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned(c, dtype_size(c_dtype))) return FP4_E_ALIGN;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  return launched(fp4lib::launch_gemm_mx(static_cast<const uint8_t*>(a_codes), a_scales, m,
+                                         static_cast<const uint8_t*>(w_codes), w_scales, n, k, c,
+                                         c_dtype == FP4_BF16, ldc, static_cast<hipStream_t>(stream)));
+}
+
 // ---- KV cache and decode attention ----
 
 namespace {

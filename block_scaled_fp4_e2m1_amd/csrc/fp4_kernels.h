@@ -92,6 +92,14 @@ hipError_t launch_attention_decode(const KvCacheArgs& c, const uint16_t* q, int 
                                    const int32_t* lengths, float scale, float* partial, void* out,
                                    int out_bf16, hipStream_t st);
 
+// MX-native FP4 (E2M1, E8M0 per 32; tiled layout: see mx.hip). rows padded to 16.
+int64_t mx_padded_rows(int64_t rows);
+hipError_t launch_mx_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, int64_t ldx, uint8_t* codes,
+                              uint8_t* scales, hipStream_t st);
+hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, const uint8_t* w_codes,
+                          const uint8_t* w_scales, int64_t n, int64_t k, void* c, int out_bf16, int64_t ldc,
+                          hipStream_t st);
+
 // out[t, :] = sum_j w[t, j] * y[token_rows[t, j], :] (float32, j in order); hidden % 8 == 0.
 hipError_t launch_moe_combine(const void* y, int in_bf16, int64_t ldy, const int32_t* token_rows,
                               const float* topk_w, int64_t tokens, int top_k, int64_t hidden,

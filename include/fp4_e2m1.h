@@ -281,6 +281,35 @@ fp4_status attention_decode_fp4kv(const void* q, int32_t q_heads, const fp4_kv_c
                                   const int32_t* lengths, float scale, void* out, int32_t out_dtype,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * MX-native FP4 -- not the two-level format: E2M1 codes with one E8M0 power-of-two scale
+ * per 32 consecutive elements of a row (OCP microscaling reading: e = floor(log2 max|x|)
+ * - 2, clamped to [-127, 127], -127 for an all-zero block; codes = x / 2^e rounded to
+ * nearest E2M1, ties to even, saturating at 6, sign kept). It is the format the block-
+ * scaled FP4 matrix instruction of gfx950 consumes, kept beside the pages' format to
+ * measure the FP4 matrix path and its accuracy against the two-level format; the pages'
+ * E4M3-per-16 micro-scales and FP16 macro-scales have no exact E8M0-per-32 form (the
+ * hardware applies powers of two only).
+ * Tiled layout (rows padded to a multiple of 16; k % 128 == 0): tile T = (r/16)*(k/128)
+ * + c/128 of 16 rows x 128 columns; codes at T*1024 + kb*256 + (r%16)*16 + (c%32)/2 with
+ * kb = (c%128)/32 (low nibble = even c), scales (E8M0 bytes) at T*64 + kb*16 + r%16.
+ * mxfp4_bytes(rows, k, FP4_MX_CODES / FP4_MX_SCALES) gives the sizes (0 when k % 128 or
+ * rows < 1). All buffers are caller-owned device memory.
+ *
+ * quantize_mxfp4 -- x device [rows x k] (FP4_BF16 or FP4_F32, finite, stride ldx, 16-byte
+ *   aligned rows) -> codes (16-byte aligned), scales; padding rows get zeros.
+ * gemm_mxfp4 -- C[m x n] = A_hat . W_hat^T, A and W quantized by quantize_mxfp4 (m and n
+ *   the real row counts), float32 accumulation by the matrix core; C FP4_BF16 (round to
+ *   nearest even) or FP4_F32, row stride ldc.
+ */
+enum { FP4_MX_CODES = 0, FP4_MX_SCALES = 1 };
+size_t mxfp4_bytes(int64_t rows, int64_t k, int32_t part);
+fp4_status quantize_mxfp4(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx, void* codes,
+                          uint8_t* scales, void* stream);
+fp4_status gemm_mxfp4(const void* a_codes, const uint8_t* a_scales, int64_t m, const void* w_codes,
+                      const uint8_t* w_scales, int64_t n, int64_t k, void* c, int32_t c_dtype, int64_t ldc,
+                      void* stream);
+
 /* Bytes of device workspace gemm_w4aX / grouped_gemm_w4aX need (0 for FP4_A16). */
 size_t fp4_workspace_bytes(int32_t act, int64_t m_or_rows, int64_t n, int64_t k);
 

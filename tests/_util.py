@@ -130,3 +130,19 @@ def kv_cache_to_canonical(cache, which: str, b: int, tokens):
     for pr in range(H // 2):
         macro[:, pr] = macro_dev[(b * (H // 2) + pr) * T + tokens]
     return codes4, micro, macro
+
+
+def mx_tiled_to_canonical(q):
+    """(codes4 uint8 [rows, k], scales uint8 [rows, k/32], padding codes, padding scales)
+    of an MX tensor, read back through the tiled layout of include/fp4_e2m1.h."""
+    rows, k = q.rows, q.k
+    pr = (rows + 15) // 16 * 16
+    codes = host(q.codes).astype(np.uint8)[: pr * k // 2].reshape(pr // 16, k // 128, 4, 16, 16)
+    scales = host(q.scales).astype(np.uint8)[: pr * k // 32].reshape(pr // 16, k // 128, 4, 16)
+    # codes [rb][kt][kb][n][byte] -> row rb*16+n, column kt*128 + kb*32 + 2*byte (+1)
+    c = codes.transpose(0, 3, 1, 2, 4).reshape(pr, k // 2)
+    codes4 = np.empty((pr, k), dtype=np.uint8)
+    codes4[:, 0::2] = c & 15
+    codes4[:, 1::2] = c >> 4
+    s = scales.transpose(0, 3, 1, 2).reshape(pr, k // 32)
+    return codes4[:rows], s[:rows], codes4[rows:], s[rows:]

@@ -177,6 +177,24 @@ def test_kv_entry_points_validate_before_device_use(lib):
     assert lib.attention_decode_fp4kv(fake, 8, ctypes.byref(good), fake, 1.0, fake, 5, ws, 1 << 30, null) == 4
 
 
+def test_mx_entry_points_validate_before_device_use(lib):
+    vp = ctypes.c_void_p
+    fake, null = vp(1 << 20), vp(0)
+    # sizes: rows padded to 16; codes rows * k / 2, scales rows * k / 32
+    assert lib.mxfp4_bytes(37, 384, 0) == 48 * 384 // 2
+    assert lib.mxfp4_bytes(37, 384, 1) == 48 * 384 // 32
+    assert lib.mxfp4_bytes(16, 96, 0) == 0 and lib.mxfp4_bytes(0, 128, 0) == 0
+    assert lib.quantize_mxfp4(null, 1, 16, 128, 128, fake, fake, null) == 1
+    assert lib.quantize_mxfp4(fake, 7, 16, 128, 128, fake, fake, null) == 4
+    assert lib.quantize_mxfp4(fake, 1, 16, 96, 96, fake, fake, null) == 2
+    assert lib.quantize_mxfp4(fake, 1, 16, 128, 100, fake, fake, null) == 2
+    assert lib.quantize_mxfp4(fake, 1, 16, 128, 132, fake, fake, null) == 3
+    assert lib.gemm_mxfp4(fake, fake, 16, fake, fake, 16, 192, fake, 1, 16, null) == 2
+    assert lib.gemm_mxfp4(fake, fake, 16, fake, fake, 16, 128, fake, 1, 8, null) == 2
+    assert lib.gemm_mxfp4(fake, null, 16, fake, fake, 16, 128, fake, 1, 16, null) == 1
+    assert lib.gemm_mxfp4(vp((1 << 20) + 4), fake, 16, fake, fake, 16, 128, fake, 1, 16, null) == 3
+
+
 def test_device_check_reports_missing_device(lib):
     import torch
     if torch.cuda.is_available():
