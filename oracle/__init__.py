@@ -1,8 +1,9 @@
 """CPU oracle for two-level block-scaled FP4 (E2M1 elements, E4M3 micro-scales per 16,
 FP16 macro-scales per 256), the W4A16 / W4A8 / W4A4 products built on it, the
 mixture-of-experts layer steps around the grouped product (routing, gated activation,
-combine), decode attention over a KV cache kept in the same format, and the MX-native
-FP4 variant (E8M0 power-of-two scale per 32) with its product.
+combine), decode attention over a KV cache kept in the same format, the MX-native FP4
+variant (E8M0 power-of-two scale per 32) with its product, and the paths for sensitive
+layers (W8A8) and calibrated (static) activation macro-scales.
 
 TEST INFRASTRUCTURE ONLY. A plain, slow, float64 numpy restatement of the method that
 the HIP library is checked against. It shares no code with the library. Only tests,
@@ -20,3 +21,6 @@ from .gemm import (activation_values, gemm, gemm_bf16, grouped_gemm, policy_sele
 from .moe import route, silu_gate, combine
 from .attention import kv_quantize_rows, kv_dequantize_rows, attention_decode
 from .mx import MX_BLOCK, e8m0_value, mx_quantize, mx_dequantize, mx_gemm
+from .sensitive import (W8A8, A4S, A8S, POLICY_SENSITIVE_W8, POLICY_STATIC, calibrate_macro,
+                        quantize_static, activation_values_static, gemm_w8a8, gemm_static,
+                        policy_select_ext)
