@@ -10,8 +10,10 @@ cannot hold the stream, and launches are replayed from a HIP graph.
 
 Also reported (same JSON line, "secondary"): the W4A4 prefill product (2048 x 4096 x
 4096, activations quantized on the device every step) in TFLOP/s, the 8-layer W4A4/W4A8
-policy stack, and the 128-expert top-8 mixture-of-experts grouped products, each with its
-roofline fraction; the oracle's CPU time on a bounded sample ("cpu_baseline").
+policy stack, the 128-expert top-8 mixture-of-experts layer, quantization, decode
+attention over the FP4 KV cache, the MX-native FP4 product, and the policy stack under
+the W8A8 ("sensitive-w8") and static-activation-scale modes, each with its roofline
+fraction; the oracle's CPU time on a bounded sample ("cpu_baseline").
 
 Rank 0 prints one JSON line. Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -381,6 +383,84 @@ def bench_policy(torch, fp4, workloads, steps):
                 layer_a4_s=t4, layer_a8_s=t8)
 
 
+def bench_sensitive(torch, fp4, workloads, steps):
+    """The 8-layer policy stack (512 x 5120 x 5120 per layer) under the two added policy
+    modes: "sensitive-w8" (flagged layers W8A8: E4M3 weights and 8-bit activations, the
+    rest W4A4) and "static" (flagged layers A8, the rest A4, both with activation macro-
+    scales calibrated beforehand on a separate batch). Per step: every layer's activation
+    pass and product. Also the time of one layer of each kind alone and, on the first
+    flagged layer, each precision's relative Frobenius error against the float32 product
+    of the unquantized inputs."""
+    cfg = workloads.WORKLOADS["policy_stack"]
+    m, k, n = cfg["m"], cfg["k"], cfg["n"]
+    flags = workloads.policy_flags()
+    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(fp4.fp4_workspace_bytes(fp4.A8, m, n, k), dtype=torch.uint8, device="cuda")
+    res = {}
+    timer = Timer(torch)
+    single = {}
+    acc_layer = int(np.nonzero(flags)[0][0])
+    for mode, name in ((fp4.POLICY_SENSITIVE_W8, "sensitive_w8"), (fp4.POLICY_STATIC, "static")):
+        fns, kinds = [], []
+        for l in range(cfg["layers"]):
+            w, x = workloads.policy_layer(l)
+            code = fp4.fp4_policy_select(mode, bool(flags[l]))
+            wd = torch.from_numpy(w).cuda()
+            xd = torch.from_numpy(x).cuda().to(torch.bfloat16)
+            if code == fp4.W8A8:
+                wq = fp4.quantize_fp4(wd, elem=fp4.ELEM_E4M3, layout=fp4.LAYOUT_TILED)
+                fns.append(lambda x=xd, q=wq: fp4.gemm_w8a8(x, q, out=out, workspace=ws))
+            elif code in (fp4.A4S, fp4.A8S):
+                act = fp4.A8 if code == fp4.A8S else fp4.A4
+                amax = torch.zeros(k // 256, dtype=torch.float32, device="cuda")
+                calib = torch.from_numpy(workloads.policy_calibration(l, rows=cfg["calib_rows"])).cuda()
+                macro = fp4.act_macro_calibrate(calib.to(torch.bfloat16), amax,
+                                                fp4.ELEM_E4M3 if act == fp4.A8 else fp4.ELEM_E2M1)
+                wq = fp4.quantize_fp4(wd, layout=fp4.LAYOUT_TILED)
+                fns.append(lambda a=act, x=xd, q=wq, mc=macro: fp4.gemm_w4aX_static(a, x, mc, q, out=out,
+                                                                                   workspace=ws))
+            else:
+                wq = fp4.quantize_fp4(wd, layout=fp4.LAYOUT_TILED)
+                fns.append(lambda a=code, x=xd, q=wq: fp4.gemm_w4aX(a, x, q, out=out, workspace=ws))
+            kinds.append(code)
+            del wd
+        for f in fns:
+            f()
+        g = capture(torch, fns)
+        g.replay()
+        per = timer.region(g.replay, steps) / steps
+        tfl = 2 * m * n * k * len(fns) / per / 1e12
+        res[name] = dict(per_step_s=per, tflops=tfl, frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
+                         codes=[int(c) for c in kinds])
+        for f, c in zip(fns, kinds):
+            if c not in single:
+                single[c] = timer.region(f, 8) / 8
+    names = {fp4.W8A8: "w8a8", fp4.A4: "w4a4", fp4.A4S: "w4a4_static", fp4.A8S: "w4a8_static"}
+    for c, t in single.items():
+        res[f"layer_{names[c]}_s"] = t
+        res[f"layer_{names[c]}_tflops"] = 2 * m * n * k / t / 1e12
+    # accuracy on the first flagged layer against the float32 product of bf16 x and float32 W
+    w, x = workloads.policy_layer(acc_layer)
+    wd = torch.from_numpy(w).cuda()
+    xd = torch.from_numpy(x).cuda().to(torch.bfloat16)
+    ref = xd.float() @ wd.t()
+    nref = torch.linalg.norm(ref).item()
+    wq4 = fp4.quantize_fp4(wd, layout=fp4.LAYOUT_TILED)
+    wq8 = fp4.quantize_fp4(wd, elem=fp4.ELEM_E4M3, layout=fp4.LAYOUT_TILED)
+    amax = torch.zeros(k // 256, dtype=torch.float32, device="cuda")
+    calib = torch.from_numpy(workloads.policy_calibration(acc_layer, rows=cfg["calib_rows"])).cuda()
+    mac8 = fp4.act_macro_calibrate(calib.to(torch.bfloat16), amax, fp4.ELEM_E4M3)
+    outs = {"w8a8": fp4.gemm_w8a8(xd, wq8, out_dtype=torch.float32),
+            "w4a16": fp4.gemm_w4aX(fp4.A16, xd, wq4, out_dtype=torch.float32),
+            "w4a8": fp4.gemm_w4aX(fp4.A8, xd, wq4, out_dtype=torch.float32),
+            "w4a8_static": fp4.gemm_w4aX_static(fp4.A8, xd, mac8, wq4, out_dtype=torch.float32),
+            "w4a4": fp4.gemm_w4aX(fp4.A4, xd, wq4, out_dtype=torch.float32)}
+    res["rel_error_vs_fp32_product"] = {kk: torch.linalg.norm(v - ref).item() / nref for kk, v in outs.items()}
+    res["accuracy_layer"] = acc_layer
+    torch.cuda.synchronize()
+    return res
+
+
 def bench_moe(torch, fp4, workloads, steps):
     """The whole mixture-of-experts layer on the device, one HIP graph per step: routing of
     the float32 router logits, the gate/up grouped product (A4, rows gathered by token),
@@ -553,7 +633,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--skip-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize", "attention", "mx"],
+    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize", "attention", "mx",
+                                       "sensitive"],
                     default=None,
                     help="run one workload only (for profiling); prints its record")
     ap.add_argument("--copy-probe", action="store_true",
@@ -600,7 +681,8 @@ def main():
               "moe": lambda: bench_moe(torch, fp4, workloads, args.steps),
               "quantize": lambda: bench_quantize(torch, fp4, workloads, args.steps),
               "attention": lambda: bench_attention(torch, fp4, workloads, args.steps),
-              "mx": lambda: bench_mx(torch, fp4, workloads, args.steps)}[args.only]
+              "mx": lambda: bench_mx(torch, fp4, workloads, args.steps),
+              "sensitive": lambda: bench_sensitive(torch, fp4, workloads, args.steps)}[args.only]
         rec = {args.only: fn()}
         if args.copy_probe:
             rec["copy_probe"] = copy_probe(torch)
@@ -623,6 +705,9 @@ def main():
         print("# attention done", file=sys.stderr, flush=True)
         secondary["prefill_mx_fp4"] = bench_mx(torch, fp4, workloads, max(8, args.steps // 8))
         print("# mx done", file=sys.stderr, flush=True)
+        secondary["policy_stack_sensitive_static"] = bench_sensitive(torch, fp4, workloads,
+                                                                     max(4, args.steps // 32))
+        print("# sensitive done", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads)
 
     traffic = load_traffic("gemv_decode_w4a16")

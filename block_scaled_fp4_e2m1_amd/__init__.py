@@ -7,8 +7,9 @@ device is not gfx950 the calls raise.
 
 Names follow the C ABI: ``quantize_fp4``, ``dequantize_fp4``, ``gemm_w4aX``,
 ``grouped_gemm_w4aX``, ``grouped_gemm_w4aX_gated``, ``moe_route``, ``moe_combine``,
-``kv_cache_append``, ``attention_decode_fp4kv``, ``fp4_workspace_bytes``,
-``fp4_policy_select``.
+``kv_cache_append``, ``attention_decode_fp4kv``, ``quantize_mxfp4``, ``gemm_mxfp4``,
+``quantize_fp4_static``, ``act_macro_calibrate``, ``gemm_w4aX_static``, ``gemm_w8a8``,
+``fp4_workspace_bytes``, ``fp4_policy_select``.
 """
 from __future__ import annotations
 
@@ -24,16 +25,18 @@ LIB_PATH = os.path.join(_HERE, "libfp4_e2m1.so")
 FP4_OK = 0
 F32, BF16 = 0, 1
 A16, A8, A4 = 16, 8, 4
+A4S, A8S, W8A8 = 40, 80, 88
 ELEM_E2M1, ELEM_E4M3 = 0, 1
 LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
-POLICY_AUTO, POLICY_Q4, POLICY_Q8 = 0, 4, 8
+POLICY_AUTO, POLICY_SENSITIVE_W8, POLICY_STATIC, POLICY_Q4, POLICY_Q8 = 0, 1, 2, 4, 8
 
 EXPORTED = ["quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
             "grouped_gemm_w4aX_gated", "moe_route", "moe_route_workspace_bytes", "moe_combine",
             "fp4_workspace_bytes", "fp4_policy_select", "fp4_status_string",
             "fp4_device_check", "fp4_kv_cache_bytes", "kv_cache_append",
             "attention_workspace_bytes", "attention_decode_fp4kv", "mxfp4_bytes",
-            "quantize_mxfp4", "gemm_mxfp4"]
+            "quantize_mxfp4", "gemm_mxfp4", "quantize_fp4_static", "act_macro_calibrate",
+            "gemm_w4aX_static", "gemm_w8a8"]
 KV_CODES, KV_MICRO, KV_MACRO = 0, 1, 2
 
 
@@ -99,9 +102,14 @@ def library() -> ctypes.CDLL:
     lib.mxfp4_bytes.restype = sz
     lib.quantize_mxfp4.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
     lib.gemm_mxfp4.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, i32, i64, vp]
+    lib.quantize_fp4_static.argtypes = [vp, i32, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
+    lib.act_macro_calibrate.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp]
+    lib.gemm_w4aX_static.argtypes = [i32, vp, i32, i64, i64, vp, T, vp, i32, i64, vp, sz, vp]
+    lib.gemm_w8a8.argtypes = [vp, i32, i64, i64, T, vp, i32, i64, vp, sz, vp]
     for name in ("quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
                  "grouped_gemm_w4aX_gated", "moe_route", "moe_combine", "fp4_device_check",
-                 "kv_cache_append", "attention_decode_fp4kv", "quantize_mxfp4", "gemm_mxfp4"):
+                 "kv_cache_append", "attention_decode_fp4kv", "quantize_mxfp4", "gemm_mxfp4",
+                 "quantize_fp4_static", "act_macro_calibrate", "gemm_w4aX_static", "gemm_w8a8"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -170,6 +178,39 @@ def quantize_fp4(x: torch.Tensor, elem: int = ELEM_E2M1, layout: int = LAYOUT_CA
     return q
 
 
+def quantize_fp4_static(x: torch.Tensor, macro_in: torch.Tensor, elem: int = ELEM_E2M1,
+                        layout: int = LAYOUT_CANONICAL, out: QTensor | None = None) -> QTensor:
+    """quantize_fp4 with the given macro-scales (int16 FP16 bits [k/256], shared by all rows)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    rows, k = x.shape
+    if macro_in.numel() != k // 256 or macro_in.element_size() != 2 or not macro_in.is_contiguous():
+        raise ValueError("macro_in must hold k/256 contiguous 16-bit values")
+    q = out if out is not None else empty_qtensor(rows, k, elem, layout, x.device)
+    st = library().quantize_fp4_static(_ptr(x), _dtype_code(x.dtype), rows, k, x.stride(0), elem,
+                                       layout, _ptr(macro_in), _ptr(q.codes), _ptr(q.micro),
+                                       _ptr(q.macro), _stream())
+    _check(st, "quantize_fp4_static")
+    return q
+
+
+def act_macro_calibrate(x: torch.Tensor, amax: torch.Tensor, elem: int = ELEM_E2M1,
+                        macro: torch.Tensor | None = None) -> torch.Tensor:
+    """Updates the running per-group maximum amax (float32 [k/256], zeroed before the first
+    batch) with x [rows, k] and returns the static macro-scales (int16 FP16 bits [k/256])."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    rows, k = x.shape
+    if amax.numel() != k // 256 or amax.dtype != torch.float32 or not amax.is_contiguous():
+        raise ValueError("amax must be a contiguous float32 tensor of k/256 values")
+    if macro is None:
+        macro = torch.empty(k // 256, dtype=torch.int16, device=x.device)
+    st = library().act_macro_calibrate(_ptr(x), _dtype_code(x.dtype), rows, k, x.stride(0), elem,
+                                       _ptr(amax), _ptr(macro), _stream())
+    _check(st, "act_macro_calibrate")
+    return macro
+
+
 def dequantize_fp4(q: QTensor, dtype: torch.dtype = torch.float32,
                    out: torch.Tensor | None = None) -> torch.Tensor:
     y = out if out is not None else torch.empty(q.rows, q.k, dtype=dtype, device=q.codes.device)
@@ -216,6 +257,41 @@ def gemm_w4aX(act: int, a: torch.Tensor, w: QTensor, out_dtype: torch.dtype = to
     st = library().gemm_w4aX(act, _ptr(a), _dtype_code(a.dtype), m, a.stride(0), ctypes.byref(ts),
                              _ptr(c), _dtype_code(c.dtype), c.stride(0), _ptr(ws), wsb, _stream())
     _check(st, "gemm_w4aX")
+    return c
+
+
+def gemm_w4aX_static(act: int, a: torch.Tensor, act_macro: torch.Tensor, w: QTensor,
+                     out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm_w4aX (act A4 or A8) with static activation macro-scales act_macro (int16 FP16
+    bits [k/256])."""
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("a must be 2-D with contiguous rows")
+    if act_macro.numel() != w.k // 256 or act_macro.element_size() != 2 or not act_macro.is_contiguous():
+        raise ValueError("act_macro must hold k/256 contiguous 16-bit values")
+    m = a.shape[0]
+    c = out if out is not None else torch.empty(m, w.rows, dtype=out_dtype, device=a.device)
+    ws, wsb = _workspace(act, m, w.rows, w.k, a.device, workspace)
+    ts = w.c_struct()
+    st = library().gemm_w4aX_static(act, _ptr(a), _dtype_code(a.dtype), m, a.stride(0), _ptr(act_macro),
+                                    ctypes.byref(ts), _ptr(c), _dtype_code(c.dtype), c.stride(0), _ptr(ws),
+                                    wsb, _stream())
+    _check(st, "gemm_w4aX_static")
+    return c
+
+
+def gemm_w8a8(a: torch.Tensor, w: QTensor, out_dtype: torch.dtype = torch.bfloat16,
+              out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """C = A8(a) . W_hat^T with W quantized with E4M3 elements in the tiled layout."""
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("a must be 2-D with contiguous rows")
+    m = a.shape[0]
+    c = out if out is not None else torch.empty(m, w.rows, dtype=out_dtype, device=a.device)
+    ws, wsb = _workspace(W8A8, m, w.rows, w.k, a.device, workspace)
+    ts = w.c_struct()
+    st = library().gemm_w8a8(_ptr(a), _dtype_code(a.dtype), m, a.stride(0), ctypes.byref(ts), _ptr(c),
+                             _dtype_code(c.dtype), c.stride(0), _ptr(ws), wsb, _stream())
+    _check(st, "gemm_w8a8")
     return c
 
 

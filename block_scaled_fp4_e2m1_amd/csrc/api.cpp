@@ -33,10 +33,12 @@ bool valid_act(int32_t act) { return act == FP4_A16 || act == FP4_A8 || act == F
 
 fp4_status launched(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_E_HIP; }
 
-// Checks on a quantized weight tensor shared by the matrix entry points.
-fp4_status check_weights(const fp4_tensor* w) {
+// Checks on a quantized weight tensor shared by the matrix entry points (elem: the
+// element type the product takes).
+fp4_status check_weights(const fp4_tensor* w, int32_t elem = FP4_ELEM_E2M1) {
   if (!w || !w->codes || !w->micro || !w->macro) return FP4_E_NULL;
-  if (w->elem != FP4_ELEM_E2M1) return w->elem == FP4_ELEM_E4M3 ? FP4_E_DTYPE : FP4_E_MODE;
+  if (w->elem != FP4_ELEM_E2M1 && w->elem != FP4_ELEM_E4M3) return FP4_E_MODE;
+  if (w->elem != elem) return FP4_E_DTYPE;
   if (w->layout != FP4_LAYOUT_TILED)
     return w->layout == FP4_LAYOUT_CANONICAL ? FP4_E_LAYOUT : FP4_E_MODE;
   if (w->rows < 16 || w->rows % 16 || w->k < 256 || w->k % 256) return FP4_E_SHAPE;
@@ -48,6 +50,15 @@ fp4_status check_weights(const fp4_tensor* w) {
 // (k + 64) measured slower with the product kernel's LDS-DMA operand copies.
 int64_t act_ws_stride(int64_t k) { return k; }
 
+// precision codes of the policy table -> the activation quantization they run
+int32_t act_of(int32_t code) {
+  switch (code) {
+    case FP4_A4S: return FP4_A4;
+    case FP4_A8S: case FP4_W8A8: return FP4_A8;
+    default: return code;
+  }
+}
+
 size_t act_workspace(int32_t act, int64_t rows, int64_t k) {
   if (act == FP4_A16) return 0;
   const size_t aq = ((size_t)rows * (size_t)act_ws_stride(k) * 2 + 255) & ~(size_t)255;
@@ -55,9 +66,10 @@ size_t act_workspace(int32_t act, int64_t rows, int64_t k) {
 }
 
 // Runs the activation pass when needed and fills the activation part of GemmArgs.
+// act_macro: static activation macro-scales (FP16 bits per group) or nullptr (dynamic).
 fp4_status prepare_activations(int32_t act, const void* a, int32_t a_dtype, int64_t rows,
                                int64_t k, int64_t lda, void* ws, fp4lib::GemmArgs& g,
-                               hipStream_t st) {
+                               hipStream_t st, const uint16_t* act_macro = nullptr) {
   if (act == FP4_A16) {
     g.a = a;
     g.a_is_bf16 = 1;
@@ -70,7 +82,7 @@ fp4_status prepare_activations(int32_t act, const void* a, int32_t a_dtype, int6
   float* scale = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                           (((size_t)rows * (size_t)ldq * 2 + 255) & ~(size_t)255));
   const hipError_t e = fp4lib::launch_act_prep(a, a_dtype == FP4_BF16, rows, k, lda,
-                                               act == FP4_A8, aq, ldq, scale, st);
+                                               act == FP4_A8, aq, ldq, scale, act_macro, st);
   if (e != hipSuccess) return FP4_E_HIP;
   g.a = aq;
   g.a_is_bf16 = 0;
@@ -107,35 +119,66 @@ int32_t fp4_policy_select(int32_t mode, int32_t layer_flag) {
     case FP4_POLICY_Q4: return FP4_A4;
     case FP4_POLICY_Q8: return FP4_A8;
     case FP4_POLICY_AUTO: return layer_flag ? FP4_A8 : FP4_A4;
+    case FP4_POLICY_SENSITIVE_W8: return layer_flag ? FP4_W8A8 : FP4_A4;
+    case FP4_POLICY_STATIC: return layer_flag ? FP4_A8S : FP4_A4S;
     default: return -FP4_E_MODE;
   }
 }
 
 size_t fp4_workspace_bytes(int32_t act, int64_t m_or_rows, int64_t n, int64_t k) {
   (void)n;
+  act = act_of(act);
   if (!valid_act(act) || m_or_rows < 0 || k < 0) return 0;
   return act_workspace(act, m_or_rows, k);
 }
 
-fp4_status quantize_fp4(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
-                        int32_t elem, int32_t layout, void* codes, uint8_t* micro,
-                        uint16_t* macro, void* stream) {
+namespace {
+fp4_status quantize_impl(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                         int32_t elem, int32_t layout, const uint16_t* macro_in, void* codes,
+                         uint8_t* micro, uint16_t* macro, void* stream) {
   if (!x || !codes || !micro || !macro) return FP4_E_NULL;
   if (!valid_dtype(x_dtype)) return FP4_E_DTYPE;
   if (elem != FP4_ELEM_E2M1 && elem != FP4_ELEM_E4M3) return FP4_E_MODE;
   if (layout != FP4_LAYOUT_CANONICAL && layout != FP4_LAYOUT_TILED) return FP4_E_MODE;
-  if (elem == FP4_ELEM_E4M3 && layout == FP4_LAYOUT_TILED) return FP4_E_LAYOUT;
   if (rows < 1 || k < 256 || k % 256 || ldx < k) return FP4_E_SHAPE;
   if (layout == FP4_LAYOUT_TILED && rows % 16) return FP4_E_SHAPE;
   if (!aligned16(x) || (ldx * (int64_t)dtype_size(x_dtype)) % 16 || !aligned16(codes) ||
-      !aligned16(micro) || !aligned(macro, 2))
+      !aligned16(micro) || !aligned(macro, 2) || (macro_in && !aligned(macro_in, 2)))
     return FP4_E_ALIGN;
   const fp4_status dev = check_device();
   if (dev != FP4_OK) return dev;
   return launched(fp4lib::launch_quantize(x, x_dtype == FP4_BF16, rows, k, ldx,
                                           elem == FP4_ELEM_E4M3, layout == FP4_LAYOUT_TILED,
-                                          static_cast<uint8_t*>(codes), micro, macro,
+                                          static_cast<uint8_t*>(codes), micro, macro, macro_in,
                                           static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+fp4_status quantize_fp4(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                        int32_t elem, int32_t layout, void* codes, uint8_t* micro,
+                        uint16_t* macro, void* stream) {
+  return quantize_impl(x, x_dtype, rows, k, ldx, elem, layout, nullptr, codes, micro, macro, stream);
+}
+
+fp4_status quantize_fp4_static(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                               int32_t elem, int32_t layout, const uint16_t* macro_in, void* codes,
+                               uint8_t* micro, uint16_t* macro, void* stream) {
+  if (!macro_in) return FP4_E_NULL;
+  return quantize_impl(x, x_dtype, rows, k, ldx, elem, layout, macro_in, codes, micro, macro, stream);
+}
+
+fp4_status act_macro_calibrate(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                               int32_t elem, float* amax, uint16_t* macro, void* stream) {
+  if (!x || !amax || !macro) return FP4_E_NULL;
+  if (!valid_dtype(x_dtype)) return FP4_E_DTYPE;
+  if (elem != FP4_ELEM_E2M1 && elem != FP4_ELEM_E4M3) return FP4_E_MODE;
+  if (rows < 1 || k < 256 || k % 256 || ldx < k) return FP4_E_SHAPE;
+  if (!aligned16(x) || (ldx * (int64_t)dtype_size(x_dtype)) % 16 || !aligned(amax, 4) || !aligned(macro, 2))
+    return FP4_E_ALIGN;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  return launched(fp4lib::launch_act_calibrate(x, x_dtype == FP4_BF16, rows, k, ldx, elem == FP4_ELEM_E4M3,
+                                               amax, macro, static_cast<hipStream_t>(stream)));
 }
 
 fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t ldy,
@@ -144,7 +187,6 @@ fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t
   if (!valid_dtype(y_dtype)) return FP4_E_DTYPE;
   if (q->elem != FP4_ELEM_E2M1 && q->elem != FP4_ELEM_E4M3) return FP4_E_MODE;
   if (q->layout != FP4_LAYOUT_CANONICAL && q->layout != FP4_LAYOUT_TILED) return FP4_E_MODE;
-  if (q->elem == FP4_ELEM_E4M3 && q->layout == FP4_LAYOUT_TILED) return FP4_E_LAYOUT;
   if (q->rows < 1 || q->k < 256 || q->k % 256 || ldy < q->k) return FP4_E_SHAPE;
   if (q->layout == FP4_LAYOUT_TILED && q->rows % 16) return FP4_E_SHAPE;
   if (!aligned16(y) || (ldy * (int64_t)dtype_size(y_dtype)) % 16 || !aligned16(q->codes) ||
@@ -198,6 +240,71 @@ fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int
   g.c = c;
   g.c_is_bf16 = c_dtype == FP4_BF16;
   g.ldc = ldc;
+  return launched(fp4lib::launch_gemm(g, st));
+}
+
+fp4_status gemm_w4aX_static(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,
+                            const uint16_t* act_macro, const fp4_tensor* w, void* c, int32_t c_dtype,
+                            int64_t ldc, void* workspace, size_t workspace_bytes, void* stream) {
+  if (act != FP4_A4 && act != FP4_A8) return FP4_E_MODE;
+  if (!a || !c || !act_macro) return FP4_E_NULL;
+  const fp4_status ws_ok = check_weights(w);
+  if (ws_ok != FP4_OK) return ws_ok;
+  if (!valid_dtype(a_dtype) || !valid_dtype(c_dtype)) return FP4_E_DTYPE;
+  const int64_t n = w->rows, k = w->k;
+  if (m < 1 || lda < k || ldc < n) return FP4_E_SHAPE;
+  if (!fp4lib::gemm_supports(k)) return FP4_E_SHAPE;
+  if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
+  if (!aligned(c, dtype_size(c_dtype)) || !aligned(act_macro, 2)) return FP4_E_ALIGN;
+  const size_t need = act_workspace(act, m, k);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return FP4_E_WORKSPACE;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  fp4lib::GemmArgs g{};
+  const fp4_status prep = prepare_activations(act, a, a_dtype, m, k, lda, workspace, g, st, act_macro);
+  if (prep != FP4_OK) return prep;
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  g.codes = static_cast<const uint8_t*>(w->codes);
+  g.micro = w->micro;
+  g.macro = w->macro;
+  g.c = c;
+  g.c_is_bf16 = c_dtype == FP4_BF16;
+  g.ldc = ldc;
+  return launched(fp4lib::launch_gemm(g, st));
+}
+
+fp4_status gemm_w8a8(const void* a, int32_t a_dtype, int64_t m, int64_t lda, const fp4_tensor* w, void* c,
+                     int32_t c_dtype, int64_t ldc, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!a || !c) return FP4_E_NULL;
+  const fp4_status ws_ok = check_weights(w, FP4_ELEM_E4M3);
+  if (ws_ok != FP4_OK) return ws_ok;
+  if (!valid_dtype(a_dtype) || !valid_dtype(c_dtype)) return FP4_E_DTYPE;
+  const int64_t n = w->rows, k = w->k;
+  if (m < 1 || lda < k || ldc < n) return FP4_E_SHAPE;
+  if (!fp4lib::gemm_supports(k)) return FP4_E_SHAPE;
+  if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
+  if (!aligned(c, dtype_size(c_dtype))) return FP4_E_ALIGN;
+  const size_t need = act_workspace(FP4_A8, m, k);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return FP4_E_WORKSPACE;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  fp4lib::GemmArgs g{};
+  const fp4_status prep = prepare_activations(FP4_A8, a, a_dtype, m, k, lda, workspace, g, st);
+  if (prep != FP4_OK) return prep;
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  g.codes = static_cast<const uint8_t*>(w->codes);
+  g.micro = w->micro;
+  g.macro = w->macro;
+  g.c = c;
+  g.c_is_bf16 = c_dtype == FP4_BF16;
+  g.ldc = ldc;
+  g.w_e4m3 = 1;
   return launched(fp4lib::launch_gemm(g, st));
 }
 

@@ -40,6 +40,7 @@ constexpr int kBlock = 16;    // elements per micro-scale
 constexpr int kGroup = 256;   // elements per macro-scale
 constexpr int kTileRows = 16;
 constexpr int kTileCodeBytes = 2048;  // 16 rows x 256 E2M1 codes
+constexpr int kTile8CodeBytes = 4096;  // 16 rows x 256 E4M3 codes
 constexpr int kTileMicroBytes = 256;  // 16 rows x 16 micro-scales
 constexpr int kTileMacro = 16;        // 16 rows x 1 macro-scale
 
@@ -208,6 +209,16 @@ __device__ __forceinline__ int64_t tiled_code_offset(int64_t r, int64_t col, int
   const int c = (int)(col & 255), n = (int)(r & 15);
   const int t = c >> 5, j = (c >> 3) & 3;
   return tile * kTileCodeBytes + (t >> 2) * 1024 + (16 * j + n) * 16 + (t & 3) * 4;
+}
+// E4M3 elements in the tiled layout: 8 codes of row r at columns [col, col + 8) (col % 8
+// == 0). Per tile, half h = t / 4 of the 256 columns (t = c / 32) holds two 1024-byte
+// pieces p = (t % 4) / 2; lane 16 j + n (j = (c % 32) / 8) owns 16 bytes of each piece,
+// the 8 codes of column run t in bytes 8 (t % 2) .. +7.
+__device__ __forceinline__ int64_t tiled8_code_offset(int64_t r, int64_t col, int64_t groups) {
+  const int64_t tile = (r >> 4) * groups + (col >> 8);
+  const int c = (int)(col & 255), n = (int)(r & 15);
+  const int t = c >> 5, j = (c >> 3) & 3;
+  return tile * kTile8CodeBytes + (t >> 2) * 2048 + ((t >> 1) & 1) * 1024 + (16 * j + n) * 16 + (t & 1) * 8;
 }
 __device__ __forceinline__ int64_t tiled_micro_offset(int64_t r, int64_t col, int64_t groups) {
   const int64_t tile = (r >> 4) * groups + (col >> 8);

@@ -6,17 +6,26 @@
 
 namespace fp4lib {
 
+// macro_in (optional): static macro-scales, FP16 bits per 256-column group shared by all
+// rows (nullptr: each row's own groups, the dynamic rule).
 hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, int64_t ldx,
                            int elem_e4m3, int tiled, uint8_t* codes, uint8_t* micro,
-                           uint16_t* macro, hipStream_t st);
+                           uint16_t* macro, const uint16_t* macro_in, hipStream_t st);
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const uint16_t* macro,
                              int64_t rows, int64_t k, int elem_e4m3, int tiled, void* y,
                              int out_bf16, int64_t ldy, hipStream_t st);
 
 // Activation pass for the matrix kernels: aq[r, c] * scale[r, c/256] == A_hat[r, c].
+// macro_in as for launch_quantize.
 hipError_t launch_act_prep(const void* a, int in_bf16, int64_t rows, int64_t k, int64_t lda,
-                           int elem_e4m3, _Float16* aq, int64_t ldq, float* scale, hipStream_t st);
+                           int elem_e4m3, _Float16* aq, int64_t ldq, float* scale,
+                           const uint16_t* macro_in, hipStream_t st);
+
+// Static activation macro-scale calibration: amax[g] = max(amax[g], max |x[:, g]|), then
+// macro[g] = the dynamic macro rule on amax[g] (0 for a zero maximum).
+hipError_t launch_act_calibrate(const void* x, int in_bf16, int64_t rows, int64_t k, int64_t ldx,
+                                int elem_e4m3, float* amax, uint16_t* macro, hipStream_t st);
 
 // Gated form: a row holds gate in [0, k) and up in [k, 2k) (bf16, row stride lda >= 2k);
 // the operand is h = bf16(silu(gate) * up).
@@ -41,7 +50,7 @@ struct GemmArgs {
   const float* a_scale;     // [a_rows x k/256] or nullptr (== 1)
   int64_t m;                // rows of C (dense) / total routed rows (grouped)
   int64_t n, k;
-  const uint8_t* codes;     // tiled E2M1 weights; experts stacked along rows
+  const uint8_t* codes;     // tiled E2M1 (or, w_e4m3, E4M3) weights; experts stacked along rows
   const uint8_t* micro;
   const uint16_t* macro;
   void* c;
@@ -50,7 +59,10 @@ struct GemmArgs {
   const int32_t* row_token;       // grouped only, may be nullptr
   const int32_t* expert_offsets;  // grouped only; nullptr for a dense product
   int32_t n_experts;
+  int w_e4m3;               // E4M3 weights (dense, FP16 activation operand only)
 };
+// Reduction lengths the product kernel covers (its per-group tables fit in LDS).
+bool gemm_supports(int64_t k);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 
 // Plain float32 product for float32 activations (small shapes): one thread per output.

@@ -15,6 +15,12 @@
 // Weight fragments come straight from the tiled layout (each lane's 16 bytes are one
 // MFMA operand row for four k-steps); activation fragments are 16-byte row pieces.
 //
+// Sensitive layers (W8A8): the same pipeline with E4M3 weight elements in their tiled
+// layout and the FP16 A8 activation operand: W' = e4m3 * mu * 2^-3 is exact in FP16 as
+// well, so the products stay exact; each wave then covers 32 weight rows (tile 64 x 128)
+// so that the doubled weight bytes fit the same LDS buffers. "NVIDIA Ships TensorRT-LLM
+// 0.16", deployment advice on outliers: FP8 kept on the most sensitive layers.
+//
 // Grouped form: the workgroup grid enumerates (expert, 64-row tile) pairs; each
 // workgroup finds its expert by a prefix sum over the per-expert tile counts, so one
 // launch covers every expert whatever the routing produced (including empty experts).
@@ -50,6 +56,19 @@ struct OpTraits<0> {  // FP16 operands
     const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * m2;
     const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * m2;
     const half2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * m2;
+    return frag{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+  }
+  // E4M3 weights (8 codes in two dwords): each code pair is converted with scale 2^5
+  // (exact: the conversion applies a power of two) and multiplied by mu * 2^-8, so the
+  // operand is e4m3 * mu * 2^-3, exact in FP16 (at most 8 significant bits, lowest bit
+  // >= 2^-21, at most 25088); the column factor carries the 8
+  static constexpr float kMicroUnit8 = 8.0f;
+  __device__ static __forceinline__ frag weight8(uint32_t d0, uint32_t d1, uint32_t mu_op) {
+    const half2_t m2 = __builtin_bit_cast(half2_t, mu_op);
+    const half2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 32.0f, false) * m2;
+    const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 32.0f, true) * m2;
+    const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 32.0f, false) * m2;
+    const half2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 32.0f, true) * m2;
     return frag{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
   }
   __device__ static __forceinline__ float4_t mfma(frag a, frag b, float4_t c) {
@@ -159,56 +178,80 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 // ---------------------------------------------------------------------------------
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 constexpr int kBM = 64;              // rows per workgroup
-constexpr int kBN = 256;             // weight rows (output columns) per workgroup
 constexpr int kStageK = 128;         // k per pipeline stage
 constexpr int kAStage = kBM * kStageK * 2 / 16;  // 16-byte chunks: [mi 4][t 4][64]
-constexpr int kWStage = kBN * kStageK / 2 / 16;  // 16-byte chunks: [wave 4][ni 4][64]
+constexpr int kWStage = 256 * kStageK / 2 / 16;  // 16-byte chunks: [wave 4][piece 4][64]
 
 __shared__ uint4 g_a0[kAStage];
 __shared__ uint4 g_a1[kAStage];
 __shared__ uint4 g_w0[kWStage];
 __shared__ uint4 g_w1[kWStage];
 
-// dynamic LDS: float sa[G][64] then uint16 mw[16][G][16]
-size_t gemm_dynamic_lds(int groups) { return (size_t)groups * kBM * 4 + (size_t)(kBN / 16) * groups * 16 * 2; }
+// dynamic LDS: float sa[G][64] then uint16 mw[16][G][16] (at most 16 row blocks per tile)
+size_t gemm_dynamic_lds(int groups) { return (size_t)groups * kBM * 4 + (size_t)16 * groups * 16 * 2; }
 
-template <int A_BF16>
-struct StepOperands {
-  typedef typename OpTraits<A_BF16>::frag frag;
-  frag af[4], wf[4];
+// Weight-side shape of the pipeline. E2M1 weights (W8 = 0): 4 row blocks of 16 weight
+// rows per wave (workgroup tile 64 x 256), one 1 KB LDS-DMA piece per row block and stage.
+// E4M3 weights (W8 = 1): 2 row blocks per wave (tile 64 x 128), two 1 KB pieces per row
+// block and stage; either way a wave copies 4 pieces per stage into the same LDS buffers
+// and keeps the same 4 code words per lane.
+template <int W8>
+struct WShape {
+  static constexpr int NI = W8 ? 2 : 4;          // row blocks per wave
+  static constexpr int BN = 64 * NI;             // weight rows per workgroup
+  static constexpr int kTile = W8 ? kTile8CodeBytes : kTileCodeBytes;
 };
 
+template <int A_BF16, int W8>
+struct StepOperands {
+  typedef typename OpTraits<A_BF16>::frag frag;
+  frag af[4], wf[WShape<W8>::NI];
+};
+
+// weight fragment of row block ni for MFMA step T (0..3) of a stage, from the stage's code
+// words: E2M1 dword T of word ni; E4M3 dwords 2 (T % 2), +1 of word 2 ni + T / 2
+template <int A_BF16, int W8, int T>
+__device__ __forceinline__ typename OpTraits<A_BF16>::frag weight_frag(const uint4 (&cw)[4], int ni, uint32_t mu_op) {
+  typedef OpTraits<A_BF16> Op;
+  if constexpr (W8) {
+    const uint4 w = cw[2 * ni + (T >> 1)];
+    return (T & 1) ? Op::weight8(w.z, w.w, mu_op) : Op::weight8(w.x, w.y, mu_op);
+  } else {
+    const uint32_t c = T == 0 ? cw[ni].x : T == 1 ? cw[ni].y : T == 2 ? cw[ni].z : cw[ni].w;
+    return Op::weight(c, mu_op);
+  }
+}
+
 // operands of step T (0..3) of a stage: activation fragments from LDS, weight fragments
-// decoded from the stage's code words (dword T of the lane's 16 bytes per row block)
-// with micro-scale byte (4h+T)
-template <int A_BF16, int T>
+// decoded from the stage's code words with micro-scale byte (4h+T)
+template <int A_BF16, int W8, int T>
 __device__ __forceinline__ void stage_operands(const uint4* abuf, const uint4 (&cw)[4],
                                                int lane, const uint2 (&mu)[4], int h,
-                                               StepOperands<A_BF16>& o) {
+                                               StepOperands<A_BF16, W8>& o) {
   typedef OpTraits<A_BF16> Op;
   typedef typename Op::frag frag;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) o.af[mi] = __builtin_bit_cast(frag, abuf[(mi * 4 + T) * 64 + lane]);
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const uint32_t c = T == 0 ? cw[ni].x : T == 1 ? cw[ni].y : T == 2 ? cw[ni].z : cw[ni].w;
+  for (int ni = 0; ni < WShape<W8>::NI; ++ni) {
     const uint32_t mw = h == 0 ? mu[ni].x : mu[ni].y;
-    o.wf[ni] = Op::weight(c, Op::micro_operand((mw >> (8 * T)) & 0xFFu));
+    o.wf[ni] = weight_frag<A_BF16, W8, T>(cw, ni, Op::micro_operand((mw >> (8 * T)) & 0xFFu));
   }
 }
 
-template <int A_BF16, int T>
-__device__ __forceinline__ void stage_mfma(const StepOperands<A_BF16>& o, float4_t (&x)[4][4]) {
+template <int A_BF16, int W8>
+__device__ __forceinline__ void stage_mfma(const StepOperands<A_BF16, W8>& o, float4_t (&x)[4][WShape<W8>::NI]) {
   typedef OpTraits<A_BF16> Op;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
+    for (int ni = 0; ni < WShape<W8>::NI; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
 }
 
-// Interleave for the 16 MFMAs of a step with the next step's operand preparation: the
-// four activation-fragment LDS reads go right after the first MFMAs (their latency then
-// hides behind the rest of the step), the weight decode 3 VALU per MFMA.
+// Interleave for the MFMAs of a step with the next step's operand preparation: the four
+// activation-fragment LDS reads go right after the first MFMAs (their latency then hides
+// behind the rest of the step), the weight decode 3 VALU per MFMA.
+template <int W8>
 __device__ __forceinline__ void interleave_step() {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -217,43 +260,45 @@ __device__ __forceinline__ void interleave_step() {
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
   }
 #pragma unroll
-  for (int i = 4; i < 16; ++i) {
+  for (int i = 4; i < 4 * WShape<W8>::NI; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
   }
 }
 
 // per-row (ra) and per-column (rw) ratios s_g / s_{g+1} for the boundary after group g
+template <int W8>
 struct Rescale {
   float ra[4][4];
-  float rw[4];
+  float rw[WShape<W8>::NI];
 };
 
-// Last MFMA step of a stage (step 3): its 16 MFMAs interleaved with
+// Last MFMA step of a stage (step 3): its MFMAs interleaved with
 //   - the code words and step-0 weight fragments of the next stage (read from the
 //     wave's own LDS buffer after waiting for its own copies: at most VMCNT younger
 //     loads may stay in flight), and
 //   - for the last stage of a group (RATIOS), the group-boundary ratios, applied in the
 //     next group's first step (the operands of step 2 are dead here).
-template <int A_BF16, bool RATIOS, int VMCNT, typename RatioFn>
-__device__ __forceinline__ void last_step(const StepOperands<A_BF16>& o, float4_t (&x)[4][4],
-                                          RatioFn&& ratios, Rescale& r, const uint4* nwbuf, int wave,
+template <int A_BF16, int W8, bool RATIOS, int VMCNT, typename RatioFn>
+__device__ __forceinline__ void last_step(const StepOperands<A_BF16, W8>& o, float4_t (&x)[4][WShape<W8>::NI],
+                                          RatioFn&& ratios, Rescale<W8>& r, const uint4* nwbuf, int wave,
                                           int lane, const uint32_t (&mw_next)[4], uint4 (&cw)[4],
-                                          typename OpTraits<A_BF16>::frag (&wf0)[4]) {
+                                          typename OpTraits<A_BF16>::frag (&wf0)[WShape<W8>::NI]) {
   typedef OpTraits<A_BF16> Op;
+  constexpr int NI = WShape<W8>::NI;
   __builtin_amdgcn_s_waitcnt(kVmcntWait<VMCNT>::value);
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) cw[ni] = nwbuf[(wave * 4 + ni) * 64 + lane];
+  for (int d = 0; d < 4; ++d) cw[d] = nwbuf[(wave * 4 + d) * 64 + lane];
   if (RATIOS) ratios(r);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
+    for (int ni = 0; ni < NI; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
-    wf0[ni] = Op::weight(cw[ni].x, Op::micro_operand(mw_next[ni] & 0xFFu));
+  for (int ni = 0; ni < NI; ++ni)
+    wf0[ni] = weight_frag<A_BF16, W8, 0>(cw, ni, Op::micro_operand(mw_next[ni] & 0xFFu));
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 4 * NI; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, RATIOS ? 5 : 3, 0);  // VALU
   }
@@ -264,67 +309,70 @@ __device__ __forceinline__ void last_step(const StepOperands<A_BF16>& o, float4_
 // group multiplies each running sum by the boundary ratios r just before that tile's
 // first MFMA of the group (no wait on MFMA results: those sums were finished a step
 // earlier). RATIOS: the last stage of a group computes the next ratios into r.
-template <int A_BF16, bool RESCALE, bool RATIOS, int VMCNT, typename RatioFn>
+template <int A_BF16, int W8, bool RESCALE, bool RATIOS, int VMCNT, typename RatioFn>
 __device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
-                                              typename OpTraits<A_BF16>::frag (&wf0)[4], int wave,
-                                              int lane, const uint2 (&mu)[4], int h, float4_t (&x)[4][4],
-                                              RatioFn&& ratios, Rescale& r, const uint4* nwbuf,
-                                              const uint2 (&mu_next)[4], int h_next) {
+                                              typename OpTraits<A_BF16>::frag (&wf0)[WShape<W8>::NI], int wave,
+                                              int lane, const uint2 (&mu)[4], int h,
+                                              float4_t (&x)[4][WShape<W8>::NI], RatioFn&& ratios, Rescale<W8>& r,
+                                              const uint4* nwbuf, const uint2 (&mu_next)[4], int h_next) {
   typedef OpTraits<A_BF16> Op;
   typedef typename Op::frag frag;
-  StepOperands<A_BF16> o0, o1;
+  constexpr int NI = WShape<W8>::NI;
+  StepOperands<A_BF16, W8> o0, o1;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) o0.af[mi] = __builtin_bit_cast(frag, abuf[(mi * 4 + 0) * 64 + lane]);
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) o0.wf[ni] = wf0[ni];
+  for (int ni = 0; ni < NI; ++ni) o0.wf[ni] = wf0[ni];
   __builtin_amdgcn_sched_barrier(0);
   if (RESCALE) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
+      for (int ni = 0; ni < NI; ++ni) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[mi][ni][i] *= A_BF16 ? r.rw[ni] : r.ra[mi][i] * r.rw[ni];
         x[mi][ni] = Op::mfma(o0.af[mi], o0.wf[ni], x[mi][ni]);
       }
-    stage_operands<A_BF16, 1>(abuf, cw, lane, mu, h, o1);
+    stage_operands<A_BF16, W8, 1>(abuf, cw, lane, mu, h, o1);
     __builtin_amdgcn_sched_group_barrier(0x002, A_BF16 ? 4 : 8, 0);  // VALU: tile 0's rescale
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 4 * NI; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       if (i < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x002, A_BF16 ? 6 : 10, 0);  // VALU
     }
   } else {
-    stage_mfma<A_BF16, 0>(o0, x);
-    stage_operands<A_BF16, 1>(abuf, cw, lane, mu, h, o1);
-    interleave_step();
+    stage_mfma<A_BF16, W8>(o0, x);
+    stage_operands<A_BF16, W8, 1>(abuf, cw, lane, mu, h, o1);
+    interleave_step<W8>();
   }
   __builtin_amdgcn_sched_barrier(0);
-  stage_mfma<A_BF16, 1>(o1, x);
-  stage_operands<A_BF16, 2>(abuf, cw, lane, mu, h, o0);
-  interleave_step();
+  stage_mfma<A_BF16, W8>(o1, x);
+  stage_operands<A_BF16, W8, 2>(abuf, cw, lane, mu, h, o0);
+  interleave_step<W8>();
   __builtin_amdgcn_sched_barrier(0);
-  stage_mfma<A_BF16, 2>(o0, x);
-  stage_operands<A_BF16, 3>(abuf, cw, lane, mu, h, o1);
-  interleave_step();
+  stage_mfma<A_BF16, W8>(o0, x);
+  stage_operands<A_BF16, W8, 3>(abuf, cw, lane, mu, h, o1);
+  interleave_step<W8>();
   __builtin_amdgcn_sched_barrier(0);
   uint32_t mw_next[4];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) mw_next[ni] = h_next == 0 ? mu_next[ni].x : mu_next[ni].y;
-  last_step<A_BF16, RATIOS, VMCNT>(o1, x, ratios, r, nwbuf, wave, lane, mw_next, cw, wf0);
+  for (int ni = 0; ni < NI; ++ni) mw_next[ni] = h_next == 0 ? mu_next[ni].x : mu_next[ni].y;
+  last_step<A_BF16, W8, RATIOS, VMCNT>(o1, x, ratios, r, nwbuf, wave, lane, mw_next, cw, wf0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int A_BF16, int C_BF16, int GROUPED>
+template <int A_BF16, int C_BF16, int GROUPED, int W8>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
+  static_assert(!W8 || (!A_BF16 && !GROUPED), "E4M3 weights: dense, FP16 activation operand");
+  constexpr int NI = WShape<W8>::NI, BN = WShape<W8>::BN, kTile = WShape<W8>::kTile;
   extern __shared__ uint8_t g_dyn[];
   const int groups = (int)(args.k >> 8);
   const int64_t n = args.n;
   const int64_t nblocks = n >> 4;
-  const int tiles_n = (int)((n + kBN - 1) / kBN);
+  const int tiles_n = (int)((n + BN - 1) / BN);
   float* g_sa = reinterpret_cast<float*>(g_dyn);                               // [g][64]
-  uint16_t* g_mw = reinterpret_cast<uint16_t*>(g_dyn + (size_t)groups * kBM * 4);  // [16][g][16]
+  uint16_t* g_mw = reinterpret_cast<uint16_t*>(g_dyn + (size_t)groups * kBM * 4);  // [BN/16][g][16]
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; give each XCD a
   // contiguous run of tiles (n fastest) so its L2 keeps the same activation rows.
@@ -348,8 +396,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   // wave index as a wave-uniform (scalar) value: LDS-DMA destinations derive from it
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q = lane >> 4, l16 = lane & 15;
-  const int64_t n0 = (int64_t)tn * kBN + wave * 64;  // first output column of this wave
-  const int64_t nb_tile0 = w_row_base / 16 + (int64_t)tn * (kBN / 16);  // first row block of the tile
+  const int64_t n0 = (int64_t)tn * BN + wave * 16 * NI;  // first output column of this wave
+  const int64_t nb_tile0 = w_row_base / 16 + (int64_t)tn * (BN / 16);  // first row block of the tile
 
   // ---- one-time tables: activation factors [g][row] and the tile's macro-scales ----
   if (!A_BF16) {  // the FP16 operand path always carries activation factors
@@ -360,8 +408,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
                                        (lds_void_ptr)(g_sa + g * kBM), 4, 0, 0);
   }
   {
-    // the tile's 16 row blocks x G groups x 16 rows of macro-scales are contiguous
-    const int mw_elems = (kBN / 16) * groups * 16;  // uint16 count
+    // the tile's BN/16 row blocks x G groups x 16 rows of macro-scales are contiguous
+    const int mw_elems = (BN / 16) * groups * 16;  // uint16 count
     const int64_t mw_first = nb_tile0 * groups * 16;
     const int64_t mw_last = (w_row_base / 16 + nblocks) * groups * 16;  // exclusive bound
     for (int c0 = wave * 64 * 2; c0 < mw_elems; c0 += 256 * 2) {  // 4-byte lanes = 2 entries
@@ -384,16 +432,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
       (void*)(a16 + a_base_row * args.lda), (short)0, (int)0xFFFFFFFF, kRsrcWord3);
   const uint32_t a_voff = (uint32_t)(((a_src_row - a_base_row) * args.lda + 8 * q) * 2);
 
-  // ---- weights: 4 row blocks (16 columns each) per wave, consecutive in the tiled layout ----
-  bool w_ok[4];
+  // ---- weights: NI row blocks (16 columns each) per wave, consecutive in the tiled layout ----
+  bool w_ok[NI];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) w_ok[ni] = n0 / 16 + ni < nblocks;
+  for (int ni = 0; ni < NI; ++ni) w_ok[ni] = n0 / 16 + ni < nblocks;
   const int64_t wb0 = w_row_base / 16 + n0 / 16;               // the wave's first row block
   const int64_t w_blocks_left = w_row_base / 16 + nblocks - wb0;  // row blocks up to the end
   const int64_t w_tiles_left = w_blocks_left > 0 ? w_blocks_left * groups : 0;
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(args.codes + wb0 * groups * kTileCodeBytes), (short)0,
-      (int)min(w_tiles_left * kTileCodeBytes, (int64_t)0xFFFFFFFF), kRsrcWord3);
+      (void*)(args.codes + wb0 * groups * kTile), (short)0,
+      (int)min(w_tiles_left * kTile, (int64_t)0xFFFFFFFF), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t mu_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(args.micro + wb0 * groups * kTileMicroBytes), (short)0,
       (int)min(w_tiles_left * kTileMicroBytes, (int64_t)0xFFFFFFFF), kRsrcWord3);
@@ -405,42 +453,48 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     for (int t = 0; t < 4; ++t)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(abuf + (wave * 4 + t) * 64), 16,
                                                a_voff, a_soff + 64 * t, 0, 0);
+    // piece d: row block d (E2M1) or d / 2, half d % 2 of the stage's 2 KB (E4M3)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          w_rsrc, (lds_void_ptr)(wbuf + (wave * 4 + ni) * 64), 16, (uint32_t)lane * 16,
-          (uint32_t)((ni * groups + g) * kTileCodeBytes + h * 1024), 0, 0);
+    for (int d = 0; d < 4; ++d) {
+      const int ni = W8 ? d >> 1 : d;
+      const uint32_t soff = (uint32_t)((ni * groups + g) * kTile + h * (kTile / 2) + (W8 ? (d & 1) * 1024 : 0));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(wbuf + (wave * 4 + d) * 64), 16,
+                                               (uint32_t)lane * 16, soff, 0, 0);
+    }
   };
   auto load_micro = [&](uint2 (&mu)[4], int g) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+    for (int ni = 0; ni < NI; ++ni) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b64(mu_rsrc, mu_voff,
                                                          (uint32_t)((ni * groups + g) * kTileMicroBytes), 0);
       mu[ni] = make_uint2(v[0], v[1]);
     }
   };
 
-  float4_t x[4][4];
+  float4_t x[4][NI];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) x[mi][ni] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ni = 0; ni < NI; ++ni) x[mi][ni] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const float* sa_lane = g_sa + 4 * q;                               // + g*64 + mi*16: rows 4q..4q+3
-  const uint16_t* mw_lane = g_mw + (wave * 4) * groups * 16 + l16;    // + (ni*G + g)*16
+  const uint16_t* mw_lane = g_mw + (wave * NI) * groups * 16 + l16;   // + (ni*G + g)*16
   // column factor M_W of group g (a zero factor counts as 1: its columns' codes are 0)
   auto col_factor = [&](int ni, int g) {
     const float v = fp16_value_hw(mw_lane[(ni * groups + g) * 16]);
     return v != 0.0f ? v : 1.0f;
   };
+  // unit the weight operand leaves in the column factor: 2^8 (E2M1 * mu * 2^-8 in FP16),
+  // 8 (E4M3 * mu * 2^-3), 1 on the bf16 path
+  constexpr float kUnit = W8 ? OpTraits<0>::kMicroUnit8 : OpTraits<A_BF16>::kMicroUnit;
   // ratios s_g / s_{g+1} for the boundary after group g, with s_G = 1: after the last
   // group the "ratio" is the final factor itself. Row ratios come from the table built
-  // in the prologue; the FP16 path's 2^8 micro unit cancels except in the final factor.
-  auto ratios_after = [&](int g, Rescale& r) {
+  // in the prologue; the weight operand's unit cancels except in the final factor.
+  auto ratios_after = [&](int g, Rescale<W8>& r) {
     const bool last = g + 1 >= groups;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      r.rw[ni] = last ? col_factor(ni, g) * OpTraits<A_BF16>::kMicroUnit
+    for (int ni = 0; ni < NI; ++ni)
+      r.rw[ni] = last ? col_factor(ni, g) * kUnit
                       : col_factor(ni, g) * __builtin_amdgcn_rcpf(col_factor(ni, g + 1));
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -457,7 +511,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   load_micro(mu_cur, 0);
   // stage 0's code words and step-0 weight fragments (the wave's own copies)
   uint4 cw[4];
-  typename OpTraits<A_BF16>::frag wf0[4];
+  typename OpTraits<A_BF16>::frag wf0[NI];
   __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
   if (!A_BF16) {
     // row factors [g][row] -> ratios f_g / f_{g+1} (last group: f_{G-1}), in place; each
@@ -473,10 +527,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     }
   }
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    cw[ni] = g_w0[(wave * 4 + ni) * 64 + lane];
-    wf0[ni] = OpTraits<A_BF16>::weight(cw[ni].x, OpTraits<A_BF16>::micro_operand(mu_cur[ni].x & 0xFFu));
-  }
+  for (int d = 0; d < 4; ++d) cw[d] = g_w0[(wave * 4 + d) * 64 + lane];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    wf0[ni] = weight_frag<A_BF16, W8, 0>(cw, ni, OpTraits<A_BF16>::micro_operand(mu_cur[ni].x & 0xFFu));
 
   // stage s in buffers (s & 1): the barrier publishes its activation tile (every wave's
   // copies are complete) and frees the other buffers, which then receive stage s + 1
@@ -484,31 +538,32 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   // every group ends with the group-boundary rescale.
   // boundary ratios carried from the last stage of a group into the first of the next
   // (1 before the first group; after the last group they are the final factors)
-  Rescale resc;
+  Rescale<W8> resc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    resc.rw[i] = 1.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) resc.ra[i][j] = 1.0f;
   }
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) resc.rw[ni] = 1.0f;
   auto run_stage = [&](auto h_const, const uint4* abuf, uint4* nabuf, uint4* nwbuf, int s) {
     constexpr int H = decltype(h_const)::value;
     __syncthreads();
     if (s + 1 < stages) copy_stage(nabuf, nwbuf, s + 1);
     __builtin_amdgcn_sched_barrier(0);
     // (unconditional in H == 0 stages, the last group re-reading its own, so that exactly
-    // four loads follow the copies when last_step waits for them)
+    // NI loads follow the copies when last_step waits for them)
     if (H == 0) load_micro(mu_nxt, min((s >> 1) + 1, groups - 1));
     __builtin_amdgcn_sched_barrier(0);
     // next stage: same group (H == 0: micro-scale word 1 of mu_cur) or the next group
-    // (H == 1: word 0 of mu_nxt); the H == 0 stage's four micro-scale loads may stay in
+    // (H == 1: word 0 of mu_nxt); the H == 0 stage's NI micro-scale loads may stay in
     // flight
-    compute_stage<A_BF16, H == 0, H == 1, H == 0 ? 4 : 0>(
-        abuf, cw, wf0, wave, lane, mu_cur, H, x, [&](Rescale& rr) { ratios_after(s >> 1, rr); }, resc,
+    compute_stage<A_BF16, W8, H == 0, H == 1, H == 0 ? NI : 0>(
+        abuf, cw, wf0, wave, lane, mu_cur, H, x, [&](Rescale<W8>& rr) { ratios_after(s >> 1, rr); }, resc,
         nwbuf, H == 0 ? mu_cur : mu_nxt, 1 - H);
     if (H == 1) {
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) mu_cur[ni] = mu_nxt[ni];
+      for (int ni = 0; ni < NI; ++ni) mu_cur[ni] = mu_nxt[ni];
     }
   };
   for (int s = 0; s < stages; s += 2) {
@@ -520,7 +575,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+    for (int ni = 0; ni < NI; ++ni) {
       if (!w_ok[ni]) continue;
       const int64_t col = n0 + 16 * ni + l16;
 #pragma unroll
@@ -580,7 +635,9 @@ bool gemm_supports(int64_t k) { return gemm_dynamic_lds((int)(k >> 8)) <= 64 * 1
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (!gemm_supports(g.k)) return hipErrorInvalidValue;
-  const int64_t tiles_n = (g.n + kBN - 1) / kBN;
+  if (g.w_e4m3 && (g.a_is_bf16 || g.expert_offsets)) return hipErrorInvalidValue;
+  const int64_t bn = g.w_e4m3 ? WShape<1>::BN : WShape<0>::BN;
+  const int64_t tiles_n = (g.n + bn - 1) / bn;
   int64_t tiles_m;
   if (g.expert_offsets) tiles_m = (g.m + kBM - 1) / kBM + g.n_experts;  // upper bound
   else tiles_m = (g.m + kBM - 1) / kBM;
@@ -588,14 +645,16 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(256);
   const size_t lds = gemm_dynamic_lds((int)(g.k >> 8));
-#define FP4_GEMM(A, C, G) hipLaunchKernelGGL((k_gemm<A, C, G>), grid, block, lds, st, g)
+#define FP4_GEMM(A, C, G, W) hipLaunchKernelGGL((k_gemm<A, C, G, W>), grid, block, lds, st, g)
   const int grouped = g.expert_offsets != nullptr;
-  if (g.a_is_bf16) {
-    if (g.c_is_bf16) { if (grouped) FP4_GEMM(1, 1, 1); else FP4_GEMM(1, 1, 0); }
-    else { if (grouped) FP4_GEMM(1, 0, 1); else FP4_GEMM(1, 0, 0); }
+  if (g.w_e4m3) {
+    if (g.c_is_bf16) FP4_GEMM(0, 1, 0, 1); else FP4_GEMM(0, 0, 0, 1);
+  } else if (g.a_is_bf16) {
+    if (g.c_is_bf16) { if (grouped) FP4_GEMM(1, 1, 1, 0); else FP4_GEMM(1, 1, 0, 0); }
+    else { if (grouped) FP4_GEMM(1, 0, 1, 0); else FP4_GEMM(1, 0, 0, 0); }
   } else {
-    if (g.c_is_bf16) { if (grouped) FP4_GEMM(0, 1, 1); else FP4_GEMM(0, 1, 0); }
-    else { if (grouped) FP4_GEMM(0, 0, 1); else FP4_GEMM(0, 0, 0); }
+    if (g.c_is_bf16) { if (grouped) FP4_GEMM(0, 1, 1, 0); else FP4_GEMM(0, 1, 0, 0); }
+    else { if (grouped) FP4_GEMM(0, 0, 1, 0); else FP4_GEMM(0, 0, 0, 0); }
   }
 #undef FP4_GEMM
   return hipGetLastError();

@@ -43,16 +43,40 @@ __device__ __forceinline__ bool seg_index(int64_t groups, int64_t& r, int64_t& g
   return g < groups;
 }
 
+// Scales of a lane that owns one micro-vector when the macro-scale is given (static
+// activation scales, calibrated beforehand): mu = RNE_e4m3(amax_16 / (emax * M)), which
+// saturates at 448 for blocks beyond the calibrated range; M = 0 gives mu = 0.
+__device__ __forceinline__ float static_block_scales(const float v[16], float emax, uint32_t m_in,
+                                                     uint32_t& m_bits, uint32_t& mu_byte, float& m_val) {
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
+  m_bits = m_in & 0xFFFFu;
+  m_val = fp16_value(m_bits);
+  mu_byte = m_val > 0.0f ? e4m3_rne_pos(amax_b / (emax * m_val)) : 0u;
+  return e4m3_value(mu_byte) * m_val;
+}
+
+template <int ELEM_E4M3, int STATIC>
+__device__ __forceinline__ float item_scales(const float v[16], int64_t g, const uint16_t* __restrict__ macro_in,
+                                             uint32_t& m_bits, uint32_t& mu_byte, float& m_val) {
+  const float emax = ELEM_E4M3 ? 448.0f : 6.0f;
+  if (STATIC) return static_block_scales(v, emax, macro_in[g], m_bits, mu_byte, m_val);
+  return block_scales(v, emax, m_bits, mu_byte, m_val);
+}
+
 // Encodes one micro-vector (v, 16 elements of row r at column col) and stores its codes,
-// micro-scale and (lane 0 of the group) macro-scale.
-template <int ELEM_E4M3, int TILED>
+// micro-scale and (lane 0 of the group) macro-scale. STATIC: the macro-scale of group g is
+// macro_in[g] (shared by every row) instead of the group's own.
+template <int ELEM_E4M3, int TILED, int STATIC>
 __device__ __forceinline__ void quantize_item(const float v[16], int64_t r, int64_t g, int li,
                                               int64_t k, int64_t groups, uint8_t* __restrict__ codes,
-                                              uint8_t* __restrict__ micro, uint16_t* __restrict__ macro) {
+                                              uint8_t* __restrict__ micro, uint16_t* __restrict__ macro,
+                                              const uint16_t* __restrict__ macro_in) {
   const int64_t col = g * kGroup + li * 16;
   uint32_t m_bits, mu_byte;
   float m_val;
-  const float s = block_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
+  const float s = item_scales<ELEM_E4M3, STATIC>(v, g, macro_in, m_bits, mu_byte, m_val);
 
   if (!ELEM_E4M3) {
     uint32_t w0, w1;
@@ -70,7 +94,12 @@ __device__ __forceinline__ void quantize_item(const float v[16], int64_t r, int6
       for (int i = 0; i < 16; ++i)
         w[i >> 2] |= (e4m3_rne_pos(fabsf(v[i]) / s) | (sign_of(v[i]) << 7)) << (8 * (i & 3));
     }
-    *reinterpret_cast<uint4*>(codes + r * k + col) = make_uint4(w[0], w[1], w[2], w[3]);
+    if (TILED) {
+      *reinterpret_cast<uint2*>(codes + tiled8_code_offset(r, col, groups)) = make_uint2(w[0], w[1]);
+      *reinterpret_cast<uint2*>(codes + tiled8_code_offset(r, col + 8, groups)) = make_uint2(w[2], w[3]);
+    } else {
+      *reinterpret_cast<uint4*>(codes + r * k + col) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
   {
     const int64_t off = TILED ? tiled_micro_offset(r, col, groups) : r * (k >> 4) + (col >> 4);
@@ -82,12 +111,13 @@ __device__ __forceinline__ void quantize_item(const float v[16], int64_t r, int6
   }
 }
 
-template <int IN_BF16, int ELEM_E4M3, int TILED>
+template <int IN_BF16, int ELEM_E4M3, int TILED, int STATIC>
 __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t ldx,
                                                   int64_t rows, int64_t k,
                                                   uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ micro,
-                                                  uint16_t* __restrict__ macro) {
+                                                  uint16_t* __restrict__ macro,
+                                                  const uint16_t* __restrict__ macro_in) {
   const int64_t groups = k >> 8;
   const int li = threadIdx.x & 15;  // micro-vector of the group
   int64_t r, g;
@@ -96,7 +126,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
   load_raw16<IN_BF16>(x, r * ldx + g * kGroup + li * 16, raw);
   float v[16];
   unpack16<IN_BF16>(raw, v);
-  quantize_item<ELEM_E4M3, TILED>(v, r, g, li, k, groups, codes, micro, macro);
+  quantize_item<ELEM_E4M3, TILED, STATIC>(v, r, g, li, k, groups, codes, micro, macro, macro_in);
 }
 
 template <int OUT_BF16, int ELEM_E4M3, int TILED>
@@ -125,7 +155,8 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
       v[i] = (c & 8u) ? -mag : mag;
     }
   } else {
-    const uint2 p = *reinterpret_cast<const uint2*>(codes + r * k + col);
+    const int64_t off = TILED ? tiled8_code_offset(r, col, groups) : r * k + col;
+    const uint2 p = *reinterpret_cast<const uint2*>(codes + off);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t b = ((i < 4 ? p.x : p.y) >> (8 * (i & 3))) & 0xFFu;
@@ -158,14 +189,16 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 // products, fused with the down product's dynamic quantization).
 // Encodes one micro-vector of the activation pass (v, 16 elements of row r at column col)
 // into the FP16 operand and, from lane 0 of the group, the group factor.
-template <int ELEM_E4M3>
+// STATIC: the macro-scale of group g is macro_in[g] for every row (calibrated activation
+// scales); the factor written is then the same for all rows.
+template <int ELEM_E4M3, int STATIC>
 __device__ __forceinline__ void act_item(float v[16], int64_t r, int64_t g, int li, int64_t groups,
                                          _Float16* __restrict__ aq, int64_t ldq,
-                                         float* __restrict__ scale) {
+                                         float* __restrict__ scale, const uint16_t* __restrict__ macro_in) {
   const int64_t col = g * kGroup + li * 16;
   uint32_t m_bits, mu_byte;
   float m_val;
-  const float s = block_scales(v, ELEM_E4M3 ? 448.0f : 6.0f, m_bits, mu_byte, m_val);
+  const float s = item_scales<ELEM_E4M3, STATIC>(v, g, macro_in, m_bits, mu_byte, m_val);
   const float mu = e4m3_value(mu_byte);
   half2_t out[8];
   if (!ELEM_E4M3) {
@@ -202,11 +235,12 @@ __device__ __forceinline__ void act_item(float v[16], int64_t r, int64_t g, int 
   if (li == 0) scale[r * groups + g] = m_val > 0.0f ? (ELEM_E4M3 ? m_val * 8.0f : m_val) : 1.0f;
 }
 
-template <int IN_BF16, int ELEM_E4M3, int GATED>
+template <int IN_BF16, int ELEM_E4M3, int GATED, int STATIC>
 __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, int64_t lda,
                                                   int64_t rows, int64_t k,
                                                   _Float16* __restrict__ aq, int64_t ldq,
-                                                  float* __restrict__ scale) {
+                                                  float* __restrict__ scale,
+                                                  const uint16_t* __restrict__ macro_in) {
   const int64_t groups = k >> 8;
   const int li = threadIdx.x & 15;
   int64_t r, g;
@@ -228,7 +262,60 @@ __global__ __launch_bounds__(256) void k_act_prep(const void* __restrict__ a, in
       v[i] = __uint_as_float(bf16_rne_bits(h) << 16);
     }
   }
-  act_item<ELEM_E4M3>(v, r, g, li, groups, aq, ldq, scale);
+  act_item<ELEM_E4M3, STATIC>(v, r, g, li, groups, aq, ldq, scale, macro_in);
+}
+
+// Calibration of static activation macro-scales. k_amax_update keeps a running maximum
+// of |x| per 256-column group over every row it has seen: block (group g, runs of 64 rows
+// strided by gridDim.y) reads 8 rows per pass, 32 lanes x 16 bytes per row; the block's
+// maximum enters amax[g] by an atomic maximum on the float bits (non-negative floats
+// order as their bit patterns, so the result does not depend on the order).
+// k_macro_from_amax then applies the dynamic macro rule to that maximum.
+constexpr int kCalRows = 64;
+
+template <int IN_BF16>
+__global__ __launch_bounds__(256) void k_amax_update(const void* __restrict__ x, int64_t ldx, int64_t rows,
+                                                     float* __restrict__ amax) {
+  const int64_t g = blockIdx.x;
+  const int sub = threadIdx.x >> 5, li = threadIdx.x & 31;
+  float m = 0.0f;
+  for (int64_t r0 = (int64_t)blockIdx.y * kCalRows; r0 < rows; r0 += (int64_t)gridDim.y * kCalRows) {
+    const int64_t r_end = min(r0 + kCalRows, rows);
+    for (int64_t r = r0 + sub; r < r_end; r += 8) {
+      const int64_t off = r * ldx + g * kGroup + li * 8;
+      if (IN_BF16) {
+        const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[j] << 16)), fabsf(__uint_as_float(w[j] & 0xFFFF0000u))));
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float4 f = p[j];
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  __shared__ float s_m[4];
+  if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float bm = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(amax + g), __float_as_uint(bm));
+  }
+}
+
+__global__ __launch_bounds__(256) void k_macro_from_amax(const float* __restrict__ amax, int64_t groups, float emax,
+                                                         uint16_t* __restrict__ macro) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= groups) return;
+  const float a = amax[g];
+  macro[g] = (uint16_t)(a > 0.0f ? fp16_rne_pos_clamped(a / (emax * 448.0f)) : 0u);
 }
 
 // one block per 16 (row, group) pairs; 0 when the grid would exceed 2^32 work-items (the
@@ -251,16 +338,22 @@ namespace fp4lib {
 
 hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, int64_t ldx,
                            int elem_e4m3, int tiled, uint8_t* codes, uint8_t* micro,
-                           uint16_t* macro, hipStream_t st) {
+                           uint16_t* macro, const uint16_t* macro_in, hipStream_t st) {
   const dim3 grid(blocks_for16(rows, k)), block(256);
   if (grid.x == 0) return hipErrorInvalidValue;
-#define FP4_Q(B, E, T) \
-  hipLaunchKernelGGL((k_quantize<B, E, T>), grid, block, 0, st, x, ldx, rows, k, codes, micro, macro)
-  if (in_bf16) {
-    if (elem_e4m3) FP4_Q(1, 1, 0); else if (tiled) FP4_Q(1, 0, 1); else FP4_Q(1, 0, 0);
-  } else {
-    if (elem_e4m3) FP4_Q(0, 1, 0); else if (tiled) FP4_Q(0, 0, 1); else FP4_Q(0, 0, 0);
-  }
+  const int stat = macro_in != nullptr;
+#define FP4_Q(B, E, T, S) \
+  hipLaunchKernelGGL((k_quantize<B, E, T, S>), grid, block, 0, st, x, ldx, rows, k, codes, micro, macro, macro_in)
+#define FP4_Q_S(B, E, T) \
+  if (stat) FP4_Q(B, E, T, 1); else FP4_Q(B, E, T, 0)
+#define FP4_Q_T(B, E) \
+  if (tiled) { FP4_Q_S(B, E, 1); } else { FP4_Q_S(B, E, 0); }
+#define FP4_Q_E(B) \
+  if (elem_e4m3) { FP4_Q_T(B, 1) } else { FP4_Q_T(B, 0) }
+  if (in_bf16) { FP4_Q_E(1) } else { FP4_Q_E(0) }
+#undef FP4_Q_E
+#undef FP4_Q_T
+#undef FP4_Q_S
 #undef FP4_Q
   return hipGetLastError();
 }
@@ -272,22 +365,27 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const u
   if (grid.x == 0) return hipErrorInvalidValue;
 #define FP4_D(B, E, T) \
   hipLaunchKernelGGL((k_dequantize<B, E, T>), grid, block, 0, st, codes, micro, macro, rows, k, y, ldy)
-  if (out_bf16) {
-    if (elem_e4m3) FP4_D(1, 1, 0); else if (tiled) FP4_D(1, 0, 1); else FP4_D(1, 0, 0);
-  } else {
-    if (elem_e4m3) FP4_D(0, 1, 0); else if (tiled) FP4_D(0, 0, 1); else FP4_D(0, 0, 0);
-  }
+#define FP4_D_E(B) \
+  if (elem_e4m3) { if (tiled) FP4_D(B, 1, 1); else FP4_D(B, 1, 0); } \
+  else { if (tiled) FP4_D(B, 0, 1); else FP4_D(B, 0, 0); }
+  if (out_bf16) { FP4_D_E(1) } else { FP4_D_E(0) }
+#undef FP4_D_E
 #undef FP4_D
   return hipGetLastError();
 }
 
 hipError_t launch_act_prep(const void* a, int in_bf16, int64_t rows, int64_t k, int64_t lda,
-                           int elem_e4m3, _Float16* aq, int64_t ldq, float* scale, hipStream_t st) {
+                           int elem_e4m3, _Float16* aq, int64_t ldq, float* scale,
+                           const uint16_t* macro_in, hipStream_t st) {
   const dim3 grid(blocks_for16(rows, k)), block(256);
   if (grid.x == 0) return hipErrorInvalidValue;
-#define FP4_ACT(B, E, G) hipLaunchKernelGGL((k_act_prep<B, E, G>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale)
-  if (in_bf16) { if (elem_e4m3) FP4_ACT(1, 1, 0); else FP4_ACT(1, 0, 0); }
-  else { if (elem_e4m3) FP4_ACT(0, 1, 0); else FP4_ACT(0, 0, 0); }
+#define FP4_ACT(B, E, G, S) \
+  hipLaunchKernelGGL((k_act_prep<B, E, G, S>), grid, block, 0, st, a, lda, rows, k, aq, ldq, scale, macro_in)
+#define FP4_ACT_S(B, E) \
+  if (macro_in) FP4_ACT(B, E, 0, 1); else FP4_ACT(B, E, 0, 0)
+  if (in_bf16) { if (elem_e4m3) { FP4_ACT_S(1, 1); } else { FP4_ACT_S(1, 0); } }
+  else { if (elem_e4m3) { FP4_ACT_S(0, 1); } else { FP4_ACT_S(0, 0); } }
+#undef FP4_ACT_S
   return hipGetLastError();
 }
 
@@ -295,8 +393,24 @@ hipError_t launch_act_prep_gated(const uint16_t* a, int64_t rows, int64_t k, int
                                  _Float16* aq, int64_t ldq, float* scale, hipStream_t st) {
   const dim3 grid(blocks_for16(rows, k)), block(256);
   if (grid.x == 0) return hipErrorInvalidValue;
-  if (elem_e4m3) FP4_ACT(1, 1, 1); else FP4_ACT(1, 0, 1);
+  const uint16_t* macro_in = nullptr;
+  if (elem_e4m3) FP4_ACT(1, 1, 1, 0); else FP4_ACT(1, 0, 1, 0);
 #undef FP4_ACT
+  return hipGetLastError();
+}
+
+hipError_t launch_act_calibrate(const void* x, int in_bf16, int64_t rows, int64_t k, int64_t ldx,
+                                int elem_e4m3, float* amax, uint16_t* macro, hipStream_t st) {
+  const int64_t groups = k >> 8;
+  if (groups < 1 || groups > 0x7FFFFFFF || rows < 1) return hipErrorInvalidValue;
+  const int64_t chunks = (rows + kCalRows - 1) / kCalRows;
+  const dim3 grid((unsigned)groups, (unsigned)min(chunks, (int64_t)65535)), block(256);
+  if (in_bf16) hipLaunchKernelGGL((k_amax_update<1>), grid, block, 0, st, x, ldx, rows, amax);
+  else hipLaunchKernelGGL((k_amax_update<0>), grid, block, 0, st, x, ldx, rows, amax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_macro_from_amax, dim3((unsigned)((groups + 255) / 256)), block, 0, st, amax, groups,
+                     elem_e4m3 ? 448.0f : 6.0f, macro);
   return hipGetLastError();
 }
 

@@ -39,6 +39,11 @@
  *                micro byte T*256 + p*128 + n*8 + t   for block b = c/16 = 2t + p
  *                macro      T*16 + n                  (uint16 index)
  *              Total sizes equal the canonical ones.
+ *              E4M3 elements (rows % 16 == 0): tiles of 4096 code bytes, T as above;
+ *              with t, j, n as above,
+ *                code byte  T*4096 + (t/4)*2048 + ((t%4)/2)*1024 + (16*j + n)*16
+ *                           + (t%2)*8 + c%8
+ *              micro and macro as for E2M1.
  */
 #ifndef FP4_E2M1_H
 #define FP4_E2M1_H
@@ -67,9 +72,13 @@ enum {
 
 enum { FP4_F32 = 0, FP4_BF16 = 1 };                         /* element types of x/y/a/c */
 enum { FP4_A16 = 16, FP4_A8 = 8, FP4_A4 = 4 };              /* activation precision      */
+/* further precision codes of the policy table: W4A4 / W4A8 with static activation
+ * macro-scales (gemm_w4aX_static) and W8A8 (gemm_w8a8) */
+enum { FP4_A4S = 40, FP4_A8S = 80, FP4_W8A8 = 88 };
 enum { FP4_ELEM_E2M1 = 0, FP4_ELEM_E4M3 = 1 };              /* quantized element type    */
 enum { FP4_LAYOUT_CANONICAL = 0, FP4_LAYOUT_TILED = 1 };
-enum { FP4_POLICY_AUTO = 0, FP4_POLICY_Q4 = 4, FP4_POLICY_Q8 = 8 };
+enum { FP4_POLICY_AUTO = 0, FP4_POLICY_SENSITIVE_W8 = 1, FP4_POLICY_STATIC = 2,
+       FP4_POLICY_Q4 = 4, FP4_POLICY_Q8 = 8 };
 
 /* A quantized tensor in device memory (see the layouts above). */
 typedef struct fp4_tensor {
@@ -86,8 +95,8 @@ typedef struct fp4_tensor {
  * quantize_fp4 -- two-level block-scaled quantization of x [rows x k].
  *   x        device, FP4_F32 or FP4_BF16 values, row r at x + r*ldx elements
  *   ldx      row stride in elements (>= k; ldx * sizeof(elem) % 16 == 0)
- *   elem     FP4_ELEM_E2M1 (4-bit codes) or FP4_ELEM_E4M3 (8-bit codes, canonical only)
- *   layout   FP4_LAYOUT_CANONICAL or FP4_LAYOUT_TILED (E2M1, rows % 16 == 0)
+ *   elem     FP4_ELEM_E2M1 (4-bit codes) or FP4_ELEM_E4M3 (8-bit codes)
+ *   layout   FP4_LAYOUT_CANONICAL or FP4_LAYOUT_TILED (rows % 16 == 0)
  *   codes    device out: rows*k/2 bytes (E2M1) or rows*k bytes (E4M3), 16-byte aligned
  *   micro    device out: rows*k/16 bytes
  *   macro    device out: rows*k/256 uint16
@@ -96,6 +105,34 @@ typedef struct fp4_tensor {
 fp4_status quantize_fp4(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
                         int32_t elem, int32_t layout, void* codes, uint8_t* micro,
                         uint16_t* macro, void* stream);
+
+/*
+ * quantize_fp4_static -- quantize_fp4 with given macro-scales: macro_in (device, FP16 bit
+ * patterns [k/256], finite and non-negative, e.g. from act_macro_calibrate) is the macro-
+ * scale of every row's group g; mu = RNE_e4m3(amax_16 / (emax * M)) saturates at 448 and
+ * elements at the element maximum for blocks beyond the calibrated range; M = 0 gives
+ * zero codes. `macro` receives M for every row. Source: TensorRT-LLM FP4 page, section
+ * "Step 2: Executing FP4 Calibration and Engine Compilation" (activation ranges are
+ * calibrated ahead of deployment) and "Deployment Guidelines and Production Safeguards",
+ * item 1 (calibration data matching production traffic).
+ */
+fp4_status quantize_fp4_static(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                               int32_t elem, int32_t layout, const uint16_t* macro_in, void* codes,
+                               uint8_t* micro, uint16_t* macro, void* stream);
+
+/*
+ * act_macro_calibrate -- static activation macro-scales from calibration data x [rows x k]
+ * (device, FP4_BF16 or FP4_F32, stride ldx, 16-byte aligned rows):
+ *   amax[g]  = max(amax[g], max |x[r, 256 g .. 256 g + 255]| over every row)   (running)
+ *   macro[g] = FP16 bits of RNE_fp16(amax[g] / (emax * 448)) clamped to [2^-24, 65504],
+ *              0 when amax[g] == 0 (the dynamic rule applied to the group's maximum)
+ * amax: device float32 [k/256], zero it before the first batch; calling once per
+ * calibration batch leaves the macro-scales of everything seen so far in `macro` (device
+ * uint16 [k/256]). elem: the element type the activations will be quantized to. The
+ * order of the rows and calls does not change the result.
+ */
+fp4_status act_macro_calibrate(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                               int32_t elem, float* amax, uint16_t* macro, void* stream);
 
 /*
  * dequantize_fp4 -- y = value(code) * mu * M for every element of q (either layout).
@@ -123,6 +160,32 @@ fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t
 fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,
                      const fp4_tensor* w, void* c, int32_t c_dtype, int64_t ldc,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gemm_w4aX_static -- gemm_w4aX (FP4_A4 or FP4_A8 only) with static activation macro-
+ * scales: A_hat = dequant(quantize_fp4_static(A, act_macro)), act_macro device uint16
+ * [k/256] as for quantize_fp4_static. The micro-scales stay per row and per 16 elements.
+ *   workspace >= fp4_workspace_bytes(act, m, n, k) (also for FP4_A4S / FP4_A8S)
+ * k <= 21760 (FP4_E_SHAPE otherwise). Source: as for quantize_fp4_static; the policy
+ * table's FP4_A4S / FP4_A8S.
+ */
+fp4_status gemm_w4aX_static(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,
+                            const uint16_t* act_macro, const fp4_tensor* w, void* c, int32_t c_dtype,
+                            int64_t ldc, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gemm_w8a8 -- the product for precision-sensitive layers: C[m x n] = A_hat . W_hat^T with
+ * A_hat = dequant(quant_e4m3(A)) (the FP4_A8 activation quantization, dynamic) and W
+ * quantized with E4M3 elements (elem FP4_ELEM_E4M3, TILED layout; FP4_E_DTYPE for E2M1
+ * weights, FP4_E_LAYOUT for canonical ones). Every product of the two operands is exact;
+ * accumulation in float32. c bf16 (round to nearest even) or f32, stride ldc.
+ *   workspace >= fp4_workspace_bytes(FP4_W8A8, m, n, k); k <= 21760
+ * Source: "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for Blackwell B200",
+ * section "Deployment Guidelines and Production Safeguards", item 2 (FP8 kept on the most
+ * sensitive layers, such as the first layer and the output head).
+ */
+fp4_status gemm_w8a8(const void* a, int32_t a_dtype, int64_t m, int64_t lda, const fp4_tensor* w, void* c,
+                     int32_t c_dtype, int64_t ldc, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * grouped_gemm_w4aX -- mixture-of-experts product: for expert e and every routed row r
@@ -310,12 +373,17 @@ fp4_status gemm_mxfp4(const void* a_codes, const uint8_t* a_scales, int64_t m, c
                       const uint8_t* w_scales, int64_t n, int64_t k, void* c, int32_t c_dtype, int64_t ldc,
                       void* stream);
 
-/* Bytes of device workspace gemm_w4aX / grouped_gemm_w4aX need (0 for FP4_A16). */
+/* Bytes of device workspace gemm_w4aX / grouped_gemm_w4aX / gemm_w4aX_static / gemm_w8a8
+ * need for a precision code (0 for FP4_A16; FP4_A4S as FP4_A4; FP4_A8S, FP4_W8A8 as FP4_A8). */
 size_t fp4_workspace_bytes(int32_t act, int64_t m_or_rows, int64_t n, int64_t k);
 
 /*
  * fp4_policy_select -- per-layer precision policy: FP4_POLICY_Q4 -> FP4_A4,
- * FP4_POLICY_Q8 -> FP4_A8, FP4_POLICY_AUTO -> (layer_flag ? FP4_A8 : FP4_A4).
+ * FP4_POLICY_Q8 -> FP4_A8, FP4_POLICY_AUTO -> (layer_flag ? FP4_A8 : FP4_A4),
+ * FP4_POLICY_SENSITIVE_W8 -> (layer_flag ? FP4_W8A8 : FP4_A4) (FP8 kept on flagged
+ * layers: TensorRT-LLM FP4 page, section "Deployment Guidelines and Production
+ * Safeguards", item 2), FP4_POLICY_STATIC -> (layer_flag ? FP4_A8S : FP4_A4S)
+ * (calibrated activation macro-scales).
  * Returns -FP4_E_MODE for an unknown mode. Source: llama.cpp precision-policy page,
  * section "Local inference is becoming a policy engine" (q4 / q8 / auto).
  */

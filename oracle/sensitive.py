@@ -3,9 +3,12 @@
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 Sources:
-* "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for Blackwell B200", the
-  deployment advice on quantization outliers: layer 0 and the output heads are more
-  sensitive, and FP8 precision can be kept on those layers while the rest runs in FP4.
+* "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for Blackwell B200", section
+  "Deployment Guidelines and Production Safeguards", item 2: layer 0 and the output heads
+  are more sensitive, and FP8 precision can be kept on those layers while the rest runs in
+  FP4; section "Step 2: Executing FP4 Calibration and Engine Compilation" and item 1 of
+  the guidelines: activation ranges are calibrated ahead of deployment on data that
+  matches production traffic.
 * "llama.cpp Put Precision Policy Inside the Model. That Matters More Than W4A4", section
   "Local inference is becoming a policy engine": the runtime picks precision per layer
   (q4 / q8 / auto).

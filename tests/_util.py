@@ -29,6 +29,19 @@ def tiled_index_maps(rows: int, k: int):
     return code_idx, micro_idx, macro_idx
 
 
+def tiled8_code_index(rows: int, k: int):
+    """Index array I such that canonical E4M3 codes = tiled[I], from the E4M3 tiled-layout
+    definition in include/fp4_e2m1.h (micro and macro share the E2M1 maps)."""
+    G = k // 256
+    r = np.arange(rows)[:, None]
+    n = r % 16
+    col = np.arange(k)[None, :]
+    T = (r // 16) * G + col // 256
+    c = col % 256
+    t, j = c // 32, (c % 32) // 8
+    return T * 4096 + (t // 4) * 2048 + ((t % 4) // 2) * 1024 + (16 * j + n) * 16 + (t % 2) * 8 + c % 8
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
@@ -40,6 +53,8 @@ def qtensor_to_canonical(q, rows: int, k: int):
     macro = host(q.macro).view(np.uint16)
     if q.layout == 1:
         ci, mi, gi = tiled_index_maps(rows, k)
+        if q.elem == 1:
+            ci = tiled8_code_index(rows, k)
         return codes[ci], micro[mi], macro[gi]
     width = k // 2 if q.elem == 0 else k
     return codes.reshape(rows, width), micro.reshape(rows, k // 16), macro.reshape(rows, k // 256)

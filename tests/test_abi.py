@@ -56,6 +56,10 @@ def test_policy_select(lib):
     assert P.fp4_policy_select(P.POLICY_Q8, False) == P.A8
     assert P.fp4_policy_select(P.POLICY_AUTO, True) == P.A8
     assert P.fp4_policy_select(P.POLICY_AUTO, False) == P.A4
+    assert P.fp4_policy_select(P.POLICY_SENSITIVE_W8, True) == P.W8A8
+    assert P.fp4_policy_select(P.POLICY_SENSITIVE_W8, False) == P.A4
+    assert P.fp4_policy_select(P.POLICY_STATIC, True) == P.A8S
+    assert P.fp4_policy_select(P.POLICY_STATIC, False) == P.A4S
     with pytest.raises(P.Fp4Error):
         P.fp4_policy_select(3, False)
 
@@ -68,6 +72,9 @@ def test_workspace_bytes(lib):
     assert need >= m * k * 2 + m * (k // 256) * 4
     assert P.fp4_workspace_bytes(P.A8, m, 4096, k) == need
     assert P.fp4_workspace_bytes(7, m, 4096, k) == 0
+    assert P.fp4_workspace_bytes(P.A4S, m, 4096, k) == need
+    assert P.fp4_workspace_bytes(P.A8S, m, 4096, k) == need
+    assert P.fp4_workspace_bytes(P.W8A8, m, 4096, k) == need
 
 
 def test_validation_happens_before_any_device_use(lib):
@@ -79,7 +86,7 @@ def test_validation_happens_before_any_device_use(lib):
     # bad dtype / elem / layout / shapes / alignment
     assert lib.quantize_fp4(fake, 7, 16, 256, 256, 0, 0, fake, fake, fake, null) == 4
     assert lib.quantize_fp4(fake, 1, 16, 256, 256, 5, 0, fake, fake, fake, null) == 5
-    assert lib.quantize_fp4(fake, 1, 16, 256, 256, 1, 1, fake, fake, fake, null) == 10
+    assert lib.quantize_fp4(fake, 1, 24, 256, 256, 1, 1, fake, fake, fake, null) == 2  # E4M3 tiled, rows % 16
     assert lib.quantize_fp4(fake, 1, 16, 300, 300, 0, 0, fake, fake, fake, null) == 2
     assert lib.quantize_fp4(fake, 1, 15, 256, 256, 0, 1, fake, fake, fake, null) == 2
     assert lib.quantize_fp4(fake, 1, 16, 256, 100, 0, 0, fake, fake, fake, null) == 2
@@ -193,6 +200,40 @@ def test_mx_entry_points_validate_before_device_use(lib):
     assert lib.gemm_mxfp4(fake, fake, 16, fake, fake, 16, 128, fake, 1, 8, null) == 2
     assert lib.gemm_mxfp4(fake, null, 16, fake, fake, 16, 128, fake, 1, 16, null) == 1
     assert lib.gemm_mxfp4(vp((1 << 20) + 4), fake, 16, fake, fake, 16, 128, fake, 1, 16, null) == 3
+
+
+def test_sensitive_and_static_entry_points_validate_before_device_use(lib):
+    vp = ctypes.c_void_p
+    fake, null = vp(1 << 20), vp(0)
+    ws, big = vp(1 << 24), 1 << 30
+    T = lib_mod._Tensor
+    w4 = T(1 << 20, 1 << 21, 1 << 22, 256, 512, 0, 1)
+    w8 = T(1 << 20, 1 << 21, 1 << 22, 256, 512, 1, 1)
+    w8c = T(1 << 20, 1 << 21, 1 << 22, 256, 512, 1, 0)  # canonical E4M3
+    w8k = T(1 << 20, 1 << 21, 1 << 22, 256, 32768, 1, 1)  # k past the kernel's tables
+    # static quantization: the macro-scales are required and 2-byte aligned
+    assert lib.quantize_fp4_static(fake, 1, 16, 256, 256, 0, 0, null, fake, fake, fake, null) == 1
+    assert lib.quantize_fp4_static(fake, 1, 16, 256, 256, 0, 0, vp((1 << 20) + 1), fake, fake, fake, null) == 3
+    assert lib.quantize_fp4_static(fake, 1, 16, 300, 300, 0, 0, fake, fake, fake, fake, null) == 2
+    # calibration
+    assert lib.act_macro_calibrate(fake, 1, 64, 512, 512, 0, null, fake, null) == 1
+    assert lib.act_macro_calibrate(fake, 7, 64, 512, 512, 0, fake, fake, null) == 4
+    assert lib.act_macro_calibrate(fake, 1, 64, 512, 512, 3, fake, fake, null) == 5
+    assert lib.act_macro_calibrate(fake, 1, 64, 500, 512, 0, fake, fake, null) == 2
+    assert lib.act_macro_calibrate(fake, 1, 0, 512, 512, 0, fake, fake, null) == 2
+    assert lib.act_macro_calibrate(fake, 1, 64, 512, 512, 0, vp((1 << 20) + 2), fake, null) == 3
+    # static product: A4 / A8 only, macro-scales required, E2M1 tiled weights, workspace
+    assert lib.gemm_w4aX_static(16, fake, 1, 8, 512, fake, ctypes.byref(w4), fake, 1, 256, ws, big, null) == 5
+    assert lib.gemm_w4aX_static(4, fake, 1, 8, 512, null, ctypes.byref(w4), fake, 1, 256, ws, big, null) == 1
+    assert lib.gemm_w4aX_static(4, fake, 1, 8, 512, fake, ctypes.byref(w8), fake, 1, 256, ws, big, null) == 4
+    assert lib.gemm_w4aX_static(8, fake, 1, 8, 512, fake, ctypes.byref(w4), fake, 1, 256, null, 0, null) == 9
+    # W8A8: E4M3 tiled weights only; k limit; workspace
+    assert lib.gemm_w8a8(fake, 1, 8, 512, ctypes.byref(w4), fake, 1, 256, ws, big, null) == 4
+    assert lib.gemm_w8a8(fake, 1, 8, 512, ctypes.byref(w8c), fake, 1, 256, ws, big, null) == 10
+    assert lib.gemm_w8a8(fake, 1, 8, 32768, ctypes.byref(w8k), fake, 1, 256, ws, big, null) == 2
+    assert lib.gemm_w8a8(fake, 1, 8, 512, ctypes.byref(w8), fake, 1, 256, null, 0, null) == 9
+    assert lib.gemm_w8a8(fake, 1, 8, 512, ctypes.byref(w8), fake, 1, 200, ws, big, null) == 2
+    assert lib.gemm_w8a8(null, 1, 8, 512, ctypes.byref(w8), fake, 1, 256, ws, big, null) == 1
 
 
 def test_device_check_reports_missing_device(lib):

@@ -20,7 +20,8 @@ import math
 import numpy as np
 
 __all__ = ["normal", "to_bf16_values", "outlier_channels", "tiny", "decode", "prefill",
-           "policy_flags", "policy_outliers", "policy_layer", "moe_router_logits", "moe_tokens",
+           "policy_flags", "policy_outliers", "policy_layer", "policy_calibration",
+           "moe_router_logits", "moe_tokens",
            "moe_expert_weights", "moe_down_inputs", "kv_lengths", "kv_key_outliers", "kv_queries",
            "kv_rows_device", "WORKLOADS"]
 
@@ -29,7 +30,7 @@ WORKLOADS = {
     "decode_w4a16": dict(seed=1, m=8, k=4096, n=14336, outlier_frac=0.001, outlier_gain=100.0),
     "prefill_w4a4": dict(seed=2, m=2048, k=4096, n=4096, outlier_frac=0.005, outlier_gain=50.0),
     "policy_stack": dict(seed=3, layers=8, flagged=2, m=512, k=5120, n=5120,
-                         outlier_frac=0.005, outlier_gain=50.0),
+                         outlier_frac=0.005, outlier_gain=50.0, calib_rows=512),
     "decode_attention_fp4kv": dict(seed=5, n_seq=32, q_heads=32, kv_heads=8, head_dim=128,
                                    max_tokens=16384, min_len=8192, max_len=16383),
     "moe_w4a4": dict(seed=4, experts=128, top_k=8, tokens=4096, hidden=2048,
@@ -106,6 +107,15 @@ def policy_layer(layer: int, m=512, k=5120, n=5120, seed=3, outlier_frac=0.005,
     x = normal(_child(seed, 3, layer), 1.0, (m, k))
     x[:, policy_outliers(k, seed, outlier_frac)] *= np.float32(outlier_gain)
     return w, to_bf16_values(x)
+
+
+def policy_calibration(layer: int, rows=512, k=5120, seed=3, outlier_frac=0.005,
+                       outlier_gain=50.0) -> np.ndarray:
+    """A separate calibration batch for layer ``layer``, bf16 [rows, k], drawn like x_l (same
+    outlier channels): the data static activation scales are calibrated on."""
+    x = normal(_child(seed, 4, layer), 1.0, (rows, k))
+    x[:, policy_outliers(k, seed, outlier_frac)] *= np.float32(outlier_gain)
+    return to_bf16_values(x)
 
 
 def moe_router_logits(tokens=4096, experts=128, seed=4):
