@@ -9,6 +9,8 @@ Sources:
   FP4; section "Step 2: Executing FP4 Calibration and Engine Compilation" and item 1 of
   the guidelines: activation ranges are calibrated ahead of deployment on data that
   matches production traffic.
+* The ClusterBid FP4 inference cost guide, section "FP4 Migration Checklist That Prevents
+  Rollbacks": when FP4 regresses, a few sensitive layers go back to FP8.
 * "llama.cpp Put Precision Policy Inside the Model. That Matters More Than W4A4", section
   "Local inference is becoming a policy engine": the runtime picks precision per layer
   (q4 / q8 / auto).
