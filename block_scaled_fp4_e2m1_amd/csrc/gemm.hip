@@ -190,30 +190,34 @@ __shared__ uint4 g_w1[kWStage];
 // dynamic LDS: float sa[G][64] then uint16 mw[16][G][16] (at most 16 row blocks per tile)
 size_t gemm_dynamic_lds(int groups) { return (size_t)groups * kBM * 4 + (size_t)16 * groups * 16 * 2; }
 
-// Weight-side shape of the pipeline. E2M1 weights (W8 = 0): 4 row blocks of 16 weight
-// rows per wave (workgroup tile 64 x 256), one 1 KB LDS-DMA piece per row block and stage.
-// E4M3 weights (W8 = 1): 2 row blocks per wave (tile 64 x 128), two 1 KB pieces per row
-// block and stage; either way a wave copies 4 pieces per stage into the same LDS buffers
-// and keeps the same 4 code words per lane.
-template <int W8>
+// Weight-side shape of the pipeline, by weight mode WM:
+//   0  E2M1, 4 row blocks of 16 weight rows per wave (workgroup tile 64 x 256), one 1 KB
+//      LDS-DMA piece per row block and stage;
+//   1  E4M3 (W8A8), 2 row blocks per wave (tile 64 x 128), two 1 KB pieces per row block
+//      and stage, so a wave still copies 4 pieces per stage into the same LDS buffers;
+//   2  E2M1 narrow, 2 row blocks per wave (tile 64 x 128): twice the workgroups, for
+//      products whose wide grid cannot fill the chip.
+template <int WM>
 struct WShape {
-  static constexpr int NI = W8 ? 2 : 4;          // row blocks per wave
-  static constexpr int BN = 64 * NI;             // weight rows per workgroup
-  static constexpr int kTile = W8 ? kTile8CodeBytes : kTileCodeBytes;
+  static constexpr bool E4M3 = WM == 1;
+  static constexpr int NI = WM == 0 ? 4 : 2;       // row blocks per wave
+  static constexpr int BN = 64 * NI;               // weight rows per workgroup
+  static constexpr int kTile = E4M3 ? kTile8CodeBytes : kTileCodeBytes;
+  static constexpr int kPieces = E4M3 ? 4 : NI;    // 1 KB LDS-DMA pieces per wave and stage
 };
 
-template <int A_BF16, int W8>
+template <int A_BF16, int WM>
 struct StepOperands {
   typedef typename OpTraits<A_BF16>::frag frag;
-  frag af[4], wf[WShape<W8>::NI];
+  frag af[4], wf[WShape<WM>::NI];
 };
 
 // weight fragment of row block ni for MFMA step T (0..3) of a stage, from the stage's code
 // words: E2M1 dword T of word ni; E4M3 dwords 2 (T % 2), +1 of word 2 ni + T / 2
-template <int A_BF16, int W8, int T>
+template <int A_BF16, int WM, int T>
 __device__ __forceinline__ typename OpTraits<A_BF16>::frag weight_frag(const uint4 (&cw)[4], int ni, uint32_t mu_op) {
   typedef OpTraits<A_BF16> Op;
-  if constexpr (W8) {
+  if constexpr (WShape<WM>::E4M3) {
     const uint4 w = cw[2 * ni + (T >> 1)];
     return (T & 1) ? Op::weight8(w.z, w.w, mu_op) : Op::weight8(w.x, w.y, mu_op);
   } else {
@@ -224,34 +228,34 @@ __device__ __forceinline__ typename OpTraits<A_BF16>::frag weight_frag(const uin
 
 // operands of step T (0..3) of a stage: activation fragments from LDS, weight fragments
 // decoded from the stage's code words with micro-scale byte (4h+T)
-template <int A_BF16, int W8, int T>
+template <int A_BF16, int WM, int T>
 __device__ __forceinline__ void stage_operands(const uint4* abuf, const uint4 (&cw)[4],
                                                int lane, const uint2 (&mu)[4], int h,
-                                               StepOperands<A_BF16, W8>& o) {
+                                               StepOperands<A_BF16, WM>& o) {
   typedef OpTraits<A_BF16> Op;
   typedef typename Op::frag frag;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) o.af[mi] = __builtin_bit_cast(frag, abuf[(mi * 4 + T) * 64 + lane]);
 #pragma unroll
-  for (int ni = 0; ni < WShape<W8>::NI; ++ni) {
+  for (int ni = 0; ni < WShape<WM>::NI; ++ni) {
     const uint32_t mw = h == 0 ? mu[ni].x : mu[ni].y;
-    o.wf[ni] = weight_frag<A_BF16, W8, T>(cw, ni, Op::micro_operand((mw >> (8 * T)) & 0xFFu));
+    o.wf[ni] = weight_frag<A_BF16, WM, T>(cw, ni, Op::micro_operand((mw >> (8 * T)) & 0xFFu));
   }
 }
 
-template <int A_BF16, int W8>
-__device__ __forceinline__ void stage_mfma(const StepOperands<A_BF16, W8>& o, float4_t (&x)[4][WShape<W8>::NI]) {
+template <int A_BF16, int WM>
+__device__ __forceinline__ void stage_mfma(const StepOperands<A_BF16, WM>& o, float4_t (&x)[4][WShape<WM>::NI]) {
   typedef OpTraits<A_BF16> Op;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < WShape<W8>::NI; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
+    for (int ni = 0; ni < WShape<WM>::NI; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
 }
 
 // Interleave for the MFMAs of a step with the next step's operand preparation: the four
 // activation-fragment LDS reads go right after the first MFMAs (their latency then hides
 // behind the rest of the step), the weight decode 3 VALU per MFMA.
-template <int W8>
+template <int WM>
 __device__ __forceinline__ void interleave_step() {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -260,17 +264,17 @@ __device__ __forceinline__ void interleave_step() {
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
   }
 #pragma unroll
-  for (int i = 4; i < 4 * WShape<W8>::NI; ++i) {
+  for (int i = 4; i < 4 * WShape<WM>::NI; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
   }
 }
 
 // per-row (ra) and per-column (rw) ratios s_g / s_{g+1} for the boundary after group g
-template <int W8>
+template <int WM>
 struct Rescale {
   float ra[4][4];
-  float rw[WShape<W8>::NI];
+  float rw[WShape<WM>::NI];
 };
 
 // Last MFMA step of a stage (step 3): its MFMAs interleaved with
@@ -279,16 +283,16 @@ struct Rescale {
 //     loads may stay in flight), and
 //   - for the last stage of a group (RATIOS), the group-boundary ratios, applied in the
 //     next group's first step (the operands of step 2 are dead here).
-template <int A_BF16, int W8, bool RATIOS, int VMCNT, typename RatioFn>
-__device__ __forceinline__ void last_step(const StepOperands<A_BF16, W8>& o, float4_t (&x)[4][WShape<W8>::NI],
-                                          RatioFn&& ratios, Rescale<W8>& r, const uint4* nwbuf, int wave,
+template <int A_BF16, int WM, bool RATIOS, int VMCNT, typename RatioFn>
+__device__ __forceinline__ void last_step(const StepOperands<A_BF16, WM>& o, float4_t (&x)[4][WShape<WM>::NI],
+                                          RatioFn&& ratios, Rescale<WM>& r, const uint4* nwbuf, int wave,
                                           int lane, const uint32_t (&mw_next)[4], uint4 (&cw)[4],
-                                          typename OpTraits<A_BF16>::frag (&wf0)[WShape<W8>::NI]) {
+                                          typename OpTraits<A_BF16>::frag (&wf0)[WShape<WM>::NI]) {
   typedef OpTraits<A_BF16> Op;
-  constexpr int NI = WShape<W8>::NI;
+  constexpr int NI = WShape<WM>::NI;
   __builtin_amdgcn_s_waitcnt(kVmcntWait<VMCNT>::value);
 #pragma unroll
-  for (int d = 0; d < 4; ++d) cw[d] = nwbuf[(wave * 4 + d) * 64 + lane];
+  for (int d = 0; d < WShape<WM>::kPieces; ++d) cw[d] = nwbuf[(wave * 4 + d) * 64 + lane];
   if (RATIOS) ratios(r);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -296,7 +300,7 @@ __device__ __forceinline__ void last_step(const StepOperands<A_BF16, W8>& o, flo
     for (int ni = 0; ni < NI; ++ni) x[mi][ni] = Op::mfma(o.af[mi], o.wf[ni], x[mi][ni]);
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
-    wf0[ni] = weight_frag<A_BF16, W8, 0>(cw, ni, Op::micro_operand(mw_next[ni] & 0xFFu));
+    wf0[ni] = weight_frag<A_BF16, WM, 0>(cw, ni, Op::micro_operand(mw_next[ni] & 0xFFu));
 #pragma unroll
   for (int i = 0; i < 4 * NI; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -309,16 +313,16 @@ __device__ __forceinline__ void last_step(const StepOperands<A_BF16, W8>& o, flo
 // group multiplies each running sum by the boundary ratios r just before that tile's
 // first MFMA of the group (no wait on MFMA results: those sums were finished a step
 // earlier). RATIOS: the last stage of a group computes the next ratios into r.
-template <int A_BF16, int W8, bool RESCALE, bool RATIOS, int VMCNT, typename RatioFn>
+template <int A_BF16, int WM, bool RESCALE, bool RATIOS, int VMCNT, typename RatioFn>
 __device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
-                                              typename OpTraits<A_BF16>::frag (&wf0)[WShape<W8>::NI], int wave,
+                                              typename OpTraits<A_BF16>::frag (&wf0)[WShape<WM>::NI], int wave,
                                               int lane, const uint2 (&mu)[4], int h,
-                                              float4_t (&x)[4][WShape<W8>::NI], RatioFn&& ratios, Rescale<W8>& r,
+                                              float4_t (&x)[4][WShape<WM>::NI], RatioFn&& ratios, Rescale<WM>& r,
                                               const uint4* nwbuf, const uint2 (&mu_next)[4], int h_next) {
   typedef OpTraits<A_BF16> Op;
   typedef typename Op::frag frag;
-  constexpr int NI = WShape<W8>::NI;
-  StepOperands<A_BF16, W8> o0, o1;
+  constexpr int NI = WShape<WM>::NI;
+  StepOperands<A_BF16, WM> o0, o1;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) o0.af[mi] = __builtin_bit_cast(frag, abuf[(mi * 4 + 0) * 64 + lane]);
 #pragma unroll
@@ -333,7 +337,7 @@ __device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
         for (int i = 0; i < 4; ++i) x[mi][ni][i] *= A_BF16 ? r.rw[ni] : r.ra[mi][i] * r.rw[ni];
         x[mi][ni] = Op::mfma(o0.af[mi], o0.wf[ni], x[mi][ni]);
       }
-    stage_operands<A_BF16, W8, 1>(abuf, cw, lane, mu, h, o1);
+    stage_operands<A_BF16, WM, 1>(abuf, cw, lane, mu, h, o1);
     __builtin_amdgcn_sched_group_barrier(0x002, A_BF16 ? 4 : 8, 0);  // VALU: tile 0's rescale
 #pragma unroll
     for (int i = 0; i < 4 * NI; ++i) {
@@ -342,30 +346,32 @@ __device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
       __builtin_amdgcn_sched_group_barrier(0x002, A_BF16 ? 6 : 10, 0);  // VALU
     }
   } else {
-    stage_mfma<A_BF16, W8>(o0, x);
-    stage_operands<A_BF16, W8, 1>(abuf, cw, lane, mu, h, o1);
-    interleave_step<W8>();
+    stage_mfma<A_BF16, WM>(o0, x);
+    stage_operands<A_BF16, WM, 1>(abuf, cw, lane, mu, h, o1);
+    interleave_step<WM>();
   }
   __builtin_amdgcn_sched_barrier(0);
-  stage_mfma<A_BF16, W8>(o1, x);
-  stage_operands<A_BF16, W8, 2>(abuf, cw, lane, mu, h, o0);
-  interleave_step<W8>();
+  stage_mfma<A_BF16, WM>(o1, x);
+  stage_operands<A_BF16, WM, 2>(abuf, cw, lane, mu, h, o0);
+  interleave_step<WM>();
   __builtin_amdgcn_sched_barrier(0);
-  stage_mfma<A_BF16, W8>(o0, x);
-  stage_operands<A_BF16, W8, 3>(abuf, cw, lane, mu, h, o1);
-  interleave_step<W8>();
+  stage_mfma<A_BF16, WM>(o0, x);
+  stage_operands<A_BF16, WM, 3>(abuf, cw, lane, mu, h, o1);
+  interleave_step<WM>();
   __builtin_amdgcn_sched_barrier(0);
   uint32_t mw_next[4];
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) mw_next[ni] = h_next == 0 ? mu_next[ni].x : mu_next[ni].y;
-  last_step<A_BF16, W8, RATIOS, VMCNT>(o1, x, ratios, r, nwbuf, wave, lane, mw_next, cw, wf0);
+  last_step<A_BF16, WM, RATIOS, VMCNT>(o1, x, ratios, r, nwbuf, wave, lane, mw_next, cw, wf0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int A_BF16, int C_BF16, int GROUPED, int W8>
+template <int A_BF16, int C_BF16, int GROUPED, int WM>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
-  static_assert(!W8 || (!A_BF16 && !GROUPED), "E4M3 weights: dense, FP16 activation operand");
-  constexpr int NI = WShape<W8>::NI, BN = WShape<W8>::BN, kTile = WShape<W8>::kTile;
+  static_assert(WM != 1 || (!A_BF16 && !GROUPED), "E4M3 weights: dense, FP16 activation operand");
+  constexpr int NI = WShape<WM>::NI, BN = WShape<WM>::BN, kTile = WShape<WM>::kTile;
+  constexpr int kPieces = WShape<WM>::kPieces;
+  constexpr bool kE4M3 = WShape<WM>::E4M3;
   extern __shared__ uint8_t g_dyn[];
   const int groups = (int)(args.k >> 8);
   const int64_t n = args.n;
@@ -455,9 +461,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
                                                a_voff, a_soff + 64 * t, 0, 0);
     // piece d: row block d (E2M1) or d / 2, half d % 2 of the stage's 2 KB (E4M3)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const int ni = W8 ? d >> 1 : d;
-      const uint32_t soff = (uint32_t)((ni * groups + g) * kTile + h * (kTile / 2) + (W8 ? (d & 1) * 1024 : 0));
+    for (int d = 0; d < kPieces; ++d) {
+      const int ni = kE4M3 ? d >> 1 : d;
+      const uint32_t soff = (uint32_t)((ni * groups + g) * kTile + h * (kTile / 2) + (kE4M3 ? (d & 1) * 1024 : 0));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(wbuf + (wave * 4 + d) * 64), 16,
                                                (uint32_t)lane * 16, soff, 0, 0);
     }
@@ -486,11 +492,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   };
   // unit the weight operand leaves in the column factor: 2^8 (E2M1 * mu * 2^-8 in FP16),
   // 8 (E4M3 * mu * 2^-3), 1 on the bf16 path
-  constexpr float kUnit = W8 ? OpTraits<0>::kMicroUnit8 : OpTraits<A_BF16>::kMicroUnit;
+  constexpr float kUnit = kE4M3 ? OpTraits<0>::kMicroUnit8 : OpTraits<A_BF16>::kMicroUnit;
   // ratios s_g / s_{g+1} for the boundary after group g, with s_G = 1: after the last
   // group the "ratio" is the final factor itself. Row ratios come from the table built
   // in the prologue; the weight operand's unit cancels except in the final factor.
-  auto ratios_after = [&](int g, Rescale<W8>& r) {
+  auto ratios_after = [&](int g, Rescale<WM>& r) {
     const bool last = g + 1 >= groups;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
@@ -527,10 +533,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     }
   }
 #pragma unroll
-  for (int d = 0; d < 4; ++d) cw[d] = g_w0[(wave * 4 + d) * 64 + lane];
+  for (int d = 0; d < kPieces; ++d) cw[d] = g_w0[(wave * 4 + d) * 64 + lane];
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
-    wf0[ni] = weight_frag<A_BF16, W8, 0>(cw, ni, OpTraits<A_BF16>::micro_operand(mu_cur[ni].x & 0xFFu));
+    wf0[ni] = weight_frag<A_BF16, WM, 0>(cw, ni, OpTraits<A_BF16>::micro_operand(mu_cur[ni].x & 0xFFu));
 
   // stage s in buffers (s & 1): the barrier publishes its activation tile (every wave's
   // copies are complete) and frees the other buffers, which then receive stage s + 1
@@ -538,7 +544,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   // every group ends with the group-boundary rescale.
   // boundary ratios carried from the last stage of a group into the first of the next
   // (1 before the first group; after the last group they are the final factors)
-  Rescale<W8> resc;
+  Rescale<WM> resc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -558,8 +564,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     // next stage: same group (H == 0: micro-scale word 1 of mu_cur) or the next group
     // (H == 1: word 0 of mu_nxt); the H == 0 stage's NI micro-scale loads may stay in
     // flight
-    compute_stage<A_BF16, W8, H == 0, H == 1, H == 0 ? NI : 0>(
-        abuf, cw, wf0, wave, lane, mu_cur, H, x, [&](Rescale<W8>& rr) { ratios_after(s >> 1, rr); }, resc,
+    compute_stage<A_BF16, WM, H == 0, H == 1, H == 0 ? NI : 0>(
+        abuf, cw, wf0, wave, lane, mu_cur, H, x, [&](Rescale<WM>& rr) { ratios_after(s >> 1, rr); }, resc,
         nwbuf, H == 0 ? mu_cur : mu_nxt, 1 - H);
     if (H == 1) {
 #pragma unroll
@@ -633,14 +639,30 @@ namespace fp4lib {
 
 bool gemm_supports(int64_t k) { return gemm_dynamic_lds((int)(k >> 8)) <= 64 * 1024; }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    cus[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0 ? v : 256;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (!gemm_supports(g.k)) return hipErrorInvalidValue;
   if (g.w_e4m3 && (g.a_is_bf16 || g.expert_offsets)) return hipErrorInvalidValue;
-  const int64_t bn = g.w_e4m3 ? WShape<1>::BN : WShape<0>::BN;
-  const int64_t tiles_n = (g.n + bn - 1) / bn;
   int64_t tiles_m;
   if (g.expert_offsets) tiles_m = (g.m + kBM - 1) / kBM + g.n_experts;  // upper bound
   else tiles_m = (g.m + kBM - 1) / kBM;
+  // dense E2M1 products whose 64 x 256 tiles cannot give every CU two workgroups take the
+  // narrow 64 x 128 tile
+  const bool narrow = !g.w_e4m3 && !g.expert_offsets &&
+                      tiles_m * ((g.n + WShape<0>::BN - 1) / WShape<0>::BN) < 2 * (int64_t)device_cus();
+  const int64_t bn = g.w_e4m3 ? WShape<1>::BN : narrow ? WShape<2>::BN : WShape<0>::BN;
+  const int64_t tiles_n = (g.n + bn - 1) / bn;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(256);
@@ -649,6 +671,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const int grouped = g.expert_offsets != nullptr;
   if (g.w_e4m3) {
     if (g.c_is_bf16) FP4_GEMM(0, 1, 0, 1); else FP4_GEMM(0, 0, 0, 1);
+  } else if (narrow) {
+    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM(1, 1, 0, 2); else FP4_GEMM(1, 0, 0, 2); }
+    else { if (g.c_is_bf16) FP4_GEMM(0, 1, 0, 2); else FP4_GEMM(0, 0, 0, 2); }
   } else if (g.a_is_bf16) {
     if (g.c_is_bf16) { if (grouped) FP4_GEMM(1, 1, 1, 0); else FP4_GEMM(1, 1, 0, 0); }
     else { if (grouped) FP4_GEMM(1, 0, 1, 0); else FP4_GEMM(1, 0, 0, 0); }

@@ -6,7 +6,9 @@ Gates (float32 accumulation on exact operands):
   bf16 output:    ||C - RNE_bf16(C64)||_F / ||RNE_bf16(C64)||_F <= 1e-3 and >= 99.9% of
                   elements equal to RNE_bf16(C64) or one bf16 step away.
 Full-size workloads are checked on sampled rows/columns that the oracle computes one by
-one; small shapes (several tiles plus ragged tails) are checked in full."""
+one; small shapes (several tiles plus ragged tails) are checked in full. Small dense
+products run on the narrow 64 x 128 tile; a ragged 2043 x 4080 product covers the wide
+64 x 256 one (the full-size prefill and the grouped products use it too)."""
 import numpy as np
 import pytest
 import torch
@@ -79,6 +81,26 @@ def test_gemm_small_shapes(act, m, n, k):
     a = workloads.to_bf16_values(a)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
     print(f"[case] gemm {ACTS[act]} m={m} n={n} k={k}", flush=True)
+    wq = _wq(w)
+    ad = to_device_bf16(a)
+    ref = _oracle_c(a.astype(np.float64), w, act)
+    f32_gate(host(fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32)), ref)
+    bf16_gate(bf16_values(fp4.gemm_w4aX(act, ad, wq)), oracle.formats.bf16_round(ref))
+
+
+@pytest.mark.parametrize("act", [16, 8, 4])
+def test_gemm_wide_tiles_ragged(act):
+    """Small products take the narrow 64 x 128 tile; this shape (2043 x 4080: 32 x 16 tiles
+    of 64 x 256, the last row and column tiles ragged) is large enough for the wide one."""
+    m, n, k = 2043, 4080, 256
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert -(-m // 64) * -(-n // 256) >= 2 * cus, "shape no longer selects the wide tile"
+    rng = np.random.default_rng(310 + act)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    a[:, rng.choice(k, 3, replace=False)] *= 50
+    a = workloads.to_bf16_values(a)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    print(f"[case] gemm wide tiles {ACTS[act]} m={m} n={n} k={k}", flush=True)
     wq = _wq(w)
     ad = to_device_bf16(a)
     ref = _oracle_c(a.astype(np.float64), w, act)
