@@ -558,7 +558,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     if (s + 1 < stages) copy_stage(nabuf, nwbuf, s + 1);
     __builtin_amdgcn_sched_barrier(0);
     // (unconditional in H == 0 stages, the last group re-reading its own, so that exactly
-    // NI loads follow the copies when last_step waits for them)
+    // NI loads follow the copies when last_step waits for them; the count holds because
+    // every iteration runs this same code: in a separately compiled last iteration these
+    // loads would be dead, the compiler would drop them, and the wait would let copies
+    // through unfinished)
     if (H == 0) load_micro(mu_nxt, min((s >> 1) + 1, groups - 1));
     __builtin_amdgcn_sched_barrier(0);
     // next stage: same group (H == 0: micro-scale word 1 of mu_cur) or the next group
