@@ -81,9 +81,13 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const void* __restrict__ x,
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 // 128 x 128 output tile per workgroup, 4 waves of 64 x 64 (4 x 4 MFMAs of 16 x 16), one
-// 128-wide k tile per step; operands for the next step are loaded while this one runs.
+// 128-wide k tile per step. Operands go straight to registers (each lane's 16-byte piece is
+// its MFMA operand), kMxDepth - 1 steps ahead of the step being computed: a step's 16
+// MFMAs take ~256 cycles per wave, shorter than a loaded L2 round trip.
+constexpr int kMxDepth = 3;
+
 template <int OUT_BF16>
-__global__ __launch_bounds__(256) void k_gemm_mx(const uint8_t* __restrict__ a_codes,
+__global__ __launch_bounds__(256, 2) void k_gemm_mx(const uint8_t* __restrict__ a_codes,
                                                  const uint8_t* __restrict__ a_scales, int64_t m,
                                                  const uint8_t* __restrict__ w_codes,
                                                  const uint8_t* __restrict__ w_scales, int64_t n, int64_t k,
@@ -101,8 +105,8 @@ __global__ __launch_bounds__(256) void k_gemm_mx(const uint8_t* __restrict__ a_c
     a_tile0[i] = min(m0 / 16 + i, a_rb_count - 1) * kt_count;
     w_tile0[i] = min(n0 / 16 + i, w_rb_count - 1) * kt_count;
   }
-  uint4 af[2][4], wf[2][4];
-  uint32_t as[2][4], ws[2][4];
+  uint4 af[kMxDepth][4], wf[kMxDepth][4];
+  uint32_t as[kMxDepth][4], ws[kMxDepth][4];
   auto load = [&](int buf, int64_t kt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -119,12 +123,14 @@ __global__ __launch_bounds__(256) void k_gemm_mx(const uint8_t* __restrict__ a_c
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  load(0, 0);
-  for (int64_t kt = 0; kt < kt_count; kt += 2) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {  // buffer h holds k tile kt + h
+  for (int d = 0; d + 1 < kMxDepth; ++d)
+    if (d < kt_count) load(d, d);
+  for (int64_t kt = 0; kt < kt_count; kt += kMxDepth) {
+#pragma unroll
+    for (int h = 0; h < kMxDepth; ++h) {  // buffer h holds k tile kt + h
       if (kt + h >= kt_count) break;
-      if (kt + h + 1 < kt_count) load(h ^ 1, kt + h + 1);
+      if (kt + h + kMxDepth - 1 < kt_count) load((h + kMxDepth - 1) % kMxDepth, kt + h + kMxDepth - 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const v8i a = {(int)af[h][i].x, (int)af[h][i].y, (int)af[h][i].z, (int)af[h][i].w, 0, 0, 0, 0};
