@@ -18,6 +18,8 @@
 // with kb = (c % 128) / 32, n = r % 16 (32 codes, low nibble first), its 64 scale bytes
 // [kb 4][n 16]. Lane l = 16 kb + n of an MFMA reads the 16 bytes at l * 16 and the scale
 // byte l: exactly its operand (row n, k = 32 kb .. +31) and that block's scale.
+#include <type_traits>
+
 #include "fp4_device.h"
 #include "fp4_kernels.h"
 
@@ -79,70 +81,142 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const void* __restrict__ x,
 }
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
 
 // 128 x 128 output tile per workgroup, 4 waves of 64 x 64 (4 x 4 MFMAs of 16 x 16), one
-// 128-wide k tile per step. Operands go straight to registers (each lane's 16-byte piece is
-// its MFMA operand), kMxDepth - 1 steps ahead of the step being computed: a step's 16
-// MFMAs take ~256 cycles per wave, shorter than a loaded L2 round trip.
-constexpr int kMxDepth = 3;
+// 128-wide k tile per stage. Each stage's operands (8 A and 8 W tiles of 1 KB, their
+// scale bytes) are copied once per workgroup into LDS by 16-byte LDS-DMA, two stages
+// ahead, and each wave reads its fragments from there: the waves sharing rows or columns
+// no longer fetch the same bytes through L1 twice. One barrier per stage; one LDS object
+// per stage and compile-time stage indices, so the compiler can tell the buffer being
+// filled from the one being read.
+struct MxStage {
+  uint4 a[8][64];      // tile i (row block i of the workgroup), lane l's 16 bytes
+  uint4 w[8][64];
+  uint32_t as[8][16];  // tile i's 64 scale bytes
+  uint32_t ws[8][16];
+};
+__shared__ MxStage g_mx0;
+__shared__ MxStage g_mx1;
+__shared__ MxStage g_mx2;
+constexpr int kMxStages = 3;
+constexpr int kMxCopies = 5;  // LDS-DMA instructions per wave and stage
+
+template <int B>
+__device__ __forceinline__ MxStage& mx_stage() {
+  if constexpr (B == 0) return g_mx0;
+  else if constexpr (B == 1) return g_mx1;
+  else return g_mx2;
+}
 
 template <int OUT_BF16>
 __global__ __launch_bounds__(256, 2) void k_gemm_mx(const uint8_t* __restrict__ a_codes,
-                                                 const uint8_t* __restrict__ a_scales, int64_t m,
-                                                 const uint8_t* __restrict__ w_codes,
-                                                 const uint8_t* __restrict__ w_scales, int64_t n, int64_t k,
-                                                 void* __restrict__ c, int64_t ldc) {
+                                                    const uint8_t* __restrict__ a_scales, int64_t m,
+                                                    const uint8_t* __restrict__ w_codes,
+                                                    const uint8_t* __restrict__ w_scales, int64_t n, int64_t k,
+                                                    void* __restrict__ c, int64_t ldc) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t kt_count = k / kMxTileK;
   const int64_t a_rb_count = (m + 15) / 16, w_rb_count = (n + 15) / 16;
-  const int64_t m0 = (int64_t)blockIdx.y * 128 + (wave & 1) * 64;
-  const int64_t n0 = (int64_t)blockIdx.x * 128 + (wave >> 1) * 64;
-  // row blocks of this wave (clamped into the arrays; clamped rows are never stored)
-  int64_t a_tile0[4], w_tile0[4];
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; give each XCD a
+  // contiguous run of tiles (n fastest), so its L2 keeps the same activation rows
+  const int gx = gridDim.x, total = gx * gridDim.y;
+  int bid = blockIdx.y * gx + blockIdx.x;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int bx = bid % gx, by = bid / gx;
+  const int64_t mb0 = (int64_t)by * 8, nb0 = (int64_t)bx * 8;  // first row block of A / W
+  // copies of wave w: A tiles 2w, 2w + 1 and W tiles 2w, 2w + 1 (1 KB each), and one
+  // scale copy (64 lanes x 4 bytes = the scale bytes of 4 tiles): A tiles 0-3 / 4-7 for
+  // waves 0 / 1, W tiles 0-3 / 4-7 for waves 2 / 3
+  int64_t a_tile[2], w_tile[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a_tile0[i] = min(m0 / 16 + i, a_rb_count - 1) * kt_count;
-    w_tile0[i] = min(n0 / 16 + i, w_rb_count - 1) * kt_count;
+  for (int i = 0; i < 2; ++i) {
+    a_tile[i] = min(mb0 + 2 * wave + i, a_rb_count - 1) * kt_count;
+    w_tile[i] = min(nb0 + 2 * wave + i, w_rb_count - 1) * kt_count;
   }
-  uint4 af[kMxDepth][4], wf[kMxDepth][4];
-  uint32_t as[kMxDepth][4], ws[kMxDepth][4];
-  auto load = [&](int buf, int64_t kt) {
+  const bool sc_a = wave < 2;
+  const int sc_first = (wave & 1) * 4 + (lane >> 4);  // tile whose scale dword this lane moves
+  const int64_t sc_tile = sc_a ? min(mb0 + sc_first, a_rb_count - 1) * kt_count
+                               : min(nb0 + sc_first, w_rb_count - 1) * kt_count;
+  const uint8_t* sc_src = (sc_a ? a_scales : w_scales) + sc_tile * kMxTileScale + (lane & 15) * 4;
+  auto copy_stage = [&](MxStage& st, int64_t kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t ta = a_tile0[i] + kt, tw = w_tile0[i] + kt;
-      af[buf][i] = *reinterpret_cast<const uint4*>(a_codes + ta * kMxTileCode + lane * 16);
-      wf[buf][i] = *reinterpret_cast<const uint4*>(w_codes + tw * kMxTileCode + lane * 16);
-      as[buf][i] = a_scales[ta * kMxTileScale + lane];
-      ws[buf][i] = w_scales[tw * kMxTileScale + lane];
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(a_codes + (a_tile[i] + kt) * kMxTileCode + lane * 16),
+                                       (lds_void_ptr)&st.a[2 * wave + i][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(w_codes + (w_tile[i] + kt) * kMxTileCode + lane * 16),
+                                       (lds_void_ptr)&st.w[2 * wave + i][0], 16, 0, 0);
     }
+    if (sc_a)  // wave-uniform
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(sc_src + kt * kMxTileScale),
+                                       (lds_void_ptr)&st.as[(wave & 1) * 4][0], 4, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(sc_src + kt * kMxTileScale),
+                                       (lds_void_ptr)&st.ws[(wave & 1) * 4][0], 4, 0, 0);
   };
+
+  const int wm = wave & 1, wn = wave >> 1;
   float4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+  auto compute = [&](const MxStage& st) {
+    uint4 af[4], wf[4];
+    uint32_t as[4], ws[4];
 #pragma unroll
-  for (int d = 0; d + 1 < kMxDepth; ++d)
-    if (d < kt_count) load(d, d);
-  for (int64_t kt = 0; kt < kt_count; kt += kMxDepth) {
+    for (int i = 0; i < 4; ++i) {
+      af[i] = st.a[wm * 4 + i][lane];
+      wf[i] = st.w[wn * 4 + i][lane];
+      as[i] = reinterpret_cast<const uint8_t*>(st.as[wm * 4 + i])[lane];
+      ws[i] = reinterpret_cast<const uint8_t*>(st.ws[wn * 4 + i])[lane];
+    }
 #pragma unroll
-    for (int h = 0; h < kMxDepth; ++h) {  // buffer h holds k tile kt + h
-      if (kt + h >= kt_count) break;
-      if (kt + h + kMxDepth - 1 < kt_count) load((h + kMxDepth - 1) % kMxDepth, kt + h + kMxDepth - 1);
+    for (int i = 0; i < 4; ++i) {
+      const v8i a = {(int)af[i].x, (int)af[i].y, (int)af[i].z, (int)af[i].w, 0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v8i a = {(int)af[h][i].x, (int)af[h][i].y, (int)af[h][i].z, (int)af[h][i].w, 0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v8i b = {(int)wf[h][j].x, (int)wf[h][j].y, (int)wf[h][j].z, (int)wf[h][j].w, 0, 0, 0, 0};
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i][j], 4, 4, 0, (int)as[h][i], 0,
-                                                                         (int)ws[h][j]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const v8i b = {(int)wf[j].x, (int)wf[j].y, (int)wf[j].z, (int)wf[j].w, 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i][j], 4, 4, 0, (int)as[i], 0,
+                                                                       (int)ws[j]);
       }
     }
+  };
+  // stage kt (buffer B = kt % 3): wait for this wave's copies of kt (the copies of kt + 1,
+  // issued later, may stay in flight) and its LDS reads, barrier (every wave's copies of kt
+  // have landed and every wave is done reading kt - 1, whose buffer receives kt + 2), copy
+  // kt + 2, compute kt. The barrier is a bare s_barrier: a workgroup fence would also wait
+  // for the copies of kt + 1. LDS is coherent inside the workgroup; the empty asm
+  // statements keep the compiler from moving memory accesses across it.
+  // Every step copies (the last stages again, into the buffer of a finished stage), so
+  // exactly kMxCopies copies are younger than a stage's own on every path.
+  auto step = [&](auto b_const, int64_t kt) {
+    constexpr int B = decltype(b_const)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<kMxCopies>::value);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    copy_stage(mx_stage<(B + 2) % kMxStages>(), min(kt + 2, kt_count - 1));
+    compute(mx_stage<B>());
+  };
+  copy_stage(g_mx0, 0);
+  copy_stage(g_mx1, min((int64_t)1, kt_count - 1));
+  for (int64_t kt = 0; kt < kt_count; kt += kMxStages) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 >= kt_count) break;
+    step(std::integral_constant<int, 1>{}, kt + 1);
+    if (kt + 2 >= kt_count) break;
+    step(std::integral_constant<int, 2>{}, kt + 2);
   }
+  // no copy may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
+  const int64_t m0 = (int64_t)by * 128 + wm * 64;
+  const int64_t n0 = (int64_t)bx * 128 + wn * 64;
   // lane l holds rows 4 (l / 16) + t, column l % 16 of each 16 x 16 tile
 #pragma unroll
   for (int i = 0; i < 4; ++i)
