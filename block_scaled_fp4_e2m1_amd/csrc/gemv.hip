@@ -14,14 +14,19 @@
 // per-element work stays far below the bandwidth budget.
 //
 // Work split: a workgroup of RBW x KS waves owns RBW 16-row blocks over the whole of k;
-// wave (rb, ks) streams row block rb over its run of at most GPW 256-column groups,
-// issuing every weight load of that run before computing. The activations (m <= 8
-// rows) are copied once per workgroup into LDS by LDS-DMA loads (no registers), in
-// MFMA-fragment order, so a wave's operand read is 512 contiguous bytes. Operand lanes
-// outside their micro-block read from a small zero region instead (no branches). The
-// KS partial results of a row block meet in LDS. With k = 4096 one workgroup holds 8
-// waves and 76 KB of LDS, two fit on a CU, and the whole weight stream is requested in
-// a single round.
+// wave (rb, ks) streams row block rb over its run of at most GPW 256-column groups. The
+// activations (m <= 8 rows) are copied once per workgroup into LDS by LDS-DMA loads (no
+// registers), in MFMA-fragment order, so a wave's operand read is 512 contiguous bytes.
+// Operand lanes outside their micro-block read from a small zero region instead (no
+// branches). The KS partial results of a row block meet in LDS. With k = 4096 one
+// workgroup holds 8 waves and 80 KB of LDS, two fit on a CU, and the weight stream of the
+// whole launch is in flight at once.
+//
+// Issue order. A compute unit's memory pipe drains at its share of HBM bandwidth, and a
+// wave cannot run past a load it has not yet issued, so loads are issued in the order
+// their data is needed and computing starts before the last of them: the activation
+// copies, the micro-scales (LDS-DMA) and macro-scales of the wave's run, then the codes of
+// its first two groups; the codes of group g + 2 are issued once group g is computed.
 #include "fp4_device.h"
 #include "fp4_kernels.h"
 
@@ -43,7 +48,7 @@ struct GemvRegs {
 };
 
 // LDS: [A chunks: (k/8) x 8 rows x 16 B][zero region][micro-scale tiles: one 256-byte
-// slot per (wave, group); reused for float red[KS][RBW*16][8] at the end]
+// slot per (wave, group)][float red[KS][RBW*16][8]]
 template <int kRBW, int GPW, int OUT_BF16>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_bf16(  // <= 128 VGPRs
     const uint16_t* __restrict__ a, int64_t lda, int m, int64_t k,
@@ -68,7 +73,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_bf16(  // <= 128 VGPRs
   const int a_chunks = (int)(k >> 3) * 8;
   uint4* zero = smem + a_chunks;
   uint4* mu_lds = zero + kZeroBytes / 16;                 // [nwaves][GPW][256 B]
-  float* red = reinterpret_cast<float*>(mu_lds);
+  float* red = reinterpret_cast<float*>(mu_lds + nwaves * GPW * (kTileMicroBytes / 16));
 
   for (int i = threadIdx.x; i < kZeroBytes / 16; i += blockDim.x) zero[i] = make_uint4(0, 0, 0, 0);
 
@@ -85,8 +90,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_bf16(  // <= 128 VGPRs
   // ---- this wave's GPW tiles (consecutive in memory). A row block past the end (odd
   // block count) re-reads the last one and is not stored, so every load is
   // unconditional and every wait can be counted. Micro-scales go to LDS by DMA (one
-  // 256-byte tile per instruction) ahead of the code stream; codes and macro-scales go
-  // to registers. ----
+  // 256-byte tile per instruction) and macro-scales to registers, ahead of the code
+  // stream; the codes of the first kAhead groups follow. ----
   const int64_t tile0 = min(nb, nblocks - 1) * groups + g0;
   uint4* mu_wave = mu_lds + wave * GPW * (kTileMicroBytes / 16);
 #pragma unroll
@@ -98,17 +103,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_bf16(  // <= 128 VGPRs
   const uint4* cp = reinterpret_cast<const uint4*>(codes + tile0 * kTileCodeBytes) + lane;
   const uint16_t* hp = macro + tile0 * kTileMacro + l16;
 #pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
+  for (int gi = 0; gi < GPW; ++gi) R.mac[gi] = hp[gi * kTileMacro];
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int kAhead = GPW < 2 ? GPW : 2;  // code groups in flight ahead of the compute
+#pragma unroll
+  for (int gi = 0; gi < kAhead; ++gi) {
     R.code[gi][0] = load_nt16(cp + gi * (kTileCodeBytes / 16));
     R.code[gi][1] = load_nt16(cp + gi * (kTileCodeBytes / 16) + 64);
-    R.mac[gi] = hp[gi * kTileMacro];
   }
-  // wait for this wave's LDS-DMA copies and zero-region writes only (issued first; the
-  // 3 * GPW code / macro loads may still be in flight), then a bare barrier: LDS is coherent
-  // inside the workgroup, and no global data needs ordering here.
-  // (sched_barrier keeps the weight loads above the wait: the count depends on it)
+  // wait for the activation and micro-scale copies, the macro-scales and the zero-region
+  // writes (issued first; the 2 * kAhead code loads may still be in flight), then a bare
+  // barrier: LDS is coherent inside the workgroup, and no global data needs ordering here.
+  // (sched_barrier keeps the code loads above the wait: the count depends on it)
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<3 * GPW>::value);
+  __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<2 * kAhead>::value);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
@@ -118,7 +126,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_bf16(  // <= 128 VGPRs
 
   // ---- compute. Each MFMA step is pinned in order (decode, MFMA, micro-scale FMA) so
   // the scheduler cannot front-load MFMAs and park their results; the activation
-  // fragment of the next step is read one step ahead. ----
+  // fragment of the next step is read one step ahead, and the codes of group gi + kAhead
+  // are requested after group gi (the compiler's waits then take each group's codes as
+  // they arrive). ----
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const float4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
   uint4 a_next = a_lane[0];
@@ -129,6 +139,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_bf16(  // <= 128 VGPRs
     const uint2 mu8 = *reinterpret_cast<const uint2*>(
         reinterpret_cast<const uint8_t*>(mu_wave + gi * (kTileMicroBytes / 16)) + p * 128 + l16 * 8);
     float accg[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float2_t mu_pair;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint4 a_cur = a_next;
@@ -144,13 +155,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_bf16(  // <= 128 VGPRs
       const float4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a_cur), wf,
                                                                  zero4, 0, 0, 0);
       const uint32_t mw = (t < 4) ? mu8.x : mu8.y;
-      float mu_f;
-      switch (t & 3) {
-        case 0: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 0); break;
-        case 1: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 1); break;
-        case 2: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 2); break;
-        default: mu_f = __builtin_amdgcn_cvt_f32_fp8((int)mw, 3); break;
-      }
+      // two micro-scales per conversion
+      if ((t & 3) == 0) mu_pair = __builtin_amdgcn_cvt_pk_f32_fp8((int)mw, false);
+      if ((t & 3) == 2) mu_pair = __builtin_amdgcn_cvt_pk_f32_fp8((int)mw, true);
+      const float mu_f = mu_pair[t & 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) accg[i] = fmaf(mu_f, d[i], accg[i]);
       __builtin_amdgcn_sched_barrier(0);
@@ -158,13 +166,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_bf16(  // <= 128 VGPRs
     const float M = fp16_value_hw(R.mac[gi] & 0xFFFFu);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(M, accg[i], acc[i]);
+    if (gi + kAhead < GPW) {
+      __builtin_amdgcn_sched_barrier(0);
+      R.code[gi + kAhead][0] = load_nt16(cp + (gi + kAhead) * (kTileCodeBytes / 16));
+      R.code[gi + kAhead][1] = load_nt16(cp + (gi + kAhead) * (kTileCodeBytes / 16) + 64);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // ---- fold the two micro-block columns, then the k-split waves, then store ----
   // output rows 4q+i = (p, m = 4(q&1)+i); the two parities meet across lane ^ 32
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], 32);
-  __syncthreads();  // every wave is done with its micro-scale slots (red reuses them)
   if (p == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[((ks * kRBW + rb) * 16 + l16) * 8 + 4 * q + i] = acc[i];
@@ -219,7 +232,7 @@ hipError_t launch_gemv_bf16(const uint16_t* a, int64_t lda, int64_t m, int64_t k
   const dim3 grid((unsigned)((nblocks + rbw - 1) / rbw)), block(64 * rbw * ks);
   const size_t mu_bytes = (size_t)ks * rbw * gpw * kTileMicroBytes;
   const size_t red_bytes = (size_t)ks * rbw * 16 * 8 * sizeof(float);
-  const size_t lds = (size_t)k * 16 + kZeroBytes + (mu_bytes > red_bytes ? mu_bytes : red_bytes);
+  const size_t lds = (size_t)k * 16 + kZeroBytes + mu_bytes + red_bytes;
 #define FP4_GEMV(R, G, B) \
   hipLaunchKernelGGL((k_gemv_bf16<R, G, B>), grid, block, lds, st, a, lda, (int)m, k, codes, micro, macro, n, c, ldc)
 #define FP4_GEMV_G(R, B) \
