@@ -34,6 +34,8 @@ hipError_t launch_act_prep_gated(const uint16_t* a, int64_t rows, int64_t k, int
 
 // Decode product for m <= 8 bf16 activation rows against tiled E2M1 weights [n x k].
 // Returns hipErrorInvalidValue when the shape is outside what the kernel covers.
+// Compute units of the current device (cached per device).
+int device_cus();
 bool gemv_supports(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemv_bf16(const uint16_t* a, int64_t lda, int64_t m, int64_t k,
                             const uint8_t* codes, const uint8_t* micro, const uint16_t* macro,

@@ -18,9 +18,10 @@
 // activations (m <= 8 rows) are copied once per workgroup into LDS by LDS-DMA loads (no
 // registers), in MFMA-fragment order, so a wave's operand read is 512 contiguous bytes.
 // Operand lanes outside their micro-block read from a small zero region instead (no
-// branches). The KS partial results of a row block meet in LDS. With k = 4096 one
-// workgroup holds 8 waves and 80 KB of LDS, two fit on a CU, and the weight stream of the
-// whole launch is in flight at once.
+// branches). The KS partial results of a row block meet in LDS. With k = 4096 and
+// n = 14336 a workgroup holds 4 row blocks x 4 runs of 1024 columns (16 waves, 92 KB of
+// LDS), one per CU on 224 CUs, and the weight stream of the whole launch is in flight at
+// once.
 //
 // Issue order. A compute unit's memory pipe drains at its share of HBM bandwidth, and a
 // wave cannot run past a load it has not yet issued, so loads are issued in the order
@@ -37,6 +38,7 @@ namespace {
 constexpr int kMaxWaves = 16;  // waves per workgroup (row blocks x waves along k)
 constexpr int kMaxKS = 8;      // waves along k per row block
 constexpr int kZeroBytes = 4096;  // zero region: covers the per-group operand offsets
+constexpr size_t kMaxLds = 160 * 1024;  // LDS of one compute unit
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
@@ -225,20 +227,26 @@ hipError_t launch_gemv_bf16(const uint16_t* a, int64_t lda, int64_t m, int64_t k
   const int gpw = gemv_gpw(groups);
   const int ks = (int)((groups + gpw - 1) / gpw);
   const int64_t nblocks = n >> 4;
-  // row blocks per workgroup: two when that still leaves at least a workgroup per CU
-  // (each workgroup copies all of A once, so wider workgroups move less; four per
-  // workgroup measured slower than two on the 14336-row decode shape)
-  const int rbw = (2 * ks <= kMaxWaves && nblocks / 2 >= 256) ? 2 : 1;
+  // Row blocks per workgroup. Each workgroup copies all of A once, so wider workgroups
+  // copy less per weight byte: four row blocks while that still keeps 3/4 of the CUs
+  // busy, two while it leaves a workgroup per CU, else one (measured at k = 4096:
+  // n = 12288..28672 run fastest with four, n = 8192 with two).
+  auto lds_bytes = [&](int rbw) {
+    return (size_t)k * 16 + kZeroBytes + (size_t)ks * rbw * gpw * kTileMicroBytes +
+           (size_t)ks * rbw * 16 * 8 * sizeof(float);
+  };
+  const int64_t cus = device_cus();
+  int rbw = 1;
+  if (4 * ks <= kMaxWaves && 4 * (nblocks / 4) >= 3 * cus && lds_bytes(4) <= kMaxLds) rbw = 4;
+  else if (2 * ks <= kMaxWaves && nblocks / 2 >= cus && lds_bytes(2) <= kMaxLds) rbw = 2;
   const dim3 grid((unsigned)((nblocks + rbw - 1) / rbw)), block(64 * rbw * ks);
-  const size_t mu_bytes = (size_t)ks * rbw * gpw * kTileMicroBytes;
-  const size_t red_bytes = (size_t)ks * rbw * 16 * 8 * sizeof(float);
-  const size_t lds = (size_t)k * 16 + kZeroBytes + mu_bytes + red_bytes;
+  const size_t lds = lds_bytes(rbw);
 #define FP4_GEMV(R, G, B) \
   hipLaunchKernelGGL((k_gemv_bf16<R, G, B>), grid, block, lds, st, a, lda, (int)m, k, codes, micro, macro, n, c, ldc)
 #define FP4_GEMV_G(R, B) \
   do { if (gpw == 1) FP4_GEMV(R, 1, B); else if (gpw == 2) FP4_GEMV(R, 2, B); else FP4_GEMV(R, 4, B); } while (0)
 #define FP4_GEMV_R(B) \
-  do { if (rbw == 2) FP4_GEMV_G(2, B); else FP4_GEMV_G(1, B); } while (0)
+  do { if (rbw == 4) FP4_GEMV_G(4, B); else if (rbw == 2) FP4_GEMV_G(2, B); else FP4_GEMV_G(1, B); } while (0)
   if (out_bf16) FP4_GEMV_R(1); else FP4_GEMV_R(0);
 #undef FP4_GEMV_R
 #undef FP4_GEMV_G

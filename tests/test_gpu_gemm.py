@@ -72,6 +72,23 @@ def test_decode_workload_full_size_sampled():
     bf16_gate(bf16_values(c)[:, cols], oracle.formats.bf16_round(ref))
 
 
+# row-block counts that leave the last workgroup partly empty, at shapes large enough
+# for workgroups of two and four row blocks (k-runs of 1 to 8 waves)
+@pytest.mark.parametrize("m,k,n", [(5, 4096, 12304), (8, 2048, 8208), (3, 8192, 8208), (8, 1024, 12304)])
+def test_decode_gemv_wide_workgroups_ragged(m, k, n):
+    rng = np.random.default_rng(210 + m + k + n)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    w[:, rng.choice(k, 4, replace=False)] *= 100
+    a = workloads.to_bf16_values(rng.standard_normal((m, k)).astype(np.float32))
+    print(f"[case] gemv wide workgroups m={m} k={k} n={n}", flush=True)
+    wq = _wq(w)
+    ad = to_device_bf16(a)
+    cols = np.union1d(rng.choice(n - 16, 368, replace=False), np.arange(n - 16, n))
+    ref = _oracle_c(a.astype(np.float64), w[cols], oracle.A16)
+    f32_gate(host(fp4.gemm_w4aX(fp4.A16, ad, wq, out_dtype=torch.float32))[:, cols], ref)
+    bf16_gate(bf16_values(fp4.gemm_w4aX(fp4.A16, ad, wq))[:, cols], oracle.formats.bf16_round(ref))
+
+
 @pytest.mark.parametrize("act", [16, 8, 4])
 @pytest.mark.parametrize("m,n,k", [(200, 400, 768), (17, 128, 256), (130, 272, 1280)])
 def test_gemm_small_shapes(act, m, n, k):
