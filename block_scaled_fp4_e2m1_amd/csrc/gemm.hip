@@ -12,6 +12,8 @@
 //
 // Tiling: 256 threads = 4 waves side by side along n, 64 x 64 outputs per wave as 4 x 4
 // tiles of v_mfma_f32_16x16x32_{f16,bf16}; the workgroup covers 64 rows x 256 weight rows.
+// Large dense products run 8 such waves (64 x 512 per workgroup, one per CU), so each
+// activation tile copied into LDS feeds twice the weight columns.
 // Weight fragments come straight from the tiled layout (each lane's 16 bytes are one
 // MFMA operand row for four k-steps); activation fragments are 16-byte row pieces.
 //
@@ -152,7 +154,8 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 // weight rows; each wave owns a 64 x 64 block as 4 x 4 MFMA tiles, so every weight
 // fragment is decoded by exactly one wave. Sized for two workgroups per CU (two waves
 // per SIMD: at most 256 registers and ~80 KB of LDS each), which is what keeps the
-// matrix pipes busy.
+// matrix pipes busy. The 8-wave form (WM = 3) keeps the same waves and pipeline, one
+// workgroup per CU: the two waves of each 16-row slice share its activation copies.
 // The k loop runs in stages of half a 256-column group:
 //   - the activation tile (64 x 128, 16 KB, MFMA-fragment order) and the weight codes
 //     (4 waves x 4 row blocks x 1 KB, contiguous in the tiled layout) are copied into LDS
@@ -186,9 +189,13 @@ __shared__ uint4 g_a0[kAStage];
 __shared__ uint4 g_a1[kAStage];
 __shared__ uint4 g_w0[kWStage];
 __shared__ uint4 g_w1[kWStage];
+__shared__ uint4 g_w0x[2 * kWStage];  // the 8-wave form: [wave 8][piece 4][64]
+__shared__ uint4 g_w1x[2 * kWStage];
 
-// dynamic LDS: float sa[G][64] then uint16 mw[16][G][16] (at most 16 row blocks per tile)
-size_t gemm_dynamic_lds(int groups) { return (size_t)groups * kBM * 4 + (size_t)16 * groups * 16 * 2; }
+// dynamic LDS: float sa[G][64] then uint16 mw[BN/16][G][16]
+size_t gemm_dynamic_lds(int groups, int bn = 256) {
+  return (size_t)groups * kBM * 4 + (size_t)(bn / 16) * groups * 16 * 2;
+}
 
 // Weight-side shape of the pipeline, by weight mode WM:
 //   0  E2M1, 4 row blocks of 16 weight rows per wave (workgroup tile 64 x 256), one 1 KB
@@ -196,12 +203,16 @@ size_t gemm_dynamic_lds(int groups) { return (size_t)groups * kBM * 4 + (size_t)
 //   1  E4M3 (W8A8), 2 row blocks per wave (tile 64 x 128), two 1 KB pieces per row block
 //      and stage, so a wave still copies 4 pieces per stage into the same LDS buffers;
 //   2  E2M1 narrow, 2 row blocks per wave (tile 64 x 128): twice the workgroups, for
-//      products whose wide grid cannot fill the chip.
+//      products whose wide grid cannot fill the chip;
+//   3  E2M1, 4 row blocks per wave and 8 waves (tile 64 x 512): one activation stage
+//      feeds twice the weight columns, halving the activation copies per CU; dense
+//      products whose 64 x 512 grid still gives every CU a workgroup.
 template <int WM>
 struct WShape {
   static constexpr bool E4M3 = WM == 1;
-  static constexpr int NI = WM == 0 ? 4 : 2;       // row blocks per wave
-  static constexpr int BN = 64 * NI;               // weight rows per workgroup
+  static constexpr int NI = (WM == 0 || WM == 3) ? 4 : 2;  // row blocks per wave
+  static constexpr int WAVES = WM == 3 ? 8 : 4;            // waves per workgroup
+  static constexpr int BN = 16 * NI * WAVES;               // weight rows per workgroup
   static constexpr int kTile = E4M3 ? kTile8CodeBytes : kTileCodeBytes;
   static constexpr int kPieces = E4M3 ? 4 : NI;    // 1 KB LDS-DMA pieces per wave and stage
 };
@@ -367,9 +378,13 @@ __device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
 }
 
 template <int A_BF16, int C_BF16, int GROUPED, int WM>
-__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   static_assert(WM != 1 || (!A_BF16 && !GROUPED), "E4M3 weights: dense, FP16 activation operand");
+  static_assert(WM != 3 || !GROUPED, "the 8-wave form is dense");
   constexpr int NI = WShape<WM>::NI, BN = WShape<WM>::BN, kTile = WShape<WM>::kTile;
+  constexpr int kWaves = WShape<WM>::WAVES;
+  uint4* const w_buf0 = WM == 3 ? g_w0x : g_w0;
+  uint4* const w_buf1 = WM == 3 ? g_w1x : g_w1;
   constexpr int kPieces = WShape<WM>::kPieces;
   constexpr bool kE4M3 = WShape<WM>::E4M3;
   extern __shared__ uint8_t g_dyn[];
@@ -409,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   if (!A_BF16) {  // the FP16 operand path always carries activation factors
     int64_t src_row = min(row_begin + lane, row_end - 1);  // lane = row of the tile
     if (GROUPED && args.row_token) src_row = args.row_token[src_row];
-    for (int g = wave; g < groups; g += 4)  // one 64-row column of factors per DMA
+    for (int g = wave; g < groups; g += kWaves)  // one 64-row column of factors per DMA
       __builtin_amdgcn_global_load_lds((global_void_ptr)(args.a_scale + src_row * groups + g),
                                        (lds_void_ptr)(g_sa + g * kBM), 4, 0, 0);
   }
@@ -418,7 +433,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     const int mw_elems = (BN / 16) * groups * 16;  // uint16 count
     const int64_t mw_first = nb_tile0 * groups * 16;
     const int64_t mw_last = (w_row_base / 16 + nblocks) * groups * 16;  // exclusive bound
-    for (int c0 = wave * 64 * 2; c0 < mw_elems; c0 += 256 * 2) {  // 4-byte lanes = 2 entries
+    for (int c0 = wave * 64 * 2; c0 < mw_elems; c0 += kWaves * 64 * 2) {  // 4-byte lanes = 2 entries
       const int64_t src = min(mw_first + c0 + 2 * lane, mw_last - 2);
       __builtin_amdgcn_global_load_lds((global_void_ptr)(args.macro + src), (lds_void_ptr)(g_mw + c0), 4, 0, 0);
     }
@@ -427,9 +442,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   // Operand copies go through raw buffer resources: the per-lane byte offset is fixed for
   // the whole k loop and the per-stage part is a scalar offset, so the loop spends no
   // vector instructions on addresses. Reads past a resource's size return zero.
-  // ---- activation copies: wave w moves row tile mi = w (16 rows), 4 steps per stage ----
+  // ---- activation copies: wave w moves row tile mi = w % 4 (16 rows); with 8 waves each
+  // of a row tile's two waves moves 2 of its 4 pieces per stage ----
   const uint16_t* a16 = static_cast<const uint16_t*>(args.a);
-  int64_t a_src_row = min(row_begin + wave * 16 + l16, row_end - 1);
+  constexpr int kAPieces = 16 / kWaves;  // per wave and stage
+  const int a_mi = wave & 3, a_t0 = (wave >> 2) * kAPieces;
+  int64_t a_src_row = min(row_begin + a_mi * 16 + l16, row_end - 1);
   if (GROUPED && args.row_token) a_src_row = args.row_token[a_src_row];
   // gathered rows are addressed from the start of A (the launcher keeps A under 4 GiB);
   // otherwise from the workgroup's first row
@@ -456,9 +474,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     const int g = s >> 1, h = s & 1;
     const uint32_t a_soff = (uint32_t)s * (kStageK * 2);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(abuf + (wave * 4 + t) * 64), 16,
+    for (int tt = 0; tt < kAPieces; ++tt) {
+      const int t = a_t0 + tt;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(abuf + (a_mi * 4 + t) * 64), 16,
                                                a_voff, a_soff + 64 * t, 0, 0);
+    }
     // piece d: row block d (E2M1) or d / 2, half d % 2 of the stage's 2 KB (E4M3)
 #pragma unroll
     for (int d = 0; d < kPieces; ++d) {
@@ -512,7 +532,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
 
   uint2 mu_cur[4], mu_nxt[4];
   const int stages = 2 * groups;
-  copy_stage(g_a0, g_w0, 0);
+  copy_stage(g_a0, w_buf0, 0);
   __builtin_amdgcn_sched_barrier(0);
   load_micro(mu_cur, 0);
   // stage 0's code words and step-0 weight fragments (the wave's own copies)
@@ -533,7 +553,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     }
   }
 #pragma unroll
-  for (int d = 0; d < kPieces; ++d) cw[d] = g_w0[(wave * 4 + d) * 64 + lane];
+  for (int d = 0; d < kPieces; ++d) cw[d] = w_buf0[(wave * 4 + d) * 64 + lane];
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
     wf0[ni] = weight_frag<A_BF16, WM, 0>(cw, ni, OpTraits<A_BF16>::micro_operand(mu_cur[ni].x & 0xFFu));
@@ -576,8 +596,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     }
   };
   for (int s = 0; s < stages; s += 2) {
-    run_stage(std::integral_constant<int, 0>{}, g_a0, g_a1, g_w1, s);
-    run_stage(std::integral_constant<int, 1>{}, g_a1, g_a0, g_w0, s + 1);
+    run_stage(std::integral_constant<int, 0>{}, g_a0, g_a1, w_buf1, s);
+    run_stage(std::integral_constant<int, 1>{}, g_a1, g_a0, w_buf0, s + 1);
   }
 
   // ---- apply the final factors, store ----
@@ -600,6 +620,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
     }
   }
 }
+// Kernels: the 4-wave forms run two workgroups per CU, the 8-wave form one.
+template <int A_BF16, int C_BF16, int GROUPED, int WM>
+__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
+  gemm_body<A_BF16, C_BF16, GROUPED, WM>(args);
+}
+
+template <int A_BF16, int C_BF16>
+__global__ __launch_bounds__(512, 1) void k_gemm_w8(GemmArgs args) {
+  gemm_body<A_BF16, C_BF16, 0, 3>(args);
+}
+
 // float32 activations: one thread per output, exact weight values, float32 FMA.
 template <int C_BF16>
 __global__ __launch_bounds__(256) void k_gemm_f32act(const float* __restrict__ a, int64_t lda,
@@ -662,17 +693,27 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   else tiles_m = (g.m + kBM - 1) / kBM;
   // dense E2M1 products whose 64 x 256 tiles cannot give every CU two workgroups take the
   // narrow 64 x 128 tile
+  const int64_t cus = device_cus();
   const bool narrow = !g.w_e4m3 && !g.expert_offsets &&
-                      tiles_m * ((g.n + WShape<0>::BN - 1) / WShape<0>::BN) < 2 * (int64_t)device_cus();
-  const int64_t bn = g.w_e4m3 ? WShape<1>::BN : narrow ? WShape<2>::BN : WShape<0>::BN;
+                      tiles_m * ((g.n + WShape<0>::BN - 1) / WShape<0>::BN) < 2 * cus;
+  // dense E2M1 products whose 64 x 512 tiles still give every CU a workgroup take the
+  // 8-wave form: one activation stage serves twice the weight columns
+  const bool eight = !g.w_e4m3 && !g.expert_offsets && !narrow &&
+                     tiles_m * ((g.n + WShape<3>::BN - 1) / WShape<3>::BN) >= cus &&
+                     gemm_dynamic_lds((int)(g.k >> 8), WShape<3>::BN) <= 160 * 1024 - 96 * 1024;
+  const int64_t bn = g.w_e4m3 ? WShape<1>::BN : narrow ? WShape<2>::BN : eight ? WShape<3>::BN : WShape<0>::BN;
   const int64_t tiles_n = (g.n + bn - 1) / bn;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(256);
-  const size_t lds = gemm_dynamic_lds((int)(g.k >> 8));
+  const dim3 grid((unsigned)blocks), block(eight ? 512 : 256);
+  const size_t lds = gemm_dynamic_lds((int)(g.k >> 8), (int)bn);
 #define FP4_GEMM(A, C, G, W) hipLaunchKernelGGL((k_gemm<A, C, G, W>), grid, block, lds, st, g)
+#define FP4_GEMM8(A, C) hipLaunchKernelGGL((k_gemm_w8<A, C>), grid, block, lds, st, g)
   const int grouped = g.expert_offsets != nullptr;
-  if (g.w_e4m3) {
+  if (eight) {
+    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM8(1, 1); else FP4_GEMM8(1, 0); }
+    else { if (g.c_is_bf16) FP4_GEMM8(0, 1); else FP4_GEMM8(0, 0); }
+  } else if (g.w_e4m3) {
     if (g.c_is_bf16) FP4_GEMM(0, 1, 0, 1); else FP4_GEMM(0, 0, 0, 1);
   } else if (narrow) {
     if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM(1, 1, 0, 2); else FP4_GEMM(1, 0, 0, 2); }
@@ -684,6 +725,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     if (g.c_is_bf16) { if (grouped) FP4_GEMM(0, 1, 1, 0); else FP4_GEMM(0, 1, 0, 0); }
     else { if (grouped) FP4_GEMM(0, 0, 1, 0); else FP4_GEMM(0, 0, 0, 0); }
   }
+#undef FP4_GEMM8
 #undef FP4_GEMM
   return hipGetLastError();
 }

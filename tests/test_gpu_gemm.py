@@ -106,23 +106,44 @@ def test_gemm_small_shapes(act, m, n, k):
 
 
 @pytest.mark.parametrize("act", [16, 8, 4])
-def test_gemm_wide_tiles_ragged(act):
-    """Small products take the narrow 64 x 128 tile; this shape (2043 x 4080: 32 x 16 tiles
-    of 64 x 256, the last row and column tiles ragged) is large enough for the wide one."""
+def test_gemm_eight_wave_tiles_ragged(act):
+    """Small products take the narrow 64 x 128 tile; this shape (2043 x 4080: 32 x 8 tiles
+    of 64 x 512, the last row and column tiles ragged) is large enough for the 8-wave
+    64 x 512 form."""
     m, n, k = 2043, 4080, 256
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert -(-m // 64) * -(-n // 256) >= 2 * cus, "shape no longer selects the wide tile"
+    assert -(-m // 64) * -(-n // 512) >= cus, "shape no longer selects the 8-wave tile"
     rng = np.random.default_rng(310 + act)
     a = rng.standard_normal((m, k)).astype(np.float32)
     a[:, rng.choice(k, 3, replace=False)] *= 50
     a = workloads.to_bf16_values(a)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
-    print(f"[case] gemm wide tiles {ACTS[act]} m={m} n={n} k={k}", flush=True)
+    print(f"[case] gemm 8-wave tiles {ACTS[act]} m={m} n={n} k={k}", flush=True)
     wq = _wq(w)
     ad = to_device_bf16(a)
     ref = _oracle_c(a.astype(np.float64), w, act)
     f32_gate(host(fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32)), ref)
     bf16_gate(bf16_values(fp4.gemm_w4aX(act, ad, wq)), oracle.formats.bf16_round(ref))
+
+
+@pytest.mark.parametrize("act", [16, 4])
+def test_gemm_wide_tiles_large_k_sampled(act):
+    """At k = 13312 (52 groups) the 8-wave form's macro-scale table no longer fits its LDS,
+    so a large dense product (1040 x 8192: 17 x 32 tiles of 64 x 256, the last row tile
+    ragged) runs the 4-wave 64 x 256 form; checked on sampled outputs, the last row and
+    column tiles among them."""
+    m, n, k = 1040, 8192, 13312
+    rng = np.random.default_rng(320 + act)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    a[:, rng.choice(k, 5, replace=False)] *= 50
+    a = workloads.to_bf16_values(a)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    print(f"[case] gemm wide tiles large k {ACTS[act]} m={m} n={n} k={k} (sampled)", flush=True)
+    c = fp4.gemm_w4aX(act, to_device_bf16(a), _wq(w), out_dtype=torch.float32)
+    rows = np.union1d(rng.choice(m - 16, 24, replace=False), np.arange(m - 16, m))
+    cols = np.union1d(rng.choice(n - 256, 56, replace=False), np.arange(n - 256, n, 32))
+    ref = _oracle_c(a[rows].astype(np.float64), w[cols], act)
+    f32_gate(host(c)[np.ix_(rows, cols)], ref)
 
 
 def test_gemm_float32_activations_a4():
