@@ -13,7 +13,8 @@
 // Tiling: 256 threads = 4 waves side by side along n, 64 x 64 outputs per wave as 4 x 4
 // tiles of v_mfma_f32_16x16x32_{f16,bf16}; the workgroup covers 64 rows x 256 weight rows.
 // Large dense products run 8 such waves (64 x 512 per workgroup, one per CU), so each
-// activation tile copied into LDS feeds twice the weight columns.
+// activation tile copied into LDS feeds twice the weight columns; small ones run 8 waves
+// of 16 columns each (64 x 128, two per CU).
 // Weight fragments come straight from the tiled layout (each lane's 16 bytes are one
 // MFMA operand row for four k-steps); activation fragments are 16-byte row pieces.
 //
@@ -202,16 +203,17 @@ size_t gemm_dynamic_lds(int groups, int bn = 256) {
 //      LDS-DMA piece per row block and stage;
 //   1  E4M3 (W8A8), 2 row blocks per wave (tile 64 x 128), two 1 KB pieces per row block
 //      and stage, so a wave still copies 4 pieces per stage into the same LDS buffers;
-//   2  E2M1 narrow, 2 row blocks per wave (tile 64 x 128): twice the workgroups, for
-//      products whose wide grid cannot fill the chip;
+//   2  E2M1 narrow, 1 row block per wave and 8 waves (tile 64 x 128): twice the
+//      workgroups of the wide grid and twice its waves per workgroup, for products whose
+//      wide grid cannot fill the chip;
 //   3  E2M1, 4 row blocks per wave and 8 waves (tile 64 x 512): one activation stage
 //      feeds twice the weight columns, halving the activation copies per CU; dense
 //      products whose 64 x 512 grid still gives every CU a workgroup.
 template <int WM>
 struct WShape {
   static constexpr bool E4M3 = WM == 1;
-  static constexpr int NI = (WM == 0 || WM == 3) ? 4 : 2;  // row blocks per wave
-  static constexpr int WAVES = WM == 3 ? 8 : 4;            // waves per workgroup
+  static constexpr int NI = (WM == 0 || WM == 3) ? 4 : WM == 2 ? 1 : 2;  // row blocks per wave
+  static constexpr int WAVES = WM >= 2 ? 8 : 4;                        // waves per workgroup
   static constexpr int BN = 16 * NI * WAVES;               // weight rows per workgroup
   static constexpr int kTile = E4M3 ? kTile8CodeBytes : kTileCodeBytes;
   static constexpr int kPieces = E4M3 ? 4 : NI;    // 1 KB LDS-DMA pieces per wave and stage
@@ -303,7 +305,7 @@ __device__ __forceinline__ void last_step(const StepOperands<A_BF16, WM>& o, flo
   constexpr int NI = WShape<WM>::NI;
   __builtin_amdgcn_s_waitcnt(kVmcntWait<VMCNT>::value);
 #pragma unroll
-  for (int d = 0; d < WShape<WM>::kPieces; ++d) cw[d] = nwbuf[(wave * 4 + d) * 64 + lane];
+  for (int d = 0; d < WShape<WM>::kPieces; ++d) cw[d] = nwbuf[(wave * WShape<WM>::kPieces + d) * 64 + lane];
   if (RATIOS) ratios(r);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -385,6 +387,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   constexpr int kWaves = WShape<WM>::WAVES;
   uint4* const w_buf0 = WM == 3 ? g_w0x : g_w0;
   uint4* const w_buf1 = WM == 3 ? g_w1x : g_w1;
+  static_assert(kWaves * WShape<WM>::kPieces * 64 <= (WM == 3 ? 2 : 1) * kWStage, "weight slots");
   constexpr int kPieces = WShape<WM>::kPieces;
   constexpr bool kE4M3 = WShape<WM>::E4M3;
   extern __shared__ uint8_t g_dyn[];
@@ -484,7 +487,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     for (int d = 0; d < kPieces; ++d) {
       const int ni = kE4M3 ? d >> 1 : d;
       const uint32_t soff = (uint32_t)((ni * groups + g) * kTile + h * (kTile / 2) + (kE4M3 ? (d & 1) * 1024 : 0));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(wbuf + (wave * 4 + d) * 64), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(wbuf + (wave * kPieces + d) * 64), 16,
                                                (uint32_t)lane * 16, soff, 0, 0);
     }
   };
@@ -553,7 +556,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     }
   }
 #pragma unroll
-  for (int d = 0; d < kPieces; ++d) cw[d] = w_buf0[(wave * 4 + d) * 64 + lane];
+  for (int d = 0; d < kPieces; ++d) cw[d] = w_buf0[(wave * kPieces + d) * 64 + lane];
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
     wf0[ni] = weight_frag<A_BF16, WM, 0>(cw, ni, OpTraits<A_BF16>::micro_operand(mu_cur[ni].x & 0xFFu));
@@ -620,7 +623,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     }
   }
 }
-// Kernels: the 4-wave forms run two workgroups per CU, the 8-wave form one.
+// Kernels: the 4-wave forms run two workgroups per CU, the 8-wave wide form one, the
+// 8-wave narrow form two.
 template <int A_BF16, int C_BF16, int GROUPED, int WM>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   gemm_body<A_BF16, C_BF16, GROUPED, WM>(args);
@@ -629,6 +633,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
 template <int A_BF16, int C_BF16>
 __global__ __launch_bounds__(512, 1) void k_gemm_w8(GemmArgs args) {
   gemm_body<A_BF16, C_BF16, 0, 3>(args);
+}
+
+template <int A_BF16, int C_BF16>
+__global__ __launch_bounds__(512, 2) void k_gemm_n8(GemmArgs args) {
+  gemm_body<A_BF16, C_BF16, 0, 2>(args);
 }
 
 // float32 activations: one thread per output, exact weight values, float32 FMA.
@@ -705,7 +714,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const int64_t tiles_n = (g.n + bn - 1) / bn;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(eight ? 512 : 256);
+  const dim3 grid((unsigned)blocks), block((eight || narrow) ? 512 : 256);
   const size_t lds = gemm_dynamic_lds((int)(g.k >> 8), (int)bn);
 #define FP4_GEMM(A, C, G, W) hipLaunchKernelGGL((k_gemm<A, C, G, W>), grid, block, lds, st, g)
 #define FP4_GEMM8(A, C) hipLaunchKernelGGL((k_gemm_w8<A, C>), grid, block, lds, st, g)
@@ -716,8 +725,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   } else if (g.w_e4m3) {
     if (g.c_is_bf16) FP4_GEMM(0, 1, 0, 1); else FP4_GEMM(0, 0, 0, 1);
   } else if (narrow) {
-    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM(1, 1, 0, 2); else FP4_GEMM(1, 0, 0, 2); }
-    else { if (g.c_is_bf16) FP4_GEMM(0, 1, 0, 2); else FP4_GEMM(0, 0, 0, 2); }
+#define FP4_GEMMN8(A, C) hipLaunchKernelGGL((k_gemm_n8<A, C>), grid, block, lds, st, g)
+    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMMN8(1, 1); else FP4_GEMMN8(1, 0); }
+    else { if (g.c_is_bf16) FP4_GEMMN8(0, 1); else FP4_GEMMN8(0, 0); }
+#undef FP4_GEMMN8
   } else if (g.a_is_bf16) {
     if (g.c_is_bf16) { if (grouped) FP4_GEMM(1, 1, 1, 0); else FP4_GEMM(1, 1, 0, 0); }
     else { if (grouped) FP4_GEMM(1, 0, 1, 0); else FP4_GEMM(1, 0, 0, 0); }
