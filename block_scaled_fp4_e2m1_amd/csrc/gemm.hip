@@ -20,8 +20,8 @@
 //
 // Sensitive layers (W8A8): the same pipeline with E4M3 weight elements in their tiled
 // layout and the FP16 A8 activation operand: W' = e4m3 * mu * 2^-3 is exact in FP16 as
-// well, so the products stay exact; each wave then covers 32 weight rows (tile 64 x 128)
-// so that the doubled weight bytes fit the same LDS buffers. "NVIDIA Ships TensorRT-LLM
+// well, so the products stay exact; each of 8 waves then covers 16 weight rows (tile
+// 64 x 128) so that the doubled weight bytes fit the same LDS buffers. "NVIDIA Ships TensorRT-LLM
 // 0.16", deployment advice on outliers: FP8 kept on the most sensitive layers.
 //
 // Grouped form: the workgroup grid enumerates (expert, 64-row tile) pairs; each
@@ -201,8 +201,8 @@ size_t gemm_dynamic_lds(int groups, int bn = 256) {
 // Weight-side shape of the pipeline, by weight mode WM:
 //   0  E2M1, 4 row blocks of 16 weight rows per wave (workgroup tile 64 x 256), one 1 KB
 //      LDS-DMA piece per row block and stage;
-//   1  E4M3 (W8A8), 2 row blocks per wave (tile 64 x 128), two 1 KB pieces per row block
-//      and stage, so a wave still copies 4 pieces per stage into the same LDS buffers;
+//   1  E4M3 (W8A8), 1 row block per wave and 8 waves (tile 64 x 128), two 1 KB pieces
+//      per row block and stage, so the doubled weight bytes fit the same LDS buffers;
 //   2  E2M1 narrow, 1 row block per wave and 8 waves (tile 64 x 128): twice the
 //      workgroups of the wide grid and twice its waves per workgroup, for products whose
 //      wide grid cannot fill the chip;
@@ -212,11 +212,11 @@ size_t gemm_dynamic_lds(int groups, int bn = 256) {
 template <int WM>
 struct WShape {
   static constexpr bool E4M3 = WM == 1;
-  static constexpr int NI = (WM == 0 || WM == 3) ? 4 : WM == 2 ? 1 : 2;  // row blocks per wave
-  static constexpr int WAVES = WM >= 2 ? 8 : 4;                        // waves per workgroup
+  static constexpr int NI = (WM == 0 || WM == 3) ? 4 : 1;  // row blocks per wave
+  static constexpr int WAVES = WM == 0 ? 4 : 8;            // waves per workgroup
   static constexpr int BN = 16 * NI * WAVES;               // weight rows per workgroup
   static constexpr int kTile = E4M3 ? kTile8CodeBytes : kTileCodeBytes;
-  static constexpr int kPieces = E4M3 ? 4 : NI;    // 1 KB LDS-DMA pieces per wave and stage
+  static constexpr int kPieces = E4M3 ? 2 * NI : NI;  // 1 KB LDS-DMA pieces per wave and stage
 };
 
 template <int A_BF16, int WM>
@@ -623,8 +623,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     }
   }
 }
-// Kernels: the 4-wave forms run two workgroups per CU, the 8-wave wide form one, the
-// 8-wave narrow form two.
+// Kernels: the 4-wave wide form runs two workgroups per CU, the 8-wave wide form one, the
+// 8-wave narrow forms (E2M1 and E4M3) two.
 template <int A_BF16, int C_BF16, int GROUPED, int WM>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   gemm_body<A_BF16, C_BF16, GROUPED, WM>(args);
@@ -635,9 +635,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_w8(GemmArgs args) {
   gemm_body<A_BF16, C_BF16, 0, 3>(args);
 }
 
-template <int A_BF16, int C_BF16>
+template <int A_BF16, int C_BF16, int WM>
 __global__ __launch_bounds__(512, 2) void k_gemm_n8(GemmArgs args) {
-  gemm_body<A_BF16, C_BF16, 0, 2>(args);
+  gemm_body<A_BF16, C_BF16, 0, WM>(args);
 }
 
 // float32 activations: one thread per output, exact weight values, float32 FMA.
@@ -714,21 +714,20 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const int64_t tiles_n = (g.n + bn - 1) / bn;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block((eight || narrow) ? 512 : 256);
+  const dim3 grid((unsigned)blocks), block((eight || narrow || g.w_e4m3) ? 512 : 256);
   const size_t lds = gemm_dynamic_lds((int)(g.k >> 8), (int)bn);
 #define FP4_GEMM(A, C, G, W) hipLaunchKernelGGL((k_gemm<A, C, G, W>), grid, block, lds, st, g)
 #define FP4_GEMM8(A, C) hipLaunchKernelGGL((k_gemm_w8<A, C>), grid, block, lds, st, g)
+#define FP4_GEMMN8(A, C, W) hipLaunchKernelGGL((k_gemm_n8<A, C, W>), grid, block, lds, st, g)
   const int grouped = g.expert_offsets != nullptr;
   if (eight) {
     if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM8(1, 1); else FP4_GEMM8(1, 0); }
     else { if (g.c_is_bf16) FP4_GEMM8(0, 1); else FP4_GEMM8(0, 0); }
   } else if (g.w_e4m3) {
-    if (g.c_is_bf16) FP4_GEMM(0, 1, 0, 1); else FP4_GEMM(0, 0, 0, 1);
+    if (g.c_is_bf16) FP4_GEMMN8(0, 1, 1); else FP4_GEMMN8(0, 0, 1);
   } else if (narrow) {
-#define FP4_GEMMN8(A, C) hipLaunchKernelGGL((k_gemm_n8<A, C>), grid, block, lds, st, g)
-    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMMN8(1, 1); else FP4_GEMMN8(1, 0); }
-    else { if (g.c_is_bf16) FP4_GEMMN8(0, 1); else FP4_GEMMN8(0, 0); }
-#undef FP4_GEMMN8
+    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMMN8(1, 1, 2); else FP4_GEMMN8(1, 0, 2); }
+    else { if (g.c_is_bf16) FP4_GEMMN8(0, 1, 2); else FP4_GEMMN8(0, 0, 2); }
   } else if (g.a_is_bf16) {
     if (g.c_is_bf16) { if (grouped) FP4_GEMM(1, 1, 1, 0); else FP4_GEMM(1, 1, 0, 0); }
     else { if (grouped) FP4_GEMM(1, 0, 1, 0); else FP4_GEMM(1, 0, 0, 0); }
@@ -736,6 +735,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     if (g.c_is_bf16) { if (grouped) FP4_GEMM(0, 1, 1, 0); else FP4_GEMM(0, 1, 0, 0); }
     else { if (grouped) FP4_GEMM(0, 0, 1, 0); else FP4_GEMM(0, 0, 0, 0); }
   }
+#undef FP4_GEMMN8
 #undef FP4_GEMM8
 #undef FP4_GEMM
   return hipGetLastError();
