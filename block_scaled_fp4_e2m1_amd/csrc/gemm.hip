@@ -10,11 +10,12 @@
 // 16-bit operands exactly; the running sums are instead kept in units of the current
 // group's factors and rescaled at each group boundary (see the kernel comment).
 //
-// Tiling: 256 threads = 4 waves side by side along n, 64 x 64 outputs per wave as 4 x 4
-// tiles of v_mfma_f32_16x16x32_{f16,bf16}; the workgroup covers 64 rows x 256 weight rows.
-// Large dense products run 8 such waves (64 x 512 per workgroup, one per CU), so each
-// activation tile copied into LDS feeds twice the weight columns; small ones run 8 waves
-// of 16 columns each (64 x 128, two per CU).
+// Tiling: waves side by side along n, each owning 64 rows x 16 NI weight rows as 4 x NI
+// tiles of v_mfma_f32_16x16x32_{f16,bf16}. Large dense products run 16 waves of 32
+// columns (64 x 512 per workgroup, one per CU); small ones 8 waves of 16 columns (64 x 128,
+// two per CU); grouped ones 4 waves of 64 columns (64 x 256, two per CU). More waves per
+// SIMD hide more of the pipeline's latency, and a wider workgroup copies each activation
+// tile into LDS once for more weight columns.
 // Weight fragments come straight from the tiled layout (each lane's 16 bytes are one
 // MFMA operand row for four k-steps); activation fragments are 16-byte row pieces.
 //
@@ -151,12 +152,13 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 }
 
 // ---------------------------------------------------------------------------------
-// Main product kernel. Workgroup: 4 waves side by side along n; tile 64 rows x 256
-// weight rows; each wave owns a 64 x 64 block as 4 x 4 MFMA tiles, so every weight
-// fragment is decoded by exactly one wave. Sized for two workgroups per CU (two waves
-// per SIMD: at most 256 registers and ~80 KB of LDS each), which is what keeps the
-// matrix pipes busy. The 8-wave form (WM = 3) keeps the same waves and pipeline, one
-// workgroup per CU: the two waves of each 16-row slice share its activation copies.
+// Main product kernel. Workgroup: waves side by side along n (4, 8 or 16 by weight mode);
+// tile 64 rows x 16 NI weight rows per wave; each wave owns a 64 x 16 NI block as 4 x NI
+// MFMA tiles, so every weight fragment is decoded by exactly one wave. The 4-wave form is
+// sized for two workgroups per CU (two waves per SIMD: at most 256 registers and ~80 KB of
+// LDS each); the 8- and 16-wave forms run four waves per SIMD (at most 128 registers).
+// However many waves, the 64-row activation tile of a stage is copied once per workgroup:
+// with 8 or 16 waves each wave moves part of one 16-row slice.
 // The k loop runs in stages of half a 256-column group:
 //   - the activation tile (64 x 128, 16 KB, MFMA-fragment order) and the weight codes
 //     (4 waves x 4 row blocks x 1 KB, contiguous in the tiled layout) are copied into LDS
@@ -190,7 +192,7 @@ __shared__ uint4 g_a0[kAStage];
 __shared__ uint4 g_a1[kAStage];
 __shared__ uint4 g_w0[kWStage];
 __shared__ uint4 g_w1[kWStage];
-__shared__ uint4 g_w0x[2 * kWStage];  // the 8-wave form: [wave 8][piece 4][64]
+__shared__ uint4 g_w0x[2 * kWStage];  // the 16-wave form: [wave 16][piece 2][64]
 __shared__ uint4 g_w1x[2 * kWStage];
 
 // dynamic LDS: float sa[G][64] then uint16 mw[BN/16][G][16]
@@ -206,14 +208,15 @@ size_t gemm_dynamic_lds(int groups, int bn = 256) {
 //   2  E2M1 narrow, 1 row block per wave and 8 waves (tile 64 x 128): twice the
 //      workgroups of the wide grid and twice its waves per workgroup, for products whose
 //      wide grid cannot fill the chip;
-//   3  E2M1, 4 row blocks per wave and 8 waves (tile 64 x 512): one activation stage
-//      feeds twice the weight columns, halving the activation copies per CU; dense
-//      products whose 64 x 512 grid still gives every CU a workgroup.
+//   3  E2M1, 2 row blocks per wave and 16 waves (tile 64 x 512, one workgroup per CU):
+//      four waves per SIMD, and one activation stage feeds twice the weight columns of
+//      the 4-wave tile; dense products whose 64 x 512 grid still gives every CU a
+//      workgroup.
 template <int WM>
 struct WShape {
   static constexpr bool E4M3 = WM == 1;
-  static constexpr int NI = (WM == 0 || WM == 3) ? 4 : 1;  // row blocks per wave
-  static constexpr int WAVES = WM == 0 ? 4 : 8;            // waves per workgroup
+  static constexpr int NI = WM == 0 ? 4 : WM == 3 ? 2 : 1;       // row blocks per wave
+  static constexpr int WAVES = WM == 0 ? 4 : WM == 3 ? 16 : 8;   // waves per workgroup
   static constexpr int BN = 16 * NI * WAVES;               // weight rows per workgroup
   static constexpr int kTile = E4M3 ? kTile8CodeBytes : kTileCodeBytes;
   static constexpr int kPieces = E4M3 ? 2 * NI : NI;  // 1 KB LDS-DMA pieces per wave and stage
@@ -382,7 +385,7 @@ __device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
 template <int A_BF16, int C_BF16, int GROUPED, int WM>
 __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   static_assert(WM != 1 || (!A_BF16 && !GROUPED), "E4M3 weights: dense, FP16 activation operand");
-  static_assert(WM != 3 || !GROUPED, "the 8-wave form is dense");
+  static_assert(WM != 3 || !GROUPED, "the 16-wave form is dense");
   constexpr int NI = WShape<WM>::NI, BN = WShape<WM>::BN, kTile = WShape<WM>::kTile;
   constexpr int kWaves = WShape<WM>::WAVES;
   uint4* const w_buf0 = WM == 3 ? g_w0x : g_w0;
@@ -445,8 +448,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   // Operand copies go through raw buffer resources: the per-lane byte offset is fixed for
   // the whole k loop and the per-stage part is a scalar offset, so the loop spends no
   // vector instructions on addresses. Reads past a resource's size return zero.
-  // ---- activation copies: wave w moves row tile mi = w % 4 (16 rows); with 8 waves each
-  // of a row tile's two waves moves 2 of its 4 pieces per stage ----
+  // ---- activation copies: wave w moves row tile mi = w % 4 (16 rows); with 8 or 16 waves
+  // the row tile's 4 pieces per stage are split over its 2 or 4 waves ----
   const uint16_t* a16 = static_cast<const uint16_t*>(args.a);
   constexpr int kAPieces = 16 / kWaves;  // per wave and stage
   const int a_mi = wave & 3, a_t0 = (wave >> 2) * kAPieces;
@@ -623,21 +626,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     }
   }
 }
-// Kernels: the 4-wave wide form runs two workgroups per CU, the 8-wave wide form one, the
-// 8-wave narrow forms (E2M1 and E4M3) two.
+// Kernels: the 4-wave wide form runs two workgroups per CU, the 8-wave narrow forms (E2M1
+// and E4M3) two, the 16-wave wide form one.
 template <int A_BF16, int C_BF16, int GROUPED, int WM>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
   gemm_body<A_BF16, C_BF16, GROUPED, WM>(args);
 }
 
-template <int A_BF16, int C_BF16>
-__global__ __launch_bounds__(512, 1) void k_gemm_w8(GemmArgs args) {
-  gemm_body<A_BF16, C_BF16, 0, 3>(args);
-}
-
 template <int A_BF16, int C_BF16, int WM>
 __global__ __launch_bounds__(512, 2) void k_gemm_n8(GemmArgs args) {
   gemm_body<A_BF16, C_BF16, 0, WM>(args);
+}
+
+template <int A_BF16, int C_BF16>
+__global__ __launch_bounds__(1024, 1) void k_gemm_w16(GemmArgs args) {
+  gemm_body<A_BF16, C_BF16, 0, 3>(args);
 }
 
 // float32 activations: one thread per output, exact weight values, float32 FMA.
@@ -706,23 +709,24 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const bool narrow = !g.w_e4m3 && !g.expert_offsets &&
                       tiles_m * ((g.n + WShape<0>::BN - 1) / WShape<0>::BN) < 2 * cus;
   // dense E2M1 products whose 64 x 512 tiles still give every CU a workgroup take the
-  // 8-wave form: one activation stage serves twice the weight columns
-  const bool eight = !g.w_e4m3 && !g.expert_offsets && !narrow &&
+  // 16-wave form: four waves per SIMD, one activation stage for twice the weight columns
+  const bool wide16 = !g.w_e4m3 && !g.expert_offsets && !narrow &&
                      tiles_m * ((g.n + WShape<3>::BN - 1) / WShape<3>::BN) >= cus &&
                      gemm_dynamic_lds((int)(g.k >> 8), WShape<3>::BN) <= 160 * 1024 - 96 * 1024;
-  const int64_t bn = g.w_e4m3 ? WShape<1>::BN : narrow ? WShape<2>::BN : eight ? WShape<3>::BN : WShape<0>::BN;
+  const int64_t bn = g.w_e4m3 ? WShape<1>::BN : narrow ? WShape<2>::BN : wide16 ? WShape<3>::BN : WShape<0>::BN;
   const int64_t tiles_n = (g.n + bn - 1) / bn;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block((eight || narrow || g.w_e4m3) ? 512 : 256);
+  const dim3 grid((unsigned)blocks), block(wide16 ? 1024 : (narrow || g.w_e4m3) ? 512 : 256);
   const size_t lds = gemm_dynamic_lds((int)(g.k >> 8), (int)bn);
 #define FP4_GEMM(A, C, G, W) hipLaunchKernelGGL((k_gemm<A, C, G, W>), grid, block, lds, st, g)
-#define FP4_GEMM8(A, C) hipLaunchKernelGGL((k_gemm_w8<A, C>), grid, block, lds, st, g)
 #define FP4_GEMMN8(A, C, W) hipLaunchKernelGGL((k_gemm_n8<A, C, W>), grid, block, lds, st, g)
   const int grouped = g.expert_offsets != nullptr;
-  if (eight) {
-    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM8(1, 1); else FP4_GEMM8(1, 0); }
-    else { if (g.c_is_bf16) FP4_GEMM8(0, 1); else FP4_GEMM8(0, 0); }
+  if (wide16) {
+#define FP4_GEMM16(A, C) hipLaunchKernelGGL((k_gemm_w16<A, C>), grid, block, lds, st, g)
+    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM16(1, 1); else FP4_GEMM16(1, 0); }
+    else { if (g.c_is_bf16) FP4_GEMM16(0, 1); else FP4_GEMM16(0, 0); }
+#undef FP4_GEMM16
   } else if (g.w_e4m3) {
     if (g.c_is_bf16) FP4_GEMMN8(0, 1, 1); else FP4_GEMMN8(0, 0, 1);
   } else if (narrow) {
@@ -736,7 +740,6 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     else { if (grouped) FP4_GEMM(0, 0, 1, 0); else FP4_GEMM(0, 0, 0, 0); }
   }
 #undef FP4_GEMMN8
-#undef FP4_GEMM8
 #undef FP4_GEMM
   return hipGetLastError();
 }

@@ -106,19 +106,19 @@ def test_gemm_small_shapes(act, m, n, k):
 
 
 @pytest.mark.parametrize("act", [16, 8, 4])
-def test_gemm_eight_wave_tiles_ragged(act):
+def test_gemm_wide_512_tiles_ragged(act):
     """Small products take the narrow 64 x 128 tile; this shape (2043 x 4080: 32 x 8 tiles
-    of 64 x 512, the last row and column tiles ragged) is large enough for the 8-wave
+    of 64 x 512, the last row and column tiles ragged) is large enough for the 16-wave
     64 x 512 form."""
     m, n, k = 2043, 4080, 256
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert -(-m // 64) * -(-n // 512) >= cus, "shape no longer selects the 8-wave tile"
+    assert -(-m // 64) * -(-n // 512) >= cus, "shape no longer selects the 64 x 512 tile"
     rng = np.random.default_rng(310 + act)
     a = rng.standard_normal((m, k)).astype(np.float32)
     a[:, rng.choice(k, 3, replace=False)] *= 50
     a = workloads.to_bf16_values(a)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
-    print(f"[case] gemm 8-wave tiles {ACTS[act]} m={m} n={n} k={k}", flush=True)
+    print(f"[case] gemm 64x512 tiles {ACTS[act]} m={m} n={n} k={k}", flush=True)
     wq = _wq(w)
     ad = to_device_bf16(a)
     ref = _oracle_c(a.astype(np.float64), w, act)
@@ -128,7 +128,7 @@ def test_gemm_eight_wave_tiles_ragged(act):
 
 @pytest.mark.parametrize("act", [16, 4])
 def test_gemm_wide_tiles_large_k_sampled(act):
-    """At k = 13312 (52 groups) the 8-wave form's macro-scale table no longer fits its LDS,
+    """At k = 13312 (52 groups) the 64 x 512 form's macro-scale table no longer fits its LDS,
     so a large dense product (1040 x 8192: 17 x 32 tiles of 64 x 256, the last row tile
     ragged) runs the 4-wave 64 x 256 form; checked on sampled outputs, the last row and
     column tiles among them."""
