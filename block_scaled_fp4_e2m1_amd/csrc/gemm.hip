@@ -13,9 +13,9 @@
 // Tiling: waves side by side along n, each owning 64 rows x 16 NI weight rows as 4 x NI
 // tiles of v_mfma_f32_16x16x32_{f16,bf16}. Large dense products run 16 waves of 32
 // columns (64 x 512 per workgroup, one per CU); small ones 8 waves of 16 columns (64 x 128,
-// two per CU); grouped ones 4 waves of 64 columns (64 x 256, two per CU). More waves per
-// SIMD hide more of the pipeline's latency, and a wider workgroup copies each activation
-// tile into LDS once for more weight columns.
+// two per CU); grouped ones 8 waves of 32 columns (64 x 256, two per CU). Every form runs
+// four waves per SIMD, which hides more of the pipeline's latency than two, and a wider
+// workgroup copies each activation tile into LDS once for more weight columns.
 // Weight fragments come straight from the tiled layout (each lane's 16 bytes are one
 // MFMA operand row for four k-steps); activation fragments are 16-byte row pieces.
 //
@@ -152,16 +152,15 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 }
 
 // ---------------------------------------------------------------------------------
-// Main product kernel. Workgroup: waves side by side along n (4, 8 or 16 by weight mode);
+// Main product kernel. Workgroup: waves side by side along n (8 or 16 by weight mode);
 // tile 64 rows x 16 NI weight rows per wave; each wave owns a 64 x 16 NI block as 4 x NI
-// MFMA tiles, so every weight fragment is decoded by exactly one wave. The 4-wave form is
-// sized for two workgroups per CU (two waves per SIMD: at most 256 registers and ~80 KB of
-// LDS each); the 8- and 16-wave forms run four waves per SIMD (at most 128 registers).
-// However many waves, the 64-row activation tile of a stage is copied once per workgroup:
-// with 8 or 16 waves each wave moves part of one 16-row slice.
+// MFMA tiles, so every weight fragment is decoded by exactly one wave. Four waves per
+// SIMD (at most 128 registers): two 8-wave workgroups or one 16-wave workgroup per CU.
+// The 64-row activation tile of a stage is copied once per workgroup, each wave moving
+// part of one 16-row slice.
 // The k loop runs in stages of half a 256-column group:
 //   - the activation tile (64 x 128, 16 KB, MFMA-fragment order) and the weight codes
-//     (4 waves x 4 row blocks x 1 KB, contiguous in the tiled layout) are copied into LDS
+//     (NI row blocks x 1 KB per wave, contiguous in the tiled layout) are copied into LDS
 //     by LDS-DMA, double-buffered in separate LDS objects, one stage ahead;
 //   - micro-scales of the next group are prefetched into registers;
 //   - per-row activation factors and the tile's macro-scales for every group are
@@ -201,22 +200,22 @@ size_t gemm_dynamic_lds(int groups, int bn = 256) {
 }
 
 // Weight-side shape of the pipeline, by weight mode WM:
-//   0  E2M1, 4 row blocks of 16 weight rows per wave (workgroup tile 64 x 256), one 1 KB
-//      LDS-DMA piece per row block and stage;
+//   0  E2M1, 2 row blocks of 16 weight rows per wave and 8 waves (workgroup tile
+//      64 x 256), one 1 KB LDS-DMA piece per row block and stage: grouped products, and
+//      dense ones whose 64 x 512 tables do not fit LDS;
 //   1  E4M3 (W8A8), 1 row block per wave and 8 waves (tile 64 x 128), two 1 KB pieces
 //      per row block and stage, so the doubled weight bytes fit the same LDS buffers;
 //   2  E2M1 narrow, 1 row block per wave and 8 waves (tile 64 x 128): twice the
 //      workgroups of the wide grid and twice its waves per workgroup, for products whose
 //      wide grid cannot fill the chip;
 //   3  E2M1, 2 row blocks per wave and 16 waves (tile 64 x 512, one workgroup per CU):
-//      four waves per SIMD, and one activation stage feeds twice the weight columns of
-//      the 4-wave tile; dense products whose 64 x 512 grid still gives every CU a
-//      workgroup.
+//      one activation stage feeds twice the weight columns of mode 0; dense products
+//      whose 64 x 512 grid still gives every CU a workgroup.
 template <int WM>
 struct WShape {
   static constexpr bool E4M3 = WM == 1;
-  static constexpr int NI = WM == 0 ? 4 : WM == 3 ? 2 : 1;       // row blocks per wave
-  static constexpr int WAVES = WM == 0 ? 4 : WM == 3 ? 16 : 8;   // waves per workgroup
+  static constexpr int NI = (WM == 0 || WM == 3) ? 2 : 1;  // row blocks per wave
+  static constexpr int WAVES = WM == 3 ? 16 : 8;           // waves per workgroup
   static constexpr int BN = 16 * NI * WAVES;               // weight rows per workgroup
   static constexpr int kTile = E4M3 ? kTile8CodeBytes : kTileCodeBytes;
   static constexpr int kPieces = E4M3 ? 2 * NI : NI;  // 1 KB LDS-DMA pieces per wave and stage
@@ -448,8 +447,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   // Operand copies go through raw buffer resources: the per-lane byte offset is fixed for
   // the whole k loop and the per-stage part is a scalar offset, so the loop spends no
   // vector instructions on addresses. Reads past a resource's size return zero.
-  // ---- activation copies: wave w moves row tile mi = w % 4 (16 rows); with 8 or 16 waves
-  // the row tile's 4 pieces per stage are split over its 2 or 4 waves ----
+  // ---- activation copies: wave w moves row tile mi = w % 4 (16 rows); the row tile's 4
+  // pieces per stage are split over its 2 (8 waves) or 4 (16 waves) waves ----
   const uint16_t* a16 = static_cast<const uint16_t*>(args.a);
   constexpr int kAPieces = 16 / kWaves;  // per wave and stage
   const int a_mi = wave & 3, a_t0 = (wave >> 2) * kAPieces;
@@ -626,16 +625,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     }
   }
 }
-// Kernels: the 4-wave wide form runs two workgroups per CU, the 8-wave narrow forms (E2M1
-// and E4M3) two, the 16-wave wide form one.
+// Kernels: the 8-wave forms run two workgroups per CU, the 16-wave form one; either way
+// four waves per SIMD.
 template <int A_BF16, int C_BF16, int GROUPED, int WM>
-__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs args) {
+__global__ __launch_bounds__(512, 2) void k_gemm(GemmArgs args) {
   gemm_body<A_BF16, C_BF16, GROUPED, WM>(args);
-}
-
-template <int A_BF16, int C_BF16, int WM>
-__global__ __launch_bounds__(512, 2) void k_gemm_n8(GemmArgs args) {
-  gemm_body<A_BF16, C_BF16, 0, WM>(args);
 }
 
 template <int A_BF16, int C_BF16>
@@ -717,10 +711,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const int64_t tiles_n = (g.n + bn - 1) / bn;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(wide16 ? 1024 : (narrow || g.w_e4m3) ? 512 : 256);
+  const dim3 grid((unsigned)blocks), block(wide16 ? 1024 : 512);
   const size_t lds = gemm_dynamic_lds((int)(g.k >> 8), (int)bn);
 #define FP4_GEMM(A, C, G, W) hipLaunchKernelGGL((k_gemm<A, C, G, W>), grid, block, lds, st, g)
-#define FP4_GEMMN8(A, C, W) hipLaunchKernelGGL((k_gemm_n8<A, C, W>), grid, block, lds, st, g)
   const int grouped = g.expert_offsets != nullptr;
   if (wide16) {
 #define FP4_GEMM16(A, C) hipLaunchKernelGGL((k_gemm_w16<A, C>), grid, block, lds, st, g)
@@ -728,10 +721,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     else { if (g.c_is_bf16) FP4_GEMM16(0, 1); else FP4_GEMM16(0, 0); }
 #undef FP4_GEMM16
   } else if (g.w_e4m3) {
-    if (g.c_is_bf16) FP4_GEMMN8(0, 1, 1); else FP4_GEMMN8(0, 0, 1);
+    if (g.c_is_bf16) FP4_GEMM(0, 1, 0, 1); else FP4_GEMM(0, 0, 0, 1);
   } else if (narrow) {
-    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMMN8(1, 1, 2); else FP4_GEMMN8(1, 0, 2); }
-    else { if (g.c_is_bf16) FP4_GEMMN8(0, 1, 2); else FP4_GEMMN8(0, 0, 2); }
+    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM(1, 1, 0, 2); else FP4_GEMM(1, 0, 0, 2); }
+    else { if (g.c_is_bf16) FP4_GEMM(0, 1, 0, 2); else FP4_GEMM(0, 0, 0, 2); }
   } else if (g.a_is_bf16) {
     if (g.c_is_bf16) { if (grouped) FP4_GEMM(1, 1, 1, 0); else FP4_GEMM(1, 1, 0, 0); }
     else { if (grouped) FP4_GEMM(1, 0, 1, 0); else FP4_GEMM(1, 0, 0, 0); }
@@ -739,7 +732,6 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     if (g.c_is_bf16) { if (grouped) FP4_GEMM(0, 1, 1, 0); else FP4_GEMM(0, 1, 0, 0); }
     else { if (grouped) FP4_GEMM(0, 0, 1, 0); else FP4_GEMM(0, 0, 0, 0); }
   }
-#undef FP4_GEMMN8
 #undef FP4_GEMM
   return hipGetLastError();
 }
