@@ -193,10 +193,19 @@ __shared__ uint4 g_w0[kWStage];
 __shared__ uint4 g_w1[kWStage];
 __shared__ uint4 g_w0x[2 * kWStage];  // the 16-wave form: [wave 16][piece 2][64]
 __shared__ uint4 g_w1x[2 * kWStage];
+__shared__ uint4 g_adummy[2 * 64];  // the 10-wave form: target of its two spare waves' copies
+// the 10-wave form's stage ring has four slots: two more activation and weight buffers
+constexpr int kW10Slots = 10 * 64;  // 16-byte chunks: [wave 10][piece 1][64]
+__shared__ uint4 g_a2[kAStage];
+__shared__ uint4 g_a3[kAStage];
+__shared__ uint4 g_w2[kW10Slots];
+__shared__ uint4 g_w3[kW10Slots];
+constexpr size_t kW10StaticLds = (4 * kAStage + 2 * kWStage + 2 * kW10Slots + 2 * 64) * 16;
 
-// dynamic LDS: float sa[G][64] then uint16 mw[BN/16][G][16]
+// dynamic LDS: float sa[G][64] then uint16 mw[BN/16][G][16], the latter rounded up to the
+// 256-byte pieces it is copied in
 size_t gemm_dynamic_lds(int groups, int bn = 256) {
-  return (size_t)groups * kBM * 4 + (size_t)(bn / 16) * groups * 16 * 2;
+  return (size_t)groups * kBM * 4 + (((size_t)(bn / 16) * groups * 16 * 2 + 255) & ~(size_t)255);
 }
 
 // Weight-side shape of the pipeline, by weight mode WM:
@@ -210,16 +219,40 @@ size_t gemm_dynamic_lds(int groups, int bn = 256) {
 //      wide grid cannot fill the chip;
 //   3  E2M1, 2 row blocks per wave and 16 waves (tile 64 x 512, one workgroup per CU):
 //      one activation stage feeds twice the weight columns of mode 0; dense products
-//      whose 64 x 512 grid still gives every CU a workgroup.
+//      whose 64 x 512 grid still gives every CU a workgroup;
+//   4  E2M1, 1 row block per wave and 10 waves (tile 64 x 160, one workgroup per CU):
+//      narrow products whose 64 x 128 grid would give some CUs two workgroups while the
+//      64 x 160 grid gives each at most one (512 x 5120: 256 tiles instead of 320).
 template <int WM>
 struct WShape {
   static constexpr bool E4M3 = WM == 1;
   static constexpr int NI = (WM == 0 || WM == 3) ? 2 : 1;  // row blocks per wave
-  static constexpr int WAVES = WM == 3 ? 16 : 8;           // waves per workgroup
+  static constexpr int WAVES = WM == 3 ? 16 : WM == 4 ? 10 : 8;  // waves per workgroup
   static constexpr int BN = 16 * NI * WAVES;               // weight rows per workgroup
   static constexpr int kTile = E4M3 ? kTile8CodeBytes : kTileCodeBytes;
   static constexpr int kPieces = E4M3 ? 2 * NI : NI;  // 1 KB LDS-DMA pieces per wave and stage
+  static constexpr int kRing = WM == 4 ? 4 : 2;       // stage buffers (copies run kRing - 1 ahead)
 };
+
+// Activation and weight buffers of ring slot B (distinct objects, so the compiler can tell
+// the slot being read from the slots being filled).
+template <int B>
+__device__ __forceinline__ uint4* a_slot() {
+  if constexpr (B == 0) return g_a0;
+  else if constexpr (B == 1) return g_a1;
+  else if constexpr (B == 2) return g_a2;
+  else return g_a3;
+}
+template <int WM, int B>
+__device__ __forceinline__ uint4* w_slot() {
+  if constexpr (WM == 3) {
+    if constexpr (B == 0) return g_w0x;
+    else return g_w1x;
+  } else if constexpr (B == 0) return g_w0;
+  else if constexpr (B == 1) return g_w1;
+  else if constexpr (B == 2) return g_w2;
+  else return g_w3;
+}
 
 template <int A_BF16, int WM>
 struct StepOperands {
@@ -384,16 +417,16 @@ __device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
 template <int A_BF16, int C_BF16, int GROUPED, int WM>
 __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   static_assert(WM != 1 || (!A_BF16 && !GROUPED), "E4M3 weights: dense, FP16 activation operand");
-  static_assert(WM != 3 || !GROUPED, "the 16-wave form is dense");
+  static_assert((WM != 3 && WM != 4) || !GROUPED, "the 16- and 10-wave forms are dense");
   constexpr int NI = WShape<WM>::NI, BN = WShape<WM>::BN, kTile = WShape<WM>::kTile;
   constexpr int kWaves = WShape<WM>::WAVES;
-  uint4* const w_buf0 = WM == 3 ? g_w0x : g_w0;
-  uint4* const w_buf1 = WM == 3 ? g_w1x : g_w1;
+  constexpr int kRing = WShape<WM>::kRing;
   static_assert(kWaves * WShape<WM>::kPieces * 64 <= (WM == 3 ? 2 : 1) * kWStage, "weight slots");
   constexpr int kPieces = WShape<WM>::kPieces;
   constexpr bool kE4M3 = WShape<WM>::E4M3;
   extern __shared__ uint8_t g_dyn[];
   const int groups = (int)(args.k >> 8);
+  if (kRing == 4 && (groups & 1)) return;  // the four-slot ring runs four stages per pass
   const int64_t n = args.n;
   const int64_t nblocks = n >> 4;
   const int tiles_n = (int)((n + BN - 1) / BN);
@@ -450,15 +483,20 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   // ---- activation copies: wave w moves row tile mi = w % 4 (16 rows); the row tile's 4
   // pieces per stage are split over its 2 (8 waves) or 4 (16 waves) waves ----
   const uint16_t* a16 = static_cast<const uint16_t*>(args.a);
-  constexpr int kAPieces = 16 / kWaves;  // per wave and stage
-  const int a_mi = wave & 3, a_t0 = (wave >> 2) * kAPieces;
+  // The 10-wave form copies with waves 0..7 as the 8-wave forms do; waves 8 and 9 issue the
+  // same two copies through an empty resource (zeros, no memory traffic) into a dummy
+  // buffer, so that every wave runs the same code and wait counts.
+  constexpr int kCopyWaves = kWaves == 10 ? 8 : kWaves;
+  constexpr int kAPieces = 16 / kCopyWaves;  // per wave and stage
+  const bool a_spare = kWaves == 10 && wave >= kCopyWaves;  // wave-uniform
+  const int a_mi = wave & 3, a_t0 = a_spare ? 0 : (wave >> 2) * kAPieces;
   int64_t a_src_row = min(row_begin + a_mi * 16 + l16, row_end - 1);
   if (GROUPED && args.row_token) a_src_row = args.row_token[a_src_row];
   // gathered rows are addressed from the start of A (the launcher keeps A under 4 GiB);
   // otherwise from the workgroup's first row
   const int64_t a_base_row = (GROUPED && args.row_token) ? 0 : row_begin;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a16 + a_base_row * args.lda), (short)0, (int)0xFFFFFFFF, kRsrcWord3);
+      (void*)(a16 + a_base_row * args.lda), (short)0, a_spare ? 0 : (int)0xFFFFFFFF, kRsrcWord3);
   const uint32_t a_voff = (uint32_t)(((a_src_row - a_base_row) * args.lda + 8 * q) * 2);
 
   // ---- weights: NI row blocks (16 columns each) per wave, consecutive in the tiled layout ----
@@ -475,21 +513,29 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
       (void*)(args.micro + wb0 * groups * kTileMicroBytes), (short)0,
       (int)min(w_tiles_left * kTileMicroBytes, (int64_t)0xFFFFFFFF), kRsrcWord3);
   const uint32_t mu_voff = (uint32_t)((q >> 1) * 128 + l16 * 8);
-  auto copy_stage = [&](uint4* abuf, uint4* wbuf, int s) {  // stage s = 2 g + h
+  // A copy for a stage past the last one (four-slot ring) goes through empty resources:
+  // zeros into a free slot, no memory traffic, the same wait counts.
+  const __amdgpu_buffer_rsrc_t a_none = __builtin_amdgcn_make_buffer_rsrc((void*)a16, (short)0, 0, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t w_none =
+      __builtin_amdgcn_make_buffer_rsrc((void*)args.codes, (short)0, 0, kRsrcWord3);
+  auto copy_stage = [&](uint4* abuf, uint4* wbuf, int s, bool past) {  // stage s = 2 g + h
     const int g = s >> 1, h = s & 1;
     const uint32_t a_soff = (uint32_t)s * (kStageK * 2);
+    const __amdgpu_buffer_rsrc_t ar = past ? a_none : a_rsrc;
+    const __amdgpu_buffer_rsrc_t wr = past ? w_none : w_rsrc;
 #pragma unroll
     for (int tt = 0; tt < kAPieces; ++tt) {
       const int t = a_t0 + tt;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(abuf + (a_mi * 4 + t) * 64), 16,
-                                               a_voff, a_soff + 64 * t, 0, 0);
+      uint4* adst = abuf + (a_mi * 4 + t) * 64;
+      if constexpr (kWaves == 10) adst = a_spare ? g_adummy + tt * 64 : adst;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void_ptr)adst, 16, a_voff, a_soff + 64 * t, 0, 0);
     }
     // piece d: row block d (E2M1) or d / 2, half d % 2 of the stage's 2 KB (E4M3)
 #pragma unroll
     for (int d = 0; d < kPieces; ++d) {
       const int ni = kE4M3 ? d >> 1 : d;
       const uint32_t soff = (uint32_t)((ni * groups + g) * kTile + h * (kTile / 2) + (kE4M3 ? (d & 1) * 1024 : 0));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(wbuf + (wave * kPieces + d) * 64), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void_ptr)(wbuf + (wave * kPieces + d) * 64), 16,
                                                (uint32_t)lane * 16, soff, 0, 0);
     }
   };
@@ -537,13 +583,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
 
   uint2 mu_cur[4], mu_nxt[4];
   const int stages = 2 * groups;
-  copy_stage(g_a0, w_buf0, 0);
+  // Two slots: stage 0, its micro-scales, wait for all. Four slots: stages 0 and 1, the
+  // micro-scales, stage 2, wait for all but stage 2, so that every stage later finds the
+  // same loads younger than the copies it waits for (see run_stage).
+  copy_stage(a_slot<0>(), w_slot<WM, 0>(), 0, false);
+  if constexpr (kRing == 4) copy_stage(a_slot<1>(), w_slot<WM, 1>(), 1, false);
   __builtin_amdgcn_sched_barrier(0);
   load_micro(mu_cur, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kRing == 4) copy_stage(a_slot<2>(), w_slot<WM, 2>(), 2, false);
   // stage 0's code words and step-0 weight fragments (the wave's own copies)
   uint4 cw[4];
   typename OpTraits<A_BF16>::frag wf0[NI];
-  __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<kRing == 4 ? kAPieces + kPieces : 0>::value);
   if (!A_BF16) {
     // row factors [g][row] -> ratios f_g / f_{g+1} (last group: f_{G-1}), in place; each
     // lane of wave 0 walks one row upwards in g, reading f_{g+1} before it is replaced
@@ -558,7 +610,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     }
   }
 #pragma unroll
-  for (int d = 0; d < kPieces; ++d) cw[d] = w_buf0[(wave * kPieces + d) * 64 + lane];
+  for (int d = 0; d < kPieces; ++d) cw[d] = w_slot<WM, 0>()[(wave * kPieces + d) * 64 + lane];
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
     wf0[ni] = weight_frag<A_BF16, WM, 0>(cw, ni, OpTraits<A_BF16>::micro_operand(mu_cur[ni].x & 0xFFu));
@@ -577,32 +629,53 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   }
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) resc.rw[ni] = 1.0f;
-  auto run_stage = [&](auto h_const, const uint4* abuf, uint4* nabuf, uint4* nwbuf, int s) {
-    constexpr int H = decltype(h_const)::value;
+  // Stage s reads ring slot B = s % kRing and first issues the copies of stage
+  // s + kRing - 1 into the slot stage s - 1 used (free after the barrier). Its last step
+  // waits for stage s + 1's copies, with these loads younger than them:
+  //   two slots:  the micro-scale loads of stage s (H == 0 stages only);
+  //   four slots: the copies of stages s + 2 and s + 3 and the micro-scale loads of
+  //               stages s - 2 .. s (two H == 0 stages when H == 0, else one).
+  auto run_stage = [&](auto h_const, auto b_const, int s) {
+    constexpr int H = decltype(h_const)::value, B = decltype(b_const)::value;
+    constexpr int kWait = kRing == 2 ? (H == 0 ? NI : 0) : 2 * (kAPieces + kPieces) + (H == 0 ? 2 : 1) * NI;
     __syncthreads();
-    if (s + 1 < stages) copy_stage(nabuf, nwbuf, s + 1);
+    if constexpr (kRing == 2) {
+      if (s + 1 < stages) copy_stage(a_slot<(B + 1) % 2>(), w_slot<WM, (B + 1) % 2>(), s + 1, false);
+    } else {
+      copy_stage(a_slot<(B + 3) % 4>(), w_slot<WM, (B + 3) % 4>(), min(s + 3, stages - 1), s + 3 >= stages);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    // (unconditional in H == 0 stages, the last group re-reading its own, so that exactly
-    // NI loads follow the copies when last_step waits for them; the count holds because
-    // every iteration runs this same code: in a separately compiled last iteration these
-    // loads would be dead, the compiler would drop them, and the wait would let copies
-    // through unfinished)
+    // (unconditional in H == 0 stages, the last group re-reading its own, so that the
+    // count of loads younger than the awaited copies is fixed; it holds because every
+    // iteration runs this same code: in a separately compiled last iteration these loads
+    // would be dead, the compiler would drop them, and the wait would let copies through
+    // unfinished)
     if (H == 0) load_micro(mu_nxt, min((s >> 1) + 1, groups - 1));
     __builtin_amdgcn_sched_barrier(0);
     // next stage: same group (H == 0: micro-scale word 1 of mu_cur) or the next group
-    // (H == 1: word 0 of mu_nxt); the H == 0 stage's NI micro-scale loads may stay in
-    // flight
-    compute_stage<A_BF16, WM, H == 0, H == 1, H == 0 ? NI : 0>(
-        abuf, cw, wf0, wave, lane, mu_cur, H, x, [&](Rescale<WM>& rr) { ratios_after(s >> 1, rr); }, resc,
-        nwbuf, H == 0 ? mu_cur : mu_nxt, 1 - H);
+    // (H == 1: word 0 of mu_nxt)
+    compute_stage<A_BF16, WM, H == 0, H == 1, kWait>(
+        a_slot<B>(), cw, wf0, wave, lane, mu_cur, H, x, [&](Rescale<WM>& rr) { ratios_after(s >> 1, rr); },
+        resc, w_slot<WM, (B + 1) % kRing>(), H == 0 ? mu_cur : mu_nxt, 1 - H);
     if (H == 1) {
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) mu_cur[ni] = mu_nxt[ni];
     }
   };
-  for (int s = 0; s < stages; s += 2) {
-    run_stage(std::integral_constant<int, 0>{}, g_a0, g_a1, w_buf1, s);
-    run_stage(std::integral_constant<int, 1>{}, g_a1, g_a0, w_buf0, s + 1);
+  typedef std::integral_constant<int, 0> C0;
+  typedef std::integral_constant<int, 1> C1;
+  if constexpr (kRing == 2) {
+    for (int s = 0; s < stages; s += 2) {
+      run_stage(C0{}, C0{}, s);
+      run_stage(C1{}, C1{}, s + 1);
+    }
+  } else {
+    for (int s = 0; s < stages; s += 4) {  // stages % 4 == 0 (checked above)
+      run_stage(C0{}, C0{}, s);
+      run_stage(C1{}, C1{}, s + 1);
+      run_stage(C0{}, std::integral_constant<int, 2>{}, s + 2);
+      run_stage(C1{}, std::integral_constant<int, 3>{}, s + 3);
+    }
   }
 
   // ---- apply the final factors, store ----
@@ -626,7 +699,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   }
 }
 // Kernels: the 8-wave forms run two workgroups per CU, the 16-wave form one; either way
-// four waves per SIMD.
+// four waves per SIMD. The 10-wave form runs one workgroup per CU (three waves on two
+// SIMDs, two on the others).
 template <int A_BF16, int C_BF16, int GROUPED, int WM>
 __global__ __launch_bounds__(512, 2) void k_gemm(GemmArgs args) {
   gemm_body<A_BF16, C_BF16, GROUPED, WM>(args);
@@ -635,6 +709,11 @@ __global__ __launch_bounds__(512, 2) void k_gemm(GemmArgs args) {
 template <int A_BF16, int C_BF16>
 __global__ __launch_bounds__(1024, 1) void k_gemm_w16(GemmArgs args) {
   gemm_body<A_BF16, C_BF16, 0, 3>(args);
+}
+
+template <int A_BF16, int C_BF16>
+__global__ __launch_bounds__(640, 1) void k_gemm_w10(GemmArgs args) {
+  gemm_body<A_BF16, C_BF16, 0, 4>(args);
 }
 
 // float32 activations: one thread per output, exact weight values, float32 FMA.
@@ -707,11 +786,26 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const bool wide16 = !g.w_e4m3 && !g.expert_offsets && !narrow &&
                      tiles_m * ((g.n + WShape<3>::BN - 1) / WShape<3>::BN) >= cus &&
                      gemm_dynamic_lds((int)(g.k >> 8), WShape<3>::BN) <= 160 * 1024 - 96 * 1024;
-  const int64_t bn = g.w_e4m3 ? WShape<1>::BN : narrow ? WShape<2>::BN : wide16 ? WShape<3>::BN : WShape<0>::BN;
+  // narrow products take the 10-wave 64 x 160 form when it puts fewer weight columns on
+  // the busiest SIMD: 48 per 64 x 160 tile on a CU (3 waves of 16), 32 per 64 x 128
+  // tile (two workgroups of 8 waves share a CU)
+  bool w10 = false;
+  if (narrow) {
+    const int64_t t128 = tiles_m * ((g.n + WShape<2>::BN - 1) / WShape<2>::BN);
+    const int64_t t160 = tiles_m * ((g.n + WShape<4>::BN - 1) / WShape<4>::BN);
+    const int groups = (int)(g.k >> 8);
+    w10 = 48 * ((t160 + cus - 1) / cus) < 32 * ((t128 + cus - 1) / cus) && groups % 2 == 0 &&
+          kW10StaticLds + gemm_dynamic_lds(groups, WShape<4>::BN) <= 160 * 1024;
+  }
+  const int64_t bn = g.w_e4m3 ? WShape<1>::BN
+                     : w10    ? WShape<4>::BN
+                     : narrow ? WShape<2>::BN
+                     : wide16 ? WShape<3>::BN
+                              : WShape<0>::BN;
   const int64_t tiles_n = (g.n + bn - 1) / bn;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(wide16 ? 1024 : 512);
+  const dim3 grid((unsigned)blocks), block(wide16 ? 1024 : w10 ? 640 : 512);
   const size_t lds = gemm_dynamic_lds((int)(g.k >> 8), (int)bn);
 #define FP4_GEMM(A, C, G, W) hipLaunchKernelGGL((k_gemm<A, C, G, W>), grid, block, lds, st, g)
   const int grouped = g.expert_offsets != nullptr;
@@ -720,6 +814,11 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM16(1, 1); else FP4_GEMM16(1, 0); }
     else { if (g.c_is_bf16) FP4_GEMM16(0, 1); else FP4_GEMM16(0, 0); }
 #undef FP4_GEMM16
+  } else if (w10) {
+#define FP4_GEMM10(A, C) hipLaunchKernelGGL((k_gemm_w10<A, C>), grid, block, lds, st, g)
+    if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM10(1, 1); else FP4_GEMM10(1, 0); }
+    else { if (g.c_is_bf16) FP4_GEMM10(0, 1); else FP4_GEMM10(0, 0); }
+#undef FP4_GEMM10
   } else if (g.w_e4m3) {
     if (g.c_is_bf16) FP4_GEMM(0, 1, 0, 1); else FP4_GEMM(0, 0, 0, 1);
   } else if (narrow) {

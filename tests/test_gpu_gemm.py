@@ -126,11 +126,34 @@ def test_gemm_wide_512_tiles_ragged(act):
     bf16_gate(bf16_values(fp4.gemm_w4aX(act, ad, wq)), oracle.formats.bf16_round(ref))
 
 
+@pytest.mark.parametrize("act", [4, 8, 16])
+@pytest.mark.parametrize("m,n,k", [(500, 4800, 1024), (505, 5008, 1536)])
+def test_gemm_ten_wave_ring_ragged(m, n, k, act):
+    """Products whose 64 x 128 grid would put two workgroups on some CUs while the 64 x 160
+    grid fits one per CU run the 10-wave form with its four-slot stage ring. Here 4 and 6
+    groups (the ring's copies run past the last stage), a ragged last row tile, and in
+    5008 a last column tile of 48 columns."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tm = -(-m // 64)
+    assert tm * -(-n // 128) > cus >= tm * -(-n // 160), "shape no longer selects the 10-wave form"
+    rng = np.random.default_rng(330 + act + k)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    a[:, rng.choice(k, 3, replace=False)] *= 50
+    a = workloads.to_bf16_values(a)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    print(f"[case] gemm 10-wave ring {ACTS[act]} m={m} n={n} k={k}", flush=True)
+    wq = _wq(w)
+    ad = to_device_bf16(a)
+    ref = _oracle_c(a.astype(np.float64), w, act)
+    f32_gate(host(fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32)), ref)
+    bf16_gate(bf16_values(fp4.gemm_w4aX(act, ad, wq)), oracle.formats.bf16_round(ref))
+
+
 @pytest.mark.parametrize("act", [16, 4])
 def test_gemm_wide_tiles_large_k_sampled(act):
     """At k = 13312 (52 groups) the 64 x 512 form's macro-scale table no longer fits its LDS,
     so a large dense product (1040 x 8192: 17 x 32 tiles of 64 x 256, the last row tile
-    ragged) runs the 4-wave 64 x 256 form; checked on sampled outputs, the last row and
+    ragged) runs the 8-wave 64 x 256 form; checked on sampled outputs, the last row and
     column tiles among them."""
     m, n, k = 1040, 8192, 13312
     rng = np.random.default_rng(320 + act)
