@@ -201,6 +201,13 @@ __shared__ uint4 g_a3[kAStage];
 __shared__ uint4 g_w2[kW10Slots];
 __shared__ uint4 g_w3[kW10Slots];
 constexpr size_t kW10StaticLds = (4 * kAStage + 2 * kWStage + 2 * kW10Slots + 2 * 64) * 16;
+// the E4M3 10-wave form: two 1 KB pieces per wave, four weight slots of its own
+constexpr int kW10eSlots = 10 * 2 * 64;
+__shared__ uint4 g_we0[kW10eSlots];
+__shared__ uint4 g_we1[kW10eSlots];
+__shared__ uint4 g_we2[kW10eSlots];
+__shared__ uint4 g_we3[kW10eSlots];
+constexpr size_t kW10eStaticLds = (4 * kAStage + 4 * kW10eSlots + 2 * 64) * 16;
 
 // dynamic LDS: float sa[G][64] then uint16 mw[BN/16][G][16], the latter rounded up to the
 // 256-byte pieces it is copied in
@@ -222,16 +229,17 @@ size_t gemm_dynamic_lds(int groups, int bn = 256) {
 //      whose 64 x 512 grid still gives every CU a workgroup;
 //   4  E2M1, 1 row block per wave and 10 waves (tile 64 x 160, one workgroup per CU):
 //      narrow products whose 64 x 128 grid would give some CUs two workgroups while the
-//      64 x 160 grid gives each at most one (512 x 5120: 256 tiles instead of 320).
+//      64 x 160 grid gives each at most one (512 x 5120: 256 tiles instead of 320);
+//   5  E4M3, the same 10-wave 64 x 160 shape for W8A8 products of that kind.
 template <int WM>
 struct WShape {
-  static constexpr bool E4M3 = WM == 1;
+  static constexpr bool E4M3 = WM == 1 || WM == 5;
   static constexpr int NI = (WM == 0 || WM == 3) ? 2 : 1;  // row blocks per wave
-  static constexpr int WAVES = WM == 3 ? 16 : WM == 4 ? 10 : 8;  // waves per workgroup
+  static constexpr int WAVES = WM == 3 ? 16 : (WM == 4 || WM == 5) ? 10 : 8;  // waves per workgroup
   static constexpr int BN = 16 * NI * WAVES;               // weight rows per workgroup
   static constexpr int kTile = E4M3 ? kTile8CodeBytes : kTileCodeBytes;
   static constexpr int kPieces = E4M3 ? 2 * NI : NI;  // 1 KB LDS-DMA pieces per wave and stage
-  static constexpr int kRing = WM == 4 ? 4 : 2;       // stage buffers (copies run kRing - 1 ahead)
+  static constexpr int kRing = WAVES == 10 ? 4 : 2;  // stage buffers (copies run kRing - 1 ahead)
 };
 
 // Activation and weight buffers of ring slot B (distinct objects, so the compiler can tell
@@ -248,6 +256,11 @@ __device__ __forceinline__ uint4* w_slot() {
   if constexpr (WM == 3) {
     if constexpr (B == 0) return g_w0x;
     else return g_w1x;
+  } else if constexpr (WM == 5) {
+    if constexpr (B == 0) return g_we0;
+    else if constexpr (B == 1) return g_we1;
+    else if constexpr (B == 2) return g_we2;
+    else return g_we3;
   } else if constexpr (B == 0) return g_w0;
   else if constexpr (B == 1) return g_w1;
   else if constexpr (B == 2) return g_w2;
@@ -416,12 +429,13 @@ __device__ __forceinline__ void compute_stage(const uint4* abuf, uint4 (&cw)[4],
 
 template <int A_BF16, int C_BF16, int GROUPED, int WM>
 __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
-  static_assert(WM != 1 || (!A_BF16 && !GROUPED), "E4M3 weights: dense, FP16 activation operand");
-  static_assert((WM != 3 && WM != 4) || !GROUPED, "the 16- and 10-wave forms are dense");
+  static_assert(!WShape<WM>::E4M3 || (!A_BF16 && !GROUPED), "E4M3 weights: dense, FP16 activation operand");
+  static_assert((WM != 3 && WM != 4 && WM != 5) || !GROUPED, "the 16- and 10-wave forms are dense");
   constexpr int NI = WShape<WM>::NI, BN = WShape<WM>::BN, kTile = WShape<WM>::kTile;
   constexpr int kWaves = WShape<WM>::WAVES;
   constexpr int kRing = WShape<WM>::kRing;
-  static_assert(kWaves * WShape<WM>::kPieces * 64 <= (WM == 3 ? 2 : 1) * kWStage, "weight slots");
+  constexpr int kSlotChunks = WM == 3 ? 2 * kWStage : WM == 4 ? kW10Slots : WM == 5 ? kW10eSlots : kWStage;
+  static_assert(kWaves * WShape<WM>::kPieces * 64 <= kSlotChunks, "weight slots");
   constexpr int kPieces = WShape<WM>::kPieces;
   constexpr bool kE4M3 = WShape<WM>::E4M3;
   extern __shared__ uint8_t g_dyn[];
@@ -716,6 +730,11 @@ __global__ __launch_bounds__(640, 1) void k_gemm_w10(GemmArgs args) {
   gemm_body<A_BF16, C_BF16, 0, 4>(args);
 }
 
+template <int C_BF16>
+__global__ __launch_bounds__(640, 1) void k_gemm_w10e(GemmArgs args) {
+  gemm_body<0, C_BF16, 0, 5>(args);
+}
+
 // float32 activations: one thread per output, exact weight values, float32 FMA.
 template <int C_BF16>
 __global__ __launch_bounds__(256) void k_gemm_f32act(const float* __restrict__ a, int64_t lda,
@@ -789,16 +808,19 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   // narrow products take the 10-wave 64 x 160 form when it puts fewer weight columns on
   // the busiest SIMD: 48 per 64 x 160 tile on a CU (3 waves of 16), 32 per 64 x 128
   // tile (two workgroups of 8 waves share a CU)
+  // (W8A8 products, whose E4M3 tile is always 64 x 128, likewise, with weight slots of
+  // twice the size)
   bool w10 = false;
-  if (narrow) {
+  if (narrow || (g.w_e4m3 && !g.expert_offsets)) {
     const int64_t t128 = tiles_m * ((g.n + WShape<2>::BN - 1) / WShape<2>::BN);
     const int64_t t160 = tiles_m * ((g.n + WShape<4>::BN - 1) / WShape<4>::BN);
     const int groups = (int)(g.k >> 8);
+    const size_t lds = (g.w_e4m3 ? kW10eStaticLds : kW10StaticLds) + gemm_dynamic_lds(groups, WShape<4>::BN);
     w10 = 48 * ((t160 + cus - 1) / cus) < 32 * ((t128 + cus - 1) / cus) && groups % 2 == 0 &&
-          kW10StaticLds + gemm_dynamic_lds(groups, WShape<4>::BN) <= 160 * 1024;
+          lds <= 160 * 1024;
   }
-  const int64_t bn = g.w_e4m3 ? WShape<1>::BN
-                     : w10    ? WShape<4>::BN
+  const int64_t bn = w10        ? WShape<4>::BN
+                     : g.w_e4m3 ? WShape<1>::BN
                      : narrow ? WShape<2>::BN
                      : wide16 ? WShape<3>::BN
                               : WShape<0>::BN;
@@ -814,6 +836,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM16(1, 1); else FP4_GEMM16(1, 0); }
     else { if (g.c_is_bf16) FP4_GEMM16(0, 1); else FP4_GEMM16(0, 0); }
 #undef FP4_GEMM16
+  } else if (w10 && g.w_e4m3) {
+    if (g.c_is_bf16) hipLaunchKernelGGL((k_gemm_w10e<1>), grid, block, lds, st, g);
+    else hipLaunchKernelGGL((k_gemm_w10e<0>), grid, block, lds, st, g);
   } else if (w10) {
 #define FP4_GEMM10(A, C) hipLaunchKernelGGL((k_gemm_w10<A, C>), grid, block, lds, st, g)
     if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM10(1, 1); else FP4_GEMM10(1, 0); }

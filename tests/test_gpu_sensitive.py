@@ -134,6 +134,25 @@ def test_gemm_w8a8_small_shapes(m, n, k):
     bf16_gate(bf16_values(fp4.gemm_w8a8(ad, wq)), oracle.formats.bf16_round(ref))
 
 
+@pytest.mark.parametrize("m,n,k", [(500, 4800, 1024), (505, 5008, 1536)])
+def test_gemm_w8a8_ten_wave_ring(m, n, k):
+    """W8A8 products whose 64 x 128 grid would put two workgroups on some CUs run the E4M3
+    10-wave 64 x 160 form with its four-slot stage ring: 4 and 6 groups (the ring's
+    copies run past the last stage), a ragged last row tile, a 48-column last tile."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tm = -(-m // 64)
+    assert tm * -(-n // 128) > cus >= tm * -(-n // 160), "shape no longer selects the 10-wave form"
+    rng = np.random.default_rng(440 + m + n + k)
+    a = _acts(rng, m, k)
+    w = _weights(rng, n, k)
+    print(f"[case] gemm_w8a8 10-wave ring m={m} n={n} k={k}", flush=True)
+    wq = fp4.quantize_fp4(_dev(w, torch.float32), elem=fp4.ELEM_E4M3, layout=fp4.LAYOUT_TILED)
+    ref = oracle.gemm_w8a8(a.astype(np.float64), oracle.quantize(w.astype(np.float64), "e4m3"))
+    ad = to_device_bf16(a)
+    f32_gate(host(fp4.gemm_w8a8(ad, wq, out_dtype=torch.float32)), ref)
+    bf16_gate(bf16_values(fp4.gemm_w8a8(ad, wq)), oracle.formats.bf16_round(ref))
+
+
 def test_gemm_w8a8_float32_activations():
     rng = np.random.default_rng(435)
     a = _acts(rng, 40, 512, torch.float32)
