@@ -9,7 +9,7 @@ Names follow the C ABI: ``quantize_fp4``, ``dequantize_fp4``, ``gemm_w4aX``,
 ``grouped_gemm_w4aX``, ``grouped_gemm_w4aX_gated``, ``moe_route``, ``moe_combine``,
 ``kv_cache_append``, ``attention_decode_fp4kv``, ``quantize_mxfp4``, ``gemm_mxfp4``,
 ``quantize_fp4_static``, ``act_macro_calibrate``, ``gemm_w4aX_static``, ``gemm_w8a8``,
-``fp4_workspace_bytes``, ``fp4_policy_select``.
+``repack_fp4``, ``fp4_workspace_bytes``, ``fp4_policy_select``, ``fp4_product_kernel``.
 """
 from __future__ import annotations
 
@@ -36,7 +36,7 @@ EXPORTED = ["quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
             "fp4_device_check", "fp4_kv_cache_bytes", "kv_cache_append",
             "attention_workspace_bytes", "attention_decode_fp4kv", "mxfp4_bytes",
             "quantize_mxfp4", "gemm_mxfp4", "quantize_fp4_static", "act_macro_calibrate",
-            "gemm_w4aX_static", "gemm_w8a8"]
+            "gemm_w4aX_static", "gemm_w8a8", "fp4_product_kernel", "repack_fp4"]
 KV_CODES, KV_MICRO, KV_MACRO = 0, 1, 2
 
 
@@ -106,10 +106,14 @@ def library() -> ctypes.CDLL:
     lib.act_macro_calibrate.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp]
     lib.gemm_w4aX_static.argtypes = [i32, vp, i32, i64, i64, vp, T, vp, i32, i64, vp, sz, vp]
     lib.gemm_w8a8.argtypes = [vp, i32, i64, i64, T, vp, i32, i64, vp, sz, vp]
+    lib.repack_fp4.argtypes = [T, i32, vp, vp, vp, vp]
+    lib.fp4_product_kernel.argtypes = [i32, i32, i64, i64, i64, i32, i32, i32]
+    lib.fp4_product_kernel.restype = ctypes.c_char_p
     for name in ("quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
                  "grouped_gemm_w4aX_gated", "moe_route", "moe_combine", "fp4_device_check",
                  "kv_cache_append", "attention_decode_fp4kv", "quantize_mxfp4", "gemm_mxfp4",
-                 "quantize_fp4_static", "act_macro_calibrate", "gemm_w4aX_static", "gemm_w8a8"):
+                 "quantize_fp4_static", "act_macro_calibrate", "gemm_w4aX_static", "gemm_w8a8",
+                 "repack_fp4"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -211,6 +215,17 @@ def act_macro_calibrate(x: torch.Tensor, amax: torch.Tensor, elem: int = ELEM_E2
     return macro
 
 
+def repack_fp4(q: QTensor, layout: int, out: QTensor | None = None) -> QTensor:
+    """The same quantized tensor in the other packed layout (a byte permutation)."""
+    r = out if out is not None else empty_qtensor(q.rows, q.k, q.elem, layout, q.codes.device)
+    if r.rows != q.rows or r.k != q.k or r.elem != q.elem or r.layout != layout:
+        raise ValueError("out does not match q in the requested layout")
+    ts = q.c_struct()
+    st = library().repack_fp4(ctypes.byref(ts), layout, _ptr(r.codes), _ptr(r.micro), _ptr(r.macro), _stream())
+    _check(st, "repack_fp4")
+    return r
+
+
 def dequantize_fp4(q: QTensor, dtype: torch.dtype = torch.float32,
                    out: torch.Tensor | None = None) -> torch.Tensor:
     y = out if out is not None else torch.empty(q.rows, q.k, dtype=dtype, device=q.codes.device)
@@ -234,6 +249,14 @@ def fp4_policy_select(mode: int, layer_flag: bool) -> int:
 
 def fp4_device_check() -> int:
     return int(library().fp4_device_check())
+
+
+def fp4_product_kernel(act: int, a_dtype: torch.dtype, m: int, n: int, k: int, grouped: bool = False,
+                       n_experts: int = 0, w_e4m3: bool = False) -> str | None:
+    """Name of the kernel form a product of this shape runs (None when it is refused)."""
+    r = library().fp4_product_kernel(act, _dtype_code(a_dtype), m, n, k, int(grouped), n_experts,
+                                     int(w_e4m3))
+    return None if r is None else r.decode()
 
 
 def _workspace(act: int, rows: int, n: int, k: int, device, workspace):

@@ -65,6 +65,16 @@ size_t act_workspace(int32_t act, int64_t rows, int64_t k) {
   return aq + (size_t)rows * (size_t)(k / 256) * 4;
 }
 
+// Launch limits of the matrix path a call takes (the activation pass over act_rows rows
+// for FP4_A4 / FP4_A8, then the product kernel), checked before anything is enqueued so
+// that a shape the kernels do not cover returns FP4_E_SHAPE with the stream untouched.
+fp4_status check_product(int32_t act, int64_t act_rows, int64_t m, int64_t n, int64_t k, bool grouped,
+                         int32_t n_experts, bool w_e4m3) {
+  if (!fp4lib::gemm_plan_ok(m, n, k, grouped ? 1 : 0, n_experts, w_e4m3 ? 1 : 0)) return FP4_E_SHAPE;
+  if (act != FP4_A16 && !fp4lib::quantize_grid_ok(act_rows, k)) return FP4_E_SHAPE;
+  return FP4_OK;
+}
+
 // Runs the activation pass when needed and fills the activation part of GemmArgs.
 // act_macro: static activation macro-scales (FP16 bits per group) or nullptr (dynamic).
 fp4_status prepare_activations(int32_t act, const void* a, int32_t a_dtype, int64_t rows,
@@ -114,6 +124,19 @@ const char* fp4_status_string(fp4_status s) {
 
 fp4_status fp4_device_check(void) { return check_device(); }
 
+const char* fp4_product_kernel(int32_t act, int32_t a_dtype, int64_t m, int64_t n, int64_t k, int32_t grouped,
+                               int32_t n_experts, int32_t w_e4m3) {
+  act = act_of(act);
+  if (!valid_act(act) || !valid_dtype(a_dtype) || m < 1 || n < 16 || n % 16 || k < 256 || k % 256) return nullptr;
+  if (w_e4m3 && (act != FP4_A8 || grouped)) return nullptr;
+  if (!grouped && !w_e4m3 && act == FP4_A16) {
+    if (a_dtype == FP4_F32) return m <= (int64_t)0xFFFFFF00 / n ? "k_gemm_f32act (one thread per output)" : nullptr;
+    if (fp4lib::gemv_supports(m, n, k)) return "k_gemv_bf16 (decode)";
+  }
+  if (grouped && act == FP4_A16 && a_dtype != FP4_BF16) return nullptr;
+  return fp4lib::gemm_kernel_name(m, n, k, grouped ? 1 : 0, n_experts, w_e4m3 ? 1 : 0);
+}
+
 int32_t fp4_policy_select(int32_t mode, int32_t layer_flag) {
   switch (mode) {
     case FP4_POLICY_Q4: return FP4_A4;
@@ -142,6 +165,7 @@ fp4_status quantize_impl(const void* x, int32_t x_dtype, int64_t rows, int64_t k
   if (layout != FP4_LAYOUT_CANONICAL && layout != FP4_LAYOUT_TILED) return FP4_E_MODE;
   if (rows < 1 || k < 256 || k % 256 || ldx < k) return FP4_E_SHAPE;
   if (layout == FP4_LAYOUT_TILED && rows % 16) return FP4_E_SHAPE;
+  if (!fp4lib::quantize_grid_ok(rows, k)) return FP4_E_SHAPE;
   if (!aligned16(x) || (ldx * (int64_t)dtype_size(x_dtype)) % 16 || !aligned16(codes) ||
       !aligned16(micro) || !aligned(macro, 2) || (macro_in && !aligned(macro_in, 2)))
     return FP4_E_ALIGN;
@@ -167,12 +191,32 @@ fp4_status quantize_fp4_static(const void* x, int32_t x_dtype, int64_t rows, int
   return quantize_impl(x, x_dtype, rows, k, ldx, elem, layout, macro_in, codes, micro, macro, stream);
 }
 
+fp4_status repack_fp4(const fp4_tensor* src, int32_t layout, void* codes, uint8_t* micro, uint16_t* macro,
+                      void* stream) {
+  if (!src || !src->codes || !src->micro || !src->macro || !codes || !micro || !macro) return FP4_E_NULL;
+  if (src->elem != FP4_ELEM_E2M1 && src->elem != FP4_ELEM_E4M3) return FP4_E_MODE;
+  if ((src->layout != FP4_LAYOUT_CANONICAL && src->layout != FP4_LAYOUT_TILED) ||
+      (layout != FP4_LAYOUT_CANONICAL && layout != FP4_LAYOUT_TILED))
+    return FP4_E_MODE;
+  if (layout == src->layout) return FP4_E_LAYOUT;
+  if (!fp4lib::repack_supports(src->rows, src->k, src->elem == FP4_ELEM_E4M3)) return FP4_E_SHAPE;
+  if (!aligned16(src->codes) || !aligned16(src->micro) || !aligned(src->macro, 2) || !aligned16(codes) ||
+      !aligned16(micro) || !aligned(macro, 2))
+    return FP4_E_ALIGN;
+  const fp4_status dev = check_device();
+  if (dev != FP4_OK) return dev;
+  return launched(fp4lib::launch_repack(static_cast<const uint8_t*>(src->codes), src->micro, src->macro,
+                                        static_cast<uint8_t*>(codes), micro, macro, src->rows, src->k,
+                                        src->elem == FP4_ELEM_E4M3, layout == FP4_LAYOUT_TILED,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 fp4_status act_macro_calibrate(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ldx,
                                int32_t elem, float* amax, uint16_t* macro, void* stream) {
   if (!x || !amax || !macro) return FP4_E_NULL;
   if (!valid_dtype(x_dtype)) return FP4_E_DTYPE;
   if (elem != FP4_ELEM_E2M1 && elem != FP4_ELEM_E4M3) return FP4_E_MODE;
-  if (rows < 1 || k < 256 || k % 256 || ldx < k) return FP4_E_SHAPE;
+  if (rows < 1 || k < 256 || k % 256 || ldx < k || k / 256 > 0x7FFFFFFF) return FP4_E_SHAPE;
   if (!aligned16(x) || (ldx * (int64_t)dtype_size(x_dtype)) % 16 || !aligned(amax, 4) || !aligned(macro, 2))
     return FP4_E_ALIGN;
   const fp4_status dev = check_device();
@@ -189,6 +233,7 @@ fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t
   if (q->layout != FP4_LAYOUT_CANONICAL && q->layout != FP4_LAYOUT_TILED) return FP4_E_MODE;
   if (q->rows < 1 || q->k < 256 || q->k % 256 || ldy < q->k) return FP4_E_SHAPE;
   if (q->layout == FP4_LAYOUT_TILED && q->rows % 16) return FP4_E_SHAPE;
+  if (!fp4lib::dequantize_grid_ok(q->rows, q->k)) return FP4_E_SHAPE;
   if (!aligned16(y) || (ldy * (int64_t)dtype_size(y_dtype)) % 16 || !aligned16(q->codes) ||
       !aligned(q->macro, 2))
     return FP4_E_ALIGN;
@@ -215,16 +260,25 @@ fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int
   const size_t need = act_workspace(act, m, k);
   if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return FP4_E_WORKSPACE;
+  // path: float32 activations (A16) -> one thread per output; A16 bf16 with m <= 8 -> the
+  // decode GEMV; everything else -> activation pass (A4 / A8) and the product kernel
+  const bool f32_path = act == FP4_A16 && a_dtype == FP4_F32;
+  const bool gemv_path = act == FP4_A16 && !f32_path && fp4lib::gemv_supports(m, n, k);
+  if (f32_path && m > (int64_t)0xFFFFFF00 / n) return FP4_E_SHAPE;
+  if (!f32_path && !gemv_path) {
+    const fp4_status lim = check_product(act, m, m, n, k, false, 0, false);
+    if (lim != FP4_OK) return lim;
+  }
   const fp4_status dev = check_device();
   if (dev != FP4_OK) return dev;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint8_t* codes = static_cast<const uint8_t*>(w->codes);
 
-  if (act == FP4_A16 && a_dtype == FP4_F32)
+  if (f32_path)
     return launched(fp4lib::launch_gemm_f32act(static_cast<const float*>(a), lda, m, k, codes,
                                                w->micro, w->macro, n, c, c_dtype == FP4_BF16,
                                                ldc, st));
-  if (act == FP4_A16 && fp4lib::gemv_supports(m, n, k))
+  if (gemv_path)
     return launched(fp4lib::launch_gemv_bf16(static_cast<const uint16_t*>(a), lda, m, k, codes,
                                              w->micro, w->macro, n, c, c_dtype == FP4_BF16,
                                              ldc, st));
@@ -253,7 +307,8 @@ fp4_status gemm_w4aX_static(int32_t act, const void* a, int32_t a_dtype, int64_t
   if (!valid_dtype(a_dtype) || !valid_dtype(c_dtype)) return FP4_E_DTYPE;
   const int64_t n = w->rows, k = w->k;
   if (m < 1 || lda < k || ldc < n) return FP4_E_SHAPE;
-  if (!fp4lib::gemm_supports(k)) return FP4_E_SHAPE;
+  const fp4_status lim = check_product(act, m, m, n, k, false, 0, false);
+  if (lim != FP4_OK) return lim;
   if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
   if (!aligned(c, dtype_size(c_dtype)) || !aligned(act_macro, 2)) return FP4_E_ALIGN;
   const size_t need = act_workspace(act, m, k);
@@ -284,7 +339,8 @@ fp4_status gemm_w8a8(const void* a, int32_t a_dtype, int64_t m, int64_t lda, con
   if (!valid_dtype(a_dtype) || !valid_dtype(c_dtype)) return FP4_E_DTYPE;
   const int64_t n = w->rows, k = w->k;
   if (m < 1 || lda < k || ldc < n) return FP4_E_SHAPE;
-  if (!fp4lib::gemm_supports(k)) return FP4_E_SHAPE;
+  const fp4_status lim = check_product(FP4_A8, m, m, n, k, false, 0, true);
+  if (lim != FP4_OK) return lim;
   if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
   if (!aligned(c, dtype_size(c_dtype))) return FP4_E_ALIGN;
   const size_t need = act_workspace(FP4_A8, m, k);
@@ -334,6 +390,10 @@ fp4_status grouped_gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_
   const size_t need = act_workspace(act, a_rows, k);
   if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return FP4_E_WORKSPACE;
+  if (total_rows > 0) {
+    const fp4_status lim = check_product(act, a_rows, total_rows, n, k, true, n_experts, false);
+    if (lim != FP4_OK) return lim;
+  }
   const fp4_status dev = check_device();
   if (dev != FP4_OK) return dev;
   if (total_rows == 0) return FP4_OK;
@@ -374,6 +434,10 @@ fp4_status grouped_gemm_w4aX_gated(int32_t act, const void* gate_up, int64_t row
   const size_t need = act_workspace(act, rows, k);
   if (rows > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return FP4_E_WORKSPACE;
+  if (rows > 0) {
+    const fp4_status lim = check_product(act, rows, rows, n, k, true, n_experts, false);
+    if (lim != FP4_OK) return lim;
+  }
   const fp4_status dev = check_device();
   if (dev != FP4_OK) return dev;
   if (rows == 0) return FP4_OK;
@@ -463,6 +527,8 @@ fp4_status quantize_mxfp4(const void* x, int32_t x_dtype, int64_t rows, int64_t 
   if (!x || !codes || !scales) return FP4_E_NULL;
   if (!valid_dtype(x_dtype)) return FP4_E_DTYPE;
   if (rows < 1 || k < 128 || k % 128 || ldx < k) return FP4_E_SHAPE;
+  // one thread per 32-element block (rows padded to 16), 256 per workgroup
+  if (fp4lib::mx_padded_rows(rows) > (int64_t)0x7FFFFFFF * 256 / (k / 32)) return FP4_E_SHAPE;
   if (!aligned16(x) || (ldx * (int64_t)dtype_size(x_dtype)) % 16 || !aligned16(codes)) return FP4_E_ALIGN;
   const fp4_status dev = check_device();
   if (dev != FP4_OK) return dev;
@@ -475,7 +541,9 @@ fp4_status gemm_mxfp4(const void* a_codes, const uint8_t* a_scales, int64_t m, c
                       void* stream) {
   if (!a_codes || !a_scales || !w_codes || !w_scales || !c) return FP4_E_NULL;
   if (!valid_dtype(c_dtype)) return FP4_E_DTYPE;
-  if (m < 1 || n < 1 || k < 128 || k % 128 || ldc < n || (m + 127) / 128 > 65535) return FP4_E_SHAPE;
+  if (m < 1 || n < 1 || k < 128 || k % 128 || ldc < n || (m + 127) / 128 > 65535 ||
+      (n + 127) / 128 > 0x7FFFFFFF)
+    return FP4_E_SHAPE;
   if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned(c, dtype_size(c_dtype))) return FP4_E_ALIGN;
   const fp4_status dev = check_device();
   if (dev != FP4_OK) return dev;

@@ -2,10 +2,11 @@
 // and the append that quantizes new tokens into the cache.
 //
 // "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for Blackwell B200": the codec
-// (section "The Mathematical Breakthrough of Microscopic FP4 Scaling") and FP4 KV caches
-// (its section on what open-source frameworks must rebuild: smaller footprint, less
-// bandwidth, new attention kernels). "AdaLLM Breakthrough: First NVFP4-Only Inference
-// Engine for RTX 4090 Unveiled": a quantized KV cache read by its own decode kernel.
+// (section "The Mathematical Breakthrough of Microscopic FP4 Scaling"). "The FP4
+// Inflection: Rethinking AI Inference Architecture", section "What does this mean for
+// model serving engines?": FP4 KV caches (smaller footprint, less bandwidth, new attention
+// kernels). "AdaLLM Breakthrough: First NVFP4-Only Inference Engine for RTX 4090
+// Unveiled": a quantized KV cache read by its own decode kernel.
 //
 // Codec reading: each token's key (value) vector over all KV heads, kv_heads * 128
 // elements, is one codec row: E4M3 micro-scale per 16 elements, FP16 macro-scale per 256

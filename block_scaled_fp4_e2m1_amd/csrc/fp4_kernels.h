@@ -6,6 +6,11 @@
 
 namespace fp4lib {
 
+// Whether the quantize / activation-pass grid (one 256-thread block per 16 (row, group)
+// pairs) and the dequantize grid fit one launch; the launchers refuse exactly these.
+bool quantize_grid_ok(int64_t rows, int64_t k);
+bool dequantize_grid_ok(int64_t rows, int64_t k);
+
 // macro_in (optional): static macro-scales, FP16 bits per 256-column group shared by all
 // rows (nullptr: each row's own groups, the dynamic rule).
 hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, int64_t ldx,
@@ -15,6 +20,14 @@ hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const uint16_t* macro,
                              int64_t rows, int64_t k, int elem_e4m3, int tiled, void* y,
                              int out_bf16, int64_t ldy, hipStream_t st);
+
+// Canonical <-> tiled repack of a quantized tensor (rows % 16 == 0, k % 256 == 0): a
+// byte permutation of codes, micro- and macro-scales. hipErrorInvalidValue outside
+// repack_supports().
+bool repack_supports(int64_t rows, int64_t k, int elem_e4m3);
+hipError_t launch_repack(const uint8_t* src_codes, const uint8_t* src_micro, const uint16_t* src_macro,
+                         uint8_t* dst_codes, uint8_t* dst_micro, uint16_t* dst_macro, int64_t rows, int64_t k,
+                         int elem_e4m3, int to_tiled, hipStream_t st);
 
 // Activation pass for the matrix kernels: aq[r, c] * scale[r, c/256] == A_hat[r, c].
 // macro_in as for launch_quantize.
@@ -65,6 +78,11 @@ struct GemmArgs {
 };
 // Reduction lengths the product kernel covers (its per-group tables fit in LDS).
 bool gemm_supports(int64_t k);
+// Whether launch_gemm covers a product of this shape (k within gemm_supports, a grid that
+// fits one launch); grouped: m = total routed rows. launch_gemm refuses exactly these.
+bool gemm_plan_ok(int64_t m, int64_t n, int64_t k, int grouped, int n_experts, int w_e4m3);
+// Name of the kernel form launch_gemm selects for that shape (nullptr when refused).
+const char* gemm_kernel_name(int64_t m, int64_t n, int64_t k, int grouped, int n_experts, int w_e4m3);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 
 // Plain float32 product for float32 activations (small shapes): one thread per output.

@@ -440,7 +440,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   constexpr bool kE4M3 = WShape<WM>::E4M3;
   extern __shared__ uint8_t g_dyn[];
   const int groups = (int)(args.k >> 8);
-  if (kRing == 4 && (groups & 1)) return;  // the four-slot ring runs four stages per pass
+  // the four-slot ring runs four stages (two groups) per pass: plan_gemm selects these
+  // forms only for an even group count, so this exit is never taken through launch_gemm
+  if (kRing == 4 && (groups & 1)) return;
   const int64_t n = args.n;
   const int64_t nblocks = n >> 4;
   const int tiles_n = (int)((n + BN - 1) / BN);
@@ -692,6 +694,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     }
   }
 
+  // the ring's last copies (zeros from empty resources) are complete before the
+  // workgroup's LDS can be handed to another
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
+
   // ---- apply the final factors, store ----
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
@@ -789,46 +795,77 @@ int device_cus() {
   return cus[dev];
 }
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
-  if (!gemm_supports(g.k)) return hipErrorInvalidValue;
-  if (g.w_e4m3 && (g.a_is_bf16 || g.expert_offsets)) return hipErrorInvalidValue;
+// Kernel form and grid of a product (the selection launch_gemm makes); false when the
+// shape is outside what the kernels cover (k tables over the LDS budget, grid too large).
+struct GemmPlan {
+  bool narrow, wide16, w10;
+  int64_t bn, blocks;
+  unsigned threads;
+  size_t lds;
+};
+
+static bool plan_gemm(int64_t m, int64_t n, int64_t k, bool grouped, int n_experts, bool e4m3, GemmPlan& p) {
+  if (m < 1 || n < 16 || n % 16 || !gemm_supports(k)) return false;
+  if (e4m3 && grouped) return false;
+  if (grouped && n_experts < 1) return false;
   int64_t tiles_m;
-  if (g.expert_offsets) tiles_m = (g.m + kBM - 1) / kBM + g.n_experts;  // upper bound
-  else tiles_m = (g.m + kBM - 1) / kBM;
+  if (grouped) tiles_m = (m + kBM - 1) / kBM + n_experts;  // upper bound
+  else tiles_m = (m + kBM - 1) / kBM;
   // dense E2M1 products whose 64 x 256 tiles cannot give every CU two workgroups take the
   // narrow 64 x 128 tile
   const int64_t cus = device_cus();
-  const bool narrow = !g.w_e4m3 && !g.expert_offsets &&
-                      tiles_m * ((g.n + WShape<0>::BN - 1) / WShape<0>::BN) < 2 * cus;
+  p.narrow = !e4m3 && !grouped && tiles_m * ((n + WShape<0>::BN - 1) / WShape<0>::BN) < 2 * cus;
   // dense E2M1 products whose 64 x 512 tiles still give every CU a workgroup take the
   // 16-wave form: four waves per SIMD, one activation stage for twice the weight columns
-  const bool wide16 = !g.w_e4m3 && !g.expert_offsets && !narrow &&
-                     tiles_m * ((g.n + WShape<3>::BN - 1) / WShape<3>::BN) >= cus &&
-                     gemm_dynamic_lds((int)(g.k >> 8), WShape<3>::BN) <= 160 * 1024 - 96 * 1024;
+  p.wide16 = !e4m3 && !grouped && !p.narrow &&
+             tiles_m * ((n + WShape<3>::BN - 1) / WShape<3>::BN) >= cus &&
+             gemm_dynamic_lds((int)(k >> 8), WShape<3>::BN) <= 160 * 1024 - 96 * 1024;
   // narrow products take the 10-wave 64 x 160 form when it puts fewer weight columns on
   // the busiest SIMD: 48 per 64 x 160 tile on a CU (3 waves of 16), 32 per 64 x 128
-  // tile (two workgroups of 8 waves share a CU)
-  // (W8A8 products, whose E4M3 tile is always 64 x 128, likewise, with weight slots of
-  // twice the size)
-  bool w10 = false;
-  if (narrow || (g.w_e4m3 && !g.expert_offsets)) {
-    const int64_t t128 = tiles_m * ((g.n + WShape<2>::BN - 1) / WShape<2>::BN);
-    const int64_t t160 = tiles_m * ((g.n + WShape<4>::BN - 1) / WShape<4>::BN);
-    const int groups = (int)(g.k >> 8);
-    const size_t lds = (g.w_e4m3 ? kW10eStaticLds : kW10StaticLds) + gemm_dynamic_lds(groups, WShape<4>::BN);
-    w10 = 48 * ((t160 + cus - 1) / cus) < 32 * ((t128 + cus - 1) / cus) && groups % 2 == 0 &&
-          lds <= 160 * 1024;
+  // tile (two workgroups of 8 waves share a CU); W8A8 products, whose E4M3 tile is
+  // always 64 x 128, likewise, with weight slots of twice the size. The form's four-slot
+  // ring runs four stages (two groups) per pass: an even group count is a precondition.
+  p.w10 = false;
+  if (p.narrow || (e4m3 && !grouped)) {
+    const int64_t t128 = tiles_m * ((n + WShape<2>::BN - 1) / WShape<2>::BN);
+    const int64_t t160 = tiles_m * ((n + WShape<4>::BN - 1) / WShape<4>::BN);
+    const int groups = (int)(k >> 8);
+    const size_t lds = (e4m3 ? kW10eStaticLds : kW10StaticLds) + gemm_dynamic_lds(groups, WShape<4>::BN);
+    p.w10 = 48 * ((t160 + cus - 1) / cus) < 32 * ((t128 + cus - 1) / cus) && groups % 2 == 0 &&
+            lds <= 160 * 1024;
   }
-  const int64_t bn = w10        ? WShape<4>::BN
-                     : g.w_e4m3 ? WShape<1>::BN
-                     : narrow ? WShape<2>::BN
-                     : wide16 ? WShape<3>::BN
-                              : WShape<0>::BN;
-  const int64_t tiles_n = (g.n + bn - 1) / bn;
-  const int64_t blocks = tiles_m * tiles_n;
-  if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(wide16 ? 1024 : w10 ? 640 : 512);
-  const size_t lds = gemm_dynamic_lds((int)(g.k >> 8), (int)bn);
+  p.bn = p.w10 ? WShape<4>::BN : e4m3 ? WShape<1>::BN : p.narrow ? WShape<2>::BN
+         : p.wide16 ? WShape<3>::BN : WShape<0>::BN;
+  p.blocks = tiles_m * ((n + p.bn - 1) / p.bn);
+  if (p.blocks <= 0 || p.blocks > 0x7FFFFFFF) return false;
+  p.threads = p.wide16 ? 1024 : p.w10 ? 640 : 512;
+  p.lds = gemm_dynamic_lds((int)(k >> 8), (int)p.bn);
+  return true;
+}
+
+bool gemm_plan_ok(int64_t m, int64_t n, int64_t k, int grouped, int n_experts, int w_e4m3) {
+  GemmPlan p;
+  return plan_gemm(m, n, k, grouped != 0, n_experts, w_e4m3 != 0, p);
+}
+
+const char* gemm_kernel_name(int64_t m, int64_t n, int64_t k, int grouped, int n_experts, int w_e4m3) {
+  GemmPlan p;
+  if (!plan_gemm(m, n, k, grouped != 0, n_experts, w_e4m3 != 0, p)) return nullptr;
+  if (p.wide16) return "k_gemm_w16 (64 x 512, 16 waves)";
+  if (p.w10) return w_e4m3 ? "k_gemm_w10e (64 x 160, 10 waves, E4M3)" : "k_gemm_w10 (64 x 160, 10 waves)";
+  if (w_e4m3) return "k_gemm (64 x 128, 8 waves, E4M3)";
+  if (p.narrow) return "k_gemm (64 x 128, 8 waves)";
+  return grouped ? "k_gemm (64 x 256, 8 waves, grouped)" : "k_gemm (64 x 256, 8 waves)";
+}
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
+  if (g.w_e4m3 && g.a_is_bf16) return hipErrorInvalidValue;
+  GemmPlan p;
+  if (!plan_gemm(g.m, g.n, g.k, g.expert_offsets != nullptr, g.n_experts, g.w_e4m3 != 0, p))
+    return hipErrorInvalidValue;
+  const bool narrow = p.narrow, wide16 = p.wide16, w10 = p.w10;
+  const dim3 grid((unsigned)p.blocks), block(p.threads);
+  const size_t lds = p.lds;
 #define FP4_GEMM(A, C, G, W) hipLaunchKernelGGL((k_gemm<A, C, G, W>), grid, block, lds, st, g)
   const int grouped = g.expert_offsets != nullptr;
   if (wide16) {

@@ -336,6 +336,9 @@ inline unsigned blocks_for(int64_t rows, int64_t k) {
 
 namespace fp4lib {
 
+bool quantize_grid_ok(int64_t rows, int64_t k) { return rows >= 1 && k >= 256 && blocks_for16(rows, k) != 0; }
+bool dequantize_grid_ok(int64_t rows, int64_t k) { return rows >= 1 && k >= 256 && blocks_for(rows, k) != 0; }
+
 hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, int64_t ldx,
                            int elem_e4m3, int tiled, uint8_t* codes, uint8_t* micro,
                            uint16_t* macro, const uint16_t* macro_in, hipStream_t st) {

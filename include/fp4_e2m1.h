@@ -135,6 +135,22 @@ fp4_status act_macro_calibrate(const void* x, int32_t x_dtype, int64_t rows, int
                                int32_t elem, float* amax, uint16_t* macro, void* stream);
 
 /*
+ * repack_fp4 -- the same quantized tensor in the other packed layout: src (either layout,
+ * E2M1 or E4M3 elements, rows % 16 == 0) is written to codes / micro / macro (device, the
+ * sizes of src's arrays, codes and micro 16-byte aligned) in `layout`, which must differ
+ * from src->layout (FP4_E_LAYOUT otherwise). A byte permutation of the codes, the micro-
+ * scales and the macro-scales: nothing is decoded or re-rounded, so repacking is exact
+ * (re-quantizing dequantized values is not: a block whose maximum rounds down gets a
+ * smaller micro-scale) and tiled -> canonical -> tiled returns the original bytes. This is
+ * how weights stored in the canonical interchange layout reach the product kernels,
+ * which read the tiled one. The source and destination must not overlap.
+ * Source: TensorRT-LLM FP4 page, section on microscopic FP4 scaling, items 1-2 (the
+ * format being moved); the tiled layout is this library's.
+ */
+fp4_status repack_fp4(const fp4_tensor* src, int32_t layout, void* codes, uint8_t* micro, uint16_t* macro,
+                      void* stream);
+
+/*
  * dequantize_fp4 -- y = value(code) * mu * M for every element of q (either layout).
  *   y        device out [q->rows x q->k], FP4_F32 (exact) or FP4_BF16 (round to nearest
  *            even of the exact value), row stride ldy elements (16-byte aligned rows)
@@ -154,6 +170,11 @@ fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t
  *   c        device out [m x n], FP4_BF16 (round to nearest even) or FP4_F32, stride ldc
  *   workspace device scratch of at least fp4_workspace_bytes(act, m, n, k) bytes
  *            (may be NULL when that is 0); contents are overwritten
+ * Paths: FP4_A16 with FP4_F32 activations runs one thread per output (m * n <= 2^32 -
+ * 256); FP4_A16 with bf16 activations and m <= 8, k <= 8192 runs the decode GEMV; every
+ * other call runs the activation pass (FP4_A4 / FP4_A8) and the product kernel, which
+ * needs k <= 21760 (its per-group tables fit LDS). Shapes outside these limits return
+ * FP4_E_SHAPE before anything is enqueued.
  * Source: "llama.cpp Put Precision Policy Inside the Model", intro and section "One model
  * can need more than one precision" (W4A4, W4A8 and W4A16 layers).
  */
@@ -200,6 +221,7 @@ fp4_status gemm_w8a8(const void* a, int32_t a_dtype, int64_t m, int64_t lda, con
  *   w              quantized weights, experts stacked: rows = n_experts * n, TILED
  *   c              device out [total_rows x n] (bf16/f32), stride ldc
  *   workspace      >= fp4_workspace_bytes(act, a_rows, n, k)
+ * k <= 21760 and n % 16 == 0 (FP4_E_SHAPE otherwise, before anything is enqueued).
  * Source: llama.cpp precision-policy page, section "One model can need more than one
  * precision" (the same routing for mixture-of-experts operations).
  */
@@ -224,6 +246,7 @@ fp4_status grouped_gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_
  *   w              quantized down weights, experts stacked: rows = n_experts * n, TILED
  *   c              device out [rows x n] (bf16/f32), stride ldc
  *   workspace      >= fp4_workspace_bytes(act, rows, n, k)
+ * k <= 21760 and n % 16 == 0 (FP4_E_SHAPE otherwise, before anything is enqueued).
  * Source: llama.cpp precision-policy page, section "One model can need more than one
  * precision" (W4A4 / W4A8 routing for mixture-of-experts operations). The pages fix no
  * activation function; SiLU gating is the usual reading for gate/up experts.
@@ -270,11 +293,12 @@ fp4_status moe_combine(const void* y, int32_t y_dtype, int64_t ldy, const int32_
 /*
  * KV cache in the two-level FP4 format, and decode attention over it.
  * Sources: "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for Blackwell B200"
- * (the codec, section "The Mathematical Breakthrough of Microscopic FP4 Scaling"; keeping
- * the KV cache in FP4 to cut its footprint and bandwidth, in its section on what
- * open-source frameworks must rebuild) and "AdaLLM Breakthrough: First NVFP4-Only
- * Inference Engine for RTX 4090 Unveiled" (a quantized KV cache with its own decode
- * kernel, grouped-query models).
+ * (the codec, section "The Mathematical Breakthrough of Microscopic FP4 Scaling"); "The
+ * FP4 Inflection: Rethinking AI Inference Architecture", section "What does this mean for
+ * model serving engines?" (a KV cache kept in FP4 cuts its memory footprint and
+ * bandwidth, and needs attention kernels written for it); and "AdaLLM Breakthrough:
+ * First NVFP4-Only Inference Engine for RTX 4090 Unveiled" (a quantized KV cache with
+ * its own decode kernel, grouped-query models).
  *
  * Codec reading: each token's key (value) vector over all KV heads (kv_heads x head_dim
  * elements) is one codec row: E2M1 codes, an E4M3 micro-scale per 16 elements, an FP16
@@ -394,6 +418,20 @@ const char* fp4_status_string(fp4_status status);
 
 /* Device check without launching anything: FP4_OK on gfx950, else the error code. */
 fp4_status fp4_device_check(void);
+
+/*
+ * fp4_product_kernel -- diagnostics: the kernel form a product call of this shape runs
+ * on the current device (the choice depends on its compute-unit count), as a static
+ * string, or NULL when the call would return FP4_E_SHAPE. Enqueues nothing.
+ *   act, a_dtype  as for gemm_w4aX (the policy codes FP4_A4S / FP4_A8S / FP4_W8A8 map to
+ *                 their activation precision)
+ *   m, n, k       the product's rows (grouped: total routed rows), columns (grouped: per
+ *                 expert) and reduction length
+ *   grouped       nonzero for grouped_gemm_w4aX / grouped_gemm_w4aX_gated, n_experts
+ *   w_e4m3        nonzero for gemm_w8a8 (E4M3 weights; act must be FP4_A8 or FP4_W8A8)
+ */
+const char* fp4_product_kernel(int32_t act, int32_t a_dtype, int64_t m, int64_t n, int64_t k,
+                               int32_t grouped, int32_t n_experts, int32_t w_e4m3);
 
 #ifdef __cplusplus
 }

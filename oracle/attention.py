@@ -5,9 +5,10 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 Sources:
 * "NVIDIA Ships TensorRT-LLM 0.16: Native FP4 Quantization for Blackwell B200", section
-  "The Mathematical Breakthrough of Microscopic FP4 Scaling" (the codec), and the section
-  on what open-source frameworks must rebuild: keeping the KV cache in FP4 cuts its memory
-  footprint and bandwidth, and needs new attention kernels.
+  "The Mathematical Breakthrough of Microscopic FP4 Scaling" (the codec).
+* "The FP4 Inflection: Rethinking AI Inference Architecture", section "What does this
+  mean for model serving engines?": keeping the KV cache in FP4 cuts its memory footprint
+  and bandwidth, and needs new attention kernels.
 * "AdaLLM Breakthrough: First NVFP4-Only Inference Engine for RTX 4090 Unveiled": a
   quantized KV cache read by a dedicated decode kernel (FP8 there), with grouped-query
   models (Qwen3, Gemma3).

@@ -110,6 +110,60 @@ def test_validation_happens_before_any_device_use(lib):
                                  256, fake, 1 << 30, null) == 1
 
 
+def test_product_k_limit_is_checked_before_anything_is_enqueued(lib):
+    """The product kernel's per-group tables fit LDS up to k = 21760 (85 groups). Past
+    that, every product entry point returns FP4_E_SHAPE before the device is even looked
+    at (on this GPU-less host a later check would return FP4_E_NO_DEVICE, and a launch
+    FP4_E_HIP): no activation pass is enqueued ahead of a refused product."""
+    vp = ctypes.c_void_p
+    fake, null = vp(1 << 20), vp(0)
+    ws, big = vp(1 << 24), 1 << 40
+    T = lib_mod._Tensor
+    k_bad, k_ok = 22016, 21760
+    w = T(1 << 20, 1 << 21, 1 << 22, 256, k_bad, 0, 1)
+    wk = T(1 << 20, 1 << 21, 1 << 22, 256, k_ok, 0, 1)
+    for act in (4, 8):
+        assert lib.gemm_w4aX(act, fake, 1, 64, k_bad, ctypes.byref(w), fake, 1, 256, ws, big, null) == 2
+        assert lib.gemm_w4aX(act, fake, 1, 64, k_ok, ctypes.byref(wk), fake, 1, 256, ws, big, null) == 6
+        assert lib.grouped_gemm_w4aX(act, fake, 1, 64, k_bad, null, fake, 2, 64, ctypes.byref(w), fake, 1,
+                                     128, ws, big, null) == 2
+        assert lib.grouped_gemm_w4aX_gated(act, fake, 64, 2 * k_bad, fake, 2, ctypes.byref(w), fake, 1, 128,
+                                           ws, big, null) == 2
+        assert lib.gemm_w4aX_static(act, fake, 1, 64, k_bad, fake, ctypes.byref(w), fake, 1, 256, ws, big,
+                                    null) == 2
+    # bf16 A16: m <= 8 with k <= 8192 runs the decode GEMV; larger k or m runs the product
+    assert lib.gemm_w4aX(16, fake, 1, 64, k_bad, ctypes.byref(w), fake, 1, 256, null, 0, null) == 2
+    assert lib.gemm_w4aX(16, fake, 1, 8, k_bad, ctypes.byref(w), fake, 1, 256, null, 0, null) == 2
+    # float32 A16 runs one thread per output and has no k limit
+    assert lib.gemm_w4aX(16, fake, 0, 8, k_bad, ctypes.byref(w), fake, 0, 256, null, 0, null) == 6
+    # grouped: an expert row count that is not a multiple of 16
+    w24 = T(1 << 20, 1 << 21, 1 << 22, 48, 512, 0, 1)
+    assert lib.grouped_gemm_w4aX(4, fake, 1, 64, 512, null, fake, 2, 64, ctypes.byref(w24), fake, 1,
+                                 24, ws, big, null) == 2
+
+
+def test_repack_validates_before_device_use(lib):
+    vp = ctypes.c_void_p
+    fake, null = vp(1 << 20), vp(0)
+    T = lib_mod._Tensor
+    can = T(1 << 20, 1 << 21, 1 << 22, 64, 512, 0, 0)
+    assert lib.repack_fp4(ctypes.byref(can), 1, null, fake, fake, null) == 1
+    assert lib.repack_fp4(None, 1, fake, fake, fake, null) == 1
+    assert lib.repack_fp4(ctypes.byref(can), 0, fake, fake, fake, null) == 10  # same layout
+    assert lib.repack_fp4(ctypes.byref(can), 3, fake, fake, fake, null) == 5
+    assert lib.repack_fp4(ctypes.byref(T(1 << 20, 1 << 21, 1 << 22, 64, 512, 2, 0)), 1, fake, fake, fake,
+                          null) == 5
+    assert lib.repack_fp4(ctypes.byref(T(1 << 20, 1 << 21, 1 << 22, 40, 512, 0, 0)), 1, fake, fake, fake,
+                          null) == 2  # rows % 16
+    assert lib.repack_fp4(ctypes.byref(T(1 << 20, 1 << 21, 1 << 22, 64, 500, 0, 0)), 1, fake, fake, fake,
+                          null) == 2
+    assert lib.repack_fp4(ctypes.byref(can), 1, vp((1 << 20) + 8), fake, fake, null) == 3
+    assert lib.repack_fp4(ctypes.byref(T(1 << 20, (1 << 21) + 4, 1 << 22, 64, 512, 0, 0)), 1, fake, fake, fake,
+                          null) == 3
+    # valid: reaches the device check (no GPU here)
+    assert lib.repack_fp4(ctypes.byref(can), 1, fake, fake, fake, null) == 6
+
+
 def test_moe_entry_points_validate_before_device_use(lib):
     vp = ctypes.c_void_p
     fake = vp(1 << 20)

@@ -4,16 +4,28 @@
 Gates:
   cache contents: codes, micro- and macro-scales bit-exact against the oracle's codec on
       the same token rows (read back through the documented device layout);
-  attention, float32 output: ||out - ref||_F <= 1e-5 * ||ref_abs||_F, where ref is the
-      float64 oracle on the oracle's own quantization of the same inputs and ref_abs the
-      same attention applied to |V|: an output is a weighted sum, and its rounding error
-      scales with the weighted sum of magnitudes (the sum's condition), not with the
-      output itself, which for near-uniform attention over 10^4 tokens is a mean of
-      signed values ~100x smaller than its terms. The kernel's scores are exact products
-      of the cache values and q accumulated in float32; the softmax weights enter the
-      value product as an FP16 pair hi + lo (~2^-22 relative); exp2 and the sums are
-      float32. (A single FP16 weight, 2^-12 relative each, measured ~1e-4 and flipped the
-      bf16 rounding of too many outputs.);
+  attention, float32 output: ||out - ref||_F <= 2e-6 * ||ref_abs||_F and
+      ||out - ref||_F <= 5e-5 * ||ref||_F, where ref is the float64 oracle on the
+      oracle's own quantization of the same inputs and ref_abs the same attention applied
+      to |V|. An output is a weighted sum; its rounding error scales with the weighted sum
+      of magnitudes (the sum's condition), not with the output itself, which for
+      near-uniform attention over 10^4 tokens is a mean of signed values ~100x smaller
+      than its terms. The first bound comes from the kernel's error model. Scores are
+      exact products of cache values and q summed in float32 by 4 MFMAs of 32 terms
+      (relative 2^-24 * sqrt(4/3) of |score| <= ~5 in base 2: ~3.5e-7 on a weight);
+      exp2 is the hardware approximation (about 1 ulp, 2^-23); the weights enter the
+      value product as an FP16 pair hi + lo (2^-22); the value and normalizer sums
+      each take a chain of about 60 float32 roundings per output (16 tiles of 32 tokens
+      per wave, each two MFMAs and the online rescale, then the 4-wave and the 8-chunk
+      combines). With independent roundings, uniform within half an ulp, the error
+      against ||ref_abs|| is about sqrt((2^-24)^2 * 2 * 60 / 3 + (2^-22)^2 / 3 +
+      (2^-23)^2 / 3 + (3.5e-7)^2) ~ 5.4e-7; the gate is 3.7x that (the largest
+      measured is 2.5e-7). The second bound caps the plain relative error so that a
+      large condition number cannot hide a real error: ||ref_abs|| / ||ref|| reaches
+      ~60 for near-uniform attention over 16384 tokens, where the cap (25x the first
+      bound) is the tighter of the two; the largest plain error measured there is 1.4e-5.
+      (A single FP16 weight, 2^-12 relative each, measured ~1e-4 and flipped the bf16
+      rounding of too many outputs.);
   attention, bf16 output: the bf16 gate (relative Frobenius <= 1e-3 against the rounded
       float64 result, >= 99.9% of elements within one bf16 step).
 """
@@ -105,12 +117,14 @@ def test_append_skips_positions_past_the_cache_and_negative():
     assert not codes4.any() and not micro.any() and not macro.any()
 
 
-def attention_gate(got, ref, ref_abs, tol=1e-5):
-    """||got - ref||_F / ||ref_abs||_F <= tol; returns (that ratio, plain relative error)."""
+def attention_gate(got, ref, ref_abs, tol=2e-6, tol_plain=5e-5):
+    """||got - ref||_F / ||ref_abs||_F <= tol and ||got - ref||_F / ||ref||_F <= tol_plain;
+    returns (the first ratio, the plain relative error)."""
     err = np.linalg.norm(np.asarray(got, np.float64) - ref)
     cond = err / max(np.linalg.norm(ref_abs), 1e-300)
     plain = err / max(np.linalg.norm(ref), 1e-300)
     assert cond <= tol, f"error {cond:.3e} of the weighted magnitudes > {tol} (plain relative {plain:.3e})"
+    assert plain <= tol_plain, f"plain relative error {plain:.3e} > {tol_plain} (weighted {cond:.3e})"
     return cond, plain
 
 

@@ -106,19 +106,21 @@ def test_gemm_small_shapes(act, m, n, k):
 
 
 @pytest.mark.parametrize("act", [16, 8, 4])
-def test_gemm_wide_512_tiles_ragged(act):
+@pytest.mark.parametrize("k", [256, 1024])
+def test_gemm_wide_512_tiles_ragged(act, k):
     """Small products take the narrow 64 x 128 tile; this shape (2043 x 4080: 32 x 8 tiles
     of 64 x 512, the last row and column tiles ragged) is large enough for the 16-wave
-    64 x 512 form."""
-    m, n, k = 2043, 4080, 256
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert -(-m // 64) * -(-n // 512) >= cus, "shape no longer selects the 64 x 512 tile"
-    rng = np.random.default_rng(310 + act)
+    64 x 512 form. k = 1024 crosses three group boundaries, so the per-group rescale of
+    both the bf16 (A16) and the FP16 (A4 / A8) operand forms runs in it."""
+    m, n = 2043, 4080
+    name = fp4.fp4_product_kernel(act, torch.bfloat16, m, n, k)
+    assert name.startswith("k_gemm_w16"), f"shape no longer selects the 16-wave form ({name})"
+    rng = np.random.default_rng(310 + act + k)
     a = rng.standard_normal((m, k)).astype(np.float32)
     a[:, rng.choice(k, 3, replace=False)] *= 50
     a = workloads.to_bf16_values(a)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
-    print(f"[case] gemm 64x512 tiles {ACTS[act]} m={m} n={n} k={k}", flush=True)
+    print(f"[case] gemm 64x512 tiles {ACTS[act]} m={m} n={n} k={k} ({name})", flush=True)
     wq = _wq(w)
     ad = to_device_bf16(a)
     ref = _oracle_c(a.astype(np.float64), w, act)
@@ -127,15 +129,15 @@ def test_gemm_wide_512_tiles_ragged(act):
 
 
 @pytest.mark.parametrize("act", [4, 8, 16])
-@pytest.mark.parametrize("m,n,k", [(500, 4800, 1024), (505, 5008, 1536)])
+@pytest.mark.parametrize("m,n,k", [(500, 4800, 512), (500, 4800, 1024), (505, 5008, 1536)])
 def test_gemm_ten_wave_ring_ragged(m, n, k, act):
     """Products whose 64 x 128 grid would put two workgroups on some CUs while the 64 x 160
-    grid fits one per CU run the 10-wave form with its four-slot stage ring. Here 4 and 6
-    groups (the ring's copies run past the last stage), a ragged last row tile, and in
-    5008 a last column tile of 48 columns."""
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tm = -(-m // 64)
-    assert tm * -(-n // 128) > cus >= tm * -(-n // 160), "shape no longer selects the 10-wave form"
+    grid fits one per CU run the 10-wave form with its four-slot stage ring. Here 2, 4 and
+    6 groups (the ring's copies run past the last stage; at 2 groups all but one copy
+    after the prologue does), a ragged last row tile, and in 5008 a last column tile of
+    48 columns."""
+    name = fp4.fp4_product_kernel(act, torch.bfloat16, m, n, k)
+    assert name.startswith("k_gemm_w10 "), f"shape no longer selects the 10-wave form ({name})"
     rng = np.random.default_rng(330 + act + k)
     a = rng.standard_normal((m, k)).astype(np.float32)
     a[:, rng.choice(k, 3, replace=False)] *= 50
@@ -156,6 +158,8 @@ def test_gemm_wide_tiles_large_k_sampled(act):
     ragged) runs the 8-wave 64 x 256 form; checked on sampled outputs, the last row and
     column tiles among them."""
     m, n, k = 1040, 8192, 13312
+    name = fp4.fp4_product_kernel(act, torch.bfloat16, m, n, k)
+    assert name == "k_gemm (64 x 256, 8 waves)", f"shape no longer selects the 64 x 256 form ({name})"
     rng = np.random.default_rng(320 + act)
     a = rng.standard_normal((m, k)).astype(np.float32)
     a[:, rng.choice(k, 5, replace=False)] *= 50

@@ -113,7 +113,8 @@ def test_edge_cases(elem, layout):
 
 def test_decode_workload_weights_full_size_sampled_rows():
     """The decode weights [14336 x 4096] quantized at full size in the tiled layout the
-    product kernels read; every row's scales and a sample of rows' codes are checked."""
+    product kernels read; the codes, micro-scales and macro-scales of 384 sampled rows
+    are checked bit for bit against the oracle."""
     _, w, _ = workloads.decode()
     print("[case] decode weights 14336x4096 tiled", flush=True)
     sel = np.sort(np.random.default_rng(103).choice(w.shape[0], 384, replace=False))

@@ -134,14 +134,13 @@ def test_gemm_w8a8_small_shapes(m, n, k):
     bf16_gate(bf16_values(fp4.gemm_w8a8(ad, wq)), oracle.formats.bf16_round(ref))
 
 
-@pytest.mark.parametrize("m,n,k", [(500, 4800, 1024), (505, 5008, 1536)])
+@pytest.mark.parametrize("m,n,k", [(500, 4800, 512), (500, 4800, 1024), (505, 5008, 1536)])
 def test_gemm_w8a8_ten_wave_ring(m, n, k):
     """W8A8 products whose 64 x 128 grid would put two workgroups on some CUs run the E4M3
-    10-wave 64 x 160 form with its four-slot stage ring: 4 and 6 groups (the ring's
+    10-wave 64 x 160 form with its four-slot stage ring: 2, 4 and 6 groups (the ring's
     copies run past the last stage), a ragged last row tile, a 48-column last tile."""
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tm = -(-m // 64)
-    assert tm * -(-n // 128) > cus >= tm * -(-n // 160), "shape no longer selects the 10-wave form"
+    name = fp4.fp4_product_kernel(fp4.W8A8, torch.bfloat16, m, n, k, w_e4m3=True)
+    assert name.startswith("k_gemm_w10e"), f"shape no longer selects the 10-wave form ({name})"
     rng = np.random.default_rng(440 + m + n + k)
     a = _acts(rng, m, k)
     w = _weights(rng, n, k)
