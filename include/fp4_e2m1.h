@@ -140,8 +140,9 @@ fp4_status act_macro_calibrate(const void* x, int32_t x_dtype, int64_t rows, int
  * sizes of src's arrays, codes and micro 16-byte aligned) in `layout`, which must differ
  * from src->layout (FP4_E_LAYOUT otherwise). A byte permutation of the codes, the micro-
  * scales and the macro-scales: nothing is decoded or re-rounded, so repacking is exact
- * (re-quantizing dequantized values is not: a block whose maximum rounds down gets a
- * smaller micro-scale) and tiled -> canonical -> tiled returns the original bytes. This is
+ * and tiled -> canonical -> tiled returns the original bytes (re-quantizing dequantized
+ * values is not exact in general: bf16 values are re-rounded, and with E4M3 elements a
+ * block maximum that rounds down changes the block's micro-scale). This is
  * how weights stored in the canonical interchange layout reach the product kernels,
  * which read the tiled one. The source and destination must not overlap.
  * Source: TensorRT-LLM FP4 page, section on microscopic FP4 scaling, items 1-2 (the
