@@ -36,7 +36,9 @@ EXPORTED = ["quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
             "fp4_device_check", "fp4_kv_cache_bytes", "kv_cache_append",
             "attention_workspace_bytes", "attention_decode_fp4kv", "mxfp4_bytes",
             "quantize_mxfp4", "gemm_mxfp4", "quantize_fp4_static", "act_macro_calibrate",
-            "gemm_w4aX_static", "gemm_w8a8", "fp4_product_kernel", "repack_fp4"]
+            "gemm_w4aX_static", "gemm_w8a8", "fp4_product_kernel", "repack_fp4",
+            "gemm_w4aX_noalloc"]
+NOALLOC_SCRATCH_BYTES = 32 << 20
 KV_CODES, KV_MICRO, KV_MACRO = 0, 1, 2
 
 
@@ -107,13 +109,14 @@ def library() -> ctypes.CDLL:
     lib.gemm_w4aX_static.argtypes = [i32, vp, i32, i64, i64, vp, T, vp, i32, i64, vp, sz, vp]
     lib.gemm_w8a8.argtypes = [vp, i32, i64, i64, T, vp, i32, i64, vp, sz, vp]
     lib.repack_fp4.argtypes = [T, i32, vp, vp, vp, vp]
+    lib.gemm_w4aX_noalloc.argtypes = [i32, vp, i32, i64, i64, T, vp, i32, i64, vp]
     lib.fp4_product_kernel.argtypes = [i32, i32, i64, i64, i64, i32, i32, i32]
     lib.fp4_product_kernel.restype = ctypes.c_char_p
     for name in ("quantize_fp4", "dequantize_fp4", "gemm_w4aX", "grouped_gemm_w4aX",
                  "grouped_gemm_w4aX_gated", "moe_route", "moe_combine", "fp4_device_check",
                  "kv_cache_append", "attention_decode_fp4kv", "quantize_mxfp4", "gemm_mxfp4",
                  "quantize_fp4_static", "act_macro_calibrate", "gemm_w4aX_static", "gemm_w8a8",
-                 "repack_fp4"):
+                 "repack_fp4", "gemm_w4aX_noalloc"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -281,6 +284,21 @@ def gemm_w4aX(act: int, a: torch.Tensor, w: QTensor, out_dtype: torch.dtype = to
                              _ptr(c), _dtype_code(c.dtype), c.stride(0), _ptr(ws), wsb, _stream())
     _check(st, "gemm_w4aX")
     return c
+
+
+def gemm_w4aX_noalloc(act: int, a: torch.Tensor, w: QTensor, out: torch.Tensor) -> torch.Tensor:
+    """gemm_w4aX without a workspace (the library's per-GPU scratch array); ``out`` is the
+    caller's [m x n] output (bf16 or float32), so the call allocates nothing."""
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("a must be 2-D with contiguous rows")
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != a.shape[0] or out.shape[1] != w.rows:
+        raise ValueError("out must be [m x n] with contiguous rows")
+    ts = w.c_struct()
+    st = library().gemm_w4aX_noalloc(act, _ptr(a), _dtype_code(a.dtype), a.shape[0], a.stride(0),
+                                     ctypes.byref(ts), _ptr(out), _dtype_code(out.dtype), out.stride(0),
+                                     _stream())
+    _check(st, "gemm_w4aX_noalloc")
+    return out
 
 
 def gemm_w4aX_static(act: int, a: torch.Tensor, act_macro: torch.Tensor, w: QTensor,

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/fp4_e2m1.h"
 #include "fp4_kernels.h"
 
@@ -63,6 +65,29 @@ size_t act_workspace(int32_t act, int64_t rows, int64_t k) {
   if (act == FP4_A16) return 0;
   const size_t aq = ((size_t)rows * (size_t)act_ws_stride(k) * 2 + 255) & ~(size_t)255;
   return aq + (size_t)rows * (size_t)(k / 256) * 4;
+}
+
+// Scratch of gemm_w4aX_noalloc, for callers that cannot allocate: the activation pass's
+// FP16 operand and per-group factors live here instead of a caller workspace. Each GPU
+// holds its own copy for the life of the process. In host code `scratch` names a host-side
+// stand-in, not device memory: host code only ever uses the device address that
+// hipGetSymbolAddress returns for the current device (looked up once per device and kept).
+constexpr size_t kScratchBytes = FP4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+fp4_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP4_E_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  void* p = dev < kMaxDevices ? g_scratch_ptr[dev] : nullptr;
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP4_E_HIP;
+    if (dev < kMaxDevices) g_scratch_ptr[dev] = p;
+  }
+  *out = p;
+  return FP4_OK;
 }
 
 // Launch limits of the matrix path a call takes (the activation pass over act_rows rows
@@ -245,9 +270,11 @@ fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t
       static_cast<hipStream_t>(stream)));
 }
 
-fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,
-                     const fp4_tensor* w, void* c, int32_t c_dtype, int64_t ldc,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// gemm_w4aX with either a caller workspace or (noalloc) this device's scratch array.
+fp4_status gemm_w4aX_impl(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,
+                          const fp4_tensor* w, void* c, int32_t c_dtype, int64_t ldc, void* workspace,
+                          size_t workspace_bytes, void* stream, bool noalloc) {
   if (!valid_act(act)) return FP4_E_MODE;
   if (!a || !c) return FP4_E_NULL;
   const fp4_status ws_ok = check_weights(w);
@@ -258,8 +285,11 @@ fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int
   if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
   if (!aligned(c, dtype_size(c_dtype))) return FP4_E_ALIGN;
   const size_t need = act_workspace(act, m, k);
-  if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+  if (noalloc) {
+    if (need > kScratchBytes) return FP4_E_WORKSPACE;
+  } else if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) {
     return FP4_E_WORKSPACE;
+  }
   // path: float32 activations (A16) -> one thread per output; A16 bf16 with m <= 8 -> the
   // decode GEMV; everything else -> activation pass (A4 / A8) and the product kernel
   const bool f32_path = act == FP4_A16 && a_dtype == FP4_F32;
@@ -271,6 +301,10 @@ fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int
   }
   const fp4_status dev = check_device();
   if (dev != FP4_OK) return dev;
+  if (noalloc && need) {
+    const fp4_status sa = scratch_address(&workspace);
+    if (sa != FP4_OK) return sa;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint8_t* codes = static_cast<const uint8_t*>(w->codes);
 
@@ -295,6 +329,18 @@ fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int
   g.c_is_bf16 = c_dtype == FP4_BF16;
   g.ldc = ldc;
   return launched(fp4lib::launch_gemm(g, st));
+}
+}  // namespace
+
+fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,
+                     const fp4_tensor* w, void* c, int32_t c_dtype, int64_t ldc,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_w4aX_impl(act, a, a_dtype, m, lda, w, c, c_dtype, ldc, workspace, workspace_bytes, stream, false);
+}
+
+fp4_status gemm_w4aX_noalloc(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,
+                             const fp4_tensor* w, void* c, int32_t c_dtype, int64_t ldc, void* stream) {
+  return gemm_w4aX_impl(act, a, a_dtype, m, lda, w, c, c_dtype, ldc, nullptr, 0, stream, true);
 }
 
 fp4_status gemm_w4aX_static(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,

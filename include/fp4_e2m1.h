@@ -184,6 +184,24 @@ fp4_status gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_t m, int
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gemm_w4aX_noalloc -- gemm_w4aX for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, results and limits as gemm_w4aX, without the workspace: the FP4_A4 / FP4_A8
+ * activation operand lives in the library's own device array of
+ * FP4_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held from the library's first use of that
+ * GPU until the process ends. A call whose workspace would exceed it
+ * (fp4_workspace_bytes(act, m, n, k) > FP4_NOALLOC_SCRATCH_BYTES, e.g. m x k above
+ * ~16.6 M activation elements at k = 4096) returns FP4_E_WORKSPACE before anything is
+ * enqueued. No hipMalloc, hipFree or allocating library routine is called. Every call on
+ * a GPU shares that GPU's array: calls enqueued on one stream are ordered, but calls that
+ * overlap on one GPU (unordered streams, host threads) race and give wrong results. Each
+ * call writes every scratch byte it reads, so nothing carries over between calls.
+ */
+enum { FP4_NOALLOC_SCRATCH_BYTES = 32 << 20 };
+fp4_status gemm_w4aX_noalloc(int32_t act, const void* a, int32_t a_dtype, int64_t m, int64_t lda,
+                             const fp4_tensor* w, void* c, int32_t c_dtype, int64_t ldc, void* stream);
+
+/*
  * gemm_w4aX_static -- gemm_w4aX (FP4_A4 or FP4_A8 only) with static activation macro-
  * scales: A_hat = dequant(quantize_fp4_static(A, act_macro)), act_macro device uint16
  * [k/256] as for quantize_fp4_static. The micro-scales stay per row and per 16 elements.

@@ -142,6 +142,19 @@ def test_product_k_limit_is_checked_before_anything_is_enqueued(lib):
                                  24, ws, big, null) == 2
 
 
+def test_noalloc_validates_before_device_use(lib):
+    vp = ctypes.c_void_p
+    fake, null = vp(1 << 20), vp(0)
+    T = lib_mod._Tensor
+    w = T(1 << 20, 1 << 21, 1 << 22, 256, 4096, 0, 1)
+    # 4096 x 4096 activations need 33.8 MB of workspace: more than the 32 MiB scratch
+    assert lib.gemm_w4aX_noalloc(4, fake, 1, 4096, 4096, ctypes.byref(w), fake, 1, 256, null) == 9
+    assert lib.gemm_w4aX_noalloc(4, fake, 1, 4064, 4096, ctypes.byref(w), fake, 1, 256, null) == 6
+    assert lib.gemm_w4aX_noalloc(16, fake, 1, 4096, 4096, ctypes.byref(w), fake, 1, 256, null) == 6
+    assert lib.gemm_w4aX_noalloc(5, fake, 1, 64, 4096, ctypes.byref(w), fake, 1, 256, null) == 5
+    assert lib.gemm_w4aX_noalloc(4, null, 1, 64, 4096, ctypes.byref(w), fake, 1, 256, null) == 1
+
+
 def test_repack_validates_before_device_use(lib):
     vp = ctypes.c_void_p
     fake, null = vp(1 << 20), vp(0)
