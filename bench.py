@@ -266,6 +266,129 @@ def copy_probe(torch, mib=256, reps=4):
     return dict(bytes_each_way=mib << 20, launches=reps)
 
 
+def device_state():
+    """Clocks and power cap of the GPU as rocm-smi reports them (read-only queries), or
+    the error text when the tool is missing; recorded so that box-to-box differences can
+    be attributed."""
+    import subprocess
+    out = {}
+    for key, args in (("clocks", ["--showclocks"]), ("max_power", ["--showmaxpower"]),
+                      ("power", ["--showpower"])):
+        try:
+            r = subprocess.run(["rocm-smi", *args, "--json"], capture_output=True, text=True, timeout=20)
+            rec = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip() else {"error": r.stderr[-200:]}
+            card = next(iter(rec.values())) if rec and "error" not in rec else rec
+            out[key] = card
+        except Exception as e:  # pragma: no cover - depends on the host
+            out[key] = {"error": str(e)[:200]}
+    return out
+
+
+def probe_library():
+    import ctypes
+    path = os.path.join(ROOT, "block_scaled_fp4_e2m1_amd", "libfp4_probes.so")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.probe_read.argtypes = [vp, i64, vp, i32, i32, vp]
+    lib.probe_mfma.argtypes = [i32, i32, i32, i32, vp, vp]  # clocks: uint64 [2 x blocks]
+    lib.probe_lds_read.argtypes = [i32, i32, vp, vp]
+    for f in (lib.probe_read, lib.probe_mfma, lib.probe_lds_read):
+        f.restype = i32
+    return lib
+
+
+def bench_probes(torch, fp4, steps):
+    """Measured ceilings of this device, beside the spec peaks the roofline fractions use:
+    the HBM read floor at the decode product's weight bytes and launch shapes (16 rotated
+    copies, over 512 MB, so the Infinity Cache cannot hold them; graph replays, per-launch
+    averages as the decode leg measures itself) and at 1 GiB; a device copy; the sustained
+    FP16 MFMA rate and the LDS read bandwidth per compute unit, each with the shader clock
+    the probe ran at (cycles from s_memtime against the 100 MHz real-time counter)."""
+    import ctypes
+    lib = probe_library()
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    res = {"compute_units": cus, "device_state_before": device_state()}
+    timer = Timer(torch)
+
+    def pct(a):
+        return [float(np.percentile(a, q)) for q in (10, 50, 90)]
+
+    # read floor at the decode weights' size (codes + micro + macro) and launch shapes
+    m, k, n = 8, 4096, 14336
+    wbytes = n * k // 2 + n * k // 16 + n * (k // 256) * 2
+    bufs = [torch.ones(wbytes // 4, dtype=torch.int32, device="cuda") for _ in range(ROTATE)]
+    shapes = {"decode_gemv_shape_224x1024": (224, 1024), "cus_x_1024": (cus, 1024),
+              "cus_x_512": (cus, 512), "2cus_x_256": (2 * cus, 256), "4cus_x_256": (4 * cus, 256)}
+    reads = {}
+    for name, (blocks, threads) in shapes.items():
+        fns = [(lambda b=b: lib.probe_read(ctypes.c_void_p(b.data_ptr()), wbytes, ctypes.c_void_p(sink.data_ptr()),
+                                           blocks, threads, st())) for b in bufs]
+        for f in fns:
+            assert f() == 0
+        g = capture(torch, fns)
+        g.replay()
+        per = []
+        for _ in range(max(8, steps // ROTATE)):
+            per.append(timer.region(g.replay, 1) / ROTATE)
+        per = np.array(per)
+        reads[name] = dict(us_per_launch_p10_p50_p90=[x * 1e6 for x in pct(per)],
+                           gbs_p50=wbytes / np.median(per) / 1e9)
+    res["read_floor_decode_weights"] = dict(bytes=wbytes, rotated_copies=ROTATE, launch="HIP graph replay",
+                                            shapes=reads)
+    del bufs
+    big = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
+    best = {}
+    for blocks, threads in ((cus, 1024), (2 * cus, 512), (4 * cus, 256)):
+        fn = lambda: lib.probe_read(ctypes.c_void_p(big.data_ptr()), big.numel() * 4,
+                                    ctypes.c_void_p(sink.data_ptr()), blocks, threads, st())
+        fn()
+        best[f"{blocks}x{threads}"] = big.numel() * 4 / (timer.region(fn, 10) / 10) / 1e9
+    res["read_1gib_gbs"] = best
+    dst = torch.empty_like(big)
+    dst.copy_(big)
+    res["copy_1gib_gbs_read_plus_write"] = 2 * big.numel() * 4 / (timer.region(lambda: dst.copy_(big), 10) / 10) / 1e9
+    del big, dst
+
+    def clocked(fn, blocks, launches):
+        """Runs fn `launches` times (the first ones bring the clocks up), returns the median
+        launch time, and the shader clock of the last launch (median over workgroups)."""
+        clocks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+        for _ in range(launches // 2):
+            assert fn(clocks) == 0
+        t = np.array([timer.region(lambda: fn(clocks), 1) for _ in range(launches // 2)])
+        c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+        ghz = float(np.median(c[:, 0] / (c[:, 1] / 100e6))) / 1e9
+        return float(np.median(t)), ghz, float(np.median(c[:, 0]))
+
+    # MFMA: shapes x waves per SIMD (blocks of 4 waves per CU) x independent accumulators
+    mf = {}
+    for kind, kname, fl in ((0, "16x16x32_f16", 16384), (1, "32x32x16_f16", 32768), (2, "16x16x32_bf16", 16384)):
+        for per_simd, chains in ((1, 8), (2, 8), (4, 8), (4, 16), (8, 4)):
+            if kind == 1 and chains == 16:
+                continue  # 16 accumulators of 16 registers
+            blocks, iters = per_simd * cus, 16384 // per_simd * 8 // chains
+            t, ghz, cyc = clocked(lambda c: lib.probe_mfma(kind, chains, blocks, iters, ctypes.c_void_p(c.data_ptr()),
+                                                           st()), blocks, 16)
+            flops = blocks * 4 * iters * chains * fl
+            mf[f"{kname}_w{per_simd}_c{chains}"] = dict(
+                tflops=round(flops / t / 1e12, 1), frac_of_spec=round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
+                shader_ghz=round(ghz, 3), cycles_per_mfma_per_simd=round(cyc / (per_simd * iters * chains), 2))
+    res["mfma"] = mf
+    # LDS: two blocks (8 waves) per CU
+    blocks, iters = 2 * cus, 8192
+    t, ghz, cyc = clocked(lambda c: lib.probe_lds_read(blocks, iters, ctypes.c_void_p(c.data_ptr()), st()),
+                          blocks, 20)
+    lds_bytes = blocks * 4 * iters * 16 * 1024
+    res["lds_read"] = dict(bytes_per_cu_per_s=lds_bytes / t / cus, shader_ghz=ghz,
+                           bytes_per_clk_per_cu=lds_bytes / t / cus / (ghz * 1e9),
+                           bytes_per_clk_per_cu_from_cycles=2 * 4 * iters * 16 * 1024 / cyc)
+    res["device_state_after"] = device_state()
+    torch.cuda.synchronize()
+    return res
+
+
 def _read_csv(path):
     import csv
     with open(path, newline="") as fh:
@@ -634,7 +757,7 @@ def main():
     ap.add_argument("--skip-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize", "attention", "mx",
-                                       "sensitive"],
+                                       "sensitive", "probes"],
                     default=None,
                     help="run one workload only (for profiling); prints its record")
     ap.add_argument("--copy-probe", action="store_true",
@@ -682,7 +805,8 @@ def main():
               "quantize": lambda: bench_quantize(torch, fp4, workloads, args.steps),
               "attention": lambda: bench_attention(torch, fp4, workloads, args.steps),
               "mx": lambda: bench_mx(torch, fp4, workloads, args.steps),
-              "sensitive": lambda: bench_sensitive(torch, fp4, workloads, args.steps)}[args.only]
+              "sensitive": lambda: bench_sensitive(torch, fp4, workloads, args.steps),
+              "probes": lambda: bench_probes(torch, fp4, args.steps)}[args.only]
         rec = {args.only: fn()}
         if args.copy_probe:
             rec["copy_probe"] = copy_probe(torch)

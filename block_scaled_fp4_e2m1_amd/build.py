@@ -22,6 +22,13 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp4_e2m1.so")
 SOURCES = ["api.cpp", "quant.hip", "repack.hip", "gemv.hip", "gemm.hip", "moe.hip", "attention.hip", "mx.hip"]
 ARCH = "gfx950"
+# measurement probes (copy / read floor, MFMA and LDS rates): a separate library that the
+# benchmark loads; nothing in the product path uses it
+PROBE_SOURCES = ["probes.hip"]
+PROBE_LIB = os.path.join(PKG, "libfp4_probes.so")
+# per-source flags: the MFMA probe keeps its accumulators in ordinary VGPRs (with the
+# accumulation registers the allocator shuffles its 16x16 accumulators every iteration)
+SOURCE_FLAGS = {"probes.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [
@@ -34,7 +41,8 @@ COMMON = [
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *SOURCE_FLAGS.get(src, []), *extra, "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
@@ -44,20 +52,27 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra or [])
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(extra: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link the shared library (and the measurement
+    probes' library); returns the library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = list(extra or [])
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

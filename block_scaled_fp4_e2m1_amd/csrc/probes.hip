@@ -1,0 +1,152 @@
+// Measurement probes for the roofline of this library's kernels on the device at hand
+// (not part of the product path; built into libfp4_probes.so and used by the benchmark):
+//   - probe_read: a streaming read of a buffer (16-byte nontemporal loads, grid-stride,
+//     four loads in flight per thread), the floor of an HBM-bound kernel that reads the
+//     same bytes with the same launch shape;
+//   - probe_mfma: 16-bit MFMAs (16x16x32 f16 / bf16, 32x32x16 f16) back to back on
+//     registers only (4 to 16 independent accumulators per wave), the sustained dense
+//     16-bit matrix rate of each shape;
+//   - probe_lds_read: 16-byte LDS reads (ds_read_b128, 64 consecutive lanes) back to back,
+//     the LDS read bandwidth per compute unit.
+// Every probe accesses only its own buffers inside their bounds and ends after a fixed
+// number of iterations.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "../../include/fp4_probes.h"
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ void k_probe_read(const u32x4_t* __restrict__ p, int64_t n16, uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t a = __builtin_nontemporal_load(p + i);
+    const u32x4_t b = __builtin_nontemporal_load(p + i + stride);
+    const u32x4_t c = __builtin_nontemporal_load(p + i + 2 * stride);
+    const u32x4_t d = __builtin_nontemporal_load(p + i + 3 * stride);
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
+    acc ^= c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4_t a = __builtin_nontemporal_load(p + i);
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+  // the xor of every word read is folded into one word per wave, then into the sink
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink + (blockIdx.x & 1023), acc);
+}
+
+// Lane 0 of wave 0 records the shader-clock and the constant 100 MHz real-time counter
+// deltas over the measured loop, so the clock the probe ran at can be derived.
+__device__ __forceinline__ void record_clocks(uint64_t* clocks, uint64_t t0, uint64_t r0, uint32_t keep) {
+  const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    clocks[2 * blockIdx.x] = t1 - t0 + (keep == 0xDEADBEEFu ? 1u : 0u);
+    clocks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+// KIND 0: v_mfma_f32_16x16x32_f16, 1: v_mfma_f32_32x32x16_f16, 2: v_mfma_f32_16x16x32_bf16;
+// CHAINS independent accumulators per wave.
+template <int KIND, int CHAINS>
+__global__ __launch_bounds__(256) void k_probe_mfma(int iters, uint64_t* __restrict__ clocks) {
+  half8_t a, b;
+  bf16x8_t ab, bb;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (_Float16)(0.001f * (float)(threadIdx.x + i));
+    b[i] = (_Float16)(0.002f * (float)(i + 1));
+    ab[i] = (__bf16)(0.001f * (float)(threadIdx.x + i));
+    bb[i] = (__bf16)(0.002f * (float)(i + 1));
+  }
+  typedef typename std::conditional<KIND == 1, float16_t, float4_t>::type acc_t;
+  acc_t acc[CHAINS];
+  // distinct starting values (a shared zero start makes the register allocator shuffle
+  // the accumulators every iteration)
+  for (int j = 0; j < CHAINS; ++j) {
+    acc[j] = acc_t{};
+    acc[j][0] = 1e-3f * (float)(threadIdx.x + j);
+  }
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < CHAINS; ++j) {
+      if constexpr (KIND == 0) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+      else if constexpr (KIND == 1) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+      else acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, bb, acc[j], 0, 0, 0);
+    }
+  }
+  float s = 0.0f;
+  for (int j = 0; j < CHAINS; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  // the sum keeps every MFMA chain alive; it never equals the marker for these inputs
+  record_clocks(clocks, t0, r0, s == 1234.5f ? 0xDEADBEEFu : 0u);
+}
+
+__global__ __launch_bounds__(256) void k_probe_lds(int iters, uint64_t* __restrict__ clocks) {
+  __shared__ u32x4_t buf[4096];  // 64 KB
+  for (int i = threadIdx.x; i < 4096; i += blockDim.x) buf[i] = u32x4_t{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  const u32x4_t* base = buf + lane;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+    // 16 chunks of 64 consecutive 16-byte words (conflict-free), at a window that moves
+    // with the iteration and the wave; the reads are volatile so that each stays a full
+    // 16-byte read while only one word of it is folded in (one VALU per read)
+    typedef const volatile __attribute__((address_space(3))) u32x4_t lds_u32x4;
+    lds_u32x4* w = (lds_u32x4*)(base + (((it + wave) & 3) << 10));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const u32x4_t v = w[j * 64];
+      acc[j & 3] ^= v[j & 3];
+    }
+  }
+  record_clocks(clocks, t0, r0, acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t probe_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks, int32_t threads,
+                   void* stream) {
+  if (!src || !sink || bytes < 16 || bytes % 16 || blocks < 1 || threads < 64 || threads > 1024 || threads % 64)
+    return 2;
+  hipLaunchKernelGGL(k_probe_read, dim3((unsigned)blocks), dim3((unsigned)threads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4_t*>(src), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 8;
+}
+
+int32_t probe_mfma(int32_t kind, int32_t chains, int32_t blocks, int32_t iters, uint64_t* clocks, void* stream) {
+  if (!clocks || blocks < 1 || iters < 1 || kind < 0 || kind > 2 || (chains != 4 && chains != 8 && chains != 16))
+    return 2;
+  const dim3 g((unsigned)blocks), b(256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+#define FP4_PM(K, C) hipLaunchKernelGGL((k_probe_mfma<K, C>), g, b, 0, st, iters, clocks)
+#define FP4_PM_C(K) do { if (chains == 4) FP4_PM(K, 4); else if (chains == 8) FP4_PM(K, 8); else FP4_PM(K, 16); } while (0)
+  if (kind == 0) FP4_PM_C(0); else if (kind == 1) FP4_PM_C(1); else FP4_PM_C(2);
+#undef FP4_PM_C
+#undef FP4_PM
+  return hipGetLastError() == hipSuccess ? 0 : 8;
+}
+
+int32_t probe_lds_read(int32_t blocks, int32_t iters, uint64_t* clocks, void* stream) {
+  if (!clocks || blocks < 1 || iters < 1) return 2;
+  hipLaunchKernelGGL(k_probe_lds, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters,
+                     clocks);
+  return hipGetLastError() == hipSuccess ? 0 : 8;
+}
+
+}  // extern "C"
