@@ -292,7 +292,9 @@ def probe_library():
     lib.probe_read.argtypes = [vp, i64, vp, i32, i32, vp]
     lib.probe_mfma.argtypes = [i32, i32, i32, i32, vp, vp]  # clocks: uint64 [2 x blocks]
     lib.probe_lds_read.argtypes = [i32, i32, vp, vp]
-    for f in (lib.probe_read, lib.probe_mfma, lib.probe_lds_read):
+    lib.probe_valu.argtypes = [i32, i32, i32, vp, vp]
+    lib.probe_mix.argtypes = [i32, i32, i32, vp, vp]
+    for f in (lib.probe_read, lib.probe_mfma, lib.probe_lds_read, lib.probe_valu, lib.probe_mix):
         f.restype = i32
     return lib
 
@@ -365,7 +367,7 @@ def bench_probes(torch, fp4, steps):
     # MFMA: shapes x waves per SIMD (blocks of 4 waves per CU) x independent accumulators
     mf = {}
     for kind, kname, fl in ((0, "16x16x32_f16", 16384), (1, "32x32x16_f16", 32768), (2, "16x16x32_bf16", 16384)):
-        for per_simd, chains in ((1, 8), (2, 8), (4, 8), (4, 16), (8, 4)):
+        for per_simd, chains in ((1, 8), (2, 8), (4, 8)):
             if kind == 1 and chains == 16:
                 continue  # 16 accumulators of 16 registers
             blocks, iters = per_simd * cus, 16384 // per_simd * 8 // chains
@@ -376,6 +378,25 @@ def bench_probes(torch, fp4, steps):
                 tflops=round(flops / t / 1e12, 1), frac_of_spec=round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
                 shader_ghz=round(ghz, 3), cycles_per_mfma_per_simd=round(cyc / (per_simd * iters * chains), 2))
     res["mfma"] = mf
+    # VALU issue rates: 4 waves per SIMD, 8 independent chains per wave
+    va = {}
+    for kind, kname in enumerate(("cvt_scalef32_pk_f16_fp4", "pk_mul_f16", "perm_b32", "mul_f32",
+                                  "cvt_scalef32_pk_f16_fp8", "and_or_merge", "cvt_scalef32_pk_f32_fp4+xor")):
+        blocks, iters = 4 * cus, 4096
+        t, ghz, cyc = clocked(lambda c: lib.probe_valu(kind, blocks, iters, ctypes.c_void_p(c.data_ptr()), st()),
+                              blocks, 8)
+        # instructions per SIMD: 4 waves x iters x 8; cycles from the wall time and the clock
+        va[kname] = dict(cycles_per_wave_instruction=round(t * ghz * 1e9 / (4 * iters * 8), 2), shader_ghz=round(ghz, 3))
+    res["valu"] = va
+    # MFMA + independent VALU in one instruction stream: cycles per iteration of 8 MFMAs
+    mx = {}
+    for per_simd in (1, 2, 4):
+        for nv in (0, 8, 16, 24, 32, 48):
+            blocks, iters = per_simd * cus, 8192 // per_simd
+            t, ghz, cyc = clocked(lambda c: lib.probe_mix(nv, blocks, iters, ctypes.c_void_p(c.data_ptr()), st()),
+                                  blocks, 8)
+            mx[f"w{per_simd}_valu{nv}"] = round(t * ghz * 1e9 / (per_simd * iters), 1)
+    res["mix_cycles_per_8_mfma_per_simd"] = mx
     # LDS: two blocks (8 waves) per CU
     blocks, iters = 2 * cus, 8192
     t, ghz, cyc = clocked(lambda c: lib.probe_lds_read(blocks, iters, ctypes.c_void_p(c.data_ptr()), st()),

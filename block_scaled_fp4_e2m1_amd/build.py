@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp4_e2m1.so")
-SOURCES = ["api.cpp", "quant.hip", "repack.hip", "gemv.hip", "gemm.hip", "moe.hip", "attention.hip", "mx.hip"]
+SOURCES = ["api.cpp", "quant.hip", "repack.hip", "gemv.hip", "gemm.hip", "gemm_r8.hip", "moe.hip", "attention.hip",
+           "mx.hip"]
 ARCH = "gfx950"
 # measurement probes (copy / read floor, MFMA and LDS rates): a separate library that the
 # benchmark loads; nothing in the product path uses it

@@ -84,6 +84,11 @@ bool gemm_plan_ok(int64_t m, int64_t n, int64_t k, int grouped, int n_experts, i
 // Name of the kernel form launch_gemm selects for that shape (nullptr when refused).
 const char* gemm_kernel_name(int64_t m, int64_t n, int64_t k, int grouped, int n_experts, int w_e4m3);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// The 128-row-wave form for large dense E2M1 products (128 x 256 workgroup tiles, one per
+// CU): the shapes it covers (its LDS holds three operand stages and the row-factor table:
+// k <= 8192) and its launcher (hipErrorInvalidValue outside gemm_r8_supports()).
+bool gemm_r8_supports(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_r8(const GemmArgs& g, hipStream_t st);
 
 // Plain float32 product for float32 activations (small shapes): one thread per output.
 hipError_t launch_gemm_f32act(const float* a, int64_t lda, int64_t m, int64_t k,

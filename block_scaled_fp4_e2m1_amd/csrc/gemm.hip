@@ -34,82 +34,14 @@
 
 #include "fp4_device.h"
 #include "fp4_kernels.h"
+#include "gemm_ops.h"
 
 using namespace fp4dev;
 using fp4lib::GemmArgs;
 
 namespace {
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(1))) void* global_void_ptr;
-
-template <int A_BF16>
-struct OpTraits;
-
-template <>
-struct OpTraits<0> {  // FP16 operands
-  typedef half8_t frag;
-  // micro-scale operand: the E4M3 byte shifted into the FP16 bit positions of both halves
-  // is mu * 2^-8 exactly (E4M3 subnormals land on FP16 subnormals); the 2^8 is folded
-  // into the column factor
-  static constexpr float kMicroUnit = 256.0f;
-  __device__ static __forceinline__ uint32_t micro_operand(uint32_t byte) { return (byte << 7) | (byte << 23); }
-  __device__ static __forceinline__ frag weight(uint32_t cw, uint32_t mu_op) {
-    const half2_t m2 = __builtin_bit_cast(half2_t, mu_op);
-    const half2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * m2;
-    const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * m2;
-    const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * m2;
-    const half2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * m2;
-    return frag{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
-  }
-  // E4M3 weights (8 codes in two dwords): each code pair is converted with scale 2^5
-  // (exact: the conversion applies a power of two) and multiplied by mu * 2^-8, so the
-  // operand is e4m3 * mu * 2^-3, exact in FP16 (at most 8 significant bits, lowest bit
-  // >= 2^-21, at most 25088); the column factor carries the 8
-  static constexpr float kMicroUnit8 = 8.0f;
-  __device__ static __forceinline__ frag weight8(uint32_t d0, uint32_t d1, uint32_t mu_op) {
-    const half2_t m2 = __builtin_bit_cast(half2_t, mu_op);
-    const half2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 32.0f, false) * m2;
-    const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 32.0f, true) * m2;
-    const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 32.0f, false) * m2;
-    const half2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 32.0f, true) * m2;
-    return frag{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
-  }
-  __device__ static __forceinline__ float4_t mfma(frag a, frag b, float4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct OpTraits<1> {  // bf16 operands
-  typedef bf16x8_t frag;
-  // micro-scale operand: the E4M3 value as float32 bits
-  static constexpr float kMicroUnit = 1.0f;
-  __device__ static __forceinline__ uint32_t micro_operand(uint32_t byte) {
-    return __float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)byte, 0));
-  }
-  __device__ static __forceinline__ uint32_t pack(float lo, float hi) {
-    // both values are exact in bf16: take the high halves
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-  }
-  __device__ static __forceinline__ frag weight(uint32_t cw, uint32_t mu_op) {
-    const float mu = __uint_as_float(mu_op);
-    uint32_t w[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float2_t f;
-      if (s == 0) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
-      else if (s == 1) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
-      else if (s == 2) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
-      else f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
-      w[s] = pack(f[0] * mu, f[1] * mu);
-    }
-    return __builtin_bit_cast(frag, make_uint4(w[0], w[1], w[2], w[3]));
-  }
-  __device__ static __forceinline__ float4_t mfma(frag a, frag b, float4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
+using namespace fp4gemm;
 
 // Locate the tile of a grouped launch: tile index t runs over the concatenation of every
 // expert's ceil(rows_e / BM) row tiles. One wave computes the prefix sum of the tile
@@ -798,7 +730,7 @@ int device_cus() {
 // Kernel form and grid of a product (the selection launch_gemm makes); false when the
 // shape is outside what the kernels cover (k tables over the LDS budget, grid too large).
 struct GemmPlan {
-  bool narrow, wide16, w10;
+  bool r8, narrow, wide16, w10;
   int64_t bn, blocks;
   unsigned threads;
   size_t lds;
@@ -811,9 +743,20 @@ static bool plan_gemm(int64_t m, int64_t n, int64_t k, bool grouped, int n_exper
   int64_t tiles_m;
   if (grouped) tiles_m = (m + kBM - 1) / kBM + n_experts;  // upper bound
   else tiles_m = (m + kBM - 1) / kBM;
+  const int64_t cus = device_cus();
+  // dense E2M1 products whose 128 x 256 tiles give every CU a workgroup take the
+  // 128-row-wave form (a decoded weight fragment feeds 8 MFMAs instead of 4)
+  p.r8 = !e4m3 && !grouped && gemm_r8_supports(m, n, k) && ((m + 127) / 128) * ((n + 255) / 256) >= cus;
+  if (p.r8) {
+    p.narrow = p.wide16 = p.w10 = false;
+    p.bn = 256;
+    p.blocks = ((m + 127) / 128) * ((n + 255) / 256);
+    p.threads = 512;
+    p.lds = 0;
+    return p.blocks <= 0x7FFFFFFF;
+  }
   // dense E2M1 products whose 64 x 256 tiles cannot give every CU two workgroups take the
   // narrow 64 x 128 tile
-  const int64_t cus = device_cus();
   p.narrow = !e4m3 && !grouped && tiles_m * ((n + WShape<0>::BN - 1) / WShape<0>::BN) < 2 * cus;
   // dense E2M1 products whose 64 x 512 tiles still give every CU a workgroup take the
   // 16-wave form: four waves per SIMD, one activation stage for twice the weight columns
@@ -851,6 +794,7 @@ bool gemm_plan_ok(int64_t m, int64_t n, int64_t k, int grouped, int n_experts, i
 const char* gemm_kernel_name(int64_t m, int64_t n, int64_t k, int grouped, int n_experts, int w_e4m3) {
   GemmPlan p;
   if (!plan_gemm(m, n, k, grouped != 0, n_experts, w_e4m3 != 0, p)) return nullptr;
+  if (p.r8) return "k_gemm_r8 (128 x 256, 8 waves of 128 x 32)";
   if (p.wide16) return "k_gemm_w16 (64 x 512, 16 waves)";
   if (p.w10) return w_e4m3 ? "k_gemm_w10e (64 x 160, 10 waves, E4M3)" : "k_gemm_w10 (64 x 160, 10 waves)";
   if (w_e4m3) return "k_gemm (64 x 128, 8 waves, E4M3)";
@@ -863,6 +807,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   GemmPlan p;
   if (!plan_gemm(g.m, g.n, g.k, g.expert_offsets != nullptr, g.n_experts, g.w_e4m3 != 0, p))
     return hipErrorInvalidValue;
+  if (p.r8) return launch_gemm_r8(g, st);
   const bool narrow = p.narrow, wide16 = p.wide16, w10 = p.w10;
   const dim3 grid((unsigned)p.blocks), block(p.threads);
   const size_t lds = p.lds;

@@ -93,6 +93,89 @@ __global__ __launch_bounds__(256) void k_probe_mfma(int iters, uint64_t* __restr
   record_clocks(clocks, t0, r0, s == 1234.5f ? 0xDEADBEEFu : 0u);
 }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// VALU throughput of one instruction kind: CHAINS (8) independent dependency chains per
+// wave, each iteration one instruction per chain. KIND 0: v_cvt_scalef32_pk_f16_fp4,
+// 1: v_pk_mul_f16, 2: v_perm_b32, 3: v_mul_f32, 4: v_cvt_scalef32_pk_f16_fp8,
+// 5: v_bfi_b32, 6: v_cvt_scalef32_pk_f32_fp4 (two results).
+template <int KIND>
+__global__ __launch_bounds__(256) void k_probe_valu(int iters, uint64_t* __restrict__ clocks) {
+  constexpr int C = 8;
+  uint32_t u[C];
+  for (int j = 0; j < C; ++j) u[j] = 0x3C003C00u ^ (threadIdx.x * 2654435761u + j * 40503u);
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      if constexpr (KIND == 0) {
+        u[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u[j], 1.0f, 0));
+      } else if constexpr (KIND == 1) {
+        const half2_t h = __builtin_bit_cast(half2_t, u[j]);
+        u[j] = __builtin_bit_cast(uint32_t, h * h);
+      } else if constexpr (KIND == 2) {
+        u[j] = __builtin_amdgcn_perm(u[j], u[(j + 1) & 7], 0x0C050C01u);
+      } else if constexpr (KIND == 3) {
+        u[j] = __float_as_uint(__uint_as_float(u[j]) * 1.0001f);
+      } else if constexpr (KIND == 4) {
+        u[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u[j], 1.0f, false));
+      } else if constexpr (KIND == 5) {
+        u[j] = (u[j] & 0x80808080u) | (u[(j + 3) & 7] & 0x7F7F7F7Fu);
+      } else {
+        const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u[j], 1.0f, 0);
+        u[j] = __float_as_uint(f[0]) ^ __float_as_uint(f[1]);
+      }
+    }
+  }
+  uint32_t x = 0;
+  for (int j = 0; j < C; ++j) x ^= u[j];
+  record_clocks(clocks, t0, r0, x);
+}
+
+// MFMA / VALU overlap: per iteration 8 v_mfma_f32_16x16x32_f16 on 8 independent
+// accumulators and NV v_pk_mul_f16 on 8 independent chains (no data shared with the
+// MFMAs), interleaved one VALU group after each MFMA. If the SIMD overlaps the two, an
+// iteration costs max(8 MFMA, NV VALU); if it serializes them, their sum.
+template <int NV>
+__global__ __launch_bounds__(256) void k_probe_mix(int iters, uint64_t* __restrict__ clocks) {
+  half8_t a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (_Float16)(0.001f * (float)(threadIdx.x + i));
+    b[i] = (_Float16)(0.002f * (float)(i + 1));
+  }
+  float4_t acc[8];
+  uint32_t u[8];
+  for (int j = 0; j < 8; ++j) {
+    acc[j] = float4_t{1e-3f * (float)(threadIdx.x + j), 0.0f, 0.0f, 0.0f};
+    u[j] = 0x3C003C00u ^ (threadIdx.x * 2654435761u + j * 40503u);
+  }
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < NV / 8; ++v) {
+        const int c = (j + v) & 7;
+        const half2_t h = __builtin_bit_cast(half2_t, u[c]);
+        u[c] = __builtin_bit_cast(uint32_t, h * h);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+      if (NV) __builtin_amdgcn_sched_group_barrier(0x002, NV / 8, 0);  // VALU
+    }
+  }
+  float s = 0.0f;
+  uint32_t x = 0;
+  for (int j = 0; j < 8; ++j) {
+    s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    x ^= u[j];
+  }
+  record_clocks(clocks, t0, r0, (s == 1234.5f ? 0xDEADBEEFu : 0u) ^ (x == 0x01234567u ? 1u : 0u));
+}
+
 __global__ __launch_bounds__(256) void k_probe_lds(int iters, uint64_t* __restrict__ clocks) {
   __shared__ u32x4_t buf[4096];  // 64 KB
   for (int i = threadIdx.x; i < 4096; i += blockDim.x) buf[i] = u32x4_t{(uint32_t)i, 1u, 2u, 3u};
@@ -139,6 +222,38 @@ int32_t probe_mfma(int32_t kind, int32_t chains, int32_t blocks, int32_t iters, 
   if (kind == 0) FP4_PM_C(0); else if (kind == 1) FP4_PM_C(1); else FP4_PM_C(2);
 #undef FP4_PM_C
 #undef FP4_PM
+  return hipGetLastError() == hipSuccess ? 0 : 8;
+}
+
+int32_t probe_valu(int32_t kind, int32_t blocks, int32_t iters, uint64_t* clocks, void* stream) {
+  if (!clocks || blocks < 1 || iters < 1 || kind < 0 || kind > 6) return 2;
+  const dim3 g((unsigned)blocks), b(256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(k_probe_valu<0>, g, b, 0, st, iters, clocks); break;
+    case 1: hipLaunchKernelGGL(k_probe_valu<1>, g, b, 0, st, iters, clocks); break;
+    case 2: hipLaunchKernelGGL(k_probe_valu<2>, g, b, 0, st, iters, clocks); break;
+    case 3: hipLaunchKernelGGL(k_probe_valu<3>, g, b, 0, st, iters, clocks); break;
+    case 4: hipLaunchKernelGGL(k_probe_valu<4>, g, b, 0, st, iters, clocks); break;
+    case 5: hipLaunchKernelGGL(k_probe_valu<5>, g, b, 0, st, iters, clocks); break;
+    default: hipLaunchKernelGGL(k_probe_valu<6>, g, b, 0, st, iters, clocks); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 8;
+}
+
+int32_t probe_mix(int32_t valu_per_8, int32_t blocks, int32_t iters, uint64_t* clocks, void* stream) {
+  if (!clocks || blocks < 1 || iters < 1) return 2;
+  const dim3 g((unsigned)blocks), b(256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (valu_per_8) {
+    case 0: hipLaunchKernelGGL(k_probe_mix<0>, g, b, 0, st, iters, clocks); break;
+    case 8: hipLaunchKernelGGL(k_probe_mix<8>, g, b, 0, st, iters, clocks); break;
+    case 16: hipLaunchKernelGGL(k_probe_mix<16>, g, b, 0, st, iters, clocks); break;
+    case 24: hipLaunchKernelGGL(k_probe_mix<24>, g, b, 0, st, iters, clocks); break;
+    case 32: hipLaunchKernelGGL(k_probe_mix<32>, g, b, 0, st, iters, clocks); break;
+    case 48: hipLaunchKernelGGL(k_probe_mix<48>, g, b, 0, st, iters, clocks); break;
+    default: return 2;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 8;
 }
 

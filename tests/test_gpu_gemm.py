@@ -6,9 +6,12 @@ Gates (float32 accumulation on exact operands):
   bf16 output:    ||C - RNE_bf16(C64)||_F / ||RNE_bf16(C64)||_F <= 1e-3 and >= 99.9% of
                   elements equal to RNE_bf16(C64) or one bf16 step away.
 Full-size workloads are checked on sampled rows/columns that the oracle computes one by
-one; small shapes (several tiles plus ragged tails) are checked in full. Small dense
-products run on the narrow 64 x 128 tile; a ragged 2043 x 4080 product covers the wide
-64 x 256 one (the full-size prefill and the grouped products use it too)."""
+one; small shapes (several tiles plus ragged tails) are checked in full. Each kernel form
+is reached by a shape chosen for it (fp4_product_kernel names the form a shape runs, and
+the tests assert it): small dense products run the narrow 64 x 128 tile, 500-row products
+the 10-wave 64 x 160 form, large ones (the prefill among them) the 128-row-wave 128 x 256
+form, large ones above k = 8192 the 16-wave 64 x 512 form, k > 13056 the 64 x 256 form;
+grouped products run the grouped 64 x 256 form. All forms agree bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -106,26 +109,74 @@ def test_gemm_small_shapes(act, m, n, k):
 
 
 @pytest.mark.parametrize("act", [16, 8, 4])
-@pytest.mark.parametrize("k", [256, 1024])
-def test_gemm_wide_512_tiles_ragged(act, k):
-    """Small products take the narrow 64 x 128 tile; this shape (2043 x 4080: 32 x 8 tiles
-    of 64 x 512, the last row and column tiles ragged) is large enough for the 16-wave
-    64 x 512 form. k = 1024 crosses three group boundaries, so the per-group rescale of
-    both the bf16 (A16) and the FP16 (A4 / A8) operand forms runs in it."""
+@pytest.mark.parametrize("k", [256, 1024, 2816])
+def test_gemm_r8_tiles_ragged(act, k):
+    """Small products take the narrow 64 x 128 tile; this shape (2043 x 4080: 16 x 16 tiles
+    of 128 x 256, the last row and column tiles ragged) is large enough for the 128-row-
+    wave form. k = 1024 and 2816 cross 3 and 10 group boundaries (an odd group count ends
+    the form's six-stage pass early), so the per-group rescale of both the bf16 (A16) and
+    the FP16 (A4 / A8) operand paths runs in it."""
     m, n = 2043, 4080
     name = fp4.fp4_product_kernel(act, torch.bfloat16, m, n, k)
-    assert name.startswith("k_gemm_w16"), f"shape no longer selects the 16-wave form ({name})"
+    assert name.startswith("k_gemm_r8"), f"shape no longer selects the 128-row-wave form ({name})"
     rng = np.random.default_rng(310 + act + k)
     a = rng.standard_normal((m, k)).astype(np.float32)
     a[:, rng.choice(k, 3, replace=False)] *= 50
     a = workloads.to_bf16_values(a)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
-    print(f"[case] gemm 64x512 tiles {ACTS[act]} m={m} n={n} k={k} ({name})", flush=True)
+    print(f"[case] gemm 128x256 tiles {ACTS[act]} m={m} n={n} k={k} ({name})", flush=True)
     wq = _wq(w)
     ad = to_device_bf16(a)
     ref = _oracle_c(a.astype(np.float64), w, act)
     f32_gate(host(fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32)), ref)
     bf16_gate(bf16_values(fp4.gemm_w4aX(act, ad, wq)), oracle.formats.bf16_round(ref))
+
+
+@pytest.mark.parametrize("act", [16, 4])
+def test_gemm_wide_512_tiles_large_k_sampled(act):
+    """Above k = 8192 the 128-row-wave form's LDS no longer holds its row-factor table, so a
+    large dense product (2043 x 4080, ragged) runs the 16-wave 64 x 512 form up to
+    k = 13056; k = 8448 (33 groups) checked on sampled rows and columns, the last row and
+    column tiles among them."""
+    m, n, k = 2043, 4080, 8448
+    name = fp4.fp4_product_kernel(act, torch.bfloat16, m, n, k)
+    assert name.startswith("k_gemm_w16"), f"shape no longer selects the 16-wave form ({name})"
+    rng = np.random.default_rng(315 + act)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    a[:, rng.choice(k, 5, replace=False)] *= 50
+    a = workloads.to_bf16_values(a)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    print(f"[case] gemm 64x512 tiles large k {ACTS[act]} m={m} n={n} k={k} (sampled)", flush=True)
+    c = fp4.gemm_w4aX(act, to_device_bf16(a), _wq(w), out_dtype=torch.float32)
+    rows = np.union1d(rng.choice(m - 64, 24, replace=False), np.arange(m - 11, m))
+    cols = np.union1d(rng.choice(n - 512, 48, replace=False), np.arange(n - 496, n, 31))
+    ref = _oracle_c(a[rows].astype(np.float64), w[cols], act)
+    f32_gate(host(c)[np.ix_(rows, cols)], ref)
+
+
+@pytest.mark.parametrize("act", [16, 4])
+def test_gemm_forms_agree_bit_for_bit(act):
+    """Every kernel form gives each output element the same operations in the same order
+    (the 16x16x32 MFMA steps in k order, the same per-group rescale), so the same product
+    computed through different forms is identical bit for bit: the full 2043 x 4080 x 1024
+    product (128-row-wave form), a 64-row slice of it (narrow 64 x 128 form) and two
+    576-row slices (10-wave 64 x 160 form) with the same weights, compared on the rows they
+    share."""
+    m, n, k = 2043, 4080, 1024
+    rng = np.random.default_rng(340 + act)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    a[:, rng.choice(k, 3, replace=False)] *= 50
+    ad = to_device_bf16(workloads.to_bf16_values(a))
+    wq = _wq((0.02 * rng.standard_normal((n, k))).astype(np.float32))
+    full = fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32)
+    seen = {fp4.fp4_product_kernel(act, torch.bfloat16, m, n, k)}
+    for r0, r1 in ((1979, 2043), (0, 576), (1024, 1600)):
+        name = fp4.fp4_product_kernel(act, torch.bfloat16, r1 - r0, n, k)
+        seen.add(name)
+        print(f"[case] forms agree {ACTS[act]} rows {r0}:{r1} ({name})", flush=True)
+        part = fp4.gemm_w4aX(act, ad[r0:r1].contiguous(), wq, out_dtype=torch.float32)
+        assert torch.equal(part, full[r0:r1]), f"rows {r0}:{r1} ({name}) differ from the full product"
+    assert len(seen) == 3, f"the slices no longer exercise three different forms: {seen}"
 
 
 @pytest.mark.parametrize("act", [4, 8, 16])
