@@ -50,7 +50,7 @@ def test_probe_library_exports_its_header_and_validates():
         pytest.fail("libfp4_probes.so is not built (python -m block_scaled_fp4_e2m1_amd.build)")
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "fp4_probes.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"^\s*int32_t\s+([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)))
-    assert names == ["probe_lds_read", "probe_mfma", "probe_read"]
+    assert names == ["probe_lds_read", "probe_mfma", "probe_mix", "probe_read", "probe_valu"]
     plib = ctypes.CDLL(path)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     for n in names:
@@ -58,6 +58,8 @@ def test_probe_library_exports_its_header_and_validates():
     plib.probe_read.argtypes = [vp, i64, vp, i32, i32, vp]
     plib.probe_mfma.argtypes = [i32, i32, i32, i32, vp, vp]
     plib.probe_lds_read.argtypes = [i32, i32, vp, vp]
+    plib.probe_valu.argtypes = [i32, i32, i32, vp, vp]
+    plib.probe_mix.argtypes = [i32, i32, i32, vp, vp]
     fake, null = vp(1 << 20), vp(0)
     assert plib.probe_read(fake, 100, fake, 4, 256, null) == 2      # bytes % 16
     assert plib.probe_read(fake, 1024, fake, 4, 96, null) == 2      # threads % 64
@@ -65,6 +67,8 @@ def test_probe_library_exports_its_header_and_validates():
     assert plib.probe_mfma(3, 8, 4, 4, fake, null) == 2            # unknown kind
     assert plib.probe_mfma(0, 5, 4, 4, fake, null) == 2            # chains
     assert plib.probe_lds_read(4, 0, fake, null) == 2
+    assert plib.probe_valu(7, 4, 4, fake, null) == 2
+    assert plib.probe_mix(12, 4, 4, fake, null) == 2
 
 
 def test_status_strings(lib):
