@@ -59,6 +59,10 @@ __shared__ uint4 g_ra2[kAChunks];
 __shared__ uint4 g_rw0[kWChunks];
 __shared__ uint4 g_rw1[kWChunks];
 __shared__ uint4 g_rw2[kWChunks];
+// row-factor ratios of the FP16 operand path, [G][128]: a static object (k <= 8192), so the
+// compiler can tell its reads from the slots the LDS-DMA copies are filling
+constexpr int kMaxGroups = 32;
+__shared__ float g_sa[kMaxGroups * kBM];
 
 template <int B>
 __device__ __forceinline__ uint4* a_slot() {
@@ -77,7 +81,6 @@ template <int A_BF16, int C_BF16>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   typedef OpTraits<A_BF16> Op;
   typedef typename Op::frag frag;
-  extern __shared__ float g_sa[];  // [G][128]: row-factor ratios f_g / f_{g+1} (last: f_{G-1})
   const int groups = (int)(args.k >> 8);
   const int stages = 2 * groups;
   const int64_t nblocks = args.n >> 4;
@@ -204,10 +207,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   const float* sa_lane = g_sa + 4 * q;  // + g * 128 + 16 mi: rows 16 mi + 4 q .. + 3
   // column ratio of the boundary after group g (after the last group: the final factor)
   auto col_ratios = [&](float (&rw)[kNI], int g, const uint32_t (&m_cur)[kNI], const uint32_t (&m_nxt)[kNI]) {
+    const bool last = g + 1 >= groups;  // (selects, not branches: the step stays one region)
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni)
-      rw[ni] = g + 1 < groups ? col_factor(m_cur[ni]) * __builtin_amdgcn_rcpf(col_factor(m_nxt[ni]))
-                              : col_factor(m_cur[ni]) * kUnit;
+      rw[ni] = col_factor(m_cur[ni]) * (last ? kUnit : __builtin_amdgcn_rcpf(col_factor(m_nxt[ni])));
   };
   auto products = [&](float (&pp)[kMI][kNI][4], int g, const float (&rw)[kNI], int mi_lo, int mi_hi) {
 #pragma unroll
@@ -231,24 +234,46 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
 
   // One MFMA step: the step's 16 MFMAs (row block major); each activation fragment is
   // reloaded for the next step right after its two MFMAs (from `anext` at step `tnext`),
-  // and the next step's weight fragments are decoded meanwhile. RESCALE: multiply each
-  // tile by its factor product just before its first MFMA of the group.
-  auto mfma_step = [&](auto rescale_c, const uint4* anext, int tnext, frag (&wn)[kNI]) {
-    constexpr bool RESCALE = decltype(rescale_c)::value;
+  // and the next step's weight fragments are decoded meanwhile. The rescale of a group
+  // boundary is split over the two steps around it: POST (a group's last step) multiplies
+  // row blocks 0..3 by the products `pp` once their last MFMAs of the group are done; PRE
+  // (the next group's first step) multiplies row blocks 4..7 before their first MFMAs.
+  auto mfma_step = [&](auto pre_c, auto post_c, const uint4* anext, int tnext, frag (&wn)[kNI],
+                       const float (&pp)[kMI][kNI][4]) {
+    constexpr bool PRE = decltype(pre_c)::value, POST = decltype(post_c)::value;
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi) {
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) {
-        if constexpr (RESCALE) {
+      for (int ni = 0; ni < kNI; ++ni) x[mi][ni] = Op::mfma(af[mi], wf[ni], x[mi][ni]);
+      if constexpr (PRE) {
+        if (mi < kMI / 2) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[mi][ni][i] *= p[mi][ni][i];
+          for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[mi + kMI / 2][ni][i] *= pp[mi + kMI / 2][ni][i];
         }
-        x[mi][ni] = Op::mfma(af[mi], wf[ni], x[mi][ni]);
+      }
+      if constexpr (POST) {
+        if (mi >= kMI / 2) {
+#pragma unroll
+          for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[mi - kMI / 2][ni][i] *= pp[mi - kMI / 2][ni][i];
+        }
       }
       af[mi] = __builtin_bit_cast(frag, anext[(mi * kSteps + tnext) * 64 + lane]);
     }
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) wf[ni] = wn[ni];
+    // MFMA, VALU, MFMA, VALU, LDS read per row block (up to 6 VALU in each slot)
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
   };
 
   typedef std::integral_constant<bool, true> kTrue;
@@ -257,38 +282,44 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   // Stage s in ring slot B (s % 3), H = s & 1 (H == 0: the first stage of group g).
   //   steps 0..2: MFMAs with the fragments reloaded from this slot; step 3 (after the
   //   barrier) reloads from the next slot and decodes the next stage's first weights;
-  //   H == 0, g > 0: step 0 applies the previous boundary's factor products;
-  //   H == 1: the products of this group's boundary are formed during steps 0..3.
+  //   H == 0 (RESCALE: every group but the first): step 0 finishes the previous boundary's
+  //   rescale; H == 1: the products of this group's boundary are formed in steps 0..2 and
+  //   step 3 starts its rescale.
   // Wait before the barrier: stage s + 1's copies (issued after barrier s - 2) must have
   // landed; younger than them are the register loads of barrier s - 1 (when s - 1 is a
   // group's first stage) and the copies of barrier s - 1.
   float pn[kMI][kNI][4];
-  auto run_stage = [&](auto b_c, auto h_c, int s) {
+  auto run_stage = [&](auto b_c, auto h_c, auto rescale_c, int s) {
     constexpr int B = decltype(b_c)::value, H = decltype(h_c)::value;
+    constexpr bool RESCALE = decltype(rescale_c)::value;
     constexpr int BN1 = (B + 1) % 3;
+    typedef std::integral_constant<bool, H == 0 && RESCALE> kPre;
+    typedef std::integral_constant<bool, H == 1> kPost;
     const int g = s >> 1;
     uint4* abuf = a_slot<B>();
     frag wn[kNI];
+    float rw[kNI];
     // step 0
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) wn[ni] = Op::template weight_step<1>((&cw[ni].x)[1], H ? mu[ni].y : mu[ni].x);
-    if (H == 0 && g > 0) mfma_step(kTrue{}, abuf, 1, wn);
-    else mfma_step(kFalse{}, abuf, 1, wn);
-    float rw[kNI];
+    for (int ni = 0; ni < kNI; ++ni) wn[ni] = Op::template weight_step<1>(cw[ni].y, H ? mu[ni].y : mu[ni].x);
     if (H == 1) {
       col_ratios(rw, g, mw0, mw1);
       products(pn, g, rw, 0, 3);
     }
+    mfma_step(kPre{}, kFalse{}, abuf, 1, wn, p);
+    __builtin_amdgcn_sched_barrier(0);
     // step 1
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) wn[ni] = Op::template weight_step<2>((&cw[ni].x)[2], H ? mu[ni].y : mu[ni].x);
-    mfma_step(kFalse{}, abuf, 2, wn);
+    for (int ni = 0; ni < kNI; ++ni) wn[ni] = Op::template weight_step<2>(cw[ni].z, H ? mu[ni].y : mu[ni].x);
     if (H == 1) products(pn, g, rw, 3, 6);
+    mfma_step(kFalse{}, kFalse{}, abuf, 2, wn, p);
+    __builtin_amdgcn_sched_barrier(0);
     // step 2
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) wn[ni] = Op::template weight_step<3>((&cw[ni].x)[3], H ? mu[ni].y : mu[ni].x);
-    mfma_step(kFalse{}, abuf, 3, wn);
+    for (int ni = 0; ni < kNI; ++ni) wn[ni] = Op::template weight_step<3>(cw[ni].w, H ? mu[ni].y : mu[ni].x);
     if (H == 1) products(pn, g, rw, 6, 8);
+    mfma_step(kFalse{}, kFalse{}, abuf, 3, wn, p);
+    __builtin_amdgcn_sched_barrier(0);
     // barrier: stage s + 1 published, this slot free
     constexpr int kWait = kCopies + (H == 1 ? kLoads : 0);
     __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<kWait>::value);
@@ -301,16 +332,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
     copy_stage(a_slot<B>(), w_slot<B>(), s + 3);
     __builtin_amdgcn_sched_barrier(0);
     // step 3: the next stage's code words and first weight fragments
-    uint4 cwn[kNI];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
-      cwn[ni] = w_slot<BN1>()[(wave * kNI + ni) * 64 + lane];
+      cw[ni] = w_slot<BN1>()[(wave * kNI + ni) * 64 + lane];
       // next stage: same group (H == 0: second micro-scale word) or the next group's first
-      wn[ni] = Op::template weight_step<0>(cwn[ni].x, H ? mun[ni].x : mu[ni].y);
+      wn[ni] = Op::template weight_step<0>(cw[ni].x, H ? mun[ni].x : mu[ni].y);
     }
-    mfma_step(kFalse{}, a_slot<BN1>(), 0, wn);
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) cw[ni] = cwn[ni];
+    mfma_step(kFalse{}, kPost{}, a_slot<BN1>(), 0, wn, pn);
+    __builtin_amdgcn_sched_barrier(0);
     if (H == 1) {  // next group: rotate the scales and the products
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni) {
@@ -329,22 +358,24 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   typedef std::integral_constant<int, 0> C0;
   typedef std::integral_constant<int, 1> C1;
   typedef std::integral_constant<int, 2> C2;
-  // six stages per pass (slots cycle by 3, halves by 2); every pass ends on a group
-  for (int s = 0;; s += 6) {
-    run_stage(C0{}, C0{}, s);
-    run_stage(C1{}, C1{}, s + 1);
+  // group 0 (no boundary before it), then six stages per pass (slots cycle by 3, halves by
+  // 2) starting at stage 2 (slot 2); every pass ends on a group boundary
+  run_stage(C0{}, C0{}, kFalse{}, 0);
+  run_stage(C1{}, C1{}, kFalse{}, 1);
+  for (int s = 2; s < stages; s += 6) {
+    run_stage(C2{}, C0{}, kTrue{}, s);
+    run_stage(C0{}, C1{}, kTrue{}, s + 1);
     if (s + 2 >= stages) break;
-    run_stage(C2{}, C0{}, s + 2);
-    run_stage(C0{}, C1{}, s + 3);
+    run_stage(C1{}, C0{}, kTrue{}, s + 2);
+    run_stage(C2{}, C1{}, kTrue{}, s + 3);
     if (s + 4 >= stages) break;
-    run_stage(C1{}, C0{}, s + 4);
-    run_stage(C2{}, C1{}, s + 5);
-    if (s + 6 >= stages) break;
+    run_stage(C0{}, C0{}, kTrue{}, s + 4);
+    run_stage(C1{}, C1{}, kTrue{}, s + 5);
   }
   // the ring's last copies (zeros from the empty resource) complete before exit
   __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
 
-  // ---- final factors (the last group's products), store ----
+  // ---- final factors (the last group's products; row blocks 0..3 have them), store ----
   const int64_t n0 = wb0 * 16;
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
@@ -356,7 +387,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
       for (int i = 0; i < 4; ++i) {
         const int64_t r = row_begin + 16 * mi + 4 * q + i;
         if (r >= row_end) continue;
-        const float v = x[mi][ni][i] * p[mi][ni][i];
+        // row blocks 0..3 were multiplied by the final factors in the last step
+        const float v = mi < kMI / 2 ? x[mi][ni][i] : x[mi][ni][i] * p[mi][ni][i];
         if (C_BF16)
           static_cast<uint16_t*>(args.c)[r * args.ldc + col] = (uint16_t)bf16_rne_bits(v);
         else
@@ -370,11 +402,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
 
 namespace fp4lib {
 
-// LDS of the form: three activation and weight slots (144 KB) and the row-factor ratios.
-size_t gemm_r8_lds(int64_t k) { return (size_t)(k >> 8) * kBM * sizeof(float); }
+// LDS of the form (all static): three activation and weight slots (144 KB) and the
+// row-factor ratios of up to 32 groups (16 KB).
 bool gemm_r8_supports(int64_t m, int64_t n, int64_t k) {
-  const size_t statics = (size_t)3 * (kAChunks + kWChunks) * 16;
-  return m >= 1 && n >= 16 && n % 16 == 0 && k >= 256 && k % 256 == 0 && statics + gemm_r8_lds(k) <= 160 * 1024;
+  return m >= 1 && n >= 16 && n % 16 == 0 && k >= 256 && k % 256 == 0 && (k >> 8) <= kMaxGroups;
 }
 
 hipError_t launch_gemm_r8(const GemmArgs& g, hipStream_t st) {
@@ -382,7 +413,7 @@ hipError_t launch_gemm_r8(const GemmArgs& g, hipStream_t st) {
   const int64_t blocks = ((g.m + kBM - 1) / kBM) * ((g.n + kBN - 1) / kBN);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(64 * kWaves);
-  const size_t lds = gemm_r8_lds(g.k);
+  const size_t lds = 0;
   if (g.a_is_bf16) {
     if (g.c_is_bf16) hipLaunchKernelGGL((k_gemm_r8<1, 1>), grid, block, lds, st, g);
     else hipLaunchKernelGGL((k_gemm_r8<1, 0>), grid, block, lds, st, g);
