@@ -56,16 +56,25 @@ struct OpTraits<0> {  // FP16 operands
   __device__ static __forceinline__ uint32_t micro_pair(uint32_t word) {
     return (T & 1) ? (word >> 1) & 0x7F807F80u : (word << 7) & 0x7F807F80u;
   }
+  // The same fragment in five independent pieces, so that a kernel can spread them over
+  // its MFMAs: the broadcast micro-scale operand of step T, then the packed pair of part P
+  // (codes 2P and 2P + 1 of the word).
+  typedef half2_t micro_t;
   template <int T>
-  __device__ static __forceinline__ frag weight_step(uint32_t cw, uint32_t word) {
+  __device__ static __forceinline__ micro_t micro_step(uint32_t word) {
     const half2_t pr = __builtin_bit_cast(half2_t, micro_pair<T>(word));
     const _Float16 m = (T >> 1) ? pr[1] : pr[0];
-    const half2_t m2 = {m, m};
-    const half2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * m2;
-    const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * m2;
-    const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * m2;
-    const half2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * m2;
-    return frag{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+    return half2_t{m, m};
+  }
+  template <int P>
+  __device__ static __forceinline__ uint32_t weight_part(uint32_t cw, micro_t m2) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, P) * m2);
+  }
+  template <int T>
+  __device__ static __forceinline__ frag weight_step(uint32_t cw, uint32_t word) {
+    const micro_t m2 = micro_step<T>(word);
+    return __builtin_bit_cast(frag, make_uint4(weight_part<0>(cw, m2), weight_part<1>(cw, m2),
+                                               weight_part<2>(cw, m2), weight_part<3>(cw, m2)));
   }
 };
 
@@ -98,10 +107,21 @@ struct OpTraits<1> {  // bf16 operands
   __device__ static __forceinline__ float4_t mfma(frag a, frag b, float4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  // weight fragment of step T (0..3) of a word of four micro-scale bytes
+  // weight fragment of step T (0..3) of a word of four micro-scale bytes, whole or in the
+  // pieces of the FP16 traits (micro-scale of step T as float32, packed pair of part P)
+  typedef float micro_t;
+  template <int T>
+  __device__ static __forceinline__ micro_t micro_step(uint32_t word) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)word, T);
+  }
+  template <int P>
+  __device__ static __forceinline__ uint32_t weight_part(uint32_t cw, micro_t mu) {
+    const float2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, P);
+    return pack(f[0] * mu, f[1] * mu);
+  }
   template <int T>
   __device__ static __forceinline__ frag weight_step(uint32_t cw, uint32_t word) {
-    return weight(cw, __float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)word, T)));
+    return weight(cw, __float_as_uint(micro_step<T>(word)));
   }
 };
 

@@ -77,6 +77,14 @@ __device__ __forceinline__ uint4* w_slot() {
   else return g_rw2;
 }
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 template <int A_BF16, int C_BF16>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   typedef OpTraits<A_BF16> Op;
@@ -97,15 +105,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   const int q = lane >> 4, l16 = lane & 15;
   const int64_t wb0 = (int64_t)tn * (kBN / 16) + wave * kNI;  // the wave's first 16-column block
 
-  // ---- row-factor ratios of the FP16 operand path: f_g / f_{g+1}, the last group f_{G-1};
-  // thread t covers row t % 128 and groups t / 128 + 4 j (a loop of uniform trip count)
+  // ---- row-factor ratios of the FP16 operand path: f_g / f_{g+1}, the last group f_{G-1}.
+  // Thread t covers row t % 128 and the t / 128-th quarter of the groups (at most 8 of 32);
+  // its row factors are loaded here, all at once, and divided after the prologue copies are
+  // issued, so the loads' latency is paid once and overlaps the first stages' transfers.
+  constexpr int kQuarter = kMaxGroups / 4;
+  const int ratio_row = threadIdx.x & (kBM - 1);
+  const int g_first = (int)(threadIdx.x >> 7) * ((groups + 3) >> 2);
+  float fq[kQuarter + 1];
   if (!A_BF16) {
-    const int r = threadIdx.x & (kBM - 1);
-    const float* f = args.a_scale + min(row_begin + r, row_end - 1) * groups;
-    for (int g0 = 0; g0 < groups; g0 += kWaves * 64 / kBM) {
-      const int g = g0 + (int)(threadIdx.x >> 7);
-      if (g < groups) g_sa[g * kBM + r] = g + 1 < groups ? f[g] / f[g + 1] : f[g];
-    }
+    const float* f = args.a_scale + min(row_begin + ratio_row, row_end - 1) * groups;
+#pragma unroll
+    for (int j = 0; j <= kQuarter; ++j) fq[j] = f[min(g_first + j, groups - 1)];
   }
 
   // ---- buffer resources: per-lane byte offsets fixed for the whole k loop ----
@@ -130,21 +141,25 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc((void*)a16, (short)0, 0, kRsrcWord3);
   const uint32_t mu_voff = (uint32_t)((q >> 1) * 128 + l16 * 8);
 
-  auto copy_stage = [&](uint4* abuf, uint4* wbuf, int s) {  // stage s = 2 g + h
+  // copy J (0..3: the activation chunk of step J; 4, 5: the codes of column block J - 4)
+  // of stage s into ring slot (abuf, wbuf)
+  auto copy_part = [&](auto j_c, uint4* abuf, uint4* wbuf, int s) {  // stage s = 2 g + h
+    constexpr int J = decltype(j_c)::value;
     const bool past = s >= stages;
     const int sc = past ? 0 : s;
     const int g = sc >> 1, h = sc & 1;
-    const __amdgpu_buffer_rsrc_t ar = past ? none : a_rsrc;
-    const __amdgpu_buffer_rsrc_t wr = past ? none : w_rsrc;
-#pragma unroll
-    for (int t = 0; t < kSteps; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void_ptr)(abuf + (wave * kSteps + t) * 64), 16, a_voff,
-                                               (uint32_t)(sc * 256 + 64 * t), 0, 0);
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void_ptr)(wbuf + (wave * kNI + ni) * 64), 16,
-                                               (uint32_t)lane * 16,
+    if constexpr (J < kSteps) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(past ? none : a_rsrc, (lds_void_ptr)(abuf + (wave * kSteps + J) * 64),
+                                               16, a_voff, (uint32_t)(sc * 256 + 64 * J), 0, 0);
+    } else {
+      constexpr int ni = J - kSteps;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(past ? none : w_rsrc, (lds_void_ptr)(wbuf + (wave * kNI + ni) * 64),
+                                               16, (uint32_t)lane * 16,
                                                (uint32_t)((ni * groups + g) * kTileCodeBytes + h * 1024), 0, 0);
+    }
+  };
+  auto copy_stage = [&](uint4* abuf, uint4* wbuf, int s) {
+    static_for<0, kCopies>([&](auto j_c) { copy_part(j_c, abuf, wbuf, s); });
   };
   // micro-scale bytes of group g (byte t = step t of the group) and macro-scale bits
   auto load_mu = [&](uint2 (&mu)[kNI], int g) {
@@ -169,14 +184,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   // ---- prologue: macro-scales of groups 0 and 1, stages 0..2 in flight, stage 0 in ----
   uint32_t mw0[kNI], mw1[kNI], mw2[kNI];
   uint2 mu[kNI], mun[kNI];
+  // (register loads first, in this order: the wait below then covers them too)
   load_mw(mw0, 0);
-  copy_stage(a_slot<0>(), w_slot<0>(), 0);
   load_mu(mu, 0);
   load_mw(mw1, min(1, groups - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  copy_stage(a_slot<0>(), w_slot<0>(), 0);
   copy_stage(a_slot<1>(), w_slot<1>(), 1);
   copy_stage(a_slot<2>(), w_slot<2>(), 2);
-  __builtin_amdgcn_s_waitcnt(kVmcntWait<2 * kCopies>::value);  // stage 0 landed
-  __syncthreads();                                              // ... for every wave; ratio table written
+  __builtin_amdgcn_sched_barrier(0);
+  if (!A_BF16) {
+    const int g_end = min(g_first + ((groups + 3) >> 2), groups);
+#pragma unroll
+    for (int j = 0; j < kQuarter; ++j) {
+      const int g = g_first + j;
+      if (g < g_end) g_sa[g * kBM + ratio_row] = g + 1 < groups ? fq[j] / fq[j + 1] : fq[j];
+    }
+  }
+  // stage 0 landed and the ratio table written, for every wave (a plain barrier: a fence
+  // would also wait for stages 1 and 2)
+  __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<2 * kCopies>::value);
+  __builtin_amdgcn_s_barrier();
 
   float4_t x[kMI][kNI];
 #pragma unroll
@@ -186,7 +214,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
 
   // operands of step 0
   frag af[kMI], wf[kNI];
-  uint4 cw[kNI];
+  uint4 cw[kNI], cwn[kNI];  // code words of the current and the next stage
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) af[mi] = __builtin_bit_cast(frag, a_slot<0>()[(mi * kSteps + 0) * 64 + lane]);
 #pragma unroll
@@ -195,133 +223,150 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
     wf[ni] = Op::template weight_step<0>(cw[ni].x, mu[ni].x);
   }
 
-  // factor products p[mi][ni][i] = ratio_row * ratio_col of the boundary after the current
-  // group (after the last group: the final factors), pn for the next group's
-  float p[kMI][kNI][4];
+  // factor products pp[mi][ni][i] = ratio_row * ratio_col of the boundary after the current
+  // group (after the last group: the final factors); formed in four steps of the group
+  // (row blocks 2j, 2j + 1 in the j-th), consumed by the rescale around the boundary
+  float pp[kMI][kNI][4];
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[mi][ni][i] = 1.0f;
+      for (int i = 0; i < 4; ++i) pp[mi][ni][i] = 1.0f;
+  float rw[kNI];
+  float4 ra[2], ra_nx[2];  // row ratios of the current / next product step
+  uint32_t wpart[kNI][4];
+  typename Op::micro_t msplat[kNI];
   const float* sa_lane = g_sa + 4 * q;  // + g * 128 + 16 mi: rows 16 mi + 4 q .. + 3
-  // column ratio of the boundary after group g (after the last group: the final factor)
-  auto col_ratios = [&](float (&rw)[kNI], int g, const uint32_t (&m_cur)[kNI], const uint32_t (&m_nxt)[kNI]) {
-    const bool last = g + 1 >= groups;  // (selects, not branches: the step stays one region)
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni)
-      rw[ni] = col_factor(m_cur[ni]) * (last ? kUnit : __builtin_amdgcn_rcpf(col_factor(m_nxt[ni])));
-  };
-  auto products = [&](float (&pp)[kMI][kNI][4], int g, const float (&rw)[kNI], int mi_lo, int mi_hi) {
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) {
-      if (mi < mi_lo || mi >= mi_hi) continue;
-      float4 ra = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-      if (!A_BF16) ra = *reinterpret_cast<const float4*>(sa_lane + g * kBM + 16 * mi);
-#pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) {
-        if (A_BF16) {
-          pp[mi][ni][0] = pp[mi][ni][1] = pp[mi][ni][2] = pp[mi][ni][3] = rw[ni];
-        } else {
-          pp[mi][ni][0] = ra.x * rw[ni];
-          pp[mi][ni][1] = ra.y * rw[ni];
-          pp[mi][ni][2] = ra.z * rw[ni];
-          pp[mi][ni][3] = ra.w * rw[ni];
-        }
-      }
-    }
-  };
 
-  // One MFMA step: the step's 16 MFMAs (row block major); each activation fragment is
-  // reloaded for the next step right after its two MFMAs (from `anext` at step `tnext`),
-  // and the next step's weight fragments are decoded meanwhile. The rescale of a group
-  // boundary is split over the two steps around it: POST (a group's last step) multiplies
-  // row blocks 0..3 by the products `pp` once their last MFMAs of the group are done; PRE
-  // (the next group's first step) multiplies row blocks 4..7 before their first MFMAs.
-  auto mfma_step = [&](auto pre_c, auto post_c, const uint4* anext, int tnext, frag (&wn)[kNI],
-                       const float (&pp)[kMI][kNI][4]) {
-    constexpr bool PRE = decltype(pre_c)::value, POST = decltype(post_c)::value;
+  // One MFMA step (T = 0..3 of a stage in ring slot B; H = 0 / 1 the group's first / second
+  // stage) as eight regions, one per row block R, each fenced so that the compiler keeps the
+  // VALU work where it is placed:
+  //   - the row block's two MFMAs, then the reload of its activation fragment for the next
+  //     step (this slot, or the next slot in step 3, after the barrier); in step 3, regions
+  //     0..5 also issue the copies that refill this slot;
+  //   - a quarter of the next step's weight decode: column block R / 4, code pair R % 4;
+  //   - around a group boundary, the rescale of row blocks whose last MFMA of the group is
+  //     at least two regions back: H == 1, T == 3 multiplies row blocks 0..5 (regions
+  //     2..7), the next group's T == 0 row blocks 6, 7 (regions 0, 1, before their MFMAs);
+  //   - in four steps per group (H == 0: T = 1, 2; H == 1: T = 0, 1), the factor products
+  //     of two row blocks (regions 3..6), their row ratios loaded one step earlier (regions
+  //     6, 7), and the column ratios once per group (first of the four steps, region 1).
+  auto step = [&](auto b_c, auto t_c, auto h_c, auto rescale_c, int g, int s_copy) {
+    constexpr int B = decltype(b_c)::value, T = decltype(t_c)::value, H = decltype(h_c)::value;
+    constexpr bool RESCALE = decltype(rescale_c)::value;
+    constexpr int TN = (T + 1) & 3;  // the next step (within the stage, or the next stage's first)
+    constexpr bool PRE = H == 0 && T == 0 && RESCALE;
+    constexpr bool POST = H == 1 && T == 3;
+    constexpr bool PROD = H == 0 ? (T == 1 || T == 2) : (T == 0 || T == 1);
+    constexpr int PS = H == 0 ? T - 1 : T + 2;  // which of the four product steps
+    // the step before each product step loads that step's row ratios (regions 6, 7)
+    constexpr bool RA_NEXT = !A_BF16 && (H == 0 ? T != 2 : T == 0);
+    constexpr int PS_NEXT = H == 0 ? (T == 3 ? 2 : T) : 3;
+    const uint4* anext = T < 3 ? a_slot<B>() : a_slot<(B + 1) % 3>();
+    static_for<0, kMI>([&](auto r_c) {
+      constexpr int R = decltype(r_c)::value;
+      constexpr int NI = R / 4, P = R % 4;
+      x[R][0] = Op::mfma(af[R], wf[0], x[R][0]);
+      x[R][1] = Op::mfma(af[R], wf[1], x[R][1]);
+      af[R] = __builtin_bit_cast(frag, anext[(R * kSteps + TN) * 64 + lane]);
+      // step 3: this slot is free (the barrier before the step); the copies that refill it
+      // go out one per region (all waves at once right after the barrier stall on issue)
+      if constexpr (T == 3 && R < kCopies)
+        copy_part(std::integral_constant<int, R>{}, a_slot<B>(), w_slot<B>(), s_copy);
+      if constexpr (T == 2 && R == 0) {  // the next stage's code words (this wave's own copies)
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) {
+        for (int ni = 0; ni < kNI; ++ni) cwn[ni] = w_slot<(B + 1) % 3>()[(wave * kNI + ni) * 64 + lane];
+      }
+      // next step's weights: micro-scale word of this stage (H == 0: first word), or of the
+      // next stage (same group's second word, or the next group's first)
+      if constexpr (P == 0) {
+        const uint32_t word = T < 3 ? (H ? mu[NI].y : mu[NI].x) : (H ? mun[NI].x : mu[NI].y);
+        msplat[NI] = Op::template micro_step<TN>(word);
+      }
+      const uint32_t code = T == 0 ? cw[NI].y : T == 1 ? cw[NI].z : T == 2 ? cw[NI].w : cwn[NI].x;
+      wpart[NI][P] = Op::template weight_part<P>(code, msplat[NI]);
+      if constexpr (PRE && R < 2) {
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) x[mi][ni] = Op::mfma(af[mi], wf[ni], x[mi][ni]);
-      if constexpr (PRE) {
-        if (mi < kMI / 2) {
+        for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[6 + R][ni][i] *= pp[6 + R][ni][i];
+      }
+      if constexpr (POST && R >= 2) {
+#pragma unroll
+        for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[R - 2][ni][i] *= pp[R - 2][ni][i];
+      }
+      if constexpr (RA_NEXT && R >= 6)
+        ra_nx[R - 6] = *reinterpret_cast<const float4*>(sa_lane + g * kBM + 16 * (2 * PS_NEXT + R - 6));
+      if constexpr (PROD) {
+        if constexpr (R == 0 && !A_BF16) {
+          ra[0] = ra_nx[0];
+          ra[1] = ra_nx[1];
+        }
+        if constexpr (R == 1 && PS == 0) {  // column ratios of the boundary after group g
+          const bool last = g + 1 >= groups;  // (selects, not branches)
 #pragma unroll
           for (int ni = 0; ni < kNI; ++ni)
+            rw[ni] = col_factor(mw0[ni]) * (last ? kUnit : __builtin_amdgcn_rcpf(col_factor(mw1[ni])));
+        }
+        if constexpr (R >= 3 && R <= 6) {
+          constexpr int U = R - 3, MI = 2 * PS + U / 2, CI = U % 2;
+          if constexpr (A_BF16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[mi + kMI / 2][ni][i] *= pp[mi + kMI / 2][ni][i];
+            for (int i = 0; i < 4; ++i) pp[MI][CI][i] = rw[CI];
+          } else {
+            pp[MI][CI][0] = ra[U / 2].x * rw[CI];
+            pp[MI][CI][1] = ra[U / 2].y * rw[CI];
+            pp[MI][CI][2] = ra[U / 2].z * rw[CI];
+            pp[MI][CI][3] = ra[U / 2].w * rw[CI];
+          }
         }
       }
-      if constexpr (POST) {
-        if (mi >= kMI / 2) {
+      // issue order: MFMA, VALU, MFMA, LDS reads, VALU
+      constexpr int kDec = (P == 0 ? (A_BF16 ? 1 : 3) : 0) + (A_BF16 ? 4 : 2);
+      constexpr int kRes = ((PRE && R < 2) || (POST && R >= 2)) ? 8 : 0;
+      constexpr int kProd = PROD && !A_BF16 && R >= 3 && R <= 6 ? 4 : 0;
+      constexpr int kRat = PROD && R == 1 && PS == 0 ? 12 : 0;
+      constexpr int kV = kDec + kRes + kProd + kRat;
+      constexpr int kDs = 1 + (T == 2 && R == 0 ? kNI : 0) + (RA_NEXT && R >= 6 ? 1 : 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, (kV + 1) / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kV / 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
 #pragma unroll
-          for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[mi - kMI / 2][ni][i] *= pp[mi - kMI / 2][ni][i];
-        }
-      }
-      af[mi] = __builtin_bit_cast(frag, anext[(mi * kSteps + tnext) * 64 + lane]);
-    }
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) wf[ni] = wn[ni];
-    // MFMA, VALU, MFMA, VALU, LDS read per row block (up to 6 VALU in each slot)
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    for (int ni = 0; ni < kNI; ++ni) {
+      // (keeps the decode in this step: otherwise it sinks past a loop exit that follows)
+      asm volatile("" : : "v"(wpart[ni][0]), "v"(wpart[ni][1]), "v"(wpart[ni][2]), "v"(wpart[ni][3]));
+      wf[ni] = __builtin_bit_cast(frag, make_uint4(wpart[ni][0], wpart[ni][1], wpart[ni][2], wpart[ni][3]));
     }
   };
 
   typedef std::integral_constant<bool, true> kTrue;
   typedef std::integral_constant<bool, false> kFalse;
+  typedef std::integral_constant<int, 0> C0;
+  typedef std::integral_constant<int, 1> C1;
+  typedef std::integral_constant<int, 2> C2;
+  typedef std::integral_constant<int, 3> C3;
 
-  // Stage s in ring slot B (s % 3), H = s & 1 (H == 0: the first stage of group g).
-  //   steps 0..2: MFMAs with the fragments reloaded from this slot; step 3 (after the
-  //   barrier) reloads from the next slot and decodes the next stage's first weights;
-  //   H == 0 (RESCALE: every group but the first): step 0 finishes the previous boundary's
-  //   rescale; H == 1: the products of this group's boundary are formed in steps 0..2 and
-  //   step 3 starts its rescale.
-  // Wait before the barrier: stage s + 1's copies (issued after barrier s - 2) must have
-  // landed; younger than them are the register loads of barrier s - 1 (when s - 1 is a
-  // group's first stage) and the copies of barrier s - 1.
-  float pn[kMI][kNI][4];
+  // Stage s in ring slot B (s % 3), H = s & 1. Before step 2 this wave's copies of stage
+  // s + 1 must have landed (its code words are read in step 2): younger than them are the
+  // copies of barrier s - 1 and, when s - 1 is a group's first stage, its register loads.
+  // The barrier before step 3 publishes stage s + 1 to every wave and frees this slot (all
+  // its reads done: lgkmcnt 0), which then receives stage s + 3.
   auto run_stage = [&](auto b_c, auto h_c, auto rescale_c, int s) {
     constexpr int B = decltype(b_c)::value, H = decltype(h_c)::value;
-    constexpr bool RESCALE = decltype(rescale_c)::value;
-    constexpr int BN1 = (B + 1) % 3;
-    typedef std::integral_constant<bool, H == 0 && RESCALE> kPre;
-    typedef std::integral_constant<bool, H == 1> kPost;
     const int g = s >> 1;
-    uint4* abuf = a_slot<B>();
-    frag wn[kNI];
-    float rw[kNI];
-    // step 0
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) wn[ni] = Op::template weight_step<1>(cw[ni].y, H ? mu[ni].y : mu[ni].x);
-    if (H == 1) {
-      col_ratios(rw, g, mw0, mw1);
-      products(pn, g, rw, 0, 3);
-    }
-    mfma_step(kPre{}, kFalse{}, abuf, 1, wn, p);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 1
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) wn[ni] = Op::template weight_step<2>(cw[ni].z, H ? mu[ni].y : mu[ni].x);
-    if (H == 1) products(pn, g, rw, 3, 6);
-    mfma_step(kFalse{}, kFalse{}, abuf, 2, wn, p);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 2
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) wn[ni] = Op::template weight_step<3>(cw[ni].w, H ? mu[ni].y : mu[ni].x);
-    if (H == 1) products(pn, g, rw, 6, 8);
-    mfma_step(kFalse{}, kFalse{}, abuf, 3, wn, p);
-    __builtin_amdgcn_sched_barrier(0);
-    // barrier: stage s + 1 published, this slot free
+    step(b_c, C0{}, h_c, rescale_c, g, 0);
+    step(b_c, C1{}, h_c, rescale_c, g, 0);
     constexpr int kWait = kCopies + (H == 1 ? kLoads : 0);
+    __builtin_amdgcn_s_waitcnt(kVmcntWait<kWait>::value);
+    __builtin_amdgcn_sched_barrier(0);
+    step(b_c, C2{}, h_c, rescale_c, g, 0);
     __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<kWait>::value);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -329,35 +374,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
       load_mu(mun, min(g + 1, groups - 1));
       load_mw(mw2, min(g + 2, groups - 1));
     }
-    copy_stage(a_slot<B>(), w_slot<B>(), s + 3);
     __builtin_amdgcn_sched_barrier(0);
-    // step 3: the next stage's code words and first weight fragments
+    step(b_c, C3{}, h_c, rescale_c, g, s + 3);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      cw[ni] = w_slot<BN1>()[(wave * kNI + ni) * 64 + lane];
-      // next stage: same group (H == 0: second micro-scale word) or the next group's first
-      wn[ni] = Op::template weight_step<0>(cw[ni].x, H ? mun[ni].x : mu[ni].y);
-    }
-    mfma_step(kFalse{}, kPost{}, a_slot<BN1>(), 0, wn, pn);
-    __builtin_amdgcn_sched_barrier(0);
-    if (H == 1) {  // next group: rotate the scales and the products
+    for (int ni = 0; ni < kNI; ++ni) cw[ni] = cwn[ni];
+    if (H == 1) {  // next group: rotate the scales
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni) {
         mu[ni] = mun[ni];
         mw0[ni] = mw1[ni];
         mw1[ni] = mw2[ni];
       }
-#pragma unroll
-      for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[mi][ni][i] = pn[mi][ni][i];
     }
   };
-  typedef std::integral_constant<int, 0> C0;
-  typedef std::integral_constant<int, 1> C1;
-  typedef std::integral_constant<int, 2> C2;
   // group 0 (no boundary before it), then six stages per pass (slots cycle by 3, halves by
   // 2) starting at stage 2 (slot 2); every pass ends on a group boundary
   run_stage(C0{}, C0{}, kFalse{}, 0);
@@ -375,20 +405,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   // the ring's last copies (zeros from the empty resource) complete before exit
   __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
 
-  // ---- final factors (the last group's products; row blocks 0..3 have them), store ----
+  // ---- final factors (the last group's products; row blocks 0..5 have them), store ----
+  // (the store addresses are formed here: opaque copies of the lane index and first row
+  // keep the compiler from computing them before the loop, where they would hold registers)
+  int lane_e = lane;
+  int64_t row0 = row_begin;
+  asm volatile("" : "+v"(lane_e), "+s"(row0));
+  const int qe = lane_e >> 4, l16e = lane_e & 15;
   const int64_t n0 = wb0 * 16;
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
       if (wb0 + ni >= nblocks) continue;
-      const int64_t col = n0 + 16 * ni + l16;
+      const int64_t col = n0 + 16 * ni + l16e;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t r = row_begin + 16 * mi + 4 * q + i;
+        const int64_t r = row0 + 16 * mi + 4 * qe + i;
         if (r >= row_end) continue;
-        // row blocks 0..3 were multiplied by the final factors in the last step
-        const float v = mi < kMI / 2 ? x[mi][ni][i] : x[mi][ni][i] * p[mi][ni][i];
+        // row blocks 0..5 were multiplied by the final factors in the last step
+        const float v = mi < kMI - 2 ? x[mi][ni][i] : x[mi][ni][i] * pp[mi][ni][i];
         if (C_BF16)
           static_cast<uint16_t*>(args.c)[r * args.ldc + col] = (uint16_t)bf16_rne_bits(v);
         else
