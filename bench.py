@@ -10,10 +10,19 @@ cannot hold the stream, and launches are replayed from a HIP graph.
 
 Also reported (same JSON line, "secondary"): the W4A4 prefill product (2048 x 4096 x
 4096, activations quantized on the device every step) in TFLOP/s, the 8-layer W4A4/W4A8
-policy stack, the 128-expert top-8 mixture-of-experts layer, quantization, decode
-attention over the FP4 KV cache, the MX-native FP4 product, and the policy stack under
-the W8A8 ("sensitive-w8") and static-activation-scale modes, each with its roofline
-fraction; the oracle's CPU time on a bounded sample ("cpu_baseline").
+policy stack, the 128-expert top-8 mixture-of-experts layer, quantization, the layout
+repack, decode attention over the FP4 KV cache, the MX-native FP4 product, and the policy
+stack under the W8A8 ("sensitive-w8") and static-activation-scale modes, each with its
+roofline fraction; the oracle's CPU time on a bounded sample ("cpu_baseline").
+
+Every leg's operands are rotated over more memory than the 256 MB Infinity Cache holds
+(20 operand sets for the prefill-size products, 3 copies of the 8-layer stacks, the
+mixture-of-experts weights alone are 344 MB), and every leg reports the per-launch
+p10 / p50 / p90 over graph replays beside its average. The line also records the device's
+clocks and power before and after, and the two ceilings measured on the same device in
+the same run (the HBM read floor at the decode weights' size, and the sustained FP16 MFMA
+rate with register operands), so that each roofline fraction is given against the spec
+peak and against the measured ceiling.
 
 Rank 0 prints one JSON line. Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -36,6 +45,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0   # dense MFMA bf16/fp16
 FP4_PEAK_TFLOPS = 10100.0   # dense MFMA fp4 (not reachable with 16-element E4M3 scales)
 ROTATE = 16
+ROTATE_GEMM = 20  # operand sets of the prefill-size products (20 x 25.7 MB > 256 MB)
+STACK_COPIES = 3  # copies of the 8-layer stacks (3 x 153 MB)
 
 
 def algorithmic_bytes_gemv(m, n, k):
@@ -117,6 +128,31 @@ def run_steps(torch, timer, graph, fns, steps):
     return timer.region(body, 1)
 
 
+def replay_samples(torch, graph, launches, reps):
+    """Per-launch seconds of each of `reps` graph replays (each replay's time over its
+    `launches` launches), on the stream the replays run on."""
+    s = torch.cuda.current_stream()
+    evs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        graph.replay()
+        e1.record(s)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) / 1e3 / launches for a, b in evs])
+
+
+def pct_us(samples):
+    """p10 / p50 / p90 of per-launch seconds, in microseconds."""
+    return [round(float(np.percentile(samples, q)) * 1e6, 3) for q in (10, 50, 90)]
+
+
+def clone_q(fp4, q):
+    """A device copy of a quantized tensor (its own memory: rotation defeats the caches)."""
+    return fp4.QTensor(q.codes.clone(), q.micro.clone(), q.macro.clone(), q.rows, q.k, q.elem, q.layout)
+
+
 def bench_decode(torch, fp4, workloads, steps, warmup):
     m, k, n = 8, 4096, 14336
     a, w, _ = workloads.decode()
@@ -155,23 +191,32 @@ def bench_decode(torch, fp4, workloads, steps, warmup):
 
 
 def bench_prefill(torch, fp4, workloads, steps):
+    """The W4A4 prefill product per step: activation pass + product, over 20 rotated
+    (A, W, C) sets (514 MB of operands), from HIP graph replays."""
     m, k, n = 2048, 4096, 4096
     a, w, _ = workloads.prefill()
-    wq = fp4.quantize_fp4(torch.from_numpy(w).cuda(), layout=fp4.LAYOUT_TILED)
-    ad = torch.from_numpy(a).cuda().to(torch.bfloat16)
-    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    wq0 = fp4.quantize_fp4(torch.from_numpy(w).cuda(), layout=fp4.LAYOUT_TILED)
+    a0 = torch.from_numpy(a).cuda().to(torch.bfloat16)
+    del a, w
+    sets = [(a0, wq0)] + [(a0.clone(), clone_q(fp4, wq0)) for _ in range(ROTATE_GEMM - 1)]
+    outs = [torch.empty(m, n, dtype=torch.bfloat16, device="cuda") for _ in sets]
     ws = torch.empty(fp4.fp4_workspace_bytes(fp4.A4, m, n, k), dtype=torch.uint8, device="cuda")
-    fn = lambda: fp4.gemm_w4aX(fp4.A4, ad, wq, out=out, workspace=ws)
-    for _ in range(3):
-        fn()
-    g = capture(torch, [fn] * 4)
+    fns = [(lambda x=x, q=q, o=o: fp4.gemm_w4aX(fp4.A4, x, q, out=o, workspace=ws)) for (x, q), o in zip(sets, outs)]
+    for f in fns:
+        f()
+    g = capture(torch, fns)
     g.replay()
     timer = Timer(torch)
-    secs = run_steps(torch, timer, g, [fn] * 4, steps)
+    steps = max(steps, len(fns))
+    secs = run_steps(torch, timer, g, fns, steps)
     per = secs / steps
+    spread = replay_samples(torch, g, len(fns), 8)
+    same = all(torch.equal(outs[0], o) for o in outs[1:])
     flops = 2 * m * n * k
     tfl = flops / per / 1e12
-    return dict(m=m, n=n, k=k, per_step_s=per, tflops=tfl,
+    return dict(m=m, n=n, k=k, per_step_s=per, tflops=tfl, operand_sets_rotated=len(fns),
+                step_us_p10_p50_p90=pct_us(spread), outputs_identical=bool(same),
+                kernel=fp4.fp4_product_kernel(fp4.A4, torch.bfloat16, m, n, k),
                 frac_bf16_peak=tfl / BF16_PEAK_TFLOPS, frac_fp4_peak=tfl / FP4_PEAK_TFLOPS,
                 bytes=algorithmic_bytes_gemm(m, n, k))
 
@@ -188,17 +233,25 @@ def bench_mx(torch, fp4, workloads, steps):
     ad = torch.from_numpy(a).cuda().to(torch.bfloat16)
     wq = fp4.quantize_mxfp4(wd)
     aq = fp4.quantize_mxfp4(ad)
-    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
-    step = lambda: (fp4.quantize_mxfp4(ad, out=aq), fp4.gemm_mxfp4(aq, wq, out=out))
-    gemm = lambda: fp4.gemm_mxfp4(aq, wq, out=out)
+    # 20 rotated operand sets (activations, their MX codes, weights, output)
+    sets = []
+    for i in range(ROTATE_GEMM):
+        x = ad if i == 0 else ad.clone()
+        wqi = wq if i == 0 else fp4.MxTensor(wq.codes.clone(), wq.scales.clone(), wq.rows, wq.k)
+        sets.append((x, fp4.quantize_mxfp4(x), wqi, torch.empty(m, n, dtype=torch.bfloat16, device="cuda")))
+    steps_fns = [(lambda x=x, q=q, wv=wv, o=o: (fp4.quantize_mxfp4(x, out=q), fp4.gemm_mxfp4(q, wv, out=o)))
+                 for x, q, wv, o in sets]
+    gemm_fns = [(lambda q=q, wv=wv, o=o: fp4.gemm_mxfp4(q, wv, out=o)) for x, q, wv, o in sets]
     timer = Timer(torch)
-    res = {}
-    for name, fn in (("step", step), ("gemm", gemm)):
-        for _ in range(3):
-            fn()
-        g = capture(torch, [fn] * 4)
+    res, spread = {}, {}
+    for name, fns in (("step", steps_fns), ("gemm", gemm_fns)):
+        for f in fns:
+            f()
+        g = capture(torch, fns)
         g.replay()
-        res[name] = run_steps(torch, timer, g, [fn] * 4, steps) / steps
+        n_steps = max(steps, len(fns))
+        res[name] = run_steps(torch, timer, g, fns, n_steps) / n_steps
+        spread[name] = pct_us(replay_samples(torch, g, len(fns), 8))
     flops = 2 * m * n * k
     # accuracy against the float32 product of the unquantized (bf16) activations and weights
     ref = ad.float() @ wd.t()
@@ -212,6 +265,8 @@ def bench_mx(torch, fp4, workloads, steps):
     tfl = flops / res["step"] / 1e12
     tfl_g = flops / res["gemm"] / 1e12
     return dict(m=m, n=n, k=k, per_step_s=res["step"], gemm_s=res["gemm"], tflops=tfl, gemm_tflops=tfl_g,
+                operand_sets_rotated=len(sets), step_us_p10_p50_p90=spread["step"],
+                gemm_us_p10_p50_p90=spread["gemm"],
                 frac_fp4_peak=tfl / FP4_PEAK_TFLOPS, gemm_frac_fp4_peak=tfl_g / FP4_PEAK_TFLOPS,
                 rel_error_vs_fp32_product=dict(mx_fp4=err_mx, two_level_w4a4=err_two))
 
@@ -233,8 +288,12 @@ def bench_quantize(torch, fp4, workloads, steps):
     timer = Timer(torch)
     reps = max(4, steps // 16)
     secs = timer.region(lambda: [f() for f in fns], reps) / (reps * len(fns))
+    gw = capture(torch, fns)
+    gw.replay()
+    spread_w = replay_samples(torch, gw, len(fns), 8)
     nbytes = n * k * 4 + n * k // 2 + n * k // 16 + n * (k // 256) * 2
-    out["weights_f32_tiled"] = dict(rows=n, k=k, per_call_s=secs, bytes=nbytes,
+    out["weights_f32_tiled"] = dict(rows=n, k=k, per_call_s=secs, bytes=nbytes, inputs_rotated=len(fns),
+                                    call_us_p10_p50_p90=pct_us(spread_w),
                                     gbs=nbytes / secs / 1e9, frac_hbm_peak=nbytes / secs / 1e9 / HBM_PEAK_GBS)
     del wd, qs, fns
     a, _, _ = workloads.prefill()
@@ -248,11 +307,82 @@ def bench_quantize(torch, fp4, workloads, steps):
     g = capture(torch, fns)
     g.replay()
     secs = run_steps(torch, timer, g, fns, max(ROTATE, steps)) / max(ROTATE, steps)
+    spread_a = replay_samples(torch, g, len(fns), 8)
     nbytes = m * k * 2 + m * k // 2 + m * k // 16 + m * (k // 256) * 2
-    out["activations_bf16_canonical"] = dict(rows=m, k=k, per_call_s=secs, bytes=nbytes,
+    out["activations_bf16_canonical"] = dict(rows=m, k=k, per_call_s=secs, bytes=nbytes, inputs_rotated=len(fns),
+                                             call_us_p10_p50_p90=pct_us(spread_a),
                                              gbs=nbytes / secs / 1e9,
                                              frac_hbm_peak=nbytes / secs / 1e9 / HBM_PEAK_GBS)
     return out
+
+
+def bench_repack(torch, fp4, workloads, steps):
+    """repack_fp4 of the decode weights (14336 x 4096 E2M1), canonical -> tiled and back:
+    codes, micro- and macro-scales read once and written once (GB/s of both). 16 source
+    copies rotate (over 500 MB)."""
+    _, w, _ = workloads.decode()
+    can0 = fp4.quantize_fp4(torch.from_numpy(w).cuda(), layout=fp4.LAYOUT_CANONICAL)
+    del w
+    n, k = can0.rows, can0.k
+    srcs = [can0] + [clone_q(fp4, can0) for _ in range(ROTATE - 1)]
+    tils = [fp4.empty_qtensor(n, k, layout=fp4.LAYOUT_TILED) for _ in srcs]
+    backs = [fp4.empty_qtensor(n, k, layout=fp4.LAYOUT_CANONICAL) for _ in srcs]
+    nbytes = 2 * (n * k // 2 + n * k // 16 + n * (k // 256) * 2)
+    timer = Timer(torch)
+    out = {}
+    for name, pairs in (("canonical_to_tiled", list(zip(srcs, tils))), ("tiled_to_canonical", list(zip(tils, backs)))):
+        dst_layout = pairs[0][1].layout
+        fns = [(lambda a=a, b=b, L=dst_layout: fp4.repack_fp4(a, L, out=b)) for a, b in pairs]
+        for f in fns:
+            f()
+        g = capture(torch, fns)
+        g.replay()
+        n_steps = max(steps, len(fns))
+        per = run_steps(torch, timer, g, fns, n_steps) / n_steps
+        out[name] = dict(rows=n, k=k, per_call_s=per, bytes=nbytes, gbs=nbytes / per / 1e9,
+                         frac_hbm_peak=nbytes / per / 1e9 / HBM_PEAK_GBS, inputs_rotated=len(fns),
+                         call_us_p10_p50_p90=pct_us(replay_samples(torch, g, len(fns), 8)))
+    torch.cuda.synchronize()
+    out["round_trip_identical"] = bool(all(torch.equal(a.codes, b.codes) and torch.equal(a.micro, b.micro)
+                                           and torch.equal(a.macro, b.macro) for a, b in zip(srcs, backs)))
+    return out
+
+
+def ceilings(torch, steps):
+    """The two ceilings of the headline legs, measured on this device in this run: the HBM
+    read floor at the decode weights' size (a plain streaming read of 16 rotated copies,
+    512 workgroups of 256 threads, graph replays: the probes' best launch shape), and the
+    sustained FP16 MFMA rate with register operands (2 waves per SIMD, 8 independent
+    accumulators; no memory traffic, so an upper bound for a product kernel)."""
+    import ctypes
+    lib = probe_library()
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    m, k, n = 8, 4096, 14336
+    wbytes = n * k // 2 + n * k // 16 + n * (k // 256) * 2
+    bufs = [torch.ones(wbytes // 4, dtype=torch.int32, device="cuda") for _ in range(ROTATE)]
+    fns = [(lambda b=b: lib.probe_read(ctypes.c_void_p(b.data_ptr()), wbytes, ctypes.c_void_p(sink.data_ptr()),
+                                       2 * cus, 256, st())) for b in bufs]
+    for f in fns:
+        assert f() == 0
+    g = capture(torch, fns)
+    g.replay()
+    per = replay_samples(torch, g, ROTATE, max(16, steps // ROTATE))
+    del bufs
+    clocks = torch.zeros(2 * 2 * cus, dtype=torch.int64, device="cuda")
+    blocks, chains, iters = 2 * cus, 8, 8192
+    fn = lambda: lib.probe_mfma(0, chains, blocks, iters, ctypes.c_void_p(clocks.data_ptr()), st())
+    timer = Timer(torch)
+    for _ in range(8):
+        assert fn() == 0
+    t = float(np.median([timer.region(fn, 1) for _ in range(8)]))
+    c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+    ghz = float(np.median(c[:, 0] / (c[:, 1] / 100e6))) / 1e9
+    mfma_tflops = blocks * 4 * iters * chains * 16384 / t / 1e12
+    return dict(read_floor_bytes=wbytes, read_floor_us_p10_p50_p90=pct_us(per),
+                read_floor_gbs=wbytes / float(np.median(per)) / 1e9,
+                mfma_f16_register_tflops=round(mfma_tflops, 1), mfma_probe_shader_ghz=round(ghz, 3))
 
 
 def copy_probe(torch, mib=256, reps=4):
@@ -495,6 +625,8 @@ def summarize_counters(csv_path, kernel_substr, title, command, simds=1024, xcds
 
 
 def bench_policy(torch, fp4, workloads, steps):
+    """The 8-layer W4A4/W4A8 policy stack (512 x 5120 x 5120 per layer), per step the eight
+    layers' activation passes and products; three copies of the stack (460 MB) rotate."""
     cfg = workloads.WORKLOADS["policy_stack"]
     m, k, n = cfg["m"], cfg["k"], cfg["n"]
     flags = workloads.policy_flags()
@@ -504,27 +636,37 @@ def bench_policy(torch, fp4, workloads, steps):
         act = fp4.fp4_policy_select(fp4.POLICY_AUTO, bool(flags[l]))
         layers.append((act, fp4.quantize_fp4(torch.from_numpy(w).cuda(), layout=fp4.LAYOUT_TILED),
                        torch.from_numpy(x).cuda().to(torch.bfloat16)))
+    copies = [layers] + [[(act, clone_q(fp4, q), x.clone()) for act, q, x in layers]
+                         for _ in range(STACK_COPIES - 1)]
     out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(fp4.fp4_workspace_bytes(fp4.A4, m, n, k), dtype=torch.uint8, device="cuda")
     fns = [(lambda a=act, q=wq, x=x: fp4.gemm_w4aX(a, x, q, out=out, workspace=ws))
-           for act, wq, x in layers]
+           for stack in copies for act, wq, x in stack]
     for f in fns:
         f()
     g = capture(torch, fns)
     g.replay()
     timer = Timer(torch)
-    secs = timer.region(g.replay, steps)
-    per = secs / steps
-    flops = 2 * m * n * k * len(fns)
-    # per precision: time one A4 and one A8 layer alone
-    a4 = next(f for f, (act, _, _) in zip(fns, layers) if act == fp4.A4)
-    a8 = next(f for f, (act, _, _) in zip(fns, layers) if act == fp4.A8)
-    t4 = timer.region(a4, 8) / 8
-    t8 = timer.region(a8, 8) / 8
+    reps = max(2, -(-steps // STACK_COPIES))
+    secs = timer.region(g.replay, reps)
+    per = secs / (reps * STACK_COPIES)  # one step = one pass over the 8 layers
+    spread = replay_samples(torch, g, STACK_COPIES, 8)
+    flops = 2 * m * n * k * len(layers)
+
+    # per precision: one A4 and one A8 layer alone, over its three copies
+    def layer_time(act):
+        i = next(j for j, (a_, _, _) in enumerate(layers) if a_ == act)
+        lf = [fns[c * len(layers) + i] for c in range(STACK_COPIES)]
+        gl = capture(torch, lf)
+        gl.replay()
+        return float(np.median(replay_samples(torch, gl, len(lf), 16)))
     tfl = flops / per / 1e12
-    return dict(layers=len(fns), flagged=[int(i) for i in np.nonzero(flags)[0]], per_step_s=per,
+    return dict(layers=len(layers), flagged=[int(i) for i in np.nonzero(flags)[0]], per_step_s=per,
+                stack_copies_rotated=STACK_COPIES, step_us_p10_p50_p90=pct_us(spread),
+                kernels={"a4": fp4.fp4_product_kernel(fp4.A4, torch.bfloat16, m, n, k),
+                         "a8": fp4.fp4_product_kernel(fp4.A8, torch.bfloat16, m, n, k)},
                 tflops=tfl, frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
-                layer_a4_s=t4, layer_a8_s=t8)
+                layer_a4_s=layer_time(fp4.A4), layer_a8_s=layer_time(fp4.A8))
 
 
 def bench_sensitive(torch, fp4, workloads, steps):
@@ -545,7 +687,7 @@ def bench_sensitive(torch, fp4, workloads, steps):
     single = {}
     acc_layer = int(np.nonzero(flags)[0][0])
     for mode, name in ((fp4.POLICY_SENSITIVE_W8, "sensitive_w8"), (fp4.POLICY_STATIC, "static")):
-        fns, kinds = [], []
+        fns, kinds, copy_fns = [], [], []
         for l in range(cfg["layers"]):
             w, x = workloads.policy_layer(l)
             code = fp4.fp4_policy_select(mode, bool(flags[l]))
@@ -554,6 +696,9 @@ def bench_sensitive(torch, fp4, workloads, steps):
             if code == fp4.W8A8:
                 wq = fp4.quantize_fp4(wd, elem=fp4.ELEM_E4M3, layout=fp4.LAYOUT_TILED)
                 fns.append(lambda x=xd, q=wq: fp4.gemm_w8a8(x, q, out=out, workspace=ws))
+                copy_fns.append(lambda x=xd, q=wq: [lambda x2=x.clone(), q2=clone_q(fp4, q):
+                                                    fp4.gemm_w8a8(x2, q2, out=out, workspace=ws)
+                                                    for _ in range(STACK_COPIES - 1)])
             elif code in (fp4.A4S, fp4.A8S):
                 act = fp4.A8 if code == fp4.A8S else fp4.A4
                 amax = torch.zeros(k // 256, dtype=torch.float32, device="cuda")
@@ -563,22 +708,39 @@ def bench_sensitive(torch, fp4, workloads, steps):
                 wq = fp4.quantize_fp4(wd, layout=fp4.LAYOUT_TILED)
                 fns.append(lambda a=act, x=xd, q=wq, mc=macro: fp4.gemm_w4aX_static(a, x, mc, q, out=out,
                                                                                    workspace=ws))
+                copy_fns.append(lambda a=act, x=xd, q=wq, mc=macro: [
+                    lambda x2=x.clone(), q2=clone_q(fp4, q): fp4.gemm_w4aX_static(a, x2, mc, q2, out=out,
+                                                                                 workspace=ws)
+                    for _ in range(STACK_COPIES - 1)])
             else:
                 wq = fp4.quantize_fp4(wd, layout=fp4.LAYOUT_TILED)
                 fns.append(lambda a=code, x=xd, q=wq: fp4.gemm_w4aX(a, x, q, out=out, workspace=ws))
+                copy_fns.append(lambda a=code, x=xd, q=wq: [
+                    lambda x2=x.clone(), q2=clone_q(fp4, q): fp4.gemm_w4aX(a, x2, q2, out=out, workspace=ws)
+                    for _ in range(STACK_COPIES - 1)])
             kinds.append(code)
             del wd
-        for f in fns:
+        # three copies of the stack rotate (layer l of copy c at index c * layers + l)
+        extra = [mk() for mk in copy_fns]
+        nl = len(fns)
+        all_fns = fns + [extra[l][c] for c in range(STACK_COPIES - 1) for l in range(nl)]
+        for f in all_fns:
             f()
-        g = capture(torch, fns)
+        g = capture(torch, all_fns)
         g.replay()
-        per = timer.region(g.replay, steps) / steps
-        tfl = 2 * m * n * k * len(fns) / per / 1e12
+        reps = max(2, -(-steps // STACK_COPIES))
+        per = timer.region(g.replay, reps) / (reps * STACK_COPIES)
+        spread = replay_samples(torch, g, STACK_COPIES, 8)
+        tfl = 2 * m * n * k * nl / per / 1e12
         res[name] = dict(per_step_s=per, tflops=tfl, frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
+                         stack_copies_rotated=STACK_COPIES, step_us_p10_p50_p90=pct_us(spread),
                          codes=[int(c) for c in kinds])
-        for f, c in zip(fns, kinds):
+        for l, c in enumerate(kinds):
             if c not in single:
-                single[c] = timer.region(f, 8) / 8
+                lf = [all_fns[cc * nl + l] for cc in range(STACK_COPIES)]
+                gl = capture(torch, lf)
+                gl.replay()
+                single[c] = float(np.median(replay_samples(torch, gl, len(lf), 16)))
     names = {fp4.W8A8: "w8a8", fp4.A4: "w4a4", fp4.A4S: "w4a4_static", fp4.A8S: "w4a8_static"}
     for c, t in single.items():
         res[f"layer_{names[c]}_s"] = t
@@ -655,6 +817,7 @@ def bench_moe(torch, fp4, workloads, steps):
     g = capture(torch, [layer])
     g.replay()
     per = timer.region(g.replay, steps) / steps
+    spread = replay_samples(torch, g, 1, max(8, steps))
     parts = {}
     for name, f in stages.items():
         gs = capture(torch, [f])
@@ -666,6 +829,9 @@ def bench_moe(torch, fp4, workloads, steps):
     gemm_s = parts["gate_up_s"] + parts["gated_down_s"]
     return dict(experts=E, top_k=K, tokens=T, hidden=H, inter=I, routed_rows=R,
                 layer_per_step_s=per, layer_tflops=flops / per / 1e12,
+                layer_us_p10_p50_p90=pct_us(spread),
+                weight_bytes=int(w1q.codes.numel() + w1q.micro.numel() + 2 * w1q.macro.numel()
+                                 + w2q.codes.numel() + w2q.micro.numel() + 2 * w2q.macro.numel()),
                 gemm_tflops=flops / gemm_s / 1e12,
                 frac_bf16_peak=flops / gemm_s / 1e12 / BF16_PEAK_TFLOPS,
                 stages=parts,
@@ -710,7 +876,7 @@ def bench_attention(torch, fp4, workloads, steps):
     def attn(i):
         fp4.attention_decode_fp4kv(q, caches[i], lengths, out=outs[i], workspace=ws)
     timer = Timer(torch)
-    res = {}
+    res, spread = {}, {}
     for name, fn in (("step", step), ("attention", attn)):
         fns = [lambda i=i: fn(i) for i in range(len(caches))]
         for f in fns:
@@ -718,6 +884,7 @@ def bench_attention(torch, fp4, workloads, steps):
         g = capture(torch, fns)
         g.replay()
         res[name] = run_steps(torch, timer, g, fns, steps) / steps
+        spread[name] = pct_us(replay_samples(torch, g, len(fns), max(8, steps // len(fns))))
     torch.cuda.synchronize()
     tokens = int((lens.astype(np.int64) + 1).sum())
     per_token_head = 2 * (D // 2 + D // 16 + 1)  # K and V: codes, micro, macro (a pair's 2 B / 2)
@@ -728,6 +895,7 @@ def bench_attention(torch, fp4, workloads, steps):
                 context_min_mean_max=[int(lens.min() + 1), float(lens.mean() + 1), int(lens.max() + 1)],
                 algorithmic_bytes=total, bf16_cache_bytes_equivalent=tokens * Hkv * 2 * D * 2,
                 step_s=res["step"], attention_s=res["attention"],
+                step_us_p10_p50_p90=spread["step"], attention_us_p10_p50_p90=spread["attention"],
                 gbs_attention=total / res["attention"] / 1e9, gbs_step=total / res["step"] / 1e9,
                 frac_hbm_attention=total / res["attention"] / 1e9 / HBM_PEAK_GBS,
                 traffic_bytes_per_launch=load_traffic("attention_decode_fp4kv"),
@@ -778,7 +946,7 @@ def main():
     ap.add_argument("--skip-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize", "attention", "mx",
-                                       "sensitive", "probes"],
+                                       "sensitive", "probes", "repack", "ceilings"],
                     default=None,
                     help="run one workload only (for profiling); prints its record")
     ap.add_argument("--copy-probe", action="store_true",
@@ -827,15 +995,21 @@ def main():
               "attention": lambda: bench_attention(torch, fp4, workloads, args.steps),
               "mx": lambda: bench_mx(torch, fp4, workloads, args.steps),
               "sensitive": lambda: bench_sensitive(torch, fp4, workloads, args.steps),
-              "probes": lambda: bench_probes(torch, fp4, args.steps)}[args.only]
+              "probes": lambda: bench_probes(torch, fp4, args.steps),
+              "repack": lambda: bench_repack(torch, fp4, workloads, args.steps),
+              "ceilings": lambda: ceilings(torch, args.steps)}[args.only]
         rec = {args.only: fn()}
         if args.copy_probe:
             rec["copy_probe"] = copy_probe(torch)
         print(json.dumps(rec), flush=True)
         return
 
+    state_before = device_state()
     dec = bench_decode(torch, fp4, workloads, args.steps, args.warmup)
     print(f"# decode done: {dec['per_launch_s'] * 1e6:.2f} us/launch", file=sys.stderr, flush=True)
+    ceil = ceilings(torch, args.steps)
+    print(f"# ceilings done: read floor {ceil['read_floor_gbs']:.0f} GB/s, "
+          f"MFMA {ceil['mfma_f16_register_tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     secondary = {}
     if not args.skip_secondary:
         secondary["prefill_w4a4"] = bench_prefill(torch, fp4, workloads, max(8, args.steps // 8))
@@ -846,6 +1020,8 @@ def main():
         print("# moe done", file=sys.stderr, flush=True)
         secondary["quantize"] = bench_quantize(torch, fp4, workloads, args.steps)
         print("# quantize done", file=sys.stderr, flush=True)
+        secondary["repack"] = bench_repack(torch, fp4, workloads, max(16, args.steps // 4))
+        print("# repack done", file=sys.stderr, flush=True)
         secondary["decode_attention_fp4kv"] = bench_attention(torch, fp4, workloads, max(8, args.steps // 8))
         print("# attention done", file=sys.stderr, flush=True)
         secondary["prefill_mx_fp4"] = bench_mx(torch, fp4, workloads, max(8, args.steps // 8))
@@ -853,7 +1029,15 @@ def main():
         secondary["policy_stack_sensitive_static"] = bench_sensitive(torch, fp4, workloads,
                                                                      max(4, args.steps // 32))
         print("# sensitive done", file=sys.stderr, flush=True)
+    state_after = device_state()
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads)
+    # fractions of the measured ceilings beside the spec ones
+    mfma_probe = ceil["mfma_f16_register_tflops"]
+    for key in ("prefill_w4a4", "policy_stack"):
+        if key in secondary:
+            secondary[key]["frac_of_mfma_probe"] = secondary[key]["tflops"] / mfma_probe
+    if "moe_w4a4" in secondary:
+        secondary["moe_w4a4"]["frac_of_mfma_probe"] = secondary["moe_w4a4"]["gemm_tflops"] / mfma_probe
 
     traffic = load_traffic("gemv_decode_w4a16")
     achieved = dec["gbs"]
@@ -878,7 +1062,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": dec["bytes"]},
+                     "algorithmic_bytes_per_launch": dec["bytes"],
+                     "measured_read_floor_gbs": round(ceil["read_floor_gbs"], 1),
+                     "frac_of_read_floor": round(achieved / ceil["read_floor_gbs"], 4)},
+        "ceilings": ceil,
+        "device_state": {"before": state_before, "after": state_after},
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
