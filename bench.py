@@ -72,6 +72,10 @@ KERNEL_SOURCES = {
     "gemv": ["block_scaled_fp4_e2m1_amd/csrc/gemv.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
     "gemm": ["block_scaled_fp4_e2m1_amd/csrc/gemm.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
     "attention": ["block_scaled_fp4_e2m1_amd/csrc/attention.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
+    "quant": ["block_scaled_fp4_e2m1_amd/csrc/quant.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
+    "repack": ["block_scaled_fp4_e2m1_amd/csrc/repack.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
+    "gemm_r8": ["block_scaled_fp4_e2m1_amd/csrc/gemm_r8.hip", "block_scaled_fp4_e2m1_amd/csrc/gemm_ops.h",
+                "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
 }
 
 
