@@ -26,9 +26,21 @@ namespace {
 // pairs with the next pair's input in flight measured slower at every cap tried.)
 // Dequantize: 32 lanes per group, block b is row b / gchunks, groups
 // (b % gchunks) * 8 + 0..7, with gchunks = ceil(groups / 8).
+// TILE_ORDER (tiled output, rows % 16 == 0): the 16 segments of a workgroup are the 16 rows
+// of one tile (one group of one 16-row block), so the workgroup writes the tile's 2 KB of
+// codes, micro- and macro-scales whole; in row order a workgroup wrote one row's piece of
+// 16 tiles in scattered 4-byte stores, and partly written lines left the L2 as partial
+// writes (2.4x the bytes).
+template <int TILE_ORDER = 0>
 __device__ __forceinline__ bool seg_index16(int64_t rows, int64_t groups, int64_t& r, int64_t& g) {
   const uint32_t f = blockIdx.x * 16u + (threadIdx.x >> 4);  // < 2^28: see blocks_for16
   if ((int64_t)f >= rows * groups) return false;
+  if (TILE_ORDER) {
+    const uint32_t tile = f >> 4, rb = tile / (uint32_t)groups;
+    r = (int64_t)rb * 16 + (f & 15u);
+    g = (int64_t)(tile - rb * (uint32_t)groups);
+    return true;
+  }
   const uint32_t row = f / (uint32_t)groups;
   r = row;
   g = (int64_t)(f - row * (uint32_t)groups);
@@ -121,7 +133,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
   const int64_t groups = k >> 8;
   const int li = threadIdx.x & 15;  // micro-vector of the group
   int64_t r, g;
-  if (!seg_index16(rows, groups, r, g)) return;  // whole 16-lane segments leave together
+  if (!seg_index16<TILED>(rows, groups, r, g)) return;  // whole 16-lane segments leave together
   Raw16<IN_BF16> raw;
   load_raw16<IN_BF16>(x, r * ldx + g * kGroup + li * 16, raw);
   float v[16];

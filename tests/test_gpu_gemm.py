@@ -301,6 +301,48 @@ def test_grouped_empty_expert_and_many_experts():
     assert np.any(np.diff(offsets) == 0)
 
 
+@pytest.mark.parametrize("act", [4, 8, 16])
+@pytest.mark.parametrize("with_token_map", [True, False])
+def test_grouped_agrees_with_dense_bit_for_bit(act, with_token_map):
+    """A grouped product of 8192 routed rows over 40 uneven experts (one empty, every
+    expert's rows ragged at its end; n = 1024, k = 768: 3 groups, an odd count): each
+    expert's rows equal, bit for bit, the dense product of those rows alone, and two experts
+    pass the float32 gate against the oracle."""
+    tokens, experts, top_k, k, n, seed = 2048, 40, 4, 768, 1024, 23
+    logits = workloads.moe_router_logits(tokens=tokens, experts=experts, seed=seed)
+    logits[:, 7] = -np.inf  # expert 7 receives no rows
+    _, _, offsets, row_token, _ = oracle.route(logits, top_k)
+    R = int(offsets[-1])
+    name = fp4.fp4_product_kernel(act, torch.bfloat16, R, n, k, grouped=True, n_experts=experts)
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((tokens, k)).astype(np.float32)
+    a[:, rng.choice(k, 2, replace=False)] *= 50
+    a = workloads.to_bf16_values(a)
+    w = (0.02 * rng.standard_normal((experts * n, k))).astype(np.float32)
+    print(f"[case] grouped vs dense {ACTS[act]} token_map={with_token_map} R={R} ({name})", flush=True)
+    a_rows = a if with_token_map else a[row_token]
+    wq = _wq(w)
+    off = torch.from_numpy(offsets).cuda()
+    c = host(fp4.grouped_gemm_w4aX(act, to_device_bf16(a_rows),
+                                   torch.from_numpy(row_token).cuda() if with_token_map else None,
+                                   off, experts, R, wq, out_dtype=torch.float32))
+    counts = np.diff(offsets)
+    assert counts[7] == 0 and np.any(counts % 64 != 0)
+    for e in range(experts):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        sub = fp4.QTensor(wq.codes[e * n * k // 2:(e + 1) * n * k // 2], wq.micro[e * n * k // 16:(e + 1) * n * k // 16],
+                          wq.macro[e * n * k // 256:(e + 1) * n * k // 256], n, k, 0, fp4.LAYOUT_TILED)
+        dense = host(fp4.gemm_w4aX(act, to_device_bf16(a[row_token[lo:hi]]), sub, out_dtype=torch.float32))
+        assert np.array_equal(c[lo:hi].view(np.uint32), dense.view(np.uint32)), f"expert {e} differs"
+    for e in (int(np.argmax(counts)), 11):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        ref = oracle.gemm(a[row_token[lo:hi]].astype(np.float64),
+                          oracle.quantize(w[e * n:(e + 1) * n].astype(np.float64)), act)
+        f32_gate(c[lo:hi], ref)
+
+
 def test_moe_workload_full_size_subset_of_experts():
     cfg = workloads.WORKLOADS["moe_w4a4"]
     E, H, I, T = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["tokens"]
