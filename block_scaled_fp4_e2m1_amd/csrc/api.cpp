@@ -126,6 +126,30 @@ fp4_status prepare_activations(int32_t act, const void* a, int32_t a_dtype, int6
   return FP4_OK;
 }
 
+// W4A4 on the 128-row-wave form: the activations are quantized to E2M1 in the canonical
+// layout (quantize_fp4's output: codes, micro-scales, macro-scales, each 256-byte aligned
+// in the workspace, together smaller than the FP16 operand of the activation pass) and
+// the product kernel decodes them into the same FP16 operand itself.
+fp4_status prepare_packed_a4(const void* a, int32_t a_dtype, int64_t rows, int64_t k, int64_t lda, void* ws,
+                             fp4lib::GemmArgs& g, hipStream_t st) {
+  if (!fp4lib::quantize_grid_ok(rows, k)) return FP4_E_SHAPE;
+  const auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  uint8_t* codes = static_cast<uint8_t*>(ws);
+  uint8_t* micro = codes + up((size_t)rows * (size_t)(k / 2));
+  uint16_t* macro = reinterpret_cast<uint16_t*>(micro + up((size_t)rows * (size_t)(k / 16)));
+  const hipError_t e = fp4lib::launch_quantize(a, a_dtype == FP4_BF16, rows, k, lda, 0, 0, codes, micro, macro,
+                                               nullptr, st);
+  if (e != hipSuccess) return FP4_E_HIP;
+  g.a = codes;
+  g.a_is_bf16 = 0;
+  g.lda = k / 2;
+  g.a_scale = nullptr;
+  g.a_packed = 1;
+  g.a_micro = micro;
+  g.a_macro = macro;
+  return FP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,6 +175,9 @@ fp4_status fp4_device_check(void) { return check_device(); }
 
 const char* fp4_product_kernel(int32_t act, int32_t a_dtype, int64_t m, int64_t n, int64_t k, int32_t grouped,
                                int32_t n_experts, int32_t w_e4m3) {
+  if (act == FP4_A4 && !grouped && !w_e4m3 && valid_dtype(a_dtype) && m >= 1 && n >= 16 && n % 16 == 0 &&
+      k >= 256 && k % 256 == 0 && fp4lib::gemm_packed_a4(m, n, k))
+    return "k_gemm_r8 (128 x 256, 8 waves of 128 x 32; E2M1 activations decoded in the kernel)";
   act = act_of(act);
   if (!valid_act(act) || !valid_dtype(a_dtype) || m < 1 || n < 16 || n % 16 || k < 256 || k % 256) return nullptr;
   if (w_e4m3 && (act != FP4_A8 || grouped)) return nullptr;
@@ -317,7 +344,9 @@ fp4_status gemm_w4aX_impl(int32_t act, const void* a, int32_t a_dtype, int64_t m
                                              w->micro, w->macro, n, c, c_dtype == FP4_BF16,
                                              ldc, st));
   fp4lib::GemmArgs g{};
-  const fp4_status prep = prepare_activations(act, a, a_dtype, m, k, lda, workspace, g, st);
+  const fp4_status prep = act == FP4_A4 && fp4lib::gemm_packed_a4(m, n, k)
+                              ? prepare_packed_a4(a, a_dtype, m, k, lda, workspace, g, st)
+                              : prepare_activations(act, a, a_dtype, m, k, lda, workspace, g, st);
   if (prep != FP4_OK) return prep;
   g.m = m;
   g.n = n;

@@ -75,6 +75,12 @@ struct GemmArgs {
   const int32_t* expert_offsets;  // grouped only; nullptr for a dense product
   int32_t n_experts;
   int w_e4m3;               // E4M3 weights (dense, FP16 activation operand only)
+  // a_packed: the activations are E2M1 in the canonical layout (quantize_fp4's output):
+  // a = codes (k/2 bytes per row), a_micro, a_macro; a_is_bf16, lda and a_scale unused.
+  // Only the 128-row-wave form takes them (gemm_packed_a4 says when it runs).
+  int a_packed;
+  const uint8_t* a_micro;
+  const uint16_t* a_macro;
 };
 // Reduction lengths the product kernel covers (its per-group tables fit in LDS).
 bool gemm_supports(int64_t k);
@@ -88,6 +94,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 // CU): the shapes it covers (its LDS holds three operand stages and the row-factor table:
 // k <= 8192) and its launcher (hipErrorInvalidValue outside gemm_r8_supports()).
 bool gemm_r8_supports(int64_t m, int64_t n, int64_t k);
+// Whether a dense E2M1-weight product of this shape runs on the 128-row-wave form, which
+// takes W4A4 activations packed (quantize_fp4's canonical output) and decodes them itself.
+bool gemm_packed_a4(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_r8(const GemmArgs& g, hipStream_t st);
 
 // Plain float32 product for float32 activations (small shapes): one thread per output.

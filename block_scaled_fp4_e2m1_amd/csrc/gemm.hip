@@ -786,6 +786,11 @@ static bool plan_gemm(int64_t m, int64_t n, int64_t k, bool grouped, int n_exper
   return true;
 }
 
+bool gemm_packed_a4(int64_t m, int64_t n, int64_t k) {
+  GemmPlan p;
+  return plan_gemm(m, n, k, false, 0, false, p) && p.r8;
+}
+
 bool gemm_plan_ok(int64_t m, int64_t n, int64_t k, int grouped, int n_experts, int w_e4m3) {
   GemmPlan p;
   return plan_gemm(m, n, k, grouped != 0, n_experts, w_e4m3 != 0, p);

@@ -64,6 +64,22 @@ __shared__ uint4 g_rw2[kWChunks];
 constexpr int kMaxGroups = 32;
 __shared__ float g_sa[kMaxGroups * kBM];
 
+// Packed activations (W4A4): per wave and stage, its 16 rows' E2M1 codes (64 chunks of
+// 16 bytes: lane L's chunk is row L % 16, bytes 16 (L / 16) of the row's 64) and their
+// micro-scales (16 chunks: lane L's 4 bytes are row L % 16, bytes 4 ((L / 16) % 2) of the
+// row's 8; lanes 32..63 repeat lanes 0..31), in the same three-slot ring as the weights.
+// The decoded FP16 stages then alternate between two activation slots.
+constexpr int kPackChunks = 80;
+__shared__ uint4 g_pa0[kWaves * kPackChunks];
+__shared__ uint4 g_pa1[kWaves * kPackChunks];
+__shared__ uint4 g_pa2[kWaves * kPackChunks];
+template <int B>
+__device__ __forceinline__ uint4* p_slot() {
+  if constexpr (B == 0) return g_pa0;
+  else if constexpr (B == 1) return g_pa1;
+  else return g_pa2;
+}
+
 template <int B>
 __device__ __forceinline__ uint4* a_slot() {
   if constexpr (B == 0) return g_ra0;
@@ -85,8 +101,14 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int A_BF16, int C_BF16>
+// A_MODE: 0 the FP16 operand of the activation pass, 1 raw bf16 activations (W4A16),
+// 2 packed E2M1 activations (W4A4) decoded here into FP16 operands identical to the
+// activation pass's (code * mu, exact).
+template <int A_MODE, int C_BF16>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
+  constexpr int A_BF16 = A_MODE == 1;
+  constexpr bool PACKED = A_MODE == 2;
+  constexpr int kCp = PACKED ? 2 + kNI : kCopies;  // LDS-DMA instructions per wave and stage
   typedef OpTraits<A_BF16> Op;
   typedef typename Op::frag frag;
   const int groups = (int)(args.k >> 8);
@@ -114,9 +136,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   const int g_first = (int)(threadIdx.x >> 7) * ((groups + 3) >> 2);
   float fq[kQuarter + 1];
   if (!A_BF16) {
-    const float* f = args.a_scale + min(row_begin + ratio_row, row_end - 1) * groups;
+    const int64_t f_row = min(row_begin + ratio_row, row_end - 1);
+    if (PACKED) {  // the group factor is the macro-scale (1 for an all-zero group)
+      const uint16_t* f = args.a_macro + f_row * groups;
 #pragma unroll
-    for (int j = 0; j <= kQuarter; ++j) fq[j] = f[min(g_first + j, groups - 1)];
+      for (int j = 0; j <= kQuarter; ++j) {
+        const float v = fp16_value_hw(f[min(g_first + j, groups - 1)]);
+        fq[j] = v != 0.0f ? v : 1.0f;
+      }
+    } else {
+      const float* f = args.a_scale + f_row * groups;
+#pragma unroll
+      for (int j = 0; j <= kQuarter; ++j) fq[j] = f[min(g_first + j, groups - 1)];
+    }
   }
 
   // ---- buffer resources: per-lane byte offsets fixed for the whole k loop ----
@@ -125,6 +157,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
       __builtin_amdgcn_make_buffer_rsrc((void*)(a16 + row_begin * args.lda), (short)0, (int)0xFFFFFFFF, kRsrcWord3);
   const int64_t a_row = min(row_begin + 16 * wave + l16, row_end - 1);  // wave w copies row block w
   const uint32_t a_voff = (uint32_t)(((a_row - row_begin) * args.lda + 8 * q) * 2);
+  // packed: codes (k / 2 bytes per row) and micro-scales (k / 16 per row) of row 16 w + L % 16
+  const int64_t p_row = min(row_begin + 16 * wave + l16, row_end - 1);
+  const __amdgpu_buffer_rsrc_t pc_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(static_cast<const uint8_t*>(args.a) + (PACKED ? row_begin * (args.k >> 1) : 0)), (short)0,
+      (int)0xFFFFFFFF, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t pm_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(PACKED ? args.a_micro + row_begin * (args.k >> 4) : args.micro), (short)0, (int)0xFFFFFFFF, kRsrcWord3);
+  const uint32_t pc_voff = (uint32_t)((p_row - row_begin) * (args.k >> 1) + 16 * q);
+  const uint32_t pm_voff = (uint32_t)((p_row - row_begin) * (args.k >> 4) + 4 * (q & 1));
   const int64_t blocks_left = nblocks - wb0 > 0 ? nblocks - wb0 : 0;
   const int64_t tiles_left = blocks_left * groups;
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -143,13 +184,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
 
   // copy J (0..3: the activation chunk of step J; 4, 5: the codes of column block J - 4)
   // of stage s into ring slot (abuf, wbuf)
-  auto copy_part = [&](auto j_c, uint4* abuf, uint4* wbuf, int s) {  // stage s = 2 g + h
-    constexpr int J = decltype(j_c)::value;
+  auto copy_part = [&](auto j_c, auto b_c, int s) {  // ring slot B, stage s = 2 g + h
+    constexpr int J = decltype(j_c)::value, B = decltype(b_c)::value;
+    uint4* wbuf = w_slot<B>();
     const bool past = s >= stages;
     const int sc = past ? 0 : s;
     const int g = sc >> 1, h = sc & 1;
-    if constexpr (J < kSteps) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(past ? none : a_rsrc, (lds_void_ptr)(abuf + (wave * kSteps + J) * 64),
+    if constexpr (PACKED && J < 2) {  // this wave's rows: codes, then micro-scales
+      uint4* pb = p_slot<B>() + wave * kPackChunks;
+      if constexpr (J == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(past ? none : pc_rsrc, (lds_void_ptr)pb, 16, pc_voff,
+                                                 (uint32_t)(sc * 64), 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(past ? none : pm_rsrc, (lds_void_ptr)(pb + 64), 4, pm_voff,
+                                                 (uint32_t)(sc * 8), 0, 0);
+    } else if constexpr (PACKED) {
+      constexpr int ni = J - 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(past ? none : w_rsrc, (lds_void_ptr)(wbuf + (wave * kNI + ni) * 64), 16,
+                                               (uint32_t)lane * 16,
+                                               (uint32_t)((ni * groups + g) * kTileCodeBytes + h * 1024), 0, 0);
+    } else if constexpr (J < kSteps) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(past ? none : a_rsrc, (lds_void_ptr)(a_slot<B>() + (wave * kSteps + J) * 64),
                                                16, a_voff, (uint32_t)(sc * 256 + 64 * J), 0, 0);
     } else {
       constexpr int ni = J - kSteps;
@@ -158,8 +213,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
                                                (uint32_t)((ni * groups + g) * kTileCodeBytes + h * 1024), 0, 0);
     }
   };
-  auto copy_stage = [&](uint4* abuf, uint4* wbuf, int s) {
-    static_for<0, kCopies>([&](auto j_c) { copy_part(j_c, abuf, wbuf, s); });
+  auto copy_stage = [&](auto b_c, int s) {
+    static_for<0, kCp>([&](auto j_c) { copy_part(j_c, b_c, s); });
   };
   // micro-scale bytes of group g (byte t = step t of the group) and macro-scale bits
   auto load_mu = [&](uint2 (&mu)[kNI], int g) {
@@ -181,6 +236,43 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   };
   constexpr float kUnit = OpTraits<A_BF16>::kMicroUnit;
 
+  // Packed activations: lane (p, l16) of a wave decodes row l16's 32 codes of step p
+  // (k = 32 p .. 32 p + 31; p = q) into the FP16 fragment chunks of lanes (q', l16), q' =
+  // 0..3: codes times mu in FP16 as the activation pass forms them (the micro byte shifted
+  // into FP16 bit positions is mu * 2^-8; times 256 is mu, exactly).
+  uint4 pk = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t pk_mu = 0u, pk_m2[2] = {0u, 0u}, pk_out[4] = {0u, 0u, 0u, 0u};
+  auto pk_read = [&](auto pb_c) {
+    const uint4* pb = p_slot<decltype(pb_c)::value>() + wave * kPackChunks;
+    pk = pb[lane];
+    pk_mu = reinterpret_cast<const uint32_t*>(pb + 64)[l16 + 16 * (q >> 1)];
+  };
+  auto pk_scales = [&]() {
+    const uint32_t sh = 16 * (q & 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // micro-blocks 2 p (codes 0..15 of the piece), 2 p + 1
+      const uint32_t b = (pk_mu >> (sh + 8 * h)) & 0xFFu;
+      const half2_t unit = {(_Float16)256.0f, (_Float16)256.0f};
+      pk_m2[h] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (b << 7) | (b << 23)) * unit);
+    }
+  };
+  auto pk_decode_part = [&](auto fs_c, auto w_c, auto part_c) {
+    constexpr int FS = decltype(fs_c)::value, W = decltype(w_c)::value, PART = decltype(part_c)::value;
+    const uint32_t word = W == 0 ? pk.x : W == 1 ? pk.y : W == 2 ? pk.z : pk.w;
+    pk_out[PART] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, PART) *
+                                                    __builtin_bit_cast(half2_t, pk_m2[W >> 1]));
+    if constexpr (PART == 3) {
+      // A plain LDS store here would make the compiler wait for every LDS-DMA copy in flight
+      // (it cannot tell these slots from the copies' ring, which they never overlap); the
+      // store is issued directly instead: it has no result, its operands are ALU results,
+      // and the stage barrier's explicit lgkmcnt(0) covers its completion.
+      typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+      const u32x4 v = {pk_out[0], pk_out[1], pk_out[2], pk_out[3]};
+      const uint32_t addr = (uint32_t)(uintptr_t)(lds_void_ptr)(a_slot<FS>() + (wave * kSteps + q) * 64 + W * 16 + l16);
+      asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+    }
+  };
+
   // ---- prologue: macro-scales of groups 0 and 1, stages 0..2 in flight, stage 0 in ----
   uint32_t mw0[kNI], mw1[kNI], mw2[kNI];
   uint2 mu[kNI], mun[kNI];
@@ -189,9 +281,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   load_mu(mu, 0);
   load_mw(mw1, min(1, groups - 1));
   __builtin_amdgcn_sched_barrier(0);
-  copy_stage(a_slot<0>(), w_slot<0>(), 0);
-  copy_stage(a_slot<1>(), w_slot<1>(), 1);
-  copy_stage(a_slot<2>(), w_slot<2>(), 2);
+  copy_stage(std::integral_constant<int, 0>{}, 0);
+  copy_stage(std::integral_constant<int, 1>{}, 1);
+  copy_stage(std::integral_constant<int, 2>{}, 2);
   __builtin_amdgcn_sched_barrier(0);
   if (!A_BF16) {
     const int g_end = min(g_first + ((groups + 3) >> 2), groups);
@@ -203,7 +295,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   }
   // stage 0 landed and the ratio table written, for every wave (a plain barrier: a fence
   // would also wait for stages 1 and 2)
-  __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<2 * kCopies>::value);
+  __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<2 * kCp>::value);
+  if constexpr (PACKED) {  // stage 0's activations: this wave's rows, decoded into slot 0
+    pk_read(std::integral_constant<int, 0>{});
+    pk_scales();
+    static_for<0, 4>([&](auto w_c) {
+      static_for<0, 4>([&](auto part_c) { pk_decode_part(std::integral_constant<int, 0>{}, w_c, part_c); });
+    });
+    __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<2 * kCp>::value);
+  }
   __builtin_amdgcn_s_barrier();
 
   float4_t x[kMI][kNI];
@@ -239,6 +339,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   typename Op::micro_t msplat[kNI];
   const float* sa_lane = g_sa + 4 * q;  // + g * 128 + 16 mi: rows 16 mi + 4 q .. + 3
 
+
   // One MFMA step (T = 0..3 of a stage in ring slot B; H = 0 / 1 the group's first / second
   // stage) as eight regions, one per row block R, each fenced so that the compiler keeps the
   // VALU work where it is placed:
@@ -263,7 +364,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
     // the step before each product step loads that step's row ratios (regions 6, 7)
     constexpr bool RA_NEXT = !A_BF16 && (H == 0 ? T != 2 : T == 0);
     constexpr int PS_NEXT = H == 0 ? (T == 3 ? 2 : T) : 3;
-    const uint4* anext = T < 3 ? a_slot<B>() : a_slot<(B + 1) % 3>();
+    const uint4* anext;
+    if constexpr (PACKED) anext = T < 3 ? a_slot<H>() : a_slot<1 - H>();  // FP16 stages alternate
+    else anext = T < 3 ? a_slot<B>() : a_slot<(B + 1) % 3>();
     static_for<0, kMI>([&](auto r_c) {
       constexpr int R = decltype(r_c)::value;
       constexpr int NI = R / 4, P = R % 4;
@@ -272,11 +375,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
       af[R] = __builtin_bit_cast(frag, anext[(R * kSteps + TN) * 64 + lane]);
       // step 3: this slot is free (the barrier before the step); the copies that refill it
       // go out one per region (all waves at once right after the barrier stall on issue)
-      if constexpr (T == 3 && R < kCopies)
-        copy_part(std::integral_constant<int, R>{}, a_slot<B>(), w_slot<B>(), s_copy);
+      if constexpr (T == 3 && R < kCp)
+        copy_part(std::integral_constant<int, R>{}, b_c, s_copy);
       if constexpr (T == 2 && R == 0) {  // the next stage's code words (this wave's own copies)
 #pragma unroll
         for (int ni = 0; ni < kNI; ++ni) cwn[ni] = w_slot<(B + 1) % 3>()[(wave * kNI + ni) * 64 + lane];
+      }
+      if constexpr (PACKED) {  // the next stage's activations: this wave's rows, decoded
+        if constexpr (T == 0 && R == 5) pk_read(std::integral_constant<int, (B + 1) % 3>{});
+        if constexpr (T == 0 && R == 7) pk_scales();
+        if constexpr (T == 1 || T == 2)
+          pk_decode_part(std::integral_constant<int, 1 - H>{}, std::integral_constant<int, 2 * (T - 1) + R / 4>{},
+                         std::integral_constant<int, R % 4>{});
       }
       // next step's weights: micro-scale word of this stage (H == 0: first word), or of the
       // next stage (same group's second word, or the next group's first)
@@ -329,8 +439,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
       constexpr int kRes = ((PRE && R < 2) || (POST && R >= 2)) ? 8 : 0;
       constexpr int kProd = PROD && !A_BF16 && R >= 3 && R <= 6 ? 4 : 0;
       constexpr int kRat = PROD && R == 1 && PS == 0 ? 12 : 0;
-      constexpr int kV = kDec + kRes + kProd + kRat;
-      constexpr int kDs = 1 + (T == 2 && R == 0 ? kNI : 0) + (RA_NEXT && R >= 6 ? 1 : 0);
+      constexpr int kPk = PACKED ? ((T == 1 || T == 2) ? 2 : (T == 0 && R == 7) ? 8 : 0) : 0;
+      constexpr int kV = kDec + kRes + kProd + kRat + kPk;
+      constexpr int kDs = 1 + (T == 2 && R == 0 ? kNI : 0) + (RA_NEXT && R >= 6 ? 1 : 0) +
+                          (PACKED && T == 0 && R == 5 ? 2 : 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, (kV + 1) / 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -361,11 +473,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   auto run_stage = [&](auto b_c, auto h_c, auto rescale_c, int s) {
     constexpr int B = decltype(b_c)::value, H = decltype(h_c)::value;
     const int g = s >> 1;
+    constexpr int kWait = kCp + (H == 1 ? kLoads : 0);
+    if constexpr (PACKED) {  // the next stage's packed rows are read in step 0
+      __builtin_amdgcn_s_waitcnt(kVmcntWait<kWait>::value);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     step(b_c, C0{}, h_c, rescale_c, g, 0);
     step(b_c, C1{}, h_c, rescale_c, g, 0);
-    constexpr int kWait = kCopies + (H == 1 ? kLoads : 0);
-    __builtin_amdgcn_s_waitcnt(kVmcntWait<kWait>::value);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!PACKED) {
+      __builtin_amdgcn_s_waitcnt(kVmcntWait<kWait>::value);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     step(b_c, C2{}, h_c, rescale_c, g, 0);
     __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<kWait>::value);
     __builtin_amdgcn_s_barrier();
@@ -450,7 +568,10 @@ hipError_t launch_gemm_r8(const GemmArgs& g, hipStream_t st) {
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(64 * kWaves);
   const size_t lds = 0;
-  if (g.a_is_bf16) {
+  if (g.a_packed) {
+    if (g.c_is_bf16) hipLaunchKernelGGL((k_gemm_r8<2, 1>), grid, block, lds, st, g);
+    else hipLaunchKernelGGL((k_gemm_r8<2, 0>), grid, block, lds, st, g);
+  } else if (g.a_is_bf16) {
     if (g.c_is_bf16) hipLaunchKernelGGL((k_gemm_r8<1, 1>), grid, block, lds, st, g);
     else hipLaunchKernelGGL((k_gemm_r8<1, 0>), grid, block, lds, st, g);
   } else {
