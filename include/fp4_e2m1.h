@@ -175,7 +175,10 @@ fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t
  * 256); FP4_A16 with bf16 activations and m <= 8, k <= 8192 runs the decode GEMV; every
  * other call runs the activation pass (FP4_A4 / FP4_A8) and the product kernel, which
  * needs k <= 21760 (its per-group tables fit LDS). Shapes outside these limits return
- * FP4_E_SHAPE before anything is enqueued.
+ * FP4_E_SHAPE before anything is enqueued. For FP4_A4 on the large-product form
+ * (fp4_product_kernel names it) the activation pass writes A in the canonical E2M1
+ * layout of quantize_fp4 into the workspace and the product kernel decodes it; other
+ * paths write an FP16 operand and per-group factors there. Results are the same bits.
  * Source: "llama.cpp Put Precision Policy Inside the Model", intro and section "One model
  * can need more than one precision" (W4A4, W4A8 and W4A16 layers).
  */
