@@ -373,7 +373,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   extern __shared__ uint8_t g_dyn[];
   const int groups = (int)(args.k >> 8);
   // the four-slot ring runs four stages (two groups) per pass: plan_gemm selects these
-  // forms only for an even group count, so this exit is never taken through launch_gemm
+  // forms only for an even group count and launch_gemm refuses an odd one, so this exit
+  // (which keeps a misuse from reading past the ring) is never taken
   if (kRing == 4 && (groups & 1)) return;
   const int64_t n = args.n;
   const int64_t nblocks = n >> 4;
@@ -813,6 +814,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (!plan_gemm(g.m, g.n, g.k, g.expert_offsets != nullptr, g.n_experts, g.w_e4m3 != 0, p))
     return hipErrorInvalidValue;
   if (p.r8) return launch_gemm_r8(g, st);
+  if (g.a_packed) return hipErrorInvalidValue;  // packed activations: the 128-row-wave form only
   const bool narrow = p.narrow, wide16 = p.wide16, w10 = p.w10;
   const dim3 grid((unsigned)p.blocks), block(p.threads);
   const size_t lds = p.lds;
@@ -823,6 +825,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     if (g.a_is_bf16) { if (g.c_is_bf16) FP4_GEMM16(1, 1); else FP4_GEMM16(1, 0); }
     else { if (g.c_is_bf16) FP4_GEMM16(0, 1); else FP4_GEMM16(0, 0); }
 #undef FP4_GEMM16
+  } else if (w10 && (g.k >> 8) % 2) {
+    // the four-slot ring's precondition (plan_gemm never selects it for an odd group count;
+    // refused here too rather than launched into the kernel's guard)
+    return hipErrorInvalidValue;
   } else if (w10 && g.w_e4m3) {
     if (g.c_is_bf16) hipLaunchKernelGGL((k_gemm_w10e<1>), grid, block, lds, st, g);
     else hipLaunchKernelGGL((k_gemm_w10e<0>), grid, block, lds, st, g);
