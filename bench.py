@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -133,8 +134,10 @@ def run_steps(torch, timer, graph, fns, steps):
 
 
 def replay_samples(torch, graph, launches, reps):
-    """Per-launch seconds of each of `reps` graph replays (each replay's time over its
-    `launches` launches), on the stream the replays run on."""
+    """Per-launch seconds of each graph replay (each replay's time over its `launches`
+    launches), on the stream the replays run on: at least `reps` replays, at least 16, and
+    at least 200 launches in all."""
+    reps = max(reps, 16, -(-200 // max(1, launches)))
     s = torch.cuda.current_stream()
     evs = []
     for _ in range(reps):
@@ -933,8 +936,15 @@ def cpu_baseline(workloads, budget_s=12.0):
     t_prod = secs - t_quant
     frac = rows_done / n
     nbytes = algorithmic_bytes_gemv(m, n, k) * frac
+    cpu_model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return {"value": nbytes / t_prod / 1e9, "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
+            "quantize_s": round(t_quant, 3), "product_s": round(t_prod, 3),
             "sample": f"decode W4A16 product on {rows_done} of {n} weight rows "
                       f"(dequantize + float64 matmul {t_prod:.2f} s; the oracle's quantization "
                       f"of those rows took {t_quant:.2f} s more); numpy elementwise work is "
