@@ -75,6 +75,7 @@ KERNEL_SOURCES = {
     "attention": ["block_scaled_fp4_e2m1_amd/csrc/attention.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
     "quant": ["block_scaled_fp4_e2m1_amd/csrc/quant.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
     "repack": ["block_scaled_fp4_e2m1_amd/csrc/repack.hip", "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
+    "probes": ["block_scaled_fp4_e2m1_amd/csrc/probes.hip"],
     "gemm_r8": ["block_scaled_fp4_e2m1_amd/csrc/gemm_r8.hip", "block_scaled_fp4_e2m1_amd/csrc/gemm_ops.h",
                 "block_scaled_fp4_e2m1_amd/csrc/fp4_device.h"],
 }

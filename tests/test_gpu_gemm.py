@@ -233,6 +233,28 @@ def test_gemm_float32_activations_a4():
     f32_gate(host(c), _oracle_c(a.astype(np.float64), w, oracle.A4))
 
 
+def test_gemm_float32_activations_a4_packed_form():
+    """float32 activations on the W4A4 large-product form (the activation pass quantizes
+    float32 input to packed E2M1, the product kernel decodes it): oracle gate, and equal
+    bit for bit to the same activations given as bf16 when they are bf16 values."""
+    rng = np.random.default_rng(303)
+    m, n, k = 2043, 4080, 1024
+    name = fp4.fp4_product_kernel(fp4.A4, torch.float32, m, n, k)
+    assert "decoded in the kernel" in name, name
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    a[:, rng.choice(k, 3, replace=False)] *= 50
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    print(f"[case] gemm A4 float32 activations, packed form m={m} n={n} k={k}", flush=True)
+    wq = _wq(w)
+    c = host(fp4.gemm_w4aX(fp4.A4, torch.from_numpy(a).cuda(), wq, out_dtype=torch.float32))
+    rows = np.r_[0:40, m - 40:m]
+    f32_gate(c[rows], _oracle_c(a[rows].astype(np.float64), w, oracle.A4))
+    ab = workloads.to_bf16_values(a)
+    c32 = fp4.gemm_w4aX(fp4.A4, torch.from_numpy(ab).cuda(), wq, out_dtype=torch.float32)
+    cbf = fp4.gemm_w4aX(fp4.A4, to_device_bf16(ab), wq, out_dtype=torch.float32)
+    assert torch.equal(c32, cbf)
+
+
 def test_prefill_w4a4_full_size_sampled():
     a, w, _ = workloads.prefill()
     print("[case] prefill W4A4 2048x4096x4096 (sampled)", flush=True)

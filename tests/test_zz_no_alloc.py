@@ -57,6 +57,23 @@ def test_noalloc_matches_workspace_entry_point_twice(act):
         assert torch.equal(got, want), f"act={act} m={m}: differs from gemm_w4aX"
 
 
+def test_noalloc_packed_activations_twice():
+    """A W4A4 shape on the large-product form (packed E2M1 activations in the scratch,
+    decoded by the product kernel), then a smaller one on the same form: identical to
+    gemm_w4aX with a workspace both times."""
+    rng = np.random.default_rng(970)
+    for m, n, k in ((2043, 4080, 1024), (1950, 4096, 512)):
+        name = fp4.fp4_product_kernel(fp4.A4, torch.bfloat16, m, n, k)
+        assert "decoded in the kernel" in name, name
+        print(f"[case] noalloc packed A4 m={m} n={n} k={k} ({name})", flush=True)
+        a, wq = _operands(rng, m, n, k)
+        want = fp4.gemm_w4aX(fp4.A4, a, wq, out_dtype=torch.bfloat16)
+        got = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+        assert _noalloc(fp4.A4, a, wq, got) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"m={m}: differs from gemm_w4aX"
+
+
 def test_noalloc_refuses_a_workspace_beyond_the_scratch():
     rng = np.random.default_rng(960)
     m, n, k = 4096, 256, 4096  # 4096 x 4096 activations: 33.8 MB > 32 MiB
