@@ -518,6 +518,46 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   // in the prologue; the weight operand's unit cancels except in the final factor.
   auto ratios_after = [&](int g, Rescale<WM>& r) {
     const bool last = g + 1 >= groups;
+    if constexpr (kRing == 4) {
+      // The tables live in dynamic LDS, which the compiler cannot tell apart from the
+      // ring's static slots: a plain read here made it wait for every copy in flight
+      // (vmcnt 0, the copies issued three stages ahead included). These reads are
+      // issued as one block that waits for its own results (lgkmcnt 0) instead; the
+      // tables were complete before the loop (prologue wait and barrier).
+      static_assert(NI == 1, "one row block per wave in the four-slot forms");
+      const int gn = min(g + 1, groups - 1);
+      const uint32_t mw_a = (uint32_t)(uintptr_t)(lds_void_ptr)(mw_lane + g * 16);
+      const uint32_t mw_b = (uint32_t)(uintptr_t)(lds_void_ptr)(mw_lane + gn * 16);
+      uint32_t h0, h1;
+      if constexpr (!A_BF16) {
+        const uint32_t sa = (uint32_t)(uintptr_t)(lds_void_ptr)(sa_lane + g * kBM);
+        float4_t v0, v1, v2, v3;
+        asm volatile(
+            "ds_read_b128 %0, %6\n\tds_read_b128 %1, %6 offset:64\n\tds_read_b128 %2, %6 offset:128\n\t"
+            "ds_read_b128 %3, %6 offset:192\n\tds_read_u16 %4, %7\n\tds_read_u16 %5, %8\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(h0), "=&v"(h1)
+            : "v"(sa), "v"(mw_a), "v"(mw_b));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          r.ra[0][i] = v0[i];
+          r.ra[1][i] = v1[i];
+          r.ra[2][i] = v2[i];
+          r.ra[3][i] = v3[i];
+        }
+      } else {
+        asm volatile("ds_read_u16 %0, %2\n\tds_read_u16 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(h0), "=&v"(h1)
+                     : "v"(mw_a), "v"(mw_b));
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r.ra[mi][i] = 1.0f;
+      }
+      const float f0 = fp16_value_hw(h0), f1 = fp16_value_hw(h1);  // a zero factor counts as 1
+      const float c0 = f0 != 0.0f ? f0 : 1.0f, c1 = f1 != 0.0f ? f1 : 1.0f;
+      r.rw[0] = c0 * (last ? kUnit : __builtin_amdgcn_rcpf(c1));
+      return;
+    }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
       r.rw[ni] = last ? col_factor(ni, g) * kUnit
@@ -532,15 +572,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
 
   uint2 mu_cur[4], mu_nxt[4];
   const int stages = 2 * groups;
-  // Two slots: stage 0, its micro-scales, wait for all. Four slots: stages 0 and 1, the
-  // micro-scales, stage 2, wait for all but stage 2, so that every stage later finds the
-  // same loads younger than the copies it waits for (see run_stage).
+  // Two slots: stage 0, its micro-scales, wait for all. Four slots: stage 0, the
+  // micro-scales, stages 1 and 2, wait for all but stage 2, so that every stage later
+  // finds the same loads younger than the copies it waits for (see run_stage).
   copy_stage(a_slot<0>(), w_slot<WM, 0>(), 0, false);
-  if constexpr (kRing == 4) copy_stage(a_slot<1>(), w_slot<WM, 1>(), 1, false);
   __builtin_amdgcn_sched_barrier(0);
   load_micro(mu_cur, 0);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kRing == 4) copy_stage(a_slot<2>(), w_slot<WM, 2>(), 2, false);
+  if constexpr (kRing == 4) {
+    copy_stage(a_slot<1>(), w_slot<WM, 1>(), 1, false);
+    copy_stage(a_slot<2>(), w_slot<WM, 2>(), 2, false);
+  }
   // stage 0's code words and step-0 weight fragments (the wave's own copies)
   uint4 cw[4];
   typename OpTraits<A_BF16>::frag wf0[NI];
@@ -581,25 +623,37 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   // Stage s reads ring slot B = s % kRing and first issues the copies of stage
   // s + kRing - 1 into the slot stage s - 1 used (free after the barrier). Its last step
   // waits for stage s + 1's copies, with these loads younger than them:
-  //   two slots:  the micro-scale loads of stage s (H == 0 stages only);
-  //   four slots: the copies of stages s + 2 and s + 3 and the micro-scale loads of
-  //               stages s - 2 .. s (two H == 0 stages when H == 0, else one).
+  //   two slots:  the micro-scale loads of stage s (H == 0 stages only), issued after
+  //               the copies;
+  //   four slots: the copies of stages s + 2 and s + 3, and the micro-scale loads of
+  //               the one H == 0 stage among s - 1 and s, issued before that stage's
+  //               copies (so the next group's micro-scales never wait behind a stage
+  //               of copies).
+  // The four-slot barrier is a bare s_barrier after lgkmcnt 0: every wave has waited
+  // for its own copies of stage s (previous stage's last step), and its reads of the
+  // slot about to be refilled are complete. __syncthreads() would add a workgroup fence,
+  // which waits for the copies still in flight, two and three stages ahead.
   auto run_stage = [&](auto h_const, auto b_const, int s) {
     constexpr int H = decltype(h_const)::value, B = decltype(b_const)::value;
-    constexpr int kWait = kRing == 2 ? (H == 0 ? NI : 0) : 2 * (kAPieces + kPieces) + (H == 0 ? 2 : 1) * NI;
-    __syncthreads();
+    constexpr int kWait = kRing == 2 ? (H == 0 ? NI : 0) : 2 * (kAPieces + kPieces) + NI;
+    // (the micro-scale loads are unconditional in H == 0 stages, the last group
+    // re-reading its own, so that the count of loads younger than the awaited copies is
+    // fixed; it holds because every iteration runs this same code: in a separately
+    // compiled last iteration these loads would be dead, the compiler would drop them,
+    // and the wait would let copies through unfinished)
     if constexpr (kRing == 2) {
+      __syncthreads();
       if (s + 1 < stages) copy_stage(a_slot<(B + 1) % 2>(), w_slot<WM, (B + 1) % 2>(), s + 1, false);
+      __builtin_amdgcn_sched_barrier(0);
+      if (H == 0) load_micro(mu_nxt, min((s >> 1) + 1, groups - 1));
     } else {
+      __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<63>::value);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (H == 0) load_micro(mu_nxt, min((s >> 1) + 1, groups - 1));
+      __builtin_amdgcn_sched_barrier(0);
       copy_stage(a_slot<(B + 3) % 4>(), w_slot<WM, (B + 3) % 4>(), min(s + 3, stages - 1), s + 3 >= stages);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // (unconditional in H == 0 stages, the last group re-reading its own, so that the
-    // count of loads younger than the awaited copies is fixed; it holds because every
-    // iteration runs this same code: in a separately compiled last iteration these loads
-    // would be dead, the compiler would drop them, and the wait would let copies through
-    // unfinished)
-    if (H == 0) load_micro(mu_nxt, min((s >> 1) + 1, groups - 1));
     __builtin_amdgcn_sched_barrier(0);
     // next stage: same group (H == 0: micro-scale word 1 of mu_cur) or the next group
     // (H == 1: word 0 of mu_nxt)

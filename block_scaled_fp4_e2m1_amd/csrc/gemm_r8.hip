@@ -471,7 +471,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
   // The barrier before step 3 publishes stage s + 1 to every wave and frees this slot (all
   // its reads done: lgkmcnt 0), which then receives stage s + 3.
   auto run_stage = [&](auto b_c, auto h_c, auto rescale_c, int s) {
-    constexpr int B = decltype(b_c)::value, H = decltype(h_c)::value;
+    constexpr int H = decltype(h_c)::value;
     const int g = s >> 1;
     constexpr int kWait = kCp + (H == 1 ? kLoads : 0);
     if constexpr (PACKED) {  // the next stage's packed rows are read in step 0
