@@ -156,6 +156,15 @@ def pct_us(samples):
     return [round(float(np.percentile(samples, q)) * 1e6, 3) for q in (10, 50, 90)]
 
 
+def count_histogram(counts, width):
+    """Experts per bin of `width` routed rows: the first bin starts at the smallest count
+    rounded down to a multiple of `width`."""
+    lo = int(counts.min()) // width * width
+    nb = (int(counts.max()) - lo) // width + 1
+    hist = np.bincount((counts - lo) // width, minlength=nb)
+    return dict(bin_rows=width, first_bin_start=lo, experts=[int(v) for v in hist])
+
+
 def clone_q(fp4, q):
     """A device copy of a quantized tensor (its own memory: rotation defeats the caches)."""
     return fp4.QTensor(q.codes.clone(), q.micro.clone(), q.macro.clone(), q.rows, q.k, q.elem, q.layout)
@@ -638,11 +647,12 @@ def bench_policy(torch, fp4, workloads, steps):
     cfg = workloads.WORKLOADS["policy_stack"]
     m, k, n = cfg["m"], cfg["k"], cfg["n"]
     flags = workloads.policy_flags()
-    layers = []
+    layers, w32 = [], []
     for l in range(cfg["layers"]):
         w, x = workloads.policy_layer(l)
         act = fp4.fp4_policy_select(fp4.POLICY_AUTO, bool(flags[l]))
-        layers.append((act, fp4.quantize_fp4(torch.from_numpy(w).cuda(), layout=fp4.LAYOUT_TILED),
+        w32.append(torch.from_numpy(w).cuda())
+        layers.append((act, fp4.quantize_fp4(w32[-1], layout=fp4.LAYOUT_TILED),
                        torch.from_numpy(x).cuda().to(torch.bfloat16)))
     copies = [layers] + [[(act, clone_q(fp4, q), x.clone()) for act, q, x in layers]
                          for _ in range(STACK_COPIES - 1)]
@@ -668,9 +678,31 @@ def bench_policy(torch, fp4, workloads, steps):
         gl = capture(torch, lf)
         gl.replay()
         return float(np.median(replay_samples(torch, gl, len(lf), 16)))
+    # chained: x_{l+1} = layer_l(x_l), layer 0 fed its own input, the three stack copies
+    # rotating as above (reported, not gated); the last output against the float32 chain
+    # of the unquantized weights from the same input
+    bufs = [torch.empty(m, n, dtype=torch.bfloat16, device="cuda") for _ in layers]
+    chain = []
+    for stack in copies:
+        xin = stack[0][2]
+        for l, (act, wq, _) in enumerate(stack):
+            chain.append(lambda a=act, q=wq, xi=xin, o=bufs[l]: fp4.gemm_w4aX(a, xi, q, out=o, workspace=ws))
+            xin = bufs[l]
+    for f in chain:
+        f()
+    gc = capture(torch, chain)
+    gc.replay()
+    chain_spread = replay_samples(torch, gc, STACK_COPIES, 8)
+    torch.cuda.synchronize()
+    y = layers[0][2].float()
+    for wl in w32:
+        y = torch.matmul(y, wl.t().contiguous())
+    chain_err = float(torch.linalg.norm(bufs[-1].float() - y) / torch.linalg.norm(y))
+    del w32
     tfl = flops / per / 1e12
     return dict(layers=len(layers), flagged=[int(i) for i in np.nonzero(flags)[0]], per_step_s=per,
                 stack_copies_rotated=STACK_COPIES, step_us_p10_p50_p90=pct_us(spread),
+                chained=dict(step_us_p10_p50_p90=pct_us(chain_spread), rel_error_vs_fp32_chain=chain_err),
                 kernels={"a4": fp4.fp4_product_kernel(fp4.A4, torch.bfloat16, m, n, k),
                          "a8": fp4.fp4_product_kernel(fp4.A8, torch.bfloat16, m, n, k)},
                 tflops=tfl, frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
@@ -844,7 +876,7 @@ def bench_moe(torch, fp4, workloads, steps):
                 frac_bf16_peak=flops / gemm_s / 1e12 / BF16_PEAK_TFLOPS,
                 stages=parts,
                 rows_per_expert=dict(min=int(counts.min()), max=int(counts.max()),
-                                     mean=float(counts.mean())))
+                                     mean=float(counts.mean()), histogram=count_histogram(counts, 8)))
 
 
 def build_kv_cache(torch, fp4, workloads, cfg, layer, chunk=4096):
