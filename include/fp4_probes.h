@@ -1,6 +1,6 @@
 /*
  * fp4_probes.h -- measurement probes (libfp4_probes.so), not part of the product API: they
- * measure, on the device at hand, the ceilings the library's kernels are judged against.
+ * measure, on the device at hand, the ceilings the library's kernels are measured against.
  * Every pointer is caller-owned device memory; `stream` is a hipStream_t. Each call
  * enqueues one kernel and returns 0, 2 for invalid arguments (nothing enqueued) or 8 when
  * the launch fails.
