@@ -86,11 +86,12 @@ typedef __attribute__((address_space(1))) void* global_void_ptr;
 
 // 128 x 128 output tile per workgroup, 4 waves of 64 x 64 (4 x 4 MFMAs of 16 x 16), one
 // 128-wide k tile per stage. Each stage's operands (8 A and 8 W tiles of 1 KB, their
-// scale bytes) are copied once per workgroup into LDS by 16-byte LDS-DMA, two stages
-// ahead, and each wave reads its fragments from there: the waves sharing rows or columns
-// no longer fetch the same bytes through L1 twice. One barrier per stage; one LDS object
-// per stage and compile-time stage indices, so the compiler can tell the buffer being
-// filled from the one being read.
+// scale bytes) are copied once per workgroup into LDS by 16-byte LDS-DMA, three stages
+// ahead into a four-slot ring, and each wave reads its fragments from there: the waves
+// sharing rows or columns no longer fetch the same bytes through L1 twice. One barrier
+// per stage publishes the next stage, whose fragments each wave then reads while its
+// MFMAs work on the current one. One LDS object per slot and compile-time slot indices,
+// so the compiler can tell the slot being filled from the ones being read.
 struct MxStage {
   uint4 a[8][64];      // tile i (row block i of the workgroup), lane l's 16 bytes
   uint4 w[8][64];
@@ -100,15 +101,23 @@ struct MxStage {
 __shared__ MxStage g_mx0;
 __shared__ MxStage g_mx1;
 __shared__ MxStage g_mx2;
-constexpr int kMxStages = 3;
+__shared__ MxStage g_mx3;
+constexpr int kMxStages = 4;
 constexpr int kMxCopies = 5;  // LDS-DMA instructions per wave and stage
 
 template <int B>
 __device__ __forceinline__ MxStage& mx_stage() {
   if constexpr (B == 0) return g_mx0;
   else if constexpr (B == 1) return g_mx1;
-  else return g_mx2;
+  else if constexpr (B == 2) return g_mx2;
+  else return g_mx3;
 }
+
+// a wave's operands of one stage
+struct MxFrags {
+  u32x4_t af[4], wf[4];
+  uint32_t as[4], ws[4];
+};
 
 template <int OUT_BF16>
 __global__ __launch_bounds__(256, 2) void k_gemm_mx(const uint8_t* __restrict__ a_codes,
@@ -164,69 +173,129 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx(const uint8_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const MxStage& st) {
-    uint4 af[4], wf[4];
-    uint32_t as[4], ws[4];
+  auto read_frags = [&](const MxStage& st, MxFrags& f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      af[i] = st.a[wm * 4 + i][lane];
-      wf[i] = st.w[wn * 4 + i][lane];
-      as[i] = reinterpret_cast<const uint8_t*>(st.as[wm * 4 + i])[lane];
-      ws[i] = reinterpret_cast<const uint8_t*>(st.ws[wn * 4 + i])[lane];
+      f.af[i] = __builtin_bit_cast(u32x4_t, st.a[wm * 4 + i][lane]);
+      f.wf[i] = __builtin_bit_cast(u32x4_t, st.w[wn * 4 + i][lane]);
+      f.as[i] = reinterpret_cast<const uint8_t*>(st.as[wm * 4 + i])[lane];
+      f.ws[i] = reinterpret_cast<const uint8_t*>(st.ws[wn * 4 + i])[lane];
     }
+  };
+  // The same reads as one inline-asm block that waits for its own results. Used by the
+  // first stage of each pass of the stage loop: where the loop's back edge meets its
+  // entry the compiler no longer knows which slots have copies in flight, and before a
+  // plain LDS read there it waited for every copy, the ones issued three stages ahead
+  // included.
+  auto read_frags_waited = [&](const MxStage& st, MxFrags& f) {
+    const uint32_t a_addr = (uint32_t)(uintptr_t)(lds_void_ptr)&st.a[wm * 4][lane];
+    const uint32_t w_addr = (uint32_t)(uintptr_t)(lds_void_ptr)&st.w[wn * 4][lane];
+    const uint32_t as_addr = (uint32_t)(uintptr_t)(lds_void_ptr)(reinterpret_cast<const uint8_t*>(st.as[wm * 4]) + lane);
+    const uint32_t ws_addr = (uint32_t)(uintptr_t)(lds_void_ptr)(reinterpret_cast<const uint8_t*>(st.ws[wn * 4]) + lane);
+    asm volatile(
+        "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:1024\n\t"
+        "ds_read_b128 %2, %16 offset:2048\n\tds_read_b128 %3, %16 offset:3072\n\t"
+        "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:1024\n\t"
+        "ds_read_b128 %6, %17 offset:2048\n\tds_read_b128 %7, %17 offset:3072\n\t"
+        "ds_read_u8 %8, %18\n\tds_read_u8 %9, %18 offset:64\n\t"
+        "ds_read_u8 %10, %18 offset:128\n\tds_read_u8 %11, %18 offset:192\n\t"
+        "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
+        "ds_read_u8 %14, %19 offset:128\n\tds_read_u8 %15, %19 offset:192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.af[0]), "=&v"(f.af[1]), "=&v"(f.af[2]), "=&v"(f.af[3]), "=&v"(f.wf[0]), "=&v"(f.wf[1]),
+          "=&v"(f.wf[2]), "=&v"(f.wf[3]), "=&v"(f.as[0]), "=&v"(f.as[1]), "=&v"(f.as[2]), "=&v"(f.as[3]),
+          "=&v"(f.ws[0]), "=&v"(f.ws[1]), "=&v"(f.ws[2]), "=&v"(f.ws[3])
+        : "v"(a_addr), "v"(w_addr), "v"(as_addr), "v"(ws_addr));
+  };
+  auto compute = [&](const MxFrags& f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const v8i a = {(int)af[i].x, (int)af[i].y, (int)af[i].z, (int)af[i].w, 0, 0, 0, 0};
+      const v8i a = {(int)f.af[i][0], (int)f.af[i][1], (int)f.af[i][2], (int)f.af[i][3], 0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const v8i b = {(int)wf[j].x, (int)wf[j].y, (int)wf[j].z, (int)wf[j].w, 0, 0, 0, 0};
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i][j], 4, 4, 0, (int)as[i], 0,
-                                                                       (int)ws[j]);
+        const v8i b = {(int)f.wf[j][0], (int)f.wf[j][1], (int)f.wf[j][2], (int)f.wf[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i][j], 4, 4, 0, (int)f.as[i], 0,
+                                                                       (int)f.ws[j]);
       }
     }
   };
-  // stage kt (buffer B = kt % 3): wait for this wave's copies of kt (the copies of kt + 1,
-  // issued later, may stay in flight) and its LDS reads, barrier (every wave's copies of kt
-  // have landed and every wave is done reading kt - 1, whose buffer receives kt + 2), copy
-  // kt + 2, compute kt. The barrier is a bare s_barrier: a workgroup fence would also wait
-  // for the copies of kt + 1. LDS is coherent inside the workgroup; the empty asm
-  // statements keep the compiler from moving memory accesses across it.
-  // Every step copies (the last stages again, into the buffer of a finished stage), so
-  // exactly kMxCopies copies are younger than a stage's own on every path.
+  // Stage kt (slot B = kt % 4), its fragments already in registers (cur): wait for this
+  // wave's copies of kt + 1 (only the copies of kt + 2, issued one stage later, may stay in
+  // flight), barrier (every wave's copies of kt + 1 have landed, and every wave is done
+  // with kt - 1: its fragments were read a stage earlier and consumed by its MFMAs), copy
+  // kt + 3 into kt - 1's slot, read kt + 1's fragments, then the MFMAs of kt. The barrier is
+  // a bare s_barrier: a workgroup fence would also wait for the copies of kt + 2. LDS is
+  // coherent inside the workgroup; the empty asm statements keep the compiler from moving
+  // memory accesses across it. Every stage copies (past the end, the last tile again into
+  // the slot of a finished stage), so exactly kMxCopies copies are younger than the awaited
+  // ones on every path; past the end the fragments read are not used.
+  MxFrags fr[2];  // stage kt's fragments in fr[kt & 1], the next stage's read into the other
   auto step = [&](auto b_const, int64_t kt) {
     constexpr int B = decltype(b_const)::value;
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<kMxCopies>::value);
+    __builtin_amdgcn_s_waitcnt(kVmcntWait<kMxCopies>::value);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    copy_stage(mx_stage<(B + 2) % kMxStages>(), min(kt + 2, kt_count - 1));
-    compute(mx_stage<B>());
+    copy_stage(mx_stage<(B + 3) % kMxStages>(), min(kt + 3, kt_count - 1));
+    MxFrags& nxt = fr[(B + 1) & 1];
+    if constexpr (B == 0)
+      read_frags_waited(mx_stage<1>(), nxt);
+    else
+      read_frags(mx_stage<(B + 1) % kMxStages>(), nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(fr[B & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    // (the next fragments are used here, after the MFMAs are issued: otherwise the
+    // compiler sinks their reads to the next stage, right before the MFMAs that need them)
+    asm volatile("" : : "v"(nxt.af[0]), "v"(nxt.af[1]), "v"(nxt.af[2]), "v"(nxt.af[3]), "v"(nxt.wf[0]),
+                 "v"(nxt.wf[1]), "v"(nxt.wf[2]), "v"(nxt.wf[3]));
+    asm volatile("" : : "v"(nxt.as[0]), "v"(nxt.as[1]), "v"(nxt.as[2]), "v"(nxt.as[3]), "v"(nxt.ws[0]),
+                 "v"(nxt.ws[1]), "v"(nxt.ws[2]), "v"(nxt.ws[3]));
   };
   copy_stage(g_mx0, 0);
   copy_stage(g_mx1, min((int64_t)1, kt_count - 1));
-  for (int64_t kt = 0; kt < kt_count; kt += kMxStages) {
+  copy_stage(g_mx2, min((int64_t)2, kt_count - 1));
+  // stage 0 published (this wave's copies of it done; those of 1 and 2 may be in flight)
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<2 * kMxCopies>::value);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_frags(g_mx0, fr[0]);
+  // whole passes over the four slots (one exit), then the last 0-3 stages
+  int64_t kt = 0;
+  for (; kt + kMxStages <= kt_count; kt += kMxStages) {
     step(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 >= kt_count) break;
     step(std::integral_constant<int, 1>{}, kt + 1);
-    if (kt + 2 >= kt_count) break;
     step(std::integral_constant<int, 2>{}, kt + 2);
+    step(std::integral_constant<int, 3>{}, kt + 3);
+  }
+  if (kt < kt_count) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < kt_count) {
+      step(std::integral_constant<int, 1>{}, kt + 1);
+      if (kt + 2 < kt_count) step(std::integral_constant<int, 2>{}, kt + 2);
+    }
   }
   // no copy may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
-  const int64_t m0 = (int64_t)by * 128 + wm * 64;
-  const int64_t n0 = (int64_t)bx * 128 + wn * 64;
+  // (opaque copies of the lane index and the tile's origin: the store addresses are formed
+  // here, not before the loop, where they would hold registers)
+  int lane_e = lane;
+  int64_t m0 = (int64_t)by * 128 + wm * 64;
+  int64_t n0 = (int64_t)bx * 128 + wn * 64;
+  asm volatile("" : "+v"(lane_e), "+s"(m0), "+s"(n0));
   // lane l holds rows 4 (l / 16) + t, column l % 16 of each 16 x 16 tile
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + 16 * j + (lane & 15);
+      const int64_t col = n0 + 16 * j + (lane_e & 15);
       if (col >= n) continue;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int64_t row = m0 + 16 * i + 4 * (lane >> 4) + t;
+        const int64_t row = m0 + 16 * i + 4 * (lane_e >> 4) + t;
         if (row >= m) continue;
         if (OUT_BF16)
           static_cast<uint16_t*>(c)[row * ldc + col] = (uint16_t)bf16_rne_bits(acc[i][j][t]);

@@ -58,7 +58,10 @@ def test_quantize_full_prefill_weight():
     assert np.array_equal(codes, rc) and np.array_equal(scales, rs)
 
 
-@pytest.mark.parametrize("m,n,k", [(37, 300, 384), (128, 128, 128), (200, 136, 1024)])
+# 128-k stages: 3 and 1 (only the last partial pass), 8 (two whole passes over the four-slot
+# ring), 5, 6 and 7 (a whole pass, then 1, 2 or 3 stages)
+@pytest.mark.parametrize("m,n,k", [(37, 300, 384), (128, 128, 128), (200, 136, 1024), (64, 200, 640),
+                                   (130, 96, 768), (96, 150, 896)])
 def test_gemm_small(m, n, k):
     rng = np.random.default_rng(m + n + k)
     a = workloads.to_bf16_values(_inputs(rng, m, k))
