@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx(const uint8_t* __restrict__ 
       }
     }
   };
-  // Stage kt (slot B = kt % 4), its fragments already in registers (cur): wait for this
+  // Stage kt (slot B = kt % 4), its fragments already in registers (fr[kt & 1]): wait for this
   // wave's copies of kt + 1 (only the copies of kt + 2, issued one stage later, may stay in
   // flight), barrier (every wave's copies of kt + 1 have landed, and every wave is done
   // with kt - 1: its fragments were read a stage earlier and consumed by its MFMAs), copy
