@@ -202,6 +202,36 @@ def test_gemm_ten_wave_ring_ragged(m, n, k, act):
     bf16_gate(bf16_values(fp4.gemm_w4aX(act, ad, wq)), oracle.formats.bf16_round(ref))
 
 
+@pytest.mark.parametrize("act", [4, 8, 16])
+def test_gemm_ten_wave_zero_groups(act):
+    """The 10-wave form's group-boundary factors where macro-scales are zero (a zero factor
+    counts as 1): a weight row with every group zero, weight rows and activation rows with
+    one zero group in the middle (ratios into and out of it), a zero activation row."""
+    m, n, k = 500, 4800, 1536
+    name = fp4.fp4_product_kernel(act, torch.bfloat16, m, n, k)
+    assert name.startswith("k_gemm_w10 "), f"shape no longer selects the 10-wave form ({name})"
+    rng = np.random.default_rng(660 + act)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    a[:, rng.choice(k, 3, replace=False)] *= 50
+    a[7] = 0.0
+    a[11, 512:768] = 0.0
+    a[300, 0:256] = 0.0
+    a = workloads.to_bf16_values(a)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    w[3] = 0.0
+    w[17, 256:512] = 0.0
+    w[4799, 1280:1536] = 0.0
+    w[160:176, 768:1024] = 0.0  # one whole 16-row block's group (another workgroup's tile)
+    print(f"[case] gemm 10-wave zero groups {ACTS[act]} m={m} n={n} k={k}", flush=True)
+    wq = _wq(w)
+    ad = to_device_bf16(a)
+    ref = _oracle_c(a.astype(np.float64), w, act)
+    got = host(fp4.gemm_w4aX(act, ad, wq, out_dtype=torch.float32))
+    assert np.all(got[7] == 0.0) and np.all(got[:, 3] == 0.0)
+    f32_gate(got, ref)
+    bf16_gate(bf16_values(fp4.gemm_w4aX(act, ad, wq)), oracle.formats.bf16_round(ref))
+
+
 @pytest.mark.parametrize("act", [16, 4])
 def test_gemm_wide_tiles_large_k_sampled(act):
     """At k = 13312 (52 groups) the 64 x 512 form's macro-scale table no longer fits its LDS,
