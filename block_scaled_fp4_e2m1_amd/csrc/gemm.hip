@@ -648,7 +648,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
       if (H == 0) load_micro(mu_nxt, min((s >> 1) + 1, groups - 1));
     } else {
       __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<63>::value);
+      asm volatile("" ::: "memory");  // (no memory access moves across the barrier)
       __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       if (H == 0) load_micro(mu_nxt, min((s >> 1) + 1, groups - 1));
       __builtin_amdgcn_sched_barrier(0);
