@@ -304,7 +304,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
     });
     __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<2 * kCp>::value);
   }
+  asm volatile("" ::: "memory");  // (no memory access moves across the barrier)
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
   float4_t x[kMI][kNI];
 #pragma unroll
@@ -486,7 +488,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_gemm_r8(GemmArgs args) {
     }
     step(b_c, C2{}, h_c, rescale_c, g, 0);
     __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<kWait>::value);
+    asm volatile("" ::: "memory");  // (no memory access moves across the barrier)
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     if (H == 0) {  // a group's first stage: micro-scales of the next group, macro of the one after
       load_mu(mun, min(g + 1, groups - 1));
