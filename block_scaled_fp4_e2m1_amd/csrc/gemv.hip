@@ -119,7 +119,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_bf16(  // <= 128 VGPRs
   // (sched_barrier keeps the code loads above the wait: the count depends on it)
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<2 * kAhead>::value);
+  asm volatile("" ::: "memory");  // (no memory access moves across the barrier)
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 
   // operand chunk of step t of local group gi: a_lane + gi * a_step + t * 32 chunks
