@@ -251,7 +251,10 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
                                                      int q_heads, const int32_t* __restrict__ lengths,
                                                      float scale_log2, float* __restrict__ partial,
                                                      int chunks) {
-  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // chunks are the grid's slowest dimension: every sequence's first chunks are dispatched
+  // before anyone's later (often partial) chunks, so the short workgroups fill the end of
+  // the launch instead of delaying long ones behind them
+  const int chunk = blockIdx.z, kvh = blockIdx.x, b = blockIdx.y;
   const int H = c.kv_heads;
   const int64_t T = c.max_tokens;
   const int64_t L = min((int64_t)max(lengths[b], 0), T);
@@ -598,8 +601,9 @@ hipError_t launch_attention_decode(const KvCacheArgs& c, const uint16_t* q, int 
       q_heads / c.kv_heads > 16 || c.n_seq < 1)
     return hipErrorInvalidValue;
   const int chunks = (int)((c.max_tokens + kChunk - 1) / kChunk);
+  if (c.n_seq > 65535 || chunks > 65535) return hipErrorInvalidValue;  // grid y and z limits
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(k_attn_decode, dim3((unsigned)chunks, (unsigned)c.kv_heads, (unsigned)c.n_seq),
+  hipLaunchKernelGGL(k_attn_decode, dim3((unsigned)c.kv_heads, (unsigned)c.n_seq, (unsigned)chunks),
                      dim3(256), 0, st, c, q, q_heads, lengths, scale_log2, partial, chunks);
   const dim3 grid2((unsigned)(c.n_seq * q_heads)), block2(kHeadDim);
   if (out_bf16)
