@@ -308,7 +308,7 @@ fp4_status gemm_w4aX_impl(int32_t act, const void* a, int32_t a_dtype, int64_t m
   if (ws_ok != FP4_OK) return ws_ok;
   if (!valid_dtype(a_dtype) || !valid_dtype(c_dtype)) return FP4_E_DTYPE;
   const int64_t n = w->rows, k = w->k;
-  if (m < 1 || lda < k || ldc < n) return FP4_E_SHAPE;
+  if (m < 1 || lda < k || ldc < n || ldc > FP4_MAX_LDC) return FP4_E_SHAPE;
   if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
   if (!aligned(c, dtype_size(c_dtype))) return FP4_E_ALIGN;
   const size_t need = act_workspace(act, m, k);
@@ -381,7 +381,7 @@ fp4_status gemm_w4aX_static(int32_t act, const void* a, int32_t a_dtype, int64_t
   if (ws_ok != FP4_OK) return ws_ok;
   if (!valid_dtype(a_dtype) || !valid_dtype(c_dtype)) return FP4_E_DTYPE;
   const int64_t n = w->rows, k = w->k;
-  if (m < 1 || lda < k || ldc < n) return FP4_E_SHAPE;
+  if (m < 1 || lda < k || ldc < n || ldc > FP4_MAX_LDC) return FP4_E_SHAPE;
   const fp4_status lim = check_product(act, m, m, n, k, false, 0, false);
   if (lim != FP4_OK) return lim;
   if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
@@ -413,7 +413,7 @@ fp4_status gemm_w8a8(const void* a, int32_t a_dtype, int64_t m, int64_t lda, con
   if (ws_ok != FP4_OK) return ws_ok;
   if (!valid_dtype(a_dtype) || !valid_dtype(c_dtype)) return FP4_E_DTYPE;
   const int64_t n = w->rows, k = w->k;
-  if (m < 1 || lda < k || ldc < n) return FP4_E_SHAPE;
+  if (m < 1 || lda < k || ldc < n || ldc > FP4_MAX_LDC) return FP4_E_SHAPE;
   const fp4_status lim = check_product(FP4_A8, m, m, n, k, false, 0, true);
   if (lim != FP4_OK) return lim;
   if (!aligned16(a) || (lda * (int64_t)dtype_size(a_dtype)) % 16) return FP4_E_ALIGN;
@@ -453,7 +453,7 @@ fp4_status grouped_gemm_w4aX(int32_t act, const void* a, int32_t a_dtype, int64_
   if (act == FP4_A16 && a_dtype != FP4_BF16) return FP4_E_DTYPE;
   if (n_experts < 1 || w->rows % n_experts) return FP4_E_SHAPE;
   const int64_t n = w->rows / n_experts, k = w->k;
-  if (n % 16 || a_rows < 1 || total_rows < 0 || lda < k || ldc < n) return FP4_E_SHAPE;
+  if (n % 16 || a_rows < 1 || total_rows < 0 || lda < k || ldc < n || ldc > FP4_MAX_LDC) return FP4_E_SHAPE;
   if (!row_token && total_rows > a_rows) return FP4_E_SHAPE;
   // gathered rows are addressed with 32-bit byte offsets from the start of the operand
   // (bf16 A for W4A16, the FP16 activation workspace otherwise: both 2 bytes/element)
@@ -503,7 +503,7 @@ fp4_status grouped_gemm_w4aX_gated(int32_t act, const void* gate_up, int64_t row
   if (!valid_dtype(c_dtype)) return FP4_E_DTYPE;
   if (n_experts < 1 || w->rows % n_experts) return FP4_E_SHAPE;
   const int64_t n = w->rows / n_experts, k = w->k;
-  if (n % 16 || rows < 0 || ld < 2 * k || ldc < n) return FP4_E_SHAPE;
+  if (n % 16 || rows < 0 || ld < 2 * k || ldc < n || ldc > FP4_MAX_LDC) return FP4_E_SHAPE;
   if (!aligned16(gate_up) || (ld * 2) % 16) return FP4_E_ALIGN;
   if (!aligned(c, dtype_size(c_dtype)) || !aligned(expert_offsets, 4)) return FP4_E_ALIGN;
   const size_t need = act_workspace(act, rows, k);

@@ -688,21 +688,29 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
   __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
 
   // ---- apply the final factors, store ----
+  // The stores go through a raw buffer over the tile's valid rows: each store's row offset
+  // is a scalar, the lane's offset is fixed, and a row at or past row_end lies outside the
+  // buffer, where the hardware drops the store (no per-element branch or 64-bit address;
+  // the boundary keeps 128 x ldc x 4 bytes below 2^31).
+  constexpr int kES = C_BF16 ? 2 : 4;
+  const int64_t tile_rows = min((int64_t)kBM, row_end - row_begin);
+  const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<char*>(args.c) + row_begin * args.ldc * kES, (short)0, (int)(tile_rows * args.ldc * kES),
+      kRsrcWord3);
+  const uint32_t c_voff = (uint32_t)(((int64_t)(4 * q) * args.ldc + n0 + l16) * kES);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       if (!w_ok[ni]) continue;
-      const int64_t col = n0 + 16 * ni + l16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t r = row_begin + 16 * mi + 4 * q + i;
-        if (r >= row_end) continue;
+        const uint32_t c_soff = (uint32_t)(((int64_t)(16 * mi + i) * args.ldc + 16 * ni) * kES);
         const float v = x[mi][ni][i] * (A_BF16 ? resc.rw[ni] : resc.ra[mi][i] * resc.rw[ni]);
         if (C_BF16)
-          static_cast<uint16_t*>(args.c)[r * args.ldc + col] = (uint16_t)bf16_rne_bits(v);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(v), c_rsrc, c_voff, c_soff, 0);
         else
-          static_cast<float*>(args.c)[r * args.ldc + col] = v;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), c_rsrc, c_voff, c_soff, 0);
       }
     }
   }

@@ -162,6 +162,14 @@ fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t
                           void* stream);
 
 /*
+ * Output row stride of the products below (gemm_w4aX and its _noalloc / _static forms,
+ * gemm_w8a8, grouped_gemm_w4aX, grouped_gemm_w4aX_gated): n <= ldc <= FP4_MAX_LDC
+ * elements, FP4_E_SHAPE otherwise, before anything is enqueued (the product kernel
+ * addresses a 128-row output tile with 32-bit byte offsets).
+ */
+enum { FP4_MAX_LDC = 1 << 21 };
+
+/*
  * gemm_w4aX -- C[m x n] = A_hat . W_hat^T with float32 accumulation.
  *   act      FP4_A16: A_hat = A;  FP4_A4: A_hat = dequant(quant_e2m1(A));
  *            FP4_A8: A_hat = dequant(quant_e4m3(A)); A is quantized on the device per

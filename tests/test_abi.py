@@ -171,6 +171,30 @@ def test_product_k_limit_is_checked_before_anything_is_enqueued(lib):
                                  24, ws, big, null) == 2
 
 
+def test_product_ldc_bound_is_checked_before_anything_is_enqueued(lib):
+    """Every product entry point takes n <= ldc <= FP4_MAX_LDC (2^21) and returns
+    FP4_E_SHAPE outside it before the device is looked at; at the bound the call reaches
+    the device check (FP4_E_NO_DEVICE on this GPU-less host)."""
+    vp = ctypes.c_void_p
+    fake, null = vp(1 << 20), vp(0)
+    ws, big = vp(1 << 24), 1 << 40
+    T = lib_mod._Tensor
+    w = T(1 << 20, 1 << 21, 1 << 22, 256, 512, 0, 1)
+    w8 = T(1 << 20, 1 << 21, 1 << 22, 256, 512, 1, 1)
+    top = 1 << 21
+    for ldc, want in ((top + 1, 2), (top, 6), (255, 2)):
+        assert lib.gemm_w4aX(4, fake, 1, 64, 512, ctypes.byref(w), fake, 1, ldc, ws, big, null) == want
+        assert lib.gemm_w4aX_noalloc(4, fake, 1, 64, 512, ctypes.byref(w), fake, 1, ldc, null) == want
+        assert lib.gemm_w4aX_static(4, fake, 1, 64, 512, fake, ctypes.byref(w), fake, 1, ldc, ws, big,
+                                    null) == want
+        assert lib.gemm_w8a8(fake, 1, 64, 512, ctypes.byref(w8), fake, 1, ldc, ws, big, null) == want
+    for ldc, want in ((top + 1, 2), (top, 6), (127, 2)):
+        assert lib.grouped_gemm_w4aX(4, fake, 1, 64, 512, null, fake, 2, 64, ctypes.byref(w), fake, 1,
+                                     ldc, ws, big, null) == want
+        assert lib.grouped_gemm_w4aX_gated(4, fake, 64, 1024, fake, 2, ctypes.byref(w), fake, 1, ldc,
+                                           ws, big, null) == want
+
+
 def test_noalloc_validates_before_device_use(lib):
     vp = ctypes.c_void_p
     fake, null = vp(1 << 20), vp(0)
