@@ -616,7 +616,7 @@ fp4_status gemm_mxfp4(const void* a_codes, const uint8_t* a_scales, int64_t m, c
                       void* stream) {
   if (!a_codes || !a_scales || !w_codes || !w_scales || !c) return FP4_E_NULL;
   if (!valid_dtype(c_dtype)) return FP4_E_DTYPE;
-  if (m < 1 || n < 1 || k < 128 || k % 128 || ldc < n || (m + 127) / 128 > 65535 ||
+  if (m < 1 || n < 1 || k < 128 || k % 128 || ldc < n || ldc > FP4_MAX_LDC || (m + 127) / 128 > 65535 ||
       (n + 127) / 128 > 0x7FFFFFFF)
     return FP4_E_SHAPE;
   if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned(c, dtype_size(c_dtype))) return FP4_E_ALIGN;

@@ -31,6 +31,7 @@ constexpr int kMxBlock = 32;
 constexpr int kMxTileK = 128;
 constexpr int kMxTileCode = 1024;
 constexpr int kMxTileScale = 64;
+constexpr int kMxRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
 // One thread per 32-element block; consecutive threads walk (row block, k tile, kb, n) with
 // n fastest, so 16 threads write 256 contiguous code bytes and 64 threads 64 scale bytes.
@@ -280,27 +281,37 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx(const uint8_t* __restrict__ 
   }
   // no copy may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(kVmcntWait<0>::value);
-  // (opaque copies of the lane index and the tile's origin: the store addresses are formed
-  // here, not before the loop, where they would hold registers)
+  // (an opaque copy of the lane index: the lane's store offset is formed here, not before
+  // the loop, where it would hold a register; the resource below is built from wave-uniform
+  // values only, so it stays in scalar registers)
   int lane_e = lane;
-  int64_t m0 = (int64_t)by * 128 + wm * 64;
-  int64_t n0 = (int64_t)bx * 128 + wn * 64;
-  asm volatile("" : "+v"(lane_e), "+s"(m0), "+s"(n0));
+  asm volatile("" : "+v"(lane_e));
+  const int64_t m0 = (int64_t)by * 128 + wm * 64;
+  const int64_t n0 = (int64_t)bx * 128 + wn * 64;
+  // The stores go through a raw buffer over the wave's valid rows: each store's row offset
+  // is a scalar, and a row at or past m lies outside the buffer, where the hardware drops
+  // the store (the boundary keeps 64 x ldc x 4 bytes below 2^31). Columns past n are
+  // masked per lane: the buffer spans whole rows of ldc elements.
+  constexpr int kES = OUT_BF16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<char*>(c) + m0 * ldc * kES, (short)0,
+      (int)(max((int64_t)0, min((int64_t)64, m - m0)) * ldc * kES), kMxRsrcWord3);
+  const int64_t col0 = n0 + (lane_e & 15);
+  const uint32_t c_voff = (uint32_t)(((int64_t)(4 * (lane_e >> 4)) * ldc + col0) * kES);
   // lane l holds rows 4 (l / 16) + t, column l % 16 of each 16 x 16 tile
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + 16 * j + (lane_e & 15);
-      if (col >= n) continue;
+      if (col0 + 16 * j >= n) continue;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int64_t row = m0 + 16 * i + 4 * (lane_e >> 4) + t;
-        if (row >= m) continue;
+        const uint32_t c_soff = (uint32_t)(((int64_t)(16 * i + t) * ldc + 16 * j) * kES);
         if (OUT_BF16)
-          static_cast<uint16_t*>(c)[row * ldc + col] = (uint16_t)bf16_rne_bits(acc[i][j][t]);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(acc[i][j][t]), c_rsrc, c_voff,
+                                                c_soff, 0);
         else
-          static_cast<float*>(c)[row * ldc + col] = acc[i][j][t];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][t]), c_rsrc, c_voff, c_soff, 0);
       }
     }
 }

@@ -163,9 +163,9 @@ fp4_status dequantize_fp4(const fp4_tensor* q, void* y, int32_t y_dtype, int64_t
 
 /*
  * Output row stride of the products below (gemm_w4aX and its _noalloc / _static forms,
- * gemm_w8a8, grouped_gemm_w4aX, grouped_gemm_w4aX_gated): n <= ldc <= FP4_MAX_LDC
- * elements, FP4_E_SHAPE otherwise, before anything is enqueued (the product kernel
- * addresses a 128-row output tile with 32-bit byte offsets).
+ * gemm_w8a8, grouped_gemm_w4aX, grouped_gemm_w4aX_gated, gemm_mxfp4): n <= ldc <=
+ * FP4_MAX_LDC elements, FP4_E_SHAPE otherwise, before anything is enqueued (the product
+ * kernels address an output tile of up to 128 rows with 32-bit byte offsets).
  */
 enum { FP4_MAX_LDC = 1 << 21 };
 

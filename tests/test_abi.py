@@ -193,6 +193,8 @@ def test_product_ldc_bound_is_checked_before_anything_is_enqueued(lib):
                                      ldc, ws, big, null) == want
         assert lib.grouped_gemm_w4aX_gated(4, fake, 64, 1024, fake, 2, ctypes.byref(w), fake, 1, ldc,
                                            ws, big, null) == want
+    for ldc, want in ((top + 1, 2), (top, 6), (255, 2)):
+        assert lib.gemm_mxfp4(fake, fake, 64, fake, fake, 256, 512, fake, 1, ldc, null) == want
 
 
 def test_noalloc_validates_before_device_use(lib):
