@@ -114,6 +114,13 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 // s, after a wait on the wave's own copies; only the activation tile needs the barrier.
 // ---------------------------------------------------------------------------------
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
+
+// Two floats to a bf16 pair (lo, hi) by the hardware conversion: round to nearest even, the
+// same bits as integer rounding of the float pattern for every non-NaN value (denormals,
+// ties and overflow to infinity included); a NaN stays a NaN.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
+}
 constexpr int kBM = 64;              // rows per workgroup
 constexpr int kStageK = 128;         // k per pipeline stage
 constexpr int kAStage = kBM * kStageK * 2 / 16;  // 16-byte chunks: [mi 4][t 4][64]
@@ -704,13 +711,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     for (int ni = 0; ni < NI; ++ni) {
       if (!w_ok[ni]) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; i += 2) {  // rows 4q + i and 4q + i + 1: one bf16 conversion
         const uint32_t c_soff = (uint32_t)(((int64_t)(16 * mi + i) * args.ldc + 16 * ni) * kES);
-        const float v = x[mi][ni][i] * (A_BF16 ? resc.rw[ni] : resc.ra[mi][i] * resc.rw[ni]);
-        if (C_BF16)
-          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(v), c_rsrc, c_voff, c_soff, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), c_rsrc, c_voff, c_soff, 0);
+        const uint32_t c_soff1 = c_soff + (uint32_t)(args.ldc * kES);
+        const float v0 = x[mi][ni][i] * (A_BF16 ? resc.rw[ni] : resc.ra[mi][i] * resc.rw[ni]);
+        const float v1 = x[mi][ni][i + 1] * (A_BF16 ? resc.rw[ni] : resc.ra[mi][i + 1] * resc.rw[ni]);
+        if (C_BF16) {
+          const uint32_t b = bf16x2_rne(v0, v1);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)b, c_rsrc, c_voff, c_soff, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(b >> 16), c_rsrc, c_voff, c_soff1, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), c_rsrc, c_voff, c_soff, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), c_rsrc, c_voff, c_soff1, 0);
+        }
       }
     }
   }

@@ -32,6 +32,13 @@ constexpr int kMaxPerLane = 16;   // E <= 1024 experts
 constexpr int kRouteThreads = 256;
 constexpr int kPlanes = 5;        // chosen + 4 rank bits (top_k <= 16)
 
+// Two floats to a bf16 pair (lo, hi) by the hardware conversion: round to nearest even, the
+// same bits as integer rounding of the float pattern for every non-NaN value (denormals,
+// ties and overflow to infinity included); a NaN stays a NaN.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
+}
+
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const void* __restrict__ y,
   if (OUT_BF16) {
     uint32_t q[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = bf16_rne_bits(acc[2 * i]) | (bf16_rne_bits(acc[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) q[i] = bf16x2_rne(acc[2 * i], acc[2 * i + 1]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + t * ldo + c) = make_uint4(q[0], q[1], q[2], q[3]);
   } else {
     float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + t * ldo + c);

@@ -33,6 +33,13 @@ constexpr int kMxTileCode = 1024;
 constexpr int kMxTileScale = 64;
 constexpr int kMxRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
+// Two floats to a bf16 pair (lo, hi) by the hardware conversion: round to nearest even, the
+// same bits as integer rounding of the float pattern for every non-NaN value (denormals,
+// ties and overflow to infinity included); a NaN stays a NaN.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
+}
+
 // One thread per 32-element block; consecutive threads walk (row block, k tile, kb, n) with
 // n fastest, so 16 threads write 256 contiguous code bytes and 64 threads 64 scale bytes.
 template <int IN_BF16>
@@ -305,13 +312,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx(const uint8_t* __restrict__ 
     for (int j = 0; j < 4; ++j) {
       if (col0 + 16 * j >= n) continue;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 4; t += 2) {  // rows t and t + 1: one bf16 conversion
         const uint32_t c_soff = (uint32_t)(((int64_t)(16 * i + t) * ldc + 16 * j) * kES);
-        if (OUT_BF16)
-          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(acc[i][j][t]), c_rsrc, c_voff,
-                                                c_soff, 0);
-        else
+        const uint32_t c_soff1 = c_soff + (uint32_t)(ldc * kES);
+        if (OUT_BF16) {
+          const uint32_t b = bf16x2_rne(acc[i][j][t], acc[i][j][t + 1]);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)b, c_rsrc, c_voff, c_soff, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(b >> 16), c_rsrc, c_voff, c_soff1, 0);
+        } else {
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][t]), c_rsrc, c_voff, c_soff, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][t + 1]), c_rsrc, c_voff, c_soff1, 0);
+        }
       }
     }
 }
