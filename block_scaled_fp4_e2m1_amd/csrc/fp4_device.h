@@ -102,11 +102,13 @@ __device__ __forceinline__ float fp16_value_hw(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// bfloat16 bits of a finite float32, round to nearest even.
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// bfloat16 bits of a float32, round to nearest even, by the hardware conversion
+// (v_cvt_pk_bf16_f32): on every non-NaN value, denormals, ties and overflow to infinity
+// included, the same bits as integer rounding of the float pattern; a NaN stays a NaN.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return bf16x2_rne(f, 0.0f) & 0xFFFFu; }
 
 __device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
 

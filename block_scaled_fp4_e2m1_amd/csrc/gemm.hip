@@ -115,12 +115,6 @@ __device__ bool find_expert_tile(const int32_t* __restrict__ offsets, int n_expe
 // ---------------------------------------------------------------------------------
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
-// Two floats to a bf16 pair (lo, hi) by the hardware conversion: round to nearest even, the
-// same bits as integer rounding of the float pattern for every non-NaN value (denormals,
-// ties and overflow to infinity included); a NaN stays a NaN.
-__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
-}
 constexpr int kBM = 64;              // rows per workgroup
 constexpr int kStageK = 128;         // k per pipeline stage
 constexpr int kAStage = kBM * kStageK * 2 / 16;  // 16-byte chunks: [mi 4][t 4][64]

@@ -32,12 +32,6 @@ constexpr int kMaxPerLane = 16;   // E <= 1024 experts
 constexpr int kRouteThreads = 256;
 constexpr int kPlanes = 5;        // chosen + 4 rank bits (top_k <= 16)
 
-// Two floats to a bf16 pair (lo, hi) by the hardware conversion: round to nearest even, the
-// same bits as integer rounding of the float pattern for every non-NaN value (denormals,
-// ties and overflow to infinity included); a NaN stays a NaN.
-__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
-}
 
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);

@@ -33,12 +33,6 @@ constexpr int kMxTileCode = 1024;
 constexpr int kMxTileScale = 64;
 constexpr int kMxRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
-// Two floats to a bf16 pair (lo, hi) by the hardware conversion: round to nearest even, the
-// same bits as integer rounding of the float pattern for every non-NaN value (denormals,
-// ties and overflow to infinity included); a NaN stays a NaN.
-__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
-}
 
 // One thread per 32-element block; consecutive threads walk (row block, k tile, kb, n) with
 // n fastest, so 16 threads write 256 contiguous code bytes and 64 threads 64 scale bytes.

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
   if (OUT_BF16) {
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = bf16_rne_bits(v[2 * i]) | (bf16_rne_bits(v[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = bf16x2_rne(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + r * ldy + col) =
         make_uint4(w[0], w[1], w[2], w[3]);
   } else {
