@@ -408,22 +408,29 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
         acc_s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[s], acc_s[mt], 0, 0, 0);
       }
     }
-    // scores (base 2) of tokens t0 + 16 mt + 4g + i for query column n
+    // scores (base 2) of tokens t0 + 16 mt + 4g + i for query column n; only the last tile
+    // of a sequence holds tokens past its length (wave-uniform test)
     float sc[8], vr[8];
+    const int rem = (int)min(L - t0, (int64_t)kTile);  // tokens of this tile inside the sequence
+    auto scores = [&](auto full_c) __attribute__((always_inline)) {
+      constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int tk = it * kTile + 16 * mt + 4 * g;  // token index inside the wave
-      const uint2 kM = *reinterpret_cast<const uint2*>(g_kM[wave] + tk);
-      const uint2 vM = *reinterpret_cast<const uint2*>(g_vM[wave] + tk);
-      const uint32_t kh[4] = {kM.x & 0xFFFFu, kM.x >> 16, kM.y & 0xFFFFu, kM.y >> 16};
-      const uint32_t vh[4] = {vM.x & 0xFFFFu, vM.x >> 16, vM.y & 0xFFFFu, vM.y >> 16};
+      for (int mt = 0; mt < 2; ++mt) {
+        const int tk = it * kTile + 16 * mt + 4 * g;  // token index inside the wave
+        const uint2 kM = *reinterpret_cast<const uint2*>(g_kM[wave] + tk);
+        const uint2 vM = *reinterpret_cast<const uint2*>(g_vM[wave] + tk);
+        const uint32_t kh[4] = {kM.x & 0xFFFFu, kM.x >> 16, kM.y & 0xFFFFu, kM.y >> 16};
+        const uint32_t vh[4] = {vM.x & 0xFFFFu, vM.x >> 16, vM.y & 0xFFFFu, vM.y >> 16};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool live = t0 + 16 * mt + 4 * g + i < L;
-        sc[4 * mt + i] = live ? acc_s[mt][i] * (fp16_bits_to_float(kh[i]) * smul) : -INFINITY;
-        vr[4 * mt + i] = live ? fp16_bits_to_float(vh[i]) * pv_mul : 0.0f;
+        for (int i = 0; i < 4; ++i) {
+          const bool live = kFull || 16 * mt + 4 * g + i < rem;
+          sc[4 * mt + i] = live ? acc_s[mt][i] * (fp16_bits_to_float(kh[i]) * smul) : -INFINITY;
+          vr[4 * mt + i] = live ? fp16_bits_to_float(vh[i]) * pv_mul : 0.0f;
+        }
       }
-    }
+    };
+    if (rem == kTile) scores(std::true_type{});
+    else scores(std::false_type{});
     float mx = sc[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
@@ -453,7 +460,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
 
     // O^T += V'^T . P''^T; slots of tokens past the length get micro-scale 0 (their cache
     // bytes may hold anything)
-    const bool tail = t0 + kTile > L;
+    const bool tail = rem < kTile;
     uint32_t keep_lo = 0xFFFFFFFFu, keep_hi = 0xFFFFFFFFu;
     if (tail) {
       keep_lo = 0u;
@@ -461,7 +468,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int tok = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);
-        if (t0 + tok < L) {
+        if (tok < rem) {
           if (i < 4) keep_lo |= 0xFFu << (8 * i); else keep_hi |= 0xFFu << (8 * (i - 4));
         }
       }
