@@ -247,7 +247,7 @@ __device__ __forceinline__ float fp16_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-__global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 3) void k_attn_decode(fp4lib::KvCacheArgs c, const uint16_t* __restrict__ q,
                                                      int q_heads, const int32_t* __restrict__ lengths,
                                                      float scale_log2, float* __restrict__ partial,
                                                      int chunks) {
@@ -458,31 +458,36 @@ __global__ __launch_bounds__(256) void k_attn_decode(fp4lib::KvCacheArgs c, cons
     l_run += psum;
     m_run = m_new;
 
-    // O^T += V'^T . P''^T; slots of tokens past the length get micro-scale 0 (their cache
-    // bytes may hold anything)
-    const bool tail = rem < kTile;
-    uint32_t keep_lo = 0xFFFFFFFFu, keep_hi = 0xFFFFFFFFu;
-    if (tail) {
-      keep_lo = 0u;
-      keep_hi = 0u;
+    // O^T += V'^T . P''^T; in the last tile of a sequence, slots of tokens past the length
+    // get micro-scale 0 (their cache bytes may hold anything)
+    auto value_product = [&](auto full_c) __attribute__((always_inline)) {
+      constexpr bool kFull = decltype(full_c)::value;
+      uint32_t keep_lo = 0xFFFFFFFFu, keep_hi = 0xFFFFFFFFu;
+      if constexpr (!kFull) {
+        keep_lo = 0u;
+        keep_hi = 0u;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);
-        if (tok < rem) {
-          if (i < 4) keep_lo |= 0xFFu << (8 * i); else keep_hi |= 0xFFu << (8 * (i - 4));
+        for (int i = 0; i < 8; ++i) {
+          const int tok = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);
+          if (tok < rem) {
+            if (i < 4) keep_lo |= 0xFFu << (8 * i); else keep_hi |= 0xFFu << (8 * (i - 4));
+          }
         }
       }
-    }
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      // column d = 16 dt + n is V code row 64 (dt / 4) + 16 (dt % 4) + n; its dword g holds
-      // slots 8g .. 8g + 7
-      const uint32_t vc = reinterpret_cast<const uint32_t*>(&st.vc[dt >> 2][16 * (dt & 3) + n])[g];
-      const uint2 vm = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(st.vm) + dt * 32 + 8 * g);
-      const half8_t a = decode_per_slot(vc, vm.x & keep_lo, vm.y & keep_hi);
-      acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp, acc_o[dt], 0, 0, 0);
-      acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp_lo, acc_o[dt], 0, 0, 0);
-    }
+      for (int dt = 0; dt < 8; ++dt) {
+        // column d = 16 dt + n is V code row 64 (dt / 4) + 16 (dt % 4) + n; its dword g holds
+        // slots 8g .. 8g + 7
+        const uint32_t vc = reinterpret_cast<const uint32_t*>(&st.vc[dt >> 2][16 * (dt & 3) + n])[g];
+        const uint2 vm =
+            *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(st.vm) + dt * 32 + 8 * g);
+        const half8_t a = decode_per_slot(vc, kFull ? vm.x : vm.x & keep_lo, kFull ? vm.y : vm.y & keep_hi);
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp, acc_o[dt], 0, 0, 0);
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp_lo, acc_o[dt], 0, 0, 0);
+      }
+    };
+    if (rem == kTile) value_product(std::true_type{});
+    else value_product(std::false_type{});
   };
   for (int it0 = 0; it0 < n_tiles; it0 += kStages) {
     step(std::integral_constant<int, 0>(), it0);
