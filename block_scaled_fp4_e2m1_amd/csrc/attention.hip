@@ -181,18 +181,14 @@ __device__ __forceinline__ half8_t decode_uniform(uint32_t cw, uint32_t mu_op) {
   return half8_t{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
 }
 
-// 8 codes with one micro-scale each: bytes of (lo, hi) are the 8 E4M3 micro-scales, turned
-// into FP16 pairs by the hardware conversion (every E4M3 value is an FP16 value); the
-// products e2m1 * mu (at most 6 significant bits, 2^-10 .. 2688) are exact in FP16
-__device__ __forceinline__ half8_t decode_per_slot(uint32_t cw, uint32_t mu_lo, uint32_t mu_hi) {
-  const half2_t m01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(mu_lo, 1.0f, false);
-  const half2_t m23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(mu_lo, 1.0f, true);
-  const half2_t m45 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(mu_hi, 1.0f, false);
-  const half2_t m67 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(mu_hi, 1.0f, true);
-  const half2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * m01;
-  const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * m23;
-  const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * m45;
-  const half2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * m67;
+// 8 codes with one micro-scale each, the micro-scales given as FP16 pairs (slots 0-1, 2-3,
+// 4-5, 6-7; every E4M3 value is an FP16 value): the products e2m1 * mu (at most 6
+// significant bits, 2^-10 .. 2688) are exact in FP16
+__device__ __forceinline__ half8_t decode_per_slot_h(uint32_t cw, uint4 m) {
+  const half2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * __builtin_bit_cast(half2_t, m.x);
+  const half2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * __builtin_bit_cast(half2_t, m.y);
+  const half2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * __builtin_bit_cast(half2_t, m.z);
+  const half2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * __builtin_bit_cast(half2_t, m.w);
   return half8_t{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
 }
 
@@ -225,6 +221,9 @@ __shared__ TileStage g_st1[4];
 __shared__ TileStage g_st2[kStages > 2 ? 4 : 1];
 __shared__ uint16_t g_kM[4][kWaveTokens];  // macro-scales of each wave's tokens
 __shared__ uint16_t g_vM[4][kWaveTokens];
+// the current tile's V micro-scales of each wave as FP16 pairs, [block][slot / 2]: every
+// byte is converted once per tile here instead of by each of the 16 lanes that read it
+__shared__ uint32_t g_vmh[4][128];
 __shared__ float g_m[4][16];
 __shared__ float g_l[4][16];
 
@@ -391,6 +390,23 @@ __global__ __launch_bounds__(256, 3) void k_attn_decode(fp4lib::KvCacheArgs c, c
     __builtin_amdgcn_s_waitcnt(kVmcntWait<kDmaPerTile * (kStages - 1)>::value);  // tile it has landed
     const TileStage& st = stage_ref<S>(wave);
     const int64_t t0 = w_lo + (int64_t)it * kTile;
+    const int rem = (int)min(L - t0, (int64_t)kTile);  // tokens of this tile inside the sequence
+    {
+      // V micro-scales to FP16: lane l converts the tile's bytes 4l .. 4l + 3 (block l / 8,
+      // slots 4 (l % 8) .. + 3), zeroing the slots of tokens past the length. Slots are not in
+      // token order: slots 8j .. 8j + 3 hold tokens 4j .. 4j + 3, slots 8j + 4 .. 8j + 7 hold
+      // tokens 16 + 4j .. 16 + 4j + 3 (the order of the scores in the P operand).
+      const uint32_t vmw = st.vm[lane];
+      uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vmw, 1.0f, false));
+      uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vmw, 1.0f, true));
+      if (rem < kTile) {
+        const int s0 = 4 * (lane & 7);                           // the lane's first slot
+        const int tok0 = 16 * ((s0 >> 2) & 1) + 4 * (s0 >> 3);  // its token
+        p0 &= (tok0 < rem ? 0xFFFFu : 0u) | (tok0 + 1 < rem ? 0xFFFF0000u : 0u);
+        p1 &= (tok0 + 2 < rem ? 0xFFFFu : 0u) | (tok0 + 3 < rem ? 0xFFFF0000u : 0u);
+      }
+      *reinterpret_cast<uint2*>(&g_vmh[wave][2 * lane]) = make_uint2(p0, p1);
+    }
 
     // S^T for the two 16-token halves
     float4_t acc_s[2];
@@ -411,7 +427,6 @@ __global__ __launch_bounds__(256, 3) void k_attn_decode(fp4lib::KvCacheArgs c, c
     // scores (base 2) of tokens t0 + 16 mt + 4g + i for query column n; only the last tile
     // of a sequence holds tokens past its length (wave-uniform test)
     float sc[8], vr[8];
-    const int rem = (int)min(L - t0, (int64_t)kTile);  // tokens of this tile inside the sequence
     auto scores = [&](auto full_c) __attribute__((always_inline)) {
       constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
@@ -458,36 +473,19 @@ __global__ __launch_bounds__(256, 3) void k_attn_decode(fp4lib::KvCacheArgs c, c
     l_run += psum;
     m_run = m_new;
 
-    // O^T += V'^T . P''^T; in the last tile of a sequence, slots of tokens past the length
-    // get micro-scale 0 (their cache bytes may hold anything)
-    auto value_product = [&](auto full_c) __attribute__((always_inline)) {
-      constexpr bool kFull = decltype(full_c)::value;
-      uint32_t keep_lo = 0xFFFFFFFFu, keep_hi = 0xFFFFFFFFu;
-      if constexpr (!kFull) {
-        keep_lo = 0u;
-        keep_hi = 0u;
+    // O^T += V'^T . P''^T, the micro-scales from the wave's FP16 table (written at the start
+    // of this tile's step; in the last tile of a sequence the slots of tokens past the
+    // length hold 0 there, since their cache bytes may hold anything)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int tok = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);
-          if (tok < rem) {
-            if (i < 4) keep_lo |= 0xFFu << (8 * i); else keep_hi |= 0xFFu << (8 * (i - 4));
-          }
-        }
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        // column d = 16 dt + n is V code row 64 (dt / 4) + 16 (dt % 4) + n; its dword g holds
-        // slots 8g .. 8g + 7
-        const uint32_t vc = reinterpret_cast<const uint32_t*>(&st.vc[dt >> 2][16 * (dt & 3) + n])[g];
-        const uint2 vm =
-            *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(st.vm) + dt * 32 + 8 * g);
-        const half8_t a = decode_per_slot(vc, kFull ? vm.x : vm.x & keep_lo, kFull ? vm.y : vm.y & keep_hi);
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp, acc_o[dt], 0, 0, 0);
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp_lo, acc_o[dt], 0, 0, 0);
-      }
-    };
-    if (rem == kTile) value_product(std::true_type{});
-    else value_product(std::false_type{});
+    for (int dt = 0; dt < 8; ++dt) {
+      // column d = 16 dt + n is V code row 64 (dt / 4) + 16 (dt % 4) + n; its dword g holds
+      // slots 8g .. 8g + 7
+      const uint32_t vc = reinterpret_cast<const uint32_t*>(&st.vc[dt >> 2][16 * (dt & 3) + n])[g];
+      const uint4 mh = *reinterpret_cast<const uint4*>(&g_vmh[wave][dt * 16 + 4 * g]);
+      const half8_t a = decode_per_slot_h(vc, mh);
+      acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp, acc_o[dt], 0, 0, 0);
+      acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp_lo, acc_o[dt], 0, 0, 0);
+    }
   };
   for (int it0 = 0; it0 < n_tiles; it0 += kStages) {
     step(std::integral_constant<int, 0>(), it0);

@@ -174,6 +174,55 @@ def test_attention_bf16_out_and_edge_lengths():
     bf16_gate(g[1:], oracle.formats.bf16_round(ref[1:]))
 
 
+def _tile_slot(t: int) -> int:
+    """Slot of token t (0..31) in its 32-token V tile (include/fp4_e2m1.h): slots 8g + i
+    hold tokens 4g + i for i < 4 and 16 + 4g + i - 4 for i >= 4."""
+    return 8 * (t // 4) + t % 4 if t < 16 else 8 * ((t - 16) // 4) + 4 + (t - 16) % 4
+
+
+def test_attention_ragged_tails_ignore_garbage_past_length():
+    """Lengths whose last 32-token tile holds 2-31 tokens (both halves of the slot order,
+    16 and 17 included), with the cache past every length poisoned: E4M3 NaN (0x7F) K and
+    V micro-scales for the rest of the last tile, FP16 NaN K and V macro-scales for every
+    token past the length. The output must match the oracle over the live tokens only."""
+    T, kv_heads, q_heads = 1024, 2, 8
+    lengths = [2, 5, 15, 16, 17, 20, 27, 30, 100, 529, 1000, 1023]
+    n_seq = len(lengths)
+    print(f"[case] attention ragged tails with NaN past the length: {lengths}", flush=True)
+    rng = np.random.default_rng(97)
+    width = kv_heads * 128
+    cache = fp4.KvCache(n_seq, T, kv_heads)
+    k = workloads.to_bf16_values(_rows(rng, n_seq * T, width))
+    v = workloads.to_bf16_values(_rows(rng, n_seq * T, width, outliers=False))
+    q = workloads.to_bf16_values(rng.standard_normal((n_seq, q_heads, 128)).astype(np.float32))
+    fp4.kv_cache_append(cache, torch.from_numpy(k).cuda().to(torch.bfloat16),
+                        torch.from_numpy(v).cuda().to(torch.bfloat16),
+                        torch.zeros(n_seq, dtype=torch.int32, device="cuda"))
+    km = host(cache.k_micro).reshape(n_seq, kv_heads, T, 8)
+    vm = host(cache.v_micro).reshape(n_seq, kv_heads, T // 32, 8, 32)
+    kM = host(cache.k_macro).reshape(n_seq, kv_heads // 2, T)
+    vM = host(cache.v_macro).reshape(n_seq, kv_heads // 2, T)
+    for b, L in enumerate(lengths):
+        tile, r = divmod(L, 32)
+        for t in range(r, 32 if r else 0):
+            km[b, :, 32 * tile + t, :] = 0x7F
+            vm[b, :, tile, :, _tile_slot(t)] = 0x7F
+        kM[b, :, L:] = 0x7E00
+        vM[b, :, L:] = 0x7E00
+    for dst, src in ((cache.k_micro, km), (cache.v_micro, vm), (cache.k_macro, kM), (cache.v_macro, vM)):
+        dst.copy_(torch.from_numpy(np.ascontiguousarray(src).reshape(-1)))
+    lens = np.asarray(lengths, dtype=np.int32)
+    got = host(fp4.attention_decode_fp4kv(torch.from_numpy(q).cuda().to(torch.bfloat16), cache,
+                                          torch.from_numpy(lens).cuda(), out_dtype=torch.float32))
+    assert np.all(np.isfinite(got))
+    k_hat = oracle.kv_dequantize_rows(k).reshape(n_seq, T, kv_heads, 128)
+    v_hat = oracle.kv_dequantize_rows(v).reshape(n_seq, T, kv_heads, 128)
+    sc = 1.0 / np.sqrt(128)
+    ref = oracle.attention_decode(q, k_hat, v_hat, lens, sc)
+    ref_abs = oracle.attention_decode(q, k_hat, np.abs(v_hat), lens, sc)
+    attention_gate(got, ref, ref_abs)
+
+
 def test_attention_deterministic():
     print("[case] attention repeat", flush=True)
     n_seq, kv_heads, q_heads, T = 2, 2, 8, 1024
