@@ -262,6 +262,16 @@ def fp4_product_kernel(act: int, a_dtype: torch.dtype, m: int, n: int, k: int, g
     return None if r is None else r.decode()
 
 
+def _out(out, rows: int, cols: int, dtype: torch.dtype, device) -> torch.Tensor:
+    """The product's output: the caller's ``out`` ([rows x cols], contiguous rows, any row
+    stride >= cols), checked, or a new tensor."""
+    if out is None:
+        return torch.empty(rows, cols, dtype=dtype, device=device)
+    if out.dim() != 2 or tuple(out.shape) != (rows, cols) or (rows > 0 and out.stride(1) != 1):
+        raise ValueError(f"out must be [{rows} x {cols}] with contiguous rows")
+    return out
+
+
 def _workspace(act: int, rows: int, n: int, k: int, device, workspace):
     need = fp4_workspace_bytes(act, rows, n, k)
     if need == 0:
@@ -277,7 +287,7 @@ def gemm_w4aX(act: int, a: torch.Tensor, w: QTensor, out_dtype: torch.dtype = to
     if a.dim() != 2 or a.stride(1) != 1:
         raise ValueError("a must be 2-D with contiguous rows")
     m = a.shape[0]
-    c = out if out is not None else torch.empty(m, w.rows, dtype=out_dtype, device=a.device)
+    c = _out(out, m, w.rows, out_dtype, a.device)
     ws, wsb = _workspace(act, m, w.rows, w.k, a.device, workspace)
     ts = w.c_struct()
     st = library().gemm_w4aX(act, _ptr(a), _dtype_code(a.dtype), m, a.stride(0), ctypes.byref(ts),
@@ -311,7 +321,7 @@ def gemm_w4aX_static(act: int, a: torch.Tensor, act_macro: torch.Tensor, w: QTen
     if act_macro.numel() != w.k // 256 or act_macro.element_size() != 2 or not act_macro.is_contiguous():
         raise ValueError("act_macro must hold k/256 contiguous 16-bit values")
     m = a.shape[0]
-    c = out if out is not None else torch.empty(m, w.rows, dtype=out_dtype, device=a.device)
+    c = _out(out, m, w.rows, out_dtype, a.device)
     ws, wsb = _workspace(act, m, w.rows, w.k, a.device, workspace)
     ts = w.c_struct()
     st = library().gemm_w4aX_static(act, _ptr(a), _dtype_code(a.dtype), m, a.stride(0), _ptr(act_macro),
@@ -327,7 +337,7 @@ def gemm_w8a8(a: torch.Tensor, w: QTensor, out_dtype: torch.dtype = torch.bfloat
     if a.dim() != 2 or a.stride(1) != 1:
         raise ValueError("a must be 2-D with contiguous rows")
     m = a.shape[0]
-    c = out if out is not None else torch.empty(m, w.rows, dtype=out_dtype, device=a.device)
+    c = _out(out, m, w.rows, out_dtype, a.device)
     ws, wsb = _workspace(W8A8, m, w.rows, w.k, a.device, workspace)
     ts = w.c_struct()
     st = library().gemm_w8a8(_ptr(a), _dtype_code(a.dtype), m, a.stride(0), ctypes.byref(ts), _ptr(c),
@@ -344,7 +354,7 @@ def grouped_gemm_w4aX(act: int, a: torch.Tensor, row_token: torch.Tensor | None,
     if a.dim() != 2 or a.stride(1) != 1:
         raise ValueError("a must be 2-D with contiguous rows")
     n = w.rows // n_experts
-    c = out if out is not None else torch.empty(total_rows, n, dtype=out_dtype, device=a.device)
+    c = _out(out, total_rows, n, out_dtype, a.device)
     ws, wsb = _workspace(act, a.shape[0], n, w.k, a.device, workspace)
     ts = w.c_struct()
     st = library().grouped_gemm_w4aX(act, _ptr(a), _dtype_code(a.dtype), a.shape[0], a.stride(0),
@@ -365,7 +375,7 @@ def grouped_gemm_w4aX_gated(act: int, gate_up: torch.Tensor, expert_offsets: tor
     if gate_up.dim() != 2 or gate_up.stride(1) != 1:
         raise ValueError("gate_up must be 2-D with contiguous rows")
     rows, n = gate_up.shape[0], w.rows // n_experts
-    c = out if out is not None else torch.empty(rows, n, dtype=out_dtype, device=gate_up.device)
+    c = _out(out, rows, n, out_dtype, gate_up.device)
     ws, wsb = _workspace(act, rows, n, w.k, gate_up.device, workspace)
     ts = w.c_struct()
     st = library().grouped_gemm_w4aX_gated(act, _ptr(gate_up), rows, gate_up.stride(0),
@@ -524,7 +534,7 @@ def gemm_mxfp4(a: MxTensor, w: MxTensor, out_dtype: torch.dtype = torch.bfloat16
     """C [a.rows, w.rows] = A_hat . W_hat^T on the block-scaled FP4 matrix instruction."""
     if a.k != w.k:
         raise ValueError("a and w must have the same k")
-    c = out if out is not None else torch.empty(a.rows, w.rows, dtype=out_dtype, device=a.codes.device)
+    c = _out(out, a.rows, w.rows, out_dtype, a.codes.device)
     st = library().gemm_mxfp4(_ptr(a.codes), _ptr(a.scales), a.rows, _ptr(w.codes), _ptr(w.scales), w.rows, a.k,
                               _ptr(c), _dtype_code(c.dtype), c.stride(0), _stream())
     _check(st, "gemm_mxfp4")
