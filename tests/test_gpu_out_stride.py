@@ -115,3 +115,32 @@ def test_out_shape_is_checked():
         fp4.gemm_w4aX(fp4.A4, a, wq, out=torch.empty(8, 48, dtype=torch.bfloat16, device="cuda"))
     with pytest.raises(ValueError):
         fp4.gemm_w4aX(fp4.A4, a, wq, out=torch.empty(32, 8, dtype=torch.bfloat16, device="cuda").t())
+
+
+@pytest.mark.parametrize("kind", ["gemm", "mx"])
+def test_largest_row_stride(kind):
+    """Row stride at the boundary's limit, FP4_MAX_LDC = 2^21 float32 elements (8 MiB per
+    row, 512 MiB for 64 rows): the 32-bit byte offsets of a tile's stores stay in range,
+    and the results equal the contiguous ones bit for bit (ragged second row tile)."""
+    m, n, k = 70, 272, 256
+    ldc = 1 << 21
+    rng = np.random.default_rng(3)
+    print(f"[case] largest row stride {kind} {m}x{n}x{k} ldc={ldc}", flush=True)
+    a = workloads.to_bf16_values(rng.standard_normal((m, k)).astype(np.float32))
+    w = (0.05 * rng.standard_normal((n, k))).astype(np.float32)
+    if kind == "gemm":
+        wq = fp4.quantize_fp4(torch.from_numpy(w).cuda(), layout=fp4.LAYOUT_TILED)
+        run = lambda out=None: fp4.gemm_w4aX(fp4.A4, to_device_bf16(a), wq, out_dtype=torch.float32, out=out)
+    else:
+        aq = fp4.quantize_mxfp4(to_device_bf16(a))
+        wq = fp4.quantize_mxfp4(torch.from_numpy(w).cuda())
+        run = lambda out=None: fp4.gemm_mxfp4(aq, wq, out_dtype=torch.float32, out=out)
+    ref = run()
+    big = torch.full((m, ldc), 3.0, dtype=torch.float32, device="cuda")
+    view = big[:, :n]
+    run(view)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(view.contiguous()).view(np.uint32), host(ref).view(np.uint32))
+    assert bool(torch.all(big[:, n:n + 4096] == 3.0)) and bool(torch.all(big[:, -4096:] == 3.0))
+    del big
+    torch.cuda.empty_cache()
