@@ -333,6 +333,31 @@ def bench_quantize(torch, fp4, workloads, steps):
     return out
 
 
+def bench_dequantize(torch, fp4, workloads, steps):
+    """dequantize_fp4 of the decode weights (14336 x 4096 E2M1, tiled) to bf16: codes,
+    micro- and macro-scales read once, the bf16 matrix written once (GB/s of both). 8
+    quantized copies rotate (268 MB) into two output buffers."""
+    _, w, _ = workloads.decode()
+    q0 = fp4.quantize_fp4(torch.from_numpy(w).cuda(), layout=fp4.LAYOUT_TILED)
+    del w
+    n, k = q0.rows, q0.k
+    srcs = [q0] + [clone_q(fp4, q0) for _ in range(7)]
+    outs = [torch.empty(n, k, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    fns = [(lambda q=q, o=outs[i % 2]: fp4.dequantize_fp4(q, out=o)) for i, q in enumerate(srcs)]
+    for f in fns:
+        f()
+    g = capture(torch, fns)
+    g.replay()
+    timer = Timer(torch)
+    n_steps = max(len(fns), steps)
+    secs = run_steps(torch, timer, g, fns, n_steps) / n_steps
+    spread = replay_samples(torch, g, len(fns), 8)
+    nbytes = n * k // 2 + n * k // 16 + n * (k // 256) * 2 + n * k * 2
+    return {"tiled_to_bf16": dict(rows=n, k=k, per_call_s=secs, bytes=nbytes, inputs_rotated=len(fns),
+                                  call_us_p10_p50_p90=pct_us(spread), gbs=nbytes / secs / 1e9,
+                                  frac_hbm_peak=nbytes / secs / 1e9 / HBM_PEAK_GBS)}
+
+
 def bench_repack(torch, fp4, workloads, steps):
     """repack_fp4 of the decode weights (14336 x 4096 E2M1), canonical -> tiled and back:
     codes, micro- and macro-scales read once and written once (GB/s of both). 16 source
@@ -992,7 +1017,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--skip-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize", "attention", "mx",
+    ap.add_argument("--only", choices=["decode", "prefill", "policy", "moe", "quantize", "dequantize", "attention", "mx",
                                        "sensitive", "probes", "repack", "ceilings"],
                     default=None,
                     help="run one workload only (for profiling); prints its record")
@@ -1039,6 +1064,7 @@ def main():
               "policy": lambda: bench_policy(torch, fp4, workloads, args.steps),
               "moe": lambda: bench_moe(torch, fp4, workloads, args.steps),
               "quantize": lambda: bench_quantize(torch, fp4, workloads, args.steps),
+              "dequantize": lambda: bench_dequantize(torch, fp4, workloads, args.steps),
               "attention": lambda: bench_attention(torch, fp4, workloads, args.steps),
               "mx": lambda: bench_mx(torch, fp4, workloads, args.steps),
               "sensitive": lambda: bench_sensitive(torch, fp4, workloads, args.steps),
@@ -1067,6 +1093,8 @@ def main():
         print("# moe done", file=sys.stderr, flush=True)
         secondary["quantize"] = bench_quantize(torch, fp4, workloads, args.steps)
         print("# quantize done", file=sys.stderr, flush=True)
+        secondary["dequantize"] = bench_dequantize(torch, fp4, workloads, args.steps)
+        print("# dequantize done", file=sys.stderr, flush=True)
         secondary["repack"] = bench_repack(torch, fp4, workloads, max(16, args.steps // 4))
         print("# repack done", file=sys.stderr, flush=True)
         secondary["decode_attention_fp4kv"] = bench_attention(torch, fp4, workloads, max(8, args.steps // 8))

@@ -188,6 +188,50 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
   }
 }
 
+// Tiled E2M1 weights to bf16 / float32, one 16 x 256 tile per wave. The tile's code bytes
+// arrive as two coalesced 1 KB loads: lane 16 j + n then holds row n's codes at columns
+// 32 t + 8 j .. + 7 (t = 0..7; its four dwords of the first half, then of the second). Its
+// micro-scales (blocks 2 t + j / 2 of row n) are one 8-byte word, and the row's
+// macro-scale one load. The lane writes eight runs of 8 columns of its row. Same arithmetic
+// as k_dequantize (the element times mu * M, both exact in float32, then the output's
+// rounding), so the same bits, without the scattered per-lane reads of the tiled layout.
+template <int OUT_BF16>
+__global__ __launch_bounds__(256) void k_dequantize_tiled(const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ micro,
+                                                          const uint16_t* __restrict__ macro, int64_t tiles,
+                                                          int64_t groups, void* __restrict__ y, int64_t ldy) {
+  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= tiles) return;  // whole waves
+  const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
+  const uint4 c0 = *reinterpret_cast<const uint4*>(codes + tile * kTileCodeBytes + lane * 16);
+  const uint4 c1 = *reinterpret_cast<const uint4*>(codes + tile * kTileCodeBytes + 1024 + lane * 16);
+  const uint2 mu = *reinterpret_cast<const uint2*>(micro + tile * kTileMicroBytes + (j >> 1) * 128 + n * 8);
+  const float M = fp16_value(macro[tile * kTileMacro + n]);
+  const int64_t r = (tile / groups) * 16 + n;
+  const int64_t col0 = (tile % groups) * kGroup + 8 * j;
+  const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float scale = e4m3_value(((t < 4 ? mu.x : mu.y) >> (8 * (t & 3))) & 0xFFu) * M;  // exact
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = (cw[t] >> (4 * i)) & 15u;
+      const float mag = e2m1_mag_value(c & 7u) * scale;
+      v[i] = (c & 8u) ? -mag : mag;
+    }
+    const int64_t col = col0 + 32 * t;
+    if (OUT_BF16) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + r * ldy + col) =
+          make_uint4(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]), bf16x2_rne(v[4], v[5]), bf16x2_rne(v[6], v[7]));
+    } else {
+      float4* p = reinterpret_cast<float4*>(static_cast<float*>(y) + r * ldy + col);
+      p[0] = make_float4(v[0], v[1], v[2], v[3]);
+      p[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
 // Activation pass for the matrix kernels. Quantizes each row like k_quantize and writes
 // the *decoded* element times its micro-scale as FP16 (exact: E2M1 * mu has at most 6
 // significant bits in [2^-10, 2688]; E4M3 * mu * 2^-3 at most 8 bits in [2^-21, 25088]),
@@ -376,6 +420,19 @@ hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t k, 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* micro, const uint16_t* macro,
                              int64_t rows, int64_t k, int elem_e4m3, int tiled, void* y,
                              int out_bf16, int64_t ldy, hipStream_t st) {
+  if (tiled && !elem_e4m3 && (reinterpret_cast<uintptr_t>(micro) & 7u) == 0) {
+    // tiled E2M1 (rows % 16 == 0, k % 256 == 0): one tile per wave, four per workgroup
+    const int64_t tiles = (rows / 16) * (k / kGroup);
+    const int64_t blocks = (tiles + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (out_bf16)
+      hipLaunchKernelGGL((k_dequantize_tiled<1>), dim3((unsigned)blocks), dim3(256), 0, st, codes, micro, macro,
+                         tiles, k / kGroup, y, ldy);
+    else
+      hipLaunchKernelGGL((k_dequantize_tiled<0>), dim3((unsigned)blocks), dim3(256), 0, st, codes, micro, macro,
+                         tiles, k / kGroup, y, ldy);
+    return hipGetLastError();
+  }
   const dim3 grid(blocks_for(rows, k)), block(256);
   if (grid.x == 0) return hipErrorInvalidValue;
 #define FP4_D(B, E, T) \
