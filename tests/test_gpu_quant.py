@@ -121,6 +121,21 @@ def test_decode_workload_weights_full_size_sampled_rows():
     _check_quant(_dev(w, "f32"), 0, 1, rows_subset=sel)
 
 
+def test_decode_weights_dequantized_full_size_sampled_rows():
+    """Tiled E2M1 weights [14336 x 4096] dequantized at full size, in the one-tile-per-wave
+    form the dequantize measurement times: 384 sampled rows are exact in float32 and
+    RNE-bf16-exact, against the oracle's dequantization of the oracle's own codes."""
+    _, w, _ = workloads.decode()
+    print("[case] dequantize decode weights 14336x4096 tiled", flush=True)
+    sel = np.sort(np.random.default_rng(105).choice(w.shape[0], 384, replace=False))
+    q, ref, _ = _check_quant(_dev(w, "f32"), 0, 1, rows_subset=sel)
+    want = oracle.dequantize(ref)
+    y32 = host(fp4.dequantize_fp4(q, torch.float32)[torch.from_numpy(sel).cuda()]).astype(np.float64)
+    assert np.array_equal(y32, want)
+    y16 = bf16_values(fp4.dequantize_fp4(q, torch.bfloat16)[torch.from_numpy(sel).cuda()])
+    assert np.array_equal(y16, F.bf16_round(want))
+
+
 def test_prefill_activations_full_size_sampled_rows():
     a, _, _ = workloads.prefill()
     print("[case] prefill activations 2048x4096 bf16", flush=True)
